@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of the batched multi-adapter LoRA layer on one MI355X.
+
+One step = one pass of the whole hot path over one batch: lora_plan (segment
+plan), then lora_apply = shrink (LoRA down projection of every planned pair)
++ base MFMA GEMM + expand epilogue (up projection added to the fp32
+accumulators, one rounding).  Default workload: Llama-7B q_proj decode,
+bf16, d_in = d_out = 4096, 64 tokens, 64 adapters of rank 16, each token on
+a uniformly drawn adapter (synthetic, seeded).
+
+Measurement
+  * value: tokens per second over exactly --steps steps, wall clock between
+    two torch.cuda.synchronize() calls.  Each step is one HIP-graph replay of
+    plan + shrink + GEMM + epilogue on one of R rotated copies of the weights
+    and adapter pool, R chosen so that R copies exceed 1 GiB: every step reads
+    its W and pages from HBM, not from the 256 MiB Infinity Cache.
+  * per-kernel durations: HIP events on the launch stream around each stage,
+    over a second timed pass of eager launches queued behind a busy prefix
+    (so the events measure the kernels, not host launch gaps).
+  * roofline: the dominant kernel (the base GEMM) against 8 TB/s HBM: its
+    algorithmic bytes (W + X) over its average event-measured duration.
+  * LoRA path: t_apply - t_base where t_base is the same step on an empty
+    plan; LoRA bytes = used A and B pages + X rows + U (written and read).
+  * cpu_baseline: the CPU oracle (fp64 numpy) on the same workload, on the
+    host's cores, for a bounded number of seconds.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+METRIC = "tokens/sec per multi-LoRA layer at 1 GPU; LoRA-path HBM GB/s as % of peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", type=int, default=2, help="workload recipe 1..5")
+    ap.add_argument("--event-steps", type=int, default=200)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotation", type=int, default=0, help="copies of W/pool (0: >= 1 GiB)")
+    ap.add_argument("--no-graph", action="store_true")
+    return ap.parse_args()
+
+
+class Copy:
+    """One rotated copy of the layer's HBM-resident tensors."""
+
+    def __init__(self, L, B, torch, clone: bool):
+        self.X = L.X.clone() if clone else L.X
+        self.W_t = L.W_t.clone() if clone else L.W_t
+        a = L.a_pages.clone() if clone else L.a_pages
+        b = L.b_pages.clone() if clone else L.b_pages
+        self.pool = B.Pool(L.dtype, L.w.d_in, L.w.d_out, a, b, L.rank, L.page_start,
+                           L.pool.tensors[4], L.scale)
+        self.plan = torch.empty_like(L.plan)
+        self.ws = torch.empty_like(L.ws)
+        self.Y = torch.empty_like(L.Y)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the layer shards over tokens with no exchange, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from lora_adapter_amd import binding as B
+    from lora_adapter_amd import device as D
+    from lora_adapter_amd import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    B.lib()
+    torch.cuda.set_device(0)
+    w = wl.config(args.workload)
+    L = D.DeviceLayer(w)
+    T, K = w.T, w.K
+    ids, gates, mask = L.ids, L.gates, L.keep_mask
+    empty_ids = torch.full_like(ids, -1)
+
+    # rotation copies: >= 1 GiB of W + pool + X
+    per_copy = (L.W_t.numel() * L.W_t.element_size() + L.a_pages.numel() * L.a_pages.element_size()
+                + L.b_pages.numel() * L.b_pages.element_size() + L.X.numel() * L.X.element_size())
+    R = args.rotation or max(2, int(np.ceil((1 << 30) / per_copy)))
+    copies = [Copy(L, B, torch, clone=(i > 0)) for i in range(R)]
+    stream = torch.cuda.current_stream()
+
+    def step(c, use_ids=ids):
+        B.lora_plan(use_ids, gates, T, K, c.pool, c.plan)
+        B.lora_shrink(c.X, mask, L.keep_scale, T, K, gates, c.pool, c.plan, c.ws)
+        B.lora_base_gemm(c.X, c.W_t, c.Y, T, K, c.pool, c.plan, c.ws)
+        B.lora_expand_epilogue(c.X, c.W_t, c.Y, T, K, c.pool, c.plan, c.ws)
+
+    # ---------------------------------------------------------------- graphs
+    def make_graphs(use_ids):
+        if args.no_graph:
+            return None
+        gs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for c in copies:       # warm the allocator / code objects outside capture
+                step(c, use_ids)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for c in copies:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(c, use_ids)
+            gs.append(g)
+        torch.cuda.synchronize()
+        return gs
+
+    def timed(use_ids, steps, warmup):
+        gs = make_graphs(use_ids)
+        run = (lambda i: gs[i % R].replay()) if gs else (lambda i: step(copies[i % R], use_ids))
+        for i in range(warmup):
+            run(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            run(i)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    elapsed = timed(ids, args.steps, args.warmup)
+    elapsed_base = timed(empty_ids, args.steps, args.warmup)
+    # results of the last apply on copy 0 must not be stale: re-run eagerly
+    step(copies[0], ids)
+    torch.cuda.synchronize()
+    hdr = copies[0].plan[L.layout[0] // 4:L.layout[0] // 4 + 16].cpu().numpy()
+
+    # ---------------------------------------------------------------- per-kernel events
+    big = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+
+    def stage_times(use_ids, n):
+        names = ("plan", "shrink", "gemm", "epilogue")
+        acc = {k: [] for k in names}
+        done = 0
+        while done < n:
+            chunk = min(25, n - done)
+            for _ in range(3):             # busy prefix: the stages below queue behind it
+                torch.mm(big, big)
+            evs = []
+            for i in range(chunk):
+                c = copies[(done + i) % R]
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+                e[0].record(stream)
+                B.lora_plan(use_ids, gates, T, K, c.pool, c.plan)
+                e[1].record(stream)
+                B.lora_shrink(c.X, mask, L.keep_scale, T, K, gates, c.pool, c.plan, c.ws)
+                e[2].record(stream)
+                B.lora_base_gemm(c.X, c.W_t, c.Y, T, K, c.pool, c.plan, c.ws)
+                e[3].record(stream)
+                B.lora_expand_epilogue(c.X, c.W_t, c.Y, T, K, c.pool, c.plan, c.ws)
+                e[4].record(stream)
+                evs.append(e)
+            torch.cuda.synchronize()
+            for e in evs:
+                for j, k in enumerate(names):
+                    acc[k].append(e[j].elapsed_time(e[j + 1]) * 1e3)   # us
+            done += chunk
+        return {k: float(np.median(v)) for k, v in acc.items()}, {k: float(np.mean(v)) for k, v in acc.items()}
+
+    st_med, st_mean = stage_times(ids, args.event_steps)
+    sb_med, sb_mean = stage_times(empty_ids, args.event_steps)
+
+    # ---------------------------------------------------------------- figures
+    e = 2 if L.dtype == B.LORA_BF16 else 4
+    P, S, R_pairs, R_used = (int(hdr[B.PH_PAIRS]), int(hdr[B.PH_SEGS]), int(hdr[B.PH_RPAIRS]),
+                             int(hdr[B.PH_RUSED]))
+    w_bytes = w.d_in * w.d_out * e
+    x_bytes = T * w.d_in * e
+    y_bytes = T * w.d_out * e
+    gemm_alg_bytes = w_bytes + x_bytes
+    t_gemm = st_mean["gemm"] * 1e-6
+    gemm_gbs = gemm_alg_bytes / t_gemm / 1e9
+    t_step = elapsed / args.steps
+    t_base_step = elapsed_base / args.steps
+    t_lora = max(t_step - t_base_step, 1e-12)
+    lora_bytes = R_used * (w.d_in + w.d_out) * e + P * w.d_in * e + 8 * R_pairs
+    if mask is not None:
+        lora_bytes += P * w.d_in
+    lora_flops = 2.0 * R_pairs * (w.d_in + w.d_out)
+    base_flops = 2.0 * T * w.d_in * w.d_out
+    value = T * args.steps / elapsed
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if L.dtype == B.LORA_BF16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": T, "K": K, "d_in": w.d_in, "d_out": w.d_out,
+                   "adapters": w.n_adapters, "ranks": sorted(set(w.rank.tolist()))[:8],
+                   "active_pairs": P, "segments": S, "R_used": R_used, "R_pairs": R_pairs,
+                   "rotation_copies": R, "graph_replay": not args.no_graph},
+        "roofline": {"bound": "hbm", "kernel": "base GEMM (gemm_bf16_kernel)",
+                     "achieved": gemm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gemm_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "alg_bytes_per_launch": gemm_alg_bytes, "avg_launch_us": st_mean["gemm"]},
+        "stages_us_median": st_med,
+        "stages_us_mean": st_mean,
+        "stages_us_mean_empty_plan": sb_mean,
+        "step_us": t_step * 1e6,
+        "step_us_empty_plan": t_base_step * 1e6,
+        "lora_path": {"t_us": t_lora * 1e6, "bytes": lora_bytes, "GB_s": lora_bytes / t_lora / 1e9,
+                      "frac_hbm": lora_bytes / t_lora / 1e9 / HBM_PEAK_GBS, "flops": lora_flops},
+        "layer": {"bytes": w_bytes + x_bytes + y_bytes + lora_bytes,
+                  "GB_s": (w_bytes + x_bytes + y_bytes + lora_bytes) / t_step / 1e9,
+                  "TFLOP_s": (base_flops + lora_flops) / t_step / 1e12,
+                  "frac_mfma": (base_flops + lora_flops) / t_step / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, seconds):
+    """The CPU oracle, untuned, on the same workload: plan + apply per step."""
+    import numpy as np
+    from oracle import lora_oracle as O
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    threads = cores
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        if info:
+            threads = max(int(i.get("num_threads", 1)) for i in info)
+    except Exception:
+        pass
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        O.plan_workload(w)
+        O.apply_workload(w)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or n >= 1000:
+            break
+    return {"value": w.T * n / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} full steps (plan + apply, fp64 numpy) of the same workload in {el:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

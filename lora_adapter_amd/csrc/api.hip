@@ -1,0 +1,315 @@
+// extern "C" entry points of liblora: argument checks on the host (before any
+// HIP call), workspace layout, and kernel dispatch on the caller's stream.
+#include <string.h>
+
+#include "lora_internal.h"
+
+using namespace lora;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+bool dims_ok(int32_t d) { return d > 0 && d % 64 == 0; }
+
+// Checks the descriptor fields every call needs; `need_pages` also asks for
+// the factor pages and scales.
+int32_t check_pool(const lora_pool_desc *p, bool need_pages) {
+  if (!p) return LORA_ERR_INVALID_ARG;
+  if (p->dtype != LORA_F32 && p->dtype != LORA_BF16) return LORA_ERR_INVALID_ARG;
+  if (p->n_adapters < 1 || p->n_pages < 0 || p->n_page_ids < 0) return LORA_ERR_INVALID_ARG;
+  if (!p->rank || !p->page_start || (p->n_page_ids > 0 && !p->page_ids)) return LORA_ERR_INVALID_ARG;
+  if (need_pages) {
+    if (!p->scale) return LORA_ERR_INVALID_ARG;
+    if (p->n_pages > 0 && (!p->a_pages || !p->b_pages)) return LORA_ERR_INVALID_ARG;
+    if (!dims_ok(p->d_in) || !dims_ok(p->d_out)) return LORA_ERR_UNSUPPORTED;
+  }
+  return LORA_OK;
+}
+
+int32_t check_batch(int32_t T, int32_t K) {
+  if (T < 0 || K < 1 || K > LORA_MAX_K) return LORA_ERR_INVALID_ARG;
+  if (int64_t(T) * K > kMaxPairs) return LORA_ERR_UNSUPPORTED;
+  return LORA_OK;
+}
+
+int32_t dev(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_ERR_DEVICE; }
+
+struct ApplyWs {
+  GemmConfig cfg;
+  size_t partial_bytes;   // aligned
+  float *partial;
+  float *U;
+  int64_t u_cap;
+};
+
+ApplyWs apply_layout(void *ws, size_t ws_bytes, int32_t T, int32_t d_in, int32_t d_out, int32_t dtype) {
+  ApplyWs w{};
+  w.cfg = choose_gemm(T > 0 ? T : 1, d_in, d_out, dtype);
+  w.partial_bytes = align_up(gemm_partial_bytes(w.cfg, T, d_out));
+  w.partial = static_cast<float *>(ws);
+  if (ws && ws_bytes >= w.partial_bytes) {
+    w.U = reinterpret_cast<float *>(static_cast<char *>(ws) + w.partial_bytes);
+    w.u_cap = int64_t((ws_bytes - w.partial_bytes) / sizeof(float));
+  } else {
+    w.U = nullptr;
+    w.u_cap = -1;
+  }
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t lora_abi_version(void) { return LORA_ABI_VERSION; }
+
+const char *lora_status_string(int32_t status) {
+  switch (status) {
+    case LORA_OK: return "ok";
+    case LORA_ERR_INVALID_ARG: return "invalid argument";
+    case LORA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case LORA_ERR_CAPACITY: return "buffer too small";
+    case LORA_ERR_DEVICE: return "HIP call failed";
+    default: return "unknown status";
+  }
+}
+
+size_t lora_plan_bytes(int32_t T, int32_t K, int32_t n_adapters) {
+  if (check_batch(T, K) != LORA_OK || n_adapters < 1) return 0;
+  return size_t(plan_layout(int64_t(T) * K, n_adapters).total) * sizeof(int32_t);
+}
+
+int32_t lora_plan_layout(int32_t T, int32_t K, int32_t n_adapters, int64_t offsets_out[9]) {
+  if (!offsets_out || n_adapters < 1) return LORA_ERR_INVALID_ARG;
+  const int32_t st = check_batch(T, K);
+  if (st != LORA_OK) return st;
+  const PlanLayout L = plan_layout(int64_t(T) * K, n_adapters);
+  const int64_t o[9] = {L.hdr, L.pair_tk, L.seg_adapter, L.seg_off, L.seg_row_off,
+                        L.bucket_seg_off, L.u_off, L.slot_pos, L.pair_adapter};
+  for (int i = 0; i < 9; ++i) offsets_out[i] = o[i] * int64_t(sizeof(int32_t));
+  return LORA_OK;
+}
+
+int32_t lora_plan(const int32_t *ids, const float *gates, int32_t T, int32_t K,
+                  const lora_pool_desc *pool, void *plan, size_t plan_bytes, void *stream) {
+  int32_t st = check_batch(T, K);
+  if (st != LORA_OK) return st;
+  if ((st = check_pool(pool, false)) != LORA_OK) return st;
+  if (!plan) return LORA_ERR_INVALID_ARG;
+  if (int64_t(T) * K > 0 && (!ids || !gates)) return LORA_ERR_INVALID_ARG;
+  if (plan_bytes < lora_plan_bytes(T, K, pool->n_adapters)) return LORA_ERR_CAPACITY;
+  return dev(launch_plan(ids, gates, T, K, pool_view(pool), static_cast<int32_t *>(plan),
+                         static_cast<hipStream_t>(stream)));
+}
+
+size_t lora_apply_workspace_bytes(int32_t T, int32_t K, int32_t d_in, int32_t d_out,
+                                  int32_t max_rank, int32_t dtype) {
+  if (check_batch(T, K) != LORA_OK || !dims_ok(d_in) || !dims_ok(d_out)) return 0;
+  if (max_rank < 0 || max_rank > LORA_MAX_RANK) return 0;
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return 0;
+  const GemmConfig c = choose_gemm(T > 0 ? T : 1, d_in, d_out, dtype);
+  const size_t u = size_t(T) * size_t(K) * size_t(max_rank) * sizeof(float);
+  return align_up(gemm_partial_bytes(c, T, d_out)) + align_up(u > 0 ? u : 1);
+}
+
+size_t lora_apply_u_offset(int32_t T, int32_t K, int32_t d_in, int32_t d_out, int32_t dtype) {
+  if (check_batch(T, K) != LORA_OK || !dims_ok(d_in) || !dims_ok(d_out)) return 0;
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return 0;
+  return align_up(gemm_partial_bytes(choose_gemm(T > 0 ? T : 1, d_in, d_out, dtype), T, d_out));
+}
+
+int32_t lora_shrink(const void *X, const uint8_t *keep_mask, float keep_scale, int32_t T,
+                    int32_t K, const float *gates, const lora_pool_desc *pool, const void *plan,
+                    void *ws, size_t ws_bytes, void *stream) {
+  int32_t st = check_batch(T, K);
+  if (st != LORA_OK) return st;
+  if ((st = check_pool(pool, true)) != LORA_OK) return st;
+  if (!plan) return LORA_ERR_INVALID_ARG;
+  if (T == 0) return LORA_OK;
+  if (!X || !gates || !ws) return LORA_ERR_INVALID_ARG;
+  const ApplyWs w = apply_layout(ws, ws_bytes, T, pool->d_in, pool->d_out, pool->dtype);
+  if (w.u_cap < 0) return LORA_ERR_CAPACITY;
+  const int64_t TK = int64_t(T) * K;
+  const PlanView pv = plan_view(plan, TK, pool->n_adapters);
+  ShrinkArgs a{};
+  a.Z = X;
+  a.mask = keep_mask;
+  a.extra_scale = keep_mask ? keep_scale : 1.0f;
+  a.T = T; a.K = K; a.d = pool->d_in;
+  a.pages = pool->a_pages;
+  a.rank = pool->rank; a.page_start = pool->page_start; a.page_ids = pool->page_ids;
+  a.scale = pool->scale;
+  a.gates = gates;
+  a.plan = pv;
+  a.err_word = const_cast<int32_t *>(pv.hdr) + LORA_PH_ERR;
+  a.out = w.U;
+  a.out_cap = w.u_cap;
+  const int64_t bound = w.u_cap < TK * LORA_MAX_RANK ? w.u_cap : TK * LORA_MAX_RANK;
+  return dev(launch_shrink(a, pool->dtype, bound, static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+
+// Shared argument checks and GemmArgs for the two halves of the base stage.
+int32_t base_args(const void *X, const void *W_t, void *Y, int32_t T, int32_t K,
+                  const lora_pool_desc *pool, const void *plan, void *ws,
+                  size_t ws_bytes, GemmConfig &cfg, GemmArgs &g) {
+  int32_t st = check_batch(T, K);
+  if (st != LORA_OK) return st;
+  if ((st = check_pool(pool, true)) != LORA_OK) return st;
+  if (!plan) return LORA_ERR_INVALID_ARG;
+  if (T == 0) return LORA_OK;
+  if (!X || !W_t || !Y || !ws) return LORA_ERR_INVALID_ARG;
+  if (Y == X || Y == W_t) return LORA_ERR_INVALID_ARG;
+  const ApplyWs w = apply_layout(ws, ws_bytes, T, pool->d_in, pool->d_out, pool->dtype);
+  if (w.u_cap < 0) return LORA_ERR_CAPACITY;
+  const int64_t TK = int64_t(T) * K;
+  const PlanView pv = plan_view(plan, TK, pool->n_adapters);
+  cfg = w.cfg;
+  g = GemmArgs{};
+  g.X = X; g.W = W_t; g.M = T; g.N = pool->d_out; g.Kd = pool->d_in;
+  g.k_split = w.cfg.k_split;
+  g.partial = w.partial;
+  g.Y = Y;
+  g.ex.K = K;
+  g.ex.slot_pos = pv.slot_pos; g.ex.u_off = pv.u_off; g.ex.pair_adapter = pv.pair_adapter;
+  g.ex.rank = pool->rank; g.ex.page_start = pool->page_start; g.ex.page_ids = pool->page_ids;
+  g.ex.b_pages = pool->b_pages; g.ex.d_out = pool->d_out;
+  g.ex.U = w.U; g.ex.hdr = pv.hdr; g.ex.u_cap = w.u_cap;
+  return LORA_OK;
+}
+
+}  // namespace
+
+int32_t lora_base_gemm(const void *X, const void *W_t, void *Y, int32_t T, int32_t K,
+                       const lora_pool_desc *pool, const void *plan, void *ws,
+                       size_t ws_bytes, void *stream) {
+  GemmConfig cfg;
+  GemmArgs g;
+  const int32_t st = base_args(X, W_t, Y, T, K, pool, plan, ws, ws_bytes, cfg, g);
+  if (st != LORA_OK || T == 0) return st;
+  return dev(launch_base_gemm(cfg, g, static_cast<hipStream_t>(stream)));
+}
+
+int32_t lora_expand_epilogue(const void *X, const void *W_t, void *Y, int32_t T, int32_t K,
+                             const lora_pool_desc *pool, const void *plan,
+                             void *ws, size_t ws_bytes, void *stream) {
+  GemmConfig cfg;
+  GemmArgs g;
+  const int32_t st = base_args(X, W_t, Y, T, K, pool, plan, ws, ws_bytes, cfg, g);
+  if (st != LORA_OK || T == 0) return st;
+  return dev(launch_epilogue(cfg, g, pool->dtype, static_cast<hipStream_t>(stream)));
+}
+
+int32_t lora_base_expand(const void *X, const void *W_t, void *Y, int32_t T, int32_t K,
+                         const lora_pool_desc *pool, const void *plan,
+                         void *ws, size_t ws_bytes, void *stream) {
+  const int32_t st = lora_base_gemm(X, W_t, Y, T, K, pool, plan, ws, ws_bytes, stream);
+  if (st != LORA_OK) return st;
+  return lora_expand_epilogue(X, W_t, Y, T, K, pool, plan, ws, ws_bytes, stream);
+}
+
+int32_t lora_apply(const void *X, const void *W_t, void *Y, int32_t T, int32_t K,
+                   const float *gates, const uint8_t *keep_mask,
+                   float keep_scale, const lora_pool_desc *pool, const void *plan, void *ws,
+                   size_t ws_bytes, void *stream) {
+  int32_t st = check_batch(T, K);
+  if (st != LORA_OK) return st;
+  if ((st = check_pool(pool, true)) != LORA_OK) return st;
+  if (T > 0 && (!X || !W_t || !Y || !gates || !ws || !plan)) return LORA_ERR_INVALID_ARG;
+  st = lora_shrink(X, keep_mask, keep_scale, T, K, gates, pool, plan, ws, ws_bytes, stream);
+  if (st != LORA_OK) return st;
+  return lora_base_expand(X, W_t, Y, T, K, pool, plan, ws, ws_bytes, stream);
+}
+
+int32_t lora_merge_delta(void *W_t, const lora_pool_desc *pool, const int32_t *merge_ids,
+                         const float *coeffs, int32_t m, void *stream) {
+  int32_t st = check_pool(pool, true);
+  if (st != LORA_OK) return st;
+  if (m < 0 || !W_t) return LORA_ERR_INVALID_ARG;
+  if (m == 0) return LORA_OK;
+  if (!merge_ids || !coeffs) return LORA_ERR_INVALID_ARG;
+  MergeArgs a{};
+  a.W = W_t; a.d_in = pool->d_in; a.d_out = pool->d_out;
+  a.a_pages = pool->a_pages; a.b_pages = pool->b_pages;
+  a.rank = pool->rank; a.page_start = pool->page_start; a.page_ids = pool->page_ids;
+  a.scale = pool->scale;
+  a.n_pages = pool->n_pages; a.n_page_ids = pool->n_page_ids; a.n_adapters = pool->n_adapters;
+  a.ids = merge_ids; a.coeffs = coeffs; a.m = m;
+  return dev(launch_merge(a, pool->dtype, static_cast<hipStream_t>(stream)));
+}
+
+size_t lora_grad_workspace_bytes(int32_t T, int32_t K, int32_t n_adapters, int32_t d_in,
+                                 int32_t d_out, int32_t max_rank, int32_t dtype) {
+  if (check_batch(T, K) != LORA_OK || !dims_ok(d_in) || !dims_ok(d_out) || n_adapters < 1) return 0;
+  if (max_rank < 1 || max_rank > LORA_MAX_RANK) return 0;
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return 0;
+  const int64_t TK = int64_t(T) * K;
+  const size_t g = align_up(size_t(TK) * size_t(max_rank) * sizeof(float) + 4);
+  const size_t pieces = size_t(grad_pieces(TK, n_adapters));
+  const size_t pa = align_up(pieces * size_t(max_rank) * size_t(d_in) * sizeof(float));
+  const size_t pb = align_up(pieces * size_t(max_rank) * size_t(d_out) * sizeof(float));
+  return g + pa + pb;
+}
+
+int32_t lora_grad(const void *X, const uint8_t *keep_mask, float keep_scale, const void *dY,
+                  int32_t T, int32_t K, const float *gates,
+                  const lora_pool_desc *pool, const void *plan, const void *apply_ws,
+                  size_t apply_ws_bytes, float *dA_pages, float *dB_pages, int32_t max_rank,
+                  void *ws, size_t ws_bytes, void *stream) {
+  int32_t st = check_batch(T, K);
+  if (st != LORA_OK) return st;
+  if ((st = check_pool(pool, true)) != LORA_OK) return st;
+  if (!plan || max_rank < 1 || max_rank > LORA_MAX_RANK) return LORA_ERR_INVALID_ARG;
+  if (T == 0) return LORA_OK;
+  if (!X || !dY || !gates || !apply_ws || !dA_pages || !dB_pages || !ws)
+    return LORA_ERR_INVALID_ARG;
+  const int64_t TK = int64_t(T) * K;
+  const size_t need = lora_grad_workspace_bytes(T, K, pool->n_adapters, pool->d_in, pool->d_out,
+                                                max_rank, pool->dtype);
+  if (ws_bytes < need) return LORA_ERR_CAPACITY;
+  const ApplyWs aw = apply_layout(const_cast<void *>(apply_ws), apply_ws_bytes, T, pool->d_in,
+                              pool->d_out, pool->dtype);
+  if (aw.u_cap < 0) return LORA_ERR_CAPACITY;
+  const PlanView pv = plan_view(plan, TK, pool->n_adapters);
+  int32_t *err_word = const_cast<int32_t *>(pv.hdr) + LORA_PH_ERR;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+
+  char *base = static_cast<char *>(ws);
+  const size_t g_bytes = align_up(size_t(TK) * size_t(max_rank) * sizeof(float) + 4);
+  const size_t pieces = size_t(grad_pieces(TK, pool->n_adapters));
+  const size_t pa = align_up(pieces * size_t(max_rank) * size_t(pool->d_in) * sizeof(float));
+  float *G = reinterpret_cast<float *>(base);
+  float *partA = reinterpret_cast<float *>(base + g_bytes);
+  float *partB = reinterpret_cast<float *>(base + g_bytes + pa);
+
+  // G = kappa . g . s . (dY . B_j): the shrink kernel on (dY, B pages)
+  ShrinkArgs sa{};
+  sa.Z = dY; sa.mask = nullptr; sa.extra_scale = keep_mask ? keep_scale : 1.0f;
+  sa.T = T; sa.K = K; sa.d = pool->d_out;
+  sa.pages = pool->b_pages;
+  sa.rank = pool->rank; sa.page_start = pool->page_start; sa.page_ids = pool->page_ids;
+  sa.scale = pool->scale; sa.gates = gates; sa.plan = pv; sa.err_word = err_word;
+  sa.out = G; sa.out_cap = int64_t(TK) * max_rank;
+  hipError_t e = launch_shrink(sa, pool->dtype, sa.out_cap, s);
+  if (e != hipSuccess) return LORA_ERR_DEVICE;
+
+  SegOuterArgs ob{};
+  ob.Z = dY; ob.mask = nullptr; ob.T = T; ob.K = K; ob.d = pool->d_out;
+  ob.coef = aw.U; ob.coef_cap = aw.u_cap; ob.plan = pv;
+  ob.rank = pool->rank; ob.page_start = pool->page_start; ob.page_ids = pool->page_ids;
+  ob.part = partB; ob.max_rank = max_rank; ob.out_pages = dB_pages; ob.err_word = err_word;
+  e = launch_seg_outer(ob, pool->dtype, TK, pool->n_adapters, s);
+  if (e != hipSuccess) return LORA_ERR_DEVICE;
+
+  SegOuterArgs oa = ob;
+  oa.Z = X; oa.mask = keep_mask; oa.d = pool->d_in; oa.coef = G; oa.coef_cap = sa.out_cap;
+  oa.part = partA;
+  oa.out_pages = dA_pages;
+  e = launch_seg_outer(oa, pool->dtype, TK, pool->n_adapters, s);
+  return dev(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,467 @@
+// Base GEMM Y = X.W with the LoRA expand in its epilogue.
+//
+// S-LoRA (section 批处理) batches the base-model product over all requests
+// and adds each request's x.A.B separately without padding; LoRAFusion
+// (section Kernel 层：图分裂融合) keeps the compute-bound GEMM main loop intact
+// and consumes the small A.X intermediate in place.  Here the main loop is a
+// plain gfx950 bf16 MFMA GEMM (v_mfma_f32_32x32x16_bf16, fp32 accumulators,
+// both operands K-contiguous: X[M][K] and W_t[N][K]); the expand
+//   acc[t][n] += sum over t's planned pairs p, rank rows j:  U[u_off[p]+j] . B_a[j][n]
+// is added to the fp32 accumulators of each output tile before the single
+// rounding to the output dtype, so the main loop never sees the adapters.
+//
+// Two epilogue placements, chosen from the shape:
+//   * fused: when the tile grid alone fills the GPU (prefill), each tile
+//     stages its accumulators through LDS, walks its rows once per wave and
+//     adds the expand with the adapter's B slice cached in registers while
+//     consecutive rows share an adapter (long prefill segments);
+//   * split-K: decode shapes have too few output tiles to stream W at full
+//     bandwidth, so K is split across workgroups that write fp32 partial
+//     products; the epilogue kernel then sums the partials in a fixed order,
+//     adds the expand with wide (512-column) coalesced B-row reads, rounds
+//     and stores.  The reduction order is fixed: results are deterministic,
+//     and rows without active slots equal the base-only result bit for bit.
+#include "lora_internal.h"
+
+namespace lora {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// ------------------------------------------------------------ vector loads/stores
+template <typename E, int CPL> struct Cols;
+template <> struct Cols<uint16_t, 1> {
+  static __device__ __forceinline__ void load(const uint16_t *p, float v[1]) { v[0] = bf2f(*p); }
+  static __device__ __forceinline__ void store(uint16_t *p, const float v[1]) { *p = f2bf(v[0]); }
+};
+template <> struct Cols<uint16_t, 2> {
+  static __device__ __forceinline__ void load(const uint16_t *p, float v[2]) {
+    const uint32_t w = *reinterpret_cast<const uint32_t *>(p);
+    v[0] = bf_lo(w); v[1] = bf_hi(w);
+  }
+  static __device__ __forceinline__ void store(uint16_t *p, const float v[2]) {
+    *reinterpret_cast<uint32_t *>(p) = uint32_t(f2bf(v[0])) | (uint32_t(f2bf(v[1])) << 16);
+  }
+};
+template <> struct Cols<uint16_t, 8> {
+  static __device__ __forceinline__ void load(const uint16_t *p, float v[8]) { Elem<uint16_t>::load8(p, v); }
+  static __device__ __forceinline__ void store(uint16_t *p, const float v[8]) {
+    uint4 w;
+    w.x = uint32_t(f2bf(v[0])) | (uint32_t(f2bf(v[1])) << 16);
+    w.y = uint32_t(f2bf(v[2])) | (uint32_t(f2bf(v[3])) << 16);
+    w.z = uint32_t(f2bf(v[4])) | (uint32_t(f2bf(v[5])) << 16);
+    w.w = uint32_t(f2bf(v[6])) | (uint32_t(f2bf(v[7])) << 16);
+    *reinterpret_cast<uint4 *>(p) = w;
+  }
+};
+template <> struct Cols<float, 8> {
+  static __device__ __forceinline__ void load(const float *p, float v[8]) { Elem<float>::load8(p, v); }
+  static __device__ __forceinline__ void store(float *p, const float v[8]) {
+    *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4 *>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+};
+
+__device__ __forceinline__ void load_f8(const float *p, float v[8]) { Elem<float>::load8(p, v); }
+
+// ------------------------------------------------------------ expand of one row
+// v[c] += sum over the row's active slots k (in slot order) and rank rows j
+// (ascending) of U[u_off[p] + j] * B_a[j][col + c].  Wave-uniform control flow:
+// every lane handles the same row; lanes own consecutive columns.
+template <typename E, int CPL>
+__device__ __forceinline__ void expand_row(float (&v)[CPL], int t, int col, bool col_ok,
+                                           const ExpandArgs &e) {
+  const E *B = static_cast<const E *>(e.b_pages);
+  for (int k = 0; k < e.K; ++k) {
+    const int p = e.slot_pos[t * e.K + k];
+    if (p < 0) continue;
+    const int ad = e.pair_adapter[p];
+    const int r = e.rank[ad];
+    const float *u = e.U + e.u_off[p];
+    const int32_t *pid = e.page_ids + e.page_start[ad];
+    int j = 0;
+    for (; j + 4 <= r; j += 4) {
+      float bv[4][CPL];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (col_ok) Cols<E, CPL>::load(B + int64_t(pid[j + q]) * e.d_out + col, bv[q]);
+        else {
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) bv[q][c] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float uj = u[j + q];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) v[c] = fmaf(uj, bv[q][c], v[c]);
+      }
+    }
+    for (; j < r; ++j) {
+      float bv[CPL];
+      if (col_ok) Cols<E, CPL>::load(B + int64_t(pid[j]) * e.d_out + col, bv);
+      else {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) bv[c] = 0.f;
+      }
+      const float uj = u[j];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) v[c] = fmaf(uj, bv[c], v[c]);
+    }
+  }
+}
+
+// Same sums in the same order, with the B slice of the last adapter (rank <=
+// RB) kept in registers: consecutive prefill rows usually share an adapter.
+template <int CPL, int RB>
+struct BCache {
+  int ad;
+  float b[RB][CPL];
+};
+
+template <int CPL, int RB>
+__device__ __forceinline__ void expand_row_cached(float (&v)[CPL], int t, int col, bool col_ok,
+                                                  const ExpandArgs &e, BCache<CPL, RB> &cache) {
+  const uint16_t *B = static_cast<const uint16_t *>(e.b_pages);
+  for (int k = 0; k < e.K; ++k) {
+    const int p = e.slot_pos[t * e.K + k];
+    if (p < 0) continue;
+    const int ad = e.pair_adapter[p];
+    const int r = e.rank[ad];
+    const float *u = e.U + e.u_off[p];
+    const int32_t *pid = e.page_ids + e.page_start[ad];
+    if (r <= RB) {
+      if (ad != cache.ad) {
+#pragma unroll
+        for (int j = 0; j < RB; ++j) {
+          if (j < r && col_ok) Cols<uint16_t, CPL>::load(B + int64_t(pid[j]) * e.d_out + col, cache.b[j]);
+          else {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) cache.b[j][c] = 0.f;
+          }
+        }
+        cache.ad = ad;
+      }
+#pragma unroll
+      for (int j = 0; j < RB; ++j) {
+        if (j < r) {
+          const float uj = u[j];
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) v[c] = fmaf(uj, cache.b[j][c], v[c]);
+        }
+      }
+    } else {
+      for (int j = 0; j < r; ++j) {
+        float bv[CPL];
+        if (col_ok) Cols<uint16_t, CPL>::load(B + int64_t(pid[j]) * e.d_out + col, bv);
+        else {
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) bv[c] = 0.f;
+        }
+        const float uj = u[j];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) v[c] = fmaf(uj, bv[c], v[c]);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ bool expand_enabled(const ExpandArgs &e) {
+  return e.U != nullptr && int64_t(e.hdr[LORA_PH_RPAIRS]) <= e.u_cap;
+}
+
+// ------------------------------------------------------------ bf16 MFMA GEMM
+// Tile BM x BN, K step 64, WM x WN waves each owning (BM/WM) x (BN/WN) as
+// 32x32 MFMA blocks.  Global -> registers -> LDS (row stride 72 elements, so
+// the 16-byte fragment reads of 8 consecutive rows fall in distinct banks),
+// double buffered: the next K tile's global loads are in flight while the
+// current one feeds the MFMAs.  Lane l of an MFMA reads row l%32 and the 8
+// K values at (l/32)*8 of each 16-wide K step, for A (X rows) and B (W_t rows).
+template <int BM, int BN, int WM, int WN, bool kFused>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs g) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int BK = 64;
+  constexpr int LDK = BK + 8;
+  constexpr int TM = BM / (WM * 32), TN = BN / (WN * 32);
+  constexpr int A_CH = BM * BK / 8 / NT, B_CH = BN * BK / 8 / NT;
+  static_assert(A_CH * NT * 8 == BM * BK && B_CH * NT * 8 == BN * BK, "tile / thread mismatch");
+  constexpr int STAGE = (BM + BN) * LDK;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+
+  const uint16_t *X = static_cast<const uint16_t *>(g.X);
+  const uint16_t *W = static_cast<const uint16_t *>(g.W);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+  const int k_begin = blockIdx.z * g.k_split;
+  const int k_end = min(g.Kd, k_begin + g.k_split);
+  const int nk = k_end > k_begin ? (k_end - k_begin) / BK : 0;
+
+  uint4 ra[A_CH], rb[B_CH];
+  auto gload = [&](int kt) {
+    const int kb = k_begin + kt * BK;
+#pragma unroll
+    for (int c = 0; c < A_CH; ++c) {
+      const int idx = tid + c * NT;
+      const int row = idx >> 3, col = (idx & 7) * 8;
+      const int gr = m0 + row;
+      ra[c] = gr < g.M ? *reinterpret_cast<const uint4 *>(X + int64_t(gr) * g.Kd + kb + col)
+                       : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < B_CH; ++c) {
+      const int idx = tid + c * NT;
+      const int row = idx >> 3, col = (idx & 7) * 8;
+      const int gr = n0 + row;
+      rb[c] = gr < g.N ? *reinterpret_cast<const uint4 *>(W + int64_t(gr) * g.Kd + kb + col)
+                       : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto sstore = [&](int buf) {
+    uint16_t *As = smem + buf * STAGE;
+    uint16_t *Bs = As + BM * LDK;
+#pragma unroll
+    for (int c = 0; c < A_CH; ++c) {
+      const int idx = tid + c * NT;
+      *reinterpret_cast<uint4 *>(As + (idx >> 3) * LDK + (idx & 7) * 8) = ra[c];
+    }
+#pragma unroll
+    for (int c = 0; c < B_CH; ++c) {
+      const int idx = tid + c * NT;
+      *reinterpret_cast<uint4 *>(Bs + (idx >> 3) * LDK + (idx & 7) * 8) = rb[c];
+    }
+  };
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  if (nk > 0) {
+    gload(0);
+    sstore(0);
+  }
+  __syncthreads();
+  const int frag_row = lane & 31, frag_k = (lane >> 5) * 8;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+    const uint16_t *As = smem + cur * STAGE;
+    const uint16_t *Bs = As + BM * LDK;
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      bf16x8_t af[TM], bf[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t *>(
+            As + (wm * TM * 32 + i * 32 + frag_row) * LDK + s * 16 + frag_k);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bf[j] = *reinterpret_cast<const bf16x8_t *>(
+            Bs + (wn * TN * 32 + j * 32 + frag_row) * LDK + s * 16 + frag_k);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) sstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // Accumulator layout of a 32x32 block: lane l holds column l%32 and rows
+  // 8*(v/4) + 4*(l/32) + v%4 for v = 0..15.
+  if constexpr (!kFused) {
+    float *Pz = g.partial + int64_t(blockIdx.z) * g.M * g.N;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = n0 + wn * TN * 32 + j * 32 + (lane & 31);
+        if (col >= g.N) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = m0 + wm * TM * 32 + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+          if (row < g.M) Pz[int64_t(row) * g.N + col] = acc[i][j][v];
+        }
+      }
+  } else {
+    constexpr int SC = TN * 32 + 1;            // staged floats per row (padded)
+    constexpr int CPL = TN * 32 / 64;          // output columns per lane
+    static_assert(CPL == 1 || CPL == 2, "fused epilogue handles 64 or 128 columns per wave");
+    static_assert(NT / 64 * 32 * SC * 4 <= int(sizeof(smem)), "staging must fit in LDS");
+    float *stage = reinterpret_cast<float *>(smem) + wave * 32 * SC;
+    const int col = n0 + wn * TN * 32 + lane * CPL;
+    const bool col_ok = col < g.N;
+    const bool lora_on = expand_enabled(g.ex);
+    uint16_t *Y = static_cast<uint16_t *>(g.Y);
+    BCache<CPL, 16> cache;
+    cache.ad = -1;
+    for (int i = 0; i < TM; ++i) {
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+          stage[r * SC + j * 32 + (lane & 31)] = acc[i][j][v];
+        }
+      __syncthreads();
+      const int rbase = m0 + wm * TM * 32 + i * 32;
+      for (int rr = 0; rr < 32; ++rr) {
+        const int row = rbase + rr;
+        if (row >= g.M) break;
+        float v[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) v[c] = stage[rr * SC + lane * CPL + c];
+        if (lora_on) expand_row_cached<CPL, 16>(v, row, col, col_ok, g.ex, cache);
+        if (col_ok) Cols<uint16_t, CPL>::store(Y + int64_t(row) * g.N + col, v);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ fp32 GEMM
+// Plain LDS-tiled fp32 product (the fp32 layer is small): 64x64 tile, 256
+// threads each owning 4x4 outputs; writes the fp32 base product.
+__global__ __launch_bounds__(256) void gemm_f32_kernel(const float *X, const float *W, float *P,
+                                                        int M, int N, int Kd) {
+  __shared__ float As[16][64 + 4];
+  __shared__ float Bs[16][64 + 4];
+  const int tid = threadIdx.x;
+  const int tx = tid & 15, ty = tid >> 4;
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < Kd; k0 += 16) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = tid + e * 256;
+      const int rr = idx >> 4, kk = idx & 15;
+      As[kk][rr] = (m0 + rr < M) ? X[int64_t(m0 + rr) * Kd + k0 + kk] : 0.f;
+      Bs[kk][rr] = (n0 + rr < N) ? W[int64_t(n0 + rr) * Kd + k0 + kk] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { av[i] = As[kk][ty * 4 + i]; bv[i] = Bs[kk][tx * 4 + i]; }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + ty * 4 + i;
+    if (row >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + tx * 4 + j;
+      if (col < N) P[int64_t(row) * N + col] = acc[i][j];
+    }
+  }
+}
+
+// ------------------------------------------------------------ epilogue kernel
+// One wave per output row and 512-column chunk: sum the split partials in
+// order, add the expand, round once, store.  16-byte B-row loads, 1 KiB per
+// wave instruction.
+template <typename E>
+__global__ __launch_bounds__(256) void epilogue_kernel(EpilogueArgs a) {
+  constexpr int CPL = 8;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = blockIdx.y * 4 + wave;
+  if (row >= a.M) return;
+  const int col = (blockIdx.x * 64 + lane) * CPL;
+  const bool col_ok = col < a.N;
+  float v[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) v[c] = 0.f;
+  if (col_ok) {
+    for (int z = 0; z < a.splits; ++z) {
+      float pv[CPL];
+      load_f8(a.partial + (int64_t(z) * a.M + row) * a.N + col, pv);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) v[c] += pv[c];
+    }
+  }
+  if (expand_enabled(a.ex)) expand_row<E, CPL>(v, row, col, col_ok, a.ex);
+  if (col_ok) Cols<E, CPL>::store(static_cast<E *>(a.Y) + int64_t(row) * a.N + col, v);
+}
+
+template <int BM, int BN, int WM, int WN, bool kFusable>
+hipError_t launch_bf16(const GemmConfig &c, const GemmArgs &g, hipStream_t s) {
+  const dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM, c.splits);
+  const dim3 block(WM * WN * 64);
+  if constexpr (kFusable) {
+    if (c.fused) {
+      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, true>), grid, block, 0, s, g);
+      return hipGetLastError();
+    }
+  }
+  if (c.fused) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, false>), grid, block, 0, s, g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+GemmConfig choose_gemm(int T, int d_in, int d_out, int dtype) {
+  GemmConfig c{};
+  if (dtype == LORA_F32) {
+    c.kind = 0; c.bm = 64; c.bn = 64; c.splits = 1; c.k_split = d_in; c.fused = false;
+    return c;
+  }
+  if (T <= 64) { c.kind = 1; c.bm = 64; c.bn = 128; }
+  else if (T <= 256) { c.kind = 2; c.bm = 128; c.bn = 128; }
+  else { c.kind = 3; c.bm = 256; c.bn = 128; }
+  const int64_t tiles = int64_t((T + c.bm - 1) / c.bm) * ((d_out + c.bn - 1) / c.bn);
+  const int kblocks = d_in / 64;
+  if (c.kind == 3 && tiles >= 128) {
+    c.splits = 1; c.k_split = d_in; c.fused = true;
+    return c;
+  }
+  int64_t want = tiles > 0 ? (512 + tiles - 1) / tiles : 1;
+  int64_t most = kblocks / 8 > 1 ? kblocks / 8 : 1;     // every split keeps >= 512 of K
+  int splits = int(want < most ? want : most);
+  if (splits < 1) splits = 1;
+  const int kb_per = (kblocks + splits - 1) / splits;
+  c.k_split = kb_per * 64;
+  c.splits = (kblocks + kb_per - 1) / kb_per;
+  c.fused = false;
+  return c;
+}
+
+size_t gemm_partial_bytes(const GemmConfig &c, int T, int d_out) {
+  return c.fused ? 0 : size_t(c.splits) * size_t(T) * size_t(d_out) * sizeof(float);
+}
+
+hipError_t launch_base_gemm(const GemmConfig &c, const GemmArgs &g, hipStream_t s) {
+  if (c.kind == 0) {
+    const dim3 grid((g.N + 63) / 64, (g.M + 63) / 64);
+    hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, s, static_cast<const float *>(g.X),
+                       static_cast<const float *>(g.W), g.partial, g.M, g.N, g.Kd);
+    return hipGetLastError();
+  }
+  if (c.kind == 1) return launch_bf16<64, 128, 1, 4, false>(c, g, s);
+  if (c.kind == 2) return launch_bf16<128, 128, 2, 2, false>(c, g, s);
+  return launch_bf16<256, 128, 2, 2, true>(c, g, s);
+}
+
+hipError_t launch_epilogue(const GemmConfig &c, const GemmArgs &g, int dtype, hipStream_t s) {
+  if (c.fused) return hipSuccess;
+  EpilogueArgs e{g.partial, c.splits, g.M, g.N, g.Y, g.ex};
+  const dim3 grid((g.N + 511) / 512, (g.M + 3) / 4);
+  if (dtype == LORA_BF16) hipLaunchKernelGGL(epilogue_kernel<uint16_t>, grid, dim3(256), 0, s, e);
+  else hipLaunchKernelGGL(epilogue_kernel<float>, grid, dim3(256), 0, s, e);
+  return hipGetLastError();
+}
+
+}  // namespace lora

@@ -1,0 +1,229 @@
+// Internal definitions shared by the HIP sources of liblora (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lora.h"
+
+namespace lora {
+
+// ----------------------------------------------------------------- limits
+constexpr int64_t kMaxPairs = int64_t(1) << 20;  // T*K: keeps prefix sums of ranks in int32
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanLdsMaxAdapters = 4096;         // per-adapter counters held in LDS up to here
+constexpr int kGradPairChunk = 256;               // pairs per partial in the gradient reduction
+constexpr int kGradRankChunk = 16;                // rank rows per gradient register block
+
+// ----------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf2f(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
+
+// float32 -> bf16, round to nearest even; NaN stays NaN (quiet bit set).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// Element traits: storage type E is float (fp32) or uint16_t (bf16 bits).
+template <typename E> struct Elem;
+template <> struct Elem<float> {
+  // 8 consecutive elements starting at p (32-byte aligned).
+  static __device__ __forceinline__ void load8(const float *p, float v[8]) {
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  static __device__ __forceinline__ float load1(const float *p) { return *p; }
+  static __device__ __forceinline__ void store1(float *p, float v) { *p = v; }
+  static __device__ __forceinline__ float to_f(float v) { return v; }
+  static __device__ __forceinline__ float from_f(float v) { return v; }
+};
+template <> struct Elem<uint16_t> {
+  static __device__ __forceinline__ void load8(const uint16_t *p, float v[8]) {
+    const uint4 a = *reinterpret_cast<const uint4 *>(p);
+    v[0] = bf_lo(a.x); v[1] = bf_hi(a.x); v[2] = bf_lo(a.y); v[3] = bf_hi(a.y);
+    v[4] = bf_lo(a.z); v[5] = bf_hi(a.z); v[6] = bf_lo(a.w); v[7] = bf_hi(a.w);
+  }
+  static __device__ __forceinline__ float load1(const uint16_t *p) { return bf2f(*p); }
+  static __device__ __forceinline__ void store1(uint16_t *p, float v) { *p = f2bf(v); }
+  static __device__ __forceinline__ float to_f(uint16_t v) { return bf2f(v); }
+  static __device__ __forceinline__ uint16_t from_f(float v) { return f2bf(v); }
+};
+
+// ----------------------------------------------------------------- wave helpers
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Sum over the 64 lanes of a wave with a fixed butterfly (deterministic).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ----------------------------------------------------------------- plan layout
+// Offsets in int32 units inside the plan buffer; every array 64-byte aligned.
+struct PlanLayout {
+  int64_t hdr, pair_tk, seg_adapter, seg_off, seg_row_off, bucket_seg_off, u_off, slot_pos;
+  int64_t pair_adapter;
+  int64_t cnt, start, ustart, cur;  // per-adapter scratch
+  int64_t total;
+};
+
+__host__ __device__ inline int64_t align16(int64_t x) { return (x + 15) & ~int64_t(15); }
+
+__host__ __device__ inline PlanLayout plan_layout(int64_t TK, int64_t N) {
+  PlanLayout L;
+  int64_t o = 0;
+  L.hdr = o;            o = align16(o + LORA_PLAN_HEADER_INTS);
+  L.pair_tk = o;        o = align16(o + TK);
+  L.seg_adapter = o;    o = align16(o + TK);
+  L.seg_off = o;        o = align16(o + TK + 1);
+  L.seg_row_off = o;    o = align16(o + TK + 1);
+  L.bucket_seg_off = o; o = align16(o + 16);
+  L.u_off = o;          o = align16(o + TK + 1);
+  L.slot_pos = o;       o = align16(o + TK);
+  L.pair_adapter = o;   o = align16(o + TK);
+  L.cnt = o;            o = align16(o + N);
+  L.start = o;          o = align16(o + N);
+  L.ustart = o;         o = align16(o + N);
+  L.cur = o;            o = align16(o + N);
+  L.total = o;
+  return L;
+}
+
+// Read-only view of a built plan.
+struct PlanView {
+  const int32_t *hdr, *pair_tk, *seg_adapter, *seg_off, *seg_row_off, *u_off, *slot_pos;
+  const int32_t *pair_adapter;
+};
+
+inline PlanView plan_view(const void *plan, int64_t TK, int64_t N) {
+  const PlanLayout L = plan_layout(TK, N);
+  const int32_t *b = static_cast<const int32_t *>(plan);
+  return PlanView{b + L.hdr, b + L.pair_tk, b + L.seg_adapter, b + L.seg_off,
+                  b + L.seg_row_off, b + L.u_off, b + L.slot_pos, b + L.pair_adapter};
+}
+
+// Device view of an adapter pool.
+struct PoolView {
+  const void *a_pages, *b_pages;
+  const int32_t *rank, *page_start, *page_ids;
+  const float *scale;
+  int64_t n_pages, n_page_ids;
+  int d_in, d_out, n_adapters;
+};
+
+inline PoolView pool_view(const lora_pool_desc *p) {
+  return PoolView{p->a_pages, p->b_pages, p->rank, p->page_start, p->page_ids, p->scale,
+                  p->n_pages, p->n_page_ids, p->d_in, p->d_out, p->n_adapters};
+}
+
+// ----------------------------------------------------------------- kernel arguments
+
+// Segmented shrink: out[u_off[p] + j] = coef_p * sum_i Z[t_p][i] (m[t_p][i]) page_j[i]
+// for every planned pair p and rank row j of its adapter, with coef_p =
+// gates[t_p][k_p] * scale[a] * extra_scale.  Used for the LoRA down projection
+// (Z = X, pages = A) and for the gradient's dY.B^T (Z = dY, pages = B).
+struct ShrinkArgs {
+  const void *Z;            // [T][d] activations
+  const uint8_t *mask;      // [T][d] 0/1 or null
+  float extra_scale;
+  int T, K, d;
+  const void *pages;        // [n_pages][d]
+  const int32_t *rank, *page_start, *page_ids;
+  const float *scale;
+  const float *gates;       // [T][K]
+  PlanView plan;
+  int32_t *err_word;        // plan header word for device errors
+  float *out;
+  int64_t out_cap;          // capacity of out in floats
+};
+
+// Everything the expand needs to add sum_j U[u_off[p]+j] * B_a[j][n] to row t.
+struct ExpandArgs {
+  int K;
+  const int32_t *slot_pos, *u_off, *pair_adapter;
+  const int32_t *rank, *page_start, *page_ids;
+  const void *b_pages;      // [n_pages][d_out]
+  int d_out;
+  const float *U;
+  const int32_t *hdr;       // plan header (R_pairs)
+  int64_t u_cap;
+};
+
+struct GemmArgs {
+  const void *X;            // [M][Kd]
+  const void *W;            // [N][Kd]
+  int M, N, Kd;
+  int k_split;              // K elements per split (multiple of 64)
+  float *partial;           // [splits][M][N]
+  void *Y;                  // fused epilogue output [M][N]
+  ExpandArgs ex;
+};
+
+struct EpilogueArgs {
+  const float *partial;     // [splits][M][N]
+  int splits, M, N;
+  void *Y;
+  ExpandArgs ex;
+};
+
+struct MergeArgs {
+  void *W;                  // [d_out][d_in]
+  int d_in, d_out;
+  const void *a_pages, *b_pages;
+  const int32_t *rank, *page_start, *page_ids;
+  const float *scale;
+  int64_t n_pages, n_page_ids;
+  int n_adapters;
+  const int32_t *ids;
+  const float *coeffs;
+  int m;
+};
+
+// Gradient outer-product reduction over the pairs of each segment:
+// out_page(a, j)[c] = sum_{p of a} coef[u_off[p] + j] * Z[t_p][c] (* m[t_p][c]).
+struct SegOuterArgs {
+  const void *Z;            // [T][d]
+  const uint8_t *mask;      // [T][d] or null
+  int T, K, d;
+  const float *coef;        // packed like U
+  int64_t coef_cap;         // floats available at coef
+  PlanView plan;
+  const int32_t *rank, *page_start, *page_ids;
+  float *part;              // [pieces][max_rank][d]
+  int max_rank;
+  float *out_pages;         // [n_pages][d]
+  int32_t *err_word;
+};
+
+// ----------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.
+hipError_t launch_plan(const int32_t *ids, const float *gates, int T, int K, const PoolView &pool,
+                       int32_t *plan, hipStream_t s);
+hipError_t launch_shrink(const ShrinkArgs &a, int dtype, int64_t rows_bound, hipStream_t s);
+
+// Base GEMM configuration chosen from the shape (host-side, deterministic).
+struct GemmConfig {
+  int kind;      // 0: fp32 tiles; 1: bf16 64x128; 2: bf16 128x128; 3: bf16 256x128
+  int bm, bn;
+  int splits;
+  int k_split;
+  bool fused;    // expand + rounding in the GEMM epilogue (splits == 1 only)
+};
+GemmConfig choose_gemm(int T, int d_in, int d_out, int dtype);
+size_t gemm_partial_bytes(const GemmConfig &c, int T, int d_out);
+hipError_t launch_base_gemm(const GemmConfig &c, const GemmArgs &g, hipStream_t s);
+hipError_t launch_epilogue(const GemmConfig &c, const GemmArgs &g, int dtype, hipStream_t s);
+
+hipError_t launch_merge(const MergeArgs &a, int dtype, hipStream_t s);
+int64_t grad_pieces(int64_t TK, int64_t n_adapters);
+hipError_t launch_seg_outer(const SegOuterArgs &a, int dtype, int64_t TK, int64_t n_adapters,
+                            hipStream_t s);
+
+}  // namespace lora

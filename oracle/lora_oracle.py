@@ -145,6 +145,7 @@ def plan(ids, gates, rank, page_start, page_ids, n_pages) -> dict:
     u_off = [0]
     for (_, a, _, _) in pairs:
         u_off.append(u_off[-1] + int(rank[a]))
+    pair_adapter = [a for (_, a, _, _) in pairs]
     slot_pos = [-1] * (T * K)
     for p, tk in enumerate(pair_tk):
         slot_pos[tk] = p
@@ -155,7 +156,8 @@ def plan(ids, gates, rank, page_start, page_ids, n_pages) -> dict:
     i32 = lambda v: np.asarray(v, dtype=np.int32)
     return {"header": i32(header), "pair_tk": i32(pair_tk), "seg_adapter": i32(seg_adapter),
             "seg_off": i32(seg_off), "seg_row_off": i32(seg_row_off),
-            "bucket_seg_off": i32(bucket_seg_off), "u_off": i32(u_off), "slot_pos": i32(slot_pos)}
+            "bucket_seg_off": i32(bucket_seg_off), "u_off": i32(u_off), "slot_pos": i32(slot_pos),
+            "pair_adapter": i32(pair_adapter)}
 
 
 def factors(a, rank, page_start, page_ids, a_pages, b_pages):

@@ -1,0 +1,351 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle on
+the same seeded inputs.
+
+Bars: the plan is integer and compared bit for bit; floating outputs satisfy
+max|gpu - oracle| / max|oracle| <= 1e-5 (fp32 inputs) or 1e-2 (bf16 inputs,
+fp32 accumulation).  Bit-identities the method fixes are checked on the GPU
+alone: rows whose slots are all inactive equal a base-only run bit for bit,
+moving adapters to other pages changes nothing, and repeated runs agree.
+"""
+import functools
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from lora_adapter_amd import binding as B
+from lora_adapter_amd import device as D
+from lora_adapter_amd import workloads as wl
+from oracle import lora_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 1e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()   # fails loudly if the HIP library is missing
+
+
+@functools.lru_cache(None)
+def small(i):
+    return wl.small(i)
+
+
+@functools.lru_cache(None)
+def full(i):
+    return wl.config(i)
+
+
+def rel_err(gpu, ref):
+    return float(np.max(np.abs(gpu - ref)) / max(np.max(np.abs(ref)), 1e-300))
+
+
+def run(w, **kw):
+    L = D.DeviceLayer(w, **kw)
+    L.run_plan()
+    L.run_apply()
+    torch.cuda.synchronize()
+    return L
+
+
+def assert_plan_equal(gpu, ref):
+    np.testing.assert_array_equal(gpu["header"][:8], ref["header"][:8])
+    for k in ("pair_tk", "seg_adapter", "seg_off", "seg_row_off", "bucket_seg_off", "u_off", "slot_pos",
+              "pair_adapter"):
+        np.testing.assert_array_equal(gpu[k], ref[k], err_msg=k)
+
+
+# ---------------------------------------------------------------- plan
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_plan_small(cfg):
+    w = small(cfg)
+    L = D.DeviceLayer(w)
+    L.run_plan()
+    torch.cuda.synchronize()
+    assert_plan_equal(L.read_plan(), O.plan_workload(w))
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_plan_full(cfg):
+    w = full(cfg)
+    L = D.DeviceLayer(w)
+    L.run_plan()
+    torch.cuda.synchronize()
+    assert_plan_equal(L.read_plan(), O.plan_workload(w))
+
+
+def _tiny_pool_workload(N, T, K, rank, ids, gates, d=64, seed=0):
+    return wl.build("tiny", seed, "bf16", T, K, d, d, np.asarray(rank, np.int32), ids, gates,
+                    x_var=1.0, w_var=0.02, a_var=1 / 64, b_var=0.02)
+
+
+def test_plan_errors_match_oracle():
+    rank = np.array([2, 0, 3, 2000, 1], np.int32)
+    ids = np.array([[0], [1], [2], [3], [4], [-1], [-2], [5]], np.int32)
+    gates = np.ones((8, 1), np.float32)
+    w = _tiny_pool_workload(5, 8, 1, [2, 0, 3, 0, 1], ids, gates)
+    w.rank = rank                                   # adapter 3 claims rank 2000
+    w.page_ids = w.page_ids.copy()
+    w.page_ids[-1] = 10 ** 6                       # adapter 4's page out of range
+    L = D.DeviceLayer(w, max_rank=4)
+    L.run_plan()
+    torch.cuda.synchronize()
+    ref = O.plan(w.ids, w.gates, w.rank, w.page_start, w.page_ids, w.n_pages)
+    got = L.read_plan()
+    assert got["header"][B.PH_ERR] == B.DEVERR_BAD_ID | B.DEVERR_BAD_RANK | B.DEVERR_BAD_POOL
+    assert_plan_equal(got, ref)
+
+
+def test_plan_large_pool_uses_global_counters():
+    rng = np.random.default_rng(11)
+    N, T, K = 10000, 3000, 2                       # N above the LDS counter limit
+    rank = rng.integers(0, 5, size=N).astype(np.int32)
+    ids = rng.integers(-1, N, size=(T, K)).astype(np.int32)
+    gates = rng.choice(np.array([0.0, 1.0, -0.5], np.float32), size=(T, K))
+    w = _tiny_pool_workload(N, T, K, rank, ids, gates)
+    L = D.DeviceLayer(w)
+    L.run_plan()
+    torch.cuda.synchronize()
+    assert_plan_equal(L.read_plan(), O.plan_workload(w))
+
+
+def test_plan_empty_batch():
+    w = _tiny_pool_workload(3, 0, 2, [1, 2, 3], np.zeros((0, 2), np.int32), np.zeros((0, 2), np.float32))
+    L = D.DeviceLayer(w)
+    L.run_plan()
+    L.run_apply()
+    torch.cuda.synchronize()
+    got = L.read_plan()
+    assert got["header"][B.PH_PAIRS] == 0 and got["header"][B.PH_SEGS] == 0
+    assert got["bucket_seg_off"].tolist() == [0] * 10
+
+
+# ---------------------------------------------------------------- apply
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_apply_small(cfg):
+    w = small(cfg)
+    L = run(w)
+    assert L.read_plan()["header"][B.PH_ERR] == 0
+    err = rel_err(D.as_f64(L.Y_host()), O.apply_workload(w))
+    assert err <= TOL[w.dtype], err
+
+
+def test_apply_fused_epilogue_path():
+    # enough output tiles that the expand runs inside the GEMM epilogue
+    w = wl.config(4, T=2100, d_in=512, d_out=8192, seed=77)
+    L = run(w)
+    err = rel_err(D.as_f64(L.Y_host()), O.apply_workload(w))
+    assert err <= TOL["bf16"], err
+
+
+def test_apply_mixed_ranks_above_bucket_edges():
+    rng = np.random.default_rng(5)
+    N, T, K = 9, 130, 2
+    rank = np.array([1, 2, 3, 7, 16, 17, 64, 129, 200], np.int32)
+    ids = rng.integers(-1, N, size=(T, K)).astype(np.int32)
+    gates = rng.standard_normal((T, K)).astype(np.float32)
+    gates[rng.random((T, K)) < 0.1] = 0
+    w = wl.build("mixed", 9, "bf16", T, K, 256, 384, rank, ids, gates,
+                 x_var=1.0, w_var=0.02, a_var=1 / 64, b_var=0.02,
+                 scale=rng.uniform(0.5, 2, N).astype(np.float32))
+    L = run(w)
+    assert_plan_equal(L.read_plan(), O.plan_workload(w))
+    err = rel_err(D.as_f64(L.Y_host()), O.apply_workload(w))
+    assert err <= TOL["bf16"], err
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 5])
+def test_apply_full(cfg):
+    w = full(cfg)
+    L = run(w)
+    assert L.read_plan()["header"][B.PH_ERR] == 0
+    err = rel_err(D.as_f64(L.Y_host()), O.apply_workload(w))
+    assert err <= TOL[w.dtype], err
+
+
+def test_apply_full_prefill_sampled_rows():
+    w = full(4)
+    L = run(w)
+    lens = np.cumsum(w.meta["segment_lengths"])
+    rng = np.random.default_rng(0)
+    rows = sorted(set(rng.choice(w.T, 48, replace=False).tolist()
+                      + [0, w.T - 1] + [int(x) for x in lens[:-1]] + [int(x) - 1 for x in lens[:-1]]))
+    ref = O.apply_workload(w, rows=rows)
+    got = D.as_f64(L.Y_host())[rows]
+    err = rel_err(got, ref)
+    assert err <= TOL["bf16"], err
+
+
+# ---------------------------------------------------------------- invariants
+
+def _base_only(L):
+    ids_saved = L.ids.clone()
+    L.ids.fill_(-1)
+    Yb = torch.empty_like(L.Y)
+    L.run_plan()
+    L.run_apply(Y=Yb)
+    torch.cuda.synchronize()
+    L.ids.copy_(ids_saved)
+    L.run_plan()
+    torch.cuda.synchronize()
+    return D.to_host(Yb)
+
+
+@pytest.mark.parametrize("cfg", [1, 3, 5])
+def test_inactive_rows_equal_base_only_bit_for_bit(cfg):
+    w = small(cfg)
+    w2 = wl.config(cfg, T=w.T, d_in=w.d_in, d_out=w.d_out, n_adapters=w.n_adapters if cfg != 1 else None,
+                   seed=w.meta["seed"])
+    w2.gates = w2.gates.copy(); w2.ids = w2.ids.copy()
+    w2.gates[::3] = 0.0
+    w2.ids[1::5] = -1
+    L = run(w2)
+    Y = L.Y_host()
+    Yb = _base_only(L)
+    inactive = [t for t in range(w2.T)
+                if all(w2.ids[t, k] < 0 or w2.gates[t, k] == 0 or w2.rank[w2.ids[t, k]] == 0
+                       for k in range(w2.K))]
+    assert len(inactive) > 0
+    assert np.array_equal(Y[inactive], Yb[inactive])
+    active = [t for t in range(w2.T) if t not in inactive]
+    assert not np.array_equal(Y[active], Yb[active])
+
+
+def test_moving_pages_changes_nothing():
+    w = small(3)
+    L1 = run(w)
+    # same factors at other pages: permute the pool's rows and remap page ids
+    rng = np.random.default_rng(4)
+    perm = rng.permutation(w.n_pages)
+    inv = np.argsort(perm)
+    w2 = wl.Workload(**{**w.__dict__})
+    w2.a_pages = w.a_pages[perm]
+    w2.b_pages = w.b_pages[perm]
+    w2.page_ids = inv[w.page_ids].astype(np.int32)
+    L2 = run(w2)
+    assert np.array_equal(L1.Y_host(), L2.Y_host())
+
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_repeated_runs_are_bitwise_identical(cfg):
+    w = small(cfg)
+    L = run(w)
+    Y1 = L.Y_host().copy()
+    for _ in range(3):
+        L.run_plan()
+        L.run_apply()
+    torch.cuda.synchronize()
+    assert np.array_equal(Y1, L.Y_host())
+
+
+def test_u_capacity_error_skips_lora_and_flags():
+    w = small(2)
+    L = D.DeviceLayer(w, max_rank=1)          # U room for one rank row per slot only
+    L.run_plan()
+    L.run_apply()
+    torch.cuda.synchronize()
+    h = L.read_plan()["header"]
+    assert h[B.PH_ERR] & B.DEVERR_CAPACITY
+    base = D.as_f64(L.Y_host())
+    ref = D.as_f64(w.X) @ D.as_f64(w.W_t).T
+    assert rel_err(base, ref) <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------- merge
+
+def _ulp_bf16(x):
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+@pytest.mark.parametrize("which", ["small1", "small5", "full5"])
+def test_merge_unmerge_and_switch(which):
+    w = {"small1": lambda: small(1), "small5": lambda: small(5), "full5": lambda: full(5)}[which]()
+    ids = w.merge_ids if w.merge_ids is not None else np.arange(min(4, w.n_adapters), dtype=np.int32)
+    co = np.ones(len(ids), np.float32)
+    L = D.DeviceLayer(w)
+    W = L.W_t.clone()
+    L.run_merge(W, ids, co)
+    torch.cuda.synchronize()
+    Wm = D.to_host(W)
+    ref = O.merge_workload(w, ids=ids, coeffs=co)
+    assert rel_err(D.as_f64(Wm), ref) <= TOL[w.dtype]
+    # unmerge restores W to within one rounding of each step
+    L.run_merge(W, ids, -co)
+    torch.cuda.synchronize()
+    W0, W2 = D.as_f64(w.W_t), D.as_f64(D.to_host(W))
+    if w.dtype == "bf16":
+        bound = _ulp_bf16(np.maximum(np.abs(W0), np.abs(D.as_f64(Wm)))) * 1.01
+    else:
+        bound = np.spacing(np.maximum(np.abs(W0), np.abs(D.as_f64(Wm))).astype(np.float32)).astype(np.float64) * 2.02
+    assert np.all(np.abs(W2 - W0) <= bound + 1e-30)
+    # fused switch from the merged state: -old, +new in one call
+    new = np.array([(int(i) + 1) % w.n_adapters for i in ids[:2]], np.int32)
+    sw_ids = np.concatenate([ids, new]).astype(np.int32)
+    sw_co = np.concatenate([-co, np.ones(2, np.float32)])
+    W3 = torch.from_numpy(np.ascontiguousarray(Wm).view(np.int16) if Wm.dtype == np.uint16 else Wm)
+    W3 = W3.to("cuda")
+    if Wm.dtype == np.uint16:
+        W3 = W3.view(torch.bfloat16)
+    L.run_merge(W3, sw_ids, sw_co)
+    torch.cuda.synchronize()
+    ref3 = O.merge_workload(w, W_t=Wm, ids=sw_ids, coeffs=sw_co)
+    assert rel_err(D.as_f64(D.to_host(W3)), ref3) <= TOL[w.dtype]
+
+
+def test_merged_weight_base_matches_apply():
+    w = small(2)
+    a = int(w.ids[0, 0])
+    g = np.float32(0.75)
+    w1 = wl.Workload(**{**w.__dict__})
+    w1.ids = np.full((w.T, 1), a, np.int32)
+    w1.gates = np.full((w.T, 1), g, np.float32)
+    L = run(w1)
+    Y_apply = D.as_f64(L.Y_host())
+    W = L.W_t.clone()
+    L.run_merge(W, [a], [g])
+    Yb = torch.empty_like(L.Y)
+    L.ids.fill_(-1)
+    L.run_plan()
+    L.run_apply(Y=Yb, W_t=W)
+    torch.cuda.synchronize()
+    assert rel_err(D.as_f64(D.to_host(Yb)), Y_apply) <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------- grads
+
+def _check_grads(w, L):
+    dA, dB, gws = L.grad_buffers()
+    L.run_grad(dA, dB, gws)
+    torch.cuda.synchronize()
+    g = O.grad_workload(w)
+    rA, rB = O.grad_pages(g, w.rank, w.page_start, w.page_ids, w.n_pages, w.d_in, w.d_out)
+    gA, gB = dA.cpu().numpy().astype(np.float64), dB.cpu().numpy().astype(np.float64)
+    used = ~np.isnan(rA[:, 0])
+    assert np.all(np.isnan(gA[~used])) and np.all(np.isnan(gB[~used]))   # other pages untouched
+    assert rel_err(gA[used], rA[used]) <= TOL[w.dtype]
+    assert rel_err(gB[used], rB[used]) <= TOL[w.dtype]
+
+
+def test_grads_small():
+    w = small(4)
+    _check_grads(w, run(w))
+
+
+def test_grads_multi_adapter_top2():
+    w = small(5)
+    w = wl.Workload(**{**w.__dict__})
+    w.dY = wl._normal(np.random.default_rng(3), (w.T, w.d_out), 1.0, "bf16")
+    _check_grads(w, run(w))
+
+
+def test_grads_full_prefill():
+    w = full(4)
+    _check_grads(w, run(w))

@@ -54,7 +54,8 @@ def test_golden_plan():
     p = O.plan(a["ids"], a["gates"], a["rank"], a["page_start"], a["page_ids"], a["a_pages"].shape[0])
     exp = g["expected_plan"]
     np.testing.assert_array_equal(p["header"][:8], exp["header"])
-    for k in ("pair_tk", "seg_adapter", "seg_off", "seg_row_off", "bucket_seg_off", "u_off", "slot_pos"):
+    for k in ("pair_tk", "seg_adapter", "seg_off", "seg_row_off", "bucket_seg_off", "u_off", "slot_pos",
+              "pair_adapter"):
         np.testing.assert_array_equal(p[k], exp[k], err_msg=k)
 
 

@@ -54,12 +54,13 @@ def _lexsort_plan(ids, gates, rank, page_start, page_ids, n_pages):
         err |= O.ERR_BAD_RANK
     if bad:
         err |= O.ERR_BAD_POOL
-    return dict(pair_tk=pair_tk, seg_adapter=seg_adapter, seg_off=seg_off, seg_row_off=seg_row_off,
+    return dict(pair_tk=pair_tk, pair_adapter=sa, seg_adapter=seg_adapter, seg_off=seg_off, seg_row_off=seg_row_off,
                 bucket_seg_off=np.asarray(bso), u_off=u_off, slot_pos=slot_pos, err=err)
 
 
 def _check_same(p, q):
-    for k in ("pair_tk", "seg_adapter", "seg_off", "seg_row_off", "bucket_seg_off", "u_off", "slot_pos"):
+    for k in ("pair_tk", "pair_adapter", "seg_adapter", "seg_off", "seg_row_off", "bucket_seg_off",
+              "u_off", "slot_pos"):
         np.testing.assert_array_equal(p[k], np.asarray(q[k], dtype=np.int64), err_msg=k)
     assert p["header"][O.H_ERR] == q["err"]
 
