@@ -148,34 +148,42 @@ def main():
     # ---------------------------------------------------------------- per-kernel events
     big = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
 
+    stages = {
+        "plan": lambda c, u: B.lora_plan(u, gates, T, K, c.pool, c.plan),
+        "shrink": lambda c, u: B.lora_shrink(c.X, mask, L.keep_scale, T, K, gates, c.pool, c.plan, c.ws),
+        "gemm": lambda c, u: B.lora_base_gemm(c.X, c.W_t, c.Y, T, K, c.pool, c.plan, c.ws),
+        "epilogue": lambda c, u: B.lora_expand_epilogue(c.X, c.W_t, c.Y, T, K, c.pool, c.plan, c.ws),
+    }
+
     def stage_times(use_ids, n):
-        names = ("plan", "shrink", "gemm", "epilogue")
-        acc = {k: [] for k in names}
-        done = 0
-        while done < n:
-            chunk = min(25, n - done)
-            for _ in range(3):             # busy prefix: the stages below queue behind it
-                torch.mm(big, big)
-            evs = []
-            for i in range(chunk):
-                c = copies[(done + i) % R]
-                e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-                e[0].record(stream)
-                B.lora_plan(use_ids, gates, T, K, c.pool, c.plan)
-                e[1].record(stream)
-                B.lora_shrink(c.X, mask, L.keep_scale, T, K, gates, c.pool, c.plan, c.ws)
-                e[2].record(stream)
-                B.lora_base_gemm(c.X, c.W_t, c.Y, T, K, c.pool, c.plan, c.ws)
-                e[3].record(stream)
-                B.lora_expand_epilogue(c.X, c.W_t, c.Y, T, K, c.pool, c.plan, c.ws)
-                e[4].record(stream)
-                evs.append(e)
-            torch.cuda.synchronize()
-            for e in evs:
-                for j, k in enumerate(names):
-                    acc[k].append(e[j].elapsed_time(e[j + 1]) * 1e3)   # us
-            done += chunk
-        return {k: float(np.median(v)) for k, v in acc.items()}, {k: float(np.mean(v)) for k, v in acc.items()}
+        """Per stage: blocks of `reps` back-to-back launches on the rotating
+        copies, bracketed by two HIP events on the launch stream and queued
+        behind a busy prefix so the events time the kernels, not the host."""
+        for c in copies:
+            step(c, use_ids)              # every copy holds a valid plan and U
+        torch.cuda.synchronize()
+        reps = min(R, 32) if R >= 8 else 16
+        rounds = max(3, n // reps)
+        out = {}
+        for name, fn in stages.items():
+            ts = []
+            for rd in range(rounds):
+                for _ in range(2):
+                    torch.mm(big, big)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for i in range(reps):
+                    fn(copies[(rd * reps + i) % R], use_ids)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3 / reps)
+            out[name] = ts
+        for c in copies:
+            step(c, use_ids)
+        torch.cuda.synchronize()
+        return ({k: float(np.median(v)) for k, v in out.items()},
+                {k: float(np.mean(v)) for k, v in out.items()})
 
     st_med, st_mean = stage_times(ids, args.event_steps)
     sb_med, sb_mean = stage_times(empty_ids, args.event_steps)
@@ -188,7 +196,7 @@ def main():
     x_bytes = T * w.d_in * e
     y_bytes = T * w.d_out * e
     gemm_alg_bytes = w_bytes + x_bytes
-    t_gemm = st_mean["gemm"] * 1e-6
+    t_gemm = st_med["gemm"] * 1e-6
     gemm_gbs = gemm_alg_bytes / t_gemm / 1e9
     t_step = elapsed / args.steps
     t_base_step = elapsed_base / args.steps
@@ -220,7 +228,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "base GEMM (gemm_bf16_kernel)",
                      "achieved": gemm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gemm_gbs / HBM_PEAK_GBS, "traffic": None,
-                     "alg_bytes_per_launch": gemm_alg_bytes, "avg_launch_us": st_mean["gemm"]},
+                     "alg_bytes_per_launch": gemm_alg_bytes, "avg_launch_us": st_med["gemm"]},
         "stages_us_median": st_med,
         "stages_us_mean": st_mean,
         "stages_us_mean_empty_plan": sb_mean,

@@ -146,8 +146,12 @@ int32_t lora_shrink(const void *X, const uint8_t *keep_mask, float keep_scale, i
   a.err_word = const_cast<int32_t *>(pv.hdr) + LORA_PH_ERR;
   a.out = w.U;
   a.out_cap = w.u_cap;
-  const int64_t bound = w.u_cap < TK * LORA_MAX_RANK ? w.u_cap : TK * LORA_MAX_RANK;
-  return dev(launch_shrink(a, pool->dtype, bound, static_cast<hipStream_t>(stream)));
+  // grid hint: the workspace was sized for ranks up to u_cap / (T*K); the
+  // kernel strides over rank rows, so a smaller hint stays correct
+  const int64_t hint = w.u_cap / (TK > 0 ? TK : 1);
+  const int max_rank = int(hint < LORA_MAX_RANK ? (hint > 0 ? hint : 1) : LORA_MAX_RANK);
+  return dev(launch_shrink(a, pool->dtype, TK, pool->n_adapters, max_rank,
+                           static_cast<hipStream_t>(stream)));
 }
 
 namespace {
@@ -174,8 +178,7 @@ int32_t base_args(const void *X, const void *W_t, void *Y, int32_t T, int32_t K,
   g.partial = w.partial;
   g.Y = Y;
   g.ex.K = K;
-  g.ex.slot_pos = pv.slot_pos; g.ex.u_off = pv.u_off; g.ex.pair_adapter = pv.pair_adapter;
-  g.ex.rank = pool->rank; g.ex.page_start = pool->page_start; g.ex.page_ids = pool->page_ids;
+  g.ex.slot_desc = pv.slot_desc; g.ex.page_ids = pool->page_ids;
   g.ex.b_pages = pool->b_pages; g.ex.d_out = pool->d_out;
   g.ex.U = w.U; g.ex.hdr = pv.hdr; g.ex.u_cap = w.u_cap;
   return LORA_OK;
@@ -293,7 +296,7 @@ int32_t lora_grad(const void *X, const uint8_t *keep_mask, float keep_scale, con
   sa.rank = pool->rank; sa.page_start = pool->page_start; sa.page_ids = pool->page_ids;
   sa.scale = pool->scale; sa.gates = gates; sa.plan = pv; sa.err_word = err_word;
   sa.out = G; sa.out_cap = int64_t(TK) * max_rank;
-  hipError_t e = launch_shrink(sa, pool->dtype, sa.out_cap, s);
+  hipError_t e = launch_shrink(sa, pool->dtype, TK, pool->n_adapters, max_rank, s);
   if (e != hipSuccess) return LORA_ERR_DEVICE;
 
   SegOuterArgs ob{};

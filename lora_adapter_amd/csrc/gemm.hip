@@ -68,80 +68,92 @@ __device__ __forceinline__ void load_f8(const float *p, float v[8]) { Elem<float
 // ------------------------------------------------------------ expand of one row
 // v[c] += sum over the row's active slots k (in slot order) and rank rows j
 // (ascending) of U[u_off[p] + j] * B_a[j][col + c].  Wave-uniform control flow:
-// every lane handles the same row; lanes own consecutive columns.
-template <typename E, int CPL>
-__device__ __forceinline__ void expand_row(float (&v)[CPL], int t, int col, bool col_ok,
-                                           const ExpandArgs &e) {
+// every lane handles the same row; lanes own consecutive columns.  `col` must
+// be a valid column (callers clamp it and mask their store), so the B loads
+// are unconditional and eight of them are in flight at a time.
+// 8 consecutive elements held raw until used, so a batch of loads is in
+// flight before the first conversion waits.
+template <typename E> struct Raw8;
+template <> struct Raw8<uint16_t> {
+  uint4 v;
+  __device__ __forceinline__ void load(const uint16_t *p) { v = *reinterpret_cast<const uint4 *>(p); }
+  __device__ __forceinline__ void to8(float o[8]) const { Elem<uint16_t>::load8(reinterpret_cast<const uint16_t *>(&v), o); }
+};
+template <> struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float *p) {
+    a = *reinterpret_cast<const float4 *>(p);
+    b = *reinterpret_cast<const float4 *>(p + 4);
+  }
+  __device__ __forceinline__ void to8(float o[8]) const {
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+  }
+};
+
+// One row, 8 columns per lane.  Control data is gathered lane-parallel and
+// broadcast: round trip 1 the row's slot descriptors ({pair, rank, u_off,
+// page_start}, lane k = slot k), round trip 2 page ids and U values of 16
+// rank rows (lane j = row j), round trip 3 sixteen B-row loads in flight.
+template <typename E>
+__device__ __forceinline__ void expand_row8(float (&v)[8], int t, int col, const ExpandArgs &e) {
   const E *B = static_cast<const E *>(e.b_pages);
+  const int lane = lane_id();
+  int4 sd = make_int4(-1, 0, 0, 0);
+  if (lane < e.K) sd = e.slot_desc[t * e.K + lane];
   for (int k = 0; k < e.K; ++k) {
-    const int p = e.slot_pos[t * e.K + k];
-    if (p < 0) continue;
-    const int ad = e.pair_adapter[p];
-    const int r = e.rank[ad];
-    const float *u = e.U + e.u_off[p];
-    const int32_t *pid = e.page_ids + e.page_start[ad];
-    int j = 0;
-    for (; j + 4 <= r; j += 4) {
-      float bv[4][CPL];
+    if (__shfl(sd.x, k, 64) < 0) continue;
+    const int r = __shfl(sd.y, k, 64), uo = __shfl(sd.z, k, 64), ps = __shfl(sd.w, k, 64);
+    for (int j0 = 0; j0 < r; j0 += 16) {
+      int pid = 0;
+      float uv = 0.f;
+      if (lane < 16) {
+        const int j = j0 + min(lane, r - j0 - 1);
+        pid = e.page_ids[ps + j];
+        uv = e.U[uo + j];
+      }
+      Raw8<E> bv[16];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (col_ok) Cols<E, CPL>::load(B + int64_t(pid[j + q]) * e.d_out + col, bv[q]);
-        else {
+      for (int q = 0; q < 16; ++q) bv[q].load(B + int64_t(__shfl(pid, q, 64)) * e.d_out + col);
 #pragma unroll
-          for (int c = 0; c < CPL; ++c) bv[q][c] = 0.f;
+      for (int q = 0; q < 16; ++q) {
+        if (j0 + q < r) {
+          float b[8];
+          bv[q].to8(b);
+          const float uj = __shfl(uv, q, 64);
+#pragma unroll
+          for (int c = 0; c < 8; ++c) v[c] = fmaf(uj, b[c], v[c]);
         }
       }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float uj = u[j + q];
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) v[c] = fmaf(uj, bv[q][c], v[c]);
-      }
-    }
-    for (; j < r; ++j) {
-      float bv[CPL];
-      if (col_ok) Cols<E, CPL>::load(B + int64_t(pid[j]) * e.d_out + col, bv);
-      else {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) bv[c] = 0.f;
-      }
-      const float uj = u[j];
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) v[c] = fmaf(uj, bv[c], v[c]);
     }
   }
 }
 
-// Same sums in the same order, with the B slice of the last adapter (rank <=
-// RB) kept in registers: consecutive prefill rows usually share an adapter.
+// Same sums in the same order, with the B slice of the last page range (rank
+// <= RB) kept in registers: consecutive prefill rows usually share an adapter.
 template <int CPL, int RB>
 struct BCache {
-  int ad;
+  int ps, r;
   float b[RB][CPL];
 };
 
 template <int CPL, int RB>
-__device__ __forceinline__ void expand_row_cached(float (&v)[CPL], int t, int col, bool col_ok,
+__device__ __forceinline__ void expand_row_cached(float (&v)[CPL], int t, int col,
                                                   const ExpandArgs &e, BCache<CPL, RB> &cache) {
   const uint16_t *B = static_cast<const uint16_t *>(e.b_pages);
   for (int k = 0; k < e.K; ++k) {
-    const int p = e.slot_pos[t * e.K + k];
-    if (p < 0) continue;
-    const int ad = e.pair_adapter[p];
-    const int r = e.rank[ad];
-    const float *u = e.U + e.u_off[p];
-    const int32_t *pid = e.page_ids + e.page_start[ad];
+    const int4 sd = e.slot_desc[t * e.K + k];
+    if (sd.x < 0) continue;
+    const int r = sd.y;
+    const float *u = e.U + sd.z;
+    const int32_t *pid = e.page_ids + sd.w;
     if (r <= RB) {
-      if (ad != cache.ad) {
+      if (sd.w != cache.ps || r != cache.r) {
+        // rows past r reload row r-1; they are never used
 #pragma unroll
-        for (int j = 0; j < RB; ++j) {
-          if (j < r && col_ok) Cols<uint16_t, CPL>::load(B + int64_t(pid[j]) * e.d_out + col, cache.b[j]);
-          else {
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) cache.b[j][c] = 0.f;
-          }
-        }
-        cache.ad = ad;
+        for (int j = 0; j < RB; ++j)
+          Cols<uint16_t, CPL>::load(B + int64_t(pid[min(j, r - 1)]) * e.d_out + col, cache.b[j]);
+        cache.ps = sd.w;
+        cache.r = r;
       }
 #pragma unroll
       for (int j = 0; j < RB; ++j) {
@@ -154,11 +166,7 @@ __device__ __forceinline__ void expand_row_cached(float (&v)[CPL], int t, int co
     } else {
       for (int j = 0; j < r; ++j) {
         float bv[CPL];
-        if (col_ok) Cols<uint16_t, CPL>::load(B + int64_t(pid[j]) * e.d_out + col, bv);
-        else {
-#pragma unroll
-          for (int c = 0; c < CPL; ++c) bv[c] = 0.f;
-        }
+        Cols<uint16_t, CPL>::load(B + int64_t(pid[j]) * e.d_out + col, bv);
         const float uj = u[j];
 #pragma unroll
         for (int c = 0; c < CPL; ++c) v[c] = fmaf(uj, bv[c], v[c]);
@@ -203,19 +211,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs g) {
     const int kb = k_begin + kt * BK;
 #pragma unroll
     for (int c = 0; c < A_CH; ++c) {
+      // clamped rows: rows past M / N only feed outputs that are never stored
       const int idx = tid + c * NT;
       const int row = idx >> 3, col = (idx & 7) * 8;
-      const int gr = m0 + row;
-      ra[c] = gr < g.M ? *reinterpret_cast<const uint4 *>(X + int64_t(gr) * g.Kd + kb + col)
-                       : make_uint4(0, 0, 0, 0);
+      const int gr = min(m0 + row, g.M - 1);
+      ra[c] = *reinterpret_cast<const uint4 *>(X + int64_t(gr) * g.Kd + kb + col);
     }
 #pragma unroll
     for (int c = 0; c < B_CH; ++c) {
       const int idx = tid + c * NT;
       const int row = idx >> 3, col = (idx & 7) * 8;
-      const int gr = n0 + row;
-      rb[c] = gr < g.N ? *reinterpret_cast<const uint4 *>(W + int64_t(gr) * g.Kd + kb + col)
-                       : make_uint4(0, 0, 0, 0);
+      const int gr = min(n0 + row, g.N - 1);
+      rb[c] = *reinterpret_cast<const uint4 *>(W + int64_t(gr) * g.Kd + kb + col);
     }
   };
   auto sstore = [&](int buf) {
@@ -295,12 +302,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs g) {
     static_assert(CPL == 1 || CPL == 2, "fused epilogue handles 64 or 128 columns per wave");
     static_assert(NT / 64 * 32 * SC * 4 <= int(sizeof(smem)), "staging must fit in LDS");
     float *stage = reinterpret_cast<float *>(smem) + wave * 32 * SC;
-    const int col = n0 + wn * TN * 32 + lane * CPL;
-    const bool col_ok = col < g.N;
+    const int col_raw = n0 + wn * TN * 32 + lane * CPL;
+    const bool col_ok = col_raw < g.N;
+    const int col = col_ok ? col_raw : g.N - CPL;    // loads stay in bounds
     const bool lora_on = expand_enabled(g.ex);
     uint16_t *Y = static_cast<uint16_t *>(g.Y);
     BCache<CPL, 16> cache;
-    cache.ad = -1;
+    cache.ps = -1;
+    cache.r = -1;
     for (int i = 0; i < TM; ++i) {
       __syncthreads();
 #pragma unroll
@@ -318,10 +327,106 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs g) {
         float v[CPL];
 #pragma unroll
         for (int c = 0; c < CPL; ++c) v[c] = stage[rr * SC + lane * CPL + c];
-        if (lora_on) expand_row_cached<CPL, 16>(v, row, col, col_ok, g.ex, cache);
+        if (lora_on) expand_row_cached<CPL, 16>(v, row, col, g.ex, cache);
         if (col_ok) Cols<uint16_t, CPL>::store(Y + int64_t(row) * g.N + col, v);
       }
     }
+  }
+}
+
+// ------------------------------------------------------------ decode GEMM
+// Few tokens (M <= 128): the product is a stream of W (d_in x d_out bf16)
+// through HBM, and every W byte is used by one wave only.  A workgroup owns
+// 128 output columns (32 per wave) and KC = 512 of K, and issues its whole
+// W share at once, straight into the MFMA B-operand registers (32 loads of
+// 16 bytes per lane, nothing staged in LDS), so a 1-workgroup-per-CU grid
+// keeps ~128 KiB per CU in flight.  The token rows (shared by the 4 waves)
+// go through LDS.  K is permuted inside each 64-wide group so that a lane's
+// W loads are 64 contiguous bytes: in step s, lanes 0-31 contract k = 8s..8s+7
+// and lanes 32-63 k = 32+8s..32+8s+7; the X fragments read from LDS use the
+// same permutation, so the sum is unchanged.  Partial sums of the K splits go
+// to the workspace for the epilogue kernel.
+template <int MB>
+__global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
+  constexpr int KC = 512;
+  constexpr int NG = KC / 64;                 // 64-wide K groups
+  constexpr int BMr = MB * 32;
+  // One token row of the K chunk = 64 slots of 16 bytes.  Row r keeps chunk c
+  // in slot c ^ (r & 7): the 8 rows a fragment read touches at once hit 8
+  // different 16-byte bank groups.
+  __shared__ __attribute__((aligned(16))) uint16_t xs[BMr * KC];
+  const uint16_t *X = static_cast<const uint16_t *>(g.X);
+  const uint16_t *W = static_cast<const uint16_t *>(g.W);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = blockIdx.x * 128 + wave * 32;
+  const int m0 = blockIdx.y * BMr;
+  const int k0 = blockIdx.z * KC;
+  const int ng = min(NG, (g.Kd - k0) / 64);
+  const int half = lane >> 5;
+
+  // All loads are unconditional, from clamped addresses, so none waits on a
+  // branch: rows past M and columns past N only feed outputs that are never
+  // stored, and K groups past the end are skipped by the MFMA loop.
+  // Token rows first, straight into LDS (no registers): wave w loads rows
+  // w, w+4, ...; lane l of the instruction fills slot l of the row.
+#pragma unroll
+  for (int i = 0; i < BMr / 4; ++i) {
+    const int r = wave + 4 * i;
+    const int row = min(m0 + r, g.M - 1);
+    const int chunk = lane ^ (r & 7);
+    const int col = min(chunk * 8, ng * 64 - 8);
+    __builtin_amdgcn_global_load_lds(X + int64_t(row) * g.Kd + k0 + col,
+                                     (__attribute__((address_space(3))) void *)(xs + r * KC), 16, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // W fragments: row n0 + lane%32, k0 + 64*grp + 32*half + [0, 32)
+  uint4 wf[NG][4];
+  const uint16_t *wrow = W + int64_t(min(n0 + (lane & 31), g.N - 1)) * g.Kd + k0 + half * 32;
+#pragma unroll
+  for (int gq = 0; gq < NG; ++gq)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      wf[gq][q] = *reinterpret_cast<const uint4 *>(wrow + min(gq, ng - 1) * 64 + q * 8);
+  __builtin_amdgcn_sched_barrier(0);
+  // the BMr/4 token-row loads were issued before the NG*4 = 32 W loads:
+  // vmcnt <= 32 means they have landed in LDS (vmcnt 32: simm16 0x8F70)
+  static_assert(NG * 4 == 32, "wait count below assumes 32 W loads in flight");
+  __builtin_amdgcn_s_waitcnt(0x8F70);
+  __syncthreads();
+
+  f32x16_t acc[MB];
+#pragma unroll
+  for (int b = 0; b < MB; ++b)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
+#pragma unroll
+  for (int gq = 0; gq < NG; ++gq) {
+    if (gq < ng) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bf16x8_t bfrag;
+        __builtin_memcpy(&bfrag, &wf[gq][s], 16);
+#pragma unroll
+        for (int b = 0; b < MB; ++b) {
+          const int r = b * 32 + (lane & 31);
+          const int chunk = (gq * 64 + half * 32 + s * 8) / 8;
+          const bf16x8_t afrag =
+              *reinterpret_cast<const bf16x8_t *>(xs + r * KC + ((chunk ^ (r & 7)) * 8));
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag, bfrag, acc[b], 0, 0, 0);
+        }
+      }
+    }
+  }
+  float *Pz = g.partial + int64_t(blockIdx.z) * g.M * g.N;
+  const int col = n0 + (lane & 31);
+  if (col < g.N) {
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + b * 32 + (v >> 2) * 8 + half * 4 + (v & 3);
+        if (row < g.M) Pz[int64_t(row) * g.N + col] = acc[b][v];
+      }
   }
 }
 
@@ -379,20 +484,29 @@ __global__ __launch_bounds__(256) void epilogue_kernel(EpilogueArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = blockIdx.y * 4 + wave;
   if (row >= a.M) return;
-  const int col = (blockIdx.x * 64 + lane) * CPL;
-  const bool col_ok = col < a.N;
+  const int col_raw = (blockIdx.x * 64 + lane) * CPL;
+  const bool col_ok = col_raw < a.N;
+  const int col = col_ok ? col_raw : a.N - CPL;      // loads stay in bounds
   float v[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) v[c] = 0.f;
-  if (col_ok) {
-    for (int z = 0; z < a.splits; ++z) {
-      float pv[CPL];
-      load_f8(a.partial + (int64_t(z) * a.M + row) * a.N + col, pv);
+  // split partials: issue up to 8 at once, add in split order
+  for (int z0 = 0; z0 < a.splits; z0 += 8) {
+    Raw8<float> pr[8];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) v[c] += pv[c];
+    for (int z = 0; z < 8; ++z)
+      pr[z].load(a.partial + (int64_t(min(z0 + z, a.splits - 1)) * a.M + row) * a.N + col);
+#pragma unroll
+    for (int z = 0; z < 8; ++z) {
+      if (z0 + z < a.splits) {
+        float pv[8];
+        pr[z].to8(pv);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) v[c] += pv[c];
+      }
     }
   }
-  if (expand_enabled(a.ex)) expand_row<E, CPL>(v, row, col, col_ok, a.ex);
+  if (expand_enabled(a.ex)) expand_row8<E>(v, row, col, a.ex);
   if (col_ok) Cols<E, CPL>::store(static_cast<E *>(a.Y) + int64_t(row) * a.N + col, v);
 }
 
@@ -419,8 +533,16 @@ GemmConfig choose_gemm(int T, int d_in, int d_out, int dtype) {
     c.kind = 0; c.bm = 64; c.bn = 64; c.splits = 1; c.k_split = d_in; c.fused = false;
     return c;
   }
-  if (T <= 64) { c.kind = 1; c.bm = 64; c.bn = 128; }
-  else if (T <= 256) { c.kind = 2; c.bm = 128; c.bn = 128; }
+  if (T <= 128) {
+    // decode: W streamed once, K split in chunks of 512 across workgroups
+    c.kind = 4; c.bn = 128;
+    c.bm = T <= 32 ? 32 : (T <= 64 ? 64 : 128);
+    c.k_split = 512;
+    c.splits = (d_in + 511) / 512;
+    c.fused = false;
+    return c;
+  }
+  if (T <= 256) { c.kind = 2; c.bm = 128; c.bn = 128; }
   else { c.kind = 3; c.bm = 256; c.bn = 128; }
   const int64_t tiles = int64_t((T + c.bm - 1) / c.bm) * ((d_out + c.bn - 1) / c.bn);
   const int kblocks = d_in / 64;
@@ -448,6 +570,13 @@ hipError_t launch_base_gemm(const GemmConfig &c, const GemmArgs &g, hipStream_t 
     const dim3 grid((g.N + 63) / 64, (g.M + 63) / 64);
     hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, s, static_cast<const float *>(g.X),
                        static_cast<const float *>(g.W), g.partial, g.M, g.N, g.Kd);
+    return hipGetLastError();
+  }
+  if (c.kind == 4) {
+    const dim3 grid((g.N + 127) / 128, (g.M + c.bm - 1) / c.bm, c.splits);
+    if (c.bm == 32) hipLaunchKernelGGL(gemm_decode_kernel<1>, grid, dim3(256), 0, s, g);
+    else if (c.bm == 64) hipLaunchKernelGGL(gemm_decode_kernel<2>, grid, dim3(256), 0, s, g);
+    else hipLaunchKernelGGL(gemm_decode_kernel<4>, grid, dim3(256), 0, s, g);
     return hipGetLastError();
   }
   if (c.kind == 1) return launch_bf16<64, 128, 1, 4, false>(c, g, s);

@@ -11,7 +11,7 @@ namespace lora {
 // ----------------------------------------------------------------- limits
 constexpr int64_t kMaxPairs = int64_t(1) << 20;  // T*K: keeps prefix sums of ranks in int32
 constexpr int kPlanThreads = 1024;
-constexpr int kPlanLdsMaxAdapters = 4096;         // per-adapter counters held in LDS up to here
+constexpr int kPlanLdsInts = 24576;               // LDS the plan kernel may use (96 KiB)
 constexpr int kGradPairChunk = 256;               // pairs per partial in the gradient reduction
 constexpr int kGradRankChunk = 16;                // rank rows per gradient register block
 
@@ -70,7 +70,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 struct PlanLayout {
   int64_t hdr, pair_tk, seg_adapter, seg_off, seg_row_off, bucket_seg_off, u_off, slot_pos;
   int64_t pair_adapter;
-  int64_t cnt, start, ustart, cur;  // per-adapter scratch
+  int64_t seg_desc;   // [S] x 8 ints: {adapter, rank, page_start, pair_begin, pair_end, u_begin, row_begin, 0}
+  int64_t slot_desc;  // [T*K] x 4 ints: {pair or -1, rank, u_off, page_start}
+  int64_t cnt, start, ustart, cur, ps, inf;  // per-adapter scratch (pools too big for LDS)
   int64_t total;
 };
 
@@ -88,10 +90,14 @@ __host__ __device__ inline PlanLayout plan_layout(int64_t TK, int64_t N) {
   L.u_off = o;          o = align16(o + TK + 1);
   L.slot_pos = o;       o = align16(o + TK);
   L.pair_adapter = o;   o = align16(o + TK);
+  L.seg_desc = o;       o = align16(o + 8 * TK);
+  L.slot_desc = o;      o = align16(o + 4 * TK);
   L.cnt = o;            o = align16(o + N);
   L.start = o;          o = align16(o + N);
   L.ustart = o;         o = align16(o + N);
   L.cur = o;            o = align16(o + N);
+  L.ps = o;             o = align16(o + N);
+  L.inf = o;            o = align16(o + N);
   L.total = o;
   return L;
 }
@@ -100,13 +106,17 @@ __host__ __device__ inline PlanLayout plan_layout(int64_t TK, int64_t N) {
 struct PlanView {
   const int32_t *hdr, *pair_tk, *seg_adapter, *seg_off, *seg_row_off, *u_off, *slot_pos;
   const int32_t *pair_adapter;
+  const int4 *seg_desc;    // two int4 per segment
+  const int4 *slot_desc;   // one int4 per slot
 };
 
 inline PlanView plan_view(const void *plan, int64_t TK, int64_t N) {
   const PlanLayout L = plan_layout(TK, N);
   const int32_t *b = static_cast<const int32_t *>(plan);
   return PlanView{b + L.hdr, b + L.pair_tk, b + L.seg_adapter, b + L.seg_off,
-                  b + L.seg_row_off, b + L.u_off, b + L.slot_pos, b + L.pair_adapter};
+                  b + L.seg_row_off, b + L.u_off, b + L.slot_pos, b + L.pair_adapter,
+                  reinterpret_cast<const int4 *>(b + L.seg_desc),
+                  reinterpret_cast<const int4 *>(b + L.slot_desc)};
 }
 
 // Device view of an adapter pool.
@@ -142,13 +152,14 @@ struct ShrinkArgs {
   int32_t *err_word;        // plan header word for device errors
   float *out;
   int64_t out_cap;          // capacity of out in floats
+  int big_segments;         // set by the launcher: large segments go to the MFMA tile kernel
 };
 
 // Everything the expand needs to add sum_j U[u_off[p]+j] * B_a[j][n] to row t.
 struct ExpandArgs {
   int K;
-  const int32_t *slot_pos, *u_off, *pair_adapter;
-  const int32_t *rank, *page_start, *page_ids;
+  const int4 *slot_desc;    // per slot {pair or -1, rank, u_off, page_start}
+  const int32_t *page_ids;
   const void *b_pages;      // [n_pages][d_out]
   int d_out;
   const float *U;
@@ -206,7 +217,9 @@ struct SegOuterArgs {
 // Each returns hipSuccess or the launch error.
 hipError_t launch_plan(const int32_t *ids, const float *gates, int T, int K, const PoolView &pool,
                        int32_t *plan, hipStream_t s);
-hipError_t launch_shrink(const ShrinkArgs &a, int dtype, int64_t rows_bound, hipStream_t s);
+// max_rank bounds the rank of every adapter the plan can hold segments for.
+hipError_t launch_shrink(const ShrinkArgs &a, int dtype, int64_t TK, int64_t n_adapters,
+                         int max_rank, hipStream_t s);
 
 // Base GEMM configuration chosen from the shape (host-side, deterministic).
 struct GemmConfig {
