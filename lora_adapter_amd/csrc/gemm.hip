@@ -430,6 +430,342 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
   }
 }
 
+// ------------------------------------------------------------ pipelined tile GEMM
+// The main GEMM for more than 128 tokens.  Tile BM x BN, K step 64, WM x WN
+// waves each owning (BM/WM) x (BN/WN) as 32x32x16 MFMA blocks.
+//   * Operands go global -> LDS with global_load_lds_dwordx4 (no VGPR
+//     staging): one instruction moves 8 tile rows of 128 bytes.  Two LDS
+//     stages; the loads of K tile kt+1 are in flight while tile kt feeds the
+//     MFMAs, and explicit vmcnt waits release each stage.
+//   * In LDS a tile row keeps 16-byte chunk c in slot c ^ (row & 7), so the
+//     8 rows a fragment read touches at once fall in 8 distinct bank groups.
+//   * Tiles are ordered so that the workgroups the hardware places on one XCD
+//     (workgroup ids equal mod 8) take consecutive tiles, walked 4 tile rows at
+//     a time: concurrently running tiles on an XCD share X rows and W columns
+//     through that XCD's L2.
+template <int BM, int BN, int WM, int WN>
+struct TileCfg {
+  static constexpr int NW = WM * WN, NT = NW * 64;
+  static constexpr int ROWB = 128;                        // bytes per 64-wide K row
+  static constexpr int STAGE = (BM + BN) * ROWB;          // bytes per LDS stage
+  static constexpr int TM = BM / (WM * 32), TN = BN / (WN * 32);
+  static constexpr int A_INS = BM / 8 / NW, B_INS = BN / 8 / NW;
+  static constexpr int LPW = A_INS + B_INS;               // loads per wave per stage
+  static_assert(A_INS * 8 * NW == BM && B_INS * 8 * NW == BN, "tile rows / waves");
+  static_assert(LPW < 64, "vmcnt field holds at most 63");
+};
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (const __attribute__((address_space(3))) char *)(p)));
+}
+
+// global_load_lds_dwordx4: each of the 64 lanes copies 16 bytes from its
+// global address to LDS at lds + 16 * lane.  Issued from inline asm so that
+// the compiler does not put a blanket vmcnt(0) in front of every later LDS
+// read (it cannot tell which LDS stage an in-flight copy writes); the
+// instruction has no register result, and the kernel waits for these copies
+// itself (wait_vmcnt) before the barrier that precedes reading the stage.
+__device__ __forceinline__ void lds_dma16(const void *gptr, uint32_t lds) {
+  const uint32_t lds_s = __builtin_amdgcn_readfirstlane(lds);   // wave-uniform LDS base
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(lds_s)
+               : "memory", "m0");
+}
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt bits 3:0 and 15:14).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ void tile_coords(int T, int tiles_m, int tiles_n, int &tm, int &tn) {
+  constexpr int G = 4;
+  const int gsize = G * tiles_n;
+  const int grp = T / gsize;
+  const int first = grp * G;
+  const int gm = min(G, tiles_m - first);
+  const int in = T - grp * gsize;
+  tm = first + in % gm;
+  tn = in / gm;
+}
+
+// Fused epilogue of a tile: add the expand to the fp32 accumulators, round
+// once, store Y.
+//   * A 32-row block whose rows all hold one active slot of the same adapter
+//     (rank <= 16) with consecutive U offsets -- the common case in prefill,
+//     where segments are long -- takes the expand as MFMAs: U_block (32 x r,
+//     fp32 split exactly into bf16 hi + lo, error < 2^-16 of U) times the
+//     adapter's B slice (r x 32 per MFMA block), accumulated into the same
+//     registers as the base product.
+//   * Other blocks stage through LDS and add the expand row by row.
+template <int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void fused_epilogue(const GemmArgs &g,
+                                               f32x16_t (&acc)[TileCfg<BM, BN, WM, WN>::TM]
+                                                              [TileCfg<BM, BN, WM, WN>::TN],
+                                               char *lds0, char *lds1, int m0, int n0) {
+  using C = TileCfg<BM, BN, WM, WN>;
+  constexpr int TM = C::TM, TN = C::TN;
+  constexpr int SC = TN * 32 + 1;            // staged floats per row (padded)
+  constexpr int CPL = TN * 32 / 64;          // output columns per lane
+  static_assert(CPL == 1 || CPL == 2, "fused epilogue handles 64 or 128 columns per wave");
+  // waves 0..NW/2-1 stage in lds0, the others in lds1
+  static_assert((C::NW / 2) * 32 * SC * 4 <= C::STAGE, "staging must fit in LDS");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int frow = lane & 31, half = lane >> 5;
+  const bool lora_on = expand_enabled(g.ex);
+  const uint16_t *Bp = static_cast<const uint16_t *>(g.ex.b_pages);
+
+  // ---- MFMA expand of single-adapter blocks
+  unsigned done = 0;
+  int bkey_ps = -1, bkey_r = -1;
+  bf16x8_t bfr[TN];
+  if (lora_on && g.ex.K == 1) {
+    // unrolled: acc is indexed with constants only (a runtime index would
+    // send the whole accumulator array to scratch memory)
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int R0 = m0 + wm * TM * 32 + i * 32;
+      const int row = min(R0 + frow, g.M - 1);
+      const int4 sd = g.ex.slot_desc[row];
+      const int s0x = __shfl(sd.x, 0, 64), r = __shfl(sd.y, 0, 64);
+      const int uz = __shfl(sd.z, 0, 64), ps = __shfl(sd.w, 0, 64);
+      const bool ok = R0 + frow < g.M && s0x >= 0 && sd.x >= 0 && sd.y == r && sd.w == ps &&
+                      sd.z == uz + frow * r && r > 0 && r <= 16;
+      if (__ballot(!ok) != 0) continue;
+      if (ps != bkey_ps || r != bkey_r) {
+        // B operand: lane (column frow of block j, rank rows 8*half .. +7)
+        int pidl = 0;
+        if (lane < 16) pidl = g.ex.page_ids[ps + min(lane, r - 1)];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col = min(n0 + wn * TN * 32 + j * 32 + frow, g.N - 1);
+          uint32_t w4[4];
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const int ja = half * 8 + e, jb = ja + 1;
+            const int pa = __shfl(pidl, min(ja, 15), 64), pb = __shfl(pidl, min(jb, 15), 64);
+            uint32_t lo = Bp[int64_t(pa) * g.ex.d_out + col];
+            uint32_t hi = Bp[int64_t(pb) * g.ex.d_out + col];
+            if (ja >= r) lo = 0;
+            if (jb >= r) hi = 0;
+            w4[e >> 1] = lo | (hi << 16);
+          }
+          const uint4 packed = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+          __builtin_memcpy(&bfr[j], &packed, 16);
+        }
+        bkey_ps = ps;
+        bkey_r = r;
+      }
+      // A operand: U of row frow, rank rows 8*half .. +7, as bf16 hi + lo
+      const float *urow = g.ex.U + uz + frow * r;
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const int ja = half * 8 + e, jb = ja + 1;
+        float ua = urow[min(ja, r - 1)], ub = urow[min(jb, r - 1)];
+        if (ja >= r) ua = 0.f;
+        if (jb >= r) ub = 0.f;
+        const uint16_t ha = f2bf(ua), hb = f2bf(ub);
+        const uint16_t la = f2bf(ua - bf2f(ha)), lb = f2bf(ub - bf2f(hb));
+        hw[e >> 1] = uint32_t(ha) | (uint32_t(hb) << 16);
+        lw[e >> 1] = uint32_t(la) | (uint32_t(lb) << 16);
+      }
+      bf16x8_t ahi, alo;
+      const uint4 ph = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      const uint4 pl = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      __builtin_memcpy(&ahi, &ph, 16);
+      __builtin_memcpy(&alo, &pl, 16);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bfr[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bfr[j], acc[i][j], 0, 0, 0);
+      }
+      done |= 1u << i;
+    }
+  }
+
+  // ---- stage, expand the remaining rows, round and store
+  float *stage = reinterpret_cast<float *>(wave < C::NW / 2 ? lds0 : lds1) +
+                 (wave % (C::NW / 2)) * 32 * SC;
+  const int col_raw = n0 + wn * TN * 32 + lane * CPL;
+  const bool col_ok = col_raw < g.N;
+  const int col = col_ok ? col_raw : g.N - CPL;     // loads stay in bounds
+  uint16_t *Y = static_cast<uint16_t *>(g.Y);
+  BCache<CPL, 16> cache;
+  cache.ps = -1;
+  cache.r = -1;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = (v >> 2) * 8 + half * 4 + (v & 3);
+        stage[r * SC + j * 32 + frow] = acc[i][j][v];
+      }
+    __syncthreads();
+    const int rbase = m0 + wm * TM * 32 + i * 32;
+    const bool rows_need_expand = lora_on && !((done >> i) & 1u);
+    for (int rr = 0; rr < 32; ++rr) {
+      const int row = rbase + rr;
+      if (row >= g.M) break;
+      float v[CPL];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) v[c] = stage[rr * SC + lane * CPL + c];
+      if (rows_need_expand) expand_row_cached<CPL, 16>(v, row, col, g.ex, cache);
+      if (col_ok) Cols<uint16_t, CPL>::store(Y + int64_t(row) * g.N + col, v);
+    }
+  }
+}
+
+// One K tile of MFMAs from an LDS stage.
+template <int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void tile_mfma(const char *As,
+                                          f32x16_t (&acc)[TileCfg<BM, BN, WM, WN>::TM]
+                                                         [TileCfg<BM, BN, WM, WN>::TN]) {
+  using C = TileCfg<BM, BN, WM, WN>;
+  constexpr int TM = C::TM, TN = C::TN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int frow = lane & 31, half = lane >> 5;
+  const char *Bs = As + BM * C::ROWB;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    bf16x8_t af[TM], bf[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int row = wm * TM * 32 + i * 32 + frow;
+      af[i] = *reinterpret_cast<const bf16x8_t *>(As + row * C::ROWB + (((2 * s + half) ^ (row & 7)) << 4));
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int row = wn * TN * 32 + j * 32 + frow;
+      bf[j] = *reinterpret_cast<const bf16x8_t *>(Bs + row * C::ROWB + (((2 * s + half) ^ (row & 7)) << 4));
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+template <int BM, int BN, int WM, int WN, bool kFused>
+__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_tile_kernel(GemmArgs g) {
+  using C = TileCfg<BM, BN, WM, WN>;
+  constexpr int TM = C::TM, TN = C::TN;
+  // two stages as two LDS objects, so that waits for one stage's loads do
+  // not also wait for the other's
+  __shared__ __attribute__((aligned(16))) char st0[C::STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[C::STAGE];
+
+  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  const int ntiles = tiles_m * tiles_n;
+  const int per = (ntiles + 7) / 8;
+  const int t = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (t >= ntiles) return;
+  int tm, tn;
+  tile_coords(t, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const uint16_t *X = static_cast<const uint16_t *>(g.X);
+  const uint16_t *W = static_cast<const uint16_t *>(g.W);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int k_begin = blockIdx.y * g.k_split;
+  const int k_end = min(g.Kd, k_begin + g.k_split);
+  const int nk = (k_end - k_begin) / 64;
+
+  // per-lane source rows, as 32-bit element offsets from the tile's first row
+  // (clamped: rows past M / N feed outputs that are never stored)
+  const int lrow = lane >> 3;
+  const int lchunk = (lane & 7) ^ lrow;
+  const uint16_t *abase = X + int64_t(m0) * g.Kd + k_begin;
+  const uint16_t *bbase = W + int64_t(n0) * g.Kd + k_begin;
+  uint32_t aoff[C::A_INS], boff[C::B_INS];
+#pragma unroll
+  for (int i = 0; i < C::A_INS; ++i) {
+    const int row = (wave * C::A_INS + i) * 8 + lrow;
+    aoff[i] = uint32_t(min(row, g.M - 1 - m0)) * uint32_t(g.Kd) + lchunk * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < C::B_INS; ++i) {
+    const int row = (wave * C::B_INS + i) * 8 + lrow;
+    boff[i] = uint32_t(min(row, g.N - 1 - n0)) * uint32_t(g.Kd) + lchunk * 8;
+  }
+  auto issue = [&](char *base, int kt) {
+    const uint16_t *a = abase + kt * 64;
+    const uint16_t *b = bbase + kt * 64;
+    const uint32_t lds = lds_addr(base);
+#pragma unroll
+    for (int i = 0; i < C::A_INS; ++i)
+      lds_dma16(a + aoff[i], lds + (wave * C::A_INS + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < C::B_INS; ++i)
+      lds_dma16(b + boff[i], lds + BM * C::ROWB + (wave * C::B_INS + i) * 1024);
+  };
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int frow = lane & 31, half = lane >> 5;
+  if (nk > 0) issue(st0, 0);
+  if (nk > 1) issue(st1, 1);
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    // even tile from stage 0 while the odd tile's loads stay in flight
+    wait_vmcnt<C::LPW>();
+    __syncthreads();
+    tile_mfma<BM, BN, WM, WN>(st0, acc);
+    __syncthreads();
+    if (kt + 2 < nk) {
+      issue(st0, kt + 2);
+      wait_vmcnt<C::LPW>();     // the odd tile (issued before this one) has landed
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();
+    tile_mfma<BM, BN, WM, WN>(st1, acc);
+    __syncthreads();
+    if (kt + 3 < nk) issue(st1, kt + 3);
+  }
+  if (kt < nk) {               // odd number of K tiles: the last one is in stage 0
+    wait_vmcnt<0>();
+    __syncthreads();
+    tile_mfma<BM, BN, WM, WN>(st0, acc);
+    __syncthreads();
+  }
+
+  if constexpr (!kFused) {
+    float *Pz = g.partial + int64_t(blockIdx.y) * g.M * g.N;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = n0 + wn * TN * 32 + j * 32 + frow;
+        if (col >= g.N) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = m0 + wm * TM * 32 + i * 32 + (v >> 2) * 8 + half * 4 + (v & 3);
+          if (row < g.M) Pz[int64_t(row) * g.N + col] = acc[i][j][v];
+        }
+      }
+  } else {
+    fused_epilogue<BM, BN, WM, WN>(g, acc, st0, st1, m0, n0);
+  }
+}
+
 // ------------------------------------------------------------ fp32 GEMM
 // Plain LDS-tiled fp32 product (the fp32 layer is small): 64x64 tile, 256
 // threads each owning 4x4 outputs; writes the fp32 base product.
@@ -542,15 +878,18 @@ GemmConfig choose_gemm(int T, int d_in, int d_out, int dtype) {
     c.fused = false;
     return c;
   }
-  if (T <= 256) { c.kind = 2; c.bm = 128; c.bn = 128; }
-  else { c.kind = 3; c.bm = 256; c.bn = 128; }
-  const int64_t tiles = int64_t((T + c.bm - 1) / c.bm) * ((d_out + c.bn - 1) / c.bn);
   const int kblocks = d_in / 64;
-  if (c.kind == 3 && tiles >= 128) {
+  // enough 256 x 256 tiles to fill the GPU: fused epilogue, no split
+  const int64_t big_tiles = int64_t((T + 255) / 256) * ((d_out + 255) / 256);
+  if (big_tiles >= 256) {
+    c.kind = 5; c.bm = 256; c.bn = 256;
     c.splits = 1; c.k_split = d_in; c.fused = true;
     return c;
   }
-  int64_t want = tiles > 0 ? (512 + tiles - 1) / tiles : 1;
+  // otherwise 256 x 128 tiles with K split so ~256 workgroups run
+  c.kind = 6; c.bm = 256; c.bn = 128;
+  const int64_t tiles = int64_t((T + c.bm - 1) / c.bm) * ((d_out + c.bn - 1) / c.bn);
+  int64_t want = tiles > 0 ? (256 + tiles - 1) / tiles : 1;
   int64_t most = kblocks / 8 > 1 ? kblocks / 8 : 1;     // every split keeps >= 512 of K
   int splits = int(want < most ? want : most);
   if (splits < 1) splits = 1;
@@ -577,6 +916,17 @@ hipError_t launch_base_gemm(const GemmConfig &c, const GemmArgs &g, hipStream_t 
     if (c.bm == 32) hipLaunchKernelGGL(gemm_decode_kernel<1>, grid, dim3(256), 0, s, g);
     else if (c.bm == 64) hipLaunchKernelGGL(gemm_decode_kernel<2>, grid, dim3(256), 0, s, g);
     else hipLaunchKernelGGL(gemm_decode_kernel<4>, grid, dim3(256), 0, s, g);
+    return hipGetLastError();
+  }
+  if (c.kind == 5 || c.kind == 6) {
+    const int tiles = ((g.M + c.bm - 1) / c.bm) * ((g.N + c.bn - 1) / c.bn);
+    const dim3 grid(8 * ((tiles + 7) / 8), c.splits);
+    if (c.kind == 5) {
+      if (c.fused) hipLaunchKernelGGL((gemm_tile_kernel<256, 256, 2, 2, true>), grid, dim3(256), 0, s, g);
+      else hipLaunchKernelGGL((gemm_tile_kernel<256, 256, 2, 2, false>), grid, dim3(256), 0, s, g);
+    } else {
+      hipLaunchKernelGGL((gemm_tile_kernel<256, 128, 2, 2, false>), grid, dim3(256), 0, s, g);
+    }
     return hipGetLastError();
   }
   if (c.kind == 1) return launch_bf16<64, 128, 1, 4, false>(c, g, s);
