@@ -72,11 +72,28 @@ struct PlanLayout {
   int64_t pair_adapter;
   int64_t seg_desc;   // [S] x 8 ints: {adapter, rank, page_start, pair_begin, pair_end, u_begin, row_begin, 0}
   int64_t slot_desc;  // [T*K] x 4 ints: {pair or -1, rank, u_off, page_start}
-  int64_t cnt, start, ustart, cur, ps, inf;  // per-adapter scratch (pools too big for LDS)
+  int64_t cnt, ubias, cur, ps, inf;  // per-adapter scratch (pools too big for LDS)
+  int64_t wcnt;                      // per (bucket, round, wave) counts, same case
   int64_t total;
 };
 
 __host__ __device__ inline int64_t align16(int64_t x) { return (x + 15) & ~int64_t(15); }
+
+// Per-bucket columns of the plan kernel's (round, wave) count table for any
+// block size of 64..kPlanThreads threads: ceil(N / nt) * (nt / 64) <= ceil(N / 64) + 16.
+__host__ __device__ inline int64_t plan_count_cols(int64_t N) {
+  return (N + 63) / 64 + kPlanThreads / 64 + 1;
+}
+
+// Threads of the plan workgroup: one per slot or adapter (the larger count),
+// rounded up to a power of two in 64..kPlanThreads, so that small batches run
+// in few waves.
+inline int plan_threads(int64_t TK, int64_t N) {
+  const int64_t work = TK > N ? TK : N;
+  int nt = 64;
+  while (nt < kPlanThreads && nt < work) nt *= 2;
+  return nt;
+}
 
 __host__ __device__ inline PlanLayout plan_layout(int64_t TK, int64_t N) {
   PlanLayout L;
@@ -93,11 +110,11 @@ __host__ __device__ inline PlanLayout plan_layout(int64_t TK, int64_t N) {
   L.seg_desc = o;       o = align16(o + 8 * TK);
   L.slot_desc = o;      o = align16(o + 4 * TK);
   L.cnt = o;            o = align16(o + N);
-  L.start = o;          o = align16(o + N);
-  L.ustart = o;         o = align16(o + N);
+  L.ubias = o;          o = align16(o + N);
   L.cur = o;            o = align16(o + N);
   L.ps = o;             o = align16(o + N);
   L.inf = o;            o = align16(o + N);
+  L.wcnt = o;           o = align16(o + LORA_N_BUCKETS * plan_count_cols(N));
   L.total = o;
   return L;
 }

@@ -7,23 +7,33 @@
 // (rank bucket, adapter, token, slot) plus the offsets and packed descriptors
 // the later kernels use.  All integer: bit-exact and deterministic.
 //
-// One workgroup of 1024 threads builds the whole plan.  At decode sizes the
-// cost is latency, so the kernel is organised around few global round trips:
-//   0. every thread loads the rank and page_start of its own block of
-//      adapters (contiguous ids) into LDS;
-//   1. each slot is classified (ids and gates: one round trip; adapter data
-//      from LDS) and counted per adapter;
-//   2. page_start consistency of every used adapter;
-//   3. one block scan per non-empty rank bucket gives each used adapter its
-//      first pair position, segment, U offset and rank-row offset;
+// One workgroup builds the whole plan.  At decode sizes the cost is latency:
+// every wave of a workgroup shares one CU's four SIMDs, so each step costs
+// its instruction count times the waves per SIMD.  The block is therefore
+// sized to the problem (64 threads for a 64-token batch over 64 adapters, up
+// to 1024), and the kernel is organised around few global round trips and
+// few barriers:
+//   0. adapters are dealt to threads round-robin; each thread loads rank and
+//      page_start of its adapters (the first slots' ids and gates are already
+//      in flight);
+//   1. each slot is classified (adapter data from LDS) and counted per adapter;
+//   2. page_start consistency of every used adapter; bucket occupancy;
+//   3. segment order: one ballot per occupied bucket gives every used adapter
+//      its rank among the used adapters of its bucket dealt to its wave; the
+//      per-wave counts are scanned (one wave per bucket), which places every
+//      adapter in (bucket, adapter) order; one block scan over the segments
+//      then gives pair, U and rank-row offsets;
 //   4. page ids of every used rank row are range-checked in parallel over rows
 //      (a bad adapter is dropped and step 3 redone once);
 //   5. pairs are placed in slot order: lanes holding the same adapter find
 //      each other with one ballot per id bit, the first of them takes
-//      positions from the adapter's cursor, and the waves of a 1024-slot
-//      chunk take their turns in order, which keeps the sort stable.
-// Per-adapter arrays live in LDS when they fit (96 KiB), else in the plan
-// buffer's scratch (accessed with agent-scope atomics where counters change).
+//      positions from the adapter's cursor, and the waves of each chunk of
+//      slots (one slot per thread) take their turns in order, which keeps the
+//      sort stable.
+// Per-adapter arrays live in LDS when they fit (96 KiB); then the barriers
+// order LDS only, and global stores (outputs only) never stall them.  Larger
+// pools keep those arrays in the plan buffer's scratch (agent-scope atomics
+// where counters change, full barriers).
 #include "lora_internal.h"
 
 namespace lora {
@@ -32,6 +42,10 @@ namespace {
 constexpr int kInfBadRank = 1 << 11;   // rank < 0 or > LORA_MAX_RANK
 constexpr int kInfBadStart = 1 << 12;  // page_start inconsistent with rank
 constexpr int kInfRankMask = 0x7ff;
+constexpr int kMaxWaves = kPlanThreads / 64;
+// Per-bucket entries of the (round, wave) count table: at most N/64 + 16.
+// When the per-adapter arrays fit LDS (N <= kPlanLdsInts / 5) this bound is:
+constexpr int kLdsCountCols = kPlanLdsInts / 5 / 64 + kMaxWaves + 1;
 
 struct PlanArgs {
   const int32_t *ids;
@@ -56,42 +70,74 @@ __device__ __forceinline__ void st_ctr(int *p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Workgroup barrier.  With every shared array in LDS it orders LDS only, so
+// outstanding global stores do not hold it up.
+template <bool kLds>
+__device__ __forceinline__ void bar() {
+  if constexpr (kLds) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  } else {
+    __syncthreads();
+  }
+}
+
+// Bitwise OR over the wave of a value below 2^LORA_N_BUCKETS (wave-uniform).
+__device__ __forceinline__ int wave_or_buckets(int v) {
+  int r = 0;
+#pragma unroll
+  for (int b = 0; b < LORA_N_BUCKETS; ++b)
+    if (__ballot((v >> b) & 1)) r |= 1 << b;
+  return r;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8
+// within each row of 16 lanes, then the last lane of row 0 is added to row 1
+// and row 3, and the last lane of row 1 to rows 2 and 3 (DPP row broadcasts).
+__device__ __forceinline__ int wave_scan_incl(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return v;
+}
+
 struct Scan4 {
   int v[4];
 };
 
-// Exclusive block scan of four ints over the 1024 threads; also the totals.
+// Exclusive block scan of four ints over the workgroup; also the totals.
+// Wave totals go through LDS once; every wave then scans the (at most 16)
+// totals in its lanes.
+template <bool kLds>
 __device__ Scan4 block_exclusive_scan4(Scan4 x, Scan4 &total, int *lds_tot /* [16*4] */) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  Scan4 inc = x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nwv = blockDim.x >> 6;
+  Scan4 inc;
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int y = __shfl_up(inc.v[q], d, 64);
-      if (lane >= d) inc.v[q] += y;
-    }
-  }
+  for (int q = 0; q < 4; ++q) inc.v[q] = wave_scan_incl(x.v[q]);
   if (lane == 63) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) lds_tot[wave * 4 + q] = inc.v[q];
   }
-  __syncthreads();
-  Scan4 before{{0, 0, 0, 0}};
-  Scan4 tot{{0, 0, 0, 0}};
-  for (int w = 0; w < kPlanThreads / 64; ++w) {
+  bar<kLds>();
+  int tw[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int t = lds_tot[w * 4 + q];
-      if (w < wave) before.v[q] += t;
-      tot.v[q] += t;
-    }
-  }
-  __syncthreads();  // lds_tot is reused by the next call
+  for (int q = 0; q < 4; ++q) tw[q] = lds_tot[min(lane, nwv - 1) * 4 + q];
   Scan4 ex;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) ex.v[q] = before.v[q] + inc.v[q] - x.v[q];
-  total = tot;
+  for (int q = 0; q < 4; ++q) {
+    const int t = lane < nwv ? tw[q] : 0;
+    const int ti = wave_scan_incl(t);
+    const int before = __builtin_amdgcn_readlane(ti - t, wave);
+    total.v[q] = __builtin_amdgcn_readlane(ti, 63);
+    ex.v[q] = before + inc.v[q] - x.v[q];
+  }
+  bar<kLds>();  // lds_tot is reused by the next call
   return ex;
 }
 
@@ -107,56 +153,89 @@ __device__ __forceinline__ uint64_t match_lanes(int a, int nbits) {
   return a >= 0 ? m : 0;
 }
 
+// Loads in flight per thread in the adapter and page-id passes.
+constexpr int kAdBatch = 4;
+constexpr int kRowBatch = 12;
+
 template <bool kLds>
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   extern __shared__ int dyn[];
-  __shared__ int lds_tot[(kPlanThreads / 64) * 4];
+  __shared__ int lds_tot[kMaxWaves * 4];
+  __shared__ int s_wcnt[kLds ? LORA_N_BUCKETS * kLdsCountCols : 1];
+  __shared__ int s_btot[LORA_N_BUCKETS];
   __shared__ int s_err, s_bmask, s_bad;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int nt = blockDim.x, nwv = nt >> 6;   // 64..1024 threads, chosen by problem size
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint64_t lt_mask = (uint64_t(1) << lane) - 1;
   const int N = a.N;
   const int64_t TK = int64_t(a.T) * a.K;
   const int Smax = int(TK < N ? TK : N);
   const PlanLayout L = plan_layout(TK, N);
   int32_t *P = a.plan;
-  // per-adapter arrays
+  // per-adapter arrays; ubias[a] = U offset of the adapter's first pair minus
+  // (its first pair position) * rank, so that a pair at position p starts at
+  // ubias[a] + p * rank
   int *cnt = kLds ? dyn : P + L.cnt;
   int *cur = kLds ? dyn + N : P + L.cur;
   int *psa = kLds ? dyn + 2 * N : P + L.ps;
   int *inf = kLds ? dyn + 3 * N : P + L.inf;
+  int *ubias = kLds ? dyn + 4 * N : P + L.ubias;
   // segment arrays (outputs; LDS copies when they fit)
-  int *seg_row = kLds ? dyn + 4 * N : P + L.seg_row_off;
-  int *seg_ad = kLds ? dyn + 4 * N + Smax + 1 : P + L.seg_adapter;
-  int *slot_ad = dyn + (kLds ? 4 * N + 2 * Smax + 1 : 0);
-  int32_t *start = P + L.start;
-  int32_t *ustart = P + L.ustart;
+  int *seg_row = kLds ? dyn + 5 * N : P + L.seg_row_off;
+  int *seg_ad = kLds ? dyn + 5 * N + Smax + 1 : P + L.seg_adapter;
+  // seg_pb[s] = page_start of segment s's adapter minus its first rank row
+  int *seg_pb = dyn + 5 * N + 2 * Smax + 1;   // LDS case only
+  int *slot_ad = dyn + (kLds ? 5 * N + 3 * Smax + 1 : 0);
+  // counts of used adapters per (bucket, round of nt adapters, wave)
+  const int Q = (N + nt - 1) / nt;
+  const int E = Q * nwv;
+  int *wcnt = kLds ? s_wcnt : P + L.wcnt;
 
-  const int m = (N + kPlanThreads - 1) / kPlanThreads;  // adapters per thread
-  const int a0 = tid * m, a1 = min(N, a0 + m);
-
-  // 0. per-adapter data
-  if (tid == 0) { s_err = 0; s_bmask = 0; s_bad = 0; }
-  for (int ad = a0; ad < a1; ++ad) {
-    const int r = a.rank[ad];
-    const int64_t s0 = a.page_start[ad], s1 = a.page_start[ad + 1];
-    int v = (r < 0 || r > LORA_MAX_RANK) ? kInfBadRank : r;
-    if (s0 < 0 || s1 - s0 != int64_t(r) || s1 > a.n_page_ids) v |= kInfBadStart;
-    inf[ad] = v;
-    psa[ad] = int(s0);
-    st_ctr(&cnt[ad], 0);
+  // The first nt slots are fetched now, so their round trip overlaps the
+  // adapter loads below.
+  int id_pre = -1;
+  float g_pre = 0.0f;
+  if (tid < TK) {
+    id_pre = a.ids[tid];
+    g_pre = a.gates[tid];
   }
-  __syncthreads();
+
+  // 0. per-adapter data; adapter ad belongs to thread ad % nt
+  if (tid == 0) { s_err = 0; s_bmask = 0; s_bad = 0; }
+  for (int base = tid; base < N; base += nt * kAdBatch) {
+    int r[kAdBatch], s0[kAdBatch], s1[kAdBatch];
+#pragma unroll
+    for (int q = 0; q < kAdBatch; ++q) {
+      const int ad = min(base + q * nt, N - 1);
+      r[q] = a.rank[ad];
+      s0[q] = a.page_start[ad];
+      s1[q] = a.page_start[ad + 1];
+    }
+#pragma unroll
+    for (int q = 0; q < kAdBatch; ++q) {
+      const int ad = base + q * nt;
+      if (ad >= N) break;
+      int v = (r[q] < 0 || r[q] > LORA_MAX_RANK) ? kInfBadRank : r[q];
+      if (s0[q] < 0 || int64_t(s1[q]) - s0[q] != int64_t(r[q]) || s1[q] > a.n_page_ids)
+        v |= kInfBadStart;
+      inf[ad] = v;
+      psa[ad] = s0[q];
+      st_ctr(&cnt[ad], 0);
+    }
+  }
+  bar<kLds>();
 
   // 1. classify and count
   const int nbits = N > 1 ? 32 - __clz(N - 1) : 1;
   int err = 0;
-  for (int64_t base = 0; base < TK; base += kPlanThreads) {
+  for (int64_t base = 0; base < TK; base += nt) {
     const int64_t i = base + tid;
     int ad = -1;
     if (i < TK) {
-      const int id = a.ids[i];
-      const float g = a.gates[i];
+      const int id = base == 0 ? id_pre : a.ids[i];
+      const float g = base == 0 ? g_pre : a.gates[i];
       if (id < -1 || id >= N) {
         err |= LORA_DEVERR_BAD_ID;
       } else if (id >= 0) {
@@ -167,15 +246,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       if (a.slot_cache) slot_ad[i] = ad;
     }
     const uint64_t mm = match_lanes(ad, nbits);
-    if (ad >= 0 && (mm & ((uint64_t(1) << lane) - 1)) == 0) atomicAdd(&cnt[ad], __popcll(mm));
+    if (ad >= 0 && (mm & lt_mask) == 0) atomicAdd(&cnt[ad], __popcll(mm));
   }
   if (err) atomicOr(&s_err, err);
-  __syncthreads();
+  bar<kLds>();
 
   // 2. page_start consistency of used adapters; bucket occupancy
   {
     int bm = 0;
-    for (int ad = a0; ad < a1; ++ad) {
+    for (int ad = tid; ad < N; ad += nt) {
       const int c = ld_ctr(&cnt[ad]);
       if (c <= 0) continue;
       const int v = inf[ad];
@@ -186,98 +265,175 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         bm |= 1 << rank_bucket(v & kInfRankMask);
       }
     }
-    if (bm) atomicOr(&s_bmask, bm);
+    bm = wave_or_buckets(bm);
+    if (lane == 0 && bm) atomicOr(&s_bmask, bm);
   }
-  __syncthreads();
+  bar<kLds>();
 
-  // 3. scans (redone once if step 4 drops an adapter)
-  int pair_base = 0, seg_base = 0, u_base = 0, row_base = 0;
+  // 3. segment order (redone once if step 4 drops an adapter)
+  int S = 0, pair_base = 0, u_base = 0, row_base = 0;
   for (int pass = 0; pass < 2; ++pass) {
     const int bmask = s_bmask;
-    pair_base = seg_base = u_base = row_base = 0;
-    for (int b = 0; b < LORA_N_BUCKETS; ++b) {
-      if (tid == 0) P[L.bucket_seg_off + b] = seg_base;
-      if (!(bmask & (1 << b))) continue;
-      Scan4 x{{0, 0, 0, 0}};
-      for (int ad = a0; ad < a1; ++ad) {
-        const int c = ld_ctr(&cnt[ad]);
-        const int r = inf[ad] & kInfRankMask;
-        if (c > 0 && rank_bucket(r) == b) {
-          x.v[0] += c; x.v[1] += 1; x.v[2] += c * r; x.v[3] += r;
-        }
+    // (a) used adapters per (bucket, round, wave)
+    for (int q = 0; q < Q; ++q) {
+      const int ad = q * nt + tid;
+      int b = -1;
+      if (ad < N && ld_ctr(&cnt[ad]) > 0) b = rank_bucket(inf[ad] & kInfRankMask);
+#pragma unroll
+      for (int bb = 0; bb < LORA_N_BUCKETS; ++bb) {
+        if (!((bmask >> bb) & 1)) continue;
+        const uint64_t m = __ballot(b == bb);
+        if (lane == 0) st_ctr(&wcnt[bb * E + q * nwv + wave], __popcll(m));
       }
-      Scan4 tot;
-      const Scan4 ex = block_exclusive_scan4(x, tot, lds_tot);
-      int st = pair_base + ex.v[0], sg = seg_base + ex.v[1];
-      int ub = u_base + ex.v[2], rb = row_base + ex.v[3];
-      for (int ad = a0; ad < a1; ++ad) {
-        const int c = ld_ctr(&cnt[ad]);
-        const int r = inf[ad] & kInfRankMask;
-        if (c > 0 && rank_bucket(r) == b) {
-          start[ad] = st;
-          ustart[ad] = ub;
-          st_ctr(&cur[ad], st);
-          seg_ad[sg] = ad;
-          seg_row[sg] = rb;
-          if (kLds) {
-            P[L.seg_adapter + sg] = ad;
-            P[L.seg_row_off + sg] = rb;
-          }
-          P[L.seg_off + sg] = st;
-          int4 *d = reinterpret_cast<int4 *>(P + L.seg_desc) + 2 * sg;
-          d[0] = make_int4(ad, r, psa[ad], st);
-          d[1] = make_int4(st + c, ub, rb, 0);
-          st += c; sg += 1; ub += c * r; rb += r;
-        }
-      }
-      pair_base += tot.v[0];
-      seg_base += tot.v[1];
-      u_base += tot.v[2];
-      row_base += tot.v[3];
     }
+    bar<kLds>();
+    // (b) exclusive scan of each occupied bucket's counts; bucket b is
+    //     scanned by wave b % nwv (every bucket total is written)
+    for (int b = wave; b < LORA_N_BUCKETS; b += nwv) {
+      int carry = 0;
+      if ((bmask >> b) & 1) {
+        for (int e0 = 0; e0 < E; e0 += 64) {
+          const int e = e0 + lane;
+          const int v = e < E ? ld_ctr(&wcnt[b * E + e]) : 0;
+          const int inc = wave_scan_incl(v);
+          if (e < E) st_ctr(&wcnt[b * E + e], carry + inc - v);
+          carry += __builtin_amdgcn_readlane(inc, 63);
+        }
+      }
+      if (lane == 0) s_btot[b] = carry;
+    }
+    bar<kLds>();
+    // (c) each used adapter's segment index: first segment of its bucket +
+    //     used adapters of the bucket in earlier (round, wave) cells + its rank
+    //     among the wave's lanes of that bucket
+    {
+      const int bt = lane < LORA_N_BUCKETS ? s_btot[lane] : 0;
+      const int bi = wave_scan_incl(bt);
+      if (tid <= LORA_N_BUCKETS) P[L.bucket_seg_off + tid] = bi - bt;   // lanes 0..9 of wave 0
+      S = __builtin_amdgcn_readlane(bi, 63);
+      for (int q = 0; q < Q; ++q) {
+        const int ad = q * nt + tid;
+        int b = -1;
+        if (ad < N && ld_ctr(&cnt[ad]) > 0) b = rank_bucket(inf[ad] & kInfRankMask);
+        int rk = 0;
+#pragma unroll
+        for (int bb = 0; bb < LORA_N_BUCKETS; ++bb) {
+          if (!((bmask >> bb) & 1)) continue;
+          const uint64_t m = __ballot(b == bb);
+          if (b == bb) rk = __popcll(m & lt_mask);
+        }
+        const int bs = __shfl(bi - bt, b < 0 ? 0 : b, 64);   // first segment of bucket b
+        if (b >= 0) seg_ad[bs + ld_ctr(&wcnt[b * E + q * nwv + wave]) + rk] = ad;
+      }
+    }
+    bar<kLds>();
+    // (d) pair, U and rank-row offsets of the segments (contiguous blocks per thread)
+    const int ms = (S + nt - 1) / nt;
+    const int g0 = min(S, tid * ms), g1 = min(S, g0 + ms);
+    Scan4 x{{0, 0, 0, 0}};
+    for (int sg = g0; sg < g1; ++sg) {
+      const int ad = seg_ad[sg];
+      const int c = ld_ctr(&cnt[ad]);
+      const int r = inf[ad] & kInfRankMask;
+      x.v[0] += c; x.v[1] += c * r; x.v[2] += r;
+    }
+    Scan4 tot;
+    const Scan4 ex = block_exclusive_scan4<kLds>(x, tot, lds_tot);
+    int st = ex.v[0], ub = ex.v[1], rb = ex.v[2];
+    for (int sg = g0; sg < g1; ++sg) {
+      const int ad = seg_ad[sg];
+      const int c = ld_ctr(&cnt[ad]);
+      const int r = inf[ad] & kInfRankMask;
+      ubias[ad] = ub - st * r;
+      st_ctr(&cur[ad], st);
+      seg_row[sg] = rb;
+      if (kLds) seg_pb[sg] = psa[ad] - rb;
+      if (kLds) {
+        P[L.seg_adapter + sg] = ad;
+        P[L.seg_row_off + sg] = rb;
+      }
+      P[L.seg_off + sg] = st;
+      int4 *d = reinterpret_cast<int4 *>(P + L.seg_desc) + 2 * sg;
+      d[0] = make_int4(ad, r, psa[ad], st);
+      d[1] = make_int4(st + c, ub, rb, 0);
+      st += c; ub += c * r; rb += r;
+    }
+    pair_base = tot.v[0];
+    u_base = tot.v[1];
+    row_base = tot.v[2];
     if (tid == 0) {
-      P[L.bucket_seg_off + LORA_N_BUCKETS] = seg_base;
-      P[L.seg_off + seg_base] = pair_base;
-      seg_row[seg_base] = row_base;
-      if (kLds) P[L.seg_row_off + seg_base] = row_base;
+      P[L.seg_off + S] = pair_base;
+      seg_row[S] = row_base;
+      if (kLds) P[L.seg_row_off + S] = row_base;
       P[L.u_off + pair_base] = u_base;
     }
-    __syncthreads();
+    bar<kLds>();
     if (pass == 1) break;
-    // 4. page ids of every used rank row, in parallel over rows
-    for (int g = tid; g < row_base; g += kPlanThreads) {
-      int lo = 0, hi = seg_base;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (seg_row[mid] <= g) lo = mid; else hi = mid;
+    // 4. page ids of every used rank row, kRowBatch rows per thread in flight.
+    //    Row g belongs to the last segment whose first row is <= g (segment
+    //    row offsets strictly increase), found by binary lifting.
+    int top = 1;
+    while (top * 2 <= S) top *= 2;
+    for (int h0 = 0; h0 < row_base; h0 += nt * kRowBatch) {
+      const int nq = min(kRowBatch, (row_base - h0 + nt - 1) / nt);   // uniform
+      int lo[kRowBatch], gq[kRowBatch], pg[kRowBatch];
+#pragma unroll
+      for (int q = 0; q < kRowBatch; ++q) {
+        gq[q] = min(h0 + q * nt + tid, row_base - 1);
+        lo[q] = 0;
       }
-      const int ad = seg_ad[lo];
-      const int64_t pg = a.page_ids[int64_t(psa[ad]) + (g - seg_row[lo])];
-      if (pg < 0 || pg >= a.n_pages) {
-        st_ctr(&cnt[ad], -1);
-        s_bad = 1;
+      // seg_row[S] = row_base exceeds every row, so clamping to S never moves lo
+      for (int step = top; step > 0; step >>= 1) {
+        int rc[kRowBatch];
+#pragma unroll
+        for (int q = 0; q < kRowBatch; ++q)
+          if (q < nq) rc[q] = seg_row[min(lo[q] + step, S)];
+#pragma unroll
+        for (int q = 0; q < kRowBatch; ++q)
+          if (q < nq) lo[q] = rc[q] <= gq[q] ? min(lo[q] + step, S) : lo[q];
+      }
+      int pix[kRowBatch];
+      if constexpr (kLds) {
+#pragma unroll
+        for (int q = 0; q < kRowBatch; ++q)
+          if (q < nq) pix[q] = seg_pb[lo[q]] + gq[q];
+      } else {
+#pragma unroll
+        for (int q = 0; q < kRowBatch; ++q)
+          if (q < nq) pix[q] = psa[seg_ad[lo[q]]] - seg_row[lo[q]] + gq[q];
+      }
+#pragma unroll
+      for (int q = 0; q < kRowBatch; ++q)
+        if (q < nq) pg[q] = a.page_ids[pix[q]];
+#pragma unroll
+      for (int q = 0; q < kRowBatch; ++q) {
+        if (q < nq && h0 + q * nt + tid < row_base && (pg[q] < 0 || pg[q] >= a.n_pages)) {
+          st_ctr(&cnt[seg_ad[lo[q]]], -1);
+          s_bad = 1;
+        }
       }
     }
-    __syncthreads();
+    bar<kLds>();
     if (s_bad == 0) break;
     if (tid == 0) {
       atomicOr(&s_err, LORA_DEVERR_BAD_POOL);
       s_bmask = 0;
     }
-    __syncthreads();
+    bar<kLds>();
     {   // the occupancy mask may have lost buckets: rebuild it
       int bm = 0;
-      for (int ad = a0; ad < a1; ++ad)
+      for (int ad = tid; ad < N; ad += nt)
         if (ld_ctr(&cnt[ad]) > 0) bm |= 1 << rank_bucket(inf[ad] & kInfRankMask);
-      if (bm) atomicOr(&s_bmask, bm);
+      bm = wave_or_buckets(bm);
+      if (lane == 0 && bm) atomicOr(&s_bmask, bm);
     }
-    __syncthreads();
+    bar<kLds>();
   }
 
-  // 5. ordered placement, one wave at a time within each 1024-slot chunk
-  const uint64_t lt_mask = (uint64_t(1) << lane) - 1;
+  // 5. ordered placement: within each nt-slot chunk the waves holding slots
+  //    take positions from the adapter cursors in wave order (stable sort)
   int4 *slot_desc = reinterpret_cast<int4 *>(P + L.slot_desc);
-  for (int64_t base = 0; base < TK; base += kPlanThreads) {
+  for (int64_t base = 0; base < TK; base += nt) {
     const int64_t i = base + tid;
     int ad = -1;
     if (i < TK) {
@@ -295,9 +451,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     const uint64_t mm = match_lanes(ad, nbits);
     const int rank_in_wave = __popcll(mm & lt_mask);
     const int leader = mm ? __ffsll((unsigned long long)mm) - 1 : lane;
+    const int64_t here = TK - base < nt ? TK - base : nt;
+    const int nw = int((here + 63) >> 6);
     int pos = -1;
-    for (int w = 0; w < kPlanThreads / 64; ++w) {
-      __syncthreads();
+    for (int w = 0; w < nw; ++w) {
+      bar<kLds>();
       if (wave == w) {
         int b0 = 0;
         if (ad >= 0 && rank_in_wave == 0) b0 = atomicAdd(&cur[ad], __popcll(mm));
@@ -309,7 +467,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       P[L.slot_pos + i] = pos;
       if (pos >= 0) {
         const int r = inf[ad] & kInfRankMask;
-        const int uo = ustart[ad] + (pos - start[ad]) * r;
+        const int uo = ubias[ad] + pos * r;
         P[L.pair_tk + pos] = int32_t(i);
         P[L.pair_adapter + pos] = ad;
         P[L.u_off + pos] = uo;
@@ -319,11 +477,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       }
     }
   }
-  __syncthreads();
+  bar<kLds>();
   if (tid == 0) {
     int32_t *h = P + L.hdr;
     h[LORA_PH_PAIRS] = pair_base;
-    h[LORA_PH_SEGS] = seg_base;
+    h[LORA_PH_SEGS] = S;
     h[LORA_PH_ERR] = s_err;
     h[LORA_PH_RPAIRS] = u_base;
     h[LORA_PH_RUSED] = row_base;
@@ -344,15 +502,17 @@ hipError_t launch_plan(const int32_t *ids, const float *gates, int T, int K, con
   const int64_t Smax = TK < N ? TK : N;
   PlanArgs a{ids, gates, T, K, pool.n_adapters, pool.rank, pool.page_start, pool.page_ids,
              pool.n_pages, pool.n_page_ids, plan, 0};
-  const int64_t adapter_ints = 4 * N + 2 * Smax + 1;
-  if (adapter_ints <= kPlanLdsInts) {
+  const int nt = plan_threads(TK, N);
+  const int64_t adapter_ints = 5 * N + 3 * Smax + 1;
+  const int64_t count_cols = (N + nt - 1) / nt * (nt / 64);
+  if (adapter_ints <= kPlanLdsInts && count_cols <= kLdsCountCols) {
     a.slot_cache = adapter_ints + TK <= kPlanLdsInts ? 1 : 0;
     const size_t lds = size_t(adapter_ints + (a.slot_cache ? TK : 0)) * sizeof(int);
-    hipLaunchKernelGGL(plan_kernel<true>, dim3(1), dim3(kPlanThreads), lds, s, a);
+    hipLaunchKernelGGL(plan_kernel<true>, dim3(1), dim3(nt), lds, s, a);
   } else {
     a.slot_cache = TK <= kPlanLdsInts ? 1 : 0;
     const size_t lds = size_t(a.slot_cache ? TK : 0) * sizeof(int);
-    hipLaunchKernelGGL(plan_kernel<false>, dim3(1), dim3(kPlanThreads), lds, s, a);
+    hipLaunchKernelGGL(plan_kernel<false>, dim3(1), dim3(nt), lds, s, a);
   }
   return hipGetLastError();
 }
