@@ -3,10 +3,10 @@
 
 One step = one pass of the whole hot path over one batch: lora_plan (segment
 plan), then lora_apply = shrink (LoRA down projection of every planned pair)
-+ base MFMA GEMM + expand epilogue (up projection added to the fp32
-accumulators, one rounding).  Default workload: Llama-7B q_proj decode,
-bf16, d_in = d_out = 4096, 64 tokens, 64 adapters of rank 16, each token on
-a uniformly drawn adapter (synthetic, seeded).
++ base MFMA GEMM + expand (up projection added to the fp32 accumulators, one
+rounding).  Default workload: Llama-7B q_proj decode, bf16, d_in = d_out =
+4096, 64 tokens, 64 adapters of rank 16, each token on a uniformly drawn
+adapter (synthetic, seeded).
 
 Measurement
   * value: tokens per second over exactly --steps steps, wall clock between
@@ -14,15 +14,26 @@ Measurement
     plan + shrink + GEMM + epilogue on one of R rotated copies of the weights
     and adapter pool, R chosen so that R copies exceed 1 GiB: every step reads
     its W and pages from HBM, not from the 256 MiB Infinity Cache.
-  * per-kernel durations: HIP events on the launch stream around each stage,
-    over a second timed pass of eager launches queued behind a busy prefix
-    (so the events measure the kernels, not host launch gaps).
-  * roofline: the dominant kernel (the base GEMM) against 8 TB/s HBM: its
-    algorithmic bytes (W + X) over its average event-measured duration.
+    value_apply_only: the same without the plan (built once per batch and
+    shared by every layer of a model).
+  * per-kernel durations: HIP events on the launch stream around blocks of
+    back-to-back launches of one stage on the rotated copies, queued behind a
+    busy prefix (so the events time the kernels, not host launch gaps).
+  * roofline: the dominant kernel (the base GEMM).  Below the MFMA/HBM ridge
+    (~312 flop/byte) it is priced against 8 TB/s HBM with its algorithmic
+    bytes (W + X), above it against 2.5 PFLOP/s bf16 MFMA with its
+    algorithmic flops (2 T d_in d_out, plus the expand when it runs inside the
+    GEMM).  traffic: HBM bytes per launch from rocprofv3 FETCH_SIZE and
+    WRITE_SIZE counters, scaled by the same counters on a copy of known size,
+    read from the committed summary profiles/traffic.json when the GEMM
+    source still matches the hash recorded there (else null).
   * LoRA path: t_apply - t_base where t_base is the same step on an empty
     plan; LoRA bytes = used A and B pages + X rows + U (written and read).
   * cpu_baseline: the CPU oracle (fp64 numpy) on the same workload, on the
     host's cores, for a bounded number of seconds.
+
+  --copy-probe runs a 256 MiB device-to-device copy five times first, so that
+  a rocprofv3 --pmc run of this script also holds the calibration kernel.
 """
 from __future__ import annotations
 
@@ -37,6 +48,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+FP32_PEAK_TFLOPS = 157.3
+RIDGE_FLOP_PER_BYTE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 METRIC = "tokens/sec per multi-LoRA layer at 1 GPU; LoRA-path HBM GB/s as % of peak"
 
 
@@ -51,6 +64,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotation", type=int, default=0, help="copies of W/pool (0: >= 1 GiB)")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter CSVs of a --copy-probe run into "
+                         "profiles/traffic.json entries, then exit")
     return ap.parse_args()
 
 
@@ -71,10 +88,13 @@ class Copy:
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(args.workload, *args.pmc_summary)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
-              "the layer shards over tokens with no exchange, see DESIGN.md", file=sys.stderr)
+              "the layer shards over tokens with no exchange between GPUs", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -87,6 +107,13 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     B.lib()
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w = wl.config(args.workload)
     L = D.DeviceLayer(w)
     T, K = w.T, w.K
@@ -100,14 +127,15 @@ def main():
     copies = [Copy(L, B, torch, clone=(i > 0)) for i in range(R)]
     stream = torch.cuda.current_stream()
 
-    def step(c, use_ids=ids):
-        B.lora_plan(use_ids, gates, T, K, c.pool, c.plan)
+    def step(c, use_ids=ids, plan=True):
+        if plan:
+            B.lora_plan(use_ids, gates, T, K, c.pool, c.plan)
         B.lora_shrink(c.X, mask, L.keep_scale, T, K, gates, c.pool, c.plan, c.ws)
         B.lora_base_gemm(c.X, c.W_t, c.Y, T, K, c.pool, c.plan, c.ws)
         B.lora_expand_epilogue(c.X, c.W_t, c.Y, T, K, c.pool, c.plan, c.ws)
 
     # ---------------------------------------------------------------- graphs
-    def make_graphs(use_ids):
+    def make_graphs(use_ids, plan):
         if args.no_graph:
             return None
         gs = []
@@ -115,20 +143,21 @@ def main():
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             for c in copies:       # warm the allocator / code objects outside capture
-                step(c, use_ids)
+                step(c, use_ids)   # (and leave a valid plan in every copy)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         for c in copies:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                step(c, use_ids)
+                step(c, use_ids, plan)
             gs.append(g)
         torch.cuda.synchronize()
         return gs
 
-    def timed(use_ids, steps, warmup):
-        gs = make_graphs(use_ids)
-        run = (lambda i: gs[i % R].replay()) if gs else (lambda i: step(copies[i % R], use_ids))
+    def timed(use_ids, steps, warmup, plan=True):
+        gs = make_graphs(use_ids, plan)
+        run = ((lambda i: gs[i % R].replay()) if gs
+               else (lambda i: step(copies[i % R], use_ids, plan)))
         for i in range(warmup):
             run(i)
         torch.cuda.synchronize()
@@ -139,6 +168,7 @@ def main():
         return time.perf_counter() - t0
 
     elapsed = timed(ids, args.steps, args.warmup)
+    elapsed_apply = timed(ids, args.steps, args.warmup, plan=False)
     elapsed_base = timed(empty_ids, args.steps, args.warmup)
     # results of the last apply on copy 0 must not be stale: re-run eagerly
     step(copies[0], ids)
@@ -195,9 +225,6 @@ def main():
     w_bytes = w.d_in * w.d_out * e
     x_bytes = T * w.d_in * e
     y_bytes = T * w.d_out * e
-    gemm_alg_bytes = w_bytes + x_bytes
-    t_gemm = st_med["gemm"] * 1e-6
-    gemm_gbs = gemm_alg_bytes / t_gemm / 1e9
     t_step = elapsed / args.steps
     t_base_step = elapsed_base / args.steps
     t_lora = max(t_step - t_base_step, 1e-12)
@@ -207,6 +234,7 @@ def main():
     lora_flops = 2.0 * R_pairs * (w.d_in + w.d_out)
     base_flops = 2.0 * T * w.d_in * w.d_out
     value = T * args.steps / elapsed
+    roofline = gemm_roofline(B, L, w, T, st_med["gemm"], base_flops, R_pairs, e)
 
     out = {
         "metric": METRIC,
@@ -225,10 +253,8 @@ def main():
                    "adapters": w.n_adapters, "ranks": sorted(set(w.rank.tolist()))[:8],
                    "active_pairs": P, "segments": S, "R_used": R_used, "R_pairs": R_pairs,
                    "rotation_copies": R, "graph_replay": not args.no_graph},
-        "roofline": {"bound": "hbm", "kernel": "base GEMM (gemm_bf16_kernel)",
-                     "achieved": gemm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gemm_gbs / HBM_PEAK_GBS, "traffic": None,
-                     "alg_bytes_per_launch": gemm_alg_bytes, "avg_launch_us": st_med["gemm"]},
+        "roofline": roofline,
+        "value_apply_only": T * args.steps / elapsed_apply,
         "stages_us_median": st_med,
         "stages_us_mean": st_mean,
         "stages_us_mean_empty_plan": sb_mean,
@@ -245,6 +271,113 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def gemm_kernel_name(T, dtype_code, B, fused):
+    if dtype_code != B.LORA_BF16:
+        return "gemm_f32_kernel"
+    if T <= 128:
+        return "gemm_decode_kernel"
+    return "gemm_tile_kernel" + (" (fused expand)" if fused else "")
+
+
+def gemm_roofline(B, L, w, T, t_us, base_flops, R_pairs, e):
+    """Roofline entry of the base GEMM kernel from its measured duration."""
+    fused = T > 128 and ((T + 255) // 256) * ((w.d_out + 255) // 256) >= 256
+    name = gemm_kernel_name(T, L.dtype, B, fused)
+    alg_bytes = (w.d_in * w.d_out + T * w.d_in) * e
+    flops = base_flops + (2.0 * R_pairs * w.d_out if fused else 0.0)
+    intensity = base_flops / ((w.d_in * w.d_out + T * w.d_in + T * w.d_out) * e)
+    t = t_us * 1e-6
+    if L.dtype != B.LORA_BF16:
+        r = {"bound": "alu", "achieved": flops / t / 1e12, "peak": FP32_PEAK_TFLOPS,
+             "unit": "TFLOP/s", "alg_flops_per_launch": flops}
+    elif intensity > RIDGE_FLOP_PER_BYTE:
+        r = {"bound": "mfma", "achieved": flops / t / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+             "unit": "TFLOP/s", "alg_flops_per_launch": flops}
+    else:
+        r = {"bound": "hbm", "achieved": alg_bytes / t / 1e9, "peak": HBM_PEAK_GBS,
+             "unit": "GB/s", "alg_bytes_per_launch": alg_bytes}
+    r["frac"] = r["achieved"] / r["peak"]
+    r["traffic"] = measured_traffic(name, w.name)
+    r["kernel"] = name
+    r["avg_launch_us"] = t_us
+    return r
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "lora_internal.h"):
+        with open(os.path.join(ROOT, "lora_adapter_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none for this kernel and workload or the source has changed."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            table = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    ent = table.get(kernel.split(" ")[0] + "|" + workload)
+    if not ent or ent.get("source_sha256_16") != kernel_source_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+COPY_PROBE_BYTES = 256 << 20
+
+
+def pmc_summary(workload_id, fetch_csv, write_csv):
+    """HBM bytes per launch of the base GEMM from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by the copy probe's reading of the same
+    counter against the bytes that copy must move."""
+    import csv
+    import numpy as np
+    from lora_adapter_amd import workloads as wl
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        return vals
+
+    w = wl.config(workload_id)
+    T = w.T
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        vals = per_kernel(path, counter)
+        copy = [v for k, vs in vals.items() if "copyBuffer" in k for v in vs
+                if v > COPY_PROBE_BYTES / 2]
+        gemm = [v for k, vs in vals.items() if "gemm_" in k for v in vs]
+        if not copy or not gemm:
+            raise SystemExit(f"{path}: no copy probe or GEMM dispatches for {counter}")
+        scale = COPY_PROBE_BYTES / float(np.median(copy))
+        out[counter] = {"raw_bytes_median": float(np.median(gemm)), "copy_scale": scale,
+                        "bytes": float(np.median(gemm)) * scale, "dispatches": len(gemm)}
+    name = gemm_kernel_name(T, 1 if w.dtype == "bf16" else 0, type("B", (), {"LORA_BF16": 1}),
+                            False).split(" ")[0]
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            table = json.load(fh)
+    except (OSError, ValueError):
+        table = {}
+    table[name + "|" + w.name] = {
+        "hbm_bytes_per_launch": out["FETCH_SIZE"]["bytes"] + out["WRITE_SIZE"]["bytes"],
+        "fetch": out["FETCH_SIZE"], "write": out["WRITE_SIZE"],
+        "source_sha256_16": kernel_source_hash(),
+    }
+    with open(path, "w") as fh:
+        json.dump(table, fh, indent=1, sort_keys=True)
+    print(json.dumps(table[name + "|" + w.name]))
 
 
 def cpu_baseline(w, seconds):

@@ -29,7 +29,7 @@ definition states.  Pages cited (by title and section):
                 the rank-specialised-kernel note (kernels specialised per
                 rank value, e.g. 4, 8, 16).
 
-Readings where the pages are silent (all listed in the design doc):
+Readings where the pages are silent (the plainest one the rest supports):
   * Factor orientation: x.A shrinks d_in -> r, then .B expands r -> d_out.
     W is d_in x d_out mathematically and stored transposed, W_t[d_out][d_in].
   * Each adapter carries a scale s_a; a slot's coefficient is c = g * s_a
