@@ -130,8 +130,7 @@ def main():
     def step(c, use_ids=ids, plan=True):
         if plan:
             B.lora_plan(use_ids, gates, T, K, c.pool, c.plan)
-        B.lora_shrink(c.X, mask, L.keep_scale, T, K, gates, c.pool, c.plan, c.ws)
-        B.lora_base_gemm(c.X, c.W_t, c.Y, T, K, c.pool, c.plan, c.ws)
+        B.lora_shrink_gemm(c.X, c.W_t, c.Y, T, K, gates, mask, L.keep_scale, c.pool, c.plan, c.ws)
         B.lora_expand_epilogue(c.X, c.W_t, c.Y, T, K, c.pool, c.plan, c.ws)
 
     # ---------------------------------------------------------------- graphs
@@ -180,6 +179,8 @@ def main():
 
     stages = {
         "plan": lambda c, u: B.lora_plan(u, gates, T, K, c.pool, c.plan),
+        "shrink_gemm": lambda c, u: B.lora_shrink_gemm(c.X, c.W_t, c.Y, T, K, gates, mask,
+                                                       L.keep_scale, c.pool, c.plan, c.ws),
         "shrink": lambda c, u: B.lora_shrink(c.X, mask, L.keep_scale, T, K, gates, c.pool, c.plan, c.ws),
         "gemm": lambda c, u: B.lora_base_gemm(c.X, c.W_t, c.Y, T, K, c.pool, c.plan, c.ws),
         "epilogue": lambda c, u: B.lora_expand_epilogue(c.X, c.W_t, c.Y, T, K, c.pool, c.plan, c.ws),
@@ -234,7 +235,7 @@ def main():
     lora_flops = 2.0 * R_pairs * (w.d_in + w.d_out)
     base_flops = 2.0 * T * w.d_in * w.d_out
     value = T * args.steps / elapsed
-    roofline = gemm_roofline(B, L, w, T, st_med["gemm"], base_flops, R_pairs, e)
+    roofline = gemm_roofline(B, L, w, T, st_med, base_flops, P, R_pairs, R_used, e)
 
     out = {
         "metric": METRIC,
@@ -273,20 +274,29 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def gemm_kernel_name(T, dtype_code, B, fused):
+def gemm_kernel_name(T, d_in, dtype_code, B, fused):
     if dtype_code != B.LORA_BF16:
         return "gemm_f32_kernel"
     if T <= 128:
-        return "gemm_decode_kernel"
+        return "decode_gemm_shrink_kernel" if d_in <= 4096 else "gemm_decode_kernel"
     return "gemm_tile_kernel" + (" (fused expand)" if fused else "")
 
 
-def gemm_roofline(B, L, w, T, t_us, base_flops, R_pairs, e):
-    """Roofline entry of the base GEMM kernel from its measured duration."""
+def gemm_roofline(B, L, w, T, st_med, base_flops, P, R_pairs, R_used, e):
+    """Roofline entry of the kernel that runs the base GEMM, from its
+    measured duration.  For decode shapes with d_in <= 4096 that kernel also
+    runs the shrink: its algorithmic bytes then include the used A pages, the
+    keep mask and U."""
     fused = T > 128 and ((T + 255) // 256) * ((w.d_out + 255) // 256) >= 256
-    name = gemm_kernel_name(T, L.dtype, B, fused)
+    name = gemm_kernel_name(T, w.d_in, L.dtype, B, fused)
     alg_bytes = (w.d_in * w.d_out + T * w.d_in) * e
     flops = base_flops + (2.0 * R_pairs * w.d_out if fused else 0.0)
+    if name == "decode_gemm_shrink_kernel":
+        t_us = st_med["shrink_gemm"]
+        alg_bytes += R_used * w.d_in * e + 4 * R_pairs + (T * w.d_in if L.keep_mask is not None else 0)
+        flops += 2.0 * R_pairs * w.d_in
+    else:
+        t_us = st_med["gemm"]
     intensity = base_flops / ((w.d_in * w.d_out + T * w.d_in + T * w.d_out) * e)
     t = t_us * 1e-6
     if L.dtype != B.LORA_BF16:
@@ -308,7 +318,7 @@ def gemm_roofline(B, L, w, T, t_us, base_flops, R_pairs, e):
 def kernel_source_hash():
     import hashlib
     h = hashlib.sha256()
-    for f in ("gemm.hip", "lora_internal.h"):
+    for f in ("gemm.hip", "shrink_units.h", "lora_internal.h"):
         with open(os.path.join(ROOT, "lora_adapter_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -351,19 +361,29 @@ def pmc_summary(workload_id, fetch_csv, write_csv):
 
     w = wl.config(workload_id)
     T = w.T
+    kname = gemm_kernel_name(T, w.d_in, 1 if w.dtype == "bf16" else 0,
+                             type("B", (), {"LORA_BF16": 1}), False).split(" ")[0]
+
+    def name_of(k):
+        for n in ("decode_gemm_shrink_kernel", "gemm_decode_kernel", "gemm_tile_kernel",
+                  "gemm_f32_kernel"):
+            if n in k:
+                return n
+        return None
+
     out = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         vals = per_kernel(path, counter)
         copy = [v for k, vs in vals.items() if "copyBuffer" in k for v in vs
                 if v > COPY_PROBE_BYTES / 2]
-        gemm = [v for k, vs in vals.items() if "gemm_" in k for v in vs]
+        gemm = [v for k, vs in vals.items() if name_of(k) == kname for v in vs]
         if not copy or not gemm:
             raise SystemExit(f"{path}: no copy probe or GEMM dispatches for {counter}")
         scale = COPY_PROBE_BYTES / float(np.median(copy))
         out[counter] = {"raw_bytes_median": float(np.median(gemm)), "copy_scale": scale,
                         "bytes": float(np.median(gemm)) * scale, "dispatches": len(gemm)}
-    name = gemm_kernel_name(T, 1 if w.dtype == "bf16" else 0, type("B", (), {"LORA_BF16": 1}),
-                            False).split(" ")[0]
+    name = gemm_kernel_name(T, w.d_in, 1 if w.dtype == "bf16" else 0,
+                            type("B", (), {"LORA_BF16": 1}), False).split(" ")[0]
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as fh:

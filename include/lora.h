@@ -122,12 +122,18 @@ const char *lora_status_string(int32_t status);
  *   u_off[T*K+1]           first P+1: prefix sum of pair ranks (U offsets)
  *   slot_pos[T*K]          sorted position of slot t*K+k, or -1
  *   pair_adapter[T*K]      first P: adapter of each sorted pair
- *   scratch                4*N ints used while building
+ *   internal               the gate of each sorted pair, packed segment and
+ *                          slot descriptors, the decode-shrink schedule,
+ *                          the segments left to the MFMA shrink, and scratch
+ *                          used while building
+ * Header words 0..7 are the LORA_PH_* values; words 8..10 hold internal
+ * scheduling counts; the rest are 0.
  * Everything is integer and bit-exact.  Built once per batch and shared by
  * every layer that uses the same routing.
  *   ids   [T][K] int32 device; -1 marks an empty slot.
  *   gates [T][K] float32 device.
- *   pool  only rank/page_start/page_ids/n_* are read.
+ *   pool  rank/page_start/page_ids/n_* are read; dtype, d_in and d_out
+ *         decide which segments the later MFMA shrink takes.
  *   plan  device buffer of at least lora_plan_bytes(T, K, N) bytes.
  * Errors: INVALID_ARG (null, T<0, K outside 1..LORA_MAX_K, N<1),
  * CAPACITY (plan_bytes too small), DEVICE (launch failed). */
@@ -149,7 +155,8 @@ int32_t lora_plan(const int32_t *ids, const float *gates, int32_t T, int32_t K,
  *   X      [T][d_in]   dtype,  W_t [d_out][d_in] dtype (nn.Linear layout),
  *   Y      [T][d_out]  dtype, must not alias X or W_t,
  *   K, gates as given to lora_plan (same T, K) and the plan built from them;
- *     later kernels read adapters from the plan only,
+ *     later kernels read adapters and gates from the plan only (the plan
+ *     records each pair's gate), so gates must not change in between,
  *   keep_mask [T][d_in] uint8 0/1 or NULL, keep_scale its scale (1/keep_p),
  *     applied to the LoRA branch input only,
  *   ws     workspace of >= lora_apply_workspace_bytes(T, K, d_in, d_out,
@@ -180,6 +187,14 @@ int32_t lora_base_gemm(const void *X, const void *W_t, void *Y, int32_t T, int32
 int32_t lora_expand_epilogue(const void *X, const void *W_t, void *Y, int32_t T, int32_t K,
                              const lora_pool_desc *pool, const void *plan,
                              void *ws, size_t ws_bytes, void *stream);
+/* lora_shrink followed by lora_base_gemm, with lora_apply's arguments.  For
+ * decode shapes (T <= 128, bf16) both run in one launch: the GEMM's
+ * workgroups and the shrink's waves side by side.  lora_apply =
+ * lora_shrink_gemm then lora_expand_epilogue. */
+int32_t lora_shrink_gemm(const void *X, const void *W_t, void *Y, int32_t T, int32_t K,
+                         const float *gates, const uint8_t *keep_mask, float keep_scale,
+                         const lora_pool_desc *pool, const void *plan, void *ws,
+                         size_t ws_bytes, void *stream);
 int32_t lora_apply(const void *X, const void *W_t, void *Y, int32_t T, int32_t K,
                    const float *gates, const uint8_t *keep_mask,
                    float keep_scale, const lora_pool_desc *pool, const void *plan, void *ws,

@@ -24,8 +24,8 @@ PH_PAIRS, PH_SEGS, PH_ERR, PH_RPAIRS, PH_RUSED, PH_T, PH_K, PH_N = range(8)
 
 EXPORTS = (
     "lora_abi_version", "lora_status_string", "lora_plan_bytes", "lora_plan_layout", "lora_plan",
-    "lora_apply_workspace_bytes", "lora_apply_u_offset", "lora_shrink", "lora_base_expand", "lora_base_gemm", "lora_expand_epilogue",
-    "lora_apply",
+    "lora_apply_workspace_bytes", "lora_apply_u_offset", "lora_shrink", "lora_base_expand",
+    "lora_base_gemm", "lora_expand_epilogue", "lora_shrink_gemm", "lora_apply",
     "lora_merge_delta", "lora_grad_workspace_bytes", "lora_grad",
 )
 
@@ -61,6 +61,7 @@ _PROTOS = {
     "lora_base_expand": (_I32, [_VP, _VP, _VP, _I32, _I32, _PD, _VP, _VP, _SZ, _VP]),
     "lora_base_gemm": (_I32, [_VP, _VP, _VP, _I32, _I32, _PD, _VP, _VP, _SZ, _VP]),
     "lora_expand_epilogue": (_I32, [_VP, _VP, _VP, _I32, _I32, _PD, _VP, _VP, _SZ, _VP]),
+    "lora_shrink_gemm": (_I32, [_VP, _VP, _VP, _I32, _I32, _VP, _VP, _F32, _PD, _VP, _VP, _SZ, _VP]),
     "lora_apply": (_I32, [_VP, _VP, _VP, _I32, _I32, _VP, _VP, _F32, _PD, _VP, _VP, _SZ, _VP]),
     "lora_merge_delta": (_I32, [_VP, _PD, _VP, _VP, _I32, _VP]),
     "lora_grad_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
@@ -176,6 +177,14 @@ def lora_expand_epilogue(X, W_t, Y, T: int, K: int, pool: Pool, plan, ws, stream
     _check("lora_expand_epilogue", lib().lora_expand_epilogue(
         _ptr(X), _ptr(W_t), _ptr(Y), T, K, pool.ref, _ptr(plan), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def lora_shrink_gemm(X, W_t, Y, T: int, K: int, gates, keep_mask, keep_scale: float, pool: Pool,
+                     plan, ws, stream=None):
+    _check("lora_shrink_gemm",
+           lib().lora_shrink_gemm(_ptr(X), _ptr(W_t), _ptr(Y), T, K, _ptr(gates), _ptr(keep_mask),
+                                  float(keep_scale), pool.ref, _ptr(plan), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def lora_apply(X, W_t, Y, T: int, K: int, gates, keep_mask, keep_scale: float, pool: Pool,

@@ -120,19 +120,11 @@ size_t lora_apply_u_offset(int32_t T, int32_t K, int32_t d_in, int32_t d_out, in
   return align_up(gemm_partial_bytes(choose_gemm(T > 0 ? T : 1, d_in, d_out, dtype), T, d_out));
 }
 
-int32_t lora_shrink(const void *X, const uint8_t *keep_mask, float keep_scale, int32_t T,
-                    int32_t K, const float *gates, const lora_pool_desc *pool, const void *plan,
-                    void *ws, size_t ws_bytes, void *stream) {
-  int32_t st = check_batch(T, K);
-  if (st != LORA_OK) return st;
-  if ((st = check_pool(pool, true)) != LORA_OK) return st;
-  if (!plan) return LORA_ERR_INVALID_ARG;
-  if (T == 0) return LORA_OK;
-  if (!X || !gates || !ws) return LORA_ERR_INVALID_ARG;
-  const ApplyWs w = apply_layout(ws, ws_bytes, T, pool->d_in, pool->d_out, pool->dtype);
-  if (w.u_cap < 0) return LORA_ERR_CAPACITY;
-  const int64_t TK = int64_t(T) * K;
-  const PlanView pv = plan_view(plan, TK, pool->n_adapters);
+namespace {
+
+ShrinkArgs apply_shrink_args(const void *X, const uint8_t *keep_mask, float keep_scale,
+                             int32_t T, int32_t K, const float *gates,
+                             const lora_pool_desc *pool, const PlanView &pv, const ApplyWs &w) {
   ShrinkArgs a{};
   a.Z = X;
   a.mask = keep_mask;
@@ -146,11 +138,27 @@ int32_t lora_shrink(const void *X, const uint8_t *keep_mask, float keep_scale, i
   a.err_word = const_cast<int32_t *>(pv.hdr) + LORA_PH_ERR;
   a.out = w.U;
   a.out_cap = w.u_cap;
-  // grid hint: the workspace was sized for ranks up to u_cap / (T*K); the
-  // kernel strides over rank rows, so a smaller hint stays correct
-  const int64_t hint = w.u_cap / (TK > 0 ? TK : 1);
-  const int max_rank = int(hint < LORA_MAX_RANK ? (hint > 0 ? hint : 1) : LORA_MAX_RANK);
-  return dev(launch_shrink(a, pool->dtype, TK, pool->n_adapters, max_rank,
+  a.big_segments = shrink_tile_enabled(pool->dtype, int64_t(T) * K, pool->d_in, pool->d_out) ? 1 : 0;
+  return a;
+}
+
+}  // namespace
+
+int32_t lora_shrink(const void *X, const uint8_t *keep_mask, float keep_scale, int32_t T,
+                    int32_t K, const float *gates, const lora_pool_desc *pool, const void *plan,
+                    void *ws, size_t ws_bytes, void *stream) {
+  int32_t st = check_batch(T, K);
+  if (st != LORA_OK) return st;
+  if ((st = check_pool(pool, true)) != LORA_OK) return st;
+  if (!plan) return LORA_ERR_INVALID_ARG;
+  if (T == 0) return LORA_OK;
+  if (!X || !gates || !ws) return LORA_ERR_INVALID_ARG;
+  const ApplyWs w = apply_layout(ws, ws_bytes, T, pool->d_in, pool->d_out, pool->dtype);
+  if (w.u_cap < 0) return LORA_ERR_CAPACITY;
+  const int64_t TK = int64_t(T) * K;
+  const PlanView pv = plan_view(plan, TK, pool->n_adapters);
+  const ShrinkArgs a = apply_shrink_args(X, keep_mask, keep_scale, T, K, gates, pool, pv, w);
+  return dev(launch_shrink(a, pool->dtype, TK, pool->n_adapters, pool->d_in, pool->d_out,
                            static_cast<hipStream_t>(stream)));
 }
 
@@ -214,6 +222,31 @@ int32_t lora_base_expand(const void *X, const void *W_t, void *Y, int32_t T, int
   return lora_expand_epilogue(X, W_t, Y, T, K, pool, plan, ws, ws_bytes, stream);
 }
 
+int32_t lora_shrink_gemm(const void *X, const void *W_t, void *Y, int32_t T, int32_t K,
+                         const float *gates, const uint8_t *keep_mask, float keep_scale,
+                         const lora_pool_desc *pool, const void *plan, void *ws,
+                         size_t ws_bytes, void *stream) {
+  GemmConfig cfg;
+  GemmArgs g;
+  int32_t st = base_args(X, W_t, Y, T, K, pool, plan, ws, ws_bytes, cfg, g);
+  if (st != LORA_OK || T == 0) return st;
+  if (!gates) return LORA_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const ApplyWs w = apply_layout(ws, ws_bytes, T, pool->d_in, pool->d_out, pool->dtype);
+  const int64_t TK = int64_t(T) * K;
+  const PlanView pv = plan_view(plan, TK, pool->n_adapters);
+  const ShrinkArgs a = apply_shrink_args(X, keep_mask, keep_scale, T, K, gates, pool, pv, w);
+  if (decode_shrink_fusable(cfg, pool->d_in)) {
+    hipError_t e = launch_shrink_big(a, pool->dtype, TK, pool->n_adapters, pool->d_in,
+                                     pool->d_out, s);
+    if (e == hipSuccess) e = launch_decode_gemm_shrink(cfg, g, a, s);
+    return dev(e);
+  }
+  hipError_t e = launch_shrink(a, pool->dtype, TK, pool->n_adapters, pool->d_in, pool->d_out, s);
+  if (e == hipSuccess) e = launch_base_gemm(cfg, g, s);
+  return dev(e);
+}
+
 int32_t lora_apply(const void *X, const void *W_t, void *Y, int32_t T, int32_t K,
                    const float *gates, const uint8_t *keep_mask,
                    float keep_scale, const lora_pool_desc *pool, const void *plan, void *ws,
@@ -222,9 +255,10 @@ int32_t lora_apply(const void *X, const void *W_t, void *Y, int32_t T, int32_t K
   if (st != LORA_OK) return st;
   if ((st = check_pool(pool, true)) != LORA_OK) return st;
   if (T > 0 && (!X || !W_t || !Y || !gates || !ws || !plan)) return LORA_ERR_INVALID_ARG;
-  st = lora_shrink(X, keep_mask, keep_scale, T, K, gates, pool, plan, ws, ws_bytes, stream);
+  st = lora_shrink_gemm(X, W_t, Y, T, K, gates, keep_mask, keep_scale, pool, plan, ws, ws_bytes,
+                        stream);
   if (st != LORA_OK) return st;
-  return lora_base_expand(X, W_t, Y, T, K, pool, plan, ws, ws_bytes, stream);
+  return lora_expand_epilogue(X, W_t, Y, T, K, pool, plan, ws, ws_bytes, stream);
 }
 
 int32_t lora_merge_delta(void *W_t, const lora_pool_desc *pool, const int32_t *merge_ids,
@@ -296,7 +330,7 @@ int32_t lora_grad(const void *X, const uint8_t *keep_mask, float keep_scale, con
   sa.rank = pool->rank; sa.page_start = pool->page_start; sa.page_ids = pool->page_ids;
   sa.scale = pool->scale; sa.gates = gates; sa.plan = pv; sa.err_word = err_word;
   sa.out = G; sa.out_cap = int64_t(TK) * max_rank;
-  hipError_t e = launch_shrink(sa, pool->dtype, TK, pool->n_adapters, max_rank, s);
+  hipError_t e = launch_shrink(sa, pool->dtype, TK, pool->n_adapters, pool->d_in, pool->d_out, s);
   if (e != hipSuccess) return LORA_ERR_DEVICE;
 
   SegOuterArgs ob{};

@@ -22,6 +22,7 @@
 //     and stores.  The reduction order is fixed: results are deterministic,
 //     and rows without active slots equal the base-only result bit for bit.
 #include "lora_internal.h"
+#include "shrink_units.h"
 
 namespace lora {
 namespace {
@@ -346,21 +347,25 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs g) {
 // and lanes 32-63 k = 32+8s..32+8s+7; the X fragments read from LDS use the
 // same permutation, so the sum is unchanged.  Partial sums of the K splits go
 // to the workspace for the epilogue kernel.
+constexpr int kDecodeKC = 512;   // K elements per decode workgroup
+
+// One decode tile: columns bx*128 .. +127, token rows by*32*MB .., K chunk bz.
+// xs: LDS of MB*32*kDecodeKC bf16 for the token rows.
 template <int MB>
-__global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
-  constexpr int KC = 512;
+__device__ __forceinline__ void decode_tile(const GemmArgs &g, int bx, int by, int bz,
+                                            uint16_t *xs) {
+  constexpr int KC = kDecodeKC;
   constexpr int NG = KC / 64;                 // 64-wide K groups
   constexpr int BMr = MB * 32;
   // One token row of the K chunk = 64 slots of 16 bytes.  Row r keeps chunk c
   // in slot c ^ (r & 7): the 8 rows a fragment read touches at once hit 8
   // different 16-byte bank groups.
-  __shared__ __attribute__((aligned(16))) uint16_t xs[BMr * KC];
   const uint16_t *X = static_cast<const uint16_t *>(g.X);
   const uint16_t *W = static_cast<const uint16_t *>(g.W);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n0 = blockIdx.x * 128 + wave * 32;
-  const int m0 = blockIdx.y * BMr;
-  const int k0 = blockIdx.z * KC;
+  const int n0 = bx * 128 + wave * 32;
+  const int m0 = by * BMr;
+  const int k0 = bz * KC;
   const int ng = min(NG, (g.Kd - k0) / 64);
   const int half = lane >> 5;
 
@@ -417,7 +422,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
       }
     }
   }
-  float *Pz = g.partial + int64_t(blockIdx.z) * g.M * g.N;
+  float *Pz = g.partial + int64_t(bz) * g.M * g.N;
   const int col = n0 + (lane & 31);
   if (col < g.N) {
 #pragma unroll
@@ -428,6 +433,32 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
         if (row < g.M) Pz[int64_t(row) * g.N + col] = acc[b][v];
       }
   }
+}
+
+template <int MB>
+__global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[MB * 32 * kDecodeKC];
+  decode_tile<MB>(g, blockIdx.x, blockIdx.y, blockIdx.z, xs);
+}
+
+// Decode GEMM and decode shrink in one launch.  Workgroups [0, n_gemm) are
+// GEMM tiles (bx fastest, then by, then bz); the others run the shrink
+// schedule, one schedule wave per wave, striding over all kShrinkWaves.  The
+// two halves stream disjoint HBM data (W, A pages) side by side and share
+// the token rows through L2, and the shrink no longer costs a launch of its
+// own on the decode critical path.
+template <int MB, bool kMask, int kCh>
+__global__ __launch_bounds__(256, 2) void decode_gemm_shrink_kernel(GemmArgs g, ShrinkArgs s,
+                                                                 int gx, int gy, int n_gemm) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[MB * 32 * kDecodeKC];
+  const int b = blockIdx.x;
+  if (b < n_gemm) {
+    decode_tile<MB>(g, b % gx, (b / gx) % gy, b / (gx * gy), xs);
+    return;
+  }
+  const int nsw = (int(gridDim.x) - n_gemm) * 4;
+  for (int w = (b - n_gemm) * 4 + (threadIdx.x >> 6); w < kShrinkWaves; w += nsw)
+    shrink_units_wave<uint16_t, kMask, kCh, true>(s, w);
 }
 
 // ------------------------------------------------------------ pipelined tile GEMM
@@ -932,6 +963,31 @@ hipError_t launch_base_gemm(const GemmConfig &c, const GemmArgs &g, hipStream_t 
   if (c.kind == 1) return launch_bf16<64, 128, 1, 4, false>(c, g, s);
   if (c.kind == 2) return launch_bf16<128, 128, 2, 2, false>(c, g, s);
   return launch_bf16<256, 128, 2, 2, true>(c, g, s);
+}
+
+bool decode_shrink_fusable(const GemmConfig &c, int d_in) {
+  return c.kind == 4 && d_in <= 8 * 512;
+}
+
+hipError_t launch_decode_gemm_shrink(const GemmConfig &c, const GemmArgs &g, const ShrinkArgs &sa,
+                                     hipStream_t st) {
+  const int gx = (g.N + 127) / 128, gy = (g.M + c.bm - 1) / c.bm;
+  const int n_gemm = gx * gy * c.splits;
+  // shrink workgroups: enough waves that each walks at most two runs of the
+  // schedule, and no more than the GEMM's own count (two workgroups per CU
+  // fit the 64 KiB of LDS each)
+  const int n_shr = kShrinkWaves / 8;
+  const dim3 grid(unsigned(n_gemm + n_shr)), block(256);
+  const bool m = sa.mask != nullptr;
+#define LORA_DGS(MB, M) \
+  hipLaunchKernelGGL((decode_gemm_shrink_kernel<MB, M, 8>), grid, block, 0, st, g, sa, gx, gy, n_gemm)
+#define LORA_DGS_M(MB) do { if (m) LORA_DGS(MB, true); else LORA_DGS(MB, false); } while (0)
+  if (c.bm == 32) LORA_DGS_M(1);
+  else if (c.bm == 64) LORA_DGS_M(2);
+  else LORA_DGS_M(4);
+#undef LORA_DGS_M
+#undef LORA_DGS
+  return hipGetLastError();
 }
 
 hipError_t launch_epilogue(const GemmConfig &c, const GemmArgs &g, int dtype, hipStream_t s) {

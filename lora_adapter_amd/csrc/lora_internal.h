@@ -14,6 +14,21 @@ constexpr int kPlanThreads = 1024;
 constexpr int kPlanLdsInts = 24576;               // LDS the plan kernel may use (96 KiB)
 constexpr int kGradPairChunk = 256;               // pairs per partial in the gradient reduction
 constexpr int kGradRankChunk = 16;                // rank rows per gradient register block
+constexpr int kBigSegPairs = 64;                  // segments this large may use the MFMA shrink
+constexpr int kShrinkRows = 2;                    // rank rows per decode-shrink unit
+constexpr int kShrinkWaves = 2048;                // waves of the decode shrink (its units split evenly)
+
+// Plan header words after the LORA_PH_* ones (scheduling data for the shrink).
+constexpr int kPhUnits = 8;          // decode-shrink units: sum over its segments of pairs x row groups
+constexpr int kPhUnitsPerWave = 9;   // units per wave of the decode shrink
+constexpr int kPhBig = 10;           // segments left to the MFMA shrink
+
+// Segments of at least kBigSegPairs pairs go to the MFMA shrink when the
+// operands are bf16, the batch is large and both projections' widths are
+// multiples of 128 (the MFMA shrink splits d over four waves in steps of 32).
+__host__ __device__ inline bool shrink_tile_enabled(int dtype, int64_t TK, int d_in, int d_out) {
+  return dtype == LORA_BF16 && TK >= 512 && d_in % 128 == 0 && d_out % 128 == 0;
+}
 
 // ----------------------------------------------------------------- bf16
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -70,6 +85,10 @@ __device__ __forceinline__ float wave_sum(float v) {
 struct PlanLayout {
   int64_t hdr, pair_tk, seg_adapter, seg_off, seg_row_off, bucket_seg_off, u_off, slot_pos;
   int64_t pair_adapter;
+  int64_t pair_gate;  // [T*K] float bits: gate of each sorted pair
+  int64_t seg_uoff;   // [S+1] first decode-shrink unit of each segment
+  int64_t wave_start; // [kShrinkWaves] x 8 ints: {seg, unit in seg, adapter, rank}, {page_start, pair_begin, pair_end, 0}
+  int64_t big_list;   // [1 + T*K/kBigSegPairs]: count, then the segments left to the MFMA shrink
   int64_t seg_desc;   // [S] x 8 ints: {adapter, rank, page_start, pair_begin, pair_end, u_begin, row_begin, 0}
   int64_t slot_desc;  // [T*K] x 4 ints: {pair or -1, rank, u_off, page_start}
   int64_t cnt, ubias, cur, ps, inf;  // per-adapter scratch (pools too big for LDS)
@@ -107,6 +126,10 @@ __host__ __device__ inline PlanLayout plan_layout(int64_t TK, int64_t N) {
   L.u_off = o;          o = align16(o + TK + 1);
   L.slot_pos = o;       o = align16(o + TK);
   L.pair_adapter = o;   o = align16(o + TK);
+  L.pair_gate = o;      o = align16(o + TK);
+  L.seg_uoff = o;       o = align16(o + TK + 1);
+  L.wave_start = o;     o = align16(o + 8 * kShrinkWaves);
+  L.big_list = o;       o = align16(o + 1 + TK / kBigSegPairs + 1);
   L.seg_desc = o;       o = align16(o + 8 * TK);
   L.slot_desc = o;      o = align16(o + 4 * TK);
   L.cnt = o;            o = align16(o + N);
@@ -125,6 +148,9 @@ struct PlanView {
   const int32_t *pair_adapter;
   const int4 *seg_desc;    // two int4 per segment
   const int4 *slot_desc;   // one int4 per slot
+  const float *pair_gate;  // gate of each sorted pair
+  const int4 *wave_start;  // two int4 per decode-shrink wave
+  const int32_t *big_list; // count, then segment ids
 };
 
 inline PlanView plan_view(const void *plan, int64_t TK, int64_t N) {
@@ -133,7 +159,9 @@ inline PlanView plan_view(const void *plan, int64_t TK, int64_t N) {
   return PlanView{b + L.hdr, b + L.pair_tk, b + L.seg_adapter, b + L.seg_off,
                   b + L.seg_row_off, b + L.u_off, b + L.slot_pos, b + L.pair_adapter,
                   reinterpret_cast<const int4 *>(b + L.seg_desc),
-                  reinterpret_cast<const int4 *>(b + L.slot_desc)};
+                  reinterpret_cast<const int4 *>(b + L.slot_desc),
+                  reinterpret_cast<const float *>(b + L.pair_gate),
+                  reinterpret_cast<const int4 *>(b + L.wave_start), b + L.big_list};
 }
 
 // Device view of an adapter pool.
@@ -142,20 +170,21 @@ struct PoolView {
   const int32_t *rank, *page_start, *page_ids;
   const float *scale;
   int64_t n_pages, n_page_ids;
-  int d_in, d_out, n_adapters;
+  int d_in, d_out, n_adapters, dtype;
 };
 
 inline PoolView pool_view(const lora_pool_desc *p) {
   return PoolView{p->a_pages, p->b_pages, p->rank, p->page_start, p->page_ids, p->scale,
-                  p->n_pages, p->n_page_ids, p->d_in, p->d_out, p->n_adapters};
+                  p->n_pages, p->n_page_ids, p->d_in, p->d_out, p->n_adapters, p->dtype};
 }
 
 // ----------------------------------------------------------------- kernel arguments
 
 // Segmented shrink: out[u_off[p] + j] = coef_p * sum_i Z[t_p][i] (m[t_p][i]) page_j[i]
 // for every planned pair p and rank row j of its adapter, with coef_p =
-// gates[t_p][k_p] * scale[a] * extra_scale.  Used for the LoRA down projection
-// (Z = X, pages = A) and for the gradient's dY.B^T (Z = dY, pages = B).
+// gate_p * (scale[a] * extra_scale) (gate_p as recorded by the plan).  Used for
+// the LoRA down projection (Z = X, pages = A) and for the gradient's dY.B^T
+// (Z = dY, pages = B).
 struct ShrinkArgs {
   const void *Z;            // [T][d] activations
   const uint8_t *mask;      // [T][d] 0/1 or null
@@ -170,6 +199,7 @@ struct ShrinkArgs {
   float *out;
   int64_t out_cap;          // capacity of out in floats
   int big_segments;         // set by the launcher: large segments go to the MFMA tile kernel
+                            // (the plan made the same choice from the same predicate)
 };
 
 // Everything the expand needs to add sum_j U[u_off[p]+j] * B_a[j][n] to row t.
@@ -234,9 +264,10 @@ struct SegOuterArgs {
 // Each returns hipSuccess or the launch error.
 hipError_t launch_plan(const int32_t *ids, const float *gates, int T, int K, const PoolView &pool,
                        int32_t *plan, hipStream_t s);
-// max_rank bounds the rank of every adapter the plan can hold segments for.
+// d_in and d_out of the pool decide, with dtype and T*K, whether the MFMA
+// shrink takes the big segments (shrink_tile_enabled, as in the plan).
 hipError_t launch_shrink(const ShrinkArgs &a, int dtype, int64_t TK, int64_t n_adapters,
-                         int max_rank, hipStream_t s);
+                         int d_in, int d_out, hipStream_t s);
 
 // Base GEMM configuration chosen from the shape (host-side, deterministic).
 struct GemmConfig {
@@ -250,6 +281,17 @@ GemmConfig choose_gemm(int T, int d_in, int d_out, int dtype);
 size_t gemm_partial_bytes(const GemmConfig &c, int T, int d_out);
 hipError_t launch_base_gemm(const GemmConfig &c, const GemmArgs &g, hipStream_t s);
 hipError_t launch_epilogue(const GemmConfig &c, const GemmArgs &g, int dtype, hipStream_t s);
+// The decode GEMM (kind 4) can run the decode shrink in the same launch when
+// d_in <= 4096 (the shrink's rank rows then stay in registers within the
+// register budget of two workgroups per CU).
+bool decode_shrink_fusable(const GemmConfig &c, int d_in);
+// Decode GEMM + decode shrink (the big-segment MFMA shrink, if enabled, is
+// launched separately by the caller).
+hipError_t launch_decode_gemm_shrink(const GemmConfig &c, const GemmArgs &g, const ShrinkArgs &sa,
+                                     hipStream_t s);
+// The MFMA shrink of the big segments alone (no-op unless enabled).
+hipError_t launch_shrink_big(const ShrinkArgs &a, int dtype, int64_t TK, int64_t n_adapters,
+                             int d_in, int d_out, hipStream_t s);
 
 hipError_t launch_merge(const MergeArgs &a, int dtype, hipStream_t s);
 int64_t grad_pieces(int64_t TK, int64_t n_adapters);

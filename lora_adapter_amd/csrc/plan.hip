@@ -55,6 +55,7 @@ struct PlanArgs {
   int64_t n_pages, n_page_ids;
   int32_t *plan;
   int slot_cache;    // 1: per-slot adapters cached in LDS
+  int use_tile;      // 1: segments of >= kBigSegPairs pairs go to the MFMA shrink
 };
 
 __device__ __forceinline__ int rank_bucket(int r) {
@@ -105,32 +106,33 @@ __device__ __forceinline__ int wave_scan_incl(int v) {
   return v;
 }
 
-struct Scan4 {
-  int v[4];
+template <int NV>
+struct ScanV {
+  int v[NV];
 };
 
-// Exclusive block scan of four ints over the workgroup; also the totals.
+// Exclusive block scan of NV ints over the workgroup; also the totals.
 // Wave totals go through LDS once; every wave then scans the (at most 16)
 // totals in its lanes.
-template <bool kLds>
-__device__ Scan4 block_exclusive_scan4(Scan4 x, Scan4 &total, int *lds_tot /* [16*4] */) {
+template <bool kLds, int NV>
+__device__ ScanV<NV> block_exclusive_scan(ScanV<NV> x, ScanV<NV> &total, int *lds_tot /* [16*NV] */) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwv = blockDim.x >> 6;
-  Scan4 inc;
+  ScanV<NV> inc;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) inc.v[q] = wave_scan_incl(x.v[q]);
+  for (int q = 0; q < NV; ++q) inc.v[q] = wave_scan_incl(x.v[q]);
   if (lane == 63) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) lds_tot[wave * 4 + q] = inc.v[q];
+    for (int q = 0; q < NV; ++q) lds_tot[wave * NV + q] = inc.v[q];
   }
   bar<kLds>();
-  int tw[4];
+  int tw[NV];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) tw[q] = lds_tot[min(lane, nwv - 1) * 4 + q];
-  Scan4 ex;
+  for (int q = 0; q < NV; ++q) tw[q] = lds_tot[min(lane, nwv - 1) * NV + q];
+  ScanV<NV> ex;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < NV; ++q) {
     const int t = lane < nwv ? tw[q] : 0;
     const int ti = wave_scan_incl(t);
     const int before = __builtin_amdgcn_readlane(ti - t, wave);
@@ -156,11 +158,12 @@ __device__ __forceinline__ uint64_t match_lanes(int a, int nbits) {
 // Loads in flight per thread in the adapter and page-id passes.
 constexpr int kAdBatch = 4;
 constexpr int kRowBatch = 12;
+constexpr int kWsBatch = 8;
 
 template <bool kLds>
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   extern __shared__ int dyn[];
-  __shared__ int lds_tot[kMaxWaves * 4];
+  __shared__ int lds_tot[kMaxWaves * 5];
   __shared__ int s_wcnt[kLds ? LORA_N_BUCKETS * kLdsCountCols : 1];
   __shared__ int s_btot[LORA_N_BUCKETS];
   __shared__ int s_err, s_bmask, s_bad;
@@ -185,9 +188,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   // segment arrays (outputs; LDS copies when they fit)
   int *seg_row = kLds ? dyn + 5 * N : P + L.seg_row_off;
   int *seg_ad = kLds ? dyn + 5 * N + Smax + 1 : P + L.seg_adapter;
-  // seg_pb[s] = page_start of segment s's adapter minus its first rank row
-  int *seg_pb = dyn + 5 * N + 2 * Smax + 1;   // LDS case only
-  int *slot_ad = dyn + (kLds ? 5 * N + 3 * Smax + 1 : 0);
+  // LDS case only: seg_pgb[s] = page_start of segment s's adapter minus its
+  // first rank row; seg_pp[s] = its first pair (copy of the seg_off output)
+  int *seg_pgb = dyn + 5 * N + 2 * Smax + 1;
+  int *seg_pp = dyn + 5 * N + 3 * Smax + 1;
+  // first decode-shrink unit of each segment
+  int *seg_uo = kLds ? dyn + 5 * N + 4 * Smax + 2 : P + L.seg_uoff;
+  int *slot_ad = dyn + (kLds ? 5 * N + 5 * Smax + 3 : 0);
   // counts of used adapters per (bucket, round of nt adapters, wave)
   const int Q = (N + nt - 1) / nt;
   const int E = Q * nwv;
@@ -271,7 +278,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   bar<kLds>();
 
   // 3. segment order (redone once if step 4 drops an adapter)
-  int S = 0, pair_base = 0, u_base = 0, row_base = 0;
+  int S = 0, pair_base = 0, u_base = 0, row_base = 0, n_units = 0, n_big = 0;
   for (int pass = 0; pass < 2; ++pass) {
     const int bmask = s_bmask;
     // (a) used adapters per (bucket, round, wave)
@@ -327,45 +334,63 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       }
     }
     bar<kLds>();
-    // (d) pair, U and rank-row offsets of the segments (contiguous blocks per thread)
+    // (d) pair, U, rank-row and decode-shrink-unit offsets of the segments
+    //     (contiguous blocks per thread), and the list of big segments
     const int ms = (S + nt - 1) / nt;
     const int g0 = min(S, tid * ms), g1 = min(S, g0 + ms);
-    Scan4 x{{0, 0, 0, 0}};
+    ScanV<5> x{{0, 0, 0, 0, 0}};
     for (int sg = g0; sg < g1; ++sg) {
       const int ad = seg_ad[sg];
       const int c = ld_ctr(&cnt[ad]);
       const int r = inf[ad] & kInfRankMask;
+      const bool big = a.use_tile && c >= kBigSegPairs;
       x.v[0] += c; x.v[1] += c * r; x.v[2] += r;
+      x.v[3] += big ? 0 : c * ((r + kShrinkRows - 1) / kShrinkRows);
+      x.v[4] += big ? 1 : 0;
     }
-    Scan4 tot;
-    const Scan4 ex = block_exclusive_scan4<kLds>(x, tot, lds_tot);
-    int st = ex.v[0], ub = ex.v[1], rb = ex.v[2];
+    ScanV<5> tot;
+    const ScanV<5> ex = block_exclusive_scan<kLds, 5>(x, tot, lds_tot);
+    int st = ex.v[0], ub = ex.v[1], rb = ex.v[2], uo = ex.v[3], bi = ex.v[4];
     for (int sg = g0; sg < g1; ++sg) {
       const int ad = seg_ad[sg];
       const int c = ld_ctr(&cnt[ad]);
       const int r = inf[ad] & kInfRankMask;
+      const bool big = a.use_tile && c >= kBigSegPairs;
       ubias[ad] = ub - st * r;
       st_ctr(&cur[ad], st);
       seg_row[sg] = rb;
-      if (kLds) seg_pb[sg] = psa[ad] - rb;
+      seg_uo[sg] = uo;
       if (kLds) {
+        seg_pgb[sg] = psa[ad] - rb;
+        seg_pp[sg] = st;
         P[L.seg_adapter + sg] = ad;
         P[L.seg_row_off + sg] = rb;
+        P[L.seg_uoff + sg] = uo;
       }
+      if (big) P[L.big_list + 1 + bi] = sg;
       P[L.seg_off + sg] = st;
       int4 *d = reinterpret_cast<int4 *>(P + L.seg_desc) + 2 * sg;
       d[0] = make_int4(ad, r, psa[ad], st);
-      d[1] = make_int4(st + c, ub, rb, 0);
-      st += c; ub += c * r; rb += r;
+      d[1] = make_int4(st + c, ub, rb, uo);
+      st += c; ub += c * r; rb += r; bi += big ? 1 : 0;
+      uo += big ? 0 : c * ((r + kShrinkRows - 1) / kShrinkRows);
     }
     pair_base = tot.v[0];
     u_base = tot.v[1];
     row_base = tot.v[2];
+    n_units = tot.v[3];
+    n_big = tot.v[4];
     if (tid == 0) {
       P[L.seg_off + S] = pair_base;
       seg_row[S] = row_base;
-      if (kLds) P[L.seg_row_off + S] = row_base;
+      seg_uo[S] = n_units;
+      if (kLds) {
+        P[L.seg_row_off + S] = row_base;
+        P[L.seg_uoff + S] = n_units;
+        seg_pp[S] = pair_base;
+      }
       P[L.u_off + pair_base] = u_base;
+      P[L.big_list] = n_big;
     }
     bar<kLds>();
     if (pass == 1) break;
@@ -396,7 +421,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       if constexpr (kLds) {
 #pragma unroll
         for (int q = 0; q < kRowBatch; ++q)
-          if (q < nq) pix[q] = seg_pb[lo[q]] + gq[q];
+          if (q < nq) pix[q] = seg_pgb[lo[q]] + gq[q];
       } else {
 #pragma unroll
         for (int q = 0; q < kRowBatch; ++q)
@@ -430,6 +455,52 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     bar<kLds>();
   }
 
+  // 4b. decode-shrink schedule: its units (pairs x groups of kShrinkRows rank
+  //     rows, over the segments it handles) split into equal runs, one per
+  //     wave; each working wave's first segment and unit, with that
+  //     segment's descriptor, so that a shrink wave starts with one load.
+  //     Runs are found kWsBatch at a time by binary lifting over the
+  //     segments' first units (seg_uo[S] = n_units exceeds every unit).
+  {
+    const int upw = max(1, (n_units + kShrinkWaves - 1) / kShrinkWaves);
+    const int n_active = (n_units + upw - 1) / upw;       // <= kShrinkWaves
+    int top = 1;
+    while (top * 2 <= S) top *= 2;
+    int4 *ws = reinterpret_cast<int4 *>(P + L.wave_start);
+    for (int w0 = 0; w0 < n_active; w0 += nt * kWsBatch) {
+      int lo[kWsBatch], uq[kWsBatch];
+#pragma unroll
+      for (int q = 0; q < kWsBatch; ++q) {
+        uq[q] = min(w0 + q * nt + tid, n_active - 1) * upw;
+        lo[q] = 0;
+      }
+      for (int step = top; step > 0; step >>= 1) {
+        int rc[kWsBatch];
+#pragma unroll
+        for (int q = 0; q < kWsBatch; ++q) rc[q] = seg_uo[min(lo[q] + step, S)];
+#pragma unroll
+        for (int q = 0; q < kWsBatch; ++q) lo[q] = rc[q] <= uq[q] ? min(lo[q] + step, S) : lo[q];
+      }
+#pragma unroll
+      for (int q = 0; q < kWsBatch; ++q) {
+        const int w = w0 + q * nt + tid;
+        if (w < n_active) {
+          const int sg = lo[q];
+          const int ad = seg_ad[sg];
+          const int pb = kLds ? seg_pp[sg] : P[L.seg_off + sg];
+          const int pe = kLds ? seg_pp[sg + 1] : P[L.seg_off + sg + 1];
+          ws[2 * w] = make_int4(sg, uq[q] - seg_uo[sg], ad, inf[ad] & kInfRankMask);
+          ws[2 * w + 1] = make_int4(psa[ad], pb, pe, 0);
+        }
+      }
+    }
+    if (tid == 0) {
+      P[L.hdr + kPhUnits] = n_units;
+      P[L.hdr + kPhUnitsPerWave] = upw;
+      P[L.hdr + kPhBig] = n_big;
+    }
+  }
+
   // 5. ordered placement: within each nt-slot chunk the waves holding slots
   //    take positions from the adapter cursors in wave order (stable sort)
   int4 *slot_desc = reinterpret_cast<int4 *>(P + L.slot_desc);
@@ -448,6 +519,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       }
       if (ad >= 0 && ld_ctr(&cnt[ad]) <= 0) ad = -1;
     }
+    const float gate = base == 0 ? g_pre : (i < TK ? a.gates[i] : 0.0f);
     const uint64_t mm = match_lanes(ad, nbits);
     const int rank_in_wave = __popcll(mm & lt_mask);
     const int leader = mm ? __ffsll((unsigned long long)mm) - 1 : lane;
@@ -470,6 +542,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         const int uo = ubias[ad] + pos * r;
         P[L.pair_tk + pos] = int32_t(i);
         P[L.pair_adapter + pos] = ad;
+        P[L.pair_gate + pos] = __float_as_int(gate);
         P[L.u_off + pos] = uo;
         slot_desc[i] = make_int4(pos, r, uo, psa[ad]);
       } else {
@@ -488,7 +561,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     h[LORA_PH_T] = a.T;
     h[LORA_PH_K] = a.K;
     h[LORA_PH_N] = N;
-    for (int q = 8; q < LORA_PLAN_HEADER_INTS; ++q) h[q] = 0;
+    for (int q = kPhBig + 1; q < LORA_PLAN_HEADER_INTS; ++q) h[q] = 0;
     for (int q = LORA_N_BUCKETS + 1; q < 16; ++q) P[L.bucket_seg_off + q] = 0;
   }
 }
@@ -501,9 +574,10 @@ hipError_t launch_plan(const int32_t *ids, const float *gates, int T, int K, con
   const int64_t N = pool.n_adapters;
   const int64_t Smax = TK < N ? TK : N;
   PlanArgs a{ids, gates, T, K, pool.n_adapters, pool.rank, pool.page_start, pool.page_ids,
-             pool.n_pages, pool.n_page_ids, plan, 0};
+             pool.n_pages, pool.n_page_ids, plan, 0,
+             shrink_tile_enabled(pool.dtype, TK, pool.d_in, pool.d_out) ? 1 : 0};
   const int nt = plan_threads(TK, N);
-  const int64_t adapter_ints = 5 * N + 3 * Smax + 1;
+  const int64_t adapter_ints = 5 * N + 5 * Smax + 3;
   const int64_t count_cols = (N + nt - 1) / nt * (nt / 64);
   if (adapter_ints <= kPlanLdsInts && count_cols <= kLdsCountCols) {
     a.slot_cache = adapter_ints + TK <= kPlanLdsInts ? 1 : 0;

@@ -11,27 +11,23 @@
 // contiguously as one page of the pool).
 //
 // Two kernels, split by segment size:
-//   * rows kernel (segments with fewer than kBigSeg pairs, i.e. decode):
-//     one wave per (segment, 4 rank rows).  It reads the segment's packed
-//     descriptor (adapter, rank, page_start, pair range), streams its A pages
-//     from HBM with 16-byte coalesced loads and dots them with each token row
-//     of the segment (rows are small and shared, so they come from L2).
-//   * tile kernel (segments with kBigSeg pairs or more, i.e. prefill):
-//     an MFMA tile of 16 tokens x 16 rank rows (v_mfma_f32_16x16x32_bf16),
-//     token rows and A pages read straight from global memory as MFMA
-//     fragments, the dropout mask applied to the bf16 fragment (exact), the
-//     four waves of a workgroup splitting d and adding through LDS.  X is
-//     read once from HBM per rank-row block.
+//   * units kernel (every segment, except those the tile kernel takes): a
+//     persistent grid of kShrinkWaves waves over the plan's unit schedule
+//     (see shrink_units_kernel); A pages stream from HBM with 16-byte
+//     coalesced loads, token rows come from L2.
+//   * tile kernel (segments of kBigSegPairs pairs or more, bf16, large
+//     batches, i.e. prefill): an MFMA tile of 16 tokens x 16 rank rows
+//     (v_mfma_f32_16x16x32_bf16), token rows and A pages read straight from
+//     global memory as MFMA fragments, the dropout mask applied to the bf16
+//     fragment (exact), the four waves of a workgroup splitting d and adding
+//     through LDS.  X is read once from HBM per rank-row block.
 // The same kernels compute the gradient's dY.B^T (Z = dY, pages = B).
 #include "lora_internal.h"
+#include "shrink_units.h"
 
 namespace lora {
 namespace {
 
-constexpr int kRowsPerWave = 2;     // rank rows per wave in the rows kernel
-constexpr int kPairsPerPass = 2;    // token rows per pass
-constexpr int kChunks = 8;          // 16-byte chunks per lane issued together (4096 bf16)
-constexpr int kBigSeg = 64;         // segments this large use the tile kernel
 constexpr int kTileTok = 16;        // tokens per MFMA tile
 constexpr int kTileRank = 16;       // rank rows per MFMA tile
 
@@ -44,169 +40,21 @@ __device__ __forceinline__ bool capacity_ok(const ShrinkArgs &s) {
   return false;
 }
 
-// 8 consecutive elements held raw until they are needed (so that a batch of
-// loads can be issued before the first conversion waits on one).
-template <typename E> struct Raw;
-template <> struct Raw<uint16_t> {
-  uint4 v;
-  __device__ __forceinline__ void load(const uint16_t *p) { v = *reinterpret_cast<const uint4 *>(p); }
-  __device__ __forceinline__ void to8(float o[8]) const {
-    o[0] = bf_lo(v.x); o[1] = bf_hi(v.x); o[2] = bf_lo(v.y); o[3] = bf_hi(v.y);
-    o[4] = bf_lo(v.z); o[5] = bf_hi(v.z); o[6] = bf_lo(v.w); o[7] = bf_hi(v.w);
-  }
-};
-template <> struct Raw<float> {
-  float4 a, b;
-  __device__ __forceinline__ void load(const float *p) {
-    a = *reinterpret_cast<const float4 *>(p);
-    b = *reinterpret_cast<const float4 *>(p + 4);
-  }
-  __device__ __forceinline__ void to8(float o[8]) const {
-    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
-  }
-};
-
-// Zero the elements of 8 gathered values whose keep-mask byte is 0.
-__device__ __forceinline__ void apply_mask8(float v[8], uint2 mb) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    if (((mb.x >> (8 * e)) & 0xffu) == 0) v[e] = 0.f;
-    if (((mb.y >> (8 * e)) & 0xffu) == 0) v[4 + e] = 0.f;
-  }
+// Standalone decode shrink: one 64-lane workgroup per wave of the schedule.
+template <typename E, bool kMask, int kCh, bool kResident>
+__global__ __launch_bounds__(64) void shrink_units_kernel(ShrinkArgs s) {
+  shrink_units_wave<E, kMask, kCh, kResident>(s, blockIdx.x);
 }
 
-// Control data is fetched lane-parallel (one lane per word, one instruction
-// per round trip) and broadcast with shuffles: a decode segment costs three
-// dependent round trips (descriptor, page and token ids, then A and X).
-template <typename E, bool kMask>
-__global__ __launch_bounds__(64) void shrink_rows_kernel(ShrinkArgs s) {
-  const int seg = blockIdx.x;
-  const int lane = threadIdx.x;
-  // round trip 1: segment descriptor (lanes 0-7) and header words (lanes 8, 9);
-  // seg < grid size <= T*K keeps the descriptor read in bounds
-  int w = 0;
-  if (lane < 8) w = reinterpret_cast<const int *>(s.plan.seg_desc)[8 * seg + lane];
-  else if (lane == 8) w = s.plan.hdr[LORA_PH_SEGS];
-  else if (lane == 9) w = s.plan.hdr[LORA_PH_RPAIRS];
-  if (seg >= __shfl(w, 8, 64)) return;
-  if (int64_t(__shfl(w, 9, 64)) > s.out_cap) {
-    if (seg == 0 && blockIdx.y == 0 && lane == 0) atomicOr(s.err_word, LORA_DEVERR_CAPACITY);
-    return;
-  }
-  const int ad = __shfl(w, 0, 64), r = __shfl(w, 1, 64), ps = __shfl(w, 2, 64);
-  const int pb = __shfl(w, 3, 64), pe = __shfl(w, 4, 64);
-  if (pe - pb >= kBigSeg && s.big_segments) return;
-  const int d = s.d;
-  const E *Z = static_cast<const E *>(s.Z);
-  const E *pages = static_cast<const E *>(s.pages);
-  for (int j0 = blockIdx.y * kRowsPerWave; j0 < r; j0 += gridDim.y * kRowsPerWave) {
-  const int nr = min(kRowsPerWave, r - j0);
-  // round trip 2: page ids (lanes 0-3) and the adapter scale (lane 4)
-  int pw = 0;
-  float scw = 0.f;
-  if (lane < kRowsPerWave) pw = s.page_ids[ps + j0 + min(lane, nr - 1)];
-  else if (lane == kRowsPerWave) scw = s.scale[ad];
-  const float sc = __shfl(scw, kRowsPerWave, 64) * s.extra_scale;
-  const E *arow[kRowsPerWave];
-#pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) arow[i] = pages + int64_t(__shfl(pw, i, 64)) * d;
-
-  for (int q = pb; q < pe; q += kPairsPerPass) {
-    const int nq = min(kPairsPerPass, pe - q);
-    // token of each pair (lanes 0-3), then each lane's own gate and U offset
-    int tkl = 0;
-    if (lane < kPairsPerPass) tkl = s.plan.pair_tk[q + min(lane, nq - 1)];
-    float gate = 0.f;
-    int uoff = 0;
-    if (lane < nq) {
-      gate = s.gates[tkl];
-      uoff = s.plan.u_off[q + lane];
-    }
-    int tk[kPairsPerPass];
-    const E *zr[kPairsPerPass];
-    const uint8_t *mr[kPairsPerPass];
-#pragma unroll
-    for (int i = 0; i < kPairsPerPass; ++i) {
-      tk[i] = __shfl(tkl, i, 64);
-      const int64_t t = tk[i] / s.K;
-      zr[i] = Z + t * d;
-      mr[i] = kMask ? s.mask + t * d : nullptr;
-    }
-    float acc[kRowsPerWave][kPairsPerPass];
-#pragma unroll
-    for (int a = 0; a < kRowsPerWave; ++a)
-#pragma unroll
-      for (int i = 0; i < kPairsPerPass; ++i) acc[a][i] = 0.f;
-    // Blocks of kChunks x 512 elements: every load of a block is issued
-    // before any is used, from clamped addresses (rows past nr / pairs past nq
-    // repeat the last valid one and are never written; chunks past d repeat
-    // the last chunk and are skipped below), so no load waits on a branch.
-    for (int cb = 0; cb < d; cb += kChunks * 512) {
-      Raw<E> ar[kRowsPerWave][kChunks], zrw[kPairsPerPass][kChunks];
-      uint2 mk[kPairsPerPass][kChunks];
-#pragma unroll
-      for (int ch = 0; ch < kChunks; ++ch) {
-        const int c = min(cb + ch * 512 + lane * 8, d - 8);
-#pragma unroll
-        for (int a = 0; a < kRowsPerWave; ++a) ar[a][ch].load(arow[a] + c);
-#pragma unroll
-        for (int i = 0; i < kPairsPerPass; ++i) {
-          zrw[i][ch].load(zr[i] + c);
-          if (kMask) mk[i][ch] = *reinterpret_cast<const uint2 *>(mr[i] + c);
-        }
-      }
-#pragma unroll
-      for (int ch = 0; ch < kChunks; ++ch) {
-        if (cb + ch * 512 + lane * 8 >= d) continue;
-        float av[kRowsPerWave][8];
-#pragma unroll
-        for (int a = 0; a < kRowsPerWave; ++a) ar[a][ch].to8(av[a]);
-#pragma unroll
-        for (int i = 0; i < kPairsPerPass; ++i) {
-          float zv[8];
-          zrw[i][ch].to8(zv);
-          if (kMask) apply_mask8(zv, mk[i][ch]);
-#pragma unroll
-          for (int a = 0; a < kRowsPerWave; ++a)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[a][i] = fmaf(zv[e], av[a][e], acc[a][i]);
-        }
-      }
-    }
-#pragma unroll
-    for (int a = 0; a < kRowsPerWave; ++a)
-#pragma unroll
-      for (int i = 0; i < kPairsPerPass; ++i) acc[a][i] = wave_sum(acc[a][i]);
-    if (lane < nq) {
-      // lane i writes pair q + i; select its sums without dynamic indexing
-      float mine[kRowsPerWave];
-#pragma unroll
-      for (int a = 0; a < kRowsPerWave; ++a) {
-        mine[a] = acc[a][0];
-#pragma unroll
-        for (int i = 1; i < kPairsPerPass; ++i)
-          if (lane == i) mine[a] = acc[a][i];
-      }
-      const float coef = gate * sc;
-      float *o = s.out + uoff + j0;
-#pragma unroll
-      for (int a = 0; a < kRowsPerWave; ++a)
-        if (a < nr) o[a] = coef * mine[a];
-    }
-  }
-  }  // rank-row groups
-}
-
-// bf16 only: MFMA operands are bf16.
+// One workgroup per (segment of the plan's big list, 16 of its pairs).
 template <bool kMask>
 __global__ __launch_bounds__(256) void shrink_tile_kernel(ShrinkArgs s) {
-  const int seg = blockIdx.x;
-  if (seg >= s.plan.hdr[LORA_PH_SEGS]) return;
+  if (int(blockIdx.x) >= s.plan.big_list[0]) return;
   if (!capacity_ok(s)) return;
+  const int seg = s.plan.big_list[1 + blockIdx.x];
   const int4 d0 = s.plan.seg_desc[2 * seg];
   const int4 d1 = s.plan.seg_desc[2 * seg + 1];
   const int ad = d0.x, r = d0.y, ps = d0.z, pb = d0.w, pe = d1.x;
-  if (pe - pb < kBigSeg) return;
   const int q0 = pb + blockIdx.y * kTileTok;
   if (q0 >= pe) return;
   const int nq = min(kTileTok, pe - q0);
@@ -268,7 +116,7 @@ __global__ __launch_bounds__(256) void shrink_tile_kernel(ShrinkArgs s) {
           const int tr = (lane >> 4) * 4 + i;
           if (tr < nq) {
             const int p = q0 + tr;
-            s.out[s.plan.u_off[p] + j] = s.gates[s.plan.pair_tk[p]] * sc * v[i];
+            s.out[s.plan.u_off[p] + j] = s.plan.pair_gate[p] * sc * v[i];
           }
         }
       }
@@ -280,24 +128,46 @@ __global__ __launch_bounds__(256) void shrink_tile_kernel(ShrinkArgs s) {
 }  // namespace
 
 hipError_t launch_shrink(const ShrinkArgs &a, int dtype, int64_t TK, int64_t n_adapters,
-                         int max_rank, hipStream_t st) {
+                         int d_in, int d_out, hipStream_t st) {
   const int64_t segs = TK < n_adapters ? TK : n_adapters;
   if (segs <= 0) return hipSuccess;
-  const unsigned gx = unsigned(segs);
-  const unsigned gy = unsigned((max_rank + kRowsPerWave - 1) / kRowsPerWave);
-  const dim3 grid{gx, gy > 0 ? gy : 1u, 1}, block{64, 1, 1};
   ShrinkArgs s = a;
-  s.big_segments = (dtype == LORA_BF16 && TK >= 512 && s.d % 128 == 0) ? 1 : 0;
+  s.big_segments = shrink_tile_enabled(dtype, TK, d_in, d_out) ? 1 : 0;
+  const dim3 grid{unsigned(kShrinkWaves), 1, 1}, block{64, 1, 1};
+#define LORA_SHRINK_UNITS(E, M, CH, RES) \
+  hipLaunchKernelGGL((shrink_units_kernel<E, M, CH, RES>), grid, block, 0, st, s)
+  const int d = s.d;
   if (dtype == LORA_BF16) {
-    if (s.mask) hipLaunchKernelGGL((shrink_rows_kernel<uint16_t, true>), grid, block, 0, st, s);
-    else hipLaunchKernelGGL((shrink_rows_kernel<uint16_t, false>), grid, block, 0, st, s);
+    if (d <= 8 * 512) {
+      if (s.mask) LORA_SHRINK_UNITS(uint16_t, true, 8, true); else LORA_SHRINK_UNITS(uint16_t, false, 8, true);
+    } else if (d <= 12 * 512) {
+      if (s.mask) LORA_SHRINK_UNITS(uint16_t, true, 12, true); else LORA_SHRINK_UNITS(uint16_t, false, 12, true);
+    } else {
+      if (s.mask) LORA_SHRINK_UNITS(uint16_t, true, 8, false); else LORA_SHRINK_UNITS(uint16_t, false, 8, false);
+    }
   } else {
-    if (s.mask) hipLaunchKernelGGL((shrink_rows_kernel<float, true>), grid, block, 0, st, s);
-    else hipLaunchKernelGGL((shrink_rows_kernel<float, false>), grid, block, 0, st, s);
+    // fp32: 8 elements are 32 bytes, two loads per chunk
+    if (d <= 4 * 512) {
+      if (s.mask) LORA_SHRINK_UNITS(float, true, 4, true); else LORA_SHRINK_UNITS(float, false, 4, true);
+    } else {
+      if (s.mask) LORA_SHRINK_UNITS(float, true, 4, false); else LORA_SHRINK_UNITS(float, false, 4, false);
+    }
   }
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || !s.big_segments) return err;
-  const dim3 g2{gx, unsigned((TK + kTileTok - 1) / kTileTok), 1}, b2{256, 1, 1};
+#undef LORA_SHRINK_UNITS
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_shrink_big(s, dtype, TK, n_adapters, d_in, d_out, st);
+}
+
+hipError_t launch_shrink_big(const ShrinkArgs &a, int dtype, int64_t TK, int64_t n_adapters,
+                             int d_in, int d_out, hipStream_t st) {
+  if (!shrink_tile_enabled(dtype, TK, d_in, d_out)) return hipSuccess;
+  ShrinkArgs s = a;
+  s.big_segments = 1;
+  // big segments: at most T*K / kBigSegPairs of them, each at most T*K pairs
+  const int64_t segs = TK < n_adapters ? TK : n_adapters;
+  const int64_t nbig = TK / kBigSegPairs < segs ? TK / kBigSegPairs : segs;
+  const dim3 g2{unsigned(nbig > 0 ? nbig : 1), unsigned((TK + kTileTok - 1) / kTileTok), 1}, b2{256, 1, 1};
   if (s.mask) hipLaunchKernelGGL((shrink_tile_kernel<true>), g2, b2, 0, st, s);
   else hipLaunchKernelGGL((shrink_tile_kernel<false>), g2, b2, 0, st, s);
   return hipGetLastError();

@@ -245,6 +245,24 @@ def test_repeated_runs_are_bitwise_identical(cfg):
     assert np.array_equal(Y1, L.Y_host())
 
 
+@pytest.mark.parametrize("cfg", ["small2", "small3", "small5", "full2"])
+def test_split_and_fused_entry_points_agree(cfg):
+    """lora_apply runs the decode shrink inside the decode GEMM launch; the
+    separate entry points (lora_shrink, lora_base_gemm, lora_expand_epilogue)
+    run the same arithmetic in three launches: U and Y agree bit for bit."""
+    w = small(int(cfg[-1])) if cfg.startswith("small") else full(int(cfg[-1]))
+    L = run(w)
+    U1, Y1 = L.U().copy(), L.Y_host().copy()
+    L.ws.zero_()
+    L.Y.zero_()
+    L.run_shrink()
+    B.lora_base_gemm(L.X, L.W_t, L.Y, L.T, L.K, L.pool, L.plan, L.ws)
+    B.lora_expand_epilogue(L.X, L.W_t, L.Y, L.T, L.K, L.pool, L.plan, L.ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(U1, L.U())
+    assert np.array_equal(Y1, L.Y_host())
+
+
 def test_u_capacity_error_skips_lora_and_flags():
     w = small(2)
     L = D.DeviceLayer(w, max_rank=1)          # U room for one rank row per slot only
