@@ -526,13 +526,21 @@ __device__ __forceinline__ void tile_coords(int T, int tiles_m, int tiles_n, int
 
 // Fused epilogue of a tile: add the expand to the fp32 accumulators, round
 // once, store Y.
-//   * A 32-row block whose rows all hold one active slot of the same adapter
-//     (rank <= 16) with consecutive U offsets -- the common case in prefill,
-//     where segments are long -- takes the expand as MFMAs: U_block (32 x r,
-//     fp32 split exactly into bf16 hi + lo, error < 2^-16 of U) times the
-//     adapter's B slice (r x 32 per MFMA block), accumulated into the same
-//     registers as the base product.
-//   * Other blocks stage through LDS and add the expand row by row.
+//   * One slot per token (K = 1) and ranks <= 16 -- prefill: the expand of a
+//     32-row block is done by MFMAs, U_block (32 x r, fp32 split exactly into
+//     bf16 hi + lo, error < 2^-16 of U) times the adapter's B slice (r x 32 per
+//     MFMA block), accumulated into the base product's registers.  A block
+//     spanning several adapters takes one pass per adapter, with the U rows
+//     of the other adapters zero.  The B fragments of the last adapter are
+//     kept, so a long segment loads them once.  The slot descriptors of all
+//     blocks, then U and page ids, then B values, are each one round trip.
+//   * Blocks with higher ranks or several slots per token add the expand row
+//     by row (all lanes on one row).
+//   * Every block is staged in LDS and stored with 16-byte stores when it
+//     needs no row-by-row expand.
+// The per-block loop is kept rolled (its body once in the code object):
+// block i is always in acc[0] and the blocks rotate down after each step,
+// since a runtime index into acc would send it to scratch memory.
 template <int BM, int BN, int WM, int WN>
 __device__ __forceinline__ void fused_epilogue(const GemmArgs &g,
                                                f32x16_t (&acc)[TileCfg<BM, BN, WM, WN>::TM]
@@ -540,118 +548,164 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs &g,
                                                char *lds0, char *lds1, int m0, int n0) {
   using C = TileCfg<BM, BN, WM, WN>;
   constexpr int TM = C::TM, TN = C::TN;
-  constexpr int SC = TN * 32 + 1;            // staged floats per row (padded)
-  constexpr int CPL = TN * 32 / 64;          // output columns per lane
+  constexpr int WC = TN * 32;                // columns of this wave's sub-tile
+  constexpr int SC = WC + 4;                 // staged floats per row (padded, 16-byte rows)
+  constexpr int CPL = WC / 64;               // columns per lane in the row-by-row path
   static_assert(CPL == 1 || CPL == 2, "fused epilogue handles 64 or 128 columns per wave");
+  static_assert(WC % 8 == 0 && 64 % (WC / 8) == 0, "16-byte store layout");
   // waves 0..NW/2-1 stage in lds0, the others in lds1
   static_assert((C::NW / 2) * 32 * SC * 4 <= C::STAGE, "staging must fit in LDS");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int frow = lane & 31, half = lane >> 5;
   const bool lora_on = expand_enabled(g.ex);
+  const bool mfma_ok = lora_on && g.ex.K == 1;
   const uint16_t *Bp = static_cast<const uint16_t *>(g.ex.b_pages);
 
-  // ---- MFMA expand of single-adapter blocks
-  unsigned done = 0;
-  int bkey_ps = -1, bkey_r = -1;
-  bf16x8_t bfr[TN];
-  if (lora_on && g.ex.K == 1) {
-    // unrolled: acc is indexed with constants only (a runtime index would
-    // send the whole accumulator array to scratch memory)
+  // round trip 1: slot descriptor of row frow of every block; round trip 2:
+  // that row's U values (rank rows 8*half .. +7)
+  int4 sdv[TM];
+  float uv[TM][8];
+  unsigned rowwise = lora_on && !mfma_ok ? (1u << TM) - 1 : 0u;   // blocks for the row path
+  if (mfma_ok) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const int R0 = m0 + wm * TM * 32 + i * 32;
-      const int row = min(R0 + frow, g.M - 1);
-      const int4 sd = g.ex.slot_desc[row];
-      const int s0x = __shfl(sd.x, 0, 64), r = __shfl(sd.y, 0, 64);
-      const int uz = __shfl(sd.z, 0, 64), ps = __shfl(sd.w, 0, 64);
-      const bool ok = R0 + frow < g.M && s0x >= 0 && sd.x >= 0 && sd.y == r && sd.w == ps &&
-                      sd.z == uz + frow * r && r > 0 && r <= 16;
-      if (__ballot(!ok) != 0) continue;
-      if (ps != bkey_ps || r != bkey_r) {
-        // B operand: lane (column frow of block j, rank rows 8*half .. +7)
-        int pidl = 0;
-        if (lane < 16) pidl = g.ex.page_ids[ps + min(lane, r - 1)];
+      const int row = m0 + wm * TM * 32 + i * 32 + frow;
+      sdv[i] = g.ex.slot_desc[min(row, g.M - 1)];
+      if (row >= g.M) sdv[i].x = -1;
+    }
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int col = min(n0 + wn * TN * 32 + j * 32 + frow, g.N - 1);
-          uint32_t w4[4];
+    for (int i = 0; i < TM; ++i) {
+      const bool act = sdv[i].x >= 0;
+      if (__ballot(act && sdv[i].y > 16) != 0) rowwise |= 1u << i;
+      const int r = act ? min(sdv[i].y, 16) : 1;
 #pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const int ja = half * 8 + e, jb = ja + 1;
-            const int pa = __shfl(pidl, min(ja, 15), 64), pb = __shfl(pidl, min(jb, 15), 64);
-            uint32_t lo = Bp[int64_t(pa) * g.ex.d_out + col];
-            uint32_t hi = Bp[int64_t(pb) * g.ex.d_out + col];
-            if (ja >= r) lo = 0;
-            if (jb >= r) hi = 0;
-            w4[e >> 1] = lo | (hi << 16);
-          }
-          const uint4 packed = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-          __builtin_memcpy(&bfr[j], &packed, 16);
-        }
-        bkey_ps = ps;
-        bkey_r = r;
+      for (int e = 0; e < 8; ++e) {
+        const int ja = half * 8 + e;
+        uv[i][e] = act ? g.ex.U[sdv[i].z + min(ja, r - 1)] : 0.f;
+        if (ja >= r) uv[i][e] = 0.f;
       }
-      // A operand: U of row frow, rank rows 8*half .. +7, as bf16 hi + lo
-      const float *urow = g.ex.U + uz + frow * r;
-      uint32_t hw[4], lw[4];
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const int ja = half * 8 + e, jb = ja + 1;
-        float ua = urow[min(ja, r - 1)], ub = urow[min(jb, r - 1)];
-        if (ja >= r) ua = 0.f;
-        if (jb >= r) ub = 0.f;
-        const uint16_t ha = f2bf(ua), hb = f2bf(ub);
-        const uint16_t la = f2bf(ua - bf2f(ha)), lb = f2bf(ub - bf2f(hb));
-        hw[e >> 1] = uint32_t(ha) | (uint32_t(hb) << 16);
-        lw[e >> 1] = uint32_t(la) | (uint32_t(lb) << 16);
-      }
-      bf16x8_t ahi, alo;
-      const uint4 ph = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      const uint4 pl = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-      __builtin_memcpy(&ahi, &ph, 16);
-      __builtin_memcpy(&alo, &pl, 16);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bfr[j], acc[i][j], 0, 0, 0);
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bfr[j], acc[i][j], 0, 0, 0);
-      }
-      done |= 1u << i;
     }
   }
 
-  // ---- stage, expand the remaining rows, round and store
   float *stage = reinterpret_cast<float *>(wave < C::NW / 2 ? lds0 : lds1) +
                  (wave % (C::NW / 2)) * 32 * SC;
-  const int col_raw = n0 + wn * TN * 32 + lane * CPL;
+  uint16_t *Y = static_cast<uint16_t *>(g.Y);
+  const int cbase = n0 + wn * WC;
+  // row-by-row path: lane owns CPL consecutive columns
+  const int col_raw = cbase + lane * CPL;
   const bool col_ok = col_raw < g.N;
   const int col = col_ok ? col_raw : g.N - CPL;     // loads stay in bounds
-  uint16_t *Y = static_cast<uint16_t *>(g.Y);
+  // 16-byte path: lane owns 8 columns of one of 64 / (WC / 8) rows per step
+  constexpr int LPR = WC / 8, RPS = 64 / LPR;
+  const int vr = lane / LPR, vc = (lane % LPR) * 8;
+  const bool c8 = cbase + vc + 8 <= g.N;
   BCache<CPL, 16> cache;
   cache.ps = -1;
   cache.r = -1;
-#pragma unroll
+  int bkey_ps = -1, bkey_r = -1;             // adapter slice held in bfr
+  bf16x8_t bfr[TN] = {};
+#pragma unroll 1
   for (int i = 0; i < TM; ++i) {
+    if (mfma_ok && !(rowwise & 1u)) {
+      // one MFMA pass per adapter present in the block (lanes 0-31 = rows)
+      const int4 sd = sdv[0];
+      unsigned long long pending = __ballot(sd.x >= 0) & 0xffffffffull;
+      while (pending) {
+        const int leader = __ffsll(pending) - 1;
+        const int kps = __shfl(sd.w, leader, 64), kr = __shfl(sd.y, leader, 64);
+        const bool mine = sd.x >= 0 && sd.w == kps && sd.y == kr;
+        pending &= ~__ballot(mine);
+        if (kps != bkey_ps || kr != bkey_r) {
+          // B operand: lane (column frow of block j, rank rows 8*half .. +7)
+          int pidl = 0;
+          if (lane < 16) pidl = g.ex.page_ids[kps + min(lane, kr - 1)];
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const int cj = min(n0 + wn * TN * 32 + j * 32 + frow, g.N - 1);
+            uint32_t w4[4];
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              const int ja = half * 8 + e, jb = ja + 1;
+              const int pa = __shfl(pidl, min(ja, 15), 64), pb = __shfl(pidl, min(jb, 15), 64);
+              uint32_t lo = Bp[int64_t(pa) * g.ex.d_out + cj];
+              uint32_t hi = Bp[int64_t(pb) * g.ex.d_out + cj];
+              if (ja >= kr) lo = 0;
+              if (jb >= kr) hi = 0;
+              w4[e >> 1] = lo | (hi << 16);
+            }
+            const uint4 packed = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+            __builtin_memcpy(&bfr[j], &packed, 16);
+          }
+          bkey_ps = kps;
+          bkey_r = kr;
+        }
+        // A operand: U of row frow (zero unless the row is on this adapter),
+        // rank rows 8*half .. +7, as bf16 hi + lo
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float ua = mine ? uv[0][e] : 0.f, ub = mine ? uv[0][e + 1] : 0.f;
+          const uint16_t ha = f2bf(ua), hb = f2bf(ub);
+          const uint16_t la = f2bf(ua - bf2f(ha)), lb = f2bf(ub - bf2f(hb));
+          hw[e >> 1] = uint32_t(ha) | (uint32_t(hb) << 16);
+          lw[e >> 1] = uint32_t(la) | (uint32_t(lb) << 16);
+        }
+        bf16x8_t ahi, alo;
+        const uint4 ph = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        const uint4 pl = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        __builtin_memcpy(&ahi, &ph, 16);
+        __builtin_memcpy(&alo, &pl, 16);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bfr[j], acc[0][j], 0, 0, 0);
+          acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bfr[j], acc[0][j], 0, 0, 0);
+        }
+      }
+    }
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = (v >> 2) * 8 + half * 4 + (v & 3);
-        stage[r * SC + j * 32 + frow] = acc[i][j][v];
+        stage[r * SC + j * 32 + frow] = acc[0][j][v];
       }
     __syncthreads();
     const int rbase = m0 + wm * TM * 32 + i * 32;
-    const bool rows_need_expand = lora_on && !((done >> i) & 1u);
-    for (int rr = 0; rr < 32; ++rr) {
-      const int row = rbase + rr;
-      if (row >= g.M) break;
-      float v[CPL];
+    if (!(rowwise & 1u)) {
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) v[c] = stage[rr * SC + lane * CPL + c];
-      if (rows_need_expand) expand_row_cached<CPL, 16>(v, row, col, g.ex, cache);
-      if (col_ok) Cols<uint16_t, CPL>::store(Y + int64_t(row) * g.N + col, v);
+      for (int rr0 = 0; rr0 < 32; rr0 += RPS) {
+        const int rr = rr0 + vr;
+        const int row = rbase + rr;
+        if (row < g.M && c8) {
+          const float4 lo = *reinterpret_cast<const float4 *>(stage + rr * SC + vc);
+          const float4 hi = *reinterpret_cast<const float4 *>(stage + rr * SC + vc + 4);
+          const float v8[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+          Cols<uint16_t, 8>::store(Y + int64_t(row) * g.N + cbase + vc, v8);
+        }
+      }
+    } else {
+      for (int rr = 0; rr < 32; ++rr) {
+        const int row = rbase + rr;
+        if (row >= g.M) break;
+        float v[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) v[c] = stage[rr * SC + lane * CPL + c];
+        expand_row_cached<CPL, 16>(v, row, col, g.ex, cache);
+        if (col_ok) Cols<uint16_t, CPL>::store(Y + int64_t(row) * g.N + col, v);
+      }
     }
+    // next block into position 0
+#pragma unroll
+    for (int k = 0; k + 1 < TM; ++k) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[k][j] = acc[k + 1][j];
+      sdv[k] = sdv[k + 1];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) uv[k][e] = uv[k + 1][e];
+    }
+    rowwise >>= 1;
   }
 }
 
