@@ -219,6 +219,60 @@ def main():
     st_med, st_mean = stage_times(ids, args.event_steps)
     sb_med, sb_mean = stage_times(empty_ids, args.event_steps)
 
+    def event_time(fn, reps, rounds=5):
+        """Median over rounds of (events around `reps` back-to-back calls) / reps."""
+        ts = []
+        for _ in range(rounds):
+            for _ in range(2):
+                torch.mm(big, big)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(reps):
+                fn(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3 / reps)
+        return float(np.median(ts))
+
+    e_bytes = 2 if L.dtype == B.LORA_BF16 else 4
+    extra = {}
+    if w.merge_ids is not None:
+        # signed merge of the workload's adapters into W, then the unmerge,
+        # alternating on the rotated copies (each copy returns near W)
+        m_ids = D.to_device(np.asarray(w.merge_ids, np.int32), "cuda")
+        plus = D.to_device(np.ones(len(w.merge_ids), np.float32), "cuda")
+        minus = D.to_device(-np.ones(len(w.merge_ids), np.float32), "cuda")
+        mcopies = [c.W_t for c in copies]
+
+        def merge_call(i):
+            B.lora_merge_delta(mcopies[(i // 2) % R], L.pool, m_ids, plus if i % 2 == 0 else minus,
+                               len(w.merge_ids))
+        t_m = event_time(merge_call, 2 * min(R, 8))
+        rsum = int(sum(int(w.rank[a]) for a in w.merge_ids))
+        m_bytes = 2 * w.d_in * w.d_out * e_bytes + rsum * (w.d_in + w.d_out) * e_bytes
+        extra["merge"] = {"adapters": len(w.merge_ids), "us": t_m, "bytes": m_bytes,
+                          "GB_s": m_bytes / t_m / 1e3, "frac_hbm": m_bytes / t_m / 1e3 / HBM_PEAK_GBS,
+                          "flops": 2.0 * w.d_in * w.d_out * rsum}
+    if w.dY is not None:
+        # LoRA grads dA, dB after the forward of copy 0 (its U in the workspace)
+        dA, dB, gws = L.grad_buffers()
+        c0 = copies[0]
+        step(c0, ids)
+        torch.cuda.synchronize()
+
+        def grad_call(i):
+            B.lora_grad(c0.X, mask, L.keep_scale, L.dY, T, K, gates, c0.pool, c0.plan, c0.ws,
+                        dA, dB, L.max_rank, gws)
+        t_g = event_time(grad_call, 8)
+        hdr0 = c0.plan[L.layout[0] // 4:L.layout[0] // 4 + 16].cpu().numpy()
+        Ru, Rp = int(hdr0[B.PH_RUSED]), int(hdr0[B.PH_RPAIRS])
+        g_bytes = (T * w.d_out * e_bytes + T * w.d_in * (e_bytes + (1 if mask is not None else 0))
+                   + Ru * (w.d_in + w.d_out) * (e_bytes + 4) + 8 * Rp)
+        extra["grads"] = {"us": t_g, "bytes": g_bytes, "GB_s": g_bytes / t_g / 1e3,
+                          "frac_hbm": g_bytes / t_g / 1e3 / HBM_PEAK_GBS,
+                          "flops": 2.0 * Rp * (2 * w.d_out + w.d_in)}
+
     # ---------------------------------------------------------------- figures
     e = 2 if L.dtype == B.LORA_BF16 else 4
     P, S, R_pairs, R_used = (int(hdr[B.PH_PAIRS]), int(hdr[B.PH_SEGS]), int(hdr[B.PH_RPAIRS]),
@@ -256,6 +310,7 @@ def main():
                    "rotation_copies": R, "graph_replay": not args.no_graph},
         "roofline": roofline,
         "value_apply_only": T * args.steps / elapsed_apply,
+        **extra,
         "stages_us_median": st_med,
         "stages_us_mean": st_mean,
         "stages_us_mean_empty_plan": sb_mean,
