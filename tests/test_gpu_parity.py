@@ -318,6 +318,23 @@ def test_merge_unmerge_and_switch(which):
     assert rel_err(D.as_f64(D.to_host(W3)), ref3) <= TOL[w.dtype]
 
 
+def test_merge_long_list_with_duplicates():
+    """300 entries (two groups of list reads), repeated ids and signed
+    coefficients, more listed rank rows than one LDS list holds."""
+    w = small(3)
+    rng = np.random.default_rng(3)
+    ids = rng.integers(0, w.n_adapters, size=300).astype(np.int32)
+    ids[::7] = ids[0]                                  # many repeats of one adapter
+    co = rng.uniform(-1.0, 1.0, size=300).astype(np.float32)
+    assert int(w.rank[ids[:256]].sum()) > 1024
+    L = D.DeviceLayer(w)
+    W = L.W_t.clone()
+    L.run_merge(W, ids, co)
+    torch.cuda.synchronize()
+    ref = O.merge_workload(w, ids=ids, coeffs=co)
+    assert rel_err(D.as_f64(D.to_host(W)), ref) <= TOL[w.dtype]
+
+
 def test_merged_weight_base_matches_apply():
     w = small(2)
     a = int(w.ids[0, 0])
