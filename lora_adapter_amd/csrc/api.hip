@@ -183,6 +183,7 @@ int32_t base_args(const void *X, const void *W_t, void *Y, int32_t T, int32_t K,
   g = GemmArgs{};
   g.X = X; g.W = W_t; g.M = T; g.N = pool->d_out; g.Kd = pool->d_in;
   g.k_split = w.cfg.k_split;
+  g.sk_g = w.cfg.sk;
   g.partial = w.partial;
   g.Y = Y;
   g.ex.K = K;

@@ -92,38 +92,56 @@ template <> struct Raw8<float> {
 };
 
 // One row, 8 columns per lane.  Control data is gathered lane-parallel and
-// broadcast: round trip 1 the row's slot descriptors ({pair, rank, u_off,
-// page_start}, lane k = slot k), round trip 2 page ids and U values of 16
-// rank rows (lane j = row j), round trip 3 sixteen B-row loads in flight.
+// broadcast: the row's slot descriptors ({pair, rank, u_off, page_start},
+// lane k = slot k; the caller loads them, so their round trip can overlap
+// its own loads), then the page ids and U values of up to 64 rank rows (lane
+// j = row j), then the B rows stream in batches of 8, the next batch in
+// flight while the current one is added.  Rank rows are added in ascending
+// order, slot by slot.
 template <typename E>
-__device__ __forceinline__ void expand_row8(float (&v)[8], int t, int col, const ExpandArgs &e) {
+__device__ __forceinline__ int4 expand_row_desc(int t, const ExpandArgs &e) {
+  int4 sd = make_int4(-1, 0, 0, 0);
+  if (lane_id() < e.K) sd = e.slot_desc[t * e.K + lane_id()];
+  return sd;
+}
+
+template <typename E>
+__device__ __forceinline__ void expand_row8(float (&v)[8], int4 sd, int col, const ExpandArgs &e) {
   const E *B = static_cast<const E *>(e.b_pages);
   const int lane = lane_id();
-  int4 sd = make_int4(-1, 0, 0, 0);
-  if (lane < e.K) sd = e.slot_desc[t * e.K + lane];
   for (int k = 0; k < e.K; ++k) {
     if (__shfl(sd.x, k, 64) < 0) continue;
     const int r = __shfl(sd.y, k, 64), uo = __shfl(sd.z, k, 64), ps = __shfl(sd.w, k, 64);
-    for (int j0 = 0; j0 < r; j0 += 16) {
-      int pid = 0;
-      float uv = 0.f;
-      if (lane < 16) {
-        const int j = j0 + min(lane, r - j0 - 1);
-        pid = e.page_ids[ps + j];
-        uv = e.U[uo + j];
-      }
-      Raw8<E> bv[16];
+    for (int jb = 0; jb < r; jb += 64) {
+      const int nrb = min(64, r - jb);
+      const int jl = jb + min(lane, nrb - 1);
+      const int pid = e.page_ids[ps + jl];
+      const float uv = e.U[uo + jl];
+      Raw8<E> ba[8], bb[8];
+      auto load8 = [&](Raw8<E> (&dst)[8], int q0) {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) bv[q].load(B + int64_t(__shfl(pid, q, 64)) * e.d_out + col);
+        for (int q = 0; q < 8; ++q)
+          dst[q].load(B + int64_t(__shfl(pid, min(q0 + q, nrb - 1), 64)) * e.d_out + col);
+      };
+      auto add8 = [&](const Raw8<E> (&src)[8], int q0) {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        if (j0 + q < r) {
-          float b[8];
-          bv[q].to8(b);
-          const float uj = __shfl(uv, q, 64);
+        for (int q = 0; q < 8; ++q) {
+          if (q0 + q < nrb) {
+            float b[8];
+            src[q].to8(b);
+            const float uj = __shfl(uv, q0 + q, 64);
 #pragma unroll
-          for (int c = 0; c < 8; ++c) v[c] = fmaf(uj, b[c], v[c]);
+            for (int c = 0; c < 8; ++c) v[c] = fmaf(uj, b[c], v[c]);
+          }
         }
+      };
+      load8(ba, 0);
+      for (int q0 = 0; q0 < nrb; q0 += 16) {
+        load8(bb, q0 + 8);
+        add8(ba, q0);
+        if (q0 + 8 >= nrb) break;
+        load8(ba, q0 + 16);
+        add8(bb, q0 + 8);
       }
     }
   }
@@ -709,11 +727,18 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs &g,
   }
 }
 
-// One K tile of MFMAs from an LDS stage.
-template <int BM, int BN, int WM, int WN>
+// One K tile of MFMAs from an LDS stage.  pre_step(s) runs before each of
+// the four 16-wide K steps (the ring pipeline issues a quarter of the next
+// tile's copies there, so that they queue while the MFMAs execute).
+struct NoStep {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
+template <int BM, int BN, int WM, int WN, typename F = NoStep>
 __device__ __forceinline__ void tile_mfma(const char *As,
                                           f32x16_t (&acc)[TileCfg<BM, BN, WM, WN>::TM]
-                                                         [TileCfg<BM, BN, WM, WN>::TN]) {
+                                                         [TileCfg<BM, BN, WM, WN>::TN],
+                                          const F &pre_step = F()) {
   using C = TileCfg<BM, BN, WM, WN>;
   constexpr int TM = C::TM, TN = C::TN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -722,6 +747,7 @@ __device__ __forceinline__ void tile_mfma(const char *As,
   const char *Bs = As + BM * C::ROWB;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
+    pre_step(s);
     bf16x8_t af[TM], bf[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -741,31 +767,31 @@ __device__ __forceinline__ void tile_mfma(const char *As,
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool kFused>
-__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_tile_kernel(GemmArgs g) {
+// Wait until at most n (0 <= n <= NS - 2) K tiles' copies are still in flight.
+template <int LPW, int NS>
+__device__ __forceinline__ void wait_tiles(int n) {
+  if constexpr (NS >= 4) {
+    if (n >= 2) { wait_vmcnt<2 * LPW>(); return; }
+  }
+  if constexpr (NS >= 3) {
+    if (n >= 1) { wait_vmcnt<LPW>(); return; }
+  }
+  wait_vmcnt<0>();
+}
+
+// One output tile (m0, n0) over K tiles [k_begin / 64, + nk): the K loop
+// and the epilogue (fp32 partials into slot `slot`, or the fused expand).
+template <int BM, int BN, int WM, int WN, int NS, bool kFused>
+__device__ __forceinline__ void tile_run(const GemmArgs &g, char *smem, int m0, int n0,
+                                         int k_begin, int nk, int slot) {
   using C = TileCfg<BM, BN, WM, WN>;
   constexpr int TM = C::TM, TN = C::TN;
-  // two stages as two LDS objects, so that waits for one stage's loads do
-  // not also wait for the other's
-  __shared__ __attribute__((aligned(16))) char st0[C::STAGE];
-  __shared__ __attribute__((aligned(16))) char st1[C::STAGE];
-
-  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
-  const int ntiles = tiles_m * tiles_n;
-  const int per = (ntiles + 7) / 8;
-  const int t = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (t >= ntiles) return;
-  int tm, tn;
-  tile_coords(t, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-
+  char *const st0 = smem;
+  char *const st1 = smem + C::STAGE;
   const uint16_t *X = static_cast<const uint16_t *>(g.X);
   const uint16_t *W = static_cast<const uint16_t *>(g.W);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
-  const int k_begin = blockIdx.y * g.k_split;
-  const int k_end = min(g.Kd, k_begin + g.k_split);
-  const int nk = (k_end - k_begin) / 64;
 
   // per-lane source rows, as 32-bit element offsets from the tile's first row
   // (clamped: rows past M / N feed outputs that are never stored)
@@ -795,6 +821,20 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_tile_kernel(GemmArgs g) 
     for (int i = 0; i < C::B_INS; ++i)
       lds_dma16(b + boff[i], lds + BM * C::ROWB + (wave * C::B_INS + i) * 1024);
   };
+  // quarter q of issue(base, kt): copies [q * LPW / 4, (q + 1) * LPW / 4) of
+  // the wave's A-then-B list, in the same order as issue()
+  static_assert(C::LPW % 4 == 0, "copies split over the four K steps");
+  auto issue_quarter = [&](char *base, int kt, int q) {
+    const uint16_t *a = abase + kt * 64;
+    const uint16_t *b = bbase + kt * 64;
+    const uint32_t lds = lds_addr(base);
+#pragma unroll
+    for (int c = 0; c < C::LPW / 4; ++c) {
+      const int i = q * (C::LPW / 4) + c;
+      if (i < C::A_INS) lds_dma16(a + aoff[i], lds + (wave * C::A_INS + i) * 1024);
+      else lds_dma16(b + boff[i - C::A_INS], lds + BM * C::ROWB + (wave * C::B_INS + i - C::A_INS) * 1024);
+    }
+  };
 
   f32x16_t acc[TM][TN];
 #pragma unroll
@@ -805,35 +845,62 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_tile_kernel(GemmArgs g) 
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   const int frow = lane & 31, half = lane >> 5;
-  if (nk > 0) issue(st0, 0);
-  if (nk > 1) issue(st1, 1);
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    // even tile from stage 0 while the odd tile's loads stay in flight
-    wait_vmcnt<C::LPW>();
-    __syncthreads();
-    tile_mfma<BM, BN, WM, WN>(st0, acc);
-    __syncthreads();
-    if (kt + 2 < nk) {
-      issue(st0, kt + 2);
-      wait_vmcnt<C::LPW>();     // the odd tile (issued before this one) has landed
-    } else {
-      wait_vmcnt<0>();
+  // NS >= 3 stages in a ring: K tile kt lives in stage kt % NS.  At the top
+  // of step kt, once tile kt has landed and every wave has left step kt - 1,
+  // tile kt + NS - 1 is issued into the stage step kt - 1 used, so NS - 1
+  // tiles' copies are in flight while tile kt feeds the MFMAs.
+  if constexpr (NS == 2) {
+    // two stages, the loop unrolled by two so each stage has a fixed address
+    if (nk > 0) issue(st0, 0);
+    if (nk > 1) issue(st1, 1);
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      // even tile from stage 0 while the odd tile's loads stay in flight
+      wait_vmcnt<C::LPW>();
+      __syncthreads();
+      tile_mfma<BM, BN, WM, WN>(st0, acc);
+      __syncthreads();
+      if (kt + 2 < nk) {
+        issue(st0, kt + 2);
+        wait_vmcnt<C::LPW>();     // the odd tile (issued before this one) has landed
+      } else {
+        wait_vmcnt<0>();
+      }
+      __syncthreads();
+      tile_mfma<BM, BN, WM, WN>(st1, acc);
+      __syncthreads();
+      if (kt + 3 < nk) issue(st1, kt + 3);
     }
-    __syncthreads();
-    tile_mfma<BM, BN, WM, WN>(st1, acc);
-    __syncthreads();
-    if (kt + 3 < nk) issue(st1, kt + 3);
-  }
-  if (kt < nk) {               // odd number of K tiles: the last one is in stage 0
-    wait_vmcnt<0>();
-    __syncthreads();
-    tile_mfma<BM, BN, WM, WN>(st0, acc);
-    __syncthreads();
+    if (kt < nk) {               // odd number of K tiles: the last one is in stage 0
+      wait_vmcnt<0>();
+      __syncthreads();
+      tile_mfma<BM, BN, WM, WN>(st0, acc);
+      __syncthreads();
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i)
+      if (i < nk) issue(smem + i * C::STAGE, i);
+    for (int kt0 = 0; kt0 < nk; kt0 += NS) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        const int kt = kt0 + u;
+        if (kt < nk) {
+          wait_tiles<C::LPW, NS>(min(NS - 2, nk - 1 - kt));
+          __syncthreads();
+          char *const nxt = smem + ((u + NS - 1) % NS) * C::STAGE;
+          const bool more = kt + NS - 1 < nk;
+          tile_mfma<BM, BN, WM, WN>(smem + u * C::STAGE, acc, [&](int q) {
+            if (more) issue_quarter(nxt, kt + NS - 1, q);
+          });
+        }
+      }
+    }
+    __syncthreads();   // the epilogue reuses the stages
   }
 
   if constexpr (!kFused) {
-    float *Pz = g.partial + int64_t(blockIdx.y) * g.M * g.N;
+    float *Pz = g.partial + int64_t(slot) * g.M * g.N;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -849,6 +916,46 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_tile_kernel(GemmArgs g) 
   } else {
     fused_epilogue<BM, BN, WM, WN>(g, acc, st0, st1, m0, n0);
   }
+}
+
+template <int BM, int BN, int WM, int WN, int NS, bool kFused>
+__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_tile_kernel(GemmArgs g) {
+  using C = TileCfg<BM, BN, WM, WN>;
+  static_assert(NS >= 2 && (NS - 2) * C::LPW < 64, "stages / vmcnt range");
+  __shared__ __attribute__((aligned(16))) char smem[NS * C::STAGE];
+  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  const int ntiles = tiles_m * tiles_n;
+  if constexpr (!kFused && NS >= 3) {
+   if (g.sk_g > 0) {
+    // stream-K: workgroup w takes units (tile, K tile) [w U / G, (w + 1) U / G)
+    // of the U = tiles x KT units, in order, across tile boundaries; each
+    // maximal run inside one tile is a piece, stored in slot w - (first
+    // workgroup of that tile).  The epilogue adds a tile's pieces in K order.
+    const int KT = g.Kd / 64;
+    const int64_t U = int64_t(ntiles) * KT;
+    const int G = g.sk_g, w = blockIdx.x;
+    int64_t u = int64_t(w) * U / G;
+    const int64_t u1 = int64_t(w + 1) * U / G;
+    while (u < u1) {
+      const int t = int(u / KT), kb = int(u % KT);
+      const int ke = int(min<int64_t>(KT, kb + (u1 - u)));
+      const int wf = int(((int64_t(t) * KT + 1) * G - 1) / U);
+      tile_run<BM, BN, WM, WN, NS, kFused>(g, smem, (t / tiles_n) * BM, (t % tiles_n) * BN,
+                                           kb * 64, ke - kb, w - wf);
+      u += ke - kb;
+    }
+    return;
+   }
+  }
+  const int per = (ntiles + 7) / 8;
+  const int t = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (t >= ntiles) return;
+  int tm, tn;
+  tile_coords(t, tiles_m, tiles_n, tm, tn);
+  const int k_begin = blockIdx.y * g.k_split;
+  const int k_end = min(g.Kd, k_begin + g.k_split);
+  tile_run<BM, BN, WM, WN, NS, kFused>(g, smem, tm * BM, tn * BN, k_begin, (k_end - k_begin) / 64,
+                                       blockIdx.y);
 }
 
 // ------------------------------------------------------------ fp32 GEMM
@@ -908,18 +1015,31 @@ __global__ __launch_bounds__(256) void epilogue_kernel(EpilogueArgs a) {
   const int col_raw = (blockIdx.x * 64 + lane) * CPL;
   const bool col_ok = col_raw < a.N;
   const int col = col_ok ? col_raw : a.N - CPL;      // loads stay in bounds
+  const bool lora_on = expand_enabled(a.ex);
+  // the row's slot descriptors first: their round trip overlaps the partials'
+  const int4 sd = lora_on ? expand_row_desc<E>(row, a.ex) : make_int4(-1, 0, 0, 0);
   float v[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) v[c] = 0.f;
-  // split partials: issue up to 8 at once, add in split order
+  // pieces of this lane's output: the K splits, or under stream-K the
+  // workgroups that covered its tile (w(x) = workgroup holding unit x)
+  int np = a.splits;
+  if (a.sk_g > 0) {
+    const int tiles_n = (a.N + a.bn - 1) / a.bn;
+    const int t = (row / a.bm) * tiles_n + col / a.bn;
+    const int64_t U = int64_t((a.M + a.bm - 1) / a.bm) * tiles_n * a.sk_kt;
+    const int64_t x0 = int64_t(t) * a.sk_kt, x1 = x0 + a.sk_kt - 1;
+    np = int(((x1 + 1) * a.sk_g - 1) / U - ((x0 + 1) * a.sk_g - 1) / U) + 1;
+  }
+  // partials: issue up to 8 at once, add in piece order
   for (int z0 = 0; z0 < a.splits; z0 += 8) {
     Raw8<float> pr[8];
 #pragma unroll
     for (int z = 0; z < 8; ++z)
-      pr[z].load(a.partial + (int64_t(min(z0 + z, a.splits - 1)) * a.M + row) * a.N + col);
+      pr[z].load(a.partial + (int64_t(min(z0 + z, np - 1)) * a.M + row) * a.N + col);
 #pragma unroll
     for (int z = 0; z < 8; ++z) {
-      if (z0 + z < a.splits) {
+      if (z0 + z < np) {
         float pv[8];
         pr[z].to8(pv);
 #pragma unroll
@@ -927,7 +1047,7 @@ __global__ __launch_bounds__(256) void epilogue_kernel(EpilogueArgs a) {
       }
     }
   }
-  if (expand_enabled(a.ex)) expand_row8<E>(v, row, col, a.ex);
+  if (lora_on) expand_row8<E>(v, sd, col, a.ex);
   if (col_ok) Cols<E, CPL>::store(static_cast<E *>(a.Y) + int64_t(row) * a.N + col, v);
 }
 
@@ -971,9 +1091,22 @@ GemmConfig choose_gemm(int T, int d_in, int d_out, int dtype) {
     c.splits = 1; c.k_split = d_in; c.fused = true;
     return c;
   }
-  // otherwise 256 x 128 tiles with K split so ~256 workgroups run
-  c.kind = 6; c.bm = 256; c.bn = 128;
+  // otherwise 256 x 128 tiles, stream-K over 256 workgroups (one per CU):
+  // every workgroup takes the same number of (tile, K tile) units, so no CU
+  // runs a second round; a tile is covered by at most ceil(KT / per) + 1
+  // workgroups (its pieces)
+  c.kind = 6; c.bm = 256; c.bn = 128; c.fused = false;
   const int64_t tiles = int64_t((T + c.bm - 1) / c.bm) * ((d_out + c.bn - 1) / c.bn);
+  const int64_t units = tiles * kblocks;
+  constexpr int kStreamWgs = 256;
+  if (units >= 4 * kStreamWgs) {
+    const int64_t per = units / kStreamWgs;
+    c.sk = kStreamWgs;
+    c.k_split = 64;
+    c.splits = int((kblocks + per - 1) / per) + 1;
+    return c;
+  }
+  // few units: classic split-K with ~256 workgroups
   int64_t want = tiles > 0 ? (256 + tiles - 1) / tiles : 1;
   int64_t most = kblocks / 8 > 1 ? kblocks / 8 : 1;     // every split keeps >= 512 of K
   int splits = int(want < most ? want : most);
@@ -981,7 +1114,7 @@ GemmConfig choose_gemm(int T, int d_in, int d_out, int dtype) {
   const int kb_per = (kblocks + splits - 1) / splits;
   c.k_split = kb_per * 64;
   c.splits = (kblocks + kb_per - 1) / kb_per;
-  c.fused = false;
+  c.sk = 0;
   return c;
 }
 
@@ -1005,12 +1138,13 @@ hipError_t launch_base_gemm(const GemmConfig &c, const GemmArgs &g, hipStream_t 
   }
   if (c.kind == 5 || c.kind == 6) {
     const int tiles = ((g.M + c.bm - 1) / c.bm) * ((g.N + c.bn - 1) / c.bn);
-    const dim3 grid(8 * ((tiles + 7) / 8), c.splits);
+    const dim3 grid = c.sk > 0 ? dim3(c.sk, 1) : dim3(8 * ((tiles + 7) / 8), c.splits);
     if (c.kind == 5) {
-      if (c.fused) hipLaunchKernelGGL((gemm_tile_kernel<256, 256, 2, 2, true>), grid, dim3(256), 0, s, g);
-      else hipLaunchKernelGGL((gemm_tile_kernel<256, 256, 2, 2, false>), grid, dim3(256), 0, s, g);
+      if (c.fused) hipLaunchKernelGGL((gemm_tile_kernel<256, 256, 2, 2, 2, true>), grid, dim3(256), 0, s, g);
+      else hipLaunchKernelGGL((gemm_tile_kernel<256, 256, 2, 2, 2, false>), grid, dim3(256), 0, s, g);
     } else {
-      hipLaunchKernelGGL((gemm_tile_kernel<256, 128, 2, 2, false>), grid, dim3(256), 0, s, g);
+      if (c.fused) hipLaunchKernelGGL((gemm_tile_kernel<256, 128, 2, 2, 3, true>), grid, dim3(256), 0, s, g);
+      else hipLaunchKernelGGL((gemm_tile_kernel<256, 128, 2, 2, 3, false>), grid, dim3(256), 0, s, g);
     }
     return hipGetLastError();
   }
@@ -1046,7 +1180,7 @@ hipError_t launch_decode_gemm_shrink(const GemmConfig &c, const GemmArgs &g, con
 
 hipError_t launch_epilogue(const GemmConfig &c, const GemmArgs &g, int dtype, hipStream_t s) {
   if (c.fused) return hipSuccess;
-  EpilogueArgs e{g.partial, c.splits, g.M, g.N, g.Y, g.ex};
+  EpilogueArgs e{g.partial, c.splits, g.M, g.N, c.sk, g.Kd / 64, c.bm, c.bn, g.Y, g.ex};
   const dim3 grid((g.N + 511) / 512, (g.M + 3) / 4);
   if (dtype == LORA_BF16) hipLaunchKernelGGL(epilogue_kernel<uint16_t>, grid, dim3(256), 0, s, e);
   else hipLaunchKernelGGL(epilogue_kernel<float>, grid, dim3(256), 0, s, e);

@@ -219,6 +219,7 @@ struct GemmArgs {
   const void *W;            // [N][Kd]
   int M, N, Kd;
   int k_split;              // K elements per split (multiple of 64)
+  int sk_g;                 // > 0: stream-K over this many workgroups (see the tile GEMM)
   float *partial;           // [splits][M][N]
   void *Y;                  // fused epilogue output [M][N]
   ExpandArgs ex;
@@ -227,6 +228,7 @@ struct GemmArgs {
 struct EpilogueArgs {
   const float *partial;     // [splits][M][N]
   int splits, M, N;
+  int sk_g, sk_kt, bm, bn;  // stream-K: workgroups, K tiles per output tile, tile shape
   void *Y;
   ExpandArgs ex;
 };
@@ -273,8 +275,9 @@ hipError_t launch_shrink(const ShrinkArgs &a, int dtype, int64_t TK, int64_t n_a
 struct GemmConfig {
   int kind;      // 0: fp32 tiles; 1: bf16 64x128; 2: bf16 128x128; 3: bf16 256x128
   int bm, bn;
-  int splits;
+  int splits;    // partial slots per output element
   int k_split;
+  int sk;        // > 0: stream-K workgroups (splits = most pieces of one tile)
   bool fused;    // expand + rounding in the GEMM epilogue (splits == 1 only)
 };
 GemmConfig choose_gemm(int T, int d_in, int d_out, int dtype);
