@@ -11,7 +11,9 @@ adapter (synthetic, seeded).
 Measurement
   * value: tokens per second over exactly --steps steps, wall clock between
     two torch.cuda.synchronize() calls.  Each step is one HIP-graph replay of
-    plan + shrink + GEMM + epilogue on one of R rotated copies of the weights
+    lora_forward (plan + shrink + GEMM + epilogue; for split-K shapes the
+    plan is built by one extra workgroup of the GEMM launch) on one of R
+    rotated copies of the weights
     and adapter pool, R chosen so that R copies exceed 1 GiB: every step reads
     its W and pages from HBM, not from the 256 MiB Infinity Cache.
     value_apply_only: the same without the plan (built once per batch and
@@ -129,7 +131,9 @@ def main():
 
     def step(c, use_ids=ids, plan=True):
         if plan:
-            B.lora_plan(use_ids, gates, T, K, c.pool, c.plan)
+            B.lora_forward(use_ids, gates, T, K, c.X, c.W_t, c.Y, mask, L.keep_scale, c.pool, c.plan,
+                           c.ws)
+            return
         B.lora_shrink_gemm(c.X, c.W_t, c.Y, T, K, gates, mask, L.keep_scale, c.pool, c.plan, c.ws)
         B.lora_expand_epilogue(c.X, c.W_t, c.Y, T, K, c.pool, c.plan, c.ws)
 

@@ -200,6 +200,21 @@ int32_t lora_apply(const void *X, const void *W_t, void *Y, int32_t T, int32_t K
                    float keep_scale, const lora_pool_desc *pool, const void *plan, void *ws,
                    size_t ws_bytes, void *stream);
 
+/* lora_plan then lora_apply for one batch, as one call.  The base GEMM does
+ * not depend on the routing: for shapes whose GEMM writes split-K partials
+ * (decode, T <= 128, bf16; stream-K shapes) the plan is built by one extra
+ * workgroup of the GEMM launch while the others compute the partials, so
+ * the plan costs no launch and no time of its own on the critical path; the
+ * shrink and the epilogue follow.  Other shapes run lora_plan then
+ * lora_apply.  Plan, U and Y equal those of lora_plan followed by lora_apply
+ * with the same arguments, bit for bit.
+ *   Arguments as for lora_plan and lora_apply, on one stream.
+ * Errors: those of lora_plan and lora_apply. */
+int32_t lora_forward(const int32_t *ids, const float *gates, int32_t T, int32_t K,
+                     const void *X, const void *W_t, void *Y, const uint8_t *keep_mask,
+                     float keep_scale, const lora_pool_desc *pool, void *plan, size_t plan_bytes,
+                     void *ws, size_t ws_bytes, void *stream);
+
 /* ----------------------------------------------------------------- merge
  * In place: W_t <- round( W_t + sum_i coeffs[i] . s_{a_i} . (A_{a_i} . B_{a_i})^T )
  * with the delta summed in float32 and one rounding per element.  One adapter

@@ -262,6 +262,42 @@ int32_t lora_apply(const void *X, const void *W_t, void *Y, int32_t T, int32_t K
   return lora_expand_epilogue(X, W_t, Y, T, K, pool, plan, ws, ws_bytes, stream);
 }
 
+int32_t lora_forward(const int32_t *ids, const float *gates, int32_t T, int32_t K,
+                     const void *X, const void *W_t, void *Y, const uint8_t *keep_mask,
+                     float keep_scale, const lora_pool_desc *pool, void *plan, size_t plan_bytes,
+                     void *ws, size_t ws_bytes, void *stream) {
+  int32_t st = check_batch(T, K);
+  if (st != LORA_OK) return st;
+  if ((st = check_pool(pool, true)) != LORA_OK) return st;
+  if (!plan) return LORA_ERR_INVALID_ARG;
+  if (plan_bytes < lora_plan_bytes(T, K, pool->n_adapters)) return LORA_ERR_CAPACITY;
+  if (T == 0) return lora_plan(ids, gates, T, K, pool, plan, plan_bytes, stream);
+  if (!ids || !gates || !X || !W_t || !Y || !ws) return LORA_ERR_INVALID_ARG;
+  GemmConfig cfg;
+  GemmArgs g;
+  if ((st = base_args(X, W_t, Y, T, K, pool, plan, ws, ws_bytes, cfg, g)) != LORA_OK) return st;
+  if (!gemm_plan_fusable(cfg)) {
+    st = lora_plan(ids, gates, T, K, pool, plan, plan_bytes, stream);
+    if (st != LORA_OK) return st;
+    return lora_apply(X, W_t, Y, T, K, gates, keep_mask, keep_scale, pool, plan, ws, ws_bytes,
+                      stream);
+  }
+  // split GEMM with the plan built in its first workgroup, then the shrink,
+  // then the epilogue
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const PlanLaunch pl = plan_setup(ids, gates, T, K, pool_view(pool), static_cast<int32_t *>(plan),
+                                   256, plan_lds_cap(cfg));
+  hipError_t e = launch_gemm_plan(cfg, g, pl, s);
+  if (e != hipSuccess) return LORA_ERR_DEVICE;
+  const ApplyWs w = apply_layout(ws, ws_bytes, T, pool->d_in, pool->d_out, pool->dtype);
+  const int64_t TK = int64_t(T) * K;
+  const PlanView pv = plan_view(plan, TK, pool->n_adapters);
+  const ShrinkArgs sa = apply_shrink_args(X, keep_mask, keep_scale, T, K, gates, pool, pv, w);
+  e = launch_shrink(sa, pool->dtype, TK, pool->n_adapters, pool->d_in, pool->d_out, s);
+  if (e != hipSuccess) return LORA_ERR_DEVICE;
+  return dev(launch_epilogue(cfg, g, pool->dtype, s));
+}
+
 int32_t lora_merge_delta(void *W_t, const lora_pool_desc *pool, const int32_t *merge_ids,
                          const float *coeffs, int32_t m, void *stream) {
   int32_t st = check_pool(pool, true);

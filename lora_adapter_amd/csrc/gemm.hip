@@ -22,6 +22,7 @@
 //     and stores.  The reduction order is fixed: results are deterministic,
 //     and rows without active slots equal the base-only result bit for bit.
 #include "lora_internal.h"
+#include "plan_build.h"
 #include "shrink_units.h"
 
 namespace lora {
@@ -479,6 +480,20 @@ __global__ __launch_bounds__(256, 2) void decode_gemm_shrink_kernel(GemmArgs g, 
     shrink_units_wave<uint16_t, kMask, kCh, true>(s, w);
 }
 
+// Decode GEMM tiles in workgroups 1 .., with the plan built by workgroup 0
+// in the LDS the others use for their token rows (dynamic: MB*32*KC bf16).
+template <int MB, bool kLds>
+__global__ __launch_bounds__(256) void decode_gemm_plan_kernel(GemmArgs g, PlanArgs pa, int gx,
+                                                                int gy) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t dxs[];
+  if (blockIdx.x == 0) {
+    plan_build<kLds>(pa, reinterpret_cast<int *>(dxs));
+    return;
+  }
+  const int t = blockIdx.x - 1;
+  decode_tile<MB>(g, t % gx, (t / gx) % gy, t / (gx * gy), dxs);
+}
+
 // ------------------------------------------------------------ pipelined tile GEMM
 // The main GEMM for more than 128 tokens.  Tile BM x BN, K step 64, WM x WN
 // waves each owning (BM/WM) x (BN/WN) as 32x32x16 MFMA blocks.
@@ -918,6 +933,30 @@ __device__ __forceinline__ void tile_run(const GemmArgs &g, char *smem, int m0, 
   }
 }
 
+// Stream-K: workgroup w of G = g.sk_g takes the units (tile, K tile)
+// [w U / G, (w + 1) U / G) of the U = tiles x KT units, in order, across tile
+// boundaries; each maximal run inside one tile is a piece, stored in slot
+// w - (first workgroup of that tile).  The epilogue adds a tile's pieces in
+// K order.
+template <int BM, int BN, int WM, int WN, int NS>
+__device__ __forceinline__ void stream_k(const GemmArgs &g, char *smem, int w) {
+  const int tiles_n = (g.N + BN - 1) / BN;
+  const int ntiles = ((g.M + BM - 1) / BM) * tiles_n;
+  const int KT = g.Kd / 64;
+  const int64_t U = int64_t(ntiles) * KT;
+  const int G = g.sk_g;
+  int64_t u = int64_t(w) * U / G;
+  const int64_t u1 = int64_t(w + 1) * U / G;
+  while (u < u1) {
+    const int t = int(u / KT), kb = int(u % KT);
+    const int ke = int(min<int64_t>(KT, kb + (u1 - u)));
+    const int wf = int(((int64_t(t) * KT + 1) * G - 1) / U);
+    tile_run<BM, BN, WM, WN, NS, false>(g, smem, (t / tiles_n) * BM, (t % tiles_n) * BN, kb * 64,
+                                        ke - kb, w - wf);
+    u += ke - kb;
+  }
+}
+
 template <int BM, int BN, int WM, int WN, int NS, bool kFused>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_tile_kernel(GemmArgs g) {
   using C = TileCfg<BM, BN, WM, WN>;
@@ -926,26 +965,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_tile_kernel(GemmArgs g) 
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   const int ntiles = tiles_m * tiles_n;
   if constexpr (!kFused && NS >= 3) {
-   if (g.sk_g > 0) {
-    // stream-K: workgroup w takes units (tile, K tile) [w U / G, (w + 1) U / G)
-    // of the U = tiles x KT units, in order, across tile boundaries; each
-    // maximal run inside one tile is a piece, stored in slot w - (first
-    // workgroup of that tile).  The epilogue adds a tile's pieces in K order.
-    const int KT = g.Kd / 64;
-    const int64_t U = int64_t(ntiles) * KT;
-    const int G = g.sk_g, w = blockIdx.x;
-    int64_t u = int64_t(w) * U / G;
-    const int64_t u1 = int64_t(w + 1) * U / G;
-    while (u < u1) {
-      const int t = int(u / KT), kb = int(u % KT);
-      const int ke = int(min<int64_t>(KT, kb + (u1 - u)));
-      const int wf = int(((int64_t(t) * KT + 1) * G - 1) / U);
-      tile_run<BM, BN, WM, WN, NS, kFused>(g, smem, (t / tiles_n) * BM, (t % tiles_n) * BN,
-                                           kb * 64, ke - kb, w - wf);
-      u += ke - kb;
+    if (g.sk_g > 0) {
+      stream_k<BM, BN, WM, WN, NS>(g, smem, blockIdx.x);
+      return;
     }
-    return;
-   }
   }
   const int per = (ntiles + 7) / 8;
   const int t = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
@@ -956,6 +979,19 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_tile_kernel(GemmArgs g) 
   const int k_end = min(g.Kd, k_begin + g.k_split);
   tile_run<BM, BN, WM, WN, NS, kFused>(g, smem, tm * BM, tn * BN, k_begin, (k_end - k_begin) / 64,
                                        blockIdx.y);
+}
+
+// Stream-K GEMM over workgroups 1 .. G, with the plan built by workgroup 0
+// in the LDS the others use for their stages.
+template <int BM, int BN, int WM, int WN, int NS, bool kLds>
+__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_tile_plan_kernel(GemmArgs g, PlanArgs pa) {
+  using C = TileCfg<BM, BN, WM, WN>;
+  __shared__ __attribute__((aligned(16))) char smem[NS * C::STAGE];
+  if (blockIdx.x == 0) {
+    plan_build<kLds>(pa, reinterpret_cast<int *>(smem));
+    return;
+  }
+  stream_k<BM, BN, WM, WN, NS>(g, smem, blockIdx.x - 1);
 }
 
 // ------------------------------------------------------------ fp32 GEMM
@@ -1091,14 +1127,15 @@ GemmConfig choose_gemm(int T, int d_in, int d_out, int dtype) {
     c.splits = 1; c.k_split = d_in; c.fused = true;
     return c;
   }
-  // otherwise 256 x 128 tiles, stream-K over 256 workgroups (one per CU):
+  // otherwise 256 x 128 tiles, stream-K over 255 workgroups (one per CU, the
+  // last CU left to the plan workgroup when the plan is built in the launch):
   // every workgroup takes the same number of (tile, K tile) units, so no CU
   // runs a second round; a tile is covered by at most ceil(KT / per) + 1
   // workgroups (its pieces)
   c.kind = 6; c.bm = 256; c.bn = 128; c.fused = false;
   const int64_t tiles = int64_t((T + c.bm - 1) / c.bm) * ((d_out + c.bn - 1) / c.bn);
   const int64_t units = tiles * kblocks;
-  constexpr int kStreamWgs = 256;
+  constexpr int kStreamWgs = 255;       // + 1 plan workgroup in launch_gemm_plan
   if (units >= 4 * kStreamWgs) {
     const int64_t per = units / kStreamWgs;
     c.sk = kStreamWgs;
@@ -1175,6 +1212,38 @@ hipError_t launch_decode_gemm_shrink(const GemmConfig &c, const GemmArgs &g, con
   else LORA_DGS_M(4);
 #undef LORA_DGS_M
 #undef LORA_DGS
+  return hipGetLastError();
+}
+
+bool gemm_plan_fusable(const GemmConfig &c) {
+  return c.kind == 4 || (c.kind == 6 && c.sk > 0);
+}
+
+size_t plan_lds_cap(const GemmConfig &c) {
+  if (c.kind == 4) return size_t(c.bm) * kDecodeKC * sizeof(uint16_t);
+  return size_t(3) * TileCfg<256, 128, 2, 2>::STAGE;
+}
+
+hipError_t launch_gemm_plan(const GemmConfig &c, const GemmArgs &g, const PlanLaunch &pl,
+                            hipStream_t s) {
+  if (!gemm_plan_fusable(c) || pl.lds_bytes > plan_lds_cap(c)) return hipErrorInvalidConfiguration;
+  if (c.kind == 4) {
+    const int gx = (g.N + 127) / 128, gy = (g.M + c.bm - 1) / c.bm;
+    const dim3 grid(unsigned(1 + gx * gy * c.splits)), block(256);
+    const size_t lds = plan_lds_cap(c);
+#define LORA_DGP(MB) do { \
+    if (pl.lds) hipLaunchKernelGGL((decode_gemm_plan_kernel<MB, true>), grid, block, lds, s, g, pl.a, gx, gy); \
+    else hipLaunchKernelGGL((decode_gemm_plan_kernel<MB, false>), grid, block, lds, s, g, pl.a, gx, gy); \
+  } while (0)
+    if (c.bm == 32) LORA_DGP(1);
+    else if (c.bm == 64) LORA_DGP(2);
+    else LORA_DGP(4);
+#undef LORA_DGP
+    return hipGetLastError();
+  }
+  const dim3 grid(unsigned(1 + c.sk)), block(256);
+  if (pl.lds) hipLaunchKernelGGL((gemm_tile_plan_kernel<256, 128, 2, 2, 3, true>), grid, block, 0, s, g, pl.a);
+  else hipLaunchKernelGGL((gemm_tile_plan_kernel<256, 128, 2, 2, 3, false>), grid, block, 0, s, g, pl.a);
   return hipGetLastError();
 }
 

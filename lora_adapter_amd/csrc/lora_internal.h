@@ -262,6 +262,30 @@ struct SegOuterArgs {
   int32_t *err_word;
 };
 
+// Arguments of the plan workgroup (plan_build).
+struct PlanArgs {
+  const int32_t *ids;
+  const float *gates;
+  int T, K, N;
+  const int32_t *rank, *page_start, *page_ids;
+  int64_t n_pages, n_page_ids;
+  int32_t *plan;
+  int slot_cache;    // 1: per-slot adapters cached in LDS
+  int use_tile;      // 1: segments of >= kBigSegPairs pairs go to the MFMA shrink
+};
+
+// A plan workgroup's arguments and LDS use for a block of nt threads with
+// lds_cap bytes of LDS: the per-adapter arrays go to LDS (lds) when they fit
+// there, else to the plan buffer's scratch; the per-slot adapter cache goes
+// to LDS when it fits too.  lds_bytes: LDS the plan workgroup uses.
+struct PlanLaunch {
+  PlanArgs a;
+  bool lds;
+  size_t lds_bytes;
+};
+PlanLaunch plan_setup(const int32_t *ids, const float *gates, int T, int K, const PoolView &pool,
+                      int32_t *plan, int nt, size_t lds_cap);
+
 // ----------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.
 hipError_t launch_plan(const int32_t *ids, const float *gates, int T, int K, const PoolView &pool,
@@ -292,6 +316,13 @@ bool decode_shrink_fusable(const GemmConfig &c, int d_in);
 // launched separately by the caller).
 hipError_t launch_decode_gemm_shrink(const GemmConfig &c, const GemmArgs &g, const ShrinkArgs &sa,
                                      hipStream_t s);
+// Split base GEMM (decode kind 4, or stream-K kind 6) whose first workgroup
+// builds the plan (pl, set up for 256 threads and plan_lds_cap(c) bytes)
+// while the others compute the partials; same partials as launch_base_gemm.
+bool gemm_plan_fusable(const GemmConfig &c);
+size_t plan_lds_cap(const GemmConfig &c);
+hipError_t launch_gemm_plan(const GemmConfig &c, const GemmArgs &g, const PlanLaunch &pl,
+                            hipStream_t s);
 // The MFMA shrink of the big segments alone (no-op unless enabled).
 hipError_t launch_shrink_big(const ShrinkArgs &a, int dtype, int64_t TK, int64_t n_adapters,
                              int d_in, int d_out, hipStream_t s);

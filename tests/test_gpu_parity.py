@@ -263,6 +263,46 @@ def test_split_and_fused_entry_points_agree(cfg):
     assert np.array_equal(Y1, L.Y_host())
 
 
+@pytest.mark.parametrize("cfg", ["small1", "small2", "small3", "small4", "small5", "full2", "full3",
+                                 "full5"])
+def test_forward_matches_plan_then_apply(cfg):
+    """lora_forward builds the plan inside the split GEMM launch (one extra
+    workgroup, 256 threads, the GEMM's LDS) and then runs the shrink and the
+    epilogue: the plan, U and Y equal those of lora_plan then lora_apply bit
+    for bit.  The same call captured in a graph is replayed three times, with
+    eager work and synchronisation in between, and every replay gives the
+    same Y."""
+    w = small(int(cfg[-1])) if cfg.startswith("small") else full(int(cfg[-1]))
+    L = run(w)
+    P1, U1, Y1 = L.read_plan(), L.U().copy(), L.Y_host().copy()
+
+    def fwd():
+        B.lora_forward(L.ids, L.gates, L.T, L.K, L.X, L.W_t, L.Y, L.keep_mask, L.keep_scale,
+                       L.pool, L.plan, L.ws)
+
+    L.ws.zero_()
+    L.Y.zero_()
+    L.plan.zero_()
+    fwd()
+    torch.cuda.synchronize()
+    assert_plan_equal(L.read_plan(), P1)
+    assert np.array_equal(U1, L.U())
+    assert np.array_equal(Y1, L.Y_host())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fwd()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        L.Y.zero_()
+        L.ws.zero_()
+        L.plan.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_plan_equal(L.read_plan(), P1)
+        assert np.array_equal(Y1, L.Y_host())
+
+
 def test_u_capacity_error_skips_lora_and_flags():
     w = small(2)
     L = D.DeviceLayer(w, max_rank=1)          # U room for one rank row per slot only
