@@ -11,9 +11,10 @@ adapter (synthetic, seeded).
 Measurement
   * value: tokens per second over exactly --steps steps, wall clock between
     two torch.cuda.synchronize() calls.  Each step is one HIP-graph replay of
-    lora_forward (plan + shrink + GEMM + epilogue; for split-K shapes the
-    plan is built by one extra workgroup of the GEMM launch) on one of R
-    rotated copies of the weights
+    lora_forward (plan + shrink + GEMM + epilogue: for decode shapes two
+    launches, GEMM + per-slot shrink, then epilogue + plan; for stream-K
+    shapes the plan is built inside the GEMM launch) on one of R rotated
+    copies of the weights
     and adapter pool, R chosen so that R copies exceed 1 GiB: every step reads
     its W and pages from HBM, not from the 256 MiB Infinity Cache.
     value_apply_only: the same without the plan (built once per batch and
@@ -183,6 +184,10 @@ def main():
 
     stages = {
         "plan": lambda c, u: B.lora_plan(u, gates, T, K, c.pool, c.plan),
+        "fwd_gemm": lambda c, u: B.lora_forward_gemm(u, gates, T, K, c.X, c.W_t, c.Y, mask,
+                                                     L.keep_scale, c.pool, c.plan, c.ws),
+        "fwd_finish": lambda c, u: B.lora_forward_finish(u, gates, T, K, c.X, c.W_t, c.Y, mask,
+                                                         L.keep_scale, c.pool, c.plan, c.ws),
         "shrink_gemm": lambda c, u: B.lora_shrink_gemm(c.X, c.W_t, c.Y, T, K, gates, mask,
                                                        L.keep_scale, c.pool, c.plan, c.ws),
         "shrink": lambda c, u: B.lora_shrink(c.X, mask, L.keep_scale, T, K, gates, c.pool, c.plan, c.ws),
@@ -333,27 +338,40 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def gemm_kernel_name(T, d_in, dtype_code, B, fused):
+def gemm_kernel_name(T, d_in, d_out, dtype_code, B, fused):
+    """The launch that runs the base GEMM inside lora_forward (the library's
+    shape rules: decode GEMM for T <= 128, with the per-slot shrink in the
+    same launch; fused-epilogue 256 x 256 tiles when they fill the GPU; else
+    256 x 128 stream-K tiles over 255 workgroups when there are at least 4
+    units each, with the plan built in the same launch)."""
     if dtype_code != B.LORA_BF16:
         return "gemm_f32_kernel"
     if T <= 128:
-        return "decode_gemm_shrink_kernel" if d_in <= 4096 else "gemm_decode_kernel"
-    return "gemm_tile_kernel" + (" (fused expand)" if fused else "")
+        return "decode_gemm_slot_kernel"
+    if fused:
+        return "gemm_tile_kernel (fused expand)"
+    units = ((T + 255) // 256) * ((d_out + 127) // 128) * (d_in // 64)
+    return "gemm_tile_plan_kernel" if units >= 4 * 255 else "gemm_tile_kernel"
 
 
 def gemm_roofline(B, L, w, T, st_med, base_flops, P, R_pairs, R_used, e):
-    """Roofline entry of the kernel that runs the base GEMM, from its
-    measured duration.  For decode shapes with d_in <= 4096 that kernel also
-    runs the shrink: its algorithmic bytes then include the used A pages, the
-    keep mask and U."""
+    """Roofline entry of the kernel that runs the base GEMM in the step, from
+    its measured duration.  When that launch also runs the per-slot shrink
+    (decode) its algorithmic bytes add the used A pages (each once), U and
+    the slot descriptors; when it builds the plan (stream-K), the plan's
+    inputs (ids, gates, the pool's rank and page tables)."""
     fused = T > 128 and ((T + 255) // 256) * ((w.d_out + 255) // 256) >= 256
-    name = gemm_kernel_name(T, w.d_in, L.dtype, B, fused)
+    name = gemm_kernel_name(T, w.d_in, w.d_out, L.dtype, B, fused)
     alg_bytes = (w.d_in * w.d_out + T * w.d_in) * e
     flops = base_flops + (2.0 * R_pairs * w.d_out if fused else 0.0)
-    if name == "decode_gemm_shrink_kernel":
-        t_us = st_med["shrink_gemm"]
-        alg_bytes += R_used * w.d_in * e + 4 * R_pairs + (T * w.d_in if L.keep_mask is not None else 0)
+    if name == "decode_gemm_slot_kernel":
+        t_us = st_med["fwd_gemm"]
+        alg_bytes += R_used * w.d_in * e + 4 * R_pairs + 16 * T * w.K
+        alg_bytes += T * w.d_in if L.keep_mask is not None else 0
         flops += 2.0 * R_pairs * w.d_in
+    elif name == "gemm_tile_plan_kernel":
+        t_us = st_med["fwd_gemm"]
+        alg_bytes += 8 * T * w.K + 8 * w.n_adapters + 4 * R_used
     else:
         t_us = st_med["gemm"]
     intensity = base_flops / ((w.d_in * w.d_out + T * w.d_in + T * w.d_out) * e)
@@ -377,7 +395,7 @@ def gemm_roofline(B, L, w, T, st_med, base_flops, P, R_pairs, R_used, e):
 def kernel_source_hash():
     import hashlib
     h = hashlib.sha256()
-    for f in ("gemm.hip", "shrink_units.h", "lora_internal.h"):
+    for f in ("gemm.hip", "shrink_units.h", "lora_internal.h", "plan_build.h"):
         with open(os.path.join(ROOT, "lora_adapter_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -420,12 +438,13 @@ def pmc_summary(workload_id, fetch_csv, write_csv):
 
     w = wl.config(workload_id)
     T = w.T
-    kname = gemm_kernel_name(T, w.d_in, 1 if w.dtype == "bf16" else 0,
-                             type("B", (), {"LORA_BF16": 1}), False).split(" ")[0]
+    fused = T > 128 and ((T + 255) // 256) * ((w.d_out + 255) // 256) >= 256
+    kname = gemm_kernel_name(T, w.d_in, w.d_out, 1 if w.dtype == "bf16" else 0,
+                             type("B", (), {"LORA_BF16": 1}), fused).split(" ")[0]
 
     def name_of(k):
-        for n in ("decode_gemm_shrink_kernel", "gemm_decode_kernel", "gemm_tile_kernel",
-                  "gemm_f32_kernel"):
+        for n in ("decode_gemm_slot_kernel", "gemm_tile_plan_kernel", "decode_gemm_shrink_kernel",
+                  "gemm_decode_kernel", "gemm_tile_kernel", "gemm_f32_kernel"):
             if n in k:
                 return n
         return None
@@ -441,8 +460,7 @@ def pmc_summary(workload_id, fetch_csv, write_csv):
         scale = COPY_PROBE_BYTES / float(np.median(copy))
         out[counter] = {"raw_bytes_median": float(np.median(gemm)), "copy_scale": scale,
                         "bytes": float(np.median(gemm)) * scale, "dispatches": len(gemm)}
-    name = gemm_kernel_name(T, w.d_in, 1 if w.dtype == "bf16" else 0,
-                            type("B", (), {"LORA_BF16": 1}), False).split(" ")[0]
+    name = kname
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as fh:

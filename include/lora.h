@@ -160,7 +160,9 @@ int32_t lora_plan(const int32_t *ids, const float *gates, int32_t T, int32_t K,
  *   keep_mask [T][d_in] uint8 0/1 or NULL, keep_scale its scale (1/keep_p),
  *     applied to the LoRA branch input only,
  *   ws     workspace of >= lora_apply_workspace_bytes(T, K, d_in, d_out,
- *          max_rank, dtype) bytes; U stays in it for lora_grad.
+ *          max_rank, dtype) bytes (split-K partials; for decode shapes U per
+ *          slot, LORA_MAX_RANK floats each, and a 16-byte descriptor per
+ *          slot; U); U stays in it for lora_grad.
  * Rows whose slots are all inactive equal the base-only result bit for bit.
  * Errors: INVALID_ARG, UNSUPPORTED (d_in or d_out not a multiple of 64,
  * dtype mismatch), CAPACITY (ws_bytes too small for the base GEMM stage),
@@ -200,16 +202,41 @@ int32_t lora_apply(const void *X, const void *W_t, void *Y, int32_t T, int32_t K
                    float keep_scale, const lora_pool_desc *pool, const void *plan, void *ws,
                    size_t ws_bytes, void *stream);
 
-/* lora_plan then lora_apply for one batch, as one call.  The base GEMM does
- * not depend on the routing: for shapes whose GEMM writes split-K partials
- * (decode, T <= 128, bf16; stream-K shapes) the plan is built by one extra
- * workgroup of the GEMM launch while the others compute the partials, so
- * the plan costs no launch and no time of its own on the critical path; the
- * shrink and the epilogue follow.  Other shapes run lora_plan then
- * lora_apply.  Plan, U and Y equal those of lora_plan followed by lora_apply
- * with the same arguments, bit for bit.
+/* lora_plan then lora_apply for one batch, as one call, in two launches
+ * for the shapes whose base GEMM writes split-K partials (the GEMM does not
+ * depend on the routing, so the plan is built beside other work):
+ *   decode (T <= 128, bf16):
+ *     lora_forward_gemm:   the GEMM's partials, and the shrink per slot (each
+ *       active slot gathers its own adapter's A pages, which needs no plan:
+ *       Punica-style gather for few tokens per adapter) into a per-slot part
+ *       of the workspace, with a descriptor per slot;
+ *     lora_forward_finish: the epilogue (partials + expand from the per-slot
+ *       U and descriptors, one rounding), and in the same launch the plan,
+ *       whose workgroup also stores U in the u_off layout.
+ *   stream-K shapes:
+ *     lora_forward_gemm:   the GEMM's partials with the plan built by one
+ *       more workgroup of the launch;
+ *     lora_forward_finish: lora_shrink, then lora_expand_epilogue.
+ *   other shapes: lora_forward_gemm = lora_plan, lora_forward_finish =
+ *     lora_apply.
+ * lora_forward = lora_forward_gemm then lora_forward_finish (same
+ * arguments, same stream).  A slot is active under the plan's rule (id in
+ * range, gate not 0, rank 1..LORA_MAX_RANK, consistent page_start, page ids
+ * in range).  The per-slot shrink adds the same products in the same order
+ * as the plan-driven shrink, so plan, U and Y equal those of lora_plan then
+ * lora_apply bit for bit, except: on the decode path, when U does not fit
+ * the workspace, the LoRA term is still added (from the per-slot U) and
+ * LORA_DEVERR_CAPACITY is set, U is not stored.
  *   Arguments as for lora_plan and lora_apply, on one stream.
  * Errors: those of lora_plan and lora_apply. */
+int32_t lora_forward_gemm(const int32_t *ids, const float *gates, int32_t T, int32_t K,
+                          const void *X, const void *W_t, void *Y, const uint8_t *keep_mask,
+                          float keep_scale, const lora_pool_desc *pool, void *plan,
+                          size_t plan_bytes, void *ws, size_t ws_bytes, void *stream);
+int32_t lora_forward_finish(const int32_t *ids, const float *gates, int32_t T, int32_t K,
+                            const void *X, const void *W_t, void *Y, const uint8_t *keep_mask,
+                            float keep_scale, const lora_pool_desc *pool, void *plan,
+                            size_t plan_bytes, void *ws, size_t ws_bytes, void *stream);
 int32_t lora_forward(const int32_t *ids, const float *gates, int32_t T, int32_t K,
                      const void *X, const void *W_t, void *Y, const uint8_t *keep_mask,
                      float keep_scale, const lora_pool_desc *pool, void *plan, size_t plan_bytes,

@@ -26,7 +26,7 @@ EXPORTS = (
     "lora_abi_version", "lora_status_string", "lora_plan_bytes", "lora_plan_layout", "lora_plan",
     "lora_apply_workspace_bytes", "lora_apply_u_offset", "lora_shrink", "lora_base_expand",
     "lora_base_gemm", "lora_expand_epilogue", "lora_shrink_gemm", "lora_apply",
-    "lora_forward", "lora_merge_delta", "lora_grad_workspace_bytes", "lora_grad",
+    "lora_forward_gemm", "lora_forward_finish", "lora_forward", "lora_merge_delta", "lora_grad_workspace_bytes", "lora_grad",
 )
 
 
@@ -63,6 +63,10 @@ _PROTOS = {
     "lora_expand_epilogue": (_I32, [_VP, _VP, _VP, _I32, _I32, _PD, _VP, _VP, _SZ, _VP]),
     "lora_shrink_gemm": (_I32, [_VP, _VP, _VP, _I32, _I32, _VP, _VP, _F32, _PD, _VP, _VP, _SZ, _VP]),
     "lora_apply": (_I32, [_VP, _VP, _VP, _I32, _I32, _VP, _VP, _F32, _PD, _VP, _VP, _SZ, _VP]),
+    "lora_forward_gemm": (_I32, [_VP, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _F32, _PD, _VP, _SZ,
+                                 _VP, _SZ, _VP]),
+    "lora_forward_finish": (_I32, [_VP, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _F32, _PD, _VP, _SZ,
+                                   _VP, _SZ, _VP]),
     "lora_forward": (_I32, [_VP, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _F32, _PD, _VP, _SZ, _VP,
                             _SZ, _VP]),
     "lora_merge_delta": (_I32, [_VP, _PD, _VP, _VP, _I32, _VP]),
@@ -196,12 +200,29 @@ def lora_apply(X, W_t, Y, T: int, K: int, gates, keep_mask, keep_scale: float, p
                                           _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
-def lora_forward(ids, gates, T: int, K: int, X, W_t, Y, keep_mask, keep_scale: float, pool: Pool,
-                 plan, ws, stream=None):
-    _check("lora_forward", lib().lora_forward(
+def _forward_call(name, ids, gates, T, K, X, W_t, Y, keep_mask, keep_scale, pool, plan, ws, stream):
+    _check(name, getattr(lib(), name)(
         _ptr(ids), _ptr(gates), T, K, _ptr(X), _ptr(W_t), _ptr(Y), _ptr(keep_mask),
         float(keep_scale), pool.ref, _ptr(plan), plan.numel() * plan.element_size(), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def lora_forward_gemm(ids, gates, T: int, K: int, X, W_t, Y, keep_mask, keep_scale: float,
+                      pool: Pool, plan, ws, stream=None):
+    _forward_call("lora_forward_gemm", ids, gates, T, K, X, W_t, Y, keep_mask, keep_scale, pool,
+                  plan, ws, stream)
+
+
+def lora_forward_finish(ids, gates, T: int, K: int, X, W_t, Y, keep_mask, keep_scale: float,
+                        pool: Pool, plan, ws, stream=None):
+    _forward_call("lora_forward_finish", ids, gates, T, K, X, W_t, Y, keep_mask, keep_scale, pool,
+                  plan, ws, stream)
+
+
+def lora_forward(ids, gates, T: int, K: int, X, W_t, Y, keep_mask, keep_scale: float, pool: Pool,
+                 plan, ws, stream=None):
+    _forward_call("lora_forward", ids, gates, T, K, X, W_t, Y, keep_mask, keep_scale, pool, plan,
+                  ws, stream)
 
 
 def lora_merge_delta(W_t, pool: Pool, merge_ids, coeffs, m: int, stream=None):

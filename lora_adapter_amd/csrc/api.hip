@@ -36,22 +36,43 @@ int32_t check_batch(int32_t T, int32_t K) {
 
 int32_t dev(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_ERR_DEVICE; }
 
+// Apply workspace: [split partials][U per slot, slot descriptors (decode
+// shapes)][U].  The per-slot U (LORA_MAX_RANK floats per slot) and the slot
+// descriptors are written by the per-slot shrink of lora_forward's decode
+// launch.
 struct ApplyWs {
   GemmConfig cfg;
   size_t partial_bytes;   // aligned
   float *partial;
+  float *slot_u;          // decode shapes: [T*K][LORA_MAX_RANK]
+  int4 *sdesc;            // decode shapes: [T*K]
   float *U;
   int64_t u_cap;
 };
 
-ApplyWs apply_layout(void *ws, size_t ws_bytes, int32_t T, int32_t d_in, int32_t d_out, int32_t dtype) {
+size_t slot_u_only_bytes(int32_t T, int32_t K) {
+  return align_up(size_t(T) * size_t(K) * LORA_MAX_RANK * sizeof(float));
+}
+
+size_t slot_u_bytes(const GemmConfig &c, int32_t T, int32_t K) {
+  return c.kind == 4 ? slot_u_only_bytes(T, K) + align_up(size_t(T) * size_t(K) * sizeof(int4)) : 0;
+}
+
+ApplyWs apply_layout(void *ws, size_t ws_bytes, int32_t T, int32_t K, int32_t d_in, int32_t d_out,
+                     int32_t dtype) {
   ApplyWs w{};
   w.cfg = choose_gemm(T > 0 ? T : 1, d_in, d_out, dtype);
   w.partial_bytes = align_up(gemm_partial_bytes(w.cfg, T, d_out));
+  const size_t head = w.partial_bytes + slot_u_bytes(w.cfg, T, K);
   w.partial = static_cast<float *>(ws);
-  if (ws && ws_bytes >= w.partial_bytes) {
-    w.U = reinterpret_cast<float *>(static_cast<char *>(ws) + w.partial_bytes);
-    w.u_cap = int64_t((ws_bytes - w.partial_bytes) / sizeof(float));
+  if (ws && ws_bytes >= head) {
+    w.slot_u = w.cfg.kind == 4
+                   ? reinterpret_cast<float *>(static_cast<char *>(ws) + w.partial_bytes) : nullptr;
+    w.sdesc = w.cfg.kind == 4
+                  ? reinterpret_cast<int4 *>(static_cast<char *>(ws) + w.partial_bytes +
+                                             slot_u_only_bytes(T, K)) : nullptr;
+    w.U = reinterpret_cast<float *>(static_cast<char *>(ws) + head);
+    w.u_cap = int64_t((ws_bytes - head) / sizeof(float));
   } else {
     w.U = nullptr;
     w.u_cap = -1;
@@ -111,13 +132,14 @@ size_t lora_apply_workspace_bytes(int32_t T, int32_t K, int32_t d_in, int32_t d_
   if (dtype != LORA_F32 && dtype != LORA_BF16) return 0;
   const GemmConfig c = choose_gemm(T > 0 ? T : 1, d_in, d_out, dtype);
   const size_t u = size_t(T) * size_t(K) * size_t(max_rank) * sizeof(float);
-  return align_up(gemm_partial_bytes(c, T, d_out)) + align_up(u > 0 ? u : 1);
+  return align_up(gemm_partial_bytes(c, T, d_out)) + slot_u_bytes(c, T, K) + align_up(u > 0 ? u : 1);
 }
 
 size_t lora_apply_u_offset(int32_t T, int32_t K, int32_t d_in, int32_t d_out, int32_t dtype) {
   if (check_batch(T, K) != LORA_OK || !dims_ok(d_in) || !dims_ok(d_out)) return 0;
   if (dtype != LORA_F32 && dtype != LORA_BF16) return 0;
-  return align_up(gemm_partial_bytes(choose_gemm(T > 0 ? T : 1, d_in, d_out, dtype), T, d_out));
+  const GemmConfig c = choose_gemm(T > 0 ? T : 1, d_in, d_out, dtype);
+  return align_up(gemm_partial_bytes(c, T, d_out)) + slot_u_bytes(c, T, K);
 }
 
 namespace {
@@ -153,7 +175,7 @@ int32_t lora_shrink(const void *X, const uint8_t *keep_mask, float keep_scale, i
   if (!plan) return LORA_ERR_INVALID_ARG;
   if (T == 0) return LORA_OK;
   if (!X || !gates || !ws) return LORA_ERR_INVALID_ARG;
-  const ApplyWs w = apply_layout(ws, ws_bytes, T, pool->d_in, pool->d_out, pool->dtype);
+  const ApplyWs w = apply_layout(ws, ws_bytes, T, K, pool->d_in, pool->d_out, pool->dtype);
   if (w.u_cap < 0) return LORA_ERR_CAPACITY;
   const int64_t TK = int64_t(T) * K;
   const PlanView pv = plan_view(plan, TK, pool->n_adapters);
@@ -175,7 +197,7 @@ int32_t base_args(const void *X, const void *W_t, void *Y, int32_t T, int32_t K,
   if (T == 0) return LORA_OK;
   if (!X || !W_t || !Y || !ws) return LORA_ERR_INVALID_ARG;
   if (Y == X || Y == W_t) return LORA_ERR_INVALID_ARG;
-  const ApplyWs w = apply_layout(ws, ws_bytes, T, pool->d_in, pool->d_out, pool->dtype);
+  const ApplyWs w = apply_layout(ws, ws_bytes, T, K, pool->d_in, pool->d_out, pool->dtype);
   if (w.u_cap < 0) return LORA_ERR_CAPACITY;
   const int64_t TK = int64_t(T) * K;
   const PlanView pv = plan_view(plan, TK, pool->n_adapters);
@@ -233,7 +255,7 @@ int32_t lora_shrink_gemm(const void *X, const void *W_t, void *Y, int32_t T, int
   if (st != LORA_OK || T == 0) return st;
   if (!gates) return LORA_ERR_INVALID_ARG;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const ApplyWs w = apply_layout(ws, ws_bytes, T, pool->d_in, pool->d_out, pool->dtype);
+  const ApplyWs w = apply_layout(ws, ws_bytes, T, K, pool->d_in, pool->d_out, pool->dtype);
   const int64_t TK = int64_t(T) * K;
   const PlanView pv = plan_view(plan, TK, pool->n_adapters);
   const ShrinkArgs a = apply_shrink_args(X, keep_mask, keep_scale, T, K, gates, pool, pv, w);
@@ -262,40 +284,108 @@ int32_t lora_apply(const void *X, const void *W_t, void *Y, int32_t T, int32_t K
   return lora_expand_epilogue(X, W_t, Y, T, K, pool, plan, ws, ws_bytes, stream);
 }
 
-int32_t lora_forward(const int32_t *ids, const float *gates, int32_t T, int32_t K,
-                     const void *X, const void *W_t, void *Y, const uint8_t *keep_mask,
-                     float keep_scale, const lora_pool_desc *pool, void *plan, size_t plan_bytes,
-                     void *ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// lora_forward's two halves.  Split GEMM shapes only (gemm_plan_fusable):
+//   decode:   first = GEMM partials + per-slot shrink (U per slot and slot
+//             descriptors); finish = epilogue from those, with the plan
+//             built (and U stored in the u_off layout) in the same launch.
+//   stream-K: first = GEMM partials with the plan built in the same launch;
+//             finish = shrink, then epilogue.
+// Other shapes: first = lora_plan, finish = lora_apply.
+struct Fwd {
+  GemmConfig cfg;
+  GemmArgs g;
+  bool split;
+};
+
+int32_t forward_args(const int32_t *ids, const float *gates, int32_t T, int32_t K, const void *X,
+                     const void *W_t, void *Y, const lora_pool_desc *pool, void *plan,
+                     size_t plan_bytes, void *ws, size_t ws_bytes, Fwd &f) {
   int32_t st = check_batch(T, K);
   if (st != LORA_OK) return st;
   if ((st = check_pool(pool, true)) != LORA_OK) return st;
   if (!plan) return LORA_ERR_INVALID_ARG;
   if (plan_bytes < lora_plan_bytes(T, K, pool->n_adapters)) return LORA_ERR_CAPACITY;
-  if (T == 0) return lora_plan(ids, gates, T, K, pool, plan, plan_bytes, stream);
+  f.split = false;
+  if (T == 0) return LORA_OK;
   if (!ids || !gates || !X || !W_t || !Y || !ws) return LORA_ERR_INVALID_ARG;
-  GemmConfig cfg;
-  GemmArgs g;
-  if ((st = base_args(X, W_t, Y, T, K, pool, plan, ws, ws_bytes, cfg, g)) != LORA_OK) return st;
-  if (!gemm_plan_fusable(cfg)) {
-    st = lora_plan(ids, gates, T, K, pool, plan, plan_bytes, stream);
-    if (st != LORA_OK) return st;
+  if ((st = base_args(X, W_t, Y, T, K, pool, plan, ws, ws_bytes, f.cfg, f.g)) != LORA_OK) return st;
+  f.split = gemm_plan_fusable(f.cfg);
+  return LORA_OK;
+}
+
+PlanLaunch forward_plan(const int32_t *ids, const float *gates, int32_t T, int32_t K,
+                        const lora_pool_desc *pool, void *plan, const Fwd &f, const ApplyWs &w) {
+  PlanLaunch pl = plan_setup(ids, gates, T, K, pool_view(pool), static_cast<int32_t *>(plan), 256,
+                             plan_lds_cap(f.cfg));
+  if (w.slot_u) {
+    pl.a.slot_u = w.slot_u;
+    pl.a.u_out = w.U;
+    pl.a.u_cap = w.u_cap;
+    pl.a.slot_stride = LORA_MAX_RANK;
+  }
+  return pl;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t lora_forward_gemm(const int32_t *ids, const float *gates, int32_t T, int32_t K,
+                          const void *X, const void *W_t, void *Y, const uint8_t *keep_mask,
+                          float keep_scale, const lora_pool_desc *pool, void *plan,
+                          size_t plan_bytes, void *ws, size_t ws_bytes, void *stream) {
+  Fwd f;
+  int32_t st = forward_args(ids, gates, T, K, X, W_t, Y, pool, plan, plan_bytes, ws, ws_bytes, f);
+  if (st != LORA_OK) return st;
+  if (!f.split) return lora_plan(ids, gates, T, K, pool, plan, plan_bytes, stream);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const ApplyWs w = apply_layout(ws, ws_bytes, T, K, pool->d_in, pool->d_out, pool->dtype);
+  if (w.slot_u) {
+    SlotShrinkArgs ss{};
+    ss.ids = ids; ss.gates = gates; ss.K = K; ss.N = pool->n_adapters;
+    ss.Z = X; ss.mask = keep_mask; ss.extra_scale = keep_mask ? keep_scale : 1.0f;
+    ss.d = pool->d_in; ss.pages = pool->a_pages;
+    ss.rank = pool->rank; ss.page_start = pool->page_start; ss.page_ids = pool->page_ids;
+    ss.scale = pool->scale; ss.n_pages = pool->n_pages; ss.n_page_ids = pool->n_page_ids;
+    ss.out = w.slot_u; ss.stride = LORA_MAX_RANK; ss.n_slots = T * K; ss.sdesc = w.sdesc;
+    return dev(launch_decode_slot(f.cfg, f.g, ss, s));
+  }
+  return dev(launch_gemm_plan(f.cfg, f.g, forward_plan(ids, gates, T, K, pool, plan, f, w), s));
+}
+
+int32_t lora_forward_finish(const int32_t *ids, const float *gates, int32_t T, int32_t K,
+                            const void *X, const void *W_t, void *Y, const uint8_t *keep_mask,
+                            float keep_scale, const lora_pool_desc *pool, void *plan,
+                            size_t plan_bytes, void *ws, size_t ws_bytes, void *stream) {
+  Fwd f;
+  int32_t st = forward_args(ids, gates, T, K, X, W_t, Y, pool, plan, plan_bytes, ws, ws_bytes, f);
+  if (st != LORA_OK || T == 0) return st;
+  if (!f.split)
     return lora_apply(X, W_t, Y, T, K, gates, keep_mask, keep_scale, pool, plan, ws, ws_bytes,
                       stream);
-  }
-  // split GEMM with the plan built in its first workgroup, then the shrink,
-  // then the epilogue
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const PlanLaunch pl = plan_setup(ids, gates, T, K, pool_view(pool), static_cast<int32_t *>(plan),
-                                   256, plan_lds_cap(cfg));
-  hipError_t e = launch_gemm_plan(cfg, g, pl, s);
-  if (e != hipSuccess) return LORA_ERR_DEVICE;
-  const ApplyWs w = apply_layout(ws, ws_bytes, T, pool->d_in, pool->d_out, pool->dtype);
-  const int64_t TK = int64_t(T) * K;
-  const PlanView pv = plan_view(plan, TK, pool->n_adapters);
-  const ShrinkArgs sa = apply_shrink_args(X, keep_mask, keep_scale, T, K, gates, pool, pv, w);
-  e = launch_shrink(sa, pool->dtype, TK, pool->n_adapters, pool->d_in, pool->d_out, s);
-  if (e != hipSuccess) return LORA_ERR_DEVICE;
-  return dev(launch_epilogue(cfg, g, pool->dtype, s));
+  const ApplyWs w = apply_layout(ws, ws_bytes, T, K, pool->d_in, pool->d_out, pool->dtype);
+  if (w.slot_u)
+    return dev(launch_epilogue_plan(f.cfg, f.g, pool->dtype, w.slot_u, w.sdesc,
+                                    forward_plan(ids, gates, T, K, pool, plan, f, w), s));
+  st = lora_shrink(X, keep_mask, keep_scale, T, K, gates, pool, plan, ws, ws_bytes, stream);
+  if (st != LORA_OK) return st;
+  return lora_expand_epilogue(X, W_t, Y, T, K, pool, plan, ws, ws_bytes, stream);
+}
+
+int32_t lora_forward(const int32_t *ids, const float *gates, int32_t T, int32_t K,
+                     const void *X, const void *W_t, void *Y, const uint8_t *keep_mask,
+                     float keep_scale, const lora_pool_desc *pool, void *plan, size_t plan_bytes,
+                     void *ws, size_t ws_bytes, void *stream) {
+  int32_t st = lora_forward_gemm(ids, gates, T, K, X, W_t, Y, keep_mask, keep_scale, pool, plan,
+                                 plan_bytes, ws, ws_bytes, stream);
+  if (st != LORA_OK || T == 0) return st;
+  return lora_forward_finish(ids, gates, T, K, X, W_t, Y, keep_mask, keep_scale, pool, plan,
+                             plan_bytes, ws, ws_bytes, stream);
 }
 
 int32_t lora_merge_delta(void *W_t, const lora_pool_desc *pool, const int32_t *merge_ids,
@@ -344,7 +434,7 @@ int32_t lora_grad(const void *X, const uint8_t *keep_mask, float keep_scale, con
   const size_t need = lora_grad_workspace_bytes(T, K, pool->n_adapters, pool->d_in, pool->d_out,
                                                 max_rank, pool->dtype);
   if (ws_bytes < need) return LORA_ERR_CAPACITY;
-  const ApplyWs aw = apply_layout(const_cast<void *>(apply_ws), apply_ws_bytes, T, pool->d_in,
+  const ApplyWs aw = apply_layout(const_cast<void *>(apply_ws), apply_ws_bytes, T, K, pool->d_in,
                               pool->d_out, pool->dtype);
   if (aw.u_cap < 0) return LORA_ERR_CAPACITY;
   const PlanView pv = plan_view(plan, TK, pool->n_adapters);

@@ -480,18 +480,19 @@ __global__ __launch_bounds__(256, 2) void decode_gemm_shrink_kernel(GemmArgs g, 
     shrink_units_wave<uint16_t, kMask, kCh, true>(s, w);
 }
 
-// Decode GEMM tiles in workgroups 1 .., with the plan built by workgroup 0
-// in the LDS the others use for their token rows (dynamic: MB*32*KC bf16).
-template <int MB, bool kLds>
-__global__ __launch_bounds__(256) void decode_gemm_plan_kernel(GemmArgs g, PlanArgs pa, int gx,
-                                                                int gy) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t dxs[];
-  if (blockIdx.x == 0) {
-    plan_build<kLds>(pa, reinterpret_cast<int *>(dxs));
+// Decode GEMM tiles in workgroups 0 .. n_gemm-1 (dealt one per CU), and the
+// per-slot shrink in the workgroups after them (second places beside the
+// tiles).  Neither reads what the other writes, and neither needs the plan.
+template <int MB, bool kMask>
+__global__ __launch_bounds__(256) void decode_gemm_slot_kernel(GemmArgs g, SlotShrinkArgs ss,
+                                                                int gx, int gy, int n_gemm) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[MB * 32 * kDecodeKC];
+  const int b = blockIdx.x;
+  if (b < n_gemm) {
+    decode_tile<MB>(g, b % gx, (b / gx) % gy, b / (gx * gy), xs);
     return;
   }
-  const int t = blockIdx.x - 1;
-  decode_tile<MB>(g, t % gx, (t / gx) % gy, t / (gx * gy), dxs);
+  slot_shrink_wg<kMask>(ss, b - n_gemm);
 }
 
 // ------------------------------------------------------------ pipelined tile GEMM
@@ -981,17 +982,17 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_tile_kernel(GemmArgs g) 
                                        blockIdx.y);
 }
 
-// Stream-K GEMM over workgroups 1 .. G, with the plan built by workgroup 0
-// in the LDS the others use for their stages.
+// Stream-K GEMM over workgroups 0 .. G-1, with the plan built by workgroup
+// G in the LDS the others use for their stages (one CU of its own).
 template <int BM, int BN, int WM, int WN, int NS, bool kLds>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_tile_plan_kernel(GemmArgs g, PlanArgs pa) {
   using C = TileCfg<BM, BN, WM, WN>;
   __shared__ __attribute__((aligned(16))) char smem[NS * C::STAGE];
-  if (blockIdx.x == 0) {
+  if (int(blockIdx.x) == g.sk_g) {
     plan_build<kLds>(pa, reinterpret_cast<int *>(smem));
     return;
   }
-  stream_k<BM, BN, WM, WN, NS>(g, smem, blockIdx.x - 1);
+  stream_k<BM, BN, WM, WN, NS>(g, smem, blockIdx.x);
 }
 
 // ------------------------------------------------------------ fp32 GEMM
@@ -1042,8 +1043,22 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float *X, const flo
 // One wave per output row and 512-column chunk: sum the split partials in
 // order, add the expand, round once, store.  16-byte B-row loads, 1 KiB per
 // wave instruction.
-template <typename E>
-__global__ __launch_bounds__(256) void epilogue_kernel(EpilogueArgs a) {
+//
+// kPlan (lora_forward's decode path): the last row of workgroups is not an
+// output row; its first workgroup builds the plan (1: arrays in LDS, 2: in
+// the plan buffer) while the others add the expand from the per-slot U and
+// descriptors, which need no plan.
+template <typename E, int kPlan>
+__global__ __launch_bounds__(256) void epilogue_kernel(EpilogueArgs a, PlanArgs pa) {
+  if constexpr (kPlan != 0) {
+    if (int(blockIdx.y) == int(gridDim.y) - 1) {
+      if (blockIdx.x == 0) {
+        extern __shared__ int edyn[];
+        plan_build<kPlan == 1>(pa, edyn);
+      }
+      return;
+    }
+  }
   constexpr int CPL = 8;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = blockIdx.y * 4 + wave;
@@ -1051,9 +1066,16 @@ __global__ __launch_bounds__(256) void epilogue_kernel(EpilogueArgs a) {
   const int col_raw = (blockIdx.x * 64 + lane) * CPL;
   const bool col_ok = col_raw < a.N;
   const int col = col_ok ? col_raw : a.N - CPL;      // loads stay in bounds
-  const bool lora_on = expand_enabled(a.ex);
+  const bool lora_on = a.sdesc ? a.ex.U != nullptr : expand_enabled(a.ex);
   // the row's slot descriptors first: their round trip overlaps the partials'
-  const int4 sd = lora_on ? expand_row_desc<E>(row, a.ex) : make_int4(-1, 0, 0, 0);
+  int4 sd = make_int4(-1, 0, 0, 0);
+  if (lora_on) {
+    if (a.sdesc) {
+      if (lane < a.ex.K) sd = a.sdesc[row * a.ex.K + lane];
+    } else {
+      sd = expand_row_desc<E>(row, a.ex);
+    }
+  }
   float v[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) v[c] = 0.f;
@@ -1219,40 +1241,66 @@ bool gemm_plan_fusable(const GemmConfig &c) {
   return c.kind == 4 || (c.kind == 6 && c.sk > 0);
 }
 
+// Decode: the plan workgroup's LDS is the epilogue launch's dynamic LDS, which
+// every epilogue workgroup then gets too: kept to 64 KiB.  Stream-K: the
+// tile kernel's stages.
 size_t plan_lds_cap(const GemmConfig &c) {
-  if (c.kind == 4) return size_t(c.bm) * kDecodeKC * sizeof(uint16_t);
+  if (c.kind == 4) return size_t(64) << 10;
   return size_t(3) * TileCfg<256, 128, 2, 2>::STAGE;
 }
 
 hipError_t launch_gemm_plan(const GemmConfig &c, const GemmArgs &g, const PlanLaunch &pl,
                             hipStream_t s) {
-  if (!gemm_plan_fusable(c) || pl.lds_bytes > plan_lds_cap(c)) return hipErrorInvalidConfiguration;
-  if (c.kind == 4) {
-    const int gx = (g.N + 127) / 128, gy = (g.M + c.bm - 1) / c.bm;
-    const dim3 grid(unsigned(1 + gx * gy * c.splits)), block(256);
-    const size_t lds = plan_lds_cap(c);
-#define LORA_DGP(MB) do { \
-    if (pl.lds) hipLaunchKernelGGL((decode_gemm_plan_kernel<MB, true>), grid, block, lds, s, g, pl.a, gx, gy); \
-    else hipLaunchKernelGGL((decode_gemm_plan_kernel<MB, false>), grid, block, lds, s, g, pl.a, gx, gy); \
-  } while (0)
-    if (c.bm == 32) LORA_DGP(1);
-    else if (c.bm == 64) LORA_DGP(2);
-    else LORA_DGP(4);
-#undef LORA_DGP
-    return hipGetLastError();
-  }
+  if (c.kind != 6 || c.sk <= 0 || pl.lds_bytes > plan_lds_cap(c)) return hipErrorInvalidConfiguration;
   const dim3 grid(unsigned(1 + c.sk)), block(256);
   if (pl.lds) hipLaunchKernelGGL((gemm_tile_plan_kernel<256, 128, 2, 2, 3, true>), grid, block, 0, s, g, pl.a);
   else hipLaunchKernelGGL((gemm_tile_plan_kernel<256, 128, 2, 2, 3, false>), grid, block, 0, s, g, pl.a);
   return hipGetLastError();
 }
 
+hipError_t launch_decode_slot(const GemmConfig &c, const GemmArgs &g, const SlotShrinkArgs &ss,
+                              hipStream_t s) {
+  if (c.kind != 4) return hipErrorInvalidConfiguration;
+  const int gx = (g.N + 127) / 128, gy = (g.M + c.bm - 1) / c.bm;
+  const int n_gemm = gx * gy * c.splits;
+  const dim3 grid(unsigned(n_gemm + ss.n_slots)), block(256);
+  const bool m = ss.mask != nullptr;
+#define LORA_DGS2(MB, M) \
+  hipLaunchKernelGGL((decode_gemm_slot_kernel<MB, M>), grid, block, 0, s, g, ss, gx, gy, n_gemm)
+#define LORA_DGS(MB) do { if (m) LORA_DGS2(MB, true); else LORA_DGS2(MB, false); } while (0)
+  if (c.bm == 32) LORA_DGS(1);
+  else if (c.bm == 64) LORA_DGS(2);
+  else LORA_DGS(4);
+#undef LORA_DGS
+#undef LORA_DGS2
+  return hipGetLastError();
+}
+
+hipError_t launch_epilogue_plan(const GemmConfig &c, const GemmArgs &g, int dtype,
+                                const float *slot_u, const int4 *sdesc, const PlanLaunch &pl,
+                                hipStream_t s) {
+  if (c.fused || pl.lds_bytes > plan_lds_cap(c)) return hipErrorInvalidConfiguration;
+  EpilogueArgs e{g.partial, c.splits, g.M, g.N, c.sk, g.Kd / 64, c.bm, c.bn, g.Y, g.ex, sdesc};
+  e.ex.U = slot_u;
+  const dim3 grid((g.N + 511) / 512, (g.M + 3) / 4 + 1);
+  const size_t lds = pl.lds_bytes;
+#define LORA_EP(E) do { \
+    if (pl.lds) hipLaunchKernelGGL((epilogue_kernel<E, 1>), grid, dim3(256), lds, s, e, pl.a); \
+    else hipLaunchKernelGGL((epilogue_kernel<E, 2>), grid, dim3(256), lds, s, e, pl.a); \
+  } while (0)
+  if (dtype == LORA_BF16) LORA_EP(uint16_t);
+  else LORA_EP(float);
+#undef LORA_EP
+  return hipGetLastError();
+}
+
 hipError_t launch_epilogue(const GemmConfig &c, const GemmArgs &g, int dtype, hipStream_t s) {
   if (c.fused) return hipSuccess;
-  EpilogueArgs e{g.partial, c.splits, g.M, g.N, c.sk, g.Kd / 64, c.bm, c.bn, g.Y, g.ex};
+  EpilogueArgs e{g.partial, c.splits, g.M, g.N, c.sk, g.Kd / 64, c.bm, c.bn, g.Y, g.ex, nullptr};
   const dim3 grid((g.N + 511) / 512, (g.M + 3) / 4);
-  if (dtype == LORA_BF16) hipLaunchKernelGGL(epilogue_kernel<uint16_t>, grid, dim3(256), 0, s, e);
-  else hipLaunchKernelGGL(epilogue_kernel<float>, grid, dim3(256), 0, s, e);
+  const PlanArgs none{};
+  if (dtype == LORA_BF16) hipLaunchKernelGGL((epilogue_kernel<uint16_t, 0>), grid, dim3(256), 0, s, e, none);
+  else hipLaunchKernelGGL((epilogue_kernel<float, 0>), grid, dim3(256), 0, s, e, none);
   return hipGetLastError();
 }
 

@@ -202,6 +202,27 @@ struct ShrinkArgs {
                             // (the plan made the same choice from the same predicate)
 };
 
+// Per-slot decode shrink (no plan): out[i * stride + j] for slot i = t*K + k
+// and rank row j of the slot's adapter, when the slot is active and its
+// adapter's page table is consistent (other entries are left untouched).
+struct SlotShrinkArgs {
+  const int32_t *ids;       // [T][K]
+  const float *gates;       // [T][K]
+  int K, N;
+  const void *Z;            // [T][d] bf16
+  const uint8_t *mask;      // [T][d] 0/1 or null
+  float extra_scale;
+  int d;
+  const void *pages;        // [n_pages][d]
+  const int32_t *rank, *page_start, *page_ids;
+  const float *scale;
+  int64_t n_pages, n_page_ids;
+  float *out;
+  int stride;               // floats per slot (LORA_MAX_RANK)
+  int n_slots;              // T*K
+  int4 *sdesc;              // [T*K] {slot, rank, slot*stride, page_start} or {-1,0,0,0}
+};
+
 // Everything the expand needs to add sum_j U[u_off[p]+j] * B_a[j][n] to row t.
 struct ExpandArgs {
   int K;
@@ -231,6 +252,9 @@ struct EpilogueArgs {
   int sk_g, sk_kt, bm, bn;  // stream-K: workgroups, K tiles per output tile, tile shape
   void *Y;
   ExpandArgs ex;
+  // not null: ex.U holds U per slot and sdesc the slot descriptors written by
+  // the per-slot shrink; the plan is not read (lora_forward's decode path)
+  const int4 *sdesc;
 };
 
 struct MergeArgs {
@@ -270,14 +294,22 @@ struct PlanArgs {
   const int32_t *rank, *page_start, *page_ids;
   int64_t n_pages, n_page_ids;
   int32_t *plan;
-  int slot_cache;    // 1: per-slot adapters cached in LDS
+  int slot_cache;    // 1: per-slot adapters and gates cached in LDS
   int use_tile;      // 1: segments of >= kBigSegPairs pairs go to the MFMA shrink
+  int page_cache;    // 1: the page table is copied to LDS (after the slot cache)
+  // not null: U per slot (stride slot_stride) to be stored in the u_off layout
+  // at u_out when the plan's R_pairs <= u_cap (else LORA_DEVERR_CAPACITY)
+  const float *slot_u;
+  float *u_out;
+  int64_t u_cap;
+  int slot_stride;
 };
 
 // A plan workgroup's arguments and LDS use for a block of nt threads with
 // lds_cap bytes of LDS: the per-adapter arrays go to LDS (lds) when they fit
-// there, else to the plan buffer's scratch; the per-slot adapter cache goes
-// to LDS when it fits too.  lds_bytes: LDS the plan workgroup uses.
+// there, else to the plan buffer's scratch; the per-slot adapter cache, then
+// the page table, go to LDS when they fit too.  lds_bytes: LDS the plan
+// workgroup uses.
 struct PlanLaunch {
   PlanArgs a;
   bool lds;
@@ -316,13 +348,22 @@ bool decode_shrink_fusable(const GemmConfig &c, int d_in);
 // launched separately by the caller).
 hipError_t launch_decode_gemm_shrink(const GemmConfig &c, const GemmArgs &g, const ShrinkArgs &sa,
                                      hipStream_t s);
-// Split base GEMM (decode kind 4, or stream-K kind 6) whose first workgroup
-// builds the plan (pl, set up for 256 threads and plan_lds_cap(c) bytes)
-// while the others compute the partials; same partials as launch_base_gemm.
+// lora_forward's launches for split GEMMs.  Decode (kind 4): the GEMM's
+// partials and the per-slot shrink (ss) in one launch (launch_decode_slot),
+// then the epilogue from the slot descriptors with the plan built by one
+// more workgroup of that launch (launch_epilogue_plan).  Stream-K (kind 6):
+// the GEMM's partials with the plan built by one more workgroup
+// (launch_gemm_plan).  The plan workgroup has 256 threads and the LDS that
+// plan_lds_cap(c) gives.
 bool gemm_plan_fusable(const GemmConfig &c);
 size_t plan_lds_cap(const GemmConfig &c);
 hipError_t launch_gemm_plan(const GemmConfig &c, const GemmArgs &g, const PlanLaunch &pl,
                             hipStream_t s);
+hipError_t launch_decode_slot(const GemmConfig &c, const GemmArgs &g, const SlotShrinkArgs &ss,
+                              hipStream_t s);
+hipError_t launch_epilogue_plan(const GemmConfig &c, const GemmArgs &g, int dtype,
+                                const float *slot_u, const int4 *sdesc, const PlanLaunch &pl,
+                                hipStream_t s);
 // The MFMA shrink of the big segments alone (no-op unless enabled).
 hipError_t launch_shrink_big(const ShrinkArgs &a, int dtype, int64_t TK, int64_t n_adapters,
                              int d_in, int d_out, hipStream_t s);

@@ -20,15 +20,18 @@ PlanLaunch plan_setup(const int32_t *ids, const float *gates, int T, int K, cons
   PlanLaunch pl{};
   pl.a = PlanArgs{ids, gates, T, K, pool.n_adapters, pool.rank, pool.page_start, pool.page_ids,
                   pool.n_pages, pool.n_page_ids, plan, 0,
-                  shrink_tile_enabled(pool.dtype, TK, pool.d_in, pool.d_out) ? 1 : 0};
+                  shrink_tile_enabled(pool.dtype, TK, pool.d_in, pool.d_out) ? 1 : 0, 0,
+                  nullptr, nullptr, 0, 0};
   int64_t cap = int64_t(lds_cap / sizeof(int));
   if (cap > kPlanLdsInts) cap = kPlanLdsInts;
   const int64_t adapter_ints = 5 * N + 5 * Smax + 3;
   const int64_t count_cols = (N + nt - 1) / nt * (nt / 64);
   pl.lds = adapter_ints <= cap && count_cols <= kLdsCountCols;
   const int64_t fixed = pl.lds ? adapter_ints : 0;
-  pl.a.slot_cache = fixed + TK <= cap ? 1 : 0;
-  pl.lds_bytes = size_t(fixed + (pl.a.slot_cache ? TK : 0)) * sizeof(int);
+  pl.a.slot_cache = fixed + 2 * TK <= cap ? 1 : 0;
+  const int64_t used = fixed + (pl.a.slot_cache ? 2 * TK : 0);
+  pl.a.page_cache = pl.a.slot_cache && pool.n_page_ids > 0 && used + pool.n_page_ids <= cap ? 1 : 0;
+  pl.lds_bytes = size_t(used + (pl.a.page_cache ? pool.n_page_ids : 0)) * sizeof(int);
   return pl;
 }
 

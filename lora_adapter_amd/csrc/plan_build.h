@@ -190,6 +190,10 @@ __device__ __forceinline__ void plan_build(const PlanArgs &a, int *dyn) {
   // first decode-shrink unit of each segment
   int *seg_uo = kLds ? dyn + 5 * N + 4 * Smax + 2 : P + L.seg_uoff;
   int *slot_ad = dyn + (kLds ? 5 * N + 5 * Smax + 3 : 0);
+  // the whole page table, when it fits (its range check then needs no
+  // global round trip after the segment order)
+  int *slot_g = slot_ad + TK;                 // gate bits of each slot (with the cache)
+  int *pcache = slot_ad + (a.slot_cache ? 2 * TK : 0);
   // counts of used adapters per (bucket, round of nt adapters, wave)
   const int Q = (N + nt - 1) / nt;
   const int E = Q * nwv;
@@ -204,8 +208,21 @@ __device__ __forceinline__ void plan_build(const PlanArgs &a, int *dyn) {
     g_pre = a.gates[tid];
   }
 
-  // 0. per-adapter data; adapter ad belongs to thread ad % nt
+  // 0. per-adapter data; adapter ad belongs to thread ad % nt.  The page
+  //    table is copied to LDS first (when cached), so that its loads are in
+  //    flight with the adapter loads.
   if (tid == 0) { s_err = 0; s_bmask = 0; s_bad = 0; }
+  if (a.page_cache) {
+    const int npi = int(a.n_page_ids);
+    for (int b0 = tid; b0 < npi; b0 += nt * kAdBatch) {
+      int v[kAdBatch];
+#pragma unroll
+      for (int q = 0; q < kAdBatch; ++q) v[q] = a.page_ids[min(b0 + q * nt, npi - 1)];
+#pragma unroll
+      for (int q = 0; q < kAdBatch; ++q)
+        if (b0 + q * nt < npi) pcache[b0 + q * nt] = v[q];
+    }
+  }
   for (int base = tid; base < N; base += nt * kAdBatch) {
     int r[kAdBatch], s0[kAdBatch], s1[kAdBatch];
 #pragma unroll
@@ -245,7 +262,10 @@ __device__ __forceinline__ void plan_build(const PlanArgs &a, int *dyn) {
         if (v & kInfBadRank) err |= LORA_DEVERR_BAD_RANK;
         else if ((v & kInfRankMask) > 0 && g != 0.0f) ad = id;
       }
-      if (a.slot_cache) slot_ad[i] = ad;
+      if (a.slot_cache) {
+        slot_ad[i] = ad;
+        slot_g[i] = __float_as_int(g);
+      }
     }
     const uint64_t mm = match_lanes(ad, nbits);
     if (ad >= 0 && (mm & lt_mask) == 0) atomicAdd(&cnt[ad], __popcll(mm));
@@ -253,14 +273,28 @@ __device__ __forceinline__ void plan_build(const PlanArgs &a, int *dyn) {
   if (err) atomicOr(&s_err, err);
   bar<kLds>();
 
-  // 2. page_start consistency of used adapters; bucket occupancy
+  // 2. page_start consistency of used adapters (and, with the page table in
+  //    LDS, the range of their page ids); bucket occupancy
   {
     int bm = 0;
     for (int ad = tid; ad < N; ad += nt) {
       const int c = ld_ctr(&cnt[ad]);
       if (c <= 0) continue;
       const int v = inf[ad];
-      if (v & kInfBadStart) {
+      bool ok = !(v & kInfBadStart);
+      if (ok && a.page_cache) {
+        const int ps = psa[ad], r = v & kInfRankMask;
+        int bad = 0;
+        for (int j0 = 0; j0 < r; j0 += 8) {      // 8 LDS reads in flight
+          int pg[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) pg[q] = pcache[ps + min(j0 + q, r - 1)];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) bad |= (pg[q] < 0 || pg[q] >= a.n_pages) ? 1 : 0;
+        }
+        ok = bad == 0;
+      }
+      if (!ok) {
         st_ctr(&cnt[ad], -1);
         atomicOr(&s_err, LORA_DEVERR_BAD_POOL);
       } else {
@@ -272,7 +306,8 @@ __device__ __forceinline__ void plan_build(const PlanArgs &a, int *dyn) {
   }
   bar<kLds>();
 
-  // 3. segment order (redone once if step 4 drops an adapter)
+  // 3. segment order (redone once if step 4 drops an adapter; step 4 is not
+  //    needed when the page table was checked in step 2)
   int S = 0, pair_base = 0, u_base = 0, row_base = 0, n_units = 0, n_big = 0;
   for (int pass = 0; pass < 2; ++pass) {
     const int bmask = s_bmask;
@@ -311,7 +346,8 @@ __device__ __forceinline__ void plan_build(const PlanArgs &a, int *dyn) {
     {
       const int bt = lane < LORA_N_BUCKETS ? s_btot[lane] : 0;
       const int bi = wave_scan_incl(bt);
-      if (tid <= LORA_N_BUCKETS) P[L.bucket_seg_off + tid] = bi - bt;   // lanes 0..9 of wave 0
+      // lanes 0..9 of wave 0 (with the arrays in LDS: stored at the end)
+      if (!kLds && tid <= LORA_N_BUCKETS) P[L.bucket_seg_off + tid] = bi - bt;
       S = __builtin_amdgcn_readlane(bi, 63);
       for (int q = 0; q < Q; ++q) {
         const int ad = q * nt + tid;
@@ -358,15 +394,13 @@ __device__ __forceinline__ void plan_build(const PlanArgs &a, int *dyn) {
       if (kLds) {
         seg_pgb[sg] = psa[ad] - rb;
         seg_pp[sg] = st;
-        P[L.seg_adapter + sg] = ad;
-        P[L.seg_row_off + sg] = rb;
-        P[L.seg_uoff + sg] = uo;
+      } else {
+        P[L.seg_off + sg] = st;
+        int4 *d = reinterpret_cast<int4 *>(P + L.seg_desc) + 2 * sg;
+        d[0] = make_int4(ad, r, psa[ad], st);
+        d[1] = make_int4(st + c, ub, rb, uo);
       }
       if (big) P[L.big_list + 1 + bi] = sg;
-      P[L.seg_off + sg] = st;
-      int4 *d = reinterpret_cast<int4 *>(P + L.seg_desc) + 2 * sg;
-      d[0] = make_int4(ad, r, psa[ad], st);
-      d[1] = make_int4(st + c, ub, rb, uo);
       st += c; ub += c * r; rb += r; bi += big ? 1 : 0;
       uo += big ? 0 : c * ((r + kShrinkRows - 1) / kShrinkRows);
     }
@@ -376,19 +410,18 @@ __device__ __forceinline__ void plan_build(const PlanArgs &a, int *dyn) {
     n_units = tot.v[3];
     n_big = tot.v[4];
     if (tid == 0) {
-      P[L.seg_off + S] = pair_base;
       seg_row[S] = row_base;
       seg_uo[S] = n_units;
       if (kLds) {
-        P[L.seg_row_off + S] = row_base;
-        P[L.seg_uoff + S] = n_units;
         seg_pp[S] = pair_base;
+      } else {
+        P[L.seg_off + S] = pair_base;
+        P[L.u_off + pair_base] = u_base;
+        P[L.big_list] = n_big;
       }
-      P[L.u_off + pair_base] = u_base;
-      P[L.big_list] = n_big;
     }
     bar<kLds>();
-    if (pass == 1) break;
+    if (pass == 1 || a.page_cache) break;   // page ids already checked
     // 4. page ids of every used rank row, kRowBatch rows per thread in flight.
     //    Row g belongs to the last segment whose first row is <= g (segment
     //    row offsets strictly increase), found by binary lifting.
@@ -450,6 +483,83 @@ __device__ __forceinline__ void plan_build(const PlanArgs &a, int *dyn) {
     bar<kLds>();
   }
 
+  // U per slot to the u_off layout needs room for R_pairs floats
+  const bool copy_u = a.slot_u != nullptr && int64_t(u_base) <= a.u_cap;
+  if (a.slot_u != nullptr && !copy_u && tid == 0) atomicOr(&s_err, LORA_DEVERR_CAPACITY);
+  // Every global load so far has landed: waiting here (no store is in flight
+  // yet) settles them, so that the loops below, which store, need no flush
+  // of the counter that, on this target, also counts stores.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  // 5. ordered placement: within each nt-slot chunk the waves holding slots
+  //    take positions from the adapter cursors in wave order (stable sort)
+  int4 *slot_desc = reinterpret_cast<int4 *>(P + L.slot_desc);
+  for (int64_t base = 0; base < TK; base += nt) {
+    const int64_t i = base + tid;
+    int ad = -1;
+    float gate = 0.0f;
+    if (i < TK) {
+      if (a.slot_cache) {
+        ad = slot_ad[i];
+        gate = __int_as_float(slot_g[i]);
+      } else {
+        const int id = a.ids[i];
+        gate = a.gates[i];
+        if (id >= 0 && id < N) {
+          const int v = inf[id];
+          if (!(v & kInfBadRank) && (v & kInfRankMask) > 0 && gate != 0.0f) ad = id;
+        }
+      }
+      if (ad >= 0 && ld_ctr(&cnt[ad]) <= 0) ad = -1;
+    }
+    const uint64_t mm = match_lanes(ad, nbits);
+    const int rank_in_wave = __popcll(mm & lt_mask);
+    const int leader = mm ? __ffsll((unsigned long long)mm) - 1 : lane;
+    const int64_t here = TK - base < nt ? TK - base : nt;
+    const int nw = int((here + 63) >> 6);
+    int pos = -1;
+    for (int w = 0; w < nw; ++w) {
+      bar<kLds>();
+      if (wave == w) {
+        int b0 = 0;
+        if (ad >= 0 && rank_in_wave == 0) b0 = atomicAdd(&cur[ad], __popcll(mm));
+        b0 = __shfl(b0, leader, 64);
+        if (ad >= 0) pos = b0 + rank_in_wave;
+      }
+    }
+    if (i < TK) {
+      P[L.slot_pos + i] = pos;
+      if (pos >= 0) {
+        const int r = inf[ad] & kInfRankMask;
+        const int uo = ubias[ad] + pos * r;
+        P[L.pair_tk + pos] = int32_t(i);
+        P[L.pair_adapter + pos] = ad;
+        P[L.pair_gate + pos] = __float_as_int(gate);
+        P[L.u_off + pos] = uo;
+        slot_desc[i] = make_int4(pos, r, uo, psa[ad]);
+        if (copy_u) {
+          // this slot's U (per-slot layout, 16-byte aligned rows of
+          // slot_stride floats) to its u_off place: 8 loads in flight
+          const float4 *src = reinterpret_cast<const float4 *>(a.slot_u + i * int64_t(a.slot_stride));
+          for (int j0 = 0; j0 < r; j0 += 32) {
+            float4 v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = src[min(j0 / 4 + q, (r - 1) / 4)];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const float e4[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (j0 + 4 * q + e < r) a.u_out[uo + j0 + 4 * q + e] = e4[e];
+            }
+          }
+        }
+      } else {
+        slot_desc[i] = make_int4(-1, 0, 0, 0);
+      }
+    }
+  }
+  bar<kLds>();
+
   // 4b. decode-shrink schedule: its units (pairs x groups of kShrinkRows rank
   //     rows, over the segments it handles) split into equal runs, one per
   //     wave; each working wave's first segment and unit, with that
@@ -496,56 +606,39 @@ __device__ __forceinline__ void plan_build(const PlanArgs &a, int *dyn) {
     }
   }
 
-  // 5. ordered placement: within each nt-slot chunk the waves holding slots
-  //    take positions from the adapter cursors in wave order (stable sort)
-  int4 *slot_desc = reinterpret_cast<int4 *>(P + L.slot_desc);
-  for (int64_t base = 0; base < TK; base += nt) {
-    const int64_t i = base + tid;
-    int ad = -1;
-    if (i < TK) {
-      if (a.slot_cache) {
-        ad = slot_ad[i];
-      } else {
-        const int id = a.ids[i];
-        if (id >= 0 && id < N) {
-          const int v = inf[id];
-          if (!(v & kInfBadRank) && (v & kInfRankMask) > 0 && a.gates[i] != 0.0f) ad = id;
-        }
-      }
-      if (ad >= 0 && ld_ctr(&cnt[ad]) <= 0) ad = -1;
+  // 6. with the arrays in LDS, the segment outputs are stored last: on this
+  //    target stores count in the same counter as loads, so earlier stores
+  //    would hold up every wait the compiler places for a later load
+  if constexpr (kLds) {
+    const int ms = (S + nt - 1) / nt;
+    const int g0 = min(S, tid * ms), g1 = min(S, g0 + ms);
+    for (int sg = g0; sg < g1; ++sg) {
+      const int ad = seg_ad[sg];
+      const int c = ld_ctr(&cnt[ad]);
+      const int r = inf[ad] & kInfRankMask;
+      const int st = seg_pp[sg], rb = seg_row[sg], uo = seg_uo[sg];
+      const int ub = ubias[ad] + st * r;
+      P[L.seg_adapter + sg] = ad;
+      P[L.seg_row_off + sg] = rb;
+      P[L.seg_uoff + sg] = uo;
+      P[L.seg_off + sg] = st;
+      int4 *d = reinterpret_cast<int4 *>(P + L.seg_desc) + 2 * sg;
+      d[0] = make_int4(ad, r, psa[ad], st);
+      d[1] = make_int4(st + c, ub, rb, uo);
     }
-    const float gate = base == 0 ? g_pre : (i < TK ? a.gates[i] : 0.0f);
-    const uint64_t mm = match_lanes(ad, nbits);
-    const int rank_in_wave = __popcll(mm & lt_mask);
-    const int leader = mm ? __ffsll((unsigned long long)mm) - 1 : lane;
-    const int64_t here = TK - base < nt ? TK - base : nt;
-    const int nw = int((here + 63) >> 6);
-    int pos = -1;
-    for (int w = 0; w < nw; ++w) {
-      bar<kLds>();
-      if (wave == w) {
-        int b0 = 0;
-        if (ad >= 0 && rank_in_wave == 0) b0 = atomicAdd(&cur[ad], __popcll(mm));
-        b0 = __shfl(b0, leader, 64);
-        if (ad >= 0) pos = b0 + rank_in_wave;
-      }
+    if (tid == 0) {
+      P[L.seg_off + S] = pair_base;
+      P[L.seg_row_off + S] = row_base;
+      P[L.seg_uoff + S] = n_units;
+      P[L.u_off + pair_base] = u_base;
+      P[L.big_list] = n_big;
     }
-    if (i < TK) {
-      P[L.slot_pos + i] = pos;
-      if (pos >= 0) {
-        const int r = inf[ad] & kInfRankMask;
-        const int uo = ubias[ad] + pos * r;
-        P[L.pair_tk + pos] = int32_t(i);
-        P[L.pair_adapter + pos] = ad;
-        P[L.pair_gate + pos] = __float_as_int(gate);
-        P[L.u_off + pos] = uo;
-        slot_desc[i] = make_int4(pos, r, uo, psa[ad]);
-      } else {
-        slot_desc[i] = make_int4(-1, 0, 0, 0);
-      }
+    if (wave == 0) {
+      const int bt = lane < LORA_N_BUCKETS ? s_btot[lane] : 0;
+      const int bi = wave_scan_incl(bt);
+      if (lane <= LORA_N_BUCKETS) P[L.bucket_seg_off + lane] = bi - bt;
     }
   }
-  bar<kLds>();
   if (tid == 0) {
     int32_t *h = P + L.hdr;
     h[LORA_PH_PAIRS] = pair_base;

@@ -261,5 +261,102 @@ __device__ __forceinline__ void shrink_units_wave(const ShrinkArgs &s, const int
   }
 }
 
+// Per-slot decode shrink: one workgroup (4 waves) per slot i = t*K + k, no
+// plan needed (each slot gathers its own adapter's rank rows, so the launch
+// that builds the plan can run it too).  Wave w takes rank rows w, w+4, ...,
+// four of them per pass.  Each lane adds its 16-byte chunks in ascending
+// order with v_dot2, then the wave sum and coef = gate . (scale . extra):
+// the same operations in the same order as shrink_units_wave, so U is
+// identical to the plan-driven shrink's.
+//
+// The workgroup's first wave also writes the slot's descriptor for the
+// epilogue: active when its id is in range, its gate is not 0, its adapter's
+// rank is in 1..LORA_MAX_RANK with a consistent page_start and every page id
+// in range (the plan's rule for keeping a slot).
+template <bool kMask>
+__device__ __forceinline__ void slot_shrink_wg(const SlotShrinkArgs &s, const int i) {
+  constexpr int RW = 4;                         // rank rows per pass
+  constexpr int kCh = 4;                        // 512-element chunks per block
+  constexpr int KB = kCh * 512;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int id = s.ids[i];
+  const float gate = s.gates[i];
+  int r = 0, ps = 0;
+  bool act = id >= 0 && id < s.N && gate != 0.0f && s.n_pages > 0;
+  if (act) {
+    r = s.rank[id];
+    ps = s.page_start[id];
+    const int pe = s.page_start[id + 1];
+    act = r > 0 && r <= LORA_MAX_RANK && ps >= 0 && int64_t(pe) - ps == r && pe <= s.n_page_ids;
+  }
+  if (!act) {
+    if (threadIdx.x == 0) s.sdesc[i] = make_int4(-1, 0, 0, 0);
+    return;
+  }
+  if (w == 0) {
+    // every page id of the adapter in range (lane-parallel), then the
+    // descriptor; the other waves only guard their own loads
+    bool bad = false;
+    for (int j = lane; j < r; j += 64) {
+      const int pid = s.page_ids[ps + j];
+      bad |= pid < 0 || pid >= s.n_pages;
+    }
+    const bool any_bad = __ballot(bad) != 0;
+    if (lane == 0)
+      s.sdesc[i] = any_bad ? make_int4(-1, 0, 0, 0) : make_int4(i, r, i * s.stride, ps);
+  }
+  const float coef = gate * (s.scale[id] * s.extra_scale);
+  const int d = s.d;
+  const int64_t t = i / s.K;
+  const uint16_t *zrow = static_cast<const uint16_t *>(s.Z) + t * d;
+  const uint8_t *mrow = kMask ? s.mask + t * d : nullptr;
+  const uint16_t *pages = static_cast<const uint16_t *>(s.pages);
+  for (int j0 = w; j0 < r; j0 += 4 * RW) {
+    const uint16_t *arow[RW];
+    bool ok[RW];
+#pragma unroll
+    for (int a2 = 0; a2 < RW; ++a2) {
+      const int j = min(j0 + 4 * a2, r - 1);
+      const int pid = s.page_ids[ps + j];
+      const bool in = pid >= 0 && pid < s.n_pages;
+      ok[a2] = j0 + 4 * a2 < r && in;
+      arow[a2] = pages + int64_t(in ? pid : 0) * d;
+    }
+    float acc[RW];
+#pragma unroll
+    for (int a2 = 0; a2 < RW; ++a2) acc[a2] = 0.f;
+    for (int cb = 0; cb < d; cb += KB) {
+      Raw<uint16_t> ar[RW][kCh], xr[kCh];
+      uint2 mk[kCh];
+#pragma unroll
+      for (int ch = 0; ch < kCh; ++ch) {
+        const int c = min(cb + ch * 512 + lane * 8, d - 8);
+        xr[ch].load(zrow + c);
+        if (kMask) mk[ch] = *reinterpret_cast<const uint2 *>(mrow + c);
+#pragma unroll
+        for (int a2 = 0; a2 < RW; ++a2) ar[a2][ch].load(arow[a2] + c);
+      }
+#pragma unroll
+      for (int ch = 0; ch < kCh; ++ch) {
+        if (cb + ch * 512 + lane * 8 >= d) continue;
+        Raw<uint16_t> xv = xr[ch];
+        if (kMask) Dot8<uint16_t>::mask(xv, mk[ch]);
+#pragma unroll
+        for (int a2 = 0; a2 < RW; ++a2) acc[a2] = Dot8<uint16_t>::run(xv, ar[a2][ch], acc[a2]);
+      }
+    }
+#pragma unroll
+    for (int a2 = 0; a2 < RW; ++a2) acc[a2] = wave_sum(acc[a2]);
+    if (lane < RW) {
+      float mine = acc[0];
+      bool mok = ok[0];
+#pragma unroll
+      for (int a2 = 1; a2 < RW; ++a2)
+        if (lane == a2) { mine = acc[a2]; mok = ok[a2]; }
+      if (mok) s.out[int64_t(i) * s.stride + j0 + 4 * lane] = coef * mine;
+    }
+  }
+}
+
 }  // namespace
 }  // namespace lora

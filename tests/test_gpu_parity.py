@@ -102,6 +102,41 @@ def test_plan_errors_match_oracle():
     assert_plan_equal(got, ref)
 
 
+def test_plan_bad_page_ids_large_table():
+    """A page table too large to copy to LDS (its ids are checked row by row
+    after the segment order) with out-of-range page ids in two used
+    adapters: both are dropped and BAD_POOL is set, as in the oracle.  The
+    same batch through lora_forward (plan built inside the decode GEMM launch,
+    per-slot shrink) gives the same plan and the oracle's Y."""
+    rng = np.random.default_rng(21)
+    N, T, K = 300, 96, 1
+    rank = np.full(N, 128, np.int32)                # 38400 page ids
+    ids = rng.integers(0, N, size=(T, K)).astype(np.int32)
+    gates = np.ones((T, K), np.float32)
+    w = wl.build("bigtable", 21, "bf16", T, K, 256, 256, rank, ids, gates,
+                 x_var=1.0, w_var=0.02, a_var=1 / 64, b_var=0.02)
+    used = np.unique(ids)
+    w.page_ids = w.page_ids.copy()
+    w.page_ids[w.page_start[used[0]] + 5] = -3
+    w.page_ids[w.page_start[used[1]] + 127] = w.n_pages
+    ref = O.plan(w.ids, w.gates, w.rank, w.page_start, w.page_ids, w.n_pages)
+    L = D.DeviceLayer(w, max_rank=128)
+    L.run_plan()
+    torch.cuda.synchronize()
+    got = L.read_plan()
+    assert got["header"][B.PH_ERR] == B.DEVERR_BAD_POOL
+    assert_plan_equal(got, ref)
+    L.plan.zero_()
+    B.lora_forward(L.ids, L.gates, L.T, L.K, L.X, L.W_t, L.Y, L.keep_mask, L.keep_scale, L.pool,
+                   L.plan, L.ws)
+    torch.cuda.synchronize()
+    got = L.read_plan()
+    assert got["header"][B.PH_ERR] == B.DEVERR_BAD_POOL
+    assert_plan_equal(got, ref)
+    err = rel_err(D.as_f64(L.Y_host()), O.apply_workload(w))
+    assert err <= TOL["bf16"], err
+
+
 def test_plan_large_pool_uses_global_counters():
     rng = np.random.default_rng(11)
     N, T, K = 10000, 3000, 2                       # N above the LDS counter limit
@@ -263,18 +298,47 @@ def test_split_and_fused_entry_points_agree(cfg):
     assert np.array_equal(Y1, L.Y_host())
 
 
+def _mixed_decode():
+    """Decode-sized batch (T <= 128, two slots) with empty slots, zero gates,
+    ranks across bucket edges and above the MFMA range, per-adapter scales."""
+    rng = np.random.default_rng(15)
+    N, T, K = 9, 100, 2
+    rank = np.array([1, 2, 3, 7, 16, 17, 64, 129, 200], np.int32)
+    ids = rng.integers(-1, N, size=(T, K)).astype(np.int32)
+    gates = rng.standard_normal((T, K)).astype(np.float32)
+    gates[rng.random((T, K)) < 0.1] = 0
+    return wl.build("mixed-decode", 15, "bf16", T, K, 4608, 384, rank, ids, gates,
+                    x_var=1.0, w_var=0.02, a_var=1 / 64, b_var=0.02,
+                    scale=rng.uniform(0.5, 2, N).astype(np.float32))
+
+
+FORWARD_CASES = {
+    # decode shapes with a keep mask, d_in above one 4096-element block, and
+    # ranks up to 128 over many adapters
+    "dec4": lambda: wl.config(4, T=96, d_in=4608, d_out=704, seed=204),
+    "dec3": lambda: wl.config(3, T=128, d_in=512, d_out=640, n_adapters=300, seed=203),
+    "decmix": _mixed_decode,
+}
+
+
 @pytest.mark.parametrize("cfg", ["small1", "small2", "small3", "small4", "small5", "full2", "full3",
-                                 "full5"])
+                                 "full5", "dec4", "dec3", "decmix"])
 def test_forward_matches_plan_then_apply(cfg):
-    """lora_forward builds the plan inside the split GEMM launch (one extra
-    workgroup, 256 threads, the GEMM's LDS) and then runs the shrink and the
-    epilogue: the plan, U and Y equal those of lora_plan then lora_apply bit
-    for bit.  The same call captured in a graph is replayed three times, with
+    """lora_forward in two launches (decode: GEMM + per-slot shrink, then
+    epilogue + plan; stream-K: GEMM + plan, then shrink and epilogue): the
+    plan, U and Y equal those of lora_plan then lora_apply bit for bit.  The same call captured in a graph is replayed three times, with
     eager work and synchronisation in between, and every replay gives the
     same Y."""
-    w = small(int(cfg[-1])) if cfg.startswith("small") else full(int(cfg[-1]))
+    if cfg in FORWARD_CASES:
+        w = FORWARD_CASES[cfg]()
+    else:
+        w = small(int(cfg[-1])) if cfg.startswith("small") else full(int(cfg[-1]))
     L = run(w)
     P1, U1, Y1 = L.read_plan(), L.U().copy(), L.Y_host().copy()
+    if cfg in FORWARD_CASES:
+        assert_plan_equal(P1, O.plan_workload(w))
+        err = rel_err(D.as_f64(Y1), O.apply_workload(w))
+        assert err <= TOL[w.dtype], err
 
     def fwd():
         B.lora_forward(L.ids, L.gates, L.T, L.K, L.X, L.W_t, L.Y, L.keep_mask, L.keep_scale,
