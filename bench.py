@@ -10,8 +10,10 @@ adapter (synthetic, seeded).
 
 Measurement
   * value: tokens per second over exactly --steps steps, wall clock between
-    two torch.cuda.synchronize() calls.  Each step is one HIP-graph replay of
-    lora_forward (plan + shrink + GEMM + epilogue: for decode shapes two
+    two torch.cuda.synchronize() calls, launches queued eagerly on one stream
+    (faster on this stack than replaying a captured HIP graph of the same
+    step, whose time is reported as step_us_graph_replay).  Each step is one
+    call of lora_forward (plan + shrink + GEMM + epilogue: for decode shapes two
     launches, GEMM + per-slot shrink, then epilogue + plan; for stream-K
     shapes the plan is built inside the GEMM launch) on one of R rotated
     copies of the weights
@@ -66,7 +68,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotation", type=int, default=0, help="copies of W/pool (0: >= 1 GiB)")
-    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay timing (the value is timed with eager launches)")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs of a --copy-probe run into "
@@ -139,8 +142,8 @@ def main():
         B.lora_expand_epilogue(c.X, c.W_t, c.Y, T, K, c.pool, c.plan, c.ws)
 
     # ---------------------------------------------------------------- graphs
-    def make_graphs(use_ids, plan):
-        if args.no_graph:
+    def make_graphs(use_ids, plan, graph):
+        if not graph:
             return None
         gs = []
         side = torch.cuda.Stream()
@@ -158,8 +161,8 @@ def main():
         torch.cuda.synchronize()
         return gs
 
-    def timed(use_ids, steps, warmup, plan=True):
-        gs = make_graphs(use_ids, plan)
+    def timed(use_ids, steps, warmup, plan=True, graph=False):
+        gs = make_graphs(use_ids, plan, graph)
         run = ((lambda i: gs[i % R].replay()) if gs
                else (lambda i: step(copies[i % R], use_ids, plan)))
         for i in range(warmup):
@@ -174,6 +177,7 @@ def main():
     elapsed = timed(ids, args.steps, args.warmup)
     elapsed_apply = timed(ids, args.steps, args.warmup, plan=False)
     elapsed_base = timed(empty_ids, args.steps, args.warmup)
+    elapsed_graph = None if args.no_graph else timed(ids, args.steps, args.warmup, graph=True)
     # results of the last apply on copy 0 must not be stale: re-run eagerly
     step(copies[0], ids)
     torch.cuda.synchronize()
@@ -316,7 +320,7 @@ def main():
         "config": {"workload": w.name, "T": T, "K": K, "d_in": w.d_in, "d_out": w.d_out,
                    "adapters": w.n_adapters, "ranks": sorted(set(w.rank.tolist()))[:8],
                    "active_pairs": P, "segments": S, "R_used": R_used, "R_pairs": R_pairs,
-                   "rotation_copies": R, "graph_replay": not args.no_graph},
+                   "rotation_copies": R, "launch": "eager"},
         "roofline": roofline,
         "value_apply_only": T * args.steps / elapsed_apply,
         **extra,
@@ -324,6 +328,7 @@ def main():
         "stages_us_mean": st_mean,
         "stages_us_mean_empty_plan": sb_mean,
         "step_us": t_step * 1e6,
+        "step_us_graph_replay": None if elapsed_graph is None else elapsed_graph / args.steps * 1e6,
         "step_us_empty_plan": t_base_step * 1e6,
         "lora_path": {"t_us": t_lora * 1e6, "bytes": lora_bytes, "GB_s": lora_bytes / t_lora / 1e9,
                       "frac_hbm": lora_bytes / t_lora / 1e9 / HBM_PEAK_GBS, "flops": lora_flops},

@@ -391,8 +391,18 @@ __device__ __forceinline__ void decode_tile(const GemmArgs &g, int bx, int by, i
   // All loads are unconditional, from clamped addresses, so none waits on a
   // branch: rows past M and columns past N only feed outputs that are never
   // stored, and K groups past the end are skipped by the MFMA loop.
-  // Token rows first, straight into LDS (no registers): wave w loads rows
-  // w, w+4, ...; lane l of the instruction fills slot l of the row.
+  // The W stream (HBM) is issued first, then the token rows (mostly L2).
+  // W fragments: row n0 + lane%32, k0 + 64*grp + 32*half + [0, 32)
+  uint4 wf[NG][4];
+  const uint16_t *wrow = W + int64_t(min(n0 + (lane & 31), g.N - 1)) * g.Kd + k0 + half * 32;
+#pragma unroll
+  for (int gq = 0; gq < NG; ++gq)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      wf[gq][q] = *reinterpret_cast<const uint4 *>(wrow + min(gq, ng - 1) * 64 + q * 8);
+  __builtin_amdgcn_sched_barrier(0);
+  // Token rows straight into LDS (no registers): wave w loads rows w, w+4,
+  // ...; lane l of the instruction fills slot l of the row.
 #pragma unroll
   for (int i = 0; i < BMr / 4; ++i) {
     const int r = wave + 4 * i;
@@ -403,19 +413,8 @@ __device__ __forceinline__ void decode_tile(const GemmArgs &g, int bx, int by, i
                                      (__attribute__((address_space(3))) void *)(xs + r * KC), 16, 0, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
-  // W fragments: row n0 + lane%32, k0 + 64*grp + 32*half + [0, 32)
-  uint4 wf[NG][4];
-  const uint16_t *wrow = W + int64_t(min(n0 + (lane & 31), g.N - 1)) * g.Kd + k0 + half * 32;
-#pragma unroll
-  for (int gq = 0; gq < NG; ++gq)
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      wf[gq][q] = *reinterpret_cast<const uint4 *>(wrow + min(gq, ng - 1) * 64 + q * 8);
-  __builtin_amdgcn_sched_barrier(0);
-  // the BMr/4 token-row loads were issued before the NG*4 = 32 W loads:
-  // vmcnt <= 32 means they have landed in LDS (vmcnt 32: simm16 0x8F70)
-  static_assert(NG * 4 == 32, "wait count below assumes 32 W loads in flight");
-  __builtin_amdgcn_s_waitcnt(0x8F70);
+  // the token rows were issued last: all loads have landed
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
 
   f32x16_t acc[MB];
@@ -441,6 +440,7 @@ __device__ __forceinline__ void decode_tile(const GemmArgs &g, int bx, int by, i
       }
     }
   }
+  // partials are read once, by the epilogue: streaming (non-temporal) stores
   float *Pz = g.partial + int64_t(bz) * g.M * g.N;
   const int col = n0 + (lane & 31);
   if (col < g.N) {
@@ -449,7 +449,7 @@ __device__ __forceinline__ void decode_tile(const GemmArgs &g, int bx, int by, i
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = m0 + b * 32 + (v >> 2) * 8 + half * 4 + (v & 3);
-        if (row < g.M) Pz[int64_t(row) * g.N + col] = acc[b][v];
+        if (row < g.M) __builtin_nontemporal_store(acc[b][v], Pz + int64_t(row) * g.N + col);
       }
   }
 }
@@ -916,6 +916,7 @@ __device__ __forceinline__ void tile_run(const GemmArgs &g, char *smem, int m0, 
   }
 
   if constexpr (!kFused) {
+    // partials are read once, by the epilogue: streaming (non-temporal) stores
     float *Pz = g.partial + int64_t(slot) * g.M * g.N;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -926,7 +927,7 @@ __device__ __forceinline__ void tile_run(const GemmArgs &g, char *smem, int m0, 
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int row = m0 + wm * TM * 32 + i * 32 + (v >> 2) * 8 + half * 4 + (v & 3);
-          if (row < g.M) Pz[int64_t(row) * g.N + col] = acc[i][j][v];
+          if (row < g.M) __builtin_nontemporal_store(acc[i][j][v], Pz + int64_t(row) * g.N + col);
         }
       }
   } else {
