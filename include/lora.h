@@ -127,7 +127,9 @@ const char *lora_status_string(int32_t status);
  *                          the segments left to the MFMA shrink, and scratch
  *                          used while building
  * Header words 0..7 are the LORA_PH_* values; words 8..10 hold internal
- * scheduling counts; the rest are 0.
+ * scheduling counts; word 11 is 1 when the decode-shrink wave records were
+ * built (lora_plan builds them; lora_forward's decode path does not, and a
+ * later shrink over its plan finds its starts by search); the rest are 0.
  * Everything is integer and bit-exact.  Built once per batch and shared by
  * every layer that uses the same routing.
  *   ids   [T][K] int32 device; -1 marks an empty slot.

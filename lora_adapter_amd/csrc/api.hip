@@ -322,10 +322,13 @@ PlanLaunch forward_plan(const int32_t *ids, const float *gates, int32_t T, int32
   PlanLaunch pl = plan_setup(ids, gates, T, K, pool_view(pool), static_cast<int32_t *>(plan), 256,
                              plan_lds_cap(f.cfg));
   if (w.slot_u) {
+    // decode: the per-slot shrink has run; the plan stores its U in the u_off
+    // layout and skips the decode-shrink wave records
     pl.a.slot_u = w.slot_u;
     pl.a.u_out = w.U;
     pl.a.u_cap = w.u_cap;
     pl.a.slot_stride = LORA_MAX_RANK;
+    pl.a.no_sched = 1;
   }
   return pl;
 }

@@ -480,19 +480,21 @@ __global__ __launch_bounds__(256, 2) void decode_gemm_shrink_kernel(GemmArgs g, 
     shrink_units_wave<uint16_t, kMask, kCh, true>(s, w);
 }
 
-// Decode GEMM tiles in workgroups 0 .. n_gemm-1 (dealt one per CU), and the
-// per-slot shrink in the workgroups after them (second places beside the
-// tiles).  Neither reads what the other writes, and neither needs the plan.
+// The per-slot shrink in workgroups 0 .. n_slots-1 and the decode GEMM tiles
+// after them.  The shrink's few dependent loads go out first, ahead of the
+// W stream; neither part reads what the other writes, and neither needs
+// the plan.
 template <int MB, bool kMask>
 __global__ __launch_bounds__(256) void decode_gemm_slot_kernel(GemmArgs g, SlotShrinkArgs ss,
                                                                 int gx, int gy, int n_gemm) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[MB * 32 * kDecodeKC];
   const int b = blockIdx.x;
-  if (b < n_gemm) {
-    decode_tile<MB>(g, b % gx, (b / gx) % gy, b / (gx * gy), xs);
+  if (b < ss.n_slots) {
+    slot_shrink_wg<kMask>(ss, b);
     return;
   }
-  slot_shrink_wg<kMask>(ss, b - n_gemm);
+  const int t = b - ss.n_slots;
+  decode_tile<MB>(g, t % gx, (t / gx) % gy, t / (gx * gy), xs);
 }
 
 // ------------------------------------------------------------ pipelined tile GEMM

@@ -22,6 +22,7 @@ constexpr int kShrinkWaves = 2048;                // waves of the decode shrink 
 constexpr int kPhUnits = 8;          // decode-shrink units: sum over its segments of pairs x row groups
 constexpr int kPhUnitsPerWave = 9;   // units per wave of the decode shrink
 constexpr int kPhBig = 10;           // segments left to the MFMA shrink
+constexpr int kPhSched = 11;         // 1: the decode-shrink wave records were built
 
 // Segments of at least kBigSegPairs pairs go to the MFMA shrink when the
 // operands are bf16, the batch is large and both projections' widths are
@@ -151,6 +152,7 @@ struct PlanView {
   const float *pair_gate;  // gate of each sorted pair
   const int4 *wave_start;  // two int4 per decode-shrink wave
   const int32_t *big_list; // count, then segment ids
+  const int32_t *seg_uoff; // first decode-shrink unit of each segment
 };
 
 inline PlanView plan_view(const void *plan, int64_t TK, int64_t N) {
@@ -161,7 +163,8 @@ inline PlanView plan_view(const void *plan, int64_t TK, int64_t N) {
                   reinterpret_cast<const int4 *>(b + L.seg_desc),
                   reinterpret_cast<const int4 *>(b + L.slot_desc),
                   reinterpret_cast<const float *>(b + L.pair_gate),
-                  reinterpret_cast<const int4 *>(b + L.wave_start), b + L.big_list};
+                  reinterpret_cast<const int4 *>(b + L.wave_start), b + L.big_list,
+                  b + L.seg_uoff};
 }
 
 // Device view of an adapter pool.
@@ -297,6 +300,7 @@ struct PlanArgs {
   int slot_cache;    // 1: per-slot adapters and gates cached in LDS
   int use_tile;      // 1: segments of >= kBigSegPairs pairs go to the MFMA shrink
   int page_cache;    // 1: the page table is copied to LDS (after the slot cache)
+  int no_sched;      // 1: skip the decode-shrink wave records (header word kPhSched = 0)
   // not null: U per slot (stride slot_stride) to be stored in the u_off layout
   // at u_out when the plan's R_pairs <= u_cap (else LORA_DEVERR_CAPACITY)
   const float *slot_u;

@@ -20,7 +20,7 @@ PlanLaunch plan_setup(const int32_t *ids, const float *gates, int T, int K, cons
   PlanLaunch pl{};
   pl.a = PlanArgs{ids, gates, T, K, pool.n_adapters, pool.rank, pool.page_start, pool.page_ids,
                   pool.n_pages, pool.n_page_ids, plan, 0,
-                  shrink_tile_enabled(pool.dtype, TK, pool.d_in, pool.d_out) ? 1 : 0, 0,
+                  shrink_tile_enabled(pool.dtype, TK, pool.d_in, pool.d_out) ? 1 : 0, 0, 0,
                   nullptr, nullptr, 0, 0};
   int64_t cap = int64_t(lds_cap / sizeof(int));
   if (cap > kPlanLdsInts) cap = kPlanLdsInts;

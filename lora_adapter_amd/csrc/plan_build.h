@@ -560,7 +560,8 @@ __device__ __forceinline__ void plan_build(const PlanArgs &a, int *dyn) {
   }
   bar<kLds>();
 
-  // 4b. decode-shrink schedule: its units (pairs x groups of kShrinkRows rank
+  // 4b. decode-shrink schedule (skipped when no_sched: the decode shrink then
+  //     finds each wave's start itself): its units (pairs x groups of kShrinkRows rank
   //     rows, over the segments it handles) split into equal runs, one per
   //     wave; each working wave's first segment and unit, with that
   //     segment's descriptor, so that a shrink wave starts with one load.
@@ -572,7 +573,7 @@ __device__ __forceinline__ void plan_build(const PlanArgs &a, int *dyn) {
     int top = 1;
     while (top * 2 <= S) top *= 2;
     int4 *ws = reinterpret_cast<int4 *>(P + L.wave_start);
-    for (int w0 = 0; w0 < n_active; w0 += nt * kWsBatch) {
+    for (int w0 = 0; w0 < (a.no_sched ? 0 : n_active); w0 += nt * kWsBatch) {
       int lo[kWsBatch], uq[kWsBatch];
 #pragma unroll
       for (int q = 0; q < kWsBatch; ++q) {
@@ -603,6 +604,7 @@ __device__ __forceinline__ void plan_build(const PlanArgs &a, int *dyn) {
       P[L.hdr + kPhUnits] = n_units;
       P[L.hdr + kPhUnitsPerWave] = upw;
       P[L.hdr + kPhBig] = n_big;
+      P[L.hdr + kPhSched] = a.no_sched ? 0 : 1;
     }
   }
 
@@ -649,7 +651,7 @@ __device__ __forceinline__ void plan_build(const PlanArgs &a, int *dyn) {
     h[LORA_PH_T] = a.T;
     h[LORA_PH_K] = a.K;
     h[LORA_PH_N] = N;
-    for (int q = kPhBig + 1; q < LORA_PLAN_HEADER_INTS; ++q) h[q] = 0;
+    for (int q = kPhSched + 1; q < LORA_PLAN_HEADER_INTS; ++q) h[q] = 0;
     for (int q = LORA_N_BUCKETS + 1; q < 16; ++q) P[L.bucket_seg_off + q] = 0;
   }
 }

@@ -104,6 +104,8 @@ __device__ __forceinline__ void shrink_units_wave(const ShrinkArgs &s, const int
   else if (lane == 8) v = s.plan.hdr[kPhUnits];
   else if (lane == 9) v = s.plan.hdr[kPhUnitsPerWave];
   else if (lane == 10) v = s.plan.hdr[LORA_PH_RPAIRS];
+  else if (lane == 11) v = s.plan.hdr[kPhSched];
+  else if (lane == 12) v = s.plan.hdr[LORA_PH_SEGS];
   if (int64_t(__builtin_amdgcn_readlane(v, 10)) > s.out_cap) {
     if (wv == 0 && lane == 0) atomicOr(s.err_word, LORA_DEVERR_CAPACITY);
     return;
@@ -111,11 +113,41 @@ __device__ __forceinline__ void shrink_units_wave(const ShrinkArgs &s, const int
   const int units = __builtin_amdgcn_readlane(v, 8), upw = __builtin_amdgcn_readlane(v, 9);
   // only waves with work have a start record (this plan's, not a stale one)
   if (int64_t(wv) * upw >= units) return;
-  int seg = __builtin_amdgcn_readlane(v, 0);
-  int loc = __builtin_amdgcn_readlane(v, 1);
-  int ad = __builtin_amdgcn_readlane(v, 2), r = __builtin_amdgcn_readlane(v, 3);
-  int ps = __builtin_amdgcn_readlane(v, 4), pb = __builtin_amdgcn_readlane(v, 5);
-  int pe = __builtin_amdgcn_readlane(v, 6);
+  int seg, loc, ad, r, ps, pb, pe;
+  if (__builtin_amdgcn_readlane(v, 11) != 0) {
+    seg = __builtin_amdgcn_readlane(v, 0);
+    loc = __builtin_amdgcn_readlane(v, 1);
+    ad = __builtin_amdgcn_readlane(v, 2);
+    r = __builtin_amdgcn_readlane(v, 3);
+    ps = __builtin_amdgcn_readlane(v, 4);
+    pb = __builtin_amdgcn_readlane(v, 5);
+    pe = __builtin_amdgcn_readlane(v, 6);
+  } else {
+    // no wave records in this plan: the last segment whose first unit is
+    // <= this wave's first unit u0, by a 64-way search over the segments'
+    // first units (seg_uoff[0] = 0 <= u0, seg_uoff[S] = units > u0)
+    const int S = __builtin_amdgcn_readlane(v, 12);
+    const int u0 = wv * upw;
+    int lo = 0, first = 0, step = 1;
+    while (int64_t(step) * 64 <= S) step *= 64;
+    for (; step > 0; step /= 64) {
+      const int idx = lo + lane * step;
+      const int val = s.plan.seg_uoff[min(idx, S)];
+      const uint64_t m = __ballot(idx <= S && val <= u0);
+      const int last = 63 - __clzll(static_cast<long long>(m));
+      first = __shfl(val, last, 64);
+      lo += last * step;
+    }
+    seg = lo;
+    loc = u0 - first;
+    int w2 = 0;
+    if (lane < 8) w2 = reinterpret_cast<const int *>(s.plan.seg_desc)[8 * seg + lane];
+    ad = __builtin_amdgcn_readlane(w2, 0);
+    r = __builtin_amdgcn_readlane(w2, 1);
+    ps = __builtin_amdgcn_readlane(w2, 2);
+    pb = __builtin_amdgcn_readlane(w2, 3);
+    pe = __builtin_amdgcn_readlane(w2, 4);
+  }
   int left = min(upw, units - wv * upw);
   const int d = s.d;
   const E *Z = static_cast<const E *>(s.Z);

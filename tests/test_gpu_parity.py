@@ -352,6 +352,12 @@ def test_forward_matches_plan_then_apply(cfg):
     assert_plan_equal(L.read_plan(), P1)
     assert np.array_equal(U1, L.U())
     assert np.array_equal(Y1, L.Y_host())
+    # the decode path's plan has no decode-shrink wave records: a shrink over
+    # it finds each wave's start by search and gives the same U
+    L.ws.zero_()
+    L.run_shrink()
+    torch.cuda.synchronize()
+    assert np.array_equal(U1, L.U())
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         fwd()
