@@ -353,7 +353,7 @@ def gemm_kernel_name(T, d_in, d_out, dtype_code, B, fused):
     256 x 128 stream-K tiles over 255 workgroups when there are at least 4
     units each, with the plan built in the same launch)."""
     if dtype_code != B.LORA_BF16:
-        return "gemm_f32_kernel"
+        return "gemm_f32_kernel (plan)"
     if T <= 128:
         return "decode_gemm_slot_kernel"
     if fused:
@@ -377,7 +377,7 @@ def gemm_roofline(B, L, w, T, st_med, base_flops, P, R_pairs, R_used, e):
         alg_bytes += R_used * w.d_in * e + 4 * R_pairs + 16 * T * w.K
         alg_bytes += T * w.d_in if L.keep_mask is not None else 0
         flops += 2.0 * R_pairs * w.d_in
-    elif name == "gemm_tile_plan_kernel":
+    elif name in ("gemm_tile_plan_kernel", "gemm_f32_kernel (plan)"):
         t_us = st_med["fwd_gemm"]
         alg_bytes += 8 * T * w.K + 8 * w.n_adapters + 4 * R_used
     else:

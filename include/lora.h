@@ -215,7 +215,7 @@ int32_t lora_apply(const void *X, const void *W_t, void *Y, int32_t T, int32_t K
  *     lora_forward_finish: the epilogue (partials + expand from the per-slot
  *       U and descriptors, one rounding), and in the same launch the plan,
  *       whose workgroup also stores U in the u_off layout.
- *   stream-K shapes:
+ *   stream-K shapes and float32:
  *     lora_forward_gemm:   the GEMM's partials with the plan built by one
  *       more workgroup of the launch;
  *     lora_forward_finish: lora_shrink, then lora_expand_epilogue.

@@ -199,161 +199,6 @@ __device__ __forceinline__ bool expand_enabled(const ExpandArgs &e) {
   return e.U != nullptr && int64_t(e.hdr[LORA_PH_RPAIRS]) <= e.u_cap;
 }
 
-// ------------------------------------------------------------ bf16 MFMA GEMM
-// Tile BM x BN, K step 64, WM x WN waves each owning (BM/WM) x (BN/WN) as
-// 32x32 MFMA blocks.  Global -> registers -> LDS (row stride 72 elements, so
-// the 16-byte fragment reads of 8 consecutive rows fall in distinct banks),
-// double buffered: the next K tile's global loads are in flight while the
-// current one feeds the MFMAs.  Lane l of an MFMA reads row l%32 and the 8
-// K values at (l/32)*8 of each 16-wide K step, for A (X rows) and B (W_t rows).
-template <int BM, int BN, int WM, int WN, bool kFused>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs g) {
-  constexpr int NT = WM * WN * 64;
-  constexpr int BK = 64;
-  constexpr int LDK = BK + 8;
-  constexpr int TM = BM / (WM * 32), TN = BN / (WN * 32);
-  constexpr int A_CH = BM * BK / 8 / NT, B_CH = BN * BK / 8 / NT;
-  static_assert(A_CH * NT * 8 == BM * BK && B_CH * NT * 8 == BN * BK, "tile / thread mismatch");
-  constexpr int STAGE = (BM + BN) * LDK;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
-
-  const uint16_t *X = static_cast<const uint16_t *>(g.X);
-  const uint16_t *W = static_cast<const uint16_t *>(g.W);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
-  const int k_begin = blockIdx.z * g.k_split;
-  const int k_end = min(g.Kd, k_begin + g.k_split);
-  const int nk = k_end > k_begin ? (k_end - k_begin) / BK : 0;
-
-  uint4 ra[A_CH], rb[B_CH];
-  auto gload = [&](int kt) {
-    const int kb = k_begin + kt * BK;
-#pragma unroll
-    for (int c = 0; c < A_CH; ++c) {
-      // clamped rows: rows past M / N only feed outputs that are never stored
-      const int idx = tid + c * NT;
-      const int row = idx >> 3, col = (idx & 7) * 8;
-      const int gr = min(m0 + row, g.M - 1);
-      ra[c] = *reinterpret_cast<const uint4 *>(X + int64_t(gr) * g.Kd + kb + col);
-    }
-#pragma unroll
-    for (int c = 0; c < B_CH; ++c) {
-      const int idx = tid + c * NT;
-      const int row = idx >> 3, col = (idx & 7) * 8;
-      const int gr = min(n0 + row, g.N - 1);
-      rb[c] = *reinterpret_cast<const uint4 *>(W + int64_t(gr) * g.Kd + kb + col);
-    }
-  };
-  auto sstore = [&](int buf) {
-    uint16_t *As = smem + buf * STAGE;
-    uint16_t *Bs = As + BM * LDK;
-#pragma unroll
-    for (int c = 0; c < A_CH; ++c) {
-      const int idx = tid + c * NT;
-      *reinterpret_cast<uint4 *>(As + (idx >> 3) * LDK + (idx & 7) * 8) = ra[c];
-    }
-#pragma unroll
-    for (int c = 0; c < B_CH; ++c) {
-      const int idx = tid + c * NT;
-      *reinterpret_cast<uint4 *>(Bs + (idx >> 3) * LDK + (idx & 7) * 8) = rb[c];
-    }
-  };
-
-  f32x16_t acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-  if (nk > 0) {
-    gload(0);
-    sstore(0);
-  }
-  __syncthreads();
-  const int frag_row = lane & 31, frag_k = (lane >> 5) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const uint16_t *As = smem + cur * STAGE;
-    const uint16_t *Bs = As + BM * LDK;
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      bf16x8_t af[TM], bf[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t *>(
-            As + (wm * TM * 32 + i * 32 + frag_row) * LDK + s * 16 + frag_k);
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bf[j] = *reinterpret_cast<const bf16x8_t *>(
-            Bs + (wn * TN * 32 + j * 32 + frag_row) * LDK + s * 16 + frag_k);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) sstore(cur ^ 1);
-    __syncthreads();
-  }
-
-  // Accumulator layout of a 32x32 block: lane l holds column l%32 and rows
-  // 8*(v/4) + 4*(l/32) + v%4 for v = 0..15.
-  if constexpr (!kFused) {
-    float *Pz = g.partial + int64_t(blockIdx.z) * g.M * g.N;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int col = n0 + wn * TN * 32 + j * 32 + (lane & 31);
-        if (col >= g.N) continue;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = m0 + wm * TM * 32 + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-          if (row < g.M) Pz[int64_t(row) * g.N + col] = acc[i][j][v];
-        }
-      }
-  } else {
-    constexpr int SC = TN * 32 + 1;            // staged floats per row (padded)
-    constexpr int CPL = TN * 32 / 64;          // output columns per lane
-    static_assert(CPL == 1 || CPL == 2, "fused epilogue handles 64 or 128 columns per wave");
-    static_assert(NT / 64 * 32 * SC * 4 <= int(sizeof(smem)), "staging must fit in LDS");
-    float *stage = reinterpret_cast<float *>(smem) + wave * 32 * SC;
-    const int col_raw = n0 + wn * TN * 32 + lane * CPL;
-    const bool col_ok = col_raw < g.N;
-    const int col = col_ok ? col_raw : g.N - CPL;    // loads stay in bounds
-    const bool lora_on = expand_enabled(g.ex);
-    uint16_t *Y = static_cast<uint16_t *>(g.Y);
-    BCache<CPL, 16> cache;
-    cache.ps = -1;
-    cache.r = -1;
-    for (int i = 0; i < TM; ++i) {
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-          stage[r * SC + j * 32 + (lane & 31)] = acc[i][j][v];
-        }
-      __syncthreads();
-      const int rbase = m0 + wm * TM * 32 + i * 32;
-      for (int rr = 0; rr < 32; ++rr) {
-        const int row = rbase + rr;
-        if (row >= g.M) break;
-        float v[CPL];
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) v[c] = stage[rr * SC + lane * CPL + c];
-        if (lora_on) expand_row_cached<CPL, 16>(v, row, col, g.ex, cache);
-        if (col_ok) Cols<uint16_t, CPL>::store(Y + int64_t(row) * g.N + col, v);
-      }
-    }
-  }
-}
-
 // ------------------------------------------------------------ decode GEMM
 // Few tokens (M <= 128): the product is a stream of W (d_in x d_out bf16)
 // through HBM, and every W byte is used by one wave only.  A workgroup owns
@@ -999,27 +844,57 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_tile_plan_kernel(GemmArg
 }
 
 // ------------------------------------------------------------ fp32 GEMM
-// Plain LDS-tiled fp32 product (the fp32 layer is small): 64x64 tile, 256
-// threads each owning 4x4 outputs; writes the fp32 base product.
+// Plain LDS-tiled fp32 product (the fp32 layer is small): 64x64 output tile,
+// 256 threads each owning 4x4 outputs, K split over blockIdx.z (partials
+// summed in order by the epilogue).  A 64-wide K chunk of both operands is
+// loaded in one round trip (16 values per thread each), the next chunk's
+// loads in flight while the current one is used.
+// Workgroup b < tiles_x * tiles_y * splits takes tile (b % tiles_x,
+// (b / tiles_x) % tiles_y) and split b / (tiles_x * tiles_y); with kPlan the
+// last workgroup builds the plan (1: arrays in LDS, 2: in the plan buffer).
+template <int kPlan>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float *X, const float *W, float *P,
-                                                        int M, int N, int Kd) {
-  __shared__ float As[16][64 + 4];
-  __shared__ float Bs[16][64 + 4];
+                                                        int M, int N, int Kd, int k_split,
+                                                        int tiles_x, int tiles_y, PlanArgs pa) {
+  constexpr int KC = 64;
+  __shared__ float As[KC][64 + 4];
+  __shared__ float Bs[KC][64 + 4];
+  if constexpr (kPlan != 0) {
+    if (blockIdx.x == gridDim.x - 1) {
+      extern __shared__ int fdyn[];
+      plan_build<kPlan == 1>(pa, fdyn);
+      return;
+    }
+  }
+  const int b = blockIdx.x;
+  const int bz = b / (tiles_x * tiles_y);
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
-  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int m0 = ((b / tiles_x) % tiles_y) * 64, n0 = (b % tiles_x) * 64;
+  const int k_begin = bz * k_split, k_end = min(Kd, k_begin + k_split);
   float acc[4][4] = {};
-  for (int k0 = 0; k0 < Kd; k0 += 16) {
+  float an[16], bn[16];
+  auto load = [&](int k0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < 16; ++e) {
       const int idx = tid + e * 256;
-      const int rr = idx >> 4, kk = idx & 15;
-      As[kk][rr] = (m0 + rr < M) ? X[int64_t(m0 + rr) * Kd + k0 + kk] : 0.f;
-      Bs[kk][rr] = (n0 + rr < N) ? W[int64_t(n0 + rr) * Kd + k0 + kk] : 0.f;
+      const int rr = idx >> 6, kk = idx & 63;
+      an[e] = X[int64_t(min(m0 + rr, M - 1)) * Kd + k0 + kk];
+      bn[e] = W[int64_t(min(n0 + rr, N - 1)) * Kd + k0 + kk];
+    }
+  };
+  if (k_begin < k_end) load(k_begin);
+  for (int k0 = k_begin; k0 < k_end; k0 += KC) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int idx = tid + e * 256;
+      As[idx & 63][idx >> 6] = an[e];
+      Bs[idx & 63][idx >> 6] = bn[e];
     }
     __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
+    if (k0 + KC < k_end) load(k0 + KC);
+#pragma unroll 8
+    for (int kk = 0; kk < KC; ++kk) {
       float av[4], bv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) { av[i] = As[kk][ty * 4 + i]; bv[i] = Bs[kk][tx * 4 + i]; }
@@ -1030,6 +905,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float *X, const flo
     }
     __syncthreads();
   }
+  float *Pz = P + int64_t(bz) * M * N;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = m0 + ty * 4 + i;
@@ -1037,7 +913,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float *X, const flo
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int col = n0 + tx * 4 + j;
-      if (col < N) P[int64_t(row) * N + col] = acc[i][j];
+      if (col < N) Pz[int64_t(row) * N + col] = acc[i][j];
     }
   }
 }
@@ -1112,27 +988,19 @@ __global__ __launch_bounds__(256) void epilogue_kernel(EpilogueArgs a, PlanArgs 
   if (col_ok) Cols<E, CPL>::store(static_cast<E *>(a.Y) + int64_t(row) * a.N + col, v);
 }
 
-template <int BM, int BN, int WM, int WN, bool kFusable>
-hipError_t launch_bf16(const GemmConfig &c, const GemmArgs &g, hipStream_t s) {
-  const dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM, c.splits);
-  const dim3 block(WM * WN * 64);
-  if constexpr (kFusable) {
-    if (c.fused) {
-      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, true>), grid, block, 0, s, g);
-      return hipGetLastError();
-    }
-  }
-  if (c.fused) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, false>), grid, block, 0, s, g);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 GemmConfig choose_gemm(int T, int d_in, int d_out, int dtype) {
   GemmConfig c{};
   if (dtype == LORA_F32) {
-    c.kind = 0; c.bm = 64; c.bn = 64; c.splits = 1; c.k_split = d_in; c.fused = false;
+    // K split so that each workgroup's K range is a few 64-wide chunks and
+    // the small fp32 layer still spreads over more than a handful of CUs
+    c.kind = 0; c.bm = 64; c.bn = 64; c.fused = false;
+    const int kb = d_in / 64;
+    const int want = kb < 8 ? kb : 8;
+    const int per = (kb + want - 1) / want;
+    c.k_split = per * 64;
+    c.splits = (kb + per - 1) / per;
     return c;
   }
   if (T <= 128) {
@@ -1186,9 +1054,10 @@ size_t gemm_partial_bytes(const GemmConfig &c, int T, int d_out) {
 
 hipError_t launch_base_gemm(const GemmConfig &c, const GemmArgs &g, hipStream_t s) {
   if (c.kind == 0) {
-    const dim3 grid((g.N + 63) / 64, (g.M + 63) / 64);
-    hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, s, static_cast<const float *>(g.X),
-                       static_cast<const float *>(g.W), g.partial, g.M, g.N, g.Kd);
+    const int tx = (g.N + 63) / 64, ty = (g.M + 63) / 64;
+    hipLaunchKernelGGL(gemm_f32_kernel<0>, dim3(unsigned(tx * ty * c.splits)), dim3(256), 0, s,
+                       static_cast<const float *>(g.X), static_cast<const float *>(g.W), g.partial,
+                       g.M, g.N, g.Kd, c.k_split, tx, ty, PlanArgs{});
     return hipGetLastError();
   }
   if (c.kind == 4) {
@@ -1210,9 +1079,7 @@ hipError_t launch_base_gemm(const GemmConfig &c, const GemmArgs &g, hipStream_t 
     }
     return hipGetLastError();
   }
-  if (c.kind == 1) return launch_bf16<64, 128, 1, 4, false>(c, g, s);
-  if (c.kind == 2) return launch_bf16<128, 128, 2, 2, false>(c, g, s);
-  return launch_bf16<256, 128, 2, 2, true>(c, g, s);
+  return hipErrorInvalidConfiguration;
 }
 
 bool decode_shrink_fusable(const GemmConfig &c, int d_in) {
@@ -1241,20 +1108,33 @@ hipError_t launch_decode_gemm_shrink(const GemmConfig &c, const GemmArgs &g, con
 }
 
 bool gemm_plan_fusable(const GemmConfig &c) {
-  return c.kind == 4 || (c.kind == 6 && c.sk > 0);
+  return c.kind == 0 || c.kind == 4 || (c.kind == 6 && c.sk > 0);
 }
 
 // Decode: the plan workgroup's LDS is the epilogue launch's dynamic LDS, which
 // every epilogue workgroup then gets too: kept to 64 KiB.  Stream-K: the
 // tile kernel's stages.
 size_t plan_lds_cap(const GemmConfig &c) {
-  if (c.kind == 4) return size_t(64) << 10;
+  if (c.kind == 4 || c.kind == 0) return size_t(64) << 10;
   return size_t(3) * TileCfg<256, 128, 2, 2>::STAGE;
 }
 
 hipError_t launch_gemm_plan(const GemmConfig &c, const GemmArgs &g, const PlanLaunch &pl,
                             hipStream_t s) {
-  if (c.kind != 6 || c.sk <= 0 || pl.lds_bytes > plan_lds_cap(c)) return hipErrorInvalidConfiguration;
+  if (pl.lds_bytes > plan_lds_cap(c)) return hipErrorInvalidConfiguration;
+  if (c.kind == 0) {
+    const int tx = (g.N + 63) / 64, ty = (g.M + 63) / 64;
+    const dim3 grid(unsigned(tx * ty * c.splits + 1)), block(256);
+    const float *X = static_cast<const float *>(g.X), *W = static_cast<const float *>(g.W);
+    if (pl.lds)
+      hipLaunchKernelGGL(gemm_f32_kernel<1>, grid, block, pl.lds_bytes, s, X, W, g.partial, g.M, g.N,
+                         g.Kd, c.k_split, tx, ty, pl.a);
+    else
+      hipLaunchKernelGGL(gemm_f32_kernel<2>, grid, block, pl.lds_bytes, s, X, W, g.partial, g.M, g.N,
+                         g.Kd, c.k_split, tx, ty, pl.a);
+    return hipGetLastError();
+  }
+  if (c.kind != 6 || c.sk <= 0) return hipErrorInvalidConfiguration;
   const dim3 grid(unsigned(1 + c.sk)), block(256);
   if (pl.lds) hipLaunchKernelGGL((gemm_tile_plan_kernel<256, 128, 2, 2, 3, true>), grid, block, 0, s, g, pl.a);
   else hipLaunchKernelGGL((gemm_tile_plan_kernel<256, 128, 2, 2, 3, false>), grid, block, 0, s, g, pl.a);

@@ -333,7 +333,7 @@ hipError_t launch_shrink(const ShrinkArgs &a, int dtype, int64_t TK, int64_t n_a
 
 // Base GEMM configuration chosen from the shape (host-side, deterministic).
 struct GemmConfig {
-  int kind;      // 0: fp32 tiles; 1: bf16 64x128; 2: bf16 128x128; 3: bf16 256x128
+  int kind;      // 0: fp32 tiles; 4: bf16 decode; 5: bf16 256x256 fused; 6: bf16 256x128 split
   int bm, bn;
   int splits;    // partial slots per output element
   int k_split;
@@ -355,10 +355,10 @@ hipError_t launch_decode_gemm_shrink(const GemmConfig &c, const GemmArgs &g, con
 // lora_forward's launches for split GEMMs.  Decode (kind 4): the GEMM's
 // partials and the per-slot shrink (ss) in one launch (launch_decode_slot),
 // then the epilogue from the slot descriptors with the plan built by one
-// more workgroup of that launch (launch_epilogue_plan).  Stream-K (kind 6):
-// the GEMM's partials with the plan built by one more workgroup
-// (launch_gemm_plan).  The plan workgroup has 256 threads and the LDS that
-// plan_lds_cap(c) gives.
+// more workgroup of that launch (launch_epilogue_plan).  Stream-K (kind 6)
+// and fp32 (kind 0): the GEMM's partials with the plan built by one more
+// workgroup (launch_gemm_plan).  The plan workgroup has 256 threads and the
+// LDS that plan_lds_cap(c) gives.
 bool gemm_plan_fusable(const GemmConfig &c);
 size_t plan_lds_cap(const GemmConfig &c);
 hipError_t launch_gemm_plan(const GemmConfig &c, const GemmArgs &g, const PlanLaunch &pl,
