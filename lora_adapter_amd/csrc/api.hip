@@ -209,7 +209,7 @@ int32_t base_args(const void *X, const void *W_t, void *Y, int32_t T, int32_t K,
   g.partial = w.partial;
   g.Y = Y;
   g.ex.K = K;
-  g.ex.slot_desc = pv.slot_desc; g.ex.page_ids = pool->page_ids;
+  g.ex.slot_desc = pv.slot_desc; g.ex.pair_tk = pv.pair_tk; g.ex.page_ids = pool->page_ids;
   g.ex.b_pages = pool->b_pages; g.ex.d_out = pool->d_out;
   g.ex.U = w.U; g.ex.hdr = pv.hdr; g.ex.u_cap = w.u_cap;
   return LORA_OK;

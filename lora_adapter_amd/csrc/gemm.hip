@@ -108,6 +108,7 @@ __device__ __forceinline__ int4 expand_row_desc(int t, const ExpandArgs &e) {
 
 template <typename E>
 __device__ __forceinline__ void expand_row8(float (&v)[8], int4 sd, int col, const ExpandArgs &e) {
+  constexpr int NB = 8;                  // B rows per batch; two batches in flight
   const E *B = static_cast<const E *>(e.b_pages);
   const int lane = lane_id();
   for (int k = 0; k < e.K; ++k) {
@@ -118,15 +119,15 @@ __device__ __forceinline__ void expand_row8(float (&v)[8], int4 sd, int col, con
       const int jl = jb + min(lane, nrb - 1);
       const int pid = e.page_ids[ps + jl];
       const float uv = e.U[uo + jl];
-      Raw8<E> ba[8], bb[8];
-      auto load8 = [&](Raw8<E> (&dst)[8], int q0) {
+      Raw8<E> ba[NB], bb[NB];
+      auto loadb = [&](Raw8<E> (&dst)[NB], int q0) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
+        for (int q = 0; q < NB; ++q)
           dst[q].load(B + int64_t(__shfl(pid, min(q0 + q, nrb - 1), 64)) * e.d_out + col);
       };
-      auto add8 = [&](const Raw8<E> (&src)[8], int q0) {
+      auto addb = [&](const Raw8<E> (&src)[NB], int q0) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < NB; ++q) {
           if (q0 + q < nrb) {
             float b[8];
             src[q].to8(b);
@@ -136,13 +137,13 @@ __device__ __forceinline__ void expand_row8(float (&v)[8], int4 sd, int col, con
           }
         }
       };
-      load8(ba, 0);
-      for (int q0 = 0; q0 < nrb; q0 += 16) {
-        load8(bb, q0 + 8);
-        add8(ba, q0);
-        if (q0 + 8 >= nrb) break;
-        load8(ba, q0 + 16);
-        add8(bb, q0 + 8);
+      loadb(ba, 0);
+      for (int q0 = 0; q0 < nrb; q0 += 2 * NB) {
+        if (q0 + NB < nrb) loadb(bb, q0 + NB);
+        addb(ba, q0);
+        if (q0 + NB >= nrb) break;
+        if (q0 + 2 * NB < nrb) loadb(ba, q0 + 2 * NB);
+        addb(bb, q0 + NB);
       }
     }
   }
@@ -927,8 +928,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float *X, const flo
 // output row; its first workgroup builds the plan (1: arrays in LDS, 2: in
 // the plan buffer) while the others add the expand from the per-slot U and
 // descriptors, which need no plan.
-template <typename E, int kPlan>
-__global__ __launch_bounds__(256) void epilogue_kernel(EpilogueArgs a, PlanArgs pa) {
+template <typename E, int kPlan, int NW>
+__global__ __launch_bounds__(NW * 64) void epilogue_kernel(EpilogueArgs a, PlanArgs pa) {
   if constexpr (kPlan != 0) {
     if (int(blockIdx.y) == int(gridDim.y) - 1) {
       if (blockIdx.x == 0) {
@@ -940,9 +941,27 @@ __global__ __launch_bounds__(256) void epilogue_kernel(EpilogueArgs a, PlanArgs 
   }
   constexpr int CPL = 8;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row = blockIdx.y * 4 + wave;
-  if (row >= a.M) return;
-  const int col_raw = (blockIdx.x * 64 + lane) * CPL;
+  int row, cx;
+  if (a.pair_tk) {
+    const int i = blockIdx.x;
+    if (i < a.n_a) {
+      const int q = (i / a.n_x) * NW + wave;
+      cx = i % a.n_x;
+      if (q >= a.ex.hdr[LORA_PH_PAIRS]) return;
+      row = a.pair_tk[q];                               // one slot per token
+    } else {
+      const int j = i - a.n_a;
+      cx = j % a.n_x;
+      row = (j / a.n_x) * NW + wave;
+      if (row >= a.M) return;
+      if (a.ex.slot_desc[row].x >= 0) return;           // taken in pair order
+    }
+  } else {
+    row = blockIdx.y * NW + wave;
+    cx = blockIdx.x;
+    if (row >= a.M) return;
+  }
+  const int col_raw = (cx * 64 + lane) * CPL;
   const bool col_ok = col_raw < a.N;
   const int col = col_ok ? col_raw : a.N - CPL;      // loads stay in bounds
   const bool lora_on = a.sdesc ? a.ex.U != nullptr : expand_enabled(a.ex);
@@ -1163,13 +1182,14 @@ hipError_t launch_epilogue_plan(const GemmConfig &c, const GemmArgs &g, int dtyp
                                 const float *slot_u, const int4 *sdesc, const PlanLaunch &pl,
                                 hipStream_t s) {
   if (c.fused || pl.lds_bytes > plan_lds_cap(c)) return hipErrorInvalidConfiguration;
-  EpilogueArgs e{g.partial, c.splits, g.M, g.N, c.sk, g.Kd / 64, c.bm, c.bn, g.Y, g.ex, sdesc};
+  EpilogueArgs e{g.partial, c.splits, g.M, g.N, c.sk, g.Kd / 64, c.bm, c.bn, g.Y, g.ex, sdesc,
+                 nullptr, 0, 0};
   e.ex.U = slot_u;
   const dim3 grid((g.N + 511) / 512, (g.M + 3) / 4 + 1);
   const size_t lds = pl.lds_bytes;
 #define LORA_EP(E) do { \
-    if (pl.lds) hipLaunchKernelGGL((epilogue_kernel<E, 1>), grid, dim3(256), lds, s, e, pl.a); \
-    else hipLaunchKernelGGL((epilogue_kernel<E, 2>), grid, dim3(256), lds, s, e, pl.a); \
+    if (pl.lds) hipLaunchKernelGGL((epilogue_kernel<E, 1, 4>), grid, dim3(256), lds, s, e, pl.a); \
+    else hipLaunchKernelGGL((epilogue_kernel<E, 2, 4>), grid, dim3(256), lds, s, e, pl.a); \
   } while (0)
   if (dtype == LORA_BF16) LORA_EP(uint16_t);
   else LORA_EP(float);
@@ -1179,11 +1199,22 @@ hipError_t launch_epilogue_plan(const GemmConfig &c, const GemmArgs &g, int dtyp
 
 hipError_t launch_epilogue(const GemmConfig &c, const GemmArgs &g, int dtype, hipStream_t s) {
   if (c.fused) return hipSuccess;
-  EpilogueArgs e{g.partial, c.splits, g.M, g.N, c.sk, g.Kd / 64, c.bm, c.bn, g.Y, g.ex, nullptr};
-  const dim3 grid((g.N + 511) / 512, (g.M + 3) / 4);
+  EpilogueArgs e{g.partial, c.splits, g.M, g.N, c.sk, g.Kd / 64, c.bm, c.bn, g.Y, g.ex, nullptr,
+                 nullptr, 0, 0};
   const PlanArgs none{};
-  if (dtype == LORA_BF16) hipLaunchKernelGGL((epilogue_kernel<uint16_t, 0>), grid, dim3(256), 0, s, e, none);
-  else hipLaunchKernelGGL((epilogue_kernel<float, 0>), grid, dim3(256), 0, s, e, none);
+  if (dtype == LORA_BF16 && c.kind == 6 && g.ex.K == 1 && g.ex.pair_tk) {
+    // one slot per token: rows in pair order, 8 per workgroup (see EpilogueArgs)
+    const int n_x = (g.N + 511) / 512;
+    e.pair_tk = g.ex.pair_tk;
+    e.n_x = n_x;
+    e.n_a = ((g.M + 7) / 8) * n_x;
+    const dim3 grid(unsigned(2 * e.n_a));
+    hipLaunchKernelGGL((epilogue_kernel<uint16_t, 0, 8>), grid, dim3(512), 0, s, e, none);
+    return hipGetLastError();
+  }
+  const dim3 grid((g.N + 511) / 512, (g.M + 3) / 4);
+  if (dtype == LORA_BF16) hipLaunchKernelGGL((epilogue_kernel<uint16_t, 0, 4>), grid, dim3(256), 0, s, e, none);
+  else hipLaunchKernelGGL((epilogue_kernel<float, 0, 4>), grid, dim3(256), 0, s, e, none);
   return hipGetLastError();
 }
 

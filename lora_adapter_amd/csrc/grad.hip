@@ -18,10 +18,13 @@
 namespace lora {
 namespace {
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 constexpr int kGradThreads = 256;
 constexpr int kGradCPL = 4;                           // columns per lane
 constexpr int kGradCols = kGradThreads * kGradCPL;    // columns per workgroup
-constexpr int kGradAhead = 8;                         // token rows in flight per lane
+constexpr int kGradAhead = 8;                         // token rows per batch (two in flight)
 static_assert(kGradPairChunk == kGradThreads, "one staged pair per thread");
 
 // 4 consecutive elements held raw until used.
@@ -112,28 +115,32 @@ __global__ __launch_bounds__(kGradThreads) void seg_outer_partial_kernel(SegOute
 #pragma unroll
         for (int c = 0; c < kGradCPL; ++c) acc[jj][c] = 0.f;
       const int l_end = send - pbeg;
-      for (int l0 = p - pbeg; l0 < l_end; l0 += kGradAhead) {
-        // every row of the group is loaded before any is used (clamped to
-        // the last pair, so no load sits behind a branch)
-        Z4<E> z[kGradAhead];
-        uint32_t mk[kGradAhead];
+      // two batches of kGradAhead token rows, the next one in flight while
+      // the current one is added (rows clamped to the segment's last pair; a
+      // row past the end, or a masked element, is multiplied by an exact 0)
+      Z4<E> za[kGradAhead], zb[kGradAhead];
+      uint32_t ma[kGradAhead], mb[kGradAhead];
+      auto load_batch = [&](Z4<E> (&z)[kGradAhead], uint32_t (&m)[kGradAhead], int l0) {
 #pragma unroll
         for (int u = 0; u < kGradAhead; ++u) {
           const int64_t row = s_row[min(l0 + u, l_end - 1)];
           z[u].load(Z + row * a.d + col);
-          if (kMask) mk[u] = *reinterpret_cast<const uint32_t *>(a.mask + row * a.d + col);
+          if (kMask) m[u] = *reinterpret_cast<const uint32_t *>(a.mask + row * a.d + col);
         }
+      };
+      auto add_batch = [&](const Z4<E> (&z)[kGradAhead], const uint32_t (&m)[kGradAhead], int l0) {
 #pragma unroll
         for (int u = 0; u < kGradAhead; ++u) {
-          if (l0 + u >= l_end) break;
           float zv[kGradCPL];
           z[u].get(zv);
-          if (kMask) {
+          const float in = l0 + u < l_end ? 1.f : 0.f;
 #pragma unroll
-            for (int c = 0; c < kGradCPL; ++c)
-              if (((mk[u] >> (8 * c)) & 0xffu) == 0) zv[c] = 0.f;
+          for (int c = 0; c < kGradCPL; ++c) {
+            float f = in;
+            if (kMask) f *= float((m[u] >> (8 * c)) & 0xffu);   // keep mask is 0/1
+            zv[c] *= f;
           }
-          const float *cf = s_cf[l0 + u];
+          const float *cf = s_cf[min(l0 + u, l_end - 1)];
 #pragma unroll
           for (int jj = 0; jj < RB; ++jj) {
             const float cj = cf[jj];   // zero past nr
@@ -141,6 +148,14 @@ __global__ __launch_bounds__(kGradThreads) void seg_outer_partial_kernel(SegOute
             for (int c = 0; c < kGradCPL; ++c) acc[jj][c] = fmaf(cj, zv[c], acc[jj][c]);
           }
         }
+      };
+      load_batch(za, ma, p - pbeg);
+      for (int l0 = p - pbeg; l0 < l_end; l0 += 2 * kGradAhead) {
+        load_batch(zb, mb, l0 + kGradAhead);
+        add_batch(za, ma, l0);
+        if (l0 + kGradAhead >= l_end) break;
+        load_batch(za, ma, l0 + 2 * kGradAhead);
+        add_batch(zb, mb, l0 + kGradAhead);
       }
       if (col_ok) {
         float *dst = a.part + (int64_t(s + q) * a.max_rank + j0) * a.d + col;
@@ -155,40 +170,194 @@ __global__ __launch_bounds__(kGradThreads) void seg_outer_partial_kernel(SegOute
   }
 }
 
-// Adds each segment's partials in chunk order (up to 8 loads in flight) and
-// writes the fp32 gradient page of every rank row.
-__global__ __launch_bounds__(kGradThreads) void seg_outer_reduce_kernel(SegOuterArgs a) {
+// The same partials with bf16 MFMA (prefill-size batches): out[j][n] =
+// sum_p cf[p][j] . Z[t_p][n] is a (16 rank rows) x (columns) product over the
+// pairs, v_mfma_f32_16x16x32_bf16 with the pairs as K.  One workgroup per
+// (256 columns, chunk of 256 pairs, 16 rank rows); per step of 32 pairs the
+// gathered token rows (keep mask applied: exact zeros) are staged in LDS, the
+// next step's rows in flight meanwhile.  The fp32 coefficients are split
+// exactly into bf16 high and low parts (two MFMAs), which keeps ~16 bits.
+constexpr int kOuterCols = 256;
+constexpr int kOuterK = 32;
+
+template <bool kMask>
+__global__ __launch_bounds__(256) void seg_outer_mfma_kernel(SegOuterArgs a) {
   constexpr int RB = kGradRankChunk;
+  constexpr int ZP = kOuterCols + 8;          // staged row pitch (bf16)
+  __shared__ int s_row[kGradPairChunk];
+  __shared__ __attribute__((aligned(16))) float s_cf[kGradPairChunk][RB];
+  __shared__ __attribute__((aligned(16))) uint16_t s_z[kOuterK][ZP];
+  const int P = a.plan.hdr[LORA_PH_PAIRS];
+  const int S = a.plan.hdr[LORA_PH_SEGS];
+  const int q = blockIdx.y;
+  const int pbeg = q * kGradPairChunk;
+  if (pbeg >= P) return;
+  if (int64_t(a.plan.hdr[LORA_PH_RPAIRS]) > a.coef_cap) {
+    if (q == 0 && blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x == 0)
+      atomicOr(a.err_word, LORA_DEVERR_CAPACITY);
+    return;
+  }
+  const int pend = min(P, pbeg + kGradPairChunk);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j0 = blockIdx.z * RB;
+  {
+    const int pp = pbeg + tid;
+    int row = 0;
+    float cf[RB];
+#pragma unroll
+    for (int jj = 0; jj < RB; ++jj) cf[jj] = 0.f;
+    if (pp < pend) {
+      row = a.plan.pair_tk[pp] / a.K;
+      const int r = a.rank[a.plan.pair_adapter[pp]];
+      const int nr = min(RB, min(r, a.max_rank) - j0);
+      const float *c = a.coef + a.plan.u_off[pp] + j0;
+#pragma unroll
+      for (int jj = 0; jj < RB; ++jj)
+        if (jj < nr) cf[jj] = c[jj];
+    }
+    s_row[tid] = row;
+#pragma unroll
+    for (int jj = 0; jj < RB; jj += 4)
+      *reinterpret_cast<float4 *>(&s_cf[tid][jj]) = make_float4(cf[jj], cf[jj + 1], cf[jj + 2], cf[jj + 3]);
+  }
+  __syncthreads();
+
+  const int c0 = blockIdx.x * kOuterCols;
+  const uint16_t *Z = static_cast<const uint16_t *>(a.Z);
+  // staging: thread tid fills row tid / 8 of the step, columns (tid % 8) * 32 .. +31
+  const int zr = tid >> 3, zc = (tid & 7) * 32;
+  int s = seg_of(a.plan.seg_off, S, pbeg);
+  for (int p = pbeg; p < pend; ++s) {
+    const int send = min(pend, a.plan.seg_off[s + 1]);
+    const int ad = a.plan.seg_adapter[s];
+    const int r = a.rank[ad];
+    if (r > a.max_rank) {
+      if (tid == 0 && blockIdx.x == 0 && j0 == 0) atomicOr(a.err_word, LORA_DEVERR_CAPACITY);
+    } else if (j0 < r) {
+      const int nr = min(RB, r - j0);
+      const int l_beg = p - pbeg, l_end = send - pbeg;
+      uint4 zv[4];
+      uint4 mv[2];
+      auto fetch = [&](int k0) {
+        const int64_t row = s_row[min(k0 + zr, l_end - 1)];
+        const uint16_t *src = Z + row * a.d + c0 + zc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) zv[e] = *reinterpret_cast<const uint4 *>(src + 8 * e);
+        if (kMask) {
+          const uint8_t *m = a.mask + row * a.d + c0 + zc;
+          mv[0] = *reinterpret_cast<const uint4 *>(m);
+          mv[1] = *reinterpret_cast<const uint4 *>(m + 16);
+        }
+      };
+      auto stage = [&](int k0) {
+        const bool in = k0 + zr < l_end;
+        uint32_t w[16];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w[4 * e] = zv[e].x; w[4 * e + 1] = zv[e].y; w[4 * e + 2] = zv[e].z; w[4 * e + 3] = zv[e].w;
+        }
+        const uint32_t mb[8] = {mv[0].x, mv[0].y, mv[0].z, mv[0].w, mv[1].x, mv[1].y, mv[1].z, mv[1].w};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          uint32_t keep = in ? 0xffffffffu : 0u;
+          if (kMask) {
+            // element 2i is byte (2i) of the mask, element 2i+1 byte (2i+1)
+            const uint32_t m4 = mb[i >> 1] >> (16 * (i & 1));
+            keep &= ((m4 & 0xffu) ? 0x0000ffffu : 0u) | ((m4 & 0xff00u) ? 0xffff0000u : 0u);
+          }
+          w[i] &= keep;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          *reinterpret_cast<uint4 *>(&s_z[zr][zc + 8 * e]) =
+              make_uint4(w[4 * e], w[4 * e + 1], w[4 * e + 2], w[4 * e + 3]);
+      };
+      f32x4_t acc[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      fetch(l_beg);
+      for (int k0 = l_beg; k0 < l_end; k0 += kOuterK) {
+        __syncthreads();                       // the previous step is done with s_z
+        stage(k0);
+        __syncthreads();
+        if (k0 + kOuterK < l_end) fetch(k0 + kOuterK);
+        // A operand: rank row j = lane % 16, pairs k0 + 8 * (lane / 16) + e
+        const int kk = (lane >> 4) * 8;
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const int la = k0 + kk + e, lb = la + 1;
+          const float ua = la < l_end ? s_cf[la][lane & 15] : 0.f;
+          const float ub = lb < l_end ? s_cf[lb][lane & 15] : 0.f;
+          const uint16_t ha = f2bf(ua), hb = f2bf(ub);
+          const uint16_t xa = f2bf(ua - bf2f(ha)), xb = f2bf(ub - bf2f(hb));
+          hw[e >> 1] = uint32_t(ha) | (uint32_t(hb) << 16);
+          lw[e >> 1] = uint32_t(xa) | (uint32_t(xb) << 16);
+        }
+        bf16x8_t ahi, alo;
+        const uint4 ph = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        const uint4 pl = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        __builtin_memcpy(&ahi, &ph, 16);
+        __builtin_memcpy(&alo, &pl, 16);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          // B operand: column wave*64 + 16b + lane % 16, the same 8 pairs
+          const int col = wave * 64 + 16 * b + (lane & 15);
+          uint32_t bw[4];
+#pragma unroll
+          for (int e = 0; e < 8; e += 2)
+            bw[e >> 1] = uint32_t(s_z[kk + e][col]) | (uint32_t(s_z[kk + e + 1][col]) << 16);
+          bf16x8_t bfrag;
+          const uint4 pb = make_uint4(bw[0], bw[1], bw[2], bw[3]);
+          __builtin_memcpy(&bfrag, &pb, 16);
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bfrag, acc[b], 0, 0, 0);
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bfrag, acc[b], 0, 0, 0);
+        }
+      }
+      // lane holds column (lane % 16) of each block and rank rows 4 * (lane / 16) + i
+      float *dst = a.part + (int64_t(s + q) * a.max_rank + j0) * a.d + c0 + wave * 64 + (lane & 15);
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int jj = (lane >> 4) * 4 + i;
+          if (jj < nr) dst[int64_t(jj) * a.d + 16 * b] = acc[b][i];
+        }
+    }
+    p = send;
+  }
+}
+
+// Adds each segment's partials in chunk order (up to 8 loads in flight) and
+// writes the fp32 gradient page of every rank row: one workgroup per (1024
+// columns, segment, rank row).
+__global__ __launch_bounds__(kGradThreads) void seg_outer_reduce_kernel(SegOuterArgs a) {
   const int S = a.plan.hdr[LORA_PH_SEGS];
   const int col = (blockIdx.x * kGradThreads + threadIdx.x) * kGradCPL;
   if (col >= a.d) return;
   if (int64_t(a.plan.hdr[LORA_PH_RPAIRS]) > a.coef_cap) return;
-  const int j0 = blockIdx.z * RB;
+  const int j = blockIdx.z;
   for (int s = blockIdx.y; s < S; s += gridDim.y) {
     const int ad = a.plan.seg_adapter[s];
     const int r = a.rank[ad];
-    if (r > a.max_rank || j0 >= r) continue;
-    const int nr = min(RB, r - j0);
+    if (r > a.max_rank || j >= r) continue;
     const int q0 = a.plan.seg_off[s] / kGradPairChunk;
     const int q1 = (a.plan.seg_off[s + 1] - 1) / kGradPairChunk;
-    const int32_t *pid = a.page_ids + a.page_start[ad];
-    for (int jj = 0; jj < nr; ++jj) {
-      float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int qb = q0; qb <= q1; qb += 8) {
-        float4 v[8];
+    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int qb = q0; qb <= q1; qb += 8) {
+      float4 v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          v[u] = *reinterpret_cast<const float4 *>(
-              a.part + (int64_t(s + min(qb + u, q1)) * a.max_rank + j0 + jj) * a.d + col);
+      for (int u = 0; u < 8; ++u)
+        v[u] = *reinterpret_cast<const float4 *>(
+            a.part + (int64_t(s + min(qb + u, q1)) * a.max_rank + j) * a.d + col);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          if (qb + u <= q1) {
-            sum.x += v[u].x; sum.y += v[u].y; sum.z += v[u].z; sum.w += v[u].w;
-          }
+      for (int u = 0; u < 8; ++u) {
+        if (qb + u <= q1) {
+          sum.x += v[u].x; sum.y += v[u].y; sum.z += v[u].z; sum.w += v[u].w;
         }
       }
-      *reinterpret_cast<float4 *>(a.out_pages + int64_t(pid[j0 + jj]) * a.d + col) = sum;
     }
+    *reinterpret_cast<float4 *>(a.out_pages + int64_t(a.page_ids[a.page_start[ad] + j]) * a.d + col) = sum;
   }
 }
 
@@ -205,7 +374,12 @@ hipError_t launch_seg_outer(const SegOuterArgs &a, int dtype, int64_t TK, int64_
   const unsigned chunks = unsigned((TK + kGradPairChunk - 1) / kGradPairChunk);
   const unsigned rchunks = unsigned((a.max_rank + kGradRankChunk - 1) / kGradRankChunk);
   const dim3 g1(cols, chunks, rchunks), block(kGradThreads);
-  if (dtype == LORA_BF16) {
+  if (dtype == LORA_BF16 && TK >= 2048 && a.d % kOuterCols == 0) {
+    // prefill-size batches: the MFMA form (long segments make it dense)
+    const dim3 gm(unsigned(a.d / kOuterCols), chunks, rchunks);
+    if (a.mask) hipLaunchKernelGGL((seg_outer_mfma_kernel<true>), gm, block, 0, st, a);
+    else hipLaunchKernelGGL((seg_outer_mfma_kernel<false>), gm, block, 0, st, a);
+  } else if (dtype == LORA_BF16) {
     if (a.mask) hipLaunchKernelGGL((seg_outer_partial_kernel<uint16_t, true>), g1, block, 0, st, a);
     else hipLaunchKernelGGL((seg_outer_partial_kernel<uint16_t, false>), g1, block, 0, st, a);
   } else {
@@ -215,7 +389,7 @@ hipError_t launch_seg_outer(const SegOuterArgs &a, int dtype, int64_t TK, int64_
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t segs = TK < N ? TK : N;
-  const dim3 g2(cols, unsigned(segs < 65535 ? segs : 65535), rchunks);
+  const dim3 g2(cols, unsigned(segs < 65535 ? segs : 65535), unsigned(a.max_rank));
   hipLaunchKernelGGL(seg_outer_reduce_kernel, g2, block, 0, st, a);
   return hipGetLastError();
 }

@@ -230,6 +230,7 @@ struct SlotShrinkArgs {
 struct ExpandArgs {
   int K;
   const int4 *slot_desc;    // per slot {pair or -1, rank, u_off, page_start}
+  const int32_t *pair_tk;   // the plan's pair order (t*K + k of each sorted pair)
   const int32_t *page_ids;
   const void *b_pages;      // [n_pages][d_out]
   int d_out;
@@ -258,6 +259,13 @@ struct EpilogueArgs {
   // not null: ex.U holds U per slot and sdesc the slot descriptors written by
   // the per-slot shrink; the plan is not read (lora_forward's decode path)
   const int4 *sdesc;
+  // not null (one slot per token, plan available): rows in the plan's pair
+  // order, 8 consecutive pairs per workgroup (one per wave), so the rows of
+  // one adapter in a workgroup share its B lines in the CU's caches (1-D
+  // grid: n_a workgroups of pair rows over n_x column chunks, then the rows
+  // without an active slot in token order)
+  const int32_t *pair_tk;
+  int n_x, n_a;
 };
 
 struct MergeArgs {

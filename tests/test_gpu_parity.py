@@ -491,6 +491,22 @@ def test_grads_multi_adapter_top2():
     _check_grads(w, run(w))
 
 
+def test_grads_mfma_mixed_ranks_top2():
+    """A batch large enough for the MFMA outer products (T*K >= 2048): two
+    slots per token, empty slots and zero gates, ranks below and above the
+    16-row blocks, a keep mask."""
+    rng = np.random.default_rng(23)
+    N, T, K = 12, 1100, 2
+    rank = np.array([3, 16, 17, 40, 64, 5, 8, 1, 33, 16, 2, 24], np.int32)
+    ids = rng.integers(-1, N, size=(T, K)).astype(np.int32)
+    gates = rng.standard_normal((T, K)).astype(np.float32)
+    gates[rng.random((T, K)) < 0.1] = 0
+    w = wl.build("grad-mfma", 23, "bf16", T, K, 512, 768, rank, ids, gates,
+                 x_var=1.0, w_var=0.02, a_var=1 / 64, b_var=0.02, keep_p=0.9, with_dY=True,
+                 scale=rng.uniform(0.5, 2, N).astype(np.float32))
+    _check_grads(w, run(w))
+
+
 def test_grads_full_prefill():
     w = full(4)
     _check_grads(w, run(w))
