@@ -194,9 +194,405 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs m) {
   }
 }
 
+// ------------------------------------------------------------ bf16 MFMA form
+// The delta of W_t is a product with the rank rows as K:
+//   delta[n][i] = sum_j A_j[i] . (c_j B_j[n])
+// computed with v_mfma_f32_32x32x16_bf16, M = i, N = n.  A pages are bf16
+// already (exact operands); c_j B_j[n] is formed in float32 and split into
+// bf16 high and low parts (two MFMAs), which keeps ~16 bits of it.  MFMA
+// rows are assigned to W columns so that every lane ends with 16 consecutive
+// columns of one W row: its W values load and store as 16-byte pieces.
+// One workgroup per 128 x 128 rectangle of W_t: its W values are requested
+// first, then the rectangle's slices of the listed A and B rows are staged in
+// LDS (transposed, rank rows contiguous), 64 rank rows at a time; wave w
+// owns rows 32 w .. 32 w + 31 of the rectangle.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kQN = 128;           // W rows per workgroup (4 waves x 32)
+constexpr int kQI = 128;           // W columns per workgroup
+constexpr int kQR = 64;            // rank rows per staged chunk
+constexpr int kQB = kQI / 32;      // 32-column MFMA blocks per wave
+
+// 16-byte chunk c (8 rank rows) of staged row x sits at chunk c ^ ((x >> 1) & 7):
+// 16 consecutive rows read the same chunk without bank conflicts.
+__device__ __forceinline__ int qswz(int x, int c) { return c ^ ((x >> 1) & 7); }
+
+// 8 x 8 bf16 transpose in registers: in[r] holds row r (8 values, 2 per
+// word); out[c] holds column c.  Each output word takes one half of a word
+// of two input rows (v_perm_b32).
+__device__ __forceinline__ uint32_t word_of(const uint4 &v, int q) {
+  return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
+}
+__device__ __forceinline__ void transpose8(const uint4 (&in)[8], uint4 (&out)[8]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t lo = word_of(in[2 * q], c >> 1), hi = word_of(in[2 * q + 1], c >> 1);
+      // even c: the low halves of (lo, hi); odd c: the high halves
+      w[q] = __builtin_amdgcn_perm(hi, lo, (c & 1) ? 0x07060302u : 0x05040100u);
+    }
+    out[c] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// Stages listed rank rows [j0, j0 + nl) (zero past nl):
+//   s_at[i][j] = A_j[i0 + i]                          i < 128
+//   s_bh[n][j] + s_bl[n][j] = c_j B_j[n0 + n]          n < 128
+// Threads 0..127 transpose one (8 rows, 8 columns) block of A each, threads
+// 128..255 one block of B.
+__device__ __forceinline__ void qstage(const MergeArgs &m, int i0, int n0, int j0, int nl,
+                                       const int *s_pid, const float *s_cf,
+                                       uint4 (*s_at)[8], uint4 (*s_bh)[8], uint4 (*s_bl)[8]) {
+  const int tid = threadIdx.x;
+  const bool is_b = tid >= 128;
+  const int jg = tid & 7, xg = (tid & 127) >> 3;
+  const uint16_t *src = static_cast<const uint16_t *>(is_b ? m.b_pages : m.a_pages);
+  const int64_t len = is_b ? m.d_out : m.d_in;
+  const int x0 = (is_b ? n0 : i0) + xg * 8;
+  uint4 rw[8], t[8];
+  float cf[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int j = jg * 8 + r;
+    const bool ok = j < nl;
+    cf[r] = ok ? s_cf[j0 + j] : 0.f;
+    rw[r] = make_uint4(0u, 0u, 0u, 0u);
+    if (ok) rw[r] = *reinterpret_cast<const uint4 *>(src + int64_t(s_pid[j0 + j]) * len + x0);
+  }
+  if (!is_b) {
+    transpose8(rw, t);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int i = xg * 8 + c;
+      s_at[i][qswz(i, jg)] = t[c];
+    }
+    return;
+  }
+  // c_j B_j[n] in float32 (after the transpose: word q of column c holds rank
+  // rows 2q and 2q + 1), split into bf16 high and low parts
+  transpose8(rw, t);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int n = xg * 8 + c;
+    const uint32_t w[4] = {t[c].x, t[c].y, t[c].z, t[c].w};
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float x0 = cf[2 * q] * bf_lo(w[q]), x1 = cf[2 * q + 1] * bf_hi(w[q]);
+      const uint16_t h0 = f2bf(x0), h1 = f2bf(x1);
+      const uint16_t l0 = f2bf(x0 - bf2f(h0)), l1 = f2bf(x1 - bf2f(h1));
+      hw[q] = uint32_t(h0) | (uint32_t(h1) << 16);
+      lw[q] = uint32_t(l0) | (uint32_t(l1) << 16);
+    }
+    s_bh[n][qswz(n, jg)] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    s_bl[n][qswz(n, jg)] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+  }
+}
+
+// acc[b] += the staged chunk's product for MFMA block b (columns 32 b ..) of
+// this wave's 32 rows.
+__device__ __forceinline__ void qmfma(int nl, const uint4 (*s_at)[8], const uint4 (*s_bh)[8],
+                                      const uint4 (*s_bl)[8], f32x16_t (&acc)[kQB]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m = lane & 31, g = lane >> 5;
+  const int n = wave * 32 + m;
+  // MFMA row m -> W column 16 (m >> 4) + 8 ((m >> 2) & 1) + 4 ((m >> 3) & 1) + (m & 3)
+  const int icol = 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
+  for (int k = 0; k < nl; k += 16) {
+    const int c = (k >> 3) + g;
+    bf16x8_t bh, bl;
+    __builtin_memcpy(&bh, &s_bh[n][qswz(n, c)], 16);
+    __builtin_memcpy(&bl, &s_bl[n][qswz(n, c)], 16);
+#pragma unroll
+    for (int b = 0; b < kQB; ++b) {
+      const int i = b * 32 + icol;
+      bf16x8_t a;
+      __builtin_memcpy(&a, &s_at[i][qswz(i, c)], 16);
+      acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, acc[b], 0, 0, 0);
+      acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl, acc[b], 0, 0, 0);
+    }
+  }
+}
+
+// Barrier for LDS traffic only: global loads in flight stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Streaming form, for merge lists of at most kQR valid rank rows (all staged
+// at once): workgroup w takes a contiguous range of 64 x 128 rectangles of
+// one 128-column slice (its A slice is staged once) and keeps kSD of them in
+// flight in registers: the W rectangle (coalesced 16-byte
+// loads, 4 rows x 256 bytes per wave instruction) and the 64 x 64 B block.
+// Per rectangle: W goes to LDS (16-byte slots swizzled by row), c.B to
+// bf16 high/low parts in LDS, the MFMA delta is added in the lane layout,
+// and the rounded rectangle is read back and stored with the same coalesced
+// pattern.
+constexpr int kSN = 64;            // W rows per rectangle
+constexpr int kSD = 3;             // rectangles in flight per workgroup
+
+__device__ __forceinline__ void merge_stream(const MergeArgs &m, int total, uint4 *raw,
+                                             const int *s_pid, const float *s_cf) {
+  uint4 (*s_at)[8] = reinterpret_cast<uint4 (*)[8]>(raw);            // [128 i][64 j]
+  uint32_t (*s_bh)[32] = reinterpret_cast<uint32_t (*)[32]>(raw + 1024);   // [64 n][64 j]
+  uint32_t (*s_bl)[32] = reinterpret_cast<uint32_t (*)[32]>(raw + 1536);
+  uint4 (*wbuf)[16] = reinterpret_cast<uint4 (*)[16]>(raw + 2048);   // [64 rows][256 bytes]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nrn = m.d_out / kSN;
+  const int gx = m.d_in / kQI;
+  // workgroup -> (column slice, part of its rectangles): gridDim.x = gx * gps
+  const int gps = gridDim.x / gx;
+  const int slice = blockIdx.x / gps, part = blockIdx.x % gps;
+  const int beg = nrn * part / gps, end = nrn * (part + 1) / gps;   // rectangle rows of the slice
+  if (slice >= gx || beg >= end) return;
+  const int i0 = slice * kQI;
+  uint16_t *W = static_cast<uint16_t *>(m.W);
+  const uint16_t *Ap = static_cast<const uint16_t *>(m.a_pages);
+  const uint16_t *Bp = static_cast<const uint16_t *>(m.b_pages);
+  // this thread's B pieces: rank rows 2 jp and 2 jp + 1, columns n0 + 8 nc .. + 7
+  const int jp = tid >> 3, nc = tid & 7;
+  const bool oka = 2 * jp < total, okb = 2 * jp + 1 < total;
+  const int64_t pga = s_pid[oka ? 2 * jp : 0], pgb = s_pid[okb ? 2 * jp + 1 : 0];
+  const float ca = oka ? s_cf[2 * jp] : 0.f, cb = okb ? s_cf[2 * jp + 1] : 0.f;
+  // this thread's W pieces: rows (tid / 16) + 16 e, 16-byte chunk tid % 16
+  const int wr0 = tid >> 4, wc = tid & 15;
+  if (tid < 128) {
+    // the A slice: threads 0..127 transpose one (8 rank rows, 8 columns) block each
+    const int jg = tid & 7, xg = tid >> 3;
+    uint4 rw[8], t[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int j = jg * 8 + q;
+      const int64_t pg = s_pid[j < total ? j : 0];
+      rw[q] = *reinterpret_cast<const uint4 *>(Ap + pg * m.d_in + i0 + xg * 8);
+      if (j >= total) rw[q] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    transpose8(rw, t);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int i = xg * 8 + c;
+      s_at[i][qswz(i, jg)] = t[c];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  auto load_rect = [&](int r, u32x4 (&wv)[4], u32x4 &ba, u32x4 &bb) __attribute__((always_inline)) {
+    const int n0 = min(r, end - 1) * kSN;   // past the range: a harmless reload, never used
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      wv[e] = *reinterpret_cast<const u32x4 *>(W + int64_t(n0 + wr0 + 16 * e) * m.d_in + i0 + 8 * wc);
+    ba = *reinterpret_cast<const u32x4 *>(Bp + pga * m.d_out + n0 + 8 * nc);
+    bb = *reinterpret_cast<const u32x4 *>(Bp + pgb * m.d_out + n0 + 8 * nc);
+  };
+  // MFMA roles: rows 32 (wave & 1) .. of the rectangle, columns 64 (wave >> 1) ..
+  const int mrow = lane & 31, g = lane >> 5;
+  const int nrow = 32 * (wave & 1) + mrow;
+  const int ih = wave >> 1;
+  const int icol = 16 * (mrow >> 4) + 8 * ((mrow >> 2) & 1) + 4 * ((mrow >> 3) & 1) + (mrow & 3);
+  // Every workgroup runs whole groups of kSD steps (a step past its range
+  // only keeps the barriers and reissues a clamped load), so the three slots
+  // stay three distinct register sets.
+  auto step = [&](int r, u32x4 (&wv)[4], u32x4 &ba, u32x4 &bb) __attribute__((always_inline)) {
+    const bool valid = r < end;
+    const int n0 = min(r, end - 1) * kSN;
+    lds_barrier();                     // the previous rectangle is done with the LDS tiles
+    if (valid) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = wr0 + 16 * e;
+        wbuf[row][wc ^ (row & 15)] = make_uint4(wv[e][0], wv[e][1], wv[e][2], wv[e][3]);
+      }
+      const uint32_t wa[4] = {ba[0], ba[1], ba[2], ba[3]}, wb[4] = {bb[0], bb[1], bb[2], bb[3]};
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t va = wa[u >> 1], vb = wb[u >> 1];
+        const float xa = oka ? ca * ((u & 1) ? bf_hi(va) : bf_lo(va)) : 0.f;
+        const float xb = okb ? cb * ((u & 1) ? bf_hi(vb) : bf_lo(vb)) : 0.f;
+        const uint16_t ha = f2bf(xa), hb = f2bf(xb);
+        const uint16_t la = f2bf(xa - bf2f(ha)), lb = f2bf(xb - bf2f(hb));
+        const int n = 8 * nc + u;
+        const int word = qswz(n, jp >> 2) * 4 + (jp & 3);
+        s_bh[n][word] = uint32_t(ha) | (uint32_t(hb) << 16);
+        s_bl[n][word] = uint32_t(la) | (uint32_t(lb) << 16);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_rect(r + kSD, wv, ba, bb);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    if (valid) {
+      f32x16_t acc[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
+      for (int k = 0; k < total; k += 16) {
+        const int c = (k >> 3) + g;
+        bf16x8_t bh, bl;
+        __builtin_memcpy(&bh, &s_bh[nrow][qswz(nrow, c) * 4], 16);
+        __builtin_memcpy(&bl, &s_bl[nrow][qswz(nrow, c) * 4], 16);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const int i = 64 * ih + 32 * b + icol;
+          bf16x8_t av;
+          __builtin_memcpy(&av, &s_at[i][qswz(i, c)], 16);
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bh, acc[b], 0, 0, 0);
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bl, acc[b], 0, 0, 0);
+        }
+      }
+      // lane value v of block b: column 64 ih + 32 b + 16 (v / 8) + 8 g + (v % 8) of row nrow
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int c = 8 * ih + 4 * b + 2 * q + g;
+          uint4 &slot = wbuf[nrow][c ^ (nrow & 15)];
+          const uint4 wvv = slot;
+          const uint32_t w[4] = {wvv.x, wvv.y, wvv.z, wvv.w};
+          uint32_t o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float lo = bf_lo(w[e]) + acc[b][8 * q + 2 * e];
+            const float hi = bf_hi(w[e]) + acc[b][8 * q + 2 * e + 1];
+            o[e] = uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
+          }
+          slot = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+    }
+    lds_barrier();
+    if (valid) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = wr0 + 16 * e;
+        *reinterpret_cast<uint4 *>(W + int64_t(n0 + row) * m.d_in + i0 + 8 * wc) = wbuf[row][wc ^ (row & 15)];
+      }
+    }
+  };
+  u32x4 w0[4], w1[4], w2[4], b0a, b0b, b1a, b1b, b2a, b2b;
+  load_rect(beg, w0, b0a, b0b);
+  __builtin_amdgcn_sched_barrier(0);
+  load_rect(beg + 1, w1, b1a, b1b);
+  __builtin_amdgcn_sched_barrier(0);
+  load_rect(beg + 2, w2, b2a, b2b);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int r = beg; r < end; r += kSD) {
+    step(r, w0, b0a, b0b);
+    step(r + 1, w1, b1a, b1b);
+    step(r + 2, w2, b2a, b2b);
+  }
+}
+
+// General form (any merge list): workgroup w takes 128 x 128 rectangles w,
+// w + G, ...; the merge list is built once per workgroup when it fits one LDS
+// list.  Lists of at most kQR rank rows take the streaming form.
+__global__ __launch_bounds__(256) void merge_mfma_kernel(MergeArgs m) {
+  __shared__ uint4 raw[3072];
+  __shared__ int s_pid[kMList];
+  __shared__ float s_cf[kMList];
+  __shared__ int s_tot[4];
+  uint4 (*s_at)[8] = reinterpret_cast<uint4 (*)[8]>(raw);
+  uint4 (*s_bh)[8] = reinterpret_cast<uint4 (*)[8]>(raw + 1024);
+  uint4 (*s_bl)[8] = reinterpret_cast<uint4 (*)[8]>(raw + 2048);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int gx = m.d_in / kQI;
+  const int nrect = gx * (m.d_out / kQN);
+  uint16_t *W = static_cast<uint16_t *>(m.W);
+  const bool one_list = m.m <= kMAd;
+  int total = 0;
+  if (one_list) {
+    total = merge_list(m, 0, 0, s_pid, s_cf, s_tot);
+    if (total == 0) return;                 // nothing valid listed: W stays as it is
+    if (total <= kQR) {
+      merge_stream(m, total, raw, s_pid, s_cf);
+      return;
+    }
+  }
+  const bool resident = one_list && total <= kMList;
+  // lane's W pieces: row n0 + 32 wave + (lane % 32), columns i0 + 32 b + 16 q + 8 (lane / 32)
+  auto wptr = [&](int rect) __attribute__((always_inline)) {
+    const int i0 = (rect % gx) * kQI, n0 = (rect / gx) * kQN;
+    return W + int64_t(n0 + wave * 32 + (lane & 31)) * m.d_in + i0 + 8 * (lane >> 5);
+  };
+  auto wload = [&](int rect, uint4 (&wv)[kQB][2]) __attribute__((always_inline)) {
+    const uint16_t *p = wptr(rect);
+#pragma unroll
+    for (int b = 0; b < kQB; ++b)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) wv[b][q] = *reinterpret_cast<const uint4 *>(p + 32 * b + 16 * q);
+  };
+  uint4 wv[kQB][2];
+  bool any = resident;
+  for (int rect = blockIdx.x; rect < nrect; rect += gridDim.x) {
+    const int i0 = (rect % gx) * kQI, n0 = (rect / gx) * kQN;
+    wload(rect, wv);
+    f32x16_t acc[kQB];
+#pragma unroll
+    for (int b = 0; b < kQB; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
+    if (resident) {
+      for (int j0 = 0; j0 < total; j0 += kQR) {
+        const int nl = min(kQR, total - j0);
+        __syncthreads();                    // the previous chunk's reads are done
+        qstage(m, i0, n0, j0, nl, s_pid, s_cf, s_at, s_bh, s_bl);
+        __syncthreads();
+        qmfma(nl, s_at, s_bh, s_bl, acc);
+      }
+    } else {
+      for (int e0 = 0; e0 < m.m; e0 += kMAd) {
+        const int tot = merge_list(m, e0, 0, s_pid, s_cf, s_tot);
+        for (int lb = 0; lb < tot; lb += kMList) {
+          if (lb > 0) merge_list(m, e0, lb, s_pid, s_cf, s_tot);
+          const int nlist = min(kMList, tot - lb);
+          for (int j0 = 0; j0 < nlist; j0 += kQR) {
+            const int nl = min(kQR, nlist - j0);
+            __syncthreads();
+            qstage(m, i0, n0, j0, nl, s_pid, s_cf, s_at, s_bh, s_bl);
+            __syncthreads();
+            qmfma(nl, s_at, s_bh, s_bl, acc);
+            any = true;
+          }
+        }
+      }
+    }
+    if (any) {
+      // lane value v of block b: column 32 b + 16 (v / 8) + 8 (lane / 32) + (v % 8)
+      uint16_t *p = wptr(rect);
+#pragma unroll
+      for (int b = 0; b < kQB; ++b)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const uint32_t w[4] = {wv[b][q].x, wv[b][q].y, wv[b][q].z, wv[b][q].w};
+          uint32_t o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float lo = bf_lo(w[e]) + acc[b][8 * q + 2 * e];
+            const float hi = bf_hi(w[e]) + acc[b][8 * q + 2 * e + 1];
+            o[e] = uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
+          }
+          *reinterpret_cast<uint4 *>(p + 32 * b + 16 * q) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_merge(const MergeArgs &a, int dtype, hipStream_t s) {
+  if (dtype == LORA_BF16 && a.d_in % kQI == 0 && a.d_out % kQN == 0) {
+    // at most 512 workgroups (two per CU, one round), a whole number per
+    // 128-column slice
+    const int gx = a.d_in / kQI, nrn = a.d_out / kSN;
+    int gps = 512 / gx;
+    gps = gps < 1 ? 1 : gps > nrn ? nrn : gps;
+    hipLaunchKernelGGL(merge_mfma_kernel, dim3(unsigned(gx * gps)), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   const int ntiles = (a.d_in / kMT) * (a.d_out / kMT);
   const dim3 grid(unsigned(ntiles < 1024 ? ntiles : 1024));
   if (dtype == LORA_BF16) hipLaunchKernelGGL(merge_kernel<uint16_t>, grid, dim3(256), 0, s, a);

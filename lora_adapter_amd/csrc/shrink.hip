@@ -30,6 +30,7 @@ namespace {
 
 constexpr int kTileTok = 16;        // tokens per MFMA tile
 constexpr int kTileRank = 16;       // rank rows per MFMA tile
+constexpr int kTileAhead = 8;       // K steps per batch of loads
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -46,21 +47,55 @@ __global__ __launch_bounds__(64) void shrink_units_kernel(ShrinkArgs s) {
   shrink_units_wave<E, kMask, kCh, kResident>(s, blockIdx.x);
 }
 
-// One workgroup per (segment of the plan's big list, 16 of its pairs).
+// Finds the big segment and the 16-pair tile of workgroup b, the tiles of the
+// big list numbered in list order (a wave-wide scan over 64 entries at a
+// time).  Returns false past the last tile.
+__device__ __forceinline__ bool tile_of(const PlanView &pv, int b, int lane, int &seg, int &q0, int &pe) {
+  const int nb = pv.big_list[0];
+  int base = 0;
+  for (int c0 = 0; c0 < nb; c0 += 64) {
+    const int i = c0 + lane;
+    int sg = 0, nt = 0, pb_ = 0, pe_ = 0;
+    if (i < nb) {
+      sg = pv.big_list[1 + i];
+      pb_ = pv.seg_desc[2 * sg].w;
+      pe_ = pv.seg_desc[2 * sg + 1].x;
+      nt = (pe_ - pb_ + kTileTok - 1) / kTileTok;
+    }
+    int incl = nt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    const uint64_t hit = __ballot(i < nb && base + incl > b);
+    if (hit) {
+      const int l = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+      seg = __shfl(sg, l, 64);
+      const int first = base + __shfl(incl - nt, l, 64);
+      q0 = __shfl(pb_, l, 64) + (b - first) * kTileTok;
+      pe = __shfl(pe_, l, 64);
+      return true;
+    }
+    base += __shfl(incl, 63, 64);
+  }
+  return false;
+}
+
+// One workgroup per 16-pair tile of the big segments, numbered across the
+// list so that consecutive workgroups (which the dispatcher spreads over the
+// XCDs) cover every segment evenly.
 template <bool kMask>
 __global__ __launch_bounds__(256) void shrink_tile_kernel(ShrinkArgs s) {
-  if (int(blockIdx.x) >= s.plan.big_list[0]) return;
   if (!capacity_ok(s)) return;
-  const int seg = s.plan.big_list[1 + blockIdx.x];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int seg = 0, q0 = 0, pe = 0;
+  if (!tile_of(s.plan, blockIdx.x, lane, seg, q0, pe)) return;
   const int4 d0 = s.plan.seg_desc[2 * seg];
-  const int4 d1 = s.plan.seg_desc[2 * seg + 1];
-  const int ad = d0.x, r = d0.y, ps = d0.z, pb = d0.w, pe = d1.x;
-  const int q0 = pb + blockIdx.y * kTileTok;
-  if (q0 >= pe) return;
+  const int ad = d0.x, r = d0.y, ps = d0.z;
   const int nq = min(kTileTok, pe - q0);
 
   __shared__ f32x4_t red[4][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int d = s.d;
   const int kw = d / 4;                          // this wave's part of d (multiple of 16)
   const int kbeg = wave * kw, kend = kbeg + kw;
@@ -74,29 +109,53 @@ __global__ __launch_bounds__(256) void shrink_tile_kernel(ShrinkArgs s) {
   const uint8_t *mrow = kMask ? s.mask + t * d : nullptr;
   const float sc = s.scale[ad] * s.extra_scale;
 
+  // K steps of 32 in batches of kTileAhead, the next batch's loads in flight
+  // while the current batch's MFMAs run (kw is a multiple of 32)
+  const int nsteps = kw / 32;
   for (int jb = 0; jb < r; jb += kTileRank) {
     // B operand: rank row jb + (lane % 16), same k offsets
     const int jr = jb + (lane & 15);
     const uint16_t *arow = pages + int64_t(s.page_ids[ps + min(jr, r - 1)]) * d;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int k = kbeg; k < kend; k += 32) {
-      uint4 xa = *reinterpret_cast<const uint4 *>(zrow + k + kofs);
-      const uint4 ab = *reinterpret_cast<const uint4 *>(arow + k + kofs);
-      if (kMask) {
-        const uint2 mb = *reinterpret_cast<const uint2 *>(mrow + k + kofs);
-        uint32_t w[4] = {xa.x, xa.y, xa.z, xa.w};
-        const uint32_t mw[2] = {mb.x, mb.y};
+    uint4 za[kTileAhead], pa[kTileAhead], zb[kTileAhead], pb2[kTileAhead];
+    uint2 ma[kTileAhead], mb[kTileAhead];
+    auto load_batch = [&](uint4 (&z)[kTileAhead], uint4 (&p)[kTileAhead], uint2 (&m)[kTileAhead], int i0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (((mw[e >> 2] >> (8 * (e & 3))) & 0xffu) == 0) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-        }
-        xa = make_uint4(w[0], w[1], w[2], w[3]);
+      for (int u = 0; u < kTileAhead; ++u) {
+        const int k = kbeg + min(i0 + u, nsteps - 1) * 32 + kofs;
+        z[u] = *reinterpret_cast<const uint4 *>(zrow + k);
+        p[u] = *reinterpret_cast<const uint4 *>(arow + k);
+        if (kMask) m[u] = *reinterpret_cast<const uint2 *>(mrow + k);
       }
-      bf16x8_t fa, fb;
-      __builtin_memcpy(&fa, &xa, 16);
-      __builtin_memcpy(&fb, &ab, 16);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc, 0, 0, 0);
+    };
+    auto mfma_batch = [&](const uint4 (&z)[kTileAhead], const uint4 (&p)[kTileAhead],
+                          const uint2 (&m)[kTileAhead], int i0) {
+#pragma unroll
+      for (int u = 0; u < kTileAhead; ++u) {
+        if (i0 + u >= nsteps) break;
+        uint4 xa = z[u];
+        if (kMask) {
+          uint32_t w[4] = {xa.x, xa.y, xa.z, xa.w};
+          const uint32_t mw[2] = {m[u].x, m[u].y};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            if (((mw[e >> 2] >> (8 * (e & 3))) & 0xffu) == 0) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+          }
+          xa = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+        bf16x8_t fa, fb;
+        __builtin_memcpy(&fa, &xa, 16);
+        __builtin_memcpy(&fb, &p[u], 16);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc, 0, 0, 0);
+      }
+    };
+    load_batch(za, pa, ma, 0);
+    for (int i0 = 0; i0 < nsteps; i0 += 2 * kTileAhead) {
+      load_batch(zb, pb2, mb, i0 + kTileAhead);
+      mfma_batch(za, pa, ma, i0);
+      if (i0 + kTileAhead >= nsteps) break;
+      load_batch(za, pa, ma, i0 + 2 * kTileAhead);
+      mfma_batch(zb, pb2, mb, i0 + kTileAhead);
     }
     red[wave][lane] = acc;
     __syncthreads();
@@ -167,7 +226,8 @@ hipError_t launch_shrink_big(const ShrinkArgs &a, int dtype, int64_t TK, int64_t
   // big segments: at most T*K / kBigSegPairs of them, each at most T*K pairs
   const int64_t segs = TK < n_adapters ? TK : n_adapters;
   const int64_t nbig = TK / kBigSegPairs < segs ? TK / kBigSegPairs : segs;
-  const dim3 g2{unsigned(nbig > 0 ? nbig : 1), unsigned((TK + kTileTok - 1) / kTileTok), 1}, b2{256, 1, 1};
+  // tiles: sum over big segments of ceil(len / 16) <= TK / 16 + nbig
+  const dim3 g2{unsigned((TK + kTileTok - 1) / kTileTok + (nbig > 0 ? nbig : 1)), 1, 1}, b2{256, 1, 1};
   if (s.mask) hipLaunchKernelGGL((shrink_tile_kernel<true>), g2, b2, 0, st, s);
   else hipLaunchKernelGGL((shrink_tile_kernel<false>), g2, b2, 0, st, s);
   return hipGetLastError();

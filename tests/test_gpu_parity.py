@@ -428,10 +428,49 @@ def test_merge_unmerge_and_switch(which):
     assert rel_err(D.as_f64(D.to_host(W3)), ref3) <= TOL[w.dtype]
 
 
-def test_merge_long_list_with_duplicates():
+def _merge_abs_delta(w, ids, co):
+    """sum_i |c_i s_i| . (|A_i| |B_i|)^T in float64: the scale of the float32
+    rounding the merged delta may carry."""
+    out = np.zeros((w.d_out, w.d_in))
+    for a, c in zip(ids.tolist(), co.tolist()):
+        if not (0 <= a < w.n_adapters) or int(w.rank[a]) == 0:
+            continue
+        A, Bf = O.factors(a, w.rank, w.page_start, w.page_ids, w.a_pages, w.b_pages)
+        out += abs(float(c) * float(w.scale[a])) * (np.abs(A) @ np.abs(Bf)).T
+    return out
+
+
+@pytest.mark.parametrize("which", ["small2", "small3", "small5", "full5"])
+def test_merge_elementwise_bound(which):
+    """Every merged element is the exact W + delta rounded once to bf16, up to
+    the float32 summation of the delta: |gpu - ref| <= ulp(ref)/2 (one
+    rounding) + 1e-5 sum|c s A B| (float32 products and sums)."""
+    w = {"small2": lambda: small(2), "small3": lambda: small(3), "small5": lambda: small(5),
+         "full5": lambda: full(5)}[which]()
+    if w.merge_ids is not None:
+        ids = np.asarray(w.merge_ids, np.int32)
+    else:
+        rng = np.random.default_rng(11)
+        ids = rng.integers(0, w.n_adapters, size=6).astype(np.int32)
+    co = np.where(np.arange(len(ids)) % 2 == 0, 1.0, -0.75).astype(np.float32)
+    L = D.DeviceLayer(w)
+    W = L.W_t.clone()
+    L.run_merge(W, ids, co)
+    torch.cuda.synchronize()
+    got = D.as_f64(D.to_host(W))
+    ref = O.merge_workload(w, ids=ids, coeffs=co)
+    bound = 0.5 * _ulp_bf16(np.abs(ref) * 1.01) + 1e-5 * _merge_abs_delta(w, ids, co) + 1e-30
+    bad = np.abs(got - ref) > bound
+    assert not bad.any(), (int(bad.sum()), np.argwhere(bad)[:4])
+
+
+@pytest.mark.parametrize("which", [3, 2])
+def test_merge_long_list_with_duplicates(which):
     """300 entries (two groups of list reads), repeated ids and signed
-    coefficients, more listed rank rows than one LDS list holds."""
-    w = small(3)
+    coefficients, more listed rank rows than one LDS list holds (workload 3:
+    d_out 1344, the float32-FMA kernel; workload 2: 512 x 768, the MFMA
+    kernel's chunked path)."""
+    w = small(which)
     rng = np.random.default_rng(3)
     ids = rng.integers(0, w.n_adapters, size=300).astype(np.int32)
     ids[::7] = ids[0]                                  # many repeats of one adapter
