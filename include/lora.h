@@ -208,13 +208,14 @@ int32_t lora_apply(const void *X, const void *W_t, void *Y, int32_t T, int32_t K
  * for the shapes whose base GEMM writes split-K partials (the GEMM does not
  * depend on the routing, so the plan is built beside other work):
  *   decode (T <= 128, bf16):
- *     lora_forward_gemm:   the GEMM's partials, and the shrink per slot (each
+ *     lora_forward_gemm:   the GEMM's partials, the shrink per slot (each
  *       active slot gathers its own adapter's A pages, which needs no plan:
  *       Punica-style gather for few tokens per adapter) into a per-slot part
- *       of the workspace, with a descriptor per slot;
+ *       of the workspace, with a descriptor per slot, and the plan, built by
+ *       the launch's first workgroup;
  *     lora_forward_finish: the epilogue (partials + expand from the per-slot
- *       U and descriptors, one rounding), and in the same launch the plan,
- *       whose workgroup also stores U in the u_off layout.
+ *       U and descriptors, one rounding), which also stores U in the plan's
+ *       u_off layout.
  *   stream-K shapes and float32:
  *     lora_forward_gemm:   the GEMM's partials with the plan built by one
  *       more workgroup of the launch;

@@ -321,15 +321,9 @@ PlanLaunch forward_plan(const int32_t *ids, const float *gates, int32_t T, int32
                         const lora_pool_desc *pool, void *plan, const Fwd &f, const ApplyWs &w) {
   PlanLaunch pl = plan_setup(ids, gates, T, K, pool_view(pool), static_cast<int32_t *>(plan), 256,
                              plan_lds_cap(f.cfg));
-  if (w.slot_u) {
-    // decode: the per-slot shrink has run; the plan stores its U in the u_off
-    // layout and skips the decode-shrink wave records
-    pl.a.slot_u = w.slot_u;
-    pl.a.u_out = w.U;
-    pl.a.u_cap = w.u_cap;
-    pl.a.slot_stride = LORA_MAX_RANK;
-    pl.a.no_sched = 1;
-  }
+  // decode: the per-slot shrink runs beside the plan, whose U the epilogue
+  // later moves to the u_off layout; the decode-shrink wave records are skipped
+  if (w.slot_u) pl.a.no_sched = 1;
   return pl;
 }
 
@@ -355,7 +349,8 @@ int32_t lora_forward_gemm(const int32_t *ids, const float *gates, int32_t T, int
     ss.rank = pool->rank; ss.page_start = pool->page_start; ss.page_ids = pool->page_ids;
     ss.scale = pool->scale; ss.n_pages = pool->n_pages; ss.n_page_ids = pool->n_page_ids;
     ss.out = w.slot_u; ss.stride = LORA_MAX_RANK; ss.n_slots = T * K; ss.sdesc = w.sdesc;
-    return dev(launch_decode_slot(f.cfg, f.g, ss, s));
+    return dev(launch_decode_slot_plan(f.cfg, f.g, ss,
+                                       forward_plan(ids, gates, T, K, pool, plan, f, w), s));
   }
   return dev(launch_gemm_plan(f.cfg, f.g, forward_plan(ids, gates, T, K, pool, plan, f, w), s));
 }
@@ -373,8 +368,7 @@ int32_t lora_forward_finish(const int32_t *ids, const float *gates, int32_t T, i
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const ApplyWs w = apply_layout(ws, ws_bytes, T, K, pool->d_in, pool->d_out, pool->dtype);
   if (w.slot_u)
-    return dev(launch_epilogue_plan(f.cfg, f.g, pool->dtype, w.slot_u, w.sdesc,
-                                    forward_plan(ids, gates, T, K, pool, plan, f, w), s));
+    return dev(launch_epilogue_ucopy(f.cfg, f.g, pool->dtype, w.slot_u, w.sdesc, w.U, w.u_cap, s));
   st = lora_shrink(X, keep_mask, keep_scale, T, K, gates, pool, plan, ws, ws_bytes, stream);
   if (st != LORA_OK) return st;
   return lora_expand_epilogue(X, W_t, Y, T, K, pool, plan, ws, ws_bytes, stream);

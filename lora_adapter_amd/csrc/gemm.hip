@@ -330,16 +330,23 @@ __global__ __launch_bounds__(256, 2) void decode_gemm_shrink_kernel(GemmArgs g, 
 // after them.  The shrink's few dependent loads go out first, ahead of the
 // W stream; neither part reads what the other writes, and neither needs
 // the plan.
-template <int MB, bool kMask>
+template <int MB, bool kMask, bool kLds>
 __global__ __launch_bounds__(256) void decode_gemm_slot_kernel(GemmArgs g, SlotShrinkArgs ss,
-                                                                int gx, int gy, int n_gemm) {
+                                                                PlanArgs pa, int gx, int gy,
+                                                                int n_gemm) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[MB * 32 * kDecodeKC];
-  const int b = blockIdx.x;
-  if (b < ss.n_slots) {
-    slot_shrink_wg<kMask>(ss, b);
+  const int b = int(blockIdx.x);
+  if (b == 0) {
+    // the plan, in the LDS the GEMM tiles use for token rows; dispatched
+    // first, so its one global round trip goes out ahead of the W stream
+    plan_build<kLds>(pa, reinterpret_cast<int *>(xs));
     return;
   }
-  const int t = b - ss.n_slots;
+  if (b - 1 < ss.n_slots) {
+    slot_shrink_wg<kMask>(ss, b - 1);
+    return;
+  }
+  const int t = b - 1 - ss.n_slots;
   decode_tile<MB>(g, t % gx, (t / gx) % gy, t / (gx * gy), xs);
 }
 
@@ -837,11 +844,13 @@ template <int BM, int BN, int WM, int WN, int NS, bool kLds>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_tile_plan_kernel(GemmArgs g, PlanArgs pa) {
   using C = TileCfg<BM, BN, WM, WN>;
   __shared__ __attribute__((aligned(16))) char smem[NS * C::STAGE];
-  if (int(blockIdx.x) == g.sk_g) {
+  // block 0 builds the plan (dispatched first, its loads go out ahead of
+  // the W stream); blocks 1..G are the stream-K workgroups
+  if (blockIdx.x == 0) {
     plan_build<kLds>(pa, reinterpret_cast<int *>(smem));
     return;
   }
-  stream_k<BM, BN, WM, WN, NS>(g, smem, blockIdx.x);
+  stream_k<BM, BN, WM, WN, NS>(g, smem, int(blockIdx.x) - 1);
 }
 
 // ------------------------------------------------------------ fp32 GEMM
@@ -928,17 +937,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float *X, const flo
 // output row; its first workgroup builds the plan (1: arrays in LDS, 2: in
 // the plan buffer) while the others add the expand from the per-slot U and
 // descriptors, which need no plan.
-template <typename E, int kPlan, int NW>
-__global__ __launch_bounds__(NW * 64) void epilogue_kernel(EpilogueArgs a, PlanArgs pa) {
-  if constexpr (kPlan != 0) {
-    if (int(blockIdx.y) == int(gridDim.y) - 1) {
-      if (blockIdx.x == 0) {
-        extern __shared__ int edyn[];
-        plan_build<kPlan == 1>(pa, edyn);
-      }
-      return;
-    }
-  }
+template <typename E, int NW>
+__global__ __launch_bounds__(NW * 64) void epilogue_kernel(EpilogueArgs a) {
   constexpr int CPL = 8;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int row, cx;
@@ -960,6 +960,24 @@ __global__ __launch_bounds__(NW * 64) void epilogue_kernel(EpilogueArgs a, PlanA
     row = blockIdx.y * NW + wave;
     cx = blockIdx.x;
     if (row >= a.M) return;
+  }
+  // decode: the first column chunk of each row also moves the row's per-slot
+  // U to the plan's u_off places; its loads go out now (up to 4 slots, the
+  // first 64 rank rows of each) so that their round trips overlap the rest
+  constexpr int kCpK = 4;
+  const bool do_copy = a.u_out != nullptr && cx == 0;
+  int4 cpd[kCpK];
+  float cpv[kCpK];
+  int64_t rpairs = 0;
+  if (do_copy) {
+    rpairs = a.plan_hdr[LORA_PH_RPAIRS];
+#pragma unroll
+    for (int k = 0; k < kCpK; ++k) {
+      const int kk = min(k, a.ex.K - 1);
+      const int64_t i = int64_t(row) * a.ex.K + kk;
+      cpd[k] = a.plan_sdesc[i];
+      cpv[k] = a.ex.U[i * a.slot_stride + lane];     // rank rows < 64 <= LORA_MAX_RANK
+    }
   }
   const int col_raw = (cx * 64 + lane) * CPL;
   const bool col_ok = col_raw < a.N;
@@ -1005,6 +1023,29 @@ __global__ __launch_bounds__(NW * 64) void epilogue_kernel(EpilogueArgs a, PlanA
   }
   if (lora_on) expand_row8<E>(v, sd, col, a.ex);
   if (col_ok) Cols<E, CPL>::store(static_cast<E *>(a.Y) + int64_t(row) * a.N + col, v);
+  if (do_copy) {
+    // this row's per-slot U to the places the plan gave its active slots
+    if (rpairs > a.u_cap) {
+      if (row == 0 && lane == 0) atomicOr(a.plan_hdr + LORA_PH_ERR, LORA_DEVERR_CAPACITY);
+      return;
+    }
+    for (int k = 0; k < a.ex.K; ++k) {
+      const int64_t i = int64_t(row) * a.ex.K + k;
+      int4 d;
+      float v0;
+      if (k < kCpK) {
+        d = k == 0 ? cpd[0] : k == 1 ? cpd[1] : k == 2 ? cpd[2] : cpd[3];
+        v0 = k == 0 ? cpv[0] : k == 1 ? cpv[1] : k == 2 ? cpv[2] : cpv[3];
+      } else {
+        d = a.plan_sdesc[i];
+        v0 = a.ex.U[i * a.slot_stride + lane];
+      }
+      if (d.x < 0) continue;
+      if (lane < d.y) a.u_out[d.z + lane] = v0;
+      const float *src = a.ex.U + i * a.slot_stride;
+      for (int j = lane + 64; j < d.y; j += 64) a.u_out[d.z + j] = src[j];
+    }
+  }
 }
 
 }  // namespace
@@ -1130,11 +1171,12 @@ bool gemm_plan_fusable(const GemmConfig &c) {
   return c.kind == 0 || c.kind == 4 || (c.kind == 6 && c.sk > 0);
 }
 
-// Decode: the plan workgroup's LDS is the epilogue launch's dynamic LDS, which
-// every epilogue workgroup then gets too: kept to 64 KiB.  Stream-K: the
-// tile kernel's stages.
+// Decode: the plan workgroup uses the decode tile's token-row LDS (bm rows
+// of kDecodeKC bf16).  fp32: the launch's dynamic LDS, kept to 64 KiB.
+// Stream-K: the tile kernel's stages.
 size_t plan_lds_cap(const GemmConfig &c) {
-  if (c.kind == 4 || c.kind == 0) return size_t(64) << 10;
+  if (c.kind == 4) return size_t(c.bm) * kDecodeKC * sizeof(uint16_t);
+  if (c.kind == 0) return size_t(64) << 10;
   return size_t(3) * TileCfg<256, 128, 2, 2>::STAGE;
 }
 
@@ -1160,40 +1202,41 @@ hipError_t launch_gemm_plan(const GemmConfig &c, const GemmArgs &g, const PlanLa
   return hipGetLastError();
 }
 
-hipError_t launch_decode_slot(const GemmConfig &c, const GemmArgs &g, const SlotShrinkArgs &ss,
-                              hipStream_t s) {
-  if (c.kind != 4) return hipErrorInvalidConfiguration;
+hipError_t launch_decode_slot_plan(const GemmConfig &c, const GemmArgs &g,
+                                   const SlotShrinkArgs &ss, const PlanLaunch &pl, hipStream_t s) {
+  if (c.kind != 4 || pl.lds_bytes > plan_lds_cap(c)) return hipErrorInvalidConfiguration;
   const int gx = (g.N + 127) / 128, gy = (g.M + c.bm - 1) / c.bm;
   const int n_gemm = gx * gy * c.splits;
-  const dim3 grid(unsigned(n_gemm + ss.n_slots)), block(256);
+  const dim3 grid(unsigned(1 + ss.n_slots + n_gemm)), block(256);
   const bool m = ss.mask != nullptr;
-#define LORA_DGS2(MB, M) \
-  hipLaunchKernelGGL((decode_gemm_slot_kernel<MB, M>), grid, block, 0, s, g, ss, gx, gy, n_gemm)
+#define LORA_DGS3(MB, M, L) \
+  hipLaunchKernelGGL((decode_gemm_slot_kernel<MB, M, L>), grid, block, 0, s, g, ss, pl.a, gx, gy, n_gemm)
+#define LORA_DGS2(MB, M) do { if (pl.lds) LORA_DGS3(MB, M, true); else LORA_DGS3(MB, M, false); } while (0)
 #define LORA_DGS(MB) do { if (m) LORA_DGS2(MB, true); else LORA_DGS2(MB, false); } while (0)
   if (c.bm == 32) LORA_DGS(1);
   else if (c.bm == 64) LORA_DGS(2);
   else LORA_DGS(4);
 #undef LORA_DGS
 #undef LORA_DGS2
+#undef LORA_DGS3
   return hipGetLastError();
 }
 
-hipError_t launch_epilogue_plan(const GemmConfig &c, const GemmArgs &g, int dtype,
-                                const float *slot_u, const int4 *sdesc, const PlanLaunch &pl,
-                                hipStream_t s) {
-  if (c.fused || pl.lds_bytes > plan_lds_cap(c)) return hipErrorInvalidConfiguration;
+hipError_t launch_epilogue_ucopy(const GemmConfig &c, const GemmArgs &g, int dtype,
+                                 const float *slot_u, const int4 *sdesc, float *u_out,
+                                 int64_t u_cap, hipStream_t s) {
+  if (c.fused || c.kind != 4) return hipErrorInvalidConfiguration;
   EpilogueArgs e{g.partial, c.splits, g.M, g.N, c.sk, g.Kd / 64, c.bm, c.bn, g.Y, g.ex, sdesc,
                  nullptr, 0, 0};
   e.ex.U = slot_u;
-  const dim3 grid((g.N + 511) / 512, (g.M + 3) / 4 + 1);
-  const size_t lds = pl.lds_bytes;
-#define LORA_EP(E) do { \
-    if (pl.lds) hipLaunchKernelGGL((epilogue_kernel<E, 1, 4>), grid, dim3(256), lds, s, e, pl.a); \
-    else hipLaunchKernelGGL((epilogue_kernel<E, 2, 4>), grid, dim3(256), lds, s, e, pl.a); \
-  } while (0)
-  if (dtype == LORA_BF16) LORA_EP(uint16_t);
-  else LORA_EP(float);
-#undef LORA_EP
+  e.plan_sdesc = g.ex.slot_desc;                 // the plan's slot descriptors and header
+  e.plan_hdr = const_cast<int32_t *>(g.ex.hdr);
+  e.u_out = u_out;
+  e.u_cap = u_cap;
+  e.slot_stride = LORA_MAX_RANK;
+  const dim3 grid((g.N + 511) / 512, (g.M + 3) / 4);
+  if (dtype == LORA_BF16) hipLaunchKernelGGL((epilogue_kernel<uint16_t, 4>), grid, dim3(256), 0, s, e);
+  else hipLaunchKernelGGL((epilogue_kernel<float, 4>), grid, dim3(256), 0, s, e);
   return hipGetLastError();
 }
 
@@ -1201,7 +1244,6 @@ hipError_t launch_epilogue(const GemmConfig &c, const GemmArgs &g, int dtype, hi
   if (c.fused) return hipSuccess;
   EpilogueArgs e{g.partial, c.splits, g.M, g.N, c.sk, g.Kd / 64, c.bm, c.bn, g.Y, g.ex, nullptr,
                  nullptr, 0, 0};
-  const PlanArgs none{};
   if (dtype == LORA_BF16 && c.kind == 6 && g.ex.K == 1 && g.ex.pair_tk) {
     // one slot per token: rows in pair order, 8 per workgroup (see EpilogueArgs)
     const int n_x = (g.N + 511) / 512;
@@ -1209,12 +1251,12 @@ hipError_t launch_epilogue(const GemmConfig &c, const GemmArgs &g, int dtype, hi
     e.n_x = n_x;
     e.n_a = ((g.M + 7) / 8) * n_x;
     const dim3 grid(unsigned(2 * e.n_a));
-    hipLaunchKernelGGL((epilogue_kernel<uint16_t, 0, 8>), grid, dim3(512), 0, s, e, none);
+    hipLaunchKernelGGL((epilogue_kernel<uint16_t, 8>), grid, dim3(512), 0, s, e);
     return hipGetLastError();
   }
   const dim3 grid((g.N + 511) / 512, (g.M + 3) / 4);
-  if (dtype == LORA_BF16) hipLaunchKernelGGL((epilogue_kernel<uint16_t, 0, 4>), grid, dim3(256), 0, s, e, none);
-  else hipLaunchKernelGGL((epilogue_kernel<float, 0, 4>), grid, dim3(256), 0, s, e, none);
+  if (dtype == LORA_BF16) hipLaunchKernelGGL((epilogue_kernel<uint16_t, 4>), grid, dim3(256), 0, s, e);
+  else hipLaunchKernelGGL((epilogue_kernel<float, 4>), grid, dim3(256), 0, s, e);
   return hipGetLastError();
 }
 

@@ -266,6 +266,15 @@ struct EpilogueArgs {
   // without an active slot in token order)
   const int32_t *pair_tk;
   int n_x, n_a;
+  // not null (decode, with sdesc): the plan built by the previous launch;
+  // the first column chunk of each row copies the row's per-slot U (ex.U,
+  // rows of slot_stride floats) to the plan's u_off places, when the plan's
+  // R_pairs fits u_cap (else LORA_DEVERR_CAPACITY in plan_hdr's error word)
+  const int4 *plan_sdesc;
+  int32_t *plan_hdr;
+  float *u_out;
+  int64_t u_cap;
+  int slot_stride;
 };
 
 struct MergeArgs {
@@ -360,22 +369,23 @@ bool decode_shrink_fusable(const GemmConfig &c, int d_in);
 // launched separately by the caller).
 hipError_t launch_decode_gemm_shrink(const GemmConfig &c, const GemmArgs &g, const ShrinkArgs &sa,
                                      hipStream_t s);
-// lora_forward's launches for split GEMMs.  Decode (kind 4): the GEMM's
-// partials and the per-slot shrink (ss) in one launch (launch_decode_slot),
-// then the epilogue from the slot descriptors with the plan built by one
-// more workgroup of that launch (launch_epilogue_plan).  Stream-K (kind 6)
-// and fp32 (kind 0): the GEMM's partials with the plan built by one more
-// workgroup (launch_gemm_plan).  The plan workgroup has 256 threads and the
-// LDS that plan_lds_cap(c) gives.
+// lora_forward's launches for split GEMMs.  Decode (kind 4): the plan
+// (built by the launch's first workgroup, in the token-row LDS), the per-slot
+// shrink (ss) and the GEMM's partials in one launch (launch_decode_slot_plan),
+// then the epilogue from the slot descriptors, which also moves the per-slot
+// U to the plan's layout (launch_epilogue_ucopy).  Stream-K (kind 6) and fp32
+// (kind 0): the GEMM's partials with the plan built by one more workgroup
+// (launch_gemm_plan).  The plan workgroup has 256 threads and the LDS that
+// plan_lds_cap(c) gives.
 bool gemm_plan_fusable(const GemmConfig &c);
 size_t plan_lds_cap(const GemmConfig &c);
 hipError_t launch_gemm_plan(const GemmConfig &c, const GemmArgs &g, const PlanLaunch &pl,
                             hipStream_t s);
-hipError_t launch_decode_slot(const GemmConfig &c, const GemmArgs &g, const SlotShrinkArgs &ss,
-                              hipStream_t s);
-hipError_t launch_epilogue_plan(const GemmConfig &c, const GemmArgs &g, int dtype,
-                                const float *slot_u, const int4 *sdesc, const PlanLaunch &pl,
-                                hipStream_t s);
+hipError_t launch_decode_slot_plan(const GemmConfig &c, const GemmArgs &g,
+                                   const SlotShrinkArgs &ss, const PlanLaunch &pl, hipStream_t s);
+hipError_t launch_epilogue_ucopy(const GemmConfig &c, const GemmArgs &g, int dtype,
+                                 const float *slot_u, const int4 *sdesc, float *u_out,
+                                 int64_t u_cap, hipStream_t s);
 // The MFMA shrink of the big segments alone (no-op unless enabled).
 hipError_t launch_shrink_big(const ShrinkArgs &a, int dtype, int64_t TK, int64_t n_adapters,
                              int d_in, int d_out, hipStream_t s);
