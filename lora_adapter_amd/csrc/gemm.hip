@@ -945,9 +945,16 @@ __global__ __launch_bounds__(NW * 64) void epilogue_kernel(EpilogueArgs a) {
   if (a.pair_tk) {
     const int i = blockIdx.x;
     if (i < a.n_a) {
-      const int q = (i / a.n_x) * NW + wave;
+      // pair groups from the last: the plan orders segments by ascending rank
+      // bucket, so the longest rows are dispatched first and short ones fill
+      // the tail
+      const int np = a.ex.hdr[LORA_PH_PAIRS];
+      const int ng = (np + NW - 1) / NW;
+      const int gi = i / a.n_x;
+      if (gi >= ng) return;
+      const int q = (ng - 1 - gi) * NW + wave;
       cx = i % a.n_x;
-      if (q >= a.ex.hdr[LORA_PH_PAIRS]) return;
+      if (q >= np) return;
       row = a.pair_tk[q];                               // one slot per token
     } else {
       const int j = i - a.n_a;
