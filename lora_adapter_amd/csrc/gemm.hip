@@ -638,6 +638,16 @@ __device__ __forceinline__ void tile_mfma(const char *As,
   }
 }
 
+// Workgroup barrier for LDS only.  The stage copies are LDS DMA issued from
+// inline asm, so every wave first waits (wait_vmcnt) for its own copies of a
+// stage and then meets the others here; no global load in flight is waited
+// for (__syncthreads() waits for all of them).
+__device__ __forceinline__ void lds_bar() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Wait until at most n (0 <= n <= NS - 2) K tiles' copies are still in flight.
 template <int LPW, int NS>
 __device__ __forceinline__ void wait_tiles(int n) {
@@ -728,25 +738,25 @@ __device__ __forceinline__ void tile_run(const GemmArgs &g, char *smem, int m0, 
     for (; kt + 1 < nk; kt += 2) {
       // even tile from stage 0 while the odd tile's loads stay in flight
       wait_vmcnt<C::LPW>();
-      __syncthreads();
+      lds_bar();
       tile_mfma<BM, BN, WM, WN>(st0, acc);
-      __syncthreads();
+      lds_bar();
       if (kt + 2 < nk) {
         issue(st0, kt + 2);
         wait_vmcnt<C::LPW>();     // the odd tile (issued before this one) has landed
       } else {
         wait_vmcnt<0>();
       }
-      __syncthreads();
+      lds_bar();
       tile_mfma<BM, BN, WM, WN>(st1, acc);
-      __syncthreads();
+      lds_bar();
       if (kt + 3 < nk) issue(st1, kt + 3);
     }
     if (kt < nk) {               // odd number of K tiles: the last one is in stage 0
       wait_vmcnt<0>();
-      __syncthreads();
+      lds_bar();
       tile_mfma<BM, BN, WM, WN>(st0, acc);
-      __syncthreads();
+      lds_bar();
     }
   } else {
 #pragma unroll
@@ -758,7 +768,7 @@ __device__ __forceinline__ void tile_run(const GemmArgs &g, char *smem, int m0, 
         const int kt = kt0 + u;
         if (kt < nk) {
           wait_tiles<C::LPW, NS>(min(NS - 2, nk - 1 - kt));
-          __syncthreads();
+          lds_bar();
           char *const nxt = smem + ((u + NS - 1) % NS) * C::STAGE;
           const bool more = kt + NS - 1 < nk;
           tile_mfma<BM, BN, WM, WN>(smem + u * C::STAGE, acc, [&](int q) {
