@@ -412,7 +412,12 @@ size_t lora_grad_workspace_bytes(int32_t T, int32_t K, int32_t n_adapters, int32
   const size_t pieces = size_t(grad_pieces(TK, n_adapters));
   const size_t pa = align_up(pieces * size_t(max_rank) * size_t(d_in) * sizeof(float));
   const size_t pb = align_up(pieces * size_t(max_rank) * size_t(d_out) * sizeof(float));
-  return g + pa + pb;
+  // MFMA form: the per-tile dY.B^T partials
+  const size_t gp = grad_mfma_form(dtype, TK, d_out)
+                        ? align_up(size_t(grad_gpart_tiles(d_out)) * size_t(TK) * size_t(max_rank) *
+                                   sizeof(float))
+                        : 0;
+  return g + pa + pb + gp;
 }
 
 int32_t lora_grad(const void *X, const uint8_t *keep_mask, float keep_scale, const void *dY,
@@ -445,6 +450,34 @@ int32_t lora_grad(const void *X, const uint8_t *keep_mask, float keep_scale, con
   float *G = reinterpret_cast<float *>(base);
   float *partA = reinterpret_cast<float *>(base + g_bytes);
   float *partB = reinterpret_cast<float *>(base + g_bytes + pa);
+  const size_t pbytes = align_up(pieces * size_t(max_rank) * size_t(pool->d_out) * sizeof(float));
+  const bool fused_g = grad_mfma_form(pool->dtype, TK, pool->d_out);
+  float *gpart = fused_g ? reinterpret_cast<float *>(base + g_bytes + pa + pbytes) : nullptr;
+
+  if (fused_g) {
+    // prefill-size bf16 batches: dB and the per-tile dY.B^T partials in one
+    // pass over dY, then G from the partials, then dA
+    SegOuterArgs ob{};
+    ob.Z = dY; ob.mask = nullptr; ob.T = T; ob.K = K; ob.d = pool->d_out;
+    ob.coef = aw.U; ob.coef_cap = aw.u_cap; ob.plan = pv;
+    ob.rank = pool->rank; ob.page_start = pool->page_start; ob.page_ids = pool->page_ids;
+    ob.part = partB; ob.max_rank = max_rank; ob.out_pages = dB_pages; ob.err_word = err_word;
+    ob.gpart = gpart; ob.b_pages = pool->b_pages;
+    hipError_t e = launch_seg_outer(ob, pool->dtype, TK, pool->n_adapters, s);
+    if (e != hipSuccess) return LORA_ERR_DEVICE;
+    GReduceArgs gr{};
+    gr.gpart = gpart; gr.n_tiles = grad_gpart_tiles(pool->d_out); gr.TK = TK;
+    gr.max_rank = max_rank; gr.plan = pv; gr.rank = pool->rank; gr.scale = pool->scale;
+    gr.extra_scale = keep_mask ? keep_scale : 1.0f;
+    gr.G = G; gr.g_cap = int64_t(TK) * max_rank;
+    e = launch_g_reduce(gr, s);
+    if (e != hipSuccess) return LORA_ERR_DEVICE;
+    SegOuterArgs oa = ob;
+    oa.Z = X; oa.mask = keep_mask; oa.d = pool->d_in; oa.coef = G; oa.coef_cap = gr.g_cap;
+    oa.part = partA; oa.out_pages = dA_pages;
+    oa.gpart = nullptr; oa.b_pages = nullptr;
+    return dev(launch_seg_outer(oa, pool->dtype, TK, pool->n_adapters, s));
+  }
 
   // G = kappa . g . s . (dY . B_j): the shrink kernel on (dY, B pages)
   ShrinkArgs sa{};

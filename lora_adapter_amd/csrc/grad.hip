@@ -275,6 +275,21 @@ __global__ __launch_bounds__(256) void seg_outer_mfma_kernel(SegOuterArgs a) {
       f32x4_t acc[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      // dY.B^T partials (dB pass): B operand = rank row j0 + lane % 16 of the
+      // segment's adapter, 8 columns at 32 ks + 8 (lane / 16) of this tile
+      uint4 gb[8];
+      const bool with_g = a.gpart != nullptr;
+      if (with_g) {
+        const int jr = lane & 15;
+        const uint16_t *Bp = static_cast<const uint16_t *>(a.b_pages);
+        const uint16_t *brow =
+            Bp + int64_t(a.page_ids[a.page_start[ad] + j0 + min(jr, nr - 1)]) * a.d + c0 + 8 * (lane >> 4);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          gb[ks] = *reinterpret_cast<const uint4 *>(brow + 32 * ks);
+          if (jr >= nr) gb[ks] = make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
       fetch(l_beg);
       for (int k0 = l_beg; k0 < l_end; k0 += kOuterK) {
         __syncthreads();                       // the previous step is done with s_z
@@ -312,6 +327,29 @@ __global__ __launch_bounds__(256) void seg_outer_mfma_kernel(SegOuterArgs a) {
           __builtin_memcpy(&bfrag, &pb, 16);
           acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bfrag, acc[b], 0, 0, 0);
           acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bfrag, acc[b], 0, 0, 0);
+        }
+        if (with_g && wave < 2) {
+          // waves 0 and 1: pairs k0 + 16 * wave .. + 15 of the step (rows of
+          // s_z) times the B rows, over the tile's 256 columns in 8 K steps
+          f32x4_t ga = {0.f, 0.f, 0.f, 0.f};
+          const int zrow = 16 * wave + (lane & 15);
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks) {
+            bf16x8_t fa, fb;
+            __builtin_memcpy(&fa, &s_z[zrow][32 * ks + 8 * (lane >> 4)], 16);
+            __builtin_memcpy(&fb, &gb[ks], 16);
+            ga = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, ga, 0, 0, 0);
+          }
+          // lane holds rank column (lane % 16) and pair rows 4 * (lane / 16) + i
+          const int jj = lane & 15;
+          if (jj < nr) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int l = k0 + 16 * wave + (lane >> 4) * 4 + i;
+              if (l < l_end)
+                a.gpart[(int64_t(blockIdx.x) * a.T * a.K + pbeg + l) * a.max_rank + j0 + jj] = ga[i];
+            }
+          }
         }
       }
       // lane holds column (lane % 16) of each block and rank rows 4 * (lane / 16) + i
@@ -361,7 +399,38 @@ __global__ __launch_bounds__(kGradThreads) void seg_outer_reduce_kernel(SegOuter
   }
 }
 
+// G[u_off[p] + j] = (gate . scale . extra) . sum over tiles of gpart, one
+// thread per (pair, rank row), tiles added in order.
+__global__ __launch_bounds__(256) void g_reduce_kernel(GReduceArgs a) {
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int P = a.plan.hdr[LORA_PH_PAIRS];
+  const int64_t p = idx / a.max_rank;
+  const int j = int(idx % a.max_rank);
+  if (p >= P) return;
+  if (int64_t(a.plan.hdr[LORA_PH_RPAIRS]) > a.g_cap) return;
+  const int adp = a.plan.pair_adapter[p];
+  const int r = a.rank[adp];
+  if (j >= r || r > a.max_rank) return;
+  float sum = 0.f;
+  for (int x = 0; x < a.n_tiles; ++x) sum += a.gpart[(int64_t(x) * a.TK + p) * a.max_rank + j];
+  const float sc = a.scale[adp] * a.extra_scale;
+  a.G[a.plan.u_off[p] + j] = a.plan.pair_gate[p] * sc * sum;
+}
+
 }  // namespace
+
+bool grad_mfma_form(int dtype, int64_t TK, int d_out) {
+  return dtype == LORA_BF16 && TK >= 2048 && d_out % kOuterCols == 0;
+}
+
+int grad_gpart_tiles(int d_out) { return d_out / kOuterCols; }
+
+hipError_t launch_g_reduce(const GReduceArgs &a, hipStream_t st) {
+  const int64_t n = a.TK * a.max_rank;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(g_reduce_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
 
 int64_t grad_pieces(int64_t TK, int64_t N) {
   const int64_t segs = TK < N ? TK : N;
@@ -374,7 +443,7 @@ hipError_t launch_seg_outer(const SegOuterArgs &a, int dtype, int64_t TK, int64_
   const unsigned chunks = unsigned((TK + kGradPairChunk - 1) / kGradPairChunk);
   const unsigned rchunks = unsigned((a.max_rank + kGradRankChunk - 1) / kGradRankChunk);
   const dim3 g1(cols, chunks, rchunks), block(kGradThreads);
-  if (dtype == LORA_BF16 && TK >= 2048 && a.d % kOuterCols == 0) {
+  if (grad_mfma_form(dtype, TK, a.d)) {
     // prefill-size batches: the MFMA form (long segments make it dense)
     const dim3 gm(unsigned(a.d / kOuterCols), chunks, rchunks);
     if (a.mask) hipLaunchKernelGGL((seg_outer_mfma_kernel<true>), gm, block, 0, st, a);

@@ -304,6 +304,26 @@ struct SegOuterArgs {
   int max_rank;
   float *out_pages;         // [n_pages][d]
   int32_t *err_word;
+  // not null (dB pass of the MFMA form): also the partial dY.B^T of every
+  // pair over each 256-column tile, gpart[tile][pair][max_rank], from the
+  // staged dY rows and the B pages (b_pages)
+  float *gpart;
+  const void *b_pages;
+};
+
+// G from gpart: G[u_off[p] + j] = (gate_p . scale_a . extra_scale) .
+// sum over the column tiles (in tile order) of gpart[tile][p][j].
+struct GReduceArgs {
+  const float *gpart;
+  int n_tiles;
+  int64_t TK;
+  int max_rank;
+  PlanView plan;
+  const int32_t *rank;
+  const float *scale;
+  float extra_scale;
+  float *G;
+  int64_t g_cap;
 };
 
 // Arguments of the plan workgroup (plan_build).
@@ -392,6 +412,10 @@ hipError_t launch_shrink_big(const ShrinkArgs &a, int dtype, int64_t TK, int64_t
 
 hipError_t launch_merge(const MergeArgs &a, int dtype, hipStream_t s);
 int64_t grad_pieces(int64_t TK, int64_t n_adapters);
+// The MFMA outer-product form (and the fused dY.B^T partials) applies.
+bool grad_mfma_form(int dtype, int64_t TK, int d_out);
+int grad_gpart_tiles(int d_out);
+hipError_t launch_g_reduce(const GReduceArgs &a, hipStream_t s);
 hipError_t launch_seg_outer(const SegOuterArgs &a, int dtype, int64_t TK, int64_t n_adapters,
                             hipStream_t s);
 
