@@ -979,22 +979,17 @@ __global__ __launch_bounds__(NW * 64) void epilogue_kernel(EpilogueArgs a) {
     if (row >= a.M) return;
   }
   // decode: the first column chunk of each row also moves the row's per-slot
-  // U to the plan's u_off places; its loads go out now (up to 4 slots, the
-  // first 64 rank rows of each) so that their round trips overlap the rest
-  constexpr int kCpK = 4;
+  // U to the plan's u_off places; the loads for its first slot (first 64 rank
+  // rows) go out now so that their round trips overlap the rest
   const bool do_copy = a.u_out != nullptr && cx == 0;
-  int4 cpd[kCpK];
-  float cpv[kCpK];
+  int4 cpd0 = make_int4(-1, 0, 0, 0);
+  float cpv0 = 0.f;
   int64_t rpairs = 0;
   if (do_copy) {
     rpairs = a.plan_hdr[LORA_PH_RPAIRS];
-#pragma unroll
-    for (int k = 0; k < kCpK; ++k) {
-      const int kk = min(k, a.ex.K - 1);
-      const int64_t i = int64_t(row) * a.ex.K + kk;
-      cpd[k] = a.plan_sdesc[i];
-      cpv[k] = a.ex.U[i * a.slot_stride + lane];     // rank rows < 64 <= LORA_MAX_RANK
-    }
+    const int64_t i = int64_t(row) * a.ex.K;
+    cpd0 = a.plan_sdesc[i];
+    cpv0 = a.ex.U[i * a.slot_stride + lane];          // rank rows < 64 <= LORA_MAX_RANK
   }
   const int col_raw = (cx * 64 + lane) * CPL;
   const bool col_ok = col_raw < a.N;
@@ -1048,12 +1043,9 @@ __global__ __launch_bounds__(NW * 64) void epilogue_kernel(EpilogueArgs a) {
     }
     for (int k = 0; k < a.ex.K; ++k) {
       const int64_t i = int64_t(row) * a.ex.K + k;
-      int4 d;
-      float v0;
-      if (k < kCpK) {
-        d = k == 0 ? cpd[0] : k == 1 ? cpd[1] : k == 2 ? cpd[2] : cpd[3];
-        v0 = k == 0 ? cpv[0] : k == 1 ? cpv[1] : k == 2 ? cpv[2] : cpv[3];
-      } else {
+      int4 d = cpd0;
+      float v0 = cpv0;
+      if (k > 0) {
         d = a.plan_sdesc[i];
         v0 = a.ex.U[i * a.slot_stride + lane];
       }
