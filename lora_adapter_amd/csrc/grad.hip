@@ -411,8 +411,18 @@ __global__ __launch_bounds__(256) void g_reduce_kernel(GReduceArgs a) {
   const int adp = a.plan.pair_adapter[p];
   const int r = a.rank[adp];
   if (j >= r || r > a.max_rank) return;
+  // tiles in order, 8 loads in flight
   float sum = 0.f;
-  for (int x = 0; x < a.n_tiles; ++x) sum += a.gpart[(int64_t(x) * a.TK + p) * a.max_rank + j];
+  const int64_t stride = a.TK * a.max_rank;
+  const float *src = a.gpart + p * a.max_rank + j;
+  for (int x0 = 0; x0 < a.n_tiles; x0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = src[int64_t(min(x0 + u, a.n_tiles - 1)) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (x0 + u < a.n_tiles) sum += v[u];
+  }
   const float sc = a.scale[adp] * a.extra_scale;
   a.G[a.plan.u_off[p] + j] = a.plan.pair_gate[p] * sc * sum;
 }
