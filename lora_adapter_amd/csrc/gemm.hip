@@ -731,33 +731,88 @@ __device__ __forceinline__ void tile_run(const GemmArgs &g, char *smem, int m0, 
   // tile kt + NS - 1 is issued into the stage step kt - 1 used, so NS - 1
   // tiles' copies are in flight while tile kt feeds the MFMAs.
   if constexpr (NS == 2) {
-    // two stages, the loop unrolled by two so each stage has a fixed address
-    if (nk > 0) issue(st0, 0);
-    if (nk > 1) issue(st1, 1);
-    int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-      // even tile from stage 0 while the odd tile's loads stay in flight
-      wait_vmcnt<C::LPW>();
-      lds_bar();
-      tile_mfma<BM, BN, WM, WN>(st0, acc);
-      lds_bar();
-      if (kt + 2 < nk) {
-        issue(st0, kt + 2);
-        wait_vmcnt<C::LPW>();     // the odd tile (issued before this one) has landed
-      } else {
-        wait_vmcnt<0>();
+    // Two stages, pipelined at fragment level.  The fragments of K step
+    // s + 1 are read from LDS while the MFMAs of step s run (two register
+    // sets: fa0/fb0 for even steps, fa1/fb1 for odd ones).  Before the last
+    // step of K tile kt one barrier both frees the stage just read (the
+    // copies of tile kt + 2 go into it, one after each MFMA of that step)
+    // and publishes tile kt + 1, whose first fragments are read at once; so
+    // the MFMA pipe is never left waiting on a fragment read.  Each step's
+    // instructions are pinned in this order (sched_barrier): left alone, the
+    // compiler keeps one register set and reads a step's fragments only
+    // after the previous step's MFMAs have issued.
+    bf16x8_t fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+    // fragment q (A blocks 0 .. TM-1, then B blocks) of K step s
+    auto frag = [&](const char *base, int s, int q) __attribute__((always_inline)) {
+      const int row = q < TM ? wm * TM * 32 + q * 32 + frow : BM + wn * TN * 32 + (q - TM) * 32 + frow;
+      return *reinterpret_cast<const bf16x8_t *>(base + row * C::ROWB + (((2 * s + half) ^ (frow & 7)) << 4));
+    };
+    // copy i of the wave's A-then-B list for K tile kt into stage base
+    auto dma_one = [&](char *base, int kt, int i) __attribute__((always_inline)) {
+      const uint32_t lds = lds_addr(base);
+      if (i < C::A_INS) lds_dma16(abase + kt * 64 + aoff[i], lds + (wave * C::A_INS + i) * 1024);
+      else lds_dma16(bbase + kt * 64 + boff[i - C::A_INS], lds + BM * C::ROWB + (wave * C::B_INS + i - C::A_INS) * 1024);
+    };
+    // One K step: MFMA m on block (m / TN, m % TN) from (xa, xb), each
+    // followed by its share of the next step's fragment reads from src (into
+    // ya, yb; mode bit 0) and of the copies of K tile kn into dst (bit 1).
+    auto kstep = [&](auto mode, bf16x8_t (&xa)[TM], bf16x8_t (&xb)[TN], bf16x8_t (&ya)[TM],
+                     bf16x8_t (&yb)[TN], const char *src, int s_next, char *dst,
+                     int kn) __attribute__((always_inline)) {
+      constexpr int MD = decltype(mode)::value;
+      constexpr int NM = TM * TN, NQ = TM + TN;
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        acc[m / TN][m % TN] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[m / TN], xb[m % TN], acc[m / TN][m % TN], 0, 0, 0);
+        if constexpr ((MD & 1) != 0) {
+#pragma unroll
+          for (int q = m * NQ / NM; q < (m + 1) * NQ / NM; ++q) {
+            if (q < TM) ya[q] = frag(src, s_next, q);
+            else yb[q - TM] = frag(src, s_next, q);
+          }
+        }
+        if constexpr ((MD & 2) != 0) {
+#pragma unroll
+          for (int c = m * C::LPW / NM; c < (m + 1) * C::LPW / NM; ++c) dma_one(dst, kn, c);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      lds_bar();
-      tile_mfma<BM, BN, WM, WN>(st1, acc);
-      lds_bar();
-      if (kt + 3 < nk) issue(st1, kt + 3);
-    }
-    if (kt < nk) {               // odd number of K tiles: the last one is in stage 0
+    };
+    if (nk > 0) issue(st0, 0);
+    if (nk > 1) {
+      issue(st1, 1);
+      wait_vmcnt<C::LPW>();
+    } else {
       wait_vmcnt<0>();
-      lds_bar();
-      tile_mfma<BM, BN, WM, WN>(st0, acc);
-      lds_bar();
     }
+    lds_bar();
+    if (nk > 0) {
+#pragma unroll
+      for (int q = 0; q < TM + TN; ++q) {
+        if (q < TM) fa0[q] = frag(st0, 0, q);
+        else fb0[q - TM] = frag(st0, 0, q);
+      }
+    }
+    // K tile kt from stage cur, its step-0 fragments in fa0/fb0 on entry.
+    // The last step reads the first fragments of tile kt + 1 from nxt and
+    // copies tile kt + 2 into cur.  Past the end the body stays the same
+    // (no branch inside the loop): the copy repeats the last tile into a
+    // stage no one reads again, and the reads of nxt go unused.
+    for (int kt = 0; kt < nk; ++kt) {
+      char *const cur = (kt & 1) ? st1 : st0;
+      char *const nxt = (kt & 1) ? st0 : st1;
+      kstep(std::integral_constant<int, 1>{}, fa0, fb0, fa1, fb1, cur, 1, cur, 0);
+      kstep(std::integral_constant<int, 1>{}, fa1, fb1, fa0, fb0, cur, 2, cur, 0);
+      kstep(std::integral_constant<int, 1>{}, fa0, fb0, fa1, fb1, cur, 3, cur, 0);
+      wait_vmcnt<0>();   // tile kt + 1, the only copies in flight, has landed
+      lds_bar();         // for every wave, and every wave has read cur
+      kstep(std::integral_constant<int, 3>{}, fa1, fb1, fa0, fb0, nxt, 0, cur, min(kt + 2, nk - 1));
+    }
+    // the copies of the last step have landed and every wave is done with
+    // the stages before anything else uses this LDS
+    wait_vmcnt<0>();
+    lds_bar();
   } else {
 #pragma unroll
     for (int i = 0; i < NS - 1; ++i)
