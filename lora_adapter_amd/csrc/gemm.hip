@@ -223,8 +223,8 @@ __device__ __forceinline__ void decode_tile(const GemmArgs &g, int bx, int by, i
   constexpr int NG = KC / 64;                 // 64-wide K groups
   constexpr int BMr = MB * 32;
   // One token row of the K chunk = 64 slots of 16 bytes.  Row r keeps chunk c
-  // in slot c ^ (r & 7): the 8 rows a fragment read touches at once hit 8
-  // different 16-byte bank groups.
+  // in slot c ^ (r & 15): the 16 rows that one quarter of a wave's fragment
+  // read touches at once (same chunk) cover the 64 banks exactly once.
   const uint16_t *X = static_cast<const uint16_t *>(g.X);
   const uint16_t *W = static_cast<const uint16_t *>(g.W);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -253,7 +253,7 @@ __device__ __forceinline__ void decode_tile(const GemmArgs &g, int bx, int by, i
   for (int i = 0; i < BMr / 4; ++i) {
     const int r = wave + 4 * i;
     const int row = min(m0 + r, g.M - 1);
-    const int chunk = lane ^ (r & 7);
+    const int chunk = lane ^ (r & 15);
     const int col = min(chunk * 8, ng * 64 - 8);
     __builtin_amdgcn_global_load_lds(X + int64_t(row) * g.Kd + k0 + col,
                                      (__attribute__((address_space(3))) void *)(xs + r * KC), 16, 0, 0);
@@ -280,7 +280,7 @@ __device__ __forceinline__ void decode_tile(const GemmArgs &g, int bx, int by, i
           const int r = b * 32 + (lane & 31);
           const int chunk = (gq * 64 + half * 32 + s * 8) / 8;
           const bf16x8_t afrag =
-              *reinterpret_cast<const bf16x8_t *>(xs + r * KC + ((chunk ^ (r & 7)) * 8));
+              *reinterpret_cast<const bf16x8_t *>(xs + r * KC + ((chunk ^ (r & 15)) * 8));
           acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag, bfrag, acc[b], 0, 0, 0);
         }
       }
@@ -357,12 +357,18 @@ __global__ __launch_bounds__(256) void decode_gemm_slot_kernel(GemmArgs g, SlotS
 //     staging): one instruction moves 8 tile rows of 128 bytes.  Two LDS
 //     stages; the loads of K tile kt+1 are in flight while tile kt feeds the
 //     MFMAs, and explicit vmcnt waits release each stage.
-//   * In LDS a tile row keeps 16-byte chunk c in slot c ^ (row & 7), so the
-//     8 rows a fragment read touches at once fall in 8 distinct bank groups.
+//   * In LDS a tile row (128 bytes) keeps 16-byte chunk c in slot
+//     tswz(row, c) = c ^ (row & 7) ^ ((row >> 3) & 1): the 16 rows that one
+//     quarter of a wave's fragment read touches at once (same chunk) cover
+//     the 64 banks exactly once.  With c ^ (row & 7) alone, rows r and r + 8
+//     collide, and every fragment read took two passes.
 //   * Tiles are ordered so that the workgroups the hardware places on one XCD
 //     (workgroup ids equal mod 8) take consecutive tiles, walked 4 tile rows at
 //     a time: concurrently running tiles on an XCD share X rows and W columns
 //     through that XCD's L2.
+// LDS slot of 16-byte chunk c (0..7) in tile row `row`.
+__device__ __forceinline__ int tswz(int row, int c) { return c ^ (row & 7) ^ ((row >> 3) & 1); }
+
 template <int BM, int BN, int WM, int WN>
 struct TileCfg {
   static constexpr int NW = WM * WN, NT = NW * 64;
@@ -623,12 +629,12 @@ __device__ __forceinline__ void tile_mfma(const char *As,
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int row = wm * TM * 32 + i * 32 + frow;
-      af[i] = *reinterpret_cast<const bf16x8_t *>(As + row * C::ROWB + (((2 * s + half) ^ (row & 7)) << 4));
+      af[i] = *reinterpret_cast<const bf16x8_t *>(As + row * C::ROWB + (tswz(row, 2 * s + half) << 4));
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int row = wn * TN * 32 + j * 32 + frow;
-      bf[j] = *reinterpret_cast<const bf16x8_t *>(Bs + row * C::ROWB + (((2 * s + half) ^ (row & 7)) << 4));
+      bf[j] = *reinterpret_cast<const bf16x8_t *>(Bs + row * C::ROWB + (tswz(row, 2 * s + half) << 4));
     }
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -677,19 +683,18 @@ __device__ __forceinline__ void tile_run(const GemmArgs &g, char *smem, int m0, 
   // per-lane source rows, as 32-bit element offsets from the tile's first row
   // (clamped: rows past M / N feed outputs that are never stored)
   const int lrow = lane >> 3;
-  const int lchunk = (lane & 7) ^ lrow;
   const uint16_t *abase = X + int64_t(m0) * g.Kd + k_begin;
   const uint16_t *bbase = W + int64_t(n0) * g.Kd + k_begin;
   uint32_t aoff[C::A_INS], boff[C::B_INS];
 #pragma unroll
   for (int i = 0; i < C::A_INS; ++i) {
     const int row = (wave * C::A_INS + i) * 8 + lrow;
-    aoff[i] = uint32_t(min(row, g.M - 1 - m0)) * uint32_t(g.Kd) + lchunk * 8;
+    aoff[i] = uint32_t(min(row, g.M - 1 - m0)) * uint32_t(g.Kd) + tswz(row, lane & 7) * 8;
   }
 #pragma unroll
   for (int i = 0; i < C::B_INS; ++i) {
     const int row = (wave * C::B_INS + i) * 8 + lrow;
-    boff[i] = uint32_t(min(row, g.N - 1 - n0)) * uint32_t(g.Kd) + lchunk * 8;
+    boff[i] = uint32_t(min(row, g.N - 1 - n0)) * uint32_t(g.Kd) + tswz(row, lane & 7) * 8;
   }
   auto issue = [&](char *base, int kt) {
     const uint16_t *a = abase + kt * 64;
@@ -745,7 +750,7 @@ __device__ __forceinline__ void tile_run(const GemmArgs &g, char *smem, int m0, 
     // fragment q (A blocks 0 .. TM-1, then B blocks) of K step s
     auto frag = [&](const char *base, int s, int q) __attribute__((always_inline)) {
       const int row = q < TM ? wm * TM * 32 + q * 32 + frow : BM + wn * TN * 32 + (q - TM) * 32 + frow;
-      return *reinterpret_cast<const bf16x8_t *>(base + row * C::ROWB + (((2 * s + half) ^ (frow & 7)) << 4));
+      return *reinterpret_cast<const bf16x8_t *>(base + row * C::ROWB + (tswz(frow, 2 * s + half) << 4));
     };
     // copy i of the wave's A-then-B list for K tile kt into stage base
     auto dma_one = [&](char *base, int kt, int i) __attribute__((always_inline)) {
