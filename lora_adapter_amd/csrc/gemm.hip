@@ -57,6 +57,17 @@ template <> struct Cols<uint16_t, 8> {
     *reinterpret_cast<uint4 *>(p) = w;
   }
 };
+// 8 bf16 values, one 16-byte streaming store (Y is written once and not
+// read back by the layer)
+__device__ __forceinline__ void store8_nt(uint16_t *p, const float v[8]) {
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+  u32x4_t w;
+  w.x = uint32_t(f2bf(v[0])) | (uint32_t(f2bf(v[1])) << 16);
+  w.y = uint32_t(f2bf(v[2])) | (uint32_t(f2bf(v[3])) << 16);
+  w.z = uint32_t(f2bf(v[4])) | (uint32_t(f2bf(v[5])) << 16);
+  w.w = uint32_t(f2bf(v[6])) | (uint32_t(f2bf(v[7])) << 16);
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t *>(p));
+}
 template <> struct Cols<float, 8> {
   static __device__ __forceinline__ void load(const float *p, float v[8]) { Elem<float>::load8(p, v); }
   static __device__ __forceinline__ void store(float *p, const float v[8]) {
@@ -558,7 +569,9 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs &g,
         }
       }
     }
-    __syncthreads();
+    // the staging region is this wave's own, and the K loop ended with a
+    // workgroup barrier: no barrier here (LDS accesses of one wave stay in
+    // order)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -566,7 +579,6 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs &g,
         const int r = (v >> 2) * 8 + half * 4 + (v & 3);
         stage[r * SC + j * 32 + frow] = acc[0][j][v];
       }
-    __syncthreads();
     const int rbase = m0 + wm * TM * 32 + i * 32;
     if (!(rowwise & 1u)) {
 #pragma unroll
@@ -577,7 +589,7 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs &g,
           const float4 lo = *reinterpret_cast<const float4 *>(stage + rr * SC + vc);
           const float4 hi = *reinterpret_cast<const float4 *>(stage + rr * SC + vc + 4);
           const float v8[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-          Cols<uint16_t, 8>::store(Y + int64_t(row) * g.N + cbase + vc, v8);
+          store8_nt(Y + int64_t(row) * g.N + cbase + vc, v8);
         }
       }
     } else {
