@@ -211,6 +211,44 @@ __device__ __forceinline__ bool expand_enabled(const ExpandArgs &e) {
   return e.U != nullptr && int64_t(e.hdr[LORA_PH_RPAIRS]) <= e.u_cap;
 }
 
+// ------------------------------------------------------------ LDS copies and waits
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (const __attribute__((address_space(3))) char *)(p)));
+}
+
+// global_load_lds_dwordx4: each of the 64 lanes copies 16 bytes from its
+// global address to LDS at lds + 16 * lane.  Issued from inline asm so that
+// the compiler does not put a blanket vmcnt(0) in front of every later LDS
+// read (it cannot tell which LDS stage an in-flight copy writes); the
+// instruction has no register result, and the kernel waits for these copies
+// itself (wait_vmcnt) before the barrier that precedes reading the stage.
+__device__ __forceinline__ void lds_dma16(const void *gptr, uint32_t lds) {
+  const uint32_t lds_s = __builtin_amdgcn_readfirstlane(lds);   // wave-uniform LDS base
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(lds_s)
+               : "memory", "m0");
+}
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt bits 3:0 and 15:14).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier for LDS only.  The stage copies are LDS DMA issued from
+// inline asm, so every wave first waits (wait_vmcnt) for its own copies of a
+// stage and then meets the others here; no global load in flight is waited
+// for (__syncthreads() waits for all of them).
+__device__ __forceinline__ void lds_bar() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ------------------------------------------------------------ decode GEMM
 // Few tokens (M <= 128): the product is a stream of W (d_in x d_out bf16)
 // through HBM, and every W byte is used by one wave only.  A workgroup owns
@@ -248,7 +286,19 @@ __device__ __forceinline__ void decode_tile(const GemmArgs &g, int bx, int by, i
   // All loads are unconditional, from clamped addresses, so none waits on a
   // branch: rows past M and columns past N only feed outputs that are never
   // stored, and K groups past the end are skipped by the MFMA loop.
-  // The W stream (HBM) is issued first, then the token rows (mostly L2).
+  // The token rows (mostly L2) go first, straight into LDS: wave w copies
+  // rows w, w+4, ...; lane l of a copy fills slot l of the row.  The copies
+  // are issued from inline asm, so the compiler does not hold every LDS read
+  // until all loads have landed; the W stream (HBM) follows, and the MFMAs
+  // of each 64-wide K group start as soon as its W fragments are in.
+#pragma unroll
+  for (int i = 0; i < BMr / 4; ++i) {
+    const int r = wave + 4 * i;
+    const int row = min(m0 + r, g.M - 1);
+    const int chunk = lane ^ (r & 15);
+    const int col = min(chunk * 8, ng * 64 - 8);
+    lds_dma16(X + int64_t(row) * g.Kd + k0 + col, lds_addr(xs + r * KC));
+  }
   // W fragments: row n0 + lane%32, k0 + 64*grp + 32*half + [0, 32)
   uint4 wf[NG][4];
   const uint16_t *wrow = W + int64_t(min(n0 + (lane & 31), g.N - 1)) * g.Kd + k0 + half * 32;
@@ -258,22 +308,8 @@ __device__ __forceinline__ void decode_tile(const GemmArgs &g, int bx, int by, i
     for (int q = 0; q < 4; ++q)
       wf[gq][q] = *reinterpret_cast<const uint4 *>(wrow + min(gq, ng - 1) * 64 + q * 8);
   __builtin_amdgcn_sched_barrier(0);
-  // Token rows straight into LDS (no registers): wave w loads rows w, w+4,
-  // ...; lane l of the instruction fills slot l of the row.
-#pragma unroll
-  for (int i = 0; i < BMr / 4; ++i) {
-    const int r = wave + 4 * i;
-    const int row = min(m0 + r, g.M - 1);
-    const int chunk = lane ^ (r & 15);
-    const int col = min(chunk * 8, ng * 64 - 8);
-    __builtin_amdgcn_global_load_lds(X + int64_t(row) * g.Kd + k0 + col,
-                                     (__attribute__((address_space(3))) void *)(xs + r * KC), 16, 0, 0);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  // the token rows were issued last: all loads have landed
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-  __syncthreads();
-
+  wait_vmcnt<NG * 4>();   // this wave's token rows have landed (its W loads came after them)
+  lds_bar();              // and every wave's
   f32x16_t acc[MB];
 #pragma unroll
   for (int b = 0; b < MB; ++b)
@@ -391,33 +427,6 @@ struct TileCfg {
   static_assert(A_INS * 8 * NW == BM && B_INS * 8 * NW == BN, "tile rows / waves");
   static_assert(LPW < 64, "vmcnt field holds at most 63");
 };
-
-// LDS byte address of a __shared__ object.
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (const __attribute__((address_space(3))) char *)(p)));
-}
-
-// global_load_lds_dwordx4: each of the 64 lanes copies 16 bytes from its
-// global address to LDS at lds + 16 * lane.  Issued from inline asm so that
-// the compiler does not put a blanket vmcnt(0) in front of every later LDS
-// read (it cannot tell which LDS stage an in-flight copy writes); the
-// instruction has no register result, and the kernel waits for these copies
-// itself (wait_vmcnt) before the barrier that precedes reading the stage.
-__device__ __forceinline__ void lds_dma16(const void *gptr, uint32_t lds) {
-  const uint32_t lds_s = __builtin_amdgcn_readfirstlane(lds);   // wave-uniform LDS base
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(gptr), "s"(lds_s)
-               : "memory", "m0");
-}
-
-// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt bits 3:0 and 15:14).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
 
 __device__ __forceinline__ void tile_coords(int T, int tiles_m, int tiles_n, int &tm, int &tn) {
   constexpr int G = 4;
@@ -656,15 +665,6 @@ __device__ __forceinline__ void tile_mfma(const char *As,
   }
 }
 
-// Workgroup barrier for LDS only.  The stage copies are LDS DMA issued from
-// inline asm, so every wave first waits (wait_vmcnt) for its own copies of a
-// stage and then meets the others here; no global load in flight is waited
-// for (__syncthreads() waits for all of them).
-__device__ __forceinline__ void lds_bar() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // Wait until at most n (0 <= n <= NS - 2) K tiles' copies are still in flight.
 template <int LPW, int NS>
