@@ -86,11 +86,11 @@ __device__ __forceinline__ bool tile_of(const PlanView &pv, int b, int lane, int
 // list so that consecutive workgroups (which the dispatcher spreads over the
 // XCDs) cover every segment evenly.
 template <bool kMask>
-__global__ __launch_bounds__(256) void shrink_tile_kernel(ShrinkArgs s) {
+__device__ __forceinline__ void shrink_tile_wg(const ShrinkArgs &s, const int b) {
   if (!capacity_ok(s)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int seg = 0, q0 = 0, pe = 0;
-  if (!tile_of(s.plan, blockIdx.x, lane, seg, q0, pe)) return;
+  if (!tile_of(s.plan, b, lane, seg, q0, pe)) return;
   const int4 d0 = s.plan.seg_desc[2 * seg];
   const int ad = d0.x, r = d0.y, ps = d0.z;
   const int nq = min(kTileTok, pe - q0);
@@ -184,6 +184,33 @@ __global__ __launch_bounds__(256) void shrink_tile_kernel(ShrinkArgs s) {
   }
 }
 
+template <bool kMask>
+__global__ __launch_bounds__(256) void shrink_tile_kernel(ShrinkArgs s) {
+  shrink_tile_wg<kMask>(s, blockIdx.x);
+}
+
+// Both shrinks in one launch (bf16 batches with big segments): workgroups
+// 0 .. n_tile-1 run the tile kernel's tiles, the others the units
+// schedule, one schedule wave per wave.  The two write disjoint pairs.
+template <bool kMask, int kCh>
+__global__ __launch_bounds__(256) void shrink_both_kernel(ShrinkArgs s, int n_tile) {
+  const int b = int(blockIdx.x);
+  if (b < n_tile) {
+    shrink_tile_wg<kMask>(s, b);
+    return;
+  }
+  shrink_units_wave<uint16_t, kMask, kCh, true>(s, (b - n_tile) * 4 + int(threadIdx.x >> 6));
+}
+
+// Workgroups of the tile shrink: big segments number at most T*K /
+// kBigSegPairs (and at most the number of segments), each at most T*K
+// pairs; their 16-pair tiles sum to at most TK / 16 + nbig.
+int shrink_tile_wgs(int64_t TK, int64_t n_adapters) {
+  const int64_t segs = TK < n_adapters ? TK : n_adapters;
+  const int64_t nbig = TK / kBigSegPairs < segs ? TK / kBigSegPairs : segs;
+  return int((TK + kTileTok - 1) / kTileTok + (nbig > 0 ? nbig : 1));
+}
+
 }  // namespace
 
 hipError_t launch_shrink(const ShrinkArgs &a, int dtype, int64_t TK, int64_t n_adapters,
@@ -192,6 +219,20 @@ hipError_t launch_shrink(const ShrinkArgs &a, int dtype, int64_t TK, int64_t n_a
   if (segs <= 0) return hipSuccess;
   ShrinkArgs s = a;
   s.big_segments = shrink_tile_enabled(dtype, TK, d_in, d_out) ? 1 : 0;
+  if (s.big_segments && s.d <= 12 * 512) {
+    // one launch for both (the units part resident: d fits its chunks)
+    static_assert(kShrinkWaves % 4 == 0, "four schedule waves per workgroup");
+    const int n_tile = shrink_tile_wgs(TK, n_adapters);
+    const dim3 g2{unsigned(n_tile + kShrinkWaves / 4), 1, 1}, b2{256, 1, 1};
+    if (s.d <= 8 * 512) {
+      if (s.mask) hipLaunchKernelGGL((shrink_both_kernel<true, 8>), g2, b2, 0, st, s, n_tile);
+      else hipLaunchKernelGGL((shrink_both_kernel<false, 8>), g2, b2, 0, st, s, n_tile);
+    } else {
+      if (s.mask) hipLaunchKernelGGL((shrink_both_kernel<true, 12>), g2, b2, 0, st, s, n_tile);
+      else hipLaunchKernelGGL((shrink_both_kernel<false, 12>), g2, b2, 0, st, s, n_tile);
+    }
+    return hipGetLastError();
+  }
   const dim3 grid{unsigned(kShrinkWaves), 1, 1}, block{64, 1, 1};
 #define LORA_SHRINK_UNITS(E, M, CH, RES) \
   hipLaunchKernelGGL((shrink_units_kernel<E, M, CH, RES>), grid, block, 0, st, s)
@@ -223,11 +264,7 @@ hipError_t launch_shrink_big(const ShrinkArgs &a, int dtype, int64_t TK, int64_t
   if (!shrink_tile_enabled(dtype, TK, d_in, d_out)) return hipSuccess;
   ShrinkArgs s = a;
   s.big_segments = 1;
-  // big segments: at most T*K / kBigSegPairs of them, each at most T*K pairs
-  const int64_t segs = TK < n_adapters ? TK : n_adapters;
-  const int64_t nbig = TK / kBigSegPairs < segs ? TK / kBigSegPairs : segs;
-  // tiles: sum over big segments of ceil(len / 16) <= TK / 16 + nbig
-  const dim3 g2{unsigned((TK + kTileTok - 1) / kTileTok + (nbig > 0 ? nbig : 1)), 1, 1}, b2{256, 1, 1};
+  const dim3 g2{unsigned(shrink_tile_wgs(TK, n_adapters)), 1, 1}, b2{256, 1, 1};
   if (s.mask) hipLaunchKernelGGL((shrink_tile_kernel<true>), g2, b2, 0, st, s);
   else hipLaunchKernelGGL((shrink_tile_kernel<false>), g2, b2, 0, st, s);
   return hipGetLastError();
