@@ -642,29 +642,45 @@ __device__ __forceinline__ void tile_mfma(const char *As,
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int frow = lane & 31, half = lane >> 5;
-  const char *Bs = As + BM * C::ROWB;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  // Fragments are pipelined inside the tile: the LDS reads of K step s + 1
+  // go out under the MFMAs of step s (two register sets), each step's
+  // instructions pinned in this order (sched_barrier).
+  bf16x8_t fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+  // fragment q (A blocks 0 .. TM-1, then B blocks) of K step s
+  auto frag = [&](int s, int q) __attribute__((always_inline)) {
+    const int row = q < TM ? wm * TM * 32 + q * 32 + frow : BM + wn * TN * 32 + (q - TM) * 32 + frow;
+    return *reinterpret_cast<const bf16x8_t *>(As + row * C::ROWB + (tswz(frow, 2 * s + half) << 4));
+  };
+  auto kstep = [&](auto nxt, int s, bf16x8_t (&xa)[TM], bf16x8_t (&xb)[TN], bf16x8_t (&ya)[TM],
+                   bf16x8_t (&yb)[TN]) __attribute__((always_inline)) {
+    constexpr bool kNext = decltype(nxt)::value;
+    constexpr int NM = TM * TN, NF = TM + TN;
     pre_step(s);
-    bf16x8_t af[TM], bf[TN];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int row = wm * TM * 32 + i * 32 + frow;
-      af[i] = *reinterpret_cast<const bf16x8_t *>(As + row * C::ROWB + (tswz(row, 2 * s + half) << 4));
+    for (int m = 0; m < NM; ++m) {
+      acc[m / TN][m % TN] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[m / TN], xb[m % TN], acc[m / TN][m % TN], 0, 0, 0);
+      if constexpr (kNext) {
+#pragma unroll
+        for (int q = m * NF / NM; q < (m + 1) * NF / NM; ++q) {
+          if (q < TM) ya[q] = frag(s + 1, q);
+          else yb[q - TM] = frag(s + 1, q);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int row = wn * TN * 32 + j * 32 + frow;
-      bf[j] = *reinterpret_cast<const bf16x8_t *>(Bs + row * C::ROWB + (tswz(row, 2 * s + half) << 4));
-    }
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+  for (int q = 0; q < TM + TN; ++q) {
+    if (q < TM) fa0[q] = frag(0, q);
+    else fb0[q - TM] = frag(0, q);
   }
+  kstep(std::true_type{}, 0, fa0, fb0, fa1, fb1);
+  kstep(std::true_type{}, 1, fa1, fb1, fa0, fb0);
+  kstep(std::true_type{}, 2, fa0, fb0, fa1, fb1);
+  kstep(std::false_type{}, 3, fa1, fb1, fa0, fb0);
 }
-
 
 // Wait until at most n (0 <= n <= NS - 2) K tiles' copies are still in flight.
 template <int LPW, int NS>
