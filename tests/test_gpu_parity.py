@@ -180,6 +180,28 @@ def test_apply_fused_epilogue_path():
     assert err <= TOL["bf16"], err
 
 
+SHORT_K_CASES = {
+    # 256x256 fused tiles with 1, 2 and 3 K tiles of 64 (prologue, loop and
+    # the copies clamped past the end)
+    "fused_k64": lambda: wl.config(4, T=2100, d_in=64, d_out=8192, seed=71),
+    "fused_k128": lambda: wl.config(4, T=2100, d_in=128, d_out=8192, seed=72),
+    "fused_k192": lambda: wl.config(4, T=2100, d_in=192, d_out=8192, seed=73),
+    # stream-K 256x128 pieces of one to a few K tiles
+    "streamk_k2048": lambda: wl.config(3, T=300, d_in=2048, d_out=2048, n_adapters=64, seed=74),
+    # decode tile whose last K chunk holds one 64-wide group
+    "decode_k576": lambda: wl.config(2, T=64, d_in=576, d_out=640, seed=75),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SHORT_K_CASES))
+def test_apply_short_k(case):
+    w = SHORT_K_CASES[case]()
+    L = run(w)
+    assert L.read_plan()["header"][B.PH_ERR] == 0
+    err = rel_err(D.as_f64(L.Y_host()), O.apply_workload(w))
+    assert err <= TOL[w.dtype], err
+
+
 def test_apply_mixed_ranks_above_bucket_edges():
     rng = np.random.default_rng(5)
     N, T, K = 9, 130, 2
