@@ -373,10 +373,10 @@ __global__ __launch_bounds__(256, 2) void decode_gemm_shrink_kernel(GemmArgs g, 
     shrink_units_wave<uint16_t, kMask, kCh, true>(s, w);
 }
 
-// The per-slot shrink in workgroups 0 .. n_slots-1 and the decode GEMM tiles
-// after them.  The shrink's few dependent loads go out first, ahead of the
-// W stream; neither part reads what the other writes, and neither needs
-// the plan.
+// Workgroup 0 builds the plan, workgroups 1 .. 4 n_slots run the per-slot
+// shrink (four per slot), the decode GEMM tiles follow.  The shrink's few
+// dependent loads go out first, ahead of the W stream; no part reads what
+// another writes, and neither the shrink nor the GEMM needs the plan.
 template <int MB, bool kMask, bool kLds>
 __global__ __launch_bounds__(256) void decode_gemm_slot_kernel(GemmArgs g, SlotShrinkArgs ss,
                                                                 PlanArgs pa, int gx, int gy,
@@ -389,11 +389,11 @@ __global__ __launch_bounds__(256) void decode_gemm_slot_kernel(GemmArgs g, SlotS
     plan_build<kLds>(pa, reinterpret_cast<int *>(xs));
     return;
   }
-  if (b - 1 < ss.n_slots) {
-    slot_shrink_wg<kMask>(ss, b - 1);
+  if (b - 1 < kSlotParts * ss.n_slots) {
+    slot_shrink_part<kMask>(ss, (b - 1) / kSlotParts, (b - 1) % kSlotParts);
     return;
   }
-  const int t = b - 1 - ss.n_slots;
+  const int t = b - 1 - kSlotParts * ss.n_slots;
   decode_tile<MB>(g, t % gx, (t / gx) % gy, t / (gx * gy), xs);
 }
 
@@ -1304,7 +1304,7 @@ hipError_t launch_decode_slot_plan(const GemmConfig &c, const GemmArgs &g,
   if (c.kind != 4 || pl.lds_bytes > plan_lds_cap(c)) return hipErrorInvalidConfiguration;
   const int gx = (g.N + 127) / 128, gy = (g.M + c.bm - 1) / c.bm;
   const int n_gemm = gx * gy * c.splits;
-  const dim3 grid(unsigned(1 + ss.n_slots + n_gemm)), block(256);
+  const dim3 grid(unsigned(1 + kSlotParts * ss.n_slots + n_gemm)), block(256);
   const bool m = ss.mask != nullptr;
 #define LORA_DGS3(MB, M, L) \
   hipLaunchKernelGGL((decode_gemm_slot_kernel<MB, M, L>), grid, block, 0, s, g, ss, pl.a, gx, gy, n_gemm)

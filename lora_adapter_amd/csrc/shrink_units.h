@@ -293,22 +293,25 @@ __device__ __forceinline__ void shrink_units_wave(const ShrinkArgs &s, const int
   }
 }
 
-// Per-slot decode shrink: one workgroup (4 waves) per slot i = t*K + k, no
-// plan needed (each slot gathers its own adapter's rank rows, so the launch
-// that builds the plan can run it too).  Wave w takes rank rows w, w+4, ...,
-// four of them per pass.  Each lane adds its 16-byte chunks in ascending
-// order with v_dot2, then the wave sum and coef = gate . (scale . extra):
-// the same operations in the same order as shrink_units_wave, so U is
-// identical to the plan-driven shrink's.
+// Per-slot decode shrink, no plan needed (each slot gathers its own
+// adapter's rank rows, so the launch that builds the plan can run it too).
+// Four workgroups (4 waves each) per slot i = t*K + k: part q, wave w takes
+// rank rows 4q + w, 4q + w + 16, ..., one row at a time with every load of
+// the row (token row and A page) in one round trip, so the slot's rows go
+// out from 16 waves at once.  Each lane adds its 16-byte chunks in
+// ascending order with v_dot2, then the wave sum and coef = gate . (scale .
+// extra): the same operations in the same order as shrink_units_wave, so U
+// is identical to the plan-driven shrink's.
 //
-// The workgroup's first wave also writes the slot's descriptor for the
-// epilogue: active when its id is in range, its gate is not 0, its adapter's
-// rank is in 1..LORA_MAX_RANK with a consistent page_start and every page id
-// in range (the plan's rule for keeping a slot).
+// Part 0's first wave also writes the slot's descriptor for the epilogue:
+// active when its id is in range, its gate is not 0, its adapter's rank is
+// in 1..LORA_MAX_RANK with a consistent page_start and every page id in
+// range (the plan's rule for keeping a slot).
+constexpr int kSlotParts = 4;    // workgroups per slot
+
 template <bool kMask>
-__device__ __forceinline__ void slot_shrink_wg(const SlotShrinkArgs &s, const int i) {
-  constexpr int RW = 4;                         // rank rows per pass
-  constexpr int kCh = 4;                        // 512-element chunks per block
+__device__ __forceinline__ void slot_shrink_part(const SlotShrinkArgs &s, const int i, const int q) {
+  constexpr int kCh = 4;                        // 512-element chunks per load batch
   constexpr int KB = kCh * 512;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int id = s.ids[i];
@@ -322,10 +325,10 @@ __device__ __forceinline__ void slot_shrink_wg(const SlotShrinkArgs &s, const in
     act = r > 0 && r <= LORA_MAX_RANK && ps >= 0 && int64_t(pe) - ps == r && pe <= s.n_page_ids;
   }
   if (!act) {
-    if (threadIdx.x == 0) s.sdesc[i] = make_int4(-1, 0, 0, 0);
+    if (q == 0 && threadIdx.x == 0) s.sdesc[i] = make_int4(-1, 0, 0, 0);
     return;
   }
-  if (w == 0) {
+  if (q == 0 && w == 0) {
     // every page id of the adapter in range (lane-parallel), then the
     // descriptor; the other waves only guard their own loads
     bool bad = false;
@@ -343,50 +346,32 @@ __device__ __forceinline__ void slot_shrink_wg(const SlotShrinkArgs &s, const in
   const uint16_t *zrow = static_cast<const uint16_t *>(s.Z) + t * d;
   const uint8_t *mrow = kMask ? s.mask + t * d : nullptr;
   const uint16_t *pages = static_cast<const uint16_t *>(s.pages);
-  for (int j0 = w; j0 < r; j0 += 4 * RW) {
-    const uint16_t *arow[RW];
-    bool ok[RW];
+  for (int j = kSlotParts * q + w; j < r; j += 4 * kSlotParts) {
+    const int pid = s.page_ids[ps + j];
+    const bool in = pid >= 0 && pid < s.n_pages;
+    const uint16_t *arow = pages + int64_t(in ? pid : 0) * d;
+    float acc = 0.f;
+    for (int cb = 0; cb < d; cb += 2 * KB) {
+      // two batches of kCh chunks in flight, added in ascending order
+      Raw<uint16_t> ar[2 * kCh], xr[2 * kCh];
+      uint2 mk[2 * kCh];
 #pragma unroll
-    for (int a2 = 0; a2 < RW; ++a2) {
-      const int j = min(j0 + 4 * a2, r - 1);
-      const int pid = s.page_ids[ps + j];
-      const bool in = pid >= 0 && pid < s.n_pages;
-      ok[a2] = j0 + 4 * a2 < r && in;
-      arow[a2] = pages + int64_t(in ? pid : 0) * d;
-    }
-    float acc[RW];
-#pragma unroll
-    for (int a2 = 0; a2 < RW; ++a2) acc[a2] = 0.f;
-    for (int cb = 0; cb < d; cb += KB) {
-      Raw<uint16_t> ar[RW][kCh], xr[kCh];
-      uint2 mk[kCh];
-#pragma unroll
-      for (int ch = 0; ch < kCh; ++ch) {
+      for (int ch = 0; ch < 2 * kCh; ++ch) {
         const int c = min(cb + ch * 512 + lane * 8, d - 8);
         xr[ch].load(zrow + c);
         if (kMask) mk[ch] = *reinterpret_cast<const uint2 *>(mrow + c);
-#pragma unroll
-        for (int a2 = 0; a2 < RW; ++a2) ar[a2][ch].load(arow[a2] + c);
+        ar[ch].load(arow + c);
       }
 #pragma unroll
-      for (int ch = 0; ch < kCh; ++ch) {
+      for (int ch = 0; ch < 2 * kCh; ++ch) {
         if (cb + ch * 512 + lane * 8 >= d) continue;
         Raw<uint16_t> xv = xr[ch];
         if (kMask) Dot8<uint16_t>::mask(xv, mk[ch]);
-#pragma unroll
-        for (int a2 = 0; a2 < RW; ++a2) acc[a2] = Dot8<uint16_t>::run(xv, ar[a2][ch], acc[a2]);
+        acc = Dot8<uint16_t>::run(xv, ar[ch], acc);
       }
     }
-#pragma unroll
-    for (int a2 = 0; a2 < RW; ++a2) acc[a2] = wave_sum(acc[a2]);
-    if (lane < RW) {
-      float mine = acc[0];
-      bool mok = ok[0];
-#pragma unroll
-      for (int a2 = 1; a2 < RW; ++a2)
-        if (lane == a2) { mine = acc[a2]; mok = ok[a2]; }
-      if (mok) s.out[int64_t(i) * s.stride + j0 + 4 * lane] = coef * mine;
-    }
+    acc = wave_sum(acc);
+    if (lane == 0 && in) s.out[int64_t(i) * s.stride + j] = coef * acc;
   }
 }
 
