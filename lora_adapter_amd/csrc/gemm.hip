@@ -373,10 +373,14 @@ __global__ __launch_bounds__(256, 2) void decode_gemm_shrink_kernel(GemmArgs g, 
     shrink_units_wave<uint16_t, kMask, kCh, true>(s, w);
 }
 
-// Workgroup 0 builds the plan, workgroups 1 .. 4 n_slots run the per-slot
-// shrink (four per slot), the decode GEMM tiles follow.  The shrink's few
-// dependent loads go out first, ahead of the W stream; no part reads what
-// another writes, and neither the shrink nor the GEMM needs the plan.
+// Workgroup 0 builds the plan, workgroups 1 .. n_gemm are the decode GEMM
+// tiles, the per-slot shrink parts (four per slot) follow.  No part reads
+// what another writes, and neither the shrink nor the GEMM needs the plan.
+// GEMM tiles first: they are dispatched one per CU whatever the shrink does.
+// With the shrink parts first, a batch whose slots are all inactive (parts
+// that end at once) had its tiles packed unevenly onto CUs: workload 2
+// with an empty plan took 22.3 us per step against 17.3 us this way, and
+// the full step is the same either way (21.9 us).
 template <int MB, bool kMask, bool kLds>
 __global__ __launch_bounds__(256) void decode_gemm_slot_kernel(GemmArgs g, SlotShrinkArgs ss,
                                                                 PlanArgs pa, int gx, int gy,
@@ -389,12 +393,12 @@ __global__ __launch_bounds__(256) void decode_gemm_slot_kernel(GemmArgs g, SlotS
     plan_build<kLds>(pa, reinterpret_cast<int *>(xs));
     return;
   }
-  if (b - 1 < kSlotParts * ss.n_slots) {
-    slot_shrink_part<kMask>(ss, (b - 1) / kSlotParts, (b - 1) % kSlotParts);
+  if (b - 1 < n_gemm) {
+    const int t = b - 1;
+    decode_tile<MB>(g, t % gx, (t / gx) % gy, t / (gx * gy), xs);
     return;
   }
-  const int t = b - 1 - kSlotParts * ss.n_slots;
-  decode_tile<MB>(g, t % gx, (t / gx) % gy, t / (gx * gy), xs);
+  slot_shrink_part<kMask>(ss, (b - 1 - n_gemm) / kSlotParts, (b - 1 - n_gemm) % kSlotParts);
 }
 
 // ------------------------------------------------------------ pipelined tile GEMM
