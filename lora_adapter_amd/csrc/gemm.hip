@@ -930,12 +930,30 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_tile_kernel(GemmArgs g) 
     }
   }
   const int per = (ntiles + 7) / 8;
-  const int t = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  int b = int(blockIdx.x), half = -1;
+  if constexpr (kFused && NS == 2 && BN == 256) {
+    // A grid larger than 8 * per asks for the last, partial round of tiles
+    // (the workgroups past the last multiple of 256) as two 256 x 128 halves
+    // each: that round then takes half a tile's time on twice the CUs.
+    const int nb = 8 * per, n_first = nb - nb % 256;
+    if (int(gridDim.x) > nb && b >= n_first) {
+      half = (b - n_first) & 1;
+      b = n_first + (b - n_first) / 2;
+    }
+  }
+  const int t = (b & 7) * per + (b >> 3);
   if (t >= ntiles) return;
   int tm, tn;
   tile_coords(t, tiles_m, tiles_n, tm, tn);
   const int k_begin = blockIdx.y * g.k_split;
   const int k_end = min(g.Kd, k_begin + g.k_split);
+  if constexpr (kFused && NS == 2 && BN == 256) {
+    if (half >= 0) {
+      tile_run<BM, BN / 2, WM, WN, NS, kFused>(g, smem, tm * BM, tn * BN + half * (BN / 2), k_begin,
+                                               (k_end - k_begin) / 64, blockIdx.y);
+      return;
+    }
+  }
   tile_run<BM, BN, WM, WN, NS, kFused>(g, smem, tm * BM, tn * BN, k_begin, (k_end - k_begin) / 64,
                                        blockIdx.y);
 }
@@ -1232,7 +1250,13 @@ hipError_t launch_base_gemm(const GemmConfig &c, const GemmArgs &g, hipStream_t 
     const int tiles = ((g.M + c.bm - 1) / c.bm) * ((g.N + c.bn - 1) / c.bn);
     const dim3 grid = c.sk > 0 ? dim3(c.sk, 1) : dim3(8 * ((tiles + 7) / 8), c.splits);
     if (c.kind == 5) {
-      if (c.fused) hipLaunchKernelGGL((gemm_tile_kernel<256, 256, 2, 2, 2, true>), grid, dim3(256), 0, s, g);
+      if (c.fused) {
+        // a last partial round of at most 128 tiles runs as 256 x 128 halves
+        unsigned gx = grid.x;
+        const unsigned nf = gx - gx % 256, rem = gx - nf;
+        if (nf > 0 && rem > 0 && rem <= 128) gx = nf + 2 * rem;
+        hipLaunchKernelGGL((gemm_tile_kernel<256, 256, 2, 2, 2, true>), dim3(gx, grid.y), dim3(256), 0, s, g);
+      }
       else hipLaunchKernelGGL((gemm_tile_kernel<256, 256, 2, 2, 2, false>), grid, dim3(256), 0, s, g);
     } else {
       if (c.fused) hipLaunchKernelGGL((gemm_tile_kernel<256, 128, 2, 2, 3, true>), grid, dim3(256), 0, s, g);
