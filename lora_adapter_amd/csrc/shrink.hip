@@ -21,7 +21,10 @@
 //     global memory as MFMA fragments, the dropout mask applied to the bf16
 //     fragment (exact), the four waves of a workgroup splitting d and adding
 //     through LDS.  X is read once from HBM per rank-row block.
-// The same kernels compute the gradient's dY.B^T (Z = dY, pages = B).
+// When the tile kernel is on and d <= 6144, both run in one launch
+// (shrink_both_kernel): its tiles first, then the units schedule.
+// The same kernels compute the gradient's dY.B^T (Z = dY, pages = B) where
+// the gradient does not form it on MFMA.
 #include "lora_internal.h"
 #include "shrink_units.h"
 
