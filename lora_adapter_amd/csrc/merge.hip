@@ -469,7 +469,10 @@ __device__ __forceinline__ void merge_stream(const MergeArgs &m, int total, uint
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = wr0 + 16 * e;
-        *reinterpret_cast<uint4 *>(W + int64_t(n0 + row) * m.d_in + i0 + 8 * wc) = wbuf[row][wc ^ (row & 15)];
+        // streaming store: the merged W is not read again by this launch
+        const uint4 o = wbuf[row][wc ^ (row & 15)];
+        const u32x4 ov = {o.x, o.y, o.z, o.w};
+        __builtin_nontemporal_store(ov, reinterpret_cast<u32x4 *>(W + int64_t(n0 + row) * m.d_in + i0 + 8 * wc));
       }
     }
   };
