@@ -183,7 +183,9 @@ constexpr int kOuterK = 32;
 template <bool kMask>
 __global__ __launch_bounds__(256) void seg_outer_mfma_kernel(SegOuterArgs a) {
   constexpr int RB = kGradRankChunk;
-  constexpr int ZP = kOuterCols + 8;          // staged row pitch (bf16)
+  // staged row pitch (bf16): rows 8 apart (the four lane groups of a
+  // transposed 16-bit read) then start 16 banks apart
+  constexpr int ZP = kOuterCols + 4;
   __shared__ int s_row[kGradPairChunk];
   __shared__ __attribute__((aligned(16))) float s_cf[kGradPairChunk][RB];
   __shared__ __attribute__((aligned(16))) uint16_t s_z[kOuterK][ZP];
@@ -267,10 +269,13 @@ __global__ __launch_bounds__(256) void seg_outer_mfma_kernel(SegOuterArgs a) {
           }
           w[i] &= keep;
         }
+        // rows are 8-byte aligned (pitch ZP): memcpy lets the compiler pick
+        // the widest aligned LDS stores
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          *reinterpret_cast<uint4 *>(&s_z[zr][zc + 8 * e]) =
-              make_uint4(w[4 * e], w[4 * e + 1], w[4 * e + 2], w[4 * e + 3]);
+        for (int e = 0; e < 4; ++e) {
+          const uint4 v4 = make_uint4(w[4 * e], w[4 * e + 1], w[4 * e + 2], w[4 * e + 3]);
+          __builtin_memcpy(&s_z[zr][zc + 8 * e], &v4, 16);
+        }
       };
       f32x4_t acc[4];
 #pragma unroll
