@@ -177,6 +177,15 @@ __global__ __launch_bounds__(kGradThreads) void seg_outer_partial_kernel(SegOute
 // gathered token rows (keep mask applied: exact zeros) are staged in LDS, the
 // next step's rows in flight meanwhile.  The fp32 coefficients are split
 // exactly into bf16 high and low parts (two MFMAs), which keeps ~16 bits.
+// Workgroup barrier for LDS only: the next step's token-row loads and the
+// partial stores stay in flight across it (__syncthreads() would wait for
+// every outstanding load and store).
+__device__ __forceinline__ void lds_bar() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 constexpr int kOuterCols = 256;
 constexpr int kOuterK = 32;
 
@@ -297,9 +306,9 @@ __global__ __launch_bounds__(256) void seg_outer_mfma_kernel(SegOuterArgs a) {
       }
       fetch(l_beg);
       for (int k0 = l_beg; k0 < l_end; k0 += kOuterK) {
-        __syncthreads();                       // the previous step is done with s_z
+        lds_bar();                             // the previous step is done with s_z
         stage(k0);
-        __syncthreads();
+        lds_bar();
         if (k0 + kOuterK < l_end) fetch(k0 + kOuterK);
         // A operand: rank row j = lane % 16, pairs k0 + 8 * (lane / 16) + e
         const int kk = (lane >> 4) * 8;
