@@ -949,8 +949,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_tile_kernel(GemmArgs g) 
   const int k_end = min(g.Kd, k_begin + g.k_split);
   if constexpr (kFused && NS == 2 && BN == 256) {
     if (half >= 0) {
-      tile_run<BM, BN / 2, WM, WN, NS, kFused>(g, smem, tm * BM, tn * BN + half * (BN / 2), k_begin,
-                                               (k_end - k_begin) / 64, blockIdx.y);
+      // a second half wholly past the last column has nothing to do (and its
+      // operand rows must not be clamped from below N)
+      const int n0 = tn * BN + half * (BN / 2);
+      if (n0 >= g.N) return;
+      tile_run<BM, BN / 2, WM, WN, NS, kFused>(g, smem, tm * BM, n0, k_begin, (k_end - k_begin) / 64,
+                                               blockIdx.y);
       return;
     }
   }

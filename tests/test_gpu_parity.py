@@ -172,9 +172,12 @@ def test_apply_small(cfg):
     assert err <= TOL[w.dtype], err
 
 
-def test_apply_fused_epilogue_path():
-    # enough output tiles that the expand runs inside the GEMM epilogue
-    w = wl.config(4, T=2100, d_in=512, d_out=8192, seed=77)
+@pytest.mark.parametrize("d_out", [8192, 8320])
+def test_apply_fused_epilogue_path(d_out):
+    # enough output tiles that the expand runs inside the GEMM epilogue; the
+    # last partial round of tiles runs as half tiles, and with d_out = 8320
+    # some second halves lie wholly past the last column
+    w = wl.config(4, T=2100, d_in=512, d_out=d_out, seed=77)
     L = run(w)
     err = rel_err(D.as_f64(L.Y_host()), O.apply_workload(w))
     assert err <= TOL["bf16"], err
