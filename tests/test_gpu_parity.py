@@ -245,6 +245,25 @@ def test_apply_full_prefill_sampled_rows():
 
 # ---------------------------------------------------------------- invariants
 
+@pytest.mark.parametrize("cfg", ["small2", "dec3"])
+def test_forward_all_inactive_equals_base_only(cfg):
+    """lora_forward on a batch whose slots are all inactive (decode path:
+    the GEMM tiles, then per-slot shrink parts that end at once): Y equals
+    the base-only product bit for bit and the plan is empty."""
+    w = small(2) if cfg == "small2" else FORWARD_CASES[cfg]()
+    L = run(w)
+    Yb = _base_only(L)
+    L.ids.fill_(-1)
+    L.Y.zero_()
+    L.ws.zero_()
+    B.lora_forward(L.ids, L.gates, L.T, L.K, L.X, L.W_t, L.Y, L.keep_mask, L.keep_scale,
+                   L.pool, L.plan, L.ws)
+    torch.cuda.synchronize()
+    hdr = L.read_plan()["header"]
+    assert hdr[B.PH_PAIRS] == 0 and hdr[B.PH_ERR] == 0
+    assert np.array_equal(L.Y_host(), Yb)
+
+
 def _base_only(L):
     ids_saved = L.ids.clone()
     L.ids.fill_(-1)
