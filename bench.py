@@ -1,41 +1,44 @@
 #!/usr/bin/env python3
 """Benchmark of the batched multi-adapter LoRA layer on one MI355X.
 
-One step = one pass of the whole hot path over one batch: lora_plan (segment
-plan), then lora_apply = shrink (LoRA down projection of every planned pair)
-+ base MFMA GEMM + expand (up projection added to the fp32 accumulators, one
-rounding).  Default workload: Llama-7B q_proj decode, bf16, d_in = d_out =
-4096, 64 tokens, 64 adapters of rank 16, each token on a uniformly drawn
-adapter (synthetic, seeded).
+One step = one pass of the whole hot path over one batch of the workload:
+  * lora_forward: the segment plan, the shrink (LoRA down projection of every
+    planned pair), the base MFMA GEMM and the expand (up projection added to
+    the fp32 accumulators before the one rounding);
+  * and, when the workload trains (it carries dY), lora_grad: dA and dB of
+    every used adapter.
+Default workload: the fine-tune/prefill shape, bf16, X 8192 x 4096, W 4096 ->
+11008, 4 adapters of rank 16 on Dirichlet(1) contiguous segments, keep mask
+Bernoulli(0.9), forward plus dA, dB for a random dY (synthetic, seeded).  The
+other workloads (q_proj decode, heterogeneous ranks, compressed fleet with
+top-2 routing and a merge/unmerge) are measured after it, more briefly, and
+reported under "workloads".
 
 Measurement
   * value: tokens per second over exactly --steps steps, wall clock between
-    two torch.cuda.synchronize() calls, launches queued eagerly on one stream
-    (faster on this stack than replaying a captured HIP graph of the same
-    step, whose time is reported as step_us_graph_replay).  Each step is one
-    call of lora_forward (plan + shrink + GEMM + epilogue: for decode shapes two
-    launches, GEMM + per-slot shrink, then epilogue + plan; for stream-K
-    shapes the plan is built inside the GEMM launch) on one of R rotated
-    copies of the weights
-    and adapter pool, R chosen so that R copies exceed 1 GiB: every step reads
-    its W and pages from HBM, not from the 256 MiB Infinity Cache.
-    value_apply_only: the same without the plan (built once per batch and
-    shared by every layer of a model).
-  * per-kernel durations: HIP events on the launch stream around blocks of
+    two torch.cuda.synchronize() calls, launches queued eagerly on one stream,
+    each step on one of R rotated copies of W, X (and dY, mask) and the adapter
+    pool, R chosen so that the copies exceed 1 GiB: every step reads from HBM,
+    not from the 256 MiB Infinity Cache.  value_forward: the same without the
+    gradients; value_apply_only: the forward on a plan built once per batch
+    (shared by every layer of a model).
+  * per-launch durations: HIP events on the launch stream around blocks of
     back-to-back launches of one stage on the rotated copies, queued behind a
     busy prefix (so the events time the kernels, not host launch gaps).
-  * roofline: the dominant kernel (the base GEMM).  Below the MFMA/HBM ridge
-    (~312 flop/byte) it is priced against 8 TB/s HBM with its algorithmic
-    bytes (W + X), above it against 2.5 PFLOP/s bf16 MFMA with its
+  * roofline: the launch that runs the base GEMM.  Above the MFMA/HBM ridge
+    (~312 flop/byte) it is priced against 2.5 PFLOP/s bf16 MFMA with its
     algorithmic flops (2 T d_in d_out, plus the expand when it runs inside the
-    GEMM).  traffic: HBM bytes per launch from rocprofv3 FETCH_SIZE and
-    WRITE_SIZE counters, scaled by the same counters on a copy of known size,
-    read from the committed summary profiles/traffic.json when the GEMM
-    source still matches the hash recorded there (else null).
-  * LoRA path: t_apply - t_base where t_base is the same step on an empty
-    plan; LoRA bytes = used A and B pages + X rows + U (written and read).
-  * cpu_baseline: the CPU oracle (fp64 numpy) on the same workload, on the
-    host's cores, for a bounded number of seconds.
+    GEMM), below it against 8 TB/s with its algorithmic bytes.  traffic: HBM
+    bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE, scaled by the
+    same counters on a copy of known size, read from profiles/traffic.json
+    when the kernel sources still match the hash recorded there (else null).
+  * LoRA path: the apply's launches (shrink + GEMM, then the epilogue) timed
+    with the batch's plan and with an empty plan; the LoRA path's time is the
+    sum of the per-launch differences, its bytes the used A and B pages, the X
+    rows (and mask) it reads and U (written and read).  The wall-clock step
+    difference is reported beside it.
+  * cpu_baseline: the CPU oracle (fp64 numpy, untuned) on a bounded sample of
+    the same workload, on the host's cores.
 
   --copy-probe runs a 256 MiB device-to-device copy five times first, so that
   a rocprofv3 --pmc run of this script also holds the calibration kernel.
@@ -45,6 +48,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import platform
 import sys
 import time
 
@@ -61,35 +65,339 @@ METRIC = "tokens/sec per multi-LoRA layer at 1 GPU; LoRA-path HBM GB/s as % of p
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", type=int, default=2, help="workload recipe 1..5")
-    ap.add_argument("--event-steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=4, help="workload recipe 1..5 (the headline)")
+    ap.add_argument("--others", default="2,3,5",
+                    help="workloads measured after the headline, comma separated ('' for none)")
+    ap.add_argument("--other-steps", type=int, default=200)
+    ap.add_argument("--event-steps", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotation", type=int, default=0, help="copies of W/pool (0: >= 1 GiB)")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="skip the HIP-graph replay timing (the value is timed with eager launches)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time a captured HIP graph of the step (the value is eager)")
+    ap.add_argument("--skip-empty-plan", action="store_true",
+                    help="no runs on an empty plan (for kernel traces whose averages should "
+                         "hold only launches with the batch's plan; no LoRA-path figures)")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs of a --copy-probe run into "
-                         "profiles/traffic.json entries, then exit")
+                         "profiles/traffic.json entries for --workload, then exit")
     return ap.parse_args()
+
+
+# ---------------------------------------------------------------- launch rules
+
+def gemm_kind(T, d_in, d_out, bf16):
+    """The library's base GEMM choice (host rules in choose_gemm): 'f32',
+    'decode' (T <= 128), 'fused' (256 x 256 tiles with the expand in the
+    epilogue, when they fill the GPU), 'streamk' (256 x 128 stream-K tiles
+    with the plan built in the launch) or 'split'."""
+    if not bf16:
+        return "f32"
+    if T <= 128:
+        return "decode"
+    if ((T + 255) // 256) * ((d_out + 255) // 256) >= 256:
+        return "fused"
+    units = ((T + 255) // 256) * ((d_out + 127) // 128) * (d_in // 64)
+    return "streamk" if units >= 4 * 255 else "split"
+
+
+GEMM_KERNEL = {"f32": "gemm_f32_kernel", "decode": "decode_gemm_slot_kernel",
+               "fused": "gemm_tile_kernel", "streamk": "gemm_tile_plan_kernel",
+               "split": "gemm_tile_kernel"}
 
 
 class Copy:
     """One rotated copy of the layer's HBM-resident tensors."""
 
     def __init__(self, L, B, torch, clone: bool):
-        self.X = L.X.clone() if clone else L.X
-        self.W_t = L.W_t.clone() if clone else L.W_t
-        a = L.a_pages.clone() if clone else L.a_pages
-        b = L.b_pages.clone() if clone else L.b_pages
+        cl = (lambda t: None if t is None else t.clone()) if clone else (lambda t: t)
+        self.X = cl(L.X)
+        self.W_t = cl(L.W_t)
+        self.dY = cl(L.dY)
+        self.mask = cl(L.keep_mask)
+        a = cl(L.a_pages)
+        b = cl(L.b_pages)
         self.pool = B.Pool(L.dtype, L.w.d_in, L.w.d_out, a, b, L.rank, L.page_start,
                            L.pool.tensors[4], L.scale)
         self.plan = torch.empty_like(L.plan)
         self.ws = torch.empty_like(L.ws)
         self.Y = torch.empty_like(L.Y)
+
+
+class Bench:
+    """Timing harness for one workload resident on the GPU."""
+
+    def __init__(self, w, args, torch, np, B, D, grads=True, rotation=0):
+        self.w, self.args, self.torch, self.np, self.B, self.D = w, args, torch, np, B, D
+        L = D.DeviceLayer(w)
+        self.L = L
+        self.T, self.K = w.T, w.K
+        self.ids, self.gates = L.ids, L.gates
+        self.empty_ids = torch.full_like(L.ids, -1)
+        per_copy = sum(t.numel() * t.element_size() for t in
+                       (L.W_t, L.a_pages, L.b_pages, L.X, L.dY, L.keep_mask) if t is not None)
+        self.R = rotation or max(2, int(np.ceil((1 << 30) / per_copy)))
+        self.copies = [Copy(L, B, torch, clone=(i > 0)) for i in range(self.R)]
+        self.stream = torch.cuda.current_stream()
+        self.grads = grads and w.dY is not None
+        if self.grads:
+            self.dA, self.dB, self.gws = L.grad_buffers()
+        self.big = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+
+    # -- the step and its parts ------------------------------------------------
+    def forward(self, c, ids):
+        B, L = self.B, self.L
+        B.lora_forward(ids, self.gates, self.T, self.K, c.X, c.W_t, c.Y, c.mask, L.keep_scale,
+                       c.pool, c.plan, c.ws)
+
+    def apply(self, c):
+        B, L = self.B, self.L
+        B.lora_apply(c.X, c.W_t, c.Y, self.T, self.K, self.gates, c.mask, L.keep_scale, c.pool,
+                     c.plan, c.ws)
+
+    def grad(self, c):
+        B, L = self.B, self.L
+        B.lora_grad(c.X, c.mask, L.keep_scale, c.dY, self.T, self.K, self.gates, c.pool, c.plan,
+                    c.ws, self.dA, self.dB, L.max_rank, self.gws)
+
+    def step(self, c, ids=None):
+        self.forward(c, self.ids if ids is None else ids)
+        if self.grads:
+            self.grad(c)
+
+    def plan_all(self, ids):
+        for c in self.copies:
+            self.B.lora_plan(ids, self.gates, self.T, self.K, c.pool, c.plan)
+
+    def timed(self, fn, steps, warmup):
+        """Seconds for `steps` calls fn(copy), after `warmup` calls, between
+        two synchronizes."""
+        R, torch = self.R, self.torch
+        for i in range(warmup):
+            fn(self.copies[i % R])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            fn(self.copies[i % R])
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    def timed_graph(self, steps, warmup):
+        """The step captured in one HIP graph per copy, replayed."""
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for c in self.copies:
+                self.step(c)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        gs = []
+        for c in self.copies:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.step(c)
+            gs.append(g)
+        torch.cuda.synchronize()
+        for i in range(warmup):
+            gs[i % self.R].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            gs[i % self.R].replay()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    def event_us(self, fn, reps, rounds):
+        """Median over rounds of (HIP events around `reps` back-to-back calls
+        fn(i) on the launch stream) / reps, each round queued behind two
+        large GEMMs so that the events time the kernels, not the host."""
+        torch, np = self.torch, self.np
+        ts = []
+        for _ in range(rounds):
+            for _ in range(2):
+                torch.mm(self.big, self.big)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(self.stream)
+            for i in range(reps):
+                fn(i)
+            e1.record(self.stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3 / reps)
+        return float(np.median(ts))
+
+    def stage_us(self, ids, n):
+        """Per-launch HIP-event times of each stage of the path, every copy
+        holding a valid plan (lora_plan) and U (lora_shrink) of `ids`."""
+        B, L, T, K, g = self.B, self.L, self.T, self.K, self.gates
+        stages = {
+            "plan": lambda c: B.lora_plan(ids, g, T, K, c.pool, c.plan),
+            "fwd_gemm": lambda c: B.lora_forward_gemm(ids, g, T, K, c.X, c.W_t, c.Y, c.mask,
+                                                      L.keep_scale, c.pool, c.plan, c.ws),
+            "fwd_finish": lambda c: B.lora_forward_finish(ids, g, T, K, c.X, c.W_t, c.Y, c.mask,
+                                                          L.keep_scale, c.pool, c.plan, c.ws),
+            "shrink_gemm": lambda c: B.lora_shrink_gemm(c.X, c.W_t, c.Y, T, K, g, c.mask,
+                                                        L.keep_scale, c.pool, c.plan, c.ws),
+            "shrink": lambda c: B.lora_shrink(c.X, c.mask, L.keep_scale, T, K, g, c.pool, c.plan,
+                                              c.ws),
+            "gemm": lambda c: B.lora_base_gemm(c.X, c.W_t, c.Y, T, K, c.pool, c.plan, c.ws),
+            "epilogue": lambda c: B.lora_expand_epilogue(c.X, c.W_t, c.Y, T, K, c.pool, c.plan,
+                                                         c.ws),
+        }
+        if self.grads:
+            stages["grad"] = lambda c: self.grad(c)
+        reps = min(self.R, 32) if self.R >= 8 else 8
+        rounds = max(3, n // reps)
+        out = {}
+        for name, fn in stages.items():
+            self.plan_all(ids)
+            for c in self.copies:
+                B.lora_shrink(c.X, c.mask, L.keep_scale, T, K, g, c.pool, c.plan, c.ws)
+            self.torch.cuda.synchronize()
+            out[name] = self.event_us(lambda i: fn(self.copies[i % self.R]), reps, rounds)
+        for c in self.copies:
+            self.step(c, ids)
+        self.torch.cuda.synchronize()
+        return out
+
+    def header(self, c):
+        return self.B.lora_plan_header(c.plan)
+
+
+def lora_bytes(w, P, R_pairs, R_used, e, masked):
+    """Algorithmic bytes of the LoRA path (shrink + expand): each used A page
+    and B page once, the X rows of the active pairs (and their mask bytes),
+    U written and read."""
+    b = R_used * (w.d_in + w.d_out) * e + P * w.d_in * e + 8 * R_pairs
+    return b + (P * w.d_in if masked else 0)
+
+
+def measure(w, args, torch, np, B, D, steps, warmup, full):
+    """Step time, per-launch times, LoRA path and (full) the roofline of one
+    workload."""
+    bn = Bench(w, args, torch, np, B, D, rotation=args.rotation)
+    T, K = w.T, w.K
+    e = 2 if bn.L.dtype == B.LORA_BF16 else 4
+    kind = gemm_kind(T, w.d_in, w.d_out, bn.L.dtype == B.LORA_BF16)
+
+    el_step = bn.timed(lambda c: bn.step(c), steps, warmup)
+    el_fwd = bn.timed(lambda c: bn.forward(c, bn.ids), steps, warmup)
+    skip0 = args.skip_empty_plan
+    el_base = None if skip0 else bn.timed(lambda c: bn.forward(c, bn.empty_ids), steps, warmup)
+    bn.plan_all(bn.ids)
+    el_apply = bn.timed(lambda c: bn.apply(c), steps, warmup)
+    el_graph = bn.timed_graph(steps, warmup) if args.graph else None
+    bn.step(bn.copies[0])
+    torch.cuda.synchronize()
+    hdr = bn.header(bn.copies[0])
+    P, S, R_pairs, R_used = (hdr[B.PH_PAIRS], hdr[B.PH_SEGS], hdr[B.PH_RPAIRS], hdr[B.PH_RUSED])
+
+    st = bn.stage_us(bn.ids, args.event_steps if full else 32)
+    st0 = None if skip0 else bn.stage_us(bn.empty_ids, args.event_steps if full else 32)
+    lb = lora_bytes(w, P, R_pairs, R_used, e, w.keep_mask is not None)
+    lf = 2.0 * R_pairs * (w.d_in + w.d_out)
+    # LoRA path from the apply's launches (the plan built once per batch):
+    # shrink + GEMM (one launch on decode shapes, two otherwise), then the
+    # epilogue (a no-op when the expand runs in the GEMM's epilogue)
+    t_lora = None if skip0 else sum(st[k] - st0[k] for k in ("shrink_gemm", "epilogue"))
+    ok = t_lora is not None and t_lora > 0.05
+    t_step, t_fwd = el_step / steps, el_fwd / steps
+    t_base = None if skip0 else el_base / steps
+    out = {
+        "workload": w.name, "T": T, "K": K, "d_in": w.d_in, "d_out": w.d_out,
+        "adapters": w.n_adapters, "active_pairs": P, "segments": S, "R_used": R_used,
+        "R_pairs": R_pairs, "rotation_copies": bn.R, "gemm": kind,
+        "step_us": t_step * 1e6,
+        "step": "forward + grads" if bn.grads else "forward",
+        "tokens_per_s": T / t_step,
+        "forward_us": t_fwd * 1e6, "forward_tokens_per_s": T / t_fwd,
+        "apply_only_us": el_apply / steps * 1e6, "apply_only_tokens_per_s": T * steps / el_apply,
+        "forward_empty_plan_us": None if skip0 else t_base * 1e6,
+        "step_us_graph_replay": None if el_graph is None else el_graph / steps * 1e6,
+        "stages_us": st, "stages_us_empty_plan": st0,
+        "lora_path": {
+            "t_us": t_lora if ok else None,
+            "bytes": lb, "flops": lf,
+            "GB_s": lb / (t_lora * 1e-6) / 1e9 if ok else None,
+            "frac_hbm": lb / (t_lora * 1e-6) / 1e9 / HBM_PEAK_GBS if ok else None,
+            "t_us_wall_difference": None if skip0 else (t_fwd - t_base) * 1e6,
+            "method": "sum over the apply launches of (time with the plan - time with an empty "
+                      "plan), HIP events",
+        },
+    }
+    base_flops = 2.0 * T * w.d_in * w.d_out
+    if full:
+        out["_roofline"] = gemm_roofline(w, bn.L, B, kind, st, base_flops, P, R_pairs, R_used, e)
+        out["_lf"] = lf
+    if w.merge_ids is not None:
+        m_ids = D.to_device(np.asarray(w.merge_ids, np.int32), "cuda")
+        plus = D.to_device(np.ones(len(w.merge_ids), np.float32), "cuda")
+        minus = D.to_device(-np.ones(len(w.merge_ids), np.float32), "cuda")
+
+        def merge_call(i):
+            B.lora_merge_delta(bn.copies[(i // 2) % bn.R].W_t, bn.L.pool, m_ids,
+                               plus if i % 2 == 0 else minus, len(w.merge_ids))
+        t_m = bn.event_us(merge_call, 2 * min(bn.R, 8), 5)
+        rsum = int(sum(int(w.rank[a]) for a in w.merge_ids))
+        mb = 2 * w.d_in * w.d_out * e + rsum * (w.d_in + w.d_out) * e
+        out["merge"] = {"adapters": len(w.merge_ids), "us": t_m, "bytes": mb, "GB_s": mb / t_m / 1e3,
+                        "frac_hbm": mb / t_m / 1e3 / HBM_PEAK_GBS,
+                        "flops": 2.0 * w.d_in * w.d_out * rsum}
+    if bn.grads:
+        t_g = st["grad"]
+        gb = (T * w.d_out * e + T * w.d_in * (e + (1 if w.keep_mask is not None else 0))
+              + R_used * (w.d_in + w.d_out) * (e + 4) + 8 * R_pairs)
+        out["grads"] = {"us": t_g, "bytes": gb, "GB_s": gb / t_g / 1e3,
+                        "frac_hbm": gb / t_g / 1e3 / HBM_PEAK_GBS,
+                        "flops": 2.0 * R_pairs * (2 * w.d_out + w.d_in)}
+    del bn
+    torch.cuda.empty_cache()
+    return out
+
+
+def gemm_roofline(w, L, B, kind, st, base_flops, P, R_pairs, R_used, e):
+    """Roofline entry of the launch that runs the base GEMM, from its
+    HIP-event duration.  On decode shapes that launch also runs the per-slot
+    shrink (its bytes add the used A pages, each once, U and the slot
+    descriptors) and builds the plan; on stream-K shapes it builds the plan
+    (its bytes add the plan's inputs); fused, it runs the expand (its flops
+    add 2 R_pairs d_out)."""
+    name = GEMM_KERNEL[kind]
+    alg_bytes = (w.d_in * w.d_out + w.T * w.d_in) * e
+    flops = base_flops
+    if kind == "fused":
+        flops += 2.0 * R_pairs * w.d_out
+        t_us = st["gemm"]
+    elif kind == "decode":
+        t_us = st["fwd_gemm"]
+        alg_bytes += R_used * w.d_in * e + 4 * R_pairs + 16 * w.T * w.K
+        alg_bytes += w.T * w.d_in if L.keep_mask is not None else 0
+        flops += 2.0 * R_pairs * w.d_in
+    elif kind in ("streamk", "f32"):
+        t_us = st["fwd_gemm"]
+        alg_bytes += 8 * w.T * w.K + 8 * w.n_adapters + 4 * R_used
+    else:
+        t_us = st["gemm"]
+    intensity = base_flops / ((w.d_in * w.d_out + w.T * w.d_in + w.T * w.d_out) * e)
+    t = t_us * 1e-6
+    if L.dtype != B.LORA_BF16:
+        r = {"bound": "alu", "achieved": flops / t / 1e12, "peak": FP32_PEAK_TFLOPS,
+             "unit": "TFLOP/s", "alg_flops_per_launch": flops}
+    elif intensity > RIDGE_FLOP_PER_BYTE:
+        r = {"bound": "mfma", "achieved": flops / t / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+             "unit": "TFLOP/s", "alg_flops_per_launch": flops}
+    else:
+        r = {"bound": "hbm", "achieved": alg_bytes / t / 1e9, "peak": HBM_PEAK_GBS,
+             "unit": "GB/s", "alg_bytes_per_launch": alg_bytes}
+    r["frac"] = r["achieved"] / r["peak"]
+    r["traffic"] = measured_traffic(name, w.name)
+    r["kernel"] = name
+    r["avg_launch_us"] = t_us
+    return r
 
 
 def main():
@@ -120,200 +428,34 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
     w = wl.config(args.workload)
-    L = D.DeviceLayer(w)
-    T, K = w.T, w.K
-    ids, gates, mask = L.ids, L.gates, L.keep_mask
-    empty_ids = torch.full_like(ids, -1)
+    print(f"bench: workload {w.name}", file=sys.stderr, flush=True)
+    head = measure(w, args, torch, np, B, D, args.steps, args.warmup, full=True)
+    roofline = head.pop("_roofline")
+    head.pop("_lf")
+    e = 2 if w.dtype == "bf16" else 4
+    t_step = head["step_us"] * 1e-6
+    base_flops = 2.0 * w.T * w.d_in * w.d_out
+    layer_bytes = (w.d_in * w.d_out + w.T * (w.d_in + w.d_out)) * e + head["lora_path"]["bytes"]
 
-    # rotation copies: >= 1 GiB of W + pool + X
-    per_copy = (L.W_t.numel() * L.W_t.element_size() + L.a_pages.numel() * L.a_pages.element_size()
-                + L.b_pages.numel() * L.b_pages.element_size() + L.X.numel() * L.X.element_size())
-    R = args.rotation or max(2, int(np.ceil((1 << 30) / per_copy)))
-    copies = [Copy(L, B, torch, clone=(i > 0)) for i in range(R)]
-    stream = torch.cuda.current_stream()
-
-    def step(c, use_ids=ids, plan=True):
-        if plan:
-            B.lora_forward(use_ids, gates, T, K, c.X, c.W_t, c.Y, mask, L.keep_scale, c.pool, c.plan,
-                           c.ws)
-            return
-        B.lora_shrink_gemm(c.X, c.W_t, c.Y, T, K, gates, mask, L.keep_scale, c.pool, c.plan, c.ws)
-        B.lora_expand_epilogue(c.X, c.W_t, c.Y, T, K, c.pool, c.plan, c.ws)
-
-    # ---------------------------------------------------------------- graphs
-    def make_graphs(use_ids, plan, graph):
-        if not graph:
-            return None
-        gs = []
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for c in copies:       # warm the allocator / code objects outside capture
-                step(c, use_ids)   # (and leave a valid plan in every copy)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        for c in copies:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                step(c, use_ids, plan)
-            gs.append(g)
-        torch.cuda.synchronize()
-        return gs
-
-    def timed(use_ids, steps, warmup, plan=True, graph=False):
-        gs = make_graphs(use_ids, plan, graph)
-        run = ((lambda i: gs[i % R].replay()) if gs
-               else (lambda i: step(copies[i % R], use_ids, plan)))
-        for i in range(warmup):
-            run(i)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(steps):
-            run(i)
-        torch.cuda.synchronize()
-        return time.perf_counter() - t0
-
-    elapsed = timed(ids, args.steps, args.warmup)
-    for c in copies:       # apply-only steps reuse a plan built once per batch by lora_plan
-        B.lora_plan(ids, gates, T, K, c.pool, c.plan)
-    elapsed_apply = timed(ids, args.steps, args.warmup, plan=False)
-    elapsed_base = timed(empty_ids, args.steps, args.warmup)
-    elapsed_graph = None if args.no_graph else timed(ids, args.steps, args.warmup, graph=True)
-    # results of the last apply on copy 0 must not be stale: re-run eagerly
-    step(copies[0], ids)
-    torch.cuda.synchronize()
-    hdr = copies[0].plan[L.layout[0] // 4:L.layout[0] // 4 + 16].cpu().numpy()
-
-    # ---------------------------------------------------------------- per-kernel events
-    big = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
-
-    stages = {
-        "plan": lambda c, u: B.lora_plan(u, gates, T, K, c.pool, c.plan),
-        "fwd_gemm": lambda c, u: B.lora_forward_gemm(u, gates, T, K, c.X, c.W_t, c.Y, mask,
-                                                     L.keep_scale, c.pool, c.plan, c.ws),
-        "fwd_finish": lambda c, u: B.lora_forward_finish(u, gates, T, K, c.X, c.W_t, c.Y, mask,
-                                                         L.keep_scale, c.pool, c.plan, c.ws),
-        "shrink_gemm": lambda c, u: B.lora_shrink_gemm(c.X, c.W_t, c.Y, T, K, gates, mask,
-                                                       L.keep_scale, c.pool, c.plan, c.ws),
-        "shrink": lambda c, u: B.lora_shrink(c.X, mask, L.keep_scale, T, K, gates, c.pool, c.plan, c.ws),
-        "gemm": lambda c, u: B.lora_base_gemm(c.X, c.W_t, c.Y, T, K, c.pool, c.plan, c.ws),
-        "epilogue": lambda c, u: B.lora_expand_epilogue(c.X, c.W_t, c.Y, T, K, c.pool, c.plan, c.ws),
-    }
-
-    def stage_times(use_ids, n):
-        """Per stage: blocks of `reps` back-to-back launches on the rotating
-        copies, bracketed by two HIP events on the launch stream and queued
-        behind a busy prefix so the events time the kernels, not the host."""
-        reps = min(R, 32) if R >= 8 else 16
-        rounds = max(3, n // reps)
-        out = {}
-        for name, fn in stages.items():
-            for c in copies:              # every copy holds a valid plan (built by lora_plan) and U
-                B.lora_plan(use_ids, gates, T, K, c.pool, c.plan)
-                B.lora_shrink(c.X, mask, L.keep_scale, T, K, gates, c.pool, c.plan, c.ws)
-            torch.cuda.synchronize()
-            ts = []
-            for rd in range(rounds):
-                for _ in range(2):
-                    torch.mm(big, big)
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                for i in range(reps):
-                    fn(copies[(rd * reps + i) % R], use_ids)
-                e1.record(stream)
-                torch.cuda.synchronize()
-                ts.append(e0.elapsed_time(e1) * 1e3 / reps)
-            out[name] = ts
-        for c in copies:
-            step(c, use_ids)
-        torch.cuda.synchronize()
-        return ({k: float(np.median(v)) for k, v in out.items()},
-                {k: float(np.mean(v)) for k, v in out.items()})
-
-    st_med, st_mean = stage_times(ids, args.event_steps)
-    sb_med, sb_mean = stage_times(empty_ids, args.event_steps)
-
-    def event_time(fn, reps, rounds=5):
-        """Median over rounds of (events around `reps` back-to-back calls) / reps."""
-        ts = []
-        for _ in range(rounds):
-            for _ in range(2):
-                torch.mm(big, big)
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(reps):
-                fn(i)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1) * 1e3 / reps)
-        return float(np.median(ts))
-
-    e_bytes = 2 if L.dtype == B.LORA_BF16 else 4
-    extra = {}
-    if w.merge_ids is not None:
-        # signed merge of the workload's adapters into W, then the unmerge,
-        # alternating on the rotated copies (each copy returns near W)
-        m_ids = D.to_device(np.asarray(w.merge_ids, np.int32), "cuda")
-        plus = D.to_device(np.ones(len(w.merge_ids), np.float32), "cuda")
-        minus = D.to_device(-np.ones(len(w.merge_ids), np.float32), "cuda")
-        mcopies = [c.W_t for c in copies]
-
-        def merge_call(i):
-            B.lora_merge_delta(mcopies[(i // 2) % R], L.pool, m_ids, plus if i % 2 == 0 else minus,
-                               len(w.merge_ids))
-        t_m = event_time(merge_call, 2 * min(R, 8))
-        rsum = int(sum(int(w.rank[a]) for a in w.merge_ids))
-        m_bytes = 2 * w.d_in * w.d_out * e_bytes + rsum * (w.d_in + w.d_out) * e_bytes
-        extra["merge"] = {"adapters": len(w.merge_ids), "us": t_m, "bytes": m_bytes,
-                          "GB_s": m_bytes / t_m / 1e3, "frac_hbm": m_bytes / t_m / 1e3 / HBM_PEAK_GBS,
-                          "flops": 2.0 * w.d_in * w.d_out * rsum}
-    if w.dY is not None:
-        # LoRA grads dA, dB after the forward of copy 0 (its U in the workspace)
-        dA, dB, gws = L.grad_buffers()
-        c0 = copies[0]
-        step(c0, ids)
-        torch.cuda.synchronize()
-
-        def grad_call(i):
-            B.lora_grad(c0.X, mask, L.keep_scale, L.dY, T, K, gates, c0.pool, c0.plan, c0.ws,
-                        dA, dB, L.max_rank, gws)
-        t_g = event_time(grad_call, 8)
-        hdr0 = c0.plan[L.layout[0] // 4:L.layout[0] // 4 + 16].cpu().numpy()
-        Ru, Rp = int(hdr0[B.PH_RUSED]), int(hdr0[B.PH_RPAIRS])
-        g_bytes = (T * w.d_out * e_bytes + T * w.d_in * (e_bytes + (1 if mask is not None else 0))
-                   + Ru * (w.d_in + w.d_out) * (e_bytes + 4) + 8 * Rp)
-        extra["grads"] = {"us": t_g, "bytes": g_bytes, "GB_s": g_bytes / t_g / 1e3,
-                          "frac_hbm": g_bytes / t_g / 1e3 / HBM_PEAK_GBS,
-                          "flops": 2.0 * Rp * (2 * w.d_out + w.d_in)}
-
-    # ---------------------------------------------------------------- figures
-    e = 2 if L.dtype == B.LORA_BF16 else 4
-    P, S, R_pairs, R_used = (int(hdr[B.PH_PAIRS]), int(hdr[B.PH_SEGS]), int(hdr[B.PH_RPAIRS]),
-                             int(hdr[B.PH_RUSED]))
-    w_bytes = w.d_in * w.d_out * e
-    x_bytes = T * w.d_in * e
-    y_bytes = T * w.d_out * e
-    t_step = elapsed / args.steps
-    t_base_step = elapsed_base / args.steps
-    # LoRA path time = step - step with an empty plan; when that difference
-    # is within run-to-run noise (the LoRA work hidden beside the base GEMM in
-    # the same launches) no rate is reported for it
-    t_lora = t_step - t_base_step
-    lora_hidden = t_lora <= 0.02 * t_step
-    lora_bytes = R_used * (w.d_in + w.d_out) * e + P * w.d_in * e + 8 * R_pairs
-    if mask is not None:
-        lora_bytes += P * w.d_in
-    lora_flops = 2.0 * R_pairs * (w.d_in + w.d_out)
-    base_flops = 2.0 * T * w.d_in * w.d_out
-    value = T * args.steps / elapsed
-    roofline = gemm_roofline(B, L, w, T, st_med, base_flops, P, R_pairs, R_used, e)
+    others = {}
+    for tok in [s for s in args.others.split(",") if s.strip()]:
+        i = int(tok)
+        if i == args.workload:
+            continue
+        wo = wl.config(i)
+        print(f"bench: workload {wo.name}", file=sys.stderr, flush=True)
+        r = measure(wo, args, torch, np, B, D, args.other_steps, max(5, args.warmup // 2),
+                    full=True)
+        r["roofline"] = r.pop("_roofline")
+        r.pop("_lf")
+        others[wo.name] = r
+        del wo
 
     out = {
         "metric": METRIC,
-        "value": value,
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -322,99 +464,36 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if L.dtype == B.LORA_BF16 else "f32",
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "T": T, "K": K, "d_in": w.d_in, "d_out": w.d_out,
+        "config": {"workload": w.name, "T": w.T, "K": w.K, "d_in": w.d_in, "d_out": w.d_out,
                    "adapters": w.n_adapters, "ranks": sorted(set(w.rank.tolist()))[:8],
-                   "active_pairs": P, "segments": S, "R_used": R_used, "R_pairs": R_pairs,
-                   "rotation_copies": R, "launch": "eager"},
+                   "step": head["step"], "launch": "eager",
+                   "rotation_copies": head["rotation_copies"]},
         "roofline": roofline,
-        "value_apply_only": T * args.steps / elapsed_apply,
-        **extra,
-        "stages_us_median": st_med,
-        "stages_us_mean": st_mean,
-        "stages_us_mean_empty_plan": sb_mean,
-        "step_us": t_step * 1e6,
-        "step_us_graph_replay": None if elapsed_graph is None else elapsed_graph / args.steps * 1e6,
-        "step_us_empty_plan": t_base_step * 1e6,
-        "lora_path": ({"t_us": t_lora * 1e6, "bytes": lora_bytes, "GB_s": None, "frac_hbm": None,
-                       "flops": lora_flops,
-                       "note": "step with LoRA within 2 % of the step with an empty plan: "
-                               "the LoRA work is hidden beside the base GEMM, no rate"}
-                      if lora_hidden else
-                      {"t_us": t_lora * 1e6, "bytes": lora_bytes, "GB_s": lora_bytes / t_lora / 1e9,
-                       "frac_hbm": lora_bytes / t_lora / 1e9 / HBM_PEAK_GBS, "flops": lora_flops}),
-        "layer": {"bytes": w_bytes + x_bytes + y_bytes + lora_bytes,
-                  "GB_s": (w_bytes + x_bytes + y_bytes + lora_bytes) / t_step / 1e9,
-                  "TFLOP_s": (base_flops + lora_flops) / t_step / 1e12,
-                  "frac_mfma": (base_flops + lora_flops) / t_step / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+        "value_forward": head["forward_tokens_per_s"],
+        "value_apply_only": head["apply_only_tokens_per_s"],
+        "lora_path": head["lora_path"],
+        "layer": {"bytes": layer_bytes, "GB_s": layer_bytes / t_step / 1e9,
+                  "TFLOP_s": (base_flops + head["lora_path"]["flops"]) / t_step / 1e12},
+        "headline": head,
+        "workloads": others,
     }
-
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
-def gemm_kernel_name(T, d_in, d_out, dtype_code, B, fused):
-    """The launch that runs the base GEMM inside lora_forward (the library's
-    shape rules: decode GEMM for T <= 128, with the per-slot shrink in the
-    same launch; fused-epilogue 256 x 256 tiles when they fill the GPU; else
-    256 x 128 stream-K tiles over 255 workgroups when there are at least 4
-    units each, with the plan built in the same launch)."""
-    if dtype_code != B.LORA_BF16:
-        return "gemm_f32_kernel (plan)"
-    if T <= 128:
-        return "decode_gemm_slot_kernel"
-    if fused:
-        return "gemm_tile_kernel (fused expand)"
-    units = ((T + 255) // 256) * ((d_out + 127) // 128) * (d_in // 64)
-    return "gemm_tile_plan_kernel" if units >= 4 * 255 else "gemm_tile_kernel"
-
-
-def gemm_roofline(B, L, w, T, st_med, base_flops, P, R_pairs, R_used, e):
-    """Roofline entry of the kernel that runs the base GEMM in the step, from
-    its measured duration.  When that launch also runs the per-slot shrink
-    (decode) its algorithmic bytes add the used A pages (each once), U and
-    the slot descriptors; when it builds the plan (stream-K), the plan's
-    inputs (ids, gates, the pool's rank and page tables)."""
-    fused = T > 128 and ((T + 255) // 256) * ((w.d_out + 255) // 256) >= 256
-    name = gemm_kernel_name(T, w.d_in, w.d_out, L.dtype, B, fused)
-    alg_bytes = (w.d_in * w.d_out + T * w.d_in) * e
-    flops = base_flops + (2.0 * R_pairs * w.d_out if fused else 0.0)
-    if name == "decode_gemm_slot_kernel":
-        t_us = st_med["fwd_gemm"]
-        alg_bytes += R_used * w.d_in * e + 4 * R_pairs + 16 * T * w.K
-        alg_bytes += T * w.d_in if L.keep_mask is not None else 0
-        flops += 2.0 * R_pairs * w.d_in
-    elif name in ("gemm_tile_plan_kernel", "gemm_f32_kernel (plan)"):
-        t_us = st_med["fwd_gemm"]
-        alg_bytes += 8 * T * w.K + 8 * w.n_adapters + 4 * R_used
-    else:
-        t_us = st_med["gemm"]
-    intensity = base_flops / ((w.d_in * w.d_out + T * w.d_in + T * w.d_out) * e)
-    t = t_us * 1e-6
-    if L.dtype != B.LORA_BF16:
-        r = {"bound": "alu", "achieved": flops / t / 1e12, "peak": FP32_PEAK_TFLOPS,
-             "unit": "TFLOP/s", "alg_flops_per_launch": flops}
-    elif intensity > RIDGE_FLOP_PER_BYTE:
-        r = {"bound": "mfma", "achieved": flops / t / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
-             "unit": "TFLOP/s", "alg_flops_per_launch": flops}
-    else:
-        r = {"bound": "hbm", "achieved": alg_bytes / t / 1e9, "peak": HBM_PEAK_GBS,
-             "unit": "GB/s", "alg_bytes_per_launch": alg_bytes}
-    r["frac"] = r["achieved"] / r["peak"]
-    r["traffic"] = measured_traffic(name, w.name)
-    r["kernel"] = name
-    r["avg_launch_us"] = t_us
-    return r
-
+# ---------------------------------------------------------------- counters
 
 def kernel_source_hash():
     import hashlib
     h = hashlib.sha256()
-    for f in ("gemm.hip", "shrink_units.h", "lora_internal.h", "plan_build.h"):
-        with open(os.path.join(ROOT, "lora_adapter_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    csrc = os.path.join(ROOT, "lora_adapter_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(fh.read())
     return h.hexdigest()[:16]
 
 
@@ -427,22 +506,35 @@ def measured_traffic(kernel, workload):
             table = json.load(fh)
     except (OSError, ValueError):
         return None
-    ent = table.get(kernel.split(" ")[0] + "|" + workload)
+    ent = table.get(kernel + "|" + workload)
     if not ent or ent.get("source_sha256_16") != kernel_source_hash():
         return None
     return ent.get("hbm_bytes_per_launch")
 
 
 COPY_PROBE_BYTES = 256 << 20
+KERNELS = ("decode_gemm_slot_kernel", "gemm_tile_plan_kernel", "decode_gemm_shrink_kernel",
+           "gemm_decode_kernel", "gemm_tile_kernel", "gemm_f32_kernel", "shrink_both_kernel",
+           "shrink_units_kernel", "shrink_tile_kernel", "epilogue_kernel", "plan_kernel",
+           "merge_mfma_kernel", "seg_outer_mfma_kernel", "seg_outer_reduce_kernel",
+           "g_reduce_kernel")
 
 
 def pmc_summary(workload_id, fetch_csv, write_csv):
-    """HBM bytes per launch of the base GEMM from FETCH_SIZE / WRITE_SIZE
-    (KiB per dispatch), each scaled by the copy probe's reading of the same
-    counter against the bytes that copy must move."""
+    """HBM bytes per launch of every library kernel in two rocprofv3 --pmc
+    runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by the
+    copy probe's reading of the same counter against the bytes that copy must
+    move."""
     import csv
     import numpy as np
     from lora_adapter_amd import workloads as wl
+
+    def name_of(k):
+        base = k.split("(")[0]
+        for n in KERNELS:
+            if n in base:
+                return n
+        return None
 
     def per_kernel(path, counter):
         vals = {}
@@ -454,73 +546,98 @@ def pmc_summary(workload_id, fetch_csv, write_csv):
         return vals
 
     w = wl.config(workload_id)
-    T = w.T
-    fused = T > 128 and ((T + 255) // 256) * ((w.d_out + 255) // 256) >= 256
-    kname = gemm_kernel_name(T, w.d_in, w.d_out, 1 if w.dtype == "bf16" else 0,
-                             type("B", (), {"LORA_BF16": 1}), fused).split(" ")[0]
-
-    def name_of(k):
-        for n in ("decode_gemm_slot_kernel", "gemm_tile_plan_kernel", "decode_gemm_shrink_kernel",
-                  "gemm_decode_kernel", "gemm_tile_kernel", "gemm_f32_kernel"):
-            if n in k:
-                return n
-        return None
-
-    out = {}
+    res = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         vals = per_kernel(path, counter)
         copy = [v for k, vs in vals.items() if "copyBuffer" in k for v in vs
                 if v > COPY_PROBE_BYTES / 2]
-        gemm = [v for k, vs in vals.items() if name_of(k) == kname for v in vs]
-        if not copy or not gemm:
-            raise SystemExit(f"{path}: no copy probe or GEMM dispatches for {counter}")
+        if not copy:
+            raise SystemExit(f"{path}: no copy probe dispatches for {counter}")
         scale = COPY_PROBE_BYTES / float(np.median(copy))
-        out[counter] = {"raw_bytes_median": float(np.median(gemm)), "copy_scale": scale,
-                        "bytes": float(np.median(gemm)) * scale, "dispatches": len(gemm)}
-    name = kname
+        for k, vs in vals.items():
+            n = name_of(k)
+            if n is None:
+                continue
+            res.setdefault(n, {})[counter] = {"raw_bytes_median": float(np.median(vs)),
+                                              "copy_scale": scale,
+                                              "bytes": float(np.median(vs)) * scale,
+                                              "dispatches": len(vs)}
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as fh:
             table = json.load(fh)
     except (OSError, ValueError):
         table = {}
-    table[name + "|" + w.name] = {
-        "hbm_bytes_per_launch": out["FETCH_SIZE"]["bytes"] + out["WRITE_SIZE"]["bytes"],
-        "fetch": out["FETCH_SIZE"], "write": out["WRITE_SIZE"],
-        "source_sha256_16": kernel_source_hash(),
-    }
+    for n, d in res.items():
+        if "FETCH_SIZE" not in d or "WRITE_SIZE" not in d:
+            continue
+        table[n + "|" + w.name] = {
+            "hbm_bytes_per_launch": d["FETCH_SIZE"]["bytes"] + d["WRITE_SIZE"]["bytes"],
+            "fetch": d["FETCH_SIZE"], "write": d["WRITE_SIZE"],
+            "source_sha256_16": kernel_source_hash(),
+        }
+        print(n, json.dumps(table[n + "|" + w.name]))
     with open(path, "w") as fh:
         json.dump(table, fh, indent=1, sort_keys=True)
-    print(json.dumps(table[name + "|" + w.name]))
+
+
+# ---------------------------------------------------------------- CPU oracle
+
+def host_info():
+    info = {"cpu_model": platform.processor() or "unknown", "numpy": None, "blas": None}
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    import numpy as np
+    info["numpy"] = np.__version__
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            info["blas"] = f"{blas[0].get('internal_api')} {blas[0].get('version')}"
+            info["blas_threads"] = int(blas[0].get("num_threads", 1))
+    except Exception:
+        pass
+    return info
 
 
 def cpu_baseline(w, seconds):
-    """The CPU oracle, untuned, on the same workload: plan + apply per step."""
+    """The CPU oracle, untuned, on a bounded sample of the same workload: the
+    plan, the forward and (when the workload trains) the gradients of a set
+    of token rows spread over the batch, repeated for about `seconds`."""
     import numpy as np
+    from lora_adapter_amd import workloads as wl
     from oracle import lora_oracle as O
+    info = host_info()
     try:
-        cores = len(os.sched_getaffinity(0))
+        affinity = len(os.sched_getaffinity(0))
     except AttributeError:
-        cores = os.cpu_count() or 1
-    threads = cores
-    try:
-        from threadpoolctl import threadpool_info
-        info = threadpool_info()
-        if info:
-            threads = max(int(i.get("num_threads", 1)) for i in info)
-    except Exception:
-        pass
+        affinity = os.cpu_count() or 1
+    n_rows = min(w.T, 256)
+    rows = np.linspace(0, w.T - 1, n_rows).round().astype(np.int64)
+    sw = wl.subset(w, rows) if n_rows < w.T else w
     n = 0
     t0 = time.perf_counter()
     while True:
-        O.plan_workload(w)
-        O.apply_workload(w)
+        O.plan_workload(sw)
+        O.apply_workload(sw)
+        if sw.dY is not None:
+            O.grad_workload(sw)
         n += 1
         el = time.perf_counter() - t0
         if el >= seconds or n >= 1000:
             break
-    return {"value": w.T * n / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} full steps (plan + apply, fp64 numpy) of the same workload in {el:.1f} s"}
+    what = "plan + forward + grads" if sw.dY is not None else "plan + forward"
+    return {"value": n_rows * n / el, "unit": "tokens/s",
+            "cores": info.get("blas_threads", affinity), "kind": "oracle",
+            "sample": f"{n} runs of the oracle's {what} (fp64 numpy) on {n_rows} token rows "
+                      f"spread evenly over the batch of {w.T}, {el:.1f} s",
+            "affinity_cpus": affinity, **info}
 
 
 if __name__ == "__main__":

@@ -25,7 +25,8 @@
  *
  * Conventions for every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller; the
- *     library never allocates, frees or synchronises, and keeps no state.
+ *     library never allocates or frees, keeps no state, and never
+ *     synchronises (lora_plan_header, a host-side reader, is the exception).
  *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
  *     asynchronously on it; buffers must outlive the enqueued work.
  *   - Host-visible argument errors return a status BEFORE any HIP call.
@@ -143,6 +144,15 @@ size_t lora_plan_bytes(int32_t T, int32_t K, int32_t n_adapters);
 int32_t lora_plan_layout(int32_t T, int32_t K, int32_t n_adapters, int64_t offsets_out[9]);
 int32_t lora_plan(const int32_t *ids, const float *gates, int32_t T, int32_t K,
                   const lora_pool_desc *pool, void *plan, size_t plan_bytes, void *stream);
+/* Copies the plan header (LORA_PLAN_HEADER_INTS int32 words: P, S, error
+ * bits, R_pairs, R_used, T, K, N, internal words) to host memory `out` once
+ * the work queued on `stream` before this call has finished.  The one entry
+ * point that waits: it enqueues a device-to-host copy on `stream` and
+ * synchronises that stream, so a host can size later buffers by R_pairs or
+ * read the device error bits.  `plan` is a device pointer to a plan buffer,
+ * `out` host memory of 16 int32 owned by the caller.
+ * Errors: INVALID_ARG (null plan or out), DEVICE (copy or sync failed). */
+int32_t lora_plan_header(const void *plan, int32_t *out, void *stream);
 
 /* ----------------------------------------------------------------- apply
  * Y = X.W + the LoRA term above ([S-LoRA] 批处理, [LoRAFusion]
@@ -227,9 +237,9 @@ int32_t lora_apply(const void *X, const void *W_t, void *Y, int32_t T, int32_t K
  * range, gate not 0, rank 1..LORA_MAX_RANK, consistent page_start, page ids
  * in range).  The per-slot shrink adds the same products in the same order
  * as the plan-driven shrink, so plan, U and Y equal those of lora_plan then
- * lora_apply bit for bit, except: on the decode path, when U does not fit
- * the workspace, the LoRA term is still added (from the per-slot U) and
- * LORA_DEVERR_CAPACITY is set, U is not stored.
+ * lora_apply bit for bit.  When U does not fit the workspace both paths
+ * behave alike: the LoRA term is skipped (Y is the base product), U is not
+ * stored and LORA_DEVERR_CAPACITY is set.
  *   Arguments as for lora_plan and lora_apply, on one stream.
  * Errors: those of lora_plan and lora_apply. */
 int32_t lora_forward_gemm(const int32_t *ids, const float *gates, int32_t T, int32_t K,

@@ -24,6 +24,7 @@ PH_PAIRS, PH_SEGS, PH_ERR, PH_RPAIRS, PH_RUSED, PH_T, PH_K, PH_N = range(8)
 
 EXPORTS = (
     "lora_abi_version", "lora_status_string", "lora_plan_bytes", "lora_plan_layout", "lora_plan",
+    "lora_plan_header",
     "lora_apply_workspace_bytes", "lora_apply_u_offset", "lora_shrink", "lora_base_expand",
     "lora_base_gemm", "lora_expand_epilogue", "lora_shrink_gemm", "lora_apply",
     "lora_forward_gemm", "lora_forward_finish", "lora_forward", "lora_merge_delta", "lora_grad_workspace_bytes", "lora_grad",
@@ -55,6 +56,7 @@ _PROTOS = {
     "lora_plan_bytes": (_SZ, [_I32, _I32, _I32]),
     "lora_plan_layout": (_I32, [_I32, _I32, _I32, ctypes.POINTER(_I64)]),
     "lora_plan": (_I32, [_VP, _VP, _I32, _I32, _PD, _VP, _SZ, _VP]),
+    "lora_plan_header": (_I32, [_VP, ctypes.POINTER(_I32), _VP]),
     "lora_apply_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "lora_apply_u_offset": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "lora_shrink": (_I32, [_VP, _VP, _F32, _I32, _I32, _VP, _PD, _VP, _VP, _SZ, _VP]),
@@ -150,6 +152,13 @@ def lora_plan_layout(T: int, K: int, n_adapters: int):
 def lora_plan(ids, gates, T: int, K: int, pool: Pool, plan, stream=None):
     _check("lora_plan", lib().lora_plan(_ptr(ids), _ptr(gates), T, K, pool.ref, _ptr(plan),
                                         plan.numel() * plan.element_size(), _stream(stream)))
+
+
+def lora_plan_header(plan, stream=None):
+    """The plan's 16 header words (waits for the work queued on the stream)."""
+    out = (_I32 * 16)()
+    _check("lora_plan_header", lib().lora_plan_header(_ptr(plan), out, _stream(stream)))
+    return [int(v) for v in out]
 
 
 def lora_apply_workspace_bytes(T: int, K: int, d_in: int, d_out: int, max_rank: int, dtype: int) -> int:

@@ -125,6 +125,16 @@ int32_t lora_plan(const int32_t *ids, const float *gates, int32_t T, int32_t K,
                          static_cast<hipStream_t>(stream)));
 }
 
+int32_t lora_plan_header(const void *plan, int32_t *out, void *stream) {
+  if (!plan || !out) return LORA_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  // the header is the plan buffer's first LORA_PLAN_HEADER_INTS words
+  if (hipMemcpyAsync(out, plan, LORA_PLAN_HEADER_INTS * sizeof(int32_t), hipMemcpyDeviceToHost,
+                     s) != hipSuccess)
+    return LORA_ERR_DEVICE;
+  return dev(hipStreamSynchronize(s));
+}
+
 size_t lora_apply_workspace_bytes(int32_t T, int32_t K, int32_t d_in, int32_t d_out,
                                   int32_t max_rank, int32_t dtype) {
   if (check_batch(T, K) != LORA_OK || !dims_ok(d_in) || !dims_ok(d_out)) return 0;
@@ -289,9 +299,10 @@ int32_t lora_apply(const void *X, const void *W_t, void *Y, int32_t T, int32_t K
 namespace {
 
 // lora_forward's two halves.  Split GEMM shapes only (gemm_plan_fusable):
-//   decode:   first = GEMM partials + per-slot shrink (U per slot and slot
-//             descriptors); finish = epilogue from those, with the plan
-//             built (and U stored in the u_off layout) in the same launch.
+//   decode:   first = the plan (built by workgroup 0), GEMM partials and the
+//             per-slot shrink (U per slot and slot descriptors), one launch;
+//             finish = epilogue from the partials, per-slot U and
+//             descriptors, which also stores U in the plan's u_off layout.
 //   stream-K: first = GEMM partials with the plan built in the same launch;
 //             finish = shrink, then epilogue.
 // Other shapes: first = lora_plan, finish = lora_apply.

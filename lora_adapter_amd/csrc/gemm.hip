@@ -1057,10 +1057,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float *X, const flo
 // order, add the expand, round once, store.  16-byte B-row loads, 1 KiB per
 // wave instruction.
 //
-// kPlan (lora_forward's decode path): the last row of workgroups is not an
-// output row; its first workgroup builds the plan (1: arrays in LDS, 2: in
-// the plan buffer) while the others add the expand from the per-slot U and
-// descriptors, which need no plan.
+// On lora_forward's decode path (a.sdesc set) the expand reads the per-slot U
+// and slot descriptors that the previous launch's per-slot shrink wrote, and
+// the first column chunk of each row also moves that row's U to the u_off
+// places of the plan the previous launch's workgroup 0 built.  As in
+// lora_apply, the LoRA term is skipped (and LORA_DEVERR_CAPACITY set) when the
+// plan's U does not fit the workspace.
 template <typename E, int NW>
 __global__ __launch_bounds__(NW * 64) void epilogue_kernel(EpilogueArgs a) {
   constexpr int CPL = 8;
@@ -1108,7 +1110,11 @@ __global__ __launch_bounds__(NW * 64) void epilogue_kernel(EpilogueArgs a) {
   const int col_raw = (cx * 64 + lane) * CPL;
   const bool col_ok = col_raw < a.N;
   const int col = col_ok ? col_raw : a.N - CPL;      // loads stay in bounds
-  const bool lora_on = a.sdesc ? a.ex.U != nullptr : expand_enabled(a.ex);
+  // decode forward: the same rule as expand_enabled, with the plan's R_pairs
+  // against the capacity of the packed U the plan layout is stored into
+  const bool lora_on = a.sdesc ? (a.ex.U != nullptr &&
+                                  (a.u_out == nullptr || int64_t(a.plan_hdr[LORA_PH_RPAIRS]) <= a.u_cap))
+                               : expand_enabled(a.ex);
   // the row's slot descriptors first: their round trip overlaps the partials'
   int4 sd = make_int4(-1, 0, 0, 0);
   if (lora_on) {

@@ -293,3 +293,17 @@ def small(i: int) -> Workload:
     if i == 5:
         return config(5, T=70, d_in=640, d_out=640, n_adapters=48, seed=105)
     raise ValueError(i)
+
+
+def subset(w: Workload, rows) -> Workload:
+    """The same layer (weights, pool, routing of the chosen tokens) restricted
+    to the token rows ``rows``, in that order: a bounded sample of a large
+    batch for timing the CPU oracle."""
+    rows = np.asarray(rows, dtype=np.int64)
+    take = lambda a: None if a is None else np.ascontiguousarray(a[rows])
+    return Workload(name=f"{w.name}-rows{len(rows)}", dtype=w.dtype, T=int(len(rows)), K=w.K,
+                    d_in=w.d_in, d_out=w.d_out, n_adapters=w.n_adapters, X=take(w.X), W_t=w.W_t,
+                    rank=w.rank, scale=w.scale, page_start=w.page_start, page_ids=w.page_ids,
+                    a_pages=w.a_pages, b_pages=w.b_pages, ids=take(w.ids), gates=take(w.gates),
+                    keep_mask=take(w.keep_mask), keep_scale=w.keep_scale, dY=take(w.dY),
+                    merge_ids=w.merge_ids, merge_coeffs=w.merge_coeffs, meta=dict(w.meta))

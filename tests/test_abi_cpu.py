@@ -106,6 +106,10 @@ def test_argument_errors_return_before_any_hip_call(B):
     assert L.lora_merge_delta(8, ref, 8, 8, -1, None) == INV
     assert L.lora_merge_delta(None, ref, 8, 8, 1, None) == INV
     assert L.lora_merge_delta(8, ref, None, None, 0, None) == 0
+    # plan header reader: null plan or output
+    out = (ctypes.c_int32 * 16)()
+    assert L.lora_plan_header(None, out, None) == INV
+    assert L.lora_plan_header(8, None, None) == INV
     # grad: bad max_rank, too-small workspace
     assert L.lora_grad(8, None, 1.0, 8, 4, 1, 8, ref, 8, 8, 1 << 20, 8, 8, 0, 8, 1 << 30, None) == INV
     assert L.lora_grad(8, None, 1.0, 8, 4, 1, 8, ref, 8, 8, 1 << 20, 8, 8, 16, 8, 16, None) == CAP

@@ -430,6 +430,37 @@ def test_u_capacity_error_skips_lora_and_flags():
     assert rel_err(base, ref) <= TOL["bf16"]
 
 
+def test_u_capacity_error_through_forward_decode():
+    """lora_forward on a decode shape (per-slot shrink in the GEMM launch)
+    follows lora_apply's rule when U does not fit the workspace: the LoRA term
+    is skipped, so Y is the base product, and the error bit is set."""
+    w = small(2)
+    L = D.DeviceLayer(w, max_rank=1)
+    B.lora_forward(L.ids, L.gates, L.T, L.K, L.X, L.W_t, L.Y, L.keep_mask, L.keep_scale, L.pool,
+                   L.plan, L.ws)
+    torch.cuda.synchronize()
+    h = B.lora_plan_header(L.plan)
+    assert h[B.PH_ERR] & B.DEVERR_CAPACITY
+    Yf = L.Y_host().copy()
+    L2 = D.DeviceLayer(w, max_rank=1)
+    L2.run_plan()
+    L2.run_apply()
+    torch.cuda.synchronize()
+    assert np.array_equal(Yf, L2.Y_host())
+    ref = D.as_f64(w.X) @ D.as_f64(w.W_t).T
+    assert rel_err(D.as_f64(Yf), ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("cfg", [2, 5])
+def test_plan_header_reader_matches_oracle(cfg):
+    w = small(cfg)
+    L = D.DeviceLayer(w)
+    L.run_plan()
+    h = B.lora_plan_header(L.plan)          # waits for the plan on the stream
+    ref = O.plan_workload(w)["header"]
+    assert h[:8] == [int(v) for v in ref[:8]]
+
+
 # ---------------------------------------------------------------- merge
 
 def _ulp_bf16(x):
