@@ -255,6 +255,33 @@ int32_t lora_forward(const int32_t *ids, const float *gates, int32_t T, int32_t 
                      float keep_scale, const lora_pool_desc *pool, void *plan, size_t plan_bytes,
                      void *ws, size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------- forward, no allocation
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * lora_forward (same arguments, same kernels, same results bit for bit) with
+ * its plan and workspace in a device array the library owns:
+ * LORA_NOALLOC_SCRATCH_BYTES per GPU, taken on the first call on that GPU and
+ * held until the process ends.  Nothing is allocated or freed by the call.
+ *   The caller passes inputs and outputs only; max_rank bounds the rank of
+ *   every adapter the batch uses (it sizes U, as in
+ *   lora_apply_workspace_bytes).  The stream must belong to the current
+ *   device.  Every call on one GPU shares that GPU's array, which keeps the
+ *   last call's plan and U: calls that overlap on one GPU (on different
+ *   streams, or from different host threads) race, and must be ordered by
+ *   the caller.  Each call rebuilds everything it reads from the array.
+ *   lora_forward_noalloc_bytes gives the array bytes a batch needs (0 for
+ *   invalid sizes).
+ * Errors: INVALID_ARG (as lora_forward, or max_rank outside 0..LORA_MAX_RANK),
+ * CAPACITY (the batch needs more than LORA_NOALLOC_SCRATCH_BYTES: use
+ * lora_forward with caller-owned buffers), UNSUPPORTED, DEVICE. */
+#define LORA_NOALLOC_SCRATCH_BYTES (64u << 20)
+size_t lora_forward_noalloc_bytes(int32_t T, int32_t K, int32_t n_adapters, int32_t d_in,
+                                  int32_t d_out, int32_t max_rank, int32_t dtype);
+int32_t lora_forward_noalloc(const int32_t *ids, const float *gates, int32_t T, int32_t K,
+                             const void *X, const void *W_t, void *Y, const uint8_t *keep_mask,
+                             float keep_scale, const lora_pool_desc *pool, int32_t max_rank,
+                             void *stream);
+
 /* ----------------------------------------------------------------- merge
  * In place: W_t <- round( W_t + sum_i coeffs[i] . s_{a_i} . (A_{a_i} . B_{a_i})^T )
  * with the delta summed in float32 and one rounding per element.  One adapter

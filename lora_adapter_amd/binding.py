@@ -27,7 +27,8 @@ EXPORTS = (
     "lora_plan_header",
     "lora_apply_workspace_bytes", "lora_apply_u_offset", "lora_shrink", "lora_base_expand",
     "lora_base_gemm", "lora_expand_epilogue", "lora_shrink_gemm", "lora_apply",
-    "lora_forward_gemm", "lora_forward_finish", "lora_forward", "lora_merge_delta", "lora_grad_workspace_bytes", "lora_grad",
+    "lora_forward_gemm", "lora_forward_finish", "lora_forward", "lora_forward_noalloc_bytes",
+    "lora_forward_noalloc", "lora_merge_delta", "lora_grad_workspace_bytes", "lora_grad",
 )
 
 
@@ -71,6 +72,9 @@ _PROTOS = {
                                    _VP, _SZ, _VP]),
     "lora_forward": (_I32, [_VP, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _F32, _PD, _VP, _SZ, _VP,
                             _SZ, _VP]),
+    "lora_forward_noalloc_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "lora_forward_noalloc": (_I32, [_VP, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _F32, _PD, _I32,
+                                    _VP]),
     "lora_merge_delta": (_I32, [_VP, _PD, _VP, _VP, _I32, _VP]),
     "lora_grad_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "lora_grad": (_I32, [_VP, _VP, _F32, _VP, _I32, _I32, _VP, _PD, _VP, _VP, _SZ, _VP, _VP,
@@ -232,6 +236,18 @@ def lora_forward(ids, gates, T: int, K: int, X, W_t, Y, keep_mask, keep_scale: f
                  plan, ws, stream=None):
     _forward_call("lora_forward", ids, gates, T, K, X, W_t, Y, keep_mask, keep_scale, pool, plan,
                   ws, stream)
+
+
+def lora_forward_noalloc_bytes(T: int, K: int, n_adapters: int, d_in: int, d_out: int,
+                               max_rank: int, dtype: int) -> int:
+    return int(lib().lora_forward_noalloc_bytes(T, K, n_adapters, d_in, d_out, max_rank, dtype))
+
+
+def lora_forward_noalloc(ids, gates, T: int, K: int, X, W_t, Y, keep_mask, keep_scale: float,
+                         pool: Pool, max_rank: int, stream=None):
+    _check("lora_forward_noalloc", lib().lora_forward_noalloc(
+        _ptr(ids), _ptr(gates), T, K, _ptr(X), _ptr(W_t), _ptr(Y), _ptr(keep_mask),
+        float(keep_scale), pool.ref, int(max_rank), _stream(stream)))
 
 
 def lora_merge_delta(W_t, pool: Pool, merge_ids, coeffs, m: int, stream=None):

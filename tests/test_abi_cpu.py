@@ -110,6 +110,12 @@ def test_argument_errors_return_before_any_hip_call(B):
     out = (ctypes.c_int32 * 16)()
     assert L.lora_plan_header(None, out, None) == INV
     assert L.lora_plan_header(8, None, None) == INV
+    # forward without allocation: bad max_rank, a batch beyond the library's
+    # array (both rejected before any HIP call)
+    assert L.lora_forward_noalloc(8, 8, 4, 1, 8, 8, 24, None, 1.0, ref, 2000, None) == INV
+    assert L.lora_forward_noalloc(8, 8, 8192, 8, 8, 8, 24, None, 1.0, ref, 1024, None) == CAP
+    assert L.lora_forward_noalloc(8, 8, 4, 1, 8, 8, 24, None, 1.0, None, 16, None) == INV
+    assert B.lora_forward_noalloc_bytes(64, 1, 64, 4096, 4096, 16, B.LORA_BF16) <= 64 << 20
     # grad: bad max_rank, too-small workspace
     assert L.lora_grad(8, None, 1.0, 8, 4, 1, 8, ref, 8, 8, 1 << 20, 8, 8, 0, 8, 1 << 30, None) == INV
     assert L.lora_grad(8, None, 1.0, 8, 4, 1, 8, ref, 8, 8, 1 << 20, 8, 8, 16, 8, 16, None) == CAP
