@@ -41,7 +41,8 @@ Readings where the pages are silent (the plainest one the rest supports):
   * Plan order: active (token, slot) pairs sorted by (rank bucket, adapter,
     token, slot); bucket(r) = smallest b in 0..7 with r <= 2^b, else 8.
   * Gradients (the pages give none; only A and B train, [LoRAFusion]) are the
-    derivatives of <dY, Y> with respect to A_a and B_a.
+    derivatives of <dY, Y> with respect to A_a and B_a, and, for the layer
+    below, with respect to X.
 """
 from __future__ import annotations
 
@@ -265,6 +266,41 @@ def grad(X, keep_mask, keep_scale, dY, rank, scale, page_start, page_ids, a_page
     return {a: (v[0], v[1]) for a, v in out.items()}
 
 
+def grad_x(X, keep_mask, keep_scale, dY, W_t, rank, scale, page_start, page_ids, a_pages,
+           b_pages, ids, gates) -> np.ndarray:
+    """Gradient of L = <dY, Y> with respect to the layer input X, float64,
+    unrounded: the input gradient a fine-tune backward hands to the layer
+    below ([LoRAFusion] 解决什么真问题: W frozen, A and B trained, dropout on
+    the LoRA branch).  The pages give no formula; differentiating the forward
+    above, per token t:
+        dX_t = dY_t.W^T  +  sum over t's active slots of  c . kappa . m_t * ((dY_t.B_a^T).A_a^T)
+    with W^T = W_t (stored [d_out][d_in]) and m_t the keep mask row (the base
+    path sees X itself, so the mask and kappa touch only the LoRA term)."""
+    ids = np.asarray(ids, dtype=np.int32)
+    T, K = ids.shape
+    n_pages = a_pages.shape[0]
+    act, _ = _classify(ids, gates, rank, page_start, page_ids, n_pages)
+    g64 = np.asarray(gates, dtype=np.float32).astype(np.float64).reshape(T, K)
+    s64 = np.asarray(scale, dtype=np.float32).astype(np.float64)
+    kappa = float(np.float32(keep_scale))
+    dY64 = widen(dY)
+    dX = dY64 @ widen(W_t)                    # (T x d_out) . (d_out x d_in)
+    cache = {}
+    for t in range(T):
+        for k in range(K):
+            a = act[t * K + k]
+            if a < 0:
+                continue
+            if a not in cache:
+                cache[a] = factors(a, rank, page_start, page_ids, a_pages, b_pages)
+            A, B = cache[a]
+            v = (g64[t, k] * s64[a]) * ((dY64[t] @ B.T) @ A.T)
+            if keep_mask is not None:
+                v = v * np.asarray(keep_mask[t], dtype=np.float64) * kappa
+            dX[t] += v
+    return dX
+
+
 def grad_pages(grads: dict, rank, page_start, page_ids, n_pages, d_in, d_out):
     """Scatter per-adapter gradients into the pool's page layout; pages of
     adapters without gradients are NaN (the kernel leaves them untouched)."""
@@ -296,3 +332,8 @@ def merge_workload(w, W_t=None, ids=None, coeffs=None):
 def grad_workload(w):
     return grad(w.X, w.keep_mask, w.keep_scale, w.dY, w.rank, w.scale, w.page_start, w.page_ids,
                 w.a_pages, w.b_pages, w.ids, w.gates)
+
+
+def grad_x_workload(w):
+    return grad_x(w.X, w.keep_mask, w.keep_scale, w.dY, w.W_t, w.rank, w.scale, w.page_start,
+                  w.page_ids, w.a_pages, w.b_pages, w.ids, w.gates)

@@ -11,7 +11,11 @@ fix, never against the oracle's own formulas retyped.
     the fused switch equals unmerge-then-merge;
   * gradients: <dY, Y> is linear in A for fixed B (and vice versa), so a
     finite difference along a random direction is exact up to rounding; and
-    CPU torch.autograd in float64 on the dense form of the layer.
+    CPU torch.autograd in float64 on the dense form of the layer;
+  * the input gradient dX: <dY, Y> is linear in X (mask fixed), so the same
+    directional difference pins it through the forward; torch.autograd; one
+    adapter for every token gives dY times the merged weight's transpose;
+    inactive rows give dY.W^T exactly.
 """
 import json
 import os
@@ -299,6 +303,15 @@ def _loss(w, a_pages, b_pages):
     return float(np.sum(Y * wl.to_f32(w.dY).astype(np.float64)))
 
 
+def test_golden_grad_x():
+    g = _gold()
+    a = _gold_arrays(g)
+    dY = np.asarray(g["dY"], dtype=np.float32)
+    dX = O.grad_x(a["X"], None, 1.0, dY, a["W_t"], a["rank"], a["scale"], a["page_start"],
+                  a["page_ids"], a["a_pages"], a["b_pages"], a["ids"], a["gates"])
+    np.testing.assert_array_equal(dX, np.asarray(g["expected_dX"], dtype=np.float64))
+
+
 def _f64_pool(w):
     w64 = type("W", (), {})()
     for k in ("X", "W_t", "rank", "scale", "page_start", "page_ids", "ids", "gates", "keep_mask",
@@ -360,6 +373,88 @@ def test_grad_matches_torch_autograd():
     for a, (dA, dB) in g.items():
         np.testing.assert_allclose(dA, Af[a].grad.numpy(), rtol=1e-10, atol=1e-9)
         np.testing.assert_allclose(dB, Bf[a].grad.numpy(), rtol=1e-10, atol=1e-9)
+
+
+def _loss_x(w, X64):
+    """<dY, Y> through the (separately pinned) forward, with X replaced."""
+    Y = O.apply(X64, w.W_t, w.rank, w.scale, w.page_start, w.page_ids, w.a_pages, w.b_pages,
+                w.ids, w.gates, w.keep_mask, w.keep_scale)
+    return float(np.sum(Y * wl.to_f32(w.dY).astype(np.float64)))
+
+
+@pytest.mark.parametrize("cfg", [4, 5])
+def test_grad_x_by_directional_difference(cfg):
+    """<dY, Y> is linear in X for a fixed mask: its central difference along a
+    random direction V equals <dX, V> up to rounding."""
+    w = wl.config(4, T=40, d_in=64, d_out=48, seed=43) if cfg == 4 else \
+        wl.config(5, T=24, d_in=64, d_out=64, n_adapters=10, seed=44)
+    if w.dY is None:
+        w.dY = wl.f32_to_bf16_bits(np.random.default_rng(7).standard_normal((w.T, w.d_out))
+                                   .astype(np.float32))
+    dX = O.grad_x_workload(w)
+    X0 = wl.to_f32(w.X).astype(np.float64)
+    V = np.random.default_rng(9).standard_normal(X0.shape)
+    fd = (_loss_x(w, X0 + V) - _loss_x(w, X0 - V)) / 2.0
+    an = float(np.sum(dX * V))
+    assert abs(fd - an) <= 1e-9 * max(1.0, abs(an))
+
+
+def test_grad_x_matches_torch_autograd():
+    torch = pytest.importorskip("torch")
+    w = wl.small(4)
+    dXo = O.grad_x_workload(w)
+    X = torch.tensor(wl.to_f32(w.X), dtype=torch.float64, requires_grad=True)
+    M = torch.tensor(w.keep_mask, dtype=torch.float64) * float(np.float32(w.keep_scale))
+    dY = torch.tensor(wl.to_f32(w.dY), dtype=torch.float64)
+    Wd = torch.tensor(wl.to_f32(w.W_t), dtype=torch.float64).T
+    Y = X @ Wd
+    rows = []
+    for t in range(w.T):
+        extra = torch.zeros(w.d_out, dtype=torch.float64)
+        for k in range(w.K):
+            a = int(w.ids[t, k])
+            if a < 0 or w.gates[t, k] == 0:
+                continue
+            A, B = _dense_factors_by_indexing(w, a)
+            c = float(w.gates[t, k]) * float(w.scale[a])
+            extra = extra + c * ((X[t] * M[t]) @ torch.tensor(A)) @ torch.tensor(B)
+        rows.append(extra)
+    Y = Y + torch.stack(rows)
+    (Y * dY).sum().backward()
+    np.testing.assert_allclose(dXo, X.grad.numpy(), rtol=1e-10, atol=1e-9)
+
+
+@pytest.mark.parametrize("cfg", [1, 3, 5])
+def test_grad_x_single_adapter_equals_merged_weight(cfg):
+    """All tokens on one adapter with gate g and no mask: dX = dY.(W + g.s.A.B)^T,
+    with the merged weight from the oracle's merge (pinned on its own)."""
+    w = wl.small(cfg)
+    a = int(np.argmax(w.rank))
+    gval = np.float32(-1.25)
+    ids = np.full((w.T, w.K), -1, dtype=np.int32)
+    ids[:, 0] = a
+    gates = np.zeros((w.T, w.K), dtype=np.float32)
+    gates[:, 0] = gval
+    dY = np.random.default_rng(3).standard_normal((w.T, w.d_out)).astype(np.float32)
+    dX = O.grad_x(w.X, None, 1.0, dY, w.W_t, w.rank, w.scale, w.page_start, w.page_ids,
+                  w.a_pages, w.b_pages, ids, gates)
+    Wm_t = O.merge(w.W_t, w.rank, w.scale, w.page_start, w.page_ids, w.a_pages, w.b_pages,
+                   np.array([a]), np.array([gval]))
+    ref = dY.astype(np.float64) @ Wm_t
+    assert np.max(np.abs(dX - ref)) <= 1e-10 * np.max(np.abs(ref))
+
+
+def test_grad_x_inactive_rows_equal_base_exactly():
+    w = wl.small(4)
+    ids = w.ids.copy(); gates = w.gates.copy()
+    ids[0, 0] = -1
+    gates[1, 0] = 0.0
+    dX = O.grad_x(w.X, w.keep_mask, w.keep_scale, w.dY, w.W_t, w.rank, w.scale, w.page_start,
+                  w.page_ids, w.a_pages, w.b_pages, ids, gates)
+    base = wl.to_f32(w.dY).astype(np.float64) @ wl.to_f32(w.W_t).astype(np.float64)
+    for t in (0, 1):
+        assert np.array_equal(dX[t], base[t])
+    assert not np.array_equal(dX[2], base[2])
 
 
 # ---------------------------------------------------------------- generator
