@@ -316,6 +316,39 @@ int32_t lora_grad(const void *X, const uint8_t *keep_mask, float keep_scale, con
                   float *dA_pages, float *dB_pages, int32_t max_rank, void *ws,
                   size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------------------ grad of X
+ * Input gradient of the fine-tune backward, handed to the layer below
+ * ([LoRAFusion] 解决什么真问题: W frozen, A and B trained, dropout on the LoRA
+ * branch; the pages give no backward formula, this is the derivative of
+ * <dY, Y> for the forward above):
+ *   dX[t][i] = round( sum_n dY[t][n] . W[i][n]
+ *                     + m[t][i] . sum_{p of t} sum_j G[u_off[p]+j] . A_a[i][j] )
+ * with G[u_off[p]+j] = g . s_a . kappa . (dY_t . B_a[j]), which lora_grad
+ * leaves at the start of its workspace (call lora_grad on the same batch
+ * first; dX reads G from grad_ws).
+ *   dY [T][d_out] dtype; W [d_in][d_out] dtype: the frozen weight in its
+ *   mathematical orientation, i.e. W_t transposed once by lora_transpose (the
+ *   product runs along d_out, and the GEMM reads both operands along it);
+ *   keep_mask [T][d_in] uint8 0/1 or NULL (the mask the forward used; its
+ *   scale is already in G); plan as for the forward; max_rank as given to
+ *   lora_grad; dX [T][d_in] dtype, must not alias dY or W;
+ *   ws >= lora_grad_x_workspace_bytes(T, d_in, d_out, dtype) (fp32 partial
+ *   products of dY . W^T).
+ * Rows whose slots are all inactive equal dY . W^T (rounded once) exactly.
+ * Errors: INVALID_ARG, UNSUPPORTED, CAPACITY (grad_ws smaller than
+ * lora_grad_workspace_bytes for these sizes, or ws too small), DEVICE. */
+size_t lora_grad_x_workspace_bytes(int32_t T, int32_t d_in, int32_t d_out, int32_t dtype);
+int32_t lora_grad_x(const void *dY, const void *W, const uint8_t *keep_mask, int32_t T, int32_t K,
+                    const lora_pool_desc *pool, const void *plan, const void *grad_ws,
+                    size_t grad_ws_bytes, int32_t max_rank, void *dX, void *ws, size_t ws_bytes,
+                    void *stream);
+/* dst[c][r] = src[r][c] for a rows x cols row-major matrix of dtype (device
+ * pointers, dst of cols x rows, not overlapping src).  Used once per frozen
+ * weight to give lora_grad_x its W from W_t (rows = d_out, cols = d_in).
+ * Errors: INVALID_ARG (null, aliasing, negative sizes, bad dtype), DEVICE. */
+int32_t lora_transpose(const void *src, void *dst, int32_t rows, int32_t cols, int32_t dtype,
+                       void *stream);
+
 #ifdef __cplusplus
 }
 #endif

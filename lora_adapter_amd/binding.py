@@ -29,6 +29,7 @@ EXPORTS = (
     "lora_base_gemm", "lora_expand_epilogue", "lora_shrink_gemm", "lora_apply",
     "lora_forward_gemm", "lora_forward_finish", "lora_forward", "lora_forward_noalloc_bytes",
     "lora_forward_noalloc", "lora_merge_delta", "lora_grad_workspace_bytes", "lora_grad",
+    "lora_grad_x_workspace_bytes", "lora_grad_x", "lora_transpose",
 )
 
 
@@ -79,6 +80,10 @@ _PROTOS = {
     "lora_grad_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "lora_grad": (_I32, [_VP, _VP, _F32, _VP, _I32, _I32, _VP, _PD, _VP, _VP, _SZ, _VP, _VP,
                          _I32, _VP, _SZ, _VP]),
+    "lora_grad_x_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+    "lora_grad_x": (_I32, [_VP, _VP, _VP, _I32, _I32, _PD, _VP, _VP, _SZ, _I32, _VP, _VP, _SZ,
+                           _VP]),
+    "lora_transpose": (_I32, [_VP, _VP, _I32, _I32, _I32, _VP]),
 }
 
 
@@ -267,3 +272,20 @@ def lora_grad(X, keep_mask, keep_scale: float, dY, T: int, K: int, gates, pool: 
                                         apply_ws.numel() * apply_ws.element_size(), _ptr(dA_pages),
                                         _ptr(dB_pages), max_rank, _ptr(ws),
                                         ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def lora_grad_x_workspace_bytes(T: int, d_in: int, d_out: int, dtype: int) -> int:
+    return int(lib().lora_grad_x_workspace_bytes(T, d_in, d_out, dtype))
+
+
+def lora_grad_x(dY, W, keep_mask, T: int, K: int, pool: Pool, plan, grad_ws, max_rank: int, dX,
+                ws, stream=None):
+    _check("lora_grad_x", lib().lora_grad_x(
+        _ptr(dY), _ptr(W), _ptr(keep_mask), T, K, pool.ref, _ptr(plan), _ptr(grad_ws),
+        grad_ws.numel() * grad_ws.element_size(), int(max_rank), _ptr(dX), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def lora_transpose(src, dst, rows: int, cols: int, dtype: int, stream=None):
+    _check("lora_transpose", lib().lora_transpose(_ptr(src), _ptr(dst), rows, cols, dtype,
+                                                  _stream(stream)))

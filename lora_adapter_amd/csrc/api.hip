@@ -518,3 +518,73 @@ int32_t lora_grad(const void *X, const uint8_t *keep_mask, float keep_scale, con
 }
 
 }  // extern "C"
+
+namespace {
+
+// dX GEMM: dY [T][d_out] times W [d_in][d_out] along d_out, into fp32 partials
+// (the epilogue adds the masked LoRA term before the one rounding).
+GemmConfig grad_x_config(int32_t T, int32_t d_in, int32_t d_out, int32_t dtype) {
+  GemmConfig c = choose_gemm(T > 0 ? T : 1, d_out, d_in, dtype);
+  c.fused = false;   // 256 x 256 tiles write their one partial slot
+  return c;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t lora_transpose(const void *src, void *dst, int32_t rows, int32_t cols, int32_t dtype,
+                       void *stream) {
+  if (!src || !dst || src == dst || rows < 0 || cols < 0) return LORA_ERR_INVALID_ARG;
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_INVALID_ARG;
+  if (rows == 0 || cols == 0) return LORA_OK;
+  return dev(launch_transpose(src, dst, rows, cols, dtype, static_cast<hipStream_t>(stream)));
+}
+
+size_t lora_grad_x_workspace_bytes(int32_t T, int32_t d_in, int32_t d_out, int32_t dtype) {
+  if (T < 0 || !dims_ok(d_in) || !dims_ok(d_out)) return 0;
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return 0;
+  const GemmConfig c = grad_x_config(T, d_in, d_out, dtype);
+  const size_t b = gemm_partial_bytes(c, T, d_in);
+  return align_up(b > 0 ? b : 1);
+}
+
+int32_t lora_grad_x(const void *dY, const void *W, const uint8_t *keep_mask, int32_t T, int32_t K,
+                    const lora_pool_desc *pool, const void *plan, const void *grad_ws,
+                    size_t grad_ws_bytes, int32_t max_rank, void *dX, void *ws, size_t ws_bytes,
+                    void *stream) {
+  int32_t st = check_batch(T, K);
+  if (st != LORA_OK) return st;
+  if ((st = check_pool(pool, true)) != LORA_OK) return st;
+  if (!plan || max_rank < 1 || max_rank > LORA_MAX_RANK) return LORA_ERR_INVALID_ARG;
+  if (T == 0) return LORA_OK;
+  if (!dY || !W || !grad_ws || !dX || !ws) return LORA_ERR_INVALID_ARG;
+  if (dX == dY || dX == W) return LORA_ERR_INVALID_ARG;
+  if (grad_ws_bytes < lora_grad_workspace_bytes(T, K, pool->n_adapters, pool->d_in, pool->d_out,
+                                                max_rank, pool->dtype))
+    return LORA_ERR_CAPACITY;
+  if (ws_bytes < lora_grad_x_workspace_bytes(T, pool->d_in, pool->d_out, pool->dtype))
+    return LORA_ERR_CAPACITY;
+  const int64_t TK = int64_t(T) * K;
+  const PlanView pv = plan_view(plan, TK, pool->n_adapters);
+  const GemmConfig c = grad_x_config(T, pool->d_in, pool->d_out, pool->dtype);
+  GemmArgs g{};
+  g.X = dY; g.W = W; g.M = T; g.N = pool->d_in; g.Kd = pool->d_out;
+  g.k_split = c.k_split;
+  g.sk_g = c.sk;
+  g.partial = static_cast<float *>(ws);
+  g.Y = dX;
+  // the expand of the epilogue, on G (lora_grad's workspace starts with it,
+  // packed like U) and the A pages, rows of d_in
+  g.ex.K = K;
+  g.ex.slot_desc = pv.slot_desc; g.ex.pair_tk = pv.pair_tk; g.ex.page_ids = pool->page_ids;
+  g.ex.b_pages = pool->a_pages; g.ex.d_out = pool->d_in;
+  g.ex.U = static_cast<const float *>(grad_ws); g.ex.hdr = pv.hdr;
+  g.ex.u_cap = TK * max_rank;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_base_gemm(c, g, s);
+  if (e == hipSuccess) e = launch_grad_x_epilogue(c, g, pool->dtype, keep_mask, s);
+  return dev(e);
+}
+
+}  // extern "C"

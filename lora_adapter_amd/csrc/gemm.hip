@@ -1063,7 +1063,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float *X, const flo
 // places of the plan the previous launch's workgroup 0 built.  As in
 // lora_apply, the LoRA term is skipped (and LORA_DEVERR_CAPACITY set) when the
 // plan's U does not fit the workspace.
-template <typename E, int NW>
+template <typename E, int NW, bool kMask = false>
 __global__ __launch_bounds__(NW * 64) void epilogue_kernel(EpilogueArgs a) {
   constexpr int CPL = 8;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1153,7 +1153,23 @@ __global__ __launch_bounds__(NW * 64) void epilogue_kernel(EpilogueArgs a) {
       }
     }
   }
-  if (lora_on) expand_row8<E>(v, sd, col, a.ex);
+  if (lora_on) {
+    if constexpr (kMask) {
+      // the expand term alone, then times the row's keep-mask bytes
+      float l[CPL];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) l[c] = 0.f;
+      expand_row8<E>(l, sd, col, a.ex);
+      const uint2 mw = *reinterpret_cast<const uint2 *>(a.mask + int64_t(row) * a.N + col);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const uint32_t word = c < 4 ? mw.x : mw.y;
+        v[c] += float((word >> (8 * (c & 3))) & 0xffu) * l[c];
+      }
+    } else {
+      expand_row8<E>(v, sd, col, a.ex);
+    }
+  }
   if (col_ok) Cols<E, CPL>::store(static_cast<E *>(a.Y) + int64_t(row) * a.N + col, v);
   if (do_copy) {
     // this row's per-slot U to the places the plan gave its active slots
@@ -1373,6 +1389,20 @@ static hipError_t launch_epilogue_rows(const EpilogueArgs &e, const GemmArgs &g,
     if (dtype == LORA_BF16) hipLaunchKernelGGL((epilogue_kernel<uint16_t, 4>), grid, dim3(256), 0, s, e);
     else hipLaunchKernelGGL((epilogue_kernel<float, 4>), grid, dim3(256), 0, s, e);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_x_epilogue(const GemmConfig &c, const GemmArgs &g, int dtype,
+                                  const uint8_t *mask, hipStream_t s) {
+  if (c.fused) return hipErrorInvalidConfiguration;
+  EpilogueArgs e{g.partial, c.splits, g.M, g.N, c.sk, g.Kd / 64, c.bm, c.bn, g.Y, g.ex, nullptr,
+                 nullptr, 0, 0};
+  if (mask == nullptr) return launch_epilogue_rows(e, g, dtype, s);
+  e.mask = mask;
+  const unsigned n_x = unsigned((g.N + 511) / 512);
+  const dim3 grid(n_x, unsigned((g.M + 3) / 4));
+  if (dtype == LORA_BF16) hipLaunchKernelGGL((epilogue_kernel<uint16_t, 4, true>), grid, dim3(256), 0, s, e);
+  else hipLaunchKernelGGL((epilogue_kernel<float, 4, true>), grid, dim3(256), 0, s, e);
   return hipGetLastError();
 }
 

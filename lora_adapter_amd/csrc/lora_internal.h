@@ -275,6 +275,9 @@ struct EpilogueArgs {
   float *u_out;
   int64_t u_cap;
   int slot_stride;
+  // not null (input gradient dX): the expand term (G . A pages) is multiplied
+  // element-wise by this [M][N] 0/1 keep mask before it is added
+  const uint8_t *mask;
 };
 
 struct MergeArgs {
@@ -409,6 +412,14 @@ hipError_t launch_epilogue_ucopy(const GemmConfig &c, const GemmArgs &g, int dty
 // The MFMA shrink of the big segments alone (no-op unless enabled).
 hipError_t launch_shrink_big(const ShrinkArgs &a, int dtype, int64_t TK, int64_t n_adapters,
                              int d_in, int d_out, hipStream_t s);
+
+// Input gradient: the epilogue of the dX GEMM (dY . W^T as split partials),
+// with the expand term from G and the A pages times the keep mask (if any).
+hipError_t launch_grad_x_epilogue(const GemmConfig &c, const GemmArgs &g, int dtype,
+                                  const uint8_t *mask, hipStream_t s);
+// dst[c][r] = src[r][c] for a rows x cols matrix of the dtype.
+hipError_t launch_transpose(const void *src, void *dst, int rows, int cols, int dtype,
+                            hipStream_t s);
 
 hipError_t launch_merge(const MergeArgs &a, int dtype, hipStream_t s);
 int64_t grad_pieces(int64_t TK, int64_t n_adapters);

@@ -104,6 +104,24 @@ class DeviceLayer:
         B.lora_grad(self.X, self.keep_mask, self.keep_scale, self.dY, self.T, self.K,
                     self.gates, self.pool, self.plan, self.ws, dA, dB, self.max_rank, gws, stream)
 
+    def weight_transposed(self, stream=None):
+        """W [d_in][d_out] (the frozen weight in its mathematical orientation)
+        from W_t, for the input gradient."""
+        w = self.w
+        Wn = torch.empty((w.d_in, w.d_out), dtype=self.W_t.dtype, device=self.device)
+        B.lora_transpose(self.W_t, Wn, w.d_out, w.d_in, self.dtype, stream)
+        return Wn
+
+    def grad_x_buffers(self):
+        w = self.w
+        dX = torch.empty((w.T, w.d_in), dtype=self.Y.dtype, device=self.device)
+        n = B.lora_grad_x_workspace_bytes(w.T, w.d_in, w.d_out, self.dtype)
+        return dX, torch.empty(n, dtype=torch.uint8, device=self.device)
+
+    def run_grad_x(self, Wn, gws, dX, xws, stream=None):
+        B.lora_grad_x(self.dY, Wn, self.keep_mask, self.T, self.K, self.pool, self.plan, gws,
+                      self.max_rank, dX, xws, stream)
+
     # -- reading results ---------------------------------------------------
     def read_plan(self) -> dict:
         P = self.plan.cpu().numpy()

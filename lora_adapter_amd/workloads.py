@@ -198,6 +198,21 @@ def top2_softmax(rng: np.random.Generator, T: int, N: int):
     return ids, gates
 
 
+def topk_softmax(rng: np.random.Generator, T: int, N: int, k: int):
+    """Per token: N(0,1) logits over N adapters, the top-k ids (ties: lower
+    id), gates = softmax over the k chosen logits (top-k routing)."""
+    ids = np.empty((T, k), dtype=np.int32)
+    gates = np.empty((T, k), dtype=np.float32)
+    for t in range(T):
+        logits = rng.standard_normal(N)
+        order = np.argsort(-logits, kind="stable")[:k]
+        sel = logits[order]
+        e = np.exp(sel - sel.max())
+        ids[t] = order
+        gates[t] = e / e.sum()
+    return ids, gates
+
+
 def dirichlet_segments(rng: np.random.Generator, T: int, n_seg: int) -> np.ndarray:
     """Contiguous segment lengths from Dirichlet(1,...,1) weights, floor for all
     but the last, last takes the rest; resampled until no segment is empty."""

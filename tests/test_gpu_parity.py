@@ -205,6 +205,14 @@ def test_apply_short_k(case):
     assert err <= TOL[w.dtype], err
 
 
+def test_apply_fused_rowwise_expand():
+    """The fused 256 x 256 epilogue's row-by-row expand (K = 2, ranks above 16),
+    every row against the oracle."""
+    w = _fused_rowwise()
+    L = run(w)
+    assert rel_err(D.as_f64(L.Y_host()), O.apply_workload(w)) <= TOL["bf16"]
+
+
 def test_apply_mixed_ranks_above_bucket_edges():
     rng = np.random.default_rng(5)
     N, T, K = 9, 130, 2
@@ -356,7 +364,38 @@ def _mixed_decode():
                     scale=rng.uniform(0.5, 2, N).astype(np.float32))
 
 
+def _topk(T, K, N, d_in, d_out, seed, ranks=(2, 5, 8, 16, 17, 33)):
+    """Top-K routing (softmax over the K chosen of N(0,1) logits) over N
+    adapters with ranks drawn from `ranks`."""
+    rng = np.random.default_rng(seed)
+    rank = rng.choice(np.asarray(ranks, np.int32), size=N).astype(np.int32)
+    ids, gates = wl.topk_softmax(rng, T, N, K)
+    return wl.build(f"top{K}-{T}x{d_in}x{d_out}", seed, "bf16", T, K, d_in, d_out, rank, ids, gates,
+                    x_var=1.0, w_var=0.02, a_var=1 / 64, b_var=0.02)
+
+
+def _decode_k4():
+    return _topk(100, 4, 40, 1024, 768, 404)
+
+
+def _fused_rowwise():
+    """256 x 256 fused-epilogue shape whose blocks take the row-by-row expand
+    (two slots per token, ranks around the MFMA-expand limit of 16)."""
+    rng = np.random.default_rng(77)
+    T, K, N = 2100, 2, 4
+    rank = np.array([3, 17, 64, 129], np.int32)
+    ids = rng.integers(0, N, size=(T, K)).astype(np.int32)
+    gates = rng.uniform(0.25, 1.0, size=(T, K)).astype(np.float32)
+    return wl.build("fused-rowwise", 77, "bf16", T, K, 256, 8192, rank, ids, gates,
+                    x_var=1.0, w_var=0.02, a_var=1 / 64, b_var=0.02)
+
+
 FORWARD_CASES = {
+    # top-4 and top-8 routing: decode (per-slot shrink), split-K and stream-K
+    "dec_k4": _decode_k4,
+    "dec_k8": lambda: _topk(64, 8, 30, 512, 640, 408),
+    "sk_k8": lambda: _topk(512, 8, 64, 2048, 2048, 418),
+    "split_k4": lambda: _topk(300, 4, 48, 1024, 1536, 414),
     # decode shapes with a keep mask, d_in above one 4096-element block, and
     # ranks up to 128 over many adapters
     "dec4": lambda: wl.config(4, T=96, d_in=4608, d_out=704, seed=204),
@@ -366,7 +405,8 @@ FORWARD_CASES = {
 
 
 @pytest.mark.parametrize("cfg", ["small1", "small2", "small3", "small4", "small5", "full2", "full3",
-                                 "full5", "dec4", "dec3", "decmix"])
+                                 "full5", "dec4", "dec3", "decmix", "dec_k4", "dec_k8", "sk_k8",
+                                 "split_k4"])
 def test_forward_matches_plan_then_apply(cfg):
     """lora_forward in two launches (decode: GEMM + per-slot shrink, then
     epilogue + plan; stream-K: GEMM + plan, then shrink and epilogue): the
@@ -624,3 +664,87 @@ def test_grads_mfma_mixed_ranks_top2():
 def test_grads_full_prefill():
     w = full(4)
     _check_grads(w, run(w))
+
+
+# ---------------------------------------------------------------- input gradient dX
+
+def _with_dY(w, seed=11):
+    """The workload with a seeded N(0,1) dY when its recipe has none."""
+    if w.dY is None:
+        v = np.random.default_rng(seed).standard_normal((w.T, w.d_out)).astype(np.float32)
+        w.dY = v if w.dtype == "f32" else wl.f32_to_bf16_bits(v)
+    return w
+
+
+def _grad_x_run(w):
+    L = D.DeviceLayer(w)
+    L.run_plan()
+    L.run_apply()
+    dA, dB, gws = L.grad_buffers()
+    L.run_grad(dA, dB, gws)
+    Wn = L.weight_transposed()
+    dX, xws = L.grad_x_buffers()
+    L.run_grad_x(Wn, gws, dX, xws)
+    torch.cuda.synchronize()
+    return L, D.to_host(dX)
+
+
+def test_transpose_is_exact():
+    for dt, (r, c) in (("bf16", (704, 512)), ("f32", (256, 192)), ("bf16", (100, 37))):
+        v = np.random.default_rng(r).standard_normal((r, c)).astype(np.float32)
+        a = v if dt == "f32" else wl.f32_to_bf16_bits(v)
+        src = D.to_device(a, "cuda")
+        dst = torch.empty((c, r), dtype=src.dtype, device="cuda")
+        B.lora_transpose(src, dst, r, c, B.LORA_F32 if dt == "f32" else B.LORA_BF16)
+        torch.cuda.synchronize()
+        assert np.array_equal(D.to_host(dst), a.T)
+
+
+@pytest.mark.parametrize("cfg", ["small1", "small2", "small3", "small4", "small5", "dec_k4"])
+def test_grad_x_small(cfg):
+    """dX = dY.W^T + the masked LoRA term, against the oracle (every GEMM
+    form: fp32 tiles, decode split-K, split/stream-K 256 x 128, and top-2 and
+    four-slot routing)."""
+    if cfg == "dec_k4":
+        w = _decode_k4()
+    else:
+        w = wl.small(int(cfg[-1]))
+    w = _with_dY(w)
+    L, got = _grad_x_run(w)
+    ref = O.grad_x_workload(w)
+    assert rel_err(D.as_f64(got), ref) <= TOL[w.dtype]
+
+
+def test_grad_x_prefill_fused_shape():
+    """A batch large enough for the 256 x 256 tile GEMM (written as partials
+    here), with the keep mask, every row against the oracle."""
+    w = wl.config(4, T=2100, d_in=1024, d_out=1536, seed=444)
+    L, got = _grad_x_run(w)
+    ref = O.grad_x_workload(w)
+    assert rel_err(D.as_f64(got), ref) <= TOL["bf16"]
+
+
+def test_grad_x_full_prefill_sampled_rows():
+    w = full(4)
+    L, got = _grad_x_run(w)
+    rows = np.unique(np.concatenate([np.arange(0, w.T, 97), [0, w.T - 1],
+                                     np.cumsum(w.meta["segment_lengths"])[:-1]]))
+    ref = O.grad_x_workload(wl.subset(w, rows))
+    assert rel_err(D.as_f64(got[rows]), ref) <= TOL["bf16"]
+
+
+def test_grad_x_inactive_rows_equal_base_bit_for_bit():
+    w = _with_dY(wl.small(5))
+    L, got = _grad_x_run(w)
+    ids0 = w.ids.copy()
+    w2 = _with_dY(wl.small(5))
+    w2.ids = ids0.copy()
+    w2.ids[::3] = -1                      # every third token: no active slot
+    L2, got2 = _grad_x_run(w2)
+    w3 = _with_dY(wl.small(5))
+    w3.ids = np.full_like(ids0, -1)
+    L3, base = _grad_x_run(w3)
+    for t in range(0, w.T, 3):
+        assert np.array_equal(got2[t], base[t])
+    ref = O.grad_x_workload(w2)
+    assert rel_err(D.as_f64(got2), ref) <= TOL["bf16"]
