@@ -228,6 +228,17 @@ def merge(W_t, rank, scale, page_start, page_ids, a_pages, b_pages, merge_ids, c
     return W
 
 
+def merge_layers(layers, merge_ids, coeffs) -> list:
+    """The same signed merge applied to every layer, each against its own pool:
+    [AdaFuse] 关键设计 item 3 packs the merges of all layers into one batched
+    operation (its inference flow switches the chosen adapters in every layer
+    at once).  ``layers`` is a list of dicts with W_t, rank, scale, page_start,
+    page_ids, a_pages, b_pages; returns each layer's merged W_t (float64,
+    unrounded), in order.  Layers do not interact."""
+    return [merge(L["W_t"], L["rank"], L["scale"], L["page_start"], L["page_ids"], L["a_pages"],
+                  L["b_pages"], merge_ids, coeffs) for L in layers]
+
+
 def grad(X, keep_mask, keep_scale, dY, rank, scale, page_start, page_ids, a_pages, b_pages,
          ids, gates) -> dict:
     """Gradients of L = <dY, Y> with respect to every used adapter's factors.

@@ -71,6 +71,27 @@ def test_golden_merge():
     np.testing.assert_array_equal(Wm, np.asarray(g["expected_merged_W_t"], dtype=np.float64))
 
 
+def test_golden_merge_layers():
+    g = _gold()
+    a = _gold_arrays(g)
+    f32 = lambda v: np.asarray(v, dtype=np.float32)
+    i32 = lambda v: np.asarray(v, dtype=np.int32)
+    l1 = g["layer1"]
+    layers = [dict(W_t=a["W_t"], rank=a["rank"], scale=a["scale"], page_start=a["page_start"],
+                   page_ids=a["page_ids"], a_pages=a["a_pages"], b_pages=a["b_pages"]),
+              dict(W_t=f32(l1["W_t"]), rank=i32(l1["rank"]), scale=f32(l1["scale"]),
+                   page_start=i32(l1["page_start"]), page_ids=i32(l1["page_ids"]),
+                   a_pages=f32(l1["a_pages"]), b_pages=f32(l1["b_pages"]))]
+    out = O.merge_layers(layers, np.asarray(g["merge_ids"]), np.asarray(g["merge_coeffs"], np.float32))
+    np.testing.assert_array_equal(out[0], np.asarray(g["expected_merged_W_t"], dtype=np.float64))
+    np.testing.assert_array_equal(out[1], np.asarray(g["expected_merged_W_t_layer1"], dtype=np.float64))
+    # layers do not interact: changing layer 1's pool leaves layer 0's result
+    layers[1]["a_pages"] = layers[1]["a_pages"] * 3
+    out2 = O.merge_layers(layers, np.asarray(g["merge_ids"]), np.asarray(g["merge_coeffs"], np.float32))
+    np.testing.assert_array_equal(out2[0], out[0])
+    assert not np.array_equal(out2[1], out[1])
+
+
 def test_golden_grad():
     g = _gold()
     a = _gold_arrays(g)
