@@ -295,6 +295,31 @@ int32_t lora_forward_noalloc(const int32_t *ids, const float *gates, int32_t T, 
 int32_t lora_merge_delta(void *W_t, const lora_pool_desc *pool, const int32_t *merge_ids,
                          const float *coeffs, int32_t m, void *stream);
 
+/* ----------------------------------------------------- merge, many layers
+ * The same signed merge applied to several layers' weights at once
+ * ([AdaFuse] 关键设计 item 3: the merges of every layer packed into one
+ * batched launch, blocked across layers, added in place; its three-step
+ * inference flow switches the chosen adapters in all layers together):
+ *   for every layer l:  W_t^l <- round( W_t^l + sum_i coeffs[i] . s^l_{a_i} . (A^l_{a_i} . B^l_{a_i})^T )
+ * with each layer's own pool (its pages, ranks, page table and scales; ids
+ * index every pool alike).  One launch covers up to LORA_MERGE_MAX_LAYERS
+ * layers when every layer is bf16 with d_in and d_out multiples of 128 (the
+ * MFMA merge form); otherwise each layer takes its own launch.  Per layer the
+ * result is the same, bit for bit, as lora_merge_delta on that layer.
+ *   layers   host array [n_layers]; W_t and every pool pointer are device
+ *            memory; all layers share one dtype; no two layers share a W_t.
+ *   merge_ids, coeffs, m   as for lora_merge_delta (device arrays).
+ * Errors: INVALID_ARG (null, n_layers < 0, mixed dtypes, a W_t given twice),
+ * UNSUPPORTED (a layer's width not a multiple of 64), DEVICE. */
+#define LORA_MERGE_MAX_LAYERS 16
+typedef struct {
+  void *W_t;                  /* [d_out][d_in] of this layer                 */
+  lora_pool_desc pool;        /* this layer's adapter pool                    */
+} lora_layer_desc;
+int32_t lora_merge_delta_layers(const lora_layer_desc *layers, int32_t n_layers,
+                                const int32_t *merge_ids, const float *coeffs, int32_t m,
+                                void *stream);
+
 /* ------------------------------------------------------------------ grad
  * Gradients of <dY, Y> with respect to the factors of every used adapter
  * (only A and B train, W frozen: [LoRAFusion] 解决什么真问题; the pages give

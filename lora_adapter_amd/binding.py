@@ -29,7 +29,7 @@ EXPORTS = (
     "lora_base_gemm", "lora_expand_epilogue", "lora_shrink_gemm", "lora_apply",
     "lora_forward_gemm", "lora_forward_finish", "lora_forward", "lora_forward_noalloc_bytes",
     "lora_forward_noalloc", "lora_merge_delta", "lora_grad_workspace_bytes", "lora_grad",
-    "lora_grad_x_workspace_bytes", "lora_grad_x", "lora_transpose",
+    "lora_grad_x_workspace_bytes", "lora_grad_x", "lora_transpose", "lora_merge_delta_layers",
 )
 
 
@@ -46,6 +46,10 @@ class PoolDesc(ctypes.Structure):
         ("a_pages", ctypes.c_void_p), ("b_pages", ctypes.c_void_p), ("rank", ctypes.c_void_p),
         ("page_start", ctypes.c_void_p), ("page_ids", ctypes.c_void_p), ("scale", ctypes.c_void_p),
     ]
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("W_t", ctypes.c_void_p), ("pool", PoolDesc)]
 
 
 _lib = None
@@ -84,6 +88,7 @@ _PROTOS = {
     "lora_grad_x": (_I32, [_VP, _VP, _VP, _I32, _I32, _PD, _VP, _VP, _SZ, _I32, _VP, _VP, _SZ,
                            _VP]),
     "lora_transpose": (_I32, [_VP, _VP, _I32, _I32, _I32, _VP]),
+    "lora_merge_delta_layers": (_I32, [ctypes.POINTER(LayerDesc), _I32, _VP, _VP, _I32, _VP]),
 }
 
 
@@ -289,3 +294,15 @@ def lora_grad_x(dY, W, keep_mask, T: int, K: int, pool: Pool, plan, grad_ws, max
 def lora_transpose(src, dst, rows: int, cols: int, dtype: int, stream=None):
     _check("lora_transpose", lib().lora_transpose(_ptr(src), _ptr(dst), rows, cols, dtype,
                                                   _stream(stream)))
+
+
+def lora_merge_delta_layers(Ws, pools, merge_ids, coeffs, m: int, stream=None):
+    """The same signed merge on every (W_t, pool) pair (one launch per up to
+    16 layers of the MFMA form)."""
+    n = len(Ws)
+    arr = (LayerDesc * max(n, 1))()
+    for i, (W, p) in enumerate(zip(Ws, pools)):
+        arr[i].W_t = _ptr(W)
+        arr[i].pool = p.desc
+    _check("lora_merge_delta_layers", lib().lora_merge_delta_layers(
+        arr, n, _ptr(merge_ids), _ptr(coeffs), m, _stream(stream)))

@@ -396,13 +396,12 @@ int32_t lora_forward(const int32_t *ids, const float *gates, int32_t T, int32_t 
                              plan_bytes, ws, ws_bytes, stream);
 }
 
-int32_t lora_merge_delta(void *W_t, const lora_pool_desc *pool, const int32_t *merge_ids,
-                         const float *coeffs, int32_t m, void *stream) {
-  int32_t st = check_pool(pool, true);
-  if (st != LORA_OK) return st;
-  if (m < 0 || !W_t) return LORA_ERR_INVALID_ARG;
-  if (m == 0) return LORA_OK;
-  if (!merge_ids || !coeffs) return LORA_ERR_INVALID_ARG;
+}  // extern "C"
+
+namespace {
+
+MergeArgs merge_args(void *W_t, const lora_pool_desc *pool, const int32_t *merge_ids,
+                     const float *coeffs, int32_t m) {
   MergeArgs a{};
   a.W = W_t; a.d_in = pool->d_in; a.d_out = pool->d_out;
   a.a_pages = pool->a_pages; a.b_pages = pool->b_pages;
@@ -410,7 +409,48 @@ int32_t lora_merge_delta(void *W_t, const lora_pool_desc *pool, const int32_t *m
   a.scale = pool->scale;
   a.n_pages = pool->n_pages; a.n_page_ids = pool->n_page_ids; a.n_adapters = pool->n_adapters;
   a.ids = merge_ids; a.coeffs = coeffs; a.m = m;
-  return dev(launch_merge(a, pool->dtype, static_cast<hipStream_t>(stream)));
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t lora_merge_delta(void *W_t, const lora_pool_desc *pool, const int32_t *merge_ids,
+                         const float *coeffs, int32_t m, void *stream) {
+  int32_t st = check_pool(pool, true);
+  if (st != LORA_OK) return st;
+  if (m < 0 || !W_t) return LORA_ERR_INVALID_ARG;
+  if (m == 0) return LORA_OK;
+  if (!merge_ids || !coeffs) return LORA_ERR_INVALID_ARG;
+  return dev(launch_merge(merge_args(W_t, pool, merge_ids, coeffs, m), pool->dtype,
+                          static_cast<hipStream_t>(stream)));
+}
+
+int32_t lora_merge_delta_layers(const lora_layer_desc *layers, int32_t n_layers,
+                                const int32_t *merge_ids, const float *coeffs, int32_t m,
+                                void *stream) {
+  if (n_layers < 0 || m < 0 || (n_layers > 0 && !layers)) return LORA_ERR_INVALID_ARG;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    const int32_t st = check_pool(&layers[l].pool, true);
+    if (st != LORA_OK) return st;
+    if (!layers[l].W_t || layers[l].pool.dtype != layers[0].pool.dtype) return LORA_ERR_INVALID_ARG;
+    for (int32_t q = 0; q < l; ++q)
+      if (layers[q].W_t == layers[l].W_t) return LORA_ERR_INVALID_ARG;   // in place, once each
+  }
+  if (n_layers == 0 || m == 0) return LORA_OK;
+  if (!merge_ids || !coeffs) return LORA_ERR_INVALID_ARG;
+  constexpr int32_t kChunk = LORA_MERGE_MAX_LAYERS;
+  MergeArgs a[kChunk];
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int32_t l0 = 0; l0 < n_layers; l0 += kChunk) {
+    const int32_t nl = n_layers - l0 < kChunk ? n_layers - l0 : kChunk;
+    for (int32_t l = 0; l < nl; ++l)
+      a[l] = merge_args(layers[l0 + l].W_t, &layers[l0 + l].pool, merge_ids, coeffs, m);
+    const int32_t st = dev(launch_merge_layers(a, nl, layers[0].pool.dtype, s));
+    if (st != LORA_OK) return st;
+  }
+  return LORA_OK;
 }
 
 size_t lora_grad_workspace_bytes(int32_t T, int32_t K, int32_t n_adapters, int32_t d_in,

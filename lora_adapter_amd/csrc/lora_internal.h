@@ -422,6 +422,9 @@ hipError_t launch_transpose(const void *src, void *dst, int rows, int cols, int 
                             hipStream_t s);
 
 hipError_t launch_merge(const MergeArgs &a, int dtype, hipStream_t s);
+// n layers' merges (same list, each layer's own W and pool): one launch per
+// LORA_MERGE_MAX_LAYERS layers when every layer takes the MFMA form.
+hipError_t launch_merge_layers(const MergeArgs *layers, int n, int dtype, hipStream_t s);
 int64_t grad_pieces(int64_t TK, int64_t n_adapters);
 // The MFMA outer-product form (and the fused dY.B^T partials) applies.
 bool grad_mfma_form(int dtype, int64_t TK, int d_out);

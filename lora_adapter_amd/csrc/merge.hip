@@ -338,7 +338,8 @@ constexpr int kSN = 64;            // W rows per rectangle
 constexpr int kSD = 3;             // rectangles in flight per workgroup
 
 __device__ __forceinline__ void merge_stream(const MergeArgs &m, int total, uint4 *raw,
-                                             const int *s_pid, const float *s_cf) {
+                                             const int *s_pid, const float *s_cf, int bid,
+                                             int nblk) {
   uint4 (*s_at)[8] = reinterpret_cast<uint4 (*)[8]>(raw);            // [128 i][64 j]
   uint32_t (*s_bh)[32] = reinterpret_cast<uint32_t (*)[32]>(raw + 1024);   // [64 n][64 j]
   uint32_t (*s_bl)[32] = reinterpret_cast<uint32_t (*)[32]>(raw + 1536);
@@ -346,9 +347,9 @@ __device__ __forceinline__ void merge_stream(const MergeArgs &m, int total, uint
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nrn = m.d_out / kSN;
   const int gx = m.d_in / kQI;
-  // workgroup -> (column slice, part of its rectangles): gridDim.x = gx * gps
-  const int gps = gridDim.x / gx;
-  const int slice = blockIdx.x / gps, part = blockIdx.x % gps;
+  // workgroup -> (column slice, part of its rectangles): nblk = gx * gps
+  const int gps = nblk / gx;
+  const int slice = bid / gps, part = bid % gps;
   const int beg = nrn * part / gps, end = nrn * (part + 1) / gps;   // rectangle rows of the slice
   if (slice >= gx || beg >= end) return;
   const int i0 = slice * kQI;
@@ -490,14 +491,12 @@ __device__ __forceinline__ void merge_stream(const MergeArgs &m, int total, uint
   }
 }
 
-// General form (any merge list): workgroup w takes 128 x 128 rectangles w,
-// w + G, ...; the merge list is built once per workgroup when it fits one LDS
-// list.  Lists of at most kQR rank rows take the streaming form.
-__global__ __launch_bounds__(256) void merge_mfma_kernel(MergeArgs m) {
-  __shared__ uint4 raw[3072];
-  __shared__ int s_pid[kMList];
-  __shared__ float s_cf[kMList];
-  __shared__ int s_tot[4];
+// General form (any merge list): workgroup w of G = nblk takes 128 x 128
+// rectangles w, w + G, ...; the merge list is built once per workgroup when
+// it fits one LDS list.  Lists of at most kQR rank rows take the streaming
+// form.
+__device__ __forceinline__ void merge_mfma_body(const MergeArgs &m, int bid, int nblk, uint4 *raw,
+                                                int *s_pid, float *s_cf, int *s_tot) {
   uint4 (*s_at)[8] = reinterpret_cast<uint4 (*)[8]>(raw);
   uint4 (*s_bh)[8] = reinterpret_cast<uint4 (*)[8]>(raw + 1024);
   uint4 (*s_bl)[8] = reinterpret_cast<uint4 (*)[8]>(raw + 2048);
@@ -511,7 +510,7 @@ __global__ __launch_bounds__(256) void merge_mfma_kernel(MergeArgs m) {
     total = merge_list(m, 0, 0, s_pid, s_cf, s_tot);
     if (total == 0) return;                 // nothing valid listed: W stays as it is
     if (total <= kQR) {
-      merge_stream(m, total, raw, s_pid, s_cf);
+      merge_stream(m, total, raw, s_pid, s_cf, bid, nblk);
       return;
     }
   }
@@ -530,7 +529,7 @@ __global__ __launch_bounds__(256) void merge_mfma_kernel(MergeArgs m) {
   };
   uint4 wv[kQB][2];
   bool any = resident;
-  for (int rect = blockIdx.x; rect < nrect; rect += gridDim.x) {
+  for (int rect = bid; rect < nrect; rect += nblk) {
     const int i0 = (rect % gx) * kQI, n0 = (rect / gx) * kQN;
     wload(rect, wv);
     f32x16_t acc[kQB];
@@ -584,16 +583,80 @@ __global__ __launch_bounds__(256) void merge_mfma_kernel(MergeArgs m) {
   }
 }
 
+__global__ __launch_bounds__(256) void merge_mfma_kernel(MergeArgs m) {
+  __shared__ uint4 raw[3072];
+  __shared__ int s_pid[kMList];
+  __shared__ float s_cf[kMList];
+  __shared__ int s_tot[4];
+  merge_mfma_body(m, int(blockIdx.x), int(gridDim.x), raw, s_pid, s_cf, s_tot);
+}
+
+// Several layers' merges in one launch (AdaFuse notes, section 关键设计 item
+// 3: the merges of every layer packed into one batched launch, blocked across
+// layers, added in place): layer blockIdx.y, its own workgroup count, the
+// same merge list read against that layer's pool.
+struct MergeLayers {
+  MergeArgs layer[LORA_MERGE_MAX_LAYERS];
+  int nblk[LORA_MERGE_MAX_LAYERS];
+};
+
+__global__ __launch_bounds__(256) void merge_layers_mfma_kernel(MergeLayers ml) {
+  __shared__ uint4 raw[3072];
+  __shared__ int s_pid[kMList];
+  __shared__ float s_cf[kMList];
+  __shared__ int s_tot[4];
+  const int l = int(blockIdx.y);
+  const int nb = ml.nblk[l];
+  if (int(blockIdx.x) >= nb) return;
+  merge_mfma_body(ml.layer[l], int(blockIdx.x), nb, raw, s_pid, s_cf, s_tot);
+}
+
+// Workgroups of the MFMA merge of one layer: at most 512 (two per CU, one
+// round), a whole number per 128-column slice.
+int merge_mfma_wgs(const MergeArgs &a) {
+  const int gx = a.d_in / kQI, nrn = a.d_out / kSN;
+  int gps = 512 / gx;
+  gps = gps < 1 ? 1 : gps > nrn ? nrn : gps;
+  return gx * gps;
+}
+
+bool merge_mfma_ok(const MergeArgs &a, int dtype) {
+  return dtype == LORA_BF16 && a.d_in % kQI == 0 && a.d_out % kQN == 0;
+}
+
 }  // namespace
 
+hipError_t launch_merge_layers(const MergeArgs *layers, int n, int dtype, hipStream_t s) {
+  for (int l0 = 0; l0 < n; l0 += LORA_MERGE_MAX_LAYERS) {
+    const int nl = n - l0 < LORA_MERGE_MAX_LAYERS ? n - l0 : LORA_MERGE_MAX_LAYERS;
+    bool all_mfma = true;
+    for (int l = 0; l < nl; ++l) all_mfma = all_mfma && merge_mfma_ok(layers[l0 + l], dtype);
+    if (!all_mfma) {
+      // other dtypes or widths: one launch per layer
+      for (int l = 0; l < nl; ++l) {
+        const hipError_t e = launch_merge(layers[l0 + l], dtype, s);
+        if (e != hipSuccess) return e;
+      }
+      continue;
+    }
+    MergeLayers ml{};
+    int gmax = 1;
+    for (int l = 0; l < nl; ++l) {
+      ml.layer[l] = layers[l0 + l];
+      ml.nblk[l] = merge_mfma_wgs(layers[l0 + l]);
+      gmax = ml.nblk[l] > gmax ? ml.nblk[l] : gmax;
+    }
+    hipLaunchKernelGGL(merge_layers_mfma_kernel, dim3(unsigned(gmax), unsigned(nl)), dim3(256), 0,
+                       s, ml);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_merge(const MergeArgs &a, int dtype, hipStream_t s) {
-  if (dtype == LORA_BF16 && a.d_in % kQI == 0 && a.d_out % kQN == 0) {
-    // at most 512 workgroups (two per CU, one round), a whole number per
-    // 128-column slice
-    const int gx = a.d_in / kQI, nrn = a.d_out / kSN;
-    int gps = 512 / gx;
-    gps = gps < 1 ? 1 : gps > nrn ? nrn : gps;
-    hipLaunchKernelGGL(merge_mfma_kernel, dim3(unsigned(gx * gps)), dim3(256), 0, s, a);
+  if (merge_mfma_ok(a, dtype)) {
+    hipLaunchKernelGGL(merge_mfma_kernel, dim3(unsigned(merge_mfma_wgs(a))), dim3(256), 0, s, a);
     return hipGetLastError();
   }
   const int ntiles = (a.d_in / kMT) * (a.d_out / kMT);

@@ -748,3 +748,58 @@ def test_grad_x_inactive_rows_equal_base_bit_for_bit():
         assert np.array_equal(got2[t], base[t])
     ref = O.grad_x_workload(w2)
     assert rel_err(D.as_f64(got2), ref) <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------- merge across layers
+
+def _layer_set(shapes, N=24, seed=900):
+    """Layers of different shapes, each with its own pool of N adapters
+    (ranks and factors drawn per layer), sharing adapter ids."""
+    return [wl.config(5, T=8, d_in=di, d_out=do, n_adapters=N, seed=seed + i)
+            for i, (di, do) in enumerate(shapes)]
+
+
+@pytest.mark.parametrize("case", ["mixed_shapes", "many_layers", "fallback_widths"])
+def test_merge_layers_matches_per_layer(case):
+    if case == "mixed_shapes":
+        shapes = [(1024, 1024), (1024, 2816), (2816, 1024), (512, 640), (1280, 1280)]
+    elif case == "many_layers":
+        shapes = [(256 + 128 * (i % 3), 384) for i in range(19)]     # two launches
+    else:
+        shapes = [(576, 704), (512, 512)]                            # 576: not a multiple of 128
+    ws = _layer_set(shapes)
+    Ls = [D.DeviceLayer(w) for w in ws]
+    rng = np.random.default_rng(31)
+    ids = rng.choice(24, size=8, replace=False).astype(np.int32)
+    co = rng.choice(np.array([1.0, -1.0, 0.5, -2.0], np.float32), size=8)
+    mi = D.to_device(ids, "cuda")
+    cf = D.to_device(co, "cuda")
+    Wm = [L.W_t.clone() for L in Ls]
+    print(f"merge layers case {case}: {len(Ls)} layers", flush=True)
+    B.lora_merge_delta_layers(Wm, [L.pool for L in Ls], mi, cf, 8)
+    Wr = [L.W_t.clone() for L in Ls]
+    for W, L in zip(Wr, Ls):
+        B.lora_merge_delta(W, L.pool, mi, cf, 8)
+    torch.cuda.synchronize()
+    refs = O.merge_layers([dict(W_t=w.W_t, rank=w.rank, scale=w.scale, page_start=w.page_start,
+                                page_ids=w.page_ids, a_pages=w.a_pages, b_pages=w.b_pages)
+                           for w in ws], ids, co)
+    for l, (a, b, ref) in enumerate(zip(Wm, Wr, refs)):
+        ga, gb = D.to_host(a), D.to_host(b)
+        assert np.array_equal(ga, gb), f"layer {l} differs from lora_merge_delta"
+        assert rel_err(D.as_f64(ga), ref) <= TOL["bf16"], l
+
+
+def test_merge_layers_rejects_shared_weight_and_mixed_dtype():
+    ws = _layer_set([(512, 512), (512, 512)])
+    Ls = [D.DeviceLayer(w) for w in ws]
+    mi = D.to_device(np.array([0, 1], np.int32), "cuda")
+    cf = D.to_device(np.array([1.0, 1.0], np.float32), "cuda")
+    W = Ls[0].W_t.clone()
+    with pytest.raises(B.LoraError) as ei:
+        B.lora_merge_delta_layers([W, W], [Ls[0].pool, Ls[1].pool], mi, cf, 2)
+    assert ei.value.status == B.LORA_ERR_INVALID_ARG
+    f = D.DeviceLayer(wl.small(1))
+    with pytest.raises(B.LoraError) as ei:
+        B.lora_merge_delta_layers([W, f.W_t], [Ls[0].pool, f.pool], mi, cf, 2)
+    assert ei.value.status == B.LORA_ERR_INVALID_ARG
