@@ -347,7 +347,39 @@ def measure(w, args, torch, np, B, D, steps, warmup, full):
         out["merge"] = {"adapters": len(w.merge_ids), "us": t_m, "bytes": mb, "GB_s": mb / t_m / 1e3,
                         "frac_hbm": mb / t_m / 1e3 / HBM_PEAK_GBS,
                         "flops": 2.0 * w.d_in * w.d_out * rsum}
+        # the same merge on every rotated copy as one layer each: one launch
+        # for all of them (lora_merge_delta_layers) against one launch per layer
+        Ws = [c.W_t for c in bn.copies]
+        pools = [c.pool for c in bn.copies]
+
+        def merge_layers_call(i):
+            B.lora_merge_delta_layers(Ws, pools, m_ids, plus if i % 2 == 0 else minus,
+                                      len(w.merge_ids))
+
+        def merge_each_call(i):
+            for W, p in zip(Ws, pools):
+                B.lora_merge_delta(W, p, m_ids, plus if i % 2 == 0 else minus, len(w.merge_ids))
+        t_ml = bn.event_us(merge_layers_call, 8, 5)
+        t_me = bn.event_us(merge_each_call, 8, 5)
+        out["merge_layers"] = {"layers": bn.R, "us": t_ml, "us_one_launch_per_layer": t_me,
+                               "GB_s": bn.R * mb / t_ml / 1e3,
+                               "frac_hbm": bn.R * mb / t_ml / 1e3 / HBM_PEAK_GBS}
     if bn.grads:
+        # input gradient dX of the same batch (after lora_grad, which leaves G)
+        Wn = bn.L.weight_transposed()
+        dX, xws = bn.L.grad_x_buffers()
+        c0 = bn.copies[0]
+        bn.step(c0)
+
+        def gx_call(i):
+            B.lora_grad_x(c0.dY, Wn, c0.mask, T, K, c0.pool, c0.plan, bn.gws, bn.L.max_rank, dX,
+                          xws)
+        t_x = bn.event_us(gx_call, 8, 5)
+        xf = 2.0 * T * w.d_in * w.d_out + 2.0 * R_pairs * w.d_in
+        out["grad_x"] = {"us": t_x, "TFLOP_s": xf / t_x / 1e6,
+                         "frac_mfma": xf / t_x / 1e6 / MFMA_BF16_PEAK_TFLOPS,
+                         "tokens_per_s": T / (t_x * 1e-6)}
+        del Wn, dX, xws
         t_g = st["grad"]
         gb = (T * w.d_out * e + T * w.d_in * (e + (1 if w.keep_mask is not None else 0))
               + R_used * (w.d_in + w.d_out) * (e + 4) + 8 * R_pairs)
