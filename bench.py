@@ -80,6 +80,10 @@ def parse():
     ap.add_argument("--skip-empty-plan", action="store_true",
                     help="no runs on an empty plan (for kernel traces whose averages should "
                          "hold only launches with the batch's plan; no LoRA-path figures)")
+    ap.add_argument("--residency", type=int, default=1,
+                    help="1: also time the heterogeneous-rank workload with its pool held to "
+                         "--residency-frac of the fleet (pages copied in from pinned host memory)")
+    ap.add_argument("--residency-frac", type=float, default=0.6)
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs of a --copy-probe run into "
@@ -386,9 +390,62 @@ def measure(w, args, torch, np, B, D, steps, warmup, full):
         out["grads"] = {"us": t_g, "bytes": gb, "GB_s": gb / t_g / 1e3,
                         "frac_hbm": gb / t_g / 1e3 / HBM_PEAK_GBS,
                         "flops": 2.0 * R_pairs * (2 * w.d_out + w.d_in)}
+    if args.residency and w.n_adapters >= 256 and not bn.grads:
+        out["residency"] = residency_run(w, bn, args, torch, np, B, D)
     del bn
     torch.cuda.empty_cache()
     return out
+
+
+def residency_run(w, bn, args, torch, np, B, D):
+    """The pool held to --residency-frac of the fleet's rank rows, filled from
+    a pinned host store: batch b + 1's copies (on a side stream) overlap batch
+    b's forward; against the same batches on the fully resident pool."""
+    from lora_adapter_amd import workloads as wl
+    rows = np.concatenate([w.page_ids[w.page_start[a]:w.page_start[a + 1]]
+                           for a in range(w.n_adapters)]).astype(np.int64)
+    store_row = w.page_start[:-1].astype(np.int64)
+    sa = D.to_device(w.a_pages[rows], "cpu").pin_memory()
+    sb = D.to_device(w.b_pages[rows], "cpu").pin_memory()
+    n_pages = int(args.residency_frac * int(w.rank.sum()))
+    ap = torch.empty((n_pages, w.d_in), dtype=torch.bfloat16, device="cuda")
+    bp = torch.empty((n_pages, w.d_out), dtype=torch.bfloat16, device="cuda")
+    res = B.Residency(B.LORA_BF16, w.d_in, w.d_out, w.rank, store_row, sa, sb, ap, bp, bn.L.scale)
+    side = torch.cuda.Stream()
+    rng = np.random.default_rng(1234)
+    nb = 40
+    batches = [wl.zipf_ids(rng, w.T, w.n_adapters).reshape(w.T, 1) for _ in range(nb)]
+    dev_ids = [D.to_device(b, "cuda") for b in batches]
+    c = bn.copies[0]
+    L = bn.L
+
+    def loop(managed):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(nb):
+            pool = res.prepare(batches[i], side) if managed else c.pool
+            B.lora_forward(dev_ids[i], L.gates, w.T, w.K, c.X, c.W_t, c.Y, None, 1.0, pool, c.plan,
+                           c.ws)
+            if managed:
+                res.finish()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / nb
+
+    loop(True)                       # warm: fill the pool once
+    s0 = res.stats()
+    t_managed = loop(True)
+    s1 = res.stats()
+    t_resident = loop(False)
+    res.close()
+    moved = (s1["bytes"] - s0["bytes"]) / nb
+    return {"pool_fraction": args.residency_frac, "pool_pages": n_pages,
+            "fleet_rank_rows": int(w.rank.sum()), "batches": nb,
+            "step_us_managed": t_managed * 1e6, "step_us_resident": t_resident * 1e6,
+            "copied_bytes_per_batch": moved,
+            "evictions_per_batch": (s1["evictions"] - s0["evictions"]) / nb,
+            "h2d_GB_s_lower_bound": moved / t_managed / 1e9,
+            "note": "each batch's missing adapters copied H2D on a side stream while the "
+                    "previous batch computes; wall time per batch over 40 Zipf batches"}
 
 
 def gemm_roofline(w, L, B, kind, st, base_flops, P, R_pairs, R_used, e):

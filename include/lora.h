@@ -341,6 +341,85 @@ int32_t lora_grad(const void *X, const uint8_t *keep_mask, float keep_scale, con
                   float *dA_pages, float *dB_pages, int32_t max_rank, void *ws,
                   size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------- pool residency
+ * Which adapters occupy the GPU pool, and the copy of a batch's missing
+ * adapters into it ([S-LoRA] 批处理, last paragraph: all adapters are held in
+ * host memory and only the running batch's adapters are loaded to the GPU;
+ * 内存管理 and Unified Paging: one shared pool of pages, one page per rank
+ * row, non-contiguous).  The victim policy (the pages leave it open):
+ *   - a batch needs its valid ids (0 <= a < N, rank > 0), once each, in
+ *     ascending order; its protected set is those plus the previous admitted
+ *     batch's adapters; if their ranks add up to more than the pool's pages
+ *     the batch is refused (LORA_ERR_CAPACITY) and nothing changes;
+ *   - needed adapters are stamped with the batch index (last use);
+ *   - each needed adapter not resident, in ascending id order, takes rank
+ *     pages: while too few are free, the resident adapter outside the
+ *     protected set with the smallest (last use, id) is evicted; then the
+ *     lowest-numbered free pages are taken, rank row j on the j-th;
+ *   - its rows are copied in maximal runs of consecutive pages.
+ * The tables a batch runs with give each resident adapter its rank and pages
+ * (page_start the prefix sums, page_ids in adapter order); adapters that are
+ * not resident have rank 0, so a plan over them sees no active slot. */
+typedef struct lora_page_table lora_page_table;      /* host object */
+typedef struct {
+  int32_t adapter, row, page, count;  /* rank rows row..row+count-1 -> pages page..page+count-1 */
+} lora_page_copy;
+/* The policy alone, in host memory (no HIP call).  rank: host [N]. */
+int32_t lora_page_table_create(const int32_t *rank, int32_t n_adapters, int64_t n_pages,
+                               lora_page_table **out);
+void lora_page_table_destroy(lora_page_table *pt);
+/* Admits one batch (host ids [n], -1 and out-of-range ids ignored): writes the
+ * copies to make (host array, max_copies >= n_pages) and the evicted
+ * adapters (host array, max_evicted >= N).  Errors: INVALID_ARG, CAPACITY. */
+int32_t lora_page_table_admit(lora_page_table *pt, const int32_t *ids, int64_t n,
+                              lora_page_copy *copies, int64_t max_copies, int64_t *n_copies,
+                              int32_t *evicted, int64_t max_evicted, int64_t *n_evicted);
+/* The current tables into host arrays rank [N], page_start [N+1],
+ * page_ids [n_pages] (the first *n_page_ids are set). */
+int32_t lora_page_table_tables(const lora_page_table *pt, int32_t *rank, int32_t *page_start,
+                               int32_t *page_ids, int64_t *n_page_ids);
+
+/* The GPU side.  The store holds every adapter's rank rows in pinned host
+ * memory (hipHostMalloc; pageable memory makes the copies synchronous):
+ * adapter a's row j is row store_row[a] + j of store_a [rows][d_in] (column j
+ * of A_a) and of store_b [rows][d_out] (row j of B_a).  All buffers are the
+ * caller's and must outlive the object. */
+typedef struct {
+  int32_t dtype, d_in, d_out, n_adapters;
+  int64_t n_pages;              /* pages of the device pool                    */
+  const int32_t *rank;          /* host [N]: every adapter's rank              */
+  const int64_t *store_row;     /* host [N]: first store row of each adapter   */
+  const void *store_a;          /* pinned host [rows][d_in]                    */
+  const void *store_b;          /* pinned host [rows][d_out]                   */
+  void *a_pages;                /* device [n_pages][d_in]                      */
+  void *b_pages;                /* device [n_pages][d_out]                     */
+  const float *scale;           /* device [N]                                  */
+  int32_t *tables;              /* device, lora_residency_table_ints() int32   */
+  int32_t *staging;             /* pinned host, the same number of int32       */
+} lora_residency_config;
+typedef struct lora_residency lora_residency;        /* host object */
+size_t lora_residency_table_ints(int32_t n_adapters, int64_t n_pages);
+int32_t lora_residency_create(const lora_residency_config *cfg, lora_residency **out);
+void lora_residency_destroy(lora_residency *r);
+/* Admits a batch (host ids [n]) and, on copy_stream, copies its missing
+ * adapters' rows into their pages and uploads its tables (one of two table
+ * sets, alternating); compute_stream then waits for those copies.  Pages and
+ * the table set that batch i - 2 used are overwritten only after batch i - 2's
+ * finish point, so the copies of batch i + 1 may run while batch i computes.
+ * pool_out: the descriptor the batch's calls must use.  Every prepare is
+ * followed by lora_residency_finish once the batch's work is queued; the
+ * compute work of all batches goes to one stream.  The host waits only when a
+ * table staging set is still being copied from (two batches back).
+ * Errors: INVALID_ARG (no finish for the previous batch), CAPACITY, DEVICE. */
+int32_t lora_residency_prepare(lora_residency *r, const int32_t *ids, int64_t n,
+                               void *copy_stream, void *compute_stream, lora_pool_desc *pool_out);
+/* Marks the end of the prepared batch's work on compute_stream. */
+int32_t lora_residency_finish(lora_residency *r, void *compute_stream);
+/* out = {batches prepared, rank rows copied, adapters evicted, bytes copied}. */
+int32_t lora_residency_stats(const lora_residency *r, int64_t out[4]);
+/* The object's page table (read it with lora_page_table_tables). */
+const lora_page_table *lora_residency_page_table(const lora_residency *r);
+
 /* ------------------------------------------------------------ grad of X
  * Input gradient of the fine-tune backward, handed to the layer below
  * ([LoRAFusion] 解决什么真问题: W frozen, A and B trained, dropout on the LoRA

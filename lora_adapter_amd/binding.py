@@ -30,6 +30,10 @@ EXPORTS = (
     "lora_forward_gemm", "lora_forward_finish", "lora_forward", "lora_forward_noalloc_bytes",
     "lora_forward_noalloc", "lora_merge_delta", "lora_grad_workspace_bytes", "lora_grad",
     "lora_grad_x_workspace_bytes", "lora_grad_x", "lora_transpose", "lora_merge_delta_layers",
+    "lora_page_table_create", "lora_page_table_destroy", "lora_page_table_admit",
+    "lora_page_table_tables", "lora_residency_table_ints", "lora_residency_create",
+    "lora_residency_destroy", "lora_residency_prepare", "lora_residency_finish",
+    "lora_residency_stats", "lora_residency_page_table",
 )
 
 
@@ -50,6 +54,21 @@ class PoolDesc(ctypes.Structure):
 
 class LayerDesc(ctypes.Structure):
     _fields_ = [("W_t", ctypes.c_void_p), ("pool", PoolDesc)]
+
+
+class PageCopy(ctypes.Structure):
+    _fields_ = [("adapter", ctypes.c_int32), ("row", ctypes.c_int32), ("page", ctypes.c_int32),
+                ("count", ctypes.c_int32)]
+
+
+class ResidencyConfig(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("d_in", ctypes.c_int32), ("d_out", ctypes.c_int32),
+                ("n_adapters", ctypes.c_int32), ("n_pages", ctypes.c_int64),
+                ("rank", ctypes.c_void_p), ("store_row", ctypes.c_void_p),
+                ("store_a", ctypes.c_void_p), ("store_b", ctypes.c_void_p),
+                ("a_pages", ctypes.c_void_p), ("b_pages", ctypes.c_void_p),
+                ("scale", ctypes.c_void_p), ("tables", ctypes.c_void_p),
+                ("staging", ctypes.c_void_p)]
 
 
 _lib = None
@@ -89,6 +108,20 @@ _PROTOS = {
                            _VP]),
     "lora_transpose": (_I32, [_VP, _VP, _I32, _I32, _I32, _VP]),
     "lora_merge_delta_layers": (_I32, [ctypes.POINTER(LayerDesc), _I32, _VP, _VP, _I32, _VP]),
+    "lora_page_table_create": (_I32, [_VP, _I32, _I64, ctypes.POINTER(_VP)]),
+    "lora_page_table_destroy": (None, [_VP]),
+    "lora_page_table_admit": (_I32, [_VP, _VP, _I64, ctypes.POINTER(PageCopy), _I64,
+                                     ctypes.POINTER(_I64), ctypes.POINTER(_I32), _I64,
+                                     ctypes.POINTER(_I64)]),
+    "lora_page_table_tables": (_I32, [_VP, ctypes.POINTER(_I32), ctypes.POINTER(_I32),
+                                      ctypes.POINTER(_I32), ctypes.POINTER(_I64)]),
+    "lora_residency_table_ints": (_SZ, [_I32, _I64]),
+    "lora_residency_create": (_I32, [ctypes.POINTER(ResidencyConfig), ctypes.POINTER(_VP)]),
+    "lora_residency_destroy": (None, [_VP]),
+    "lora_residency_prepare": (_I32, [_VP, _VP, _I64, _VP, _VP, _PD]),
+    "lora_residency_finish": (_I32, [_VP, _VP]),
+    "lora_residency_stats": (_I32, [_VP, ctypes.POINTER(_I64)]),
+    "lora_residency_page_table": (_VP, [_VP]),
 }
 
 
@@ -122,7 +155,7 @@ def _ptr(t) -> Optional[int]:
 
 def _stream(stream) -> Optional[int]:
     if stream is not None:
-        return int(stream)
+        return int(getattr(stream, "cuda_stream", stream))
     import torch
     return int(torch.cuda.current_stream().cuda_stream)
 
@@ -306,3 +339,126 @@ def lora_merge_delta_layers(Ws, pools, merge_ids, coeffs, m: int, stream=None):
         arr[i].pool = p.desc
     _check("lora_merge_delta_layers", lib().lora_merge_delta_layers(
         arr, n, _ptr(merge_ids), _ptr(coeffs), m, _stream(stream)))
+
+
+# ---------------------------------------------------------------- pool residency
+
+def _host_i32(a):
+    import numpy as np
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+class PageTable:
+    """The residency policy alone (host object, no GPU)."""
+
+    def __init__(self, rank, n_pages: int, handle=None):
+        self._rank = _host_i32(rank)
+        self.N, self.n_pages = int(self._rank.size), int(n_pages)
+        self._own = handle is None
+        if handle is None:
+            h = _VP()
+            _check("lora_page_table_create", lib().lora_page_table_create(
+                self._rank.ctypes.data, self.N, self.n_pages, ctypes.byref(h)))
+            handle = h.value
+        self.h = handle
+
+    def admit(self, ids):
+        """{"copies": [(adapter, row, page, count)], "evicted": [...]} or
+        {"error": "capacity"}."""
+        ids = _host_i32(ids).reshape(-1)
+        cp = (PageCopy * max(self.n_pages, 1))()
+        ev = (_I32 * max(self.N, 1))()
+        nc, ne = _I64(), _I64()
+        st = lib().lora_page_table_admit(self.h, ids.ctypes.data if ids.size else None, ids.size,
+                                         cp, self.n_pages, ctypes.byref(nc), ev, self.N,
+                                         ctypes.byref(ne))
+        if st == LORA_ERR_CAPACITY:
+            return {"error": "capacity"}
+        _check("lora_page_table_admit", st)
+        return {"copies": [(c.adapter, c.row, c.page, c.count) for c in cp[:nc.value]],
+                "evicted": [int(v) for v in ev[:ne.value]]}
+
+    def tables(self):
+        import numpy as np
+        rk = np.zeros(self.N, np.int32)
+        ps = np.zeros(self.N + 1, np.int32)
+        pid = np.zeros(max(self.n_pages, 1), np.int32)
+        n = _I64()
+        _check("lora_page_table_tables", lib().lora_page_table_tables(
+            self.h, rk.ctypes.data_as(ctypes.POINTER(_I32)), ps.ctypes.data_as(ctypes.POINTER(_I32)),
+            pid.ctypes.data_as(ctypes.POINTER(_I32)), ctypes.byref(n)))
+        return rk, ps, pid[:n.value].copy()
+
+    def close(self):
+        if self._own and self.h:
+            lib().lora_page_table_destroy(self.h)
+        self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Residency:
+    """The GPU pool of one projection, filled from a pinned host store on a
+    copy stream (lora_residency_*).  `store_a`/`store_b` are pinned CPU torch
+    tensors [rows][d]; `a_pages`/`b_pages` device tensors [n_pages][d]."""
+
+    def __init__(self, dtype, d_in, d_out, rank, store_row, store_a, store_b, a_pages, b_pages,
+                 scale):
+        import numpy as np
+        import torch
+        self._rank = _host_i32(rank)
+        self._row = np.ascontiguousarray(np.asarray(store_row, dtype=np.int64))
+        self.N, self.n_pages = int(self._rank.size), int(a_pages.shape[0])
+        nt = int(lib().lora_residency_table_ints(self.N, self.n_pages))
+        self.tables = torch.zeros(nt, dtype=torch.int32, device=a_pages.device)
+        self.staging = torch.zeros(nt, dtype=torch.int32).pin_memory()
+        self._keep = (store_a, store_b, a_pages, b_pages, scale)
+        self.cfg = ResidencyConfig(dtype, d_in, d_out, self.N, self.n_pages, self._rank.ctypes.data,
+                                   self._row.ctypes.data, _ptr(store_a), _ptr(store_b),
+                                   _ptr(a_pages), _ptr(b_pages), _ptr(scale), _ptr(self.tables),
+                                   _ptr(self.staging))
+        h = _VP()
+        _check("lora_residency_create", lib().lora_residency_create(ctypes.byref(self.cfg),
+                                                                    ctypes.byref(h)))
+        self.h = h.value
+        self.dtype, self.d_in, self.d_out = dtype, d_in, d_out
+
+    def prepare(self, ids, copy_stream, compute_stream=None):
+        """Returns a Pool (descriptor of the batch's tables) for the batch."""
+        ids = _host_i32(ids).reshape(-1)
+        desc = PoolDesc()
+        st = lib().lora_residency_prepare(self.h, ids.ctypes.data if ids.size else None, ids.size,
+                                          _stream(copy_stream), _stream(compute_stream),
+                                          ctypes.byref(desc))
+        _check("lora_residency_prepare", st)
+        p = Pool.__new__(Pool)
+        p.tensors = self._keep + (self.tables,)
+        p.dtype, p.d_in, p.d_out, p.n_adapters = self.dtype, self.d_in, self.d_out, self.N
+        p.desc = desc
+        return p
+
+    def finish(self, compute_stream=None):
+        _check("lora_residency_finish", lib().lora_residency_finish(self.h, _stream(compute_stream)))
+
+    def stats(self):
+        out = (_I64 * 4)()
+        _check("lora_residency_stats", lib().lora_residency_stats(self.h, out))
+        return {"batches": out[0], "rows_copied": out[1], "evictions": out[2], "bytes": out[3]}
+
+    def page_table(self):
+        return PageTable(self._rank, self.n_pages, handle=lib().lora_residency_page_table(self.h))
+
+    def close(self):
+        if self.h:
+            lib().lora_residency_destroy(self.h)
+        self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

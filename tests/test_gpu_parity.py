@@ -803,3 +803,64 @@ def test_merge_layers_rejects_shared_weight_and_mixed_dtype():
     with pytest.raises(B.LoraError) as ei:
         B.lora_merge_delta_layers([W, f.W_t], [Ls[0].pool, f.pool], mi, cf, 2)
     assert ei.value.status == B.LORA_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------- pool residency
+
+def test_residency_batches_match_a_fully_resident_pool():
+    """Adapters streamed from a pinned host store into a pool that holds
+    85 % of their rank rows: each batch's copies run on a side stream while
+    the previous batch computes; every batch's Y equals lora_forward over the
+    fully resident pool bit for bit, the tables equal the policy oracle's, and
+    every resident adapter's pages hold its rows."""
+    from oracle import residency as RO
+    w = wl.config(3, T=96, d_in=512, d_out=1344, n_adapters=60, seed=303)
+    L = D.DeviceLayer(w)
+    # host store: adapter a's rows in rank-row order
+    rows = np.concatenate([w.page_ids[w.page_start[a]:w.page_start[a + 1]]
+                           for a in range(w.n_adapters)]).astype(np.int64)
+    store_row = w.page_start[:-1].astype(np.int64)
+    sa = D.to_device(w.a_pages[rows], "cpu").pin_memory()
+    sb = D.to_device(w.b_pages[rows], "cpu").pin_memory()
+    n_pages = int(0.85 * int(w.rank.sum()))     # two batches fit; later ones evict
+    ap = torch.zeros((n_pages, w.d_in), dtype=torch.bfloat16, device="cuda")
+    bp = torch.zeros((n_pages, w.d_out), dtype=torch.bfloat16, device="cuda")
+    res = B.Residency(B.LORA_BF16, w.d_in, w.d_out, w.rank, store_row, sa, sb, ap, bp, L.scale)
+    side = torch.cuda.Stream()
+    rng = np.random.default_rng(7)
+    batches = [wl.zipf_ids(rng, w.T, w.n_adapters).reshape(w.T, 1) for _ in range(6)]
+    oracle = RO.trace(w.rank, n_pages, batches)
+    outs, refs = [], []
+    plan = torch.empty_like(L.plan)
+    for b, ids in enumerate(batches):
+        print(f"residency batch {b}", flush=True)
+        ids_d = D.to_device(ids, "cuda")
+        pool = res.prepare(ids, side)
+        Y = torch.empty_like(L.Y)
+        B.lora_forward(ids_d, L.gates, w.T, 1, L.X, L.W_t, Y, None, 1.0, pool, plan, L.ws)
+        res.finish()
+        outs.append(Y)
+        Yr = torch.empty_like(L.Y)
+        plan_r = torch.empty_like(L.plan)
+        ws_r = torch.empty_like(L.ws)
+        B.lora_forward(ids_d, L.gates, w.T, 1, L.X, L.W_t, Yr, None, 1.0, L.pool, plan_r, ws_r)
+        refs.append(Yr)
+        # host tables of the library's policy = the oracle's
+        rk, ps, pid = res.page_table().tables()
+        assert "error" not in oracle[b]
+        assert np.array_equal(rk, oracle[b]["rank"]) and np.array_equal(pid, oracle[b]["page_ids"])
+    torch.cuda.synchronize()
+    for b in range(len(batches)):
+        assert np.array_equal(D.to_host(outs[b]), D.to_host(refs[b])), f"batch {b}"
+    # the pool now holds every resident adapter's rows
+    rk, ps, pid = res.page_table().tables()
+    A, Bh = D.to_host(ap), D.to_host(bp)
+    for a in range(w.n_adapters):
+        if rk[a] == 0:
+            continue
+        pg = pid[ps[a]:ps[a + 1]]
+        src = w.page_ids[w.page_start[a]:w.page_start[a + 1]]
+        assert np.array_equal(A[pg], w.a_pages[src]) and np.array_equal(Bh[pg], w.b_pages[src])
+    st = res.stats()
+    assert st["batches"] == 6 and st["evictions"] > 0
+    res.close()

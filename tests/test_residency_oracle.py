@@ -70,3 +70,48 @@ def test_random_traces_keep_the_invariants(seed):
             assert a not in pt.resident and a not in need and a not in prev_batch
         rk, ps, pid = pt.tables()
         assert ps[-1] == len(pid) and np.all(np.diff(ps) == rk)
+
+
+# ---------------------------------------------------------------- the library's page table
+
+def _lib_trace(rank, n_pages, batches):
+    from lora_adapter_amd import binding as B
+    pt = B.PageTable(rank, n_pages)
+    out = []
+    for ids in batches:
+        res = pt.admit(ids)
+        rk, ps, pid = pt.tables()
+        out.append(dict(res, rank=rk, page_start=ps, page_ids=pid))
+    pt.close()
+    return out
+
+
+def _same(a, b):
+    assert a.get("error") == b.get("error")
+    if "error" not in a:
+        assert [tuple(c) for c in a["copies"]] == [tuple(c) for c in b["copies"]]
+        assert list(a["evicted"]) == list(b["evicted"])
+    for k in ("rank", "page_start", "page_ids"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_library_page_table_matches_the_golden_trace():
+    g = json.load(open(GOLD))
+    for a, e in zip(_lib_trace(g["rank"], g["n_pages"], g["batches"]), g["expected"]):
+        e = dict(e)
+        for k in ("rank", "page_start", "page_ids"):
+            e[k] = np.asarray(e[k], np.int32)
+        _same(a, e)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_library_page_table_matches_the_oracle(seed):
+    """The host policy in the library, through the C ABI, against the oracle
+    on random traces: copies, evictions and tables bit for bit."""
+    rng = np.random.default_rng(100 + seed)
+    N = int(rng.integers(3, 200))
+    rank = rng.integers(0, 17, size=N)
+    n_pages = int(rng.integers(16, 400))
+    batches = [rng.integers(-2, N + 2, size=int(rng.integers(0, 24))) for _ in range(80)]
+    for a, b in zip(_lib_trace(rank, n_pages, batches), R.trace(rank, n_pages, batches)):
+        _same(a, b)
