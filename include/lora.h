@@ -420,6 +420,27 @@ int32_t lora_residency_stats(const lora_residency *r, int64_t out[4]);
 /* The object's page table (read it with lora_page_table_tables). */
 const lora_page_table *lora_residency_page_table(const lora_residency *r);
 
+/* ------------------------------------------------------- tall-skinny QR
+ * Batched thin QR of M tall, skinny matrices ([LoRAForge] section
+ * FlashTSQR：批量因子构造的加速器 and its TSQR note: QR factorisations of
+ * thousands of adapter modules for post-hoc compression, computed as local
+ * QRs of row blocks merged afterwards, parallel over modules and row blocks):
+ *   A_i = Q_i . R_i,  Q_i m x n with orthonormal columns, R_i n x n upper
+ *   triangular with a non-negative diagonal (unique for full column rank).
+ * Matrix i is given by its n columns: column j is row cols[i * n + j] of src
+ * ([rows][m], dtype), so an adapter's A (its pages of a_pages, m = d_in) or
+ * B^T (its pages of b_pages, m = d_out) is factored where it lies.
+ *   cols  device int32 [M * n];  1 <= n <= 64, n <= m <= 2^24.
+ *   Qt    device float32 [M][n][m] (Q's columns, the page layout) or NULL.
+ *   R     device float32 [M][n][n] row-major.
+ *   ws    >= lora_tsqr_workspace_bytes(M, m, n) bytes.
+ * Float32 Householder reflections; a zero column below the diagonal takes
+ * none (its R diagonal entry is then the column's own entry, sign-fixed).
+ * Errors: INVALID_ARG, UNSUPPORTED (shape), CAPACITY (ws), DEVICE. */
+size_t lora_tsqr_workspace_bytes(int32_t M, int32_t m, int32_t n);
+int32_t lora_tsqr(const void *src, int32_t dtype, const int32_t *cols, int32_t M, int32_t m,
+                  int32_t n, float *Qt, float *R, void *ws, size_t ws_bytes, void *stream);
+
 /* ------------------------------------------------------------ grad of X
  * Input gradient of the fine-tune backward, handed to the layer below
  * ([LoRAFusion] 解决什么真问题: W frozen, A and B trained, dropout on the LoRA

@@ -33,7 +33,7 @@ EXPORTS = (
     "lora_page_table_create", "lora_page_table_destroy", "lora_page_table_admit",
     "lora_page_table_tables", "lora_residency_table_ints", "lora_residency_create",
     "lora_residency_destroy", "lora_residency_prepare", "lora_residency_finish",
-    "lora_residency_stats", "lora_residency_page_table",
+    "lora_residency_stats", "lora_residency_page_table", "lora_tsqr_workspace_bytes", "lora_tsqr",
 )
 
 
@@ -122,6 +122,8 @@ _PROTOS = {
     "lora_residency_finish": (_I32, [_VP, _VP]),
     "lora_residency_stats": (_I32, [_VP, ctypes.POINTER(_I64)]),
     "lora_residency_page_table": (_VP, [_VP]),
+    "lora_tsqr_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+    "lora_tsqr": (_I32, [_VP, _I32, _VP, _I32, _I32, _I32, _VP, _VP, _VP, _SZ, _VP]),
 }
 
 
@@ -462,3 +464,14 @@ class Residency:
             self.close()
         except Exception:
             pass
+
+
+# ---------------------------------------------------------------- tall-skinny QR
+
+def lora_tsqr_workspace_bytes(M: int, m: int, n: int) -> int:
+    return int(lib().lora_tsqr_workspace_bytes(M, m, n))
+
+
+def lora_tsqr(src, dtype: int, cols, M: int, m: int, n: int, Qt, R, ws, stream=None):
+    _check("lora_tsqr", lib().lora_tsqr(_ptr(src), dtype, _ptr(cols), M, m, n, _ptr(Qt), _ptr(R),
+                                        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))

@@ -628,3 +628,23 @@ int32_t lora_grad_x(const void *dY, const void *W, const uint8_t *keep_mask, int
 }
 
 }  // extern "C"
+
+extern "C" {
+
+size_t lora_tsqr_workspace_bytes(int32_t M, int32_t m, int32_t n) {
+  if (!tsqr_shape_ok(M, m, n) || m > (1 << 24)) return 0;
+  return align_up(tsqr_workspace_bytes(M, m, n));
+}
+
+int32_t lora_tsqr(const void *src, int32_t dtype, const int32_t *cols, int32_t M, int32_t m,
+                  int32_t n, float *Qt, float *R, void *ws, size_t ws_bytes, void *stream) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_INVALID_ARG;
+  if (M < 0 || m < 1 || n < 1) return LORA_ERR_INVALID_ARG;
+  if (M == 0) return LORA_OK;
+  if (!tsqr_shape_ok(M, m, n) || m > (1 << 24)) return LORA_ERR_UNSUPPORTED;
+  if (!src || !cols || !R || !ws) return LORA_ERR_INVALID_ARG;
+  if (ws_bytes < lora_tsqr_workspace_bytes(M, m, n)) return LORA_ERR_CAPACITY;
+  return dev(launch_tsqr(src, dtype, cols, M, m, n, Qt, R, ws, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

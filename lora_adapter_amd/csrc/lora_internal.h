@@ -421,6 +421,12 @@ hipError_t launch_grad_x_epilogue(const GemmConfig &c, const GemmArgs &g, int dt
 hipError_t launch_transpose(const void *src, void *dst, int rows, int cols, int dtype,
                             hipStream_t s);
 
+// Batched tall-skinny QR (see tsqr.hip).
+bool tsqr_shape_ok(int M, int m, int n);
+size_t tsqr_workspace_bytes(int M, int m, int n);
+hipError_t launch_tsqr(const void *src, int dtype, const int32_t *cols, int M, int m, int n,
+                       float *Qt, float *R, void *ws, hipStream_t s);
+
 hipError_t launch_merge(const MergeArgs &a, int dtype, hipStream_t s);
 // n layers' merges (same list, each layer's own W and pool): one launch per
 // LORA_MERGE_MAX_LAYERS layers when every layer takes the MFMA form.

@@ -1,0 +1,275 @@
+// Batched tall-skinny QR (TSQR) of many m x n matrices, n <= 64.
+//
+// The LoRAForge page ("LoRAForge：压缩与执行协同，让多LoRA服务更高效", section
+// FlashTSQR：批量因子构造的加速器 and its glossary note on TSQR) describes the
+// factor construction of post-hoc adapter compression as QR factorisations
+// of thousands of tall, skinny matrices, computed by local QRs of row blocks
+// whose triangular factors are then merged, with parallelism across modules
+// and across row blocks.  Here:
+//   * level 0: one workgroup per (matrix, 256-row tile) factors its tile by
+//     Householder reflections in LDS (float32, column-major, reductions by a
+//     fixed butterfly then a fixed 4-wave sum: deterministic); the tile's
+//     n x n triangle becomes n rows of the level-1 matrix, the stack of all
+//     tiles' triangles;
+//   * the same kernel factors level 1, 2, ... until a level is one tile;
+//   * Q is formed top-down: a tile's Q block is its reflectors applied, last
+//     to first, to [the tile's n x n block of the level above's Q ; 0]; the
+//     top level starts from the diagonal of signs that makes diag(R) >= 0.
+// A matrix is given by its n columns, each a row of length m of a source
+// array selected through an index table: the pages of an adapter pool (A's
+// column j = one page, B^T's column j = one page) are factored where they
+// are.  Rows past m in a tile are zero; a zero column (below the diagonal)
+// takes no reflection.
+#include "lora_internal.h"
+
+namespace lora {
+namespace {
+
+constexpr int kTR = 256;        // rows per tile
+constexpr int kTN = 64;         // most columns
+
+struct TsqrLevel {
+  // input of the level: level 0 gathers column j of matrix i from row
+  // cols[i * n + j] of src ([rows][m], dtype); higher levels read
+  // X [M][n][m_l] (float32, columns contiguous)
+  const void *src;
+  const int32_t *cols;
+  const float *X;
+  int m_l;              // rows of this level's matrices
+  int tiles;            // ceil(m_l / kTR)
+  int n, M;
+  float *V;             // [M][n][m_l] reflectors (v_j = 1 implicit at the diagonal)
+  float *tau;           // [M][tiles][n]
+  float *Xn;            // next level's input [M][n][tiles * n], or null at the top
+  float *R;             // top level: R [M][n][n] with diag >= 0
+  float *sgn;           // top level: [M][n] the signs applied
+};
+
+__device__ __forceinline__ float block_sum4(float v, float *red) {
+  // butterfly within the wave, then the four wave sums in order
+  v = wave_sum(v);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  const float s = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+  return s;
+}
+
+template <typename E, bool kLevel0>
+__global__ __launch_bounds__(256) void tsqr_factor_kernel(TsqrLevel a) {
+  __shared__ float col[kTN][kTR];       // the tile, column-major
+  __shared__ float s_tau[kTN];
+  __shared__ float red[4];
+  const int tile = blockIdx.x, mat = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = a.n;
+  const int r0 = tile * kTR;
+  const int rows = min(kTR, a.m_l - r0);
+  // load: thread tid owns row tid of every column
+  for (int c = 0; c < n; ++c) {
+    float v = 0.f;
+    if (tid < rows) {
+      if constexpr (kLevel0) {
+        const int64_t srow = a.cols[int64_t(mat) * n + c];
+        v = Elem<E>::to_f(static_cast<const E *>(a.src)[srow * a.m_l + r0 + tid]);
+      } else {
+        v = a.X[(int64_t(mat) * n + c) * a.m_l + r0 + tid];
+      }
+    }
+    col[c][tid] = v;
+  }
+  __syncthreads();
+  for (int j = 0; j < n; ++j) {
+    // reflector for column j, rows j.. of the tile
+    const float x = tid >= j ? col[j][tid] : 0.f;
+    const float xj = col[j][j];
+    const float below = block_sum4(tid > j ? x * x : 0.f, red);
+    float beta = xj, tau = 0.f, scl = 0.f;
+    if (below > 0.f) {
+      const float nrm = sqrtf(xj * xj + below);
+      beta = xj >= 0.f ? -nrm : nrm;
+      tau = (beta - xj) / beta;
+      scl = 1.f / (xj - beta);
+    }
+    if (tid > j) col[j][tid] = x * scl;       // v (v_j = 1 implicit)
+    if (tid == 0) {
+      col[j][j] = beta;
+      s_tau[j] = tau;
+    }
+    __syncthreads();
+    // apply H_j to columns j+1 .. n-1, one wave per column
+    if (tau != 0.f) {
+      float v4[kTR / 64];
+#pragma unroll
+      for (int q = 0; q < kTR / 64; ++q) {
+        const int r = lane + 64 * q;
+        v4[q] = r > j ? col[j][r] : (r == j ? 1.f : 0.f);
+      }
+      for (int c = j + 1 + wave; c < n; c += 4) {
+        float d = 0.f;
+#pragma unroll
+        for (int q = 0; q < kTR / 64; ++q) d = fmaf(v4[q], col[c][lane + 64 * q], d);
+        const float w = tau * wave_sum(d);
+#pragma unroll
+        for (int q = 0; q < kTR / 64; ++q) {
+          const int r = lane + 64 * q;
+          if (r >= j) col[c][r] = fmaf(-w, v4[q], col[c][r]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // reflectors and taus out
+  float *V = a.V + int64_t(mat) * n * a.m_l;
+  for (int c = 0; c < n; ++c)
+    if (tid < rows) V[int64_t(c) * a.m_l + r0 + tid] = tid > c ? col[c][tid] : 0.f;
+  if (tid < n) a.tau[(int64_t(mat) * a.tiles + tile) * n + tid] = s_tau[tid];
+  // the tile's triangle: rows i <= c of column c (zero rows where the tile
+  // had fewer rows than columns)
+  if (a.Xn) {
+    const int mn = a.tiles * n;
+    for (int c = 0; c < n; ++c)
+      if (tid < n) a.Xn[(int64_t(mat) * n + c) * mn + tile * n + tid] = tid <= c ? col[c][tid] : 0.f;
+  } else {
+    // top: R with the signs that make its diagonal non-negative
+    __shared__ float s_sg[kTN];
+    if (tid < n) s_sg[tid] = col[tid][tid] < 0.f ? -1.f : 1.f;
+    __syncthreads();
+    for (int c = 0; c < n; ++c)
+      if (tid < n) a.R[(int64_t(mat) * n + tid) * n + c] = tid <= c ? s_sg[tid] * col[c][tid] : 0.f;
+    if (tid < n) a.sgn[int64_t(mat) * n + tid] = s_sg[tid];
+  }
+}
+
+struct TsqrForm {
+  const float *V, *tau;    // this level's reflectors
+  int m_l, tiles, n, M;
+  const float *Qup;        // [M][n][tiles * n] the level above's Q, or null at the top
+  const float *sgn;        // top: [M][n]
+  float *Q;                // this level's Q [M][n][m_l] (level 0: the output Qt)
+};
+
+__global__ __launch_bounds__(256) void tsqr_form_kernel(TsqrForm a) {
+  __shared__ float C[kTN][kTR];
+  __shared__ float Vs[kTN][kTR];
+  const int tile = blockIdx.x, mat = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = a.n;
+  const int r0 = tile * kTR;
+  const int rows = min(kTR, a.m_l - r0);
+  const float *V = a.V + int64_t(mat) * n * a.m_l;
+  for (int c = 0; c < n; ++c) {
+    Vs[c][tid] = tid < rows ? V[int64_t(c) * a.m_l + r0 + tid] : 0.f;
+    float b = 0.f;
+    if (tid < n) {
+      if (a.Qup) b = a.Qup[(int64_t(mat) * n + c) * (int64_t(a.tiles) * n) + tile * n + tid];
+      else b = tid == c ? a.sgn[int64_t(mat) * n + c] : 0.f;
+    }
+    C[c][tid] = b;
+  }
+  __syncthreads();
+  const float *tau = a.tau + (int64_t(mat) * a.tiles + tile) * n;
+  for (int j = n - 1; j >= 0; --j) {
+    const float t = tau[j];
+    if (t != 0.f) {
+      float v4[kTR / 64];
+#pragma unroll
+      for (int q = 0; q < kTR / 64; ++q) {
+        const int r = lane + 64 * q;
+        v4[q] = r > j ? Vs[j][r] : (r == j ? 1.f : 0.f);
+      }
+      for (int c = wave; c < n; c += 4) {
+        float d = 0.f;
+#pragma unroll
+        for (int q = 0; q < kTR / 64; ++q) d = fmaf(v4[q], C[c][lane + 64 * q], d);
+        const float w = t * wave_sum(d);
+#pragma unroll
+        for (int q = 0; q < kTR / 64; ++q) {
+          const int r = lane + 64 * q;
+          if (r >= j) C[c][r] = fmaf(-w, v4[q], C[c][r]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  float *Q = a.Q + int64_t(mat) * n * a.m_l;
+  for (int c = 0; c < n; ++c)
+    if (tid < rows) Q[int64_t(c) * a.m_l + r0 + tid] = C[c][tid];
+}
+
+// Rows of each level: m, then tiles * n while more than one tile.
+int tsqr_levels(int m, int n, int out_m[16]) {
+  int L = 0, ml = m;
+  while (true) {
+    out_m[L++] = ml;
+    const int t = (ml + kTR - 1) / kTR;
+    if (t == 1 || L == 16) break;
+    ml = t * n;
+  }
+  return L;
+}
+
+}  // namespace
+
+bool tsqr_shape_ok(int M, int m, int n) { return M >= 1 && n >= 1 && n <= kTN && m >= n; }
+
+size_t tsqr_workspace_bytes(int M, int m, int n) {
+  int ml[16];
+  const int L = tsqr_levels(m, n, ml);
+  size_t f = 0;
+  for (int l = 0; l < L; ++l) {
+    const size_t tiles = size_t((ml[l] + kTR - 1) / kTR);
+    f += 2 * size_t(M) * n * ml[l];         // V, and X (level > 0) / Q (level > 0)
+    f += size_t(M) * tiles * n;             // tau
+  }
+  f += size_t(M) * n;                       // signs
+  return f * sizeof(float);
+}
+
+hipError_t launch_tsqr(const void *src, int dtype, const int32_t *cols, int M, int m, int n,
+                       float *Qt, float *R, void *ws, hipStream_t s) {
+  int ml[16];
+  const int L = tsqr_levels(m, n, ml);
+  float *p = static_cast<float *>(ws);
+  float *V[16], *X[16], *tau[16];
+  for (int l = 0; l < L; ++l) {
+    const int tiles = (ml[l] + kTR - 1) / kTR;
+    V[l] = p; p += size_t(M) * n * ml[l];
+    X[l] = p; p += size_t(M) * n * ml[l];    // level l's input (level 0: unused) and Q (l > 0)
+    tau[l] = p; p += size_t(M) * tiles * n;
+  }
+  float *sgn = p;
+  for (int l = 0; l < L; ++l) {
+    TsqrLevel a{};
+    a.src = src; a.cols = cols; a.X = X[l];
+    a.m_l = ml[l]; a.tiles = (ml[l] + kTR - 1) / kTR; a.n = n; a.M = M;
+    a.V = V[l]; a.tau = tau[l];
+    a.Xn = l + 1 < L ? X[l + 1] : nullptr;
+    a.R = R; a.sgn = sgn;
+    const dim3 grid(unsigned(a.tiles), unsigned(M)), block(256);
+    if (l == 0) {
+      if (dtype == LORA_BF16) hipLaunchKernelGGL((tsqr_factor_kernel<uint16_t, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((tsqr_factor_kernel<float, true>), grid, block, 0, s, a);
+    } else {
+      hipLaunchKernelGGL((tsqr_factor_kernel<float, false>), grid, block, 0, s, a);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!Qt) return hipSuccess;
+  // Q top-down; level l > 0 writes its Q over its input X[l] (no longer read)
+  for (int l = L - 1; l >= 0; --l) {
+    TsqrForm f{};
+    f.V = V[l]; f.tau = tau[l]; f.m_l = ml[l]; f.tiles = (ml[l] + kTR - 1) / kTR; f.n = n; f.M = M;
+    f.Qup = l + 1 < L ? X[l + 1] : nullptr;
+    f.sgn = sgn;
+    f.Q = l == 0 ? Qt : X[l];
+    hipLaunchKernelGGL(tsqr_form_kernel, dim3(unsigned(f.tiles), unsigned(M)), dim3(256), 0, s, f);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace lora

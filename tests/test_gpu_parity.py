@@ -864,3 +864,64 @@ def test_residency_batches_match_a_fully_resident_pool():
     st = res.stats()
     assert st["batches"] == 6 and st["evictions"] > 0
     res.close()
+
+
+# ---------------------------------------------------------------- tall-skinny QR
+
+def _tsqr_gpu(src, dtype, cols, M, m, n):
+    Qt = torch.full((M, n, m), float("nan"), dtype=torch.float32, device="cuda")
+    R = torch.full((M, n, n), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(B.lora_tsqr_workspace_bytes(M, m, n), dtype=torch.uint8, device="cuda")
+    B.lora_tsqr(src, dtype, cols, M, m, n, Qt, R, ws)
+    torch.cuda.synchronize()
+    return Qt.cpu().numpy().astype(np.float64), R.cpu().numpy().astype(np.float64)
+
+
+TSQR_TOL = 1e-5
+
+
+@pytest.mark.parametrize("M,m,n", [(5, 1000, 16), (3, 300, 64), (2, 11008, 64), (4, 4096, 1),
+                                   (3, 512, 2), (6, 64, 64), (2, 257, 33)])
+def test_tsqr_fp32_matches_oracle(M, m, n):
+    """Level counts 1..4, ragged last tiles, square and one-column matrices."""
+    from oracle import tsqr as TQ
+    rng = np.random.default_rng(M * 1000 + m + n)
+    A = rng.standard_normal((M, n, m)).astype(np.float32)
+    cols = D.to_device(np.arange(M * n, dtype=np.int32), "cuda")
+    print(f"tsqr fp32 M={M} m={m} n={n}", flush=True)
+    Qt, R = _tsqr_gpu(D.to_device(A.reshape(M * n, m), "cuda"), B.LORA_F32, cols, M, m, n)
+    Qo, Ro = TQ.batched_thin_qr(A)
+    assert rel_err(R, Ro) <= TSQR_TOL
+    assert rel_err(Qt, Qo) <= TSQR_TOL
+    assert np.all(np.tril(R, -1) == 0) and np.all(np.diagonal(R, axis1=1, axis2=2) >= 0)
+
+
+def test_tsqr_bf16_adapter_pages_in_place():
+    """The A factors of a pool's adapters (rank 16, d_in 4096), each matrix's
+    columns gathered from its pages; the B^T factors likewise (d_out 11008)."""
+    from oracle import tsqr as TQ
+    w = wl.config(4, T=64, d_in=4096, d_out=11008, seed=41)
+    L = D.DeviceLayer(w)
+    M, n = w.n_adapters, 16
+    cols_h = np.concatenate([w.page_ids[w.page_start[a]:w.page_start[a + 1]] for a in range(M)])
+    cols = D.to_device(cols_h.astype(np.int32), "cuda")
+    for pages, d, host in ((L.a_pages, w.d_in, w.a_pages), (L.b_pages, w.d_out, w.b_pages)):
+        Qt, R = _tsqr_gpu(pages, B.LORA_BF16, cols, M, d, n)
+        At = wl.to_f32(host[cols_h]).reshape(M, n, d)
+        Qo, Ro = TQ.batched_thin_qr(At)
+        assert rel_err(R, Ro) <= TSQR_TOL
+        assert rel_err(Qt, Qo) <= TSQR_TOL
+
+
+def test_tsqr_zero_column():
+    """A zero column takes no reflection: R's column is zero there and
+    Q.R still equals A."""
+    rng = np.random.default_rng(5)
+    M, m, n = 2, 700, 8
+    A = rng.standard_normal((M, n, m)).astype(np.float32)
+    A[1, 3] = 0.0
+    cols = D.to_device(np.arange(M * n, dtype=np.int32), "cuda")
+    Qt, R = _tsqr_gpu(D.to_device(A.reshape(M * n, m), "cuda"), B.LORA_F32, cols, M, m, n)
+    assert np.all(R[1][:, 3] == 0)
+    for i in range(M):
+        assert rel_err(Qt[i].T @ R[i], A[i].T.astype(np.float64)) <= TSQR_TOL
