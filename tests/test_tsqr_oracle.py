@@ -64,3 +64,46 @@ def test_batched_layout_is_columns_per_row():
     Qt, R = TQ.batched_thin_qr(At)
     for i in range(3):
         np.testing.assert_allclose(Qt[i].T @ R[i], At[i].T, atol=1e-12)
+
+
+# ---------------------------------------------------------------- recompression
+
+def _gold_module():
+    g = json.load(open(GOLD))["compress"]
+    P = np.asarray(g["P_columns"], float).T
+    Q = np.asarray(g["Q_columns"], float).T
+    s = np.asarray(g["s"], float)
+    return g, P * s[None, :], Q.T
+
+
+def test_golden_retained_ranks_and_errors():
+    g, A, B = _gold_module()
+    for c in g["cases"]:
+        k, s, A2, B2 = TQ.compress(A, B, c["policy"], c.get("ratio", 1.0), c.get("energy", 1.0),
+                                   c["floor"])
+        assert k == c["k"], c
+        np.testing.assert_allclose(s, g["s"], atol=1e-12)
+        err = np.sum((A @ B - A2 @ B2) ** 2)
+        assert abs(err - c["tail_energy"]) <= 1e-12
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_compression_is_the_best_rank_k_approximation(seed):
+    """Eckart-Young: the squared Frobenius error of A'.B' equals the energy of
+    the dropped singular values, which equal those of the n x n core
+    R_A.R_B^T (from the QRs of A and B^T: a route that never forms A.B)."""
+    rng = np.random.default_rng(seed)
+    d_in, d_out, n = 96, 80, 12
+    A = rng.standard_normal((d_in, n))
+    B = rng.standard_normal((n, d_out))
+    _, Ra = TQ.thin_qr(A)
+    _, Rb = TQ.thin_qr(B.T)
+    s_core = np.linalg.svd(Ra @ Rb.T, compute_uv=False)
+    for k_pol in ((1, 1.0, 0.8, 1), (0, 0.5, 1.0, 1), (1, 1.0, 0.1, 5)):
+        k, s, A2, B2 = TQ.compress(A, B, *k_pol)
+        np.testing.assert_allclose(s, s_core, rtol=1e-10)
+        err = np.sum((A @ B - A2 @ B2) ** 2)
+        np.testing.assert_allclose(err, np.sum(s_core[k:] ** 2), rtol=1e-8, atol=1e-9)
+        # the new factors' columns / rows are orthogonal with norms sqrt(sigma)
+        np.testing.assert_allclose(A2.T @ A2, np.diag(s[:k]), atol=1e-9 * s[0])
+        np.testing.assert_allclose(B2 @ B2.T, np.diag(s[:k]), atol=1e-9 * s[0])
