@@ -441,6 +441,33 @@ size_t lora_tsqr_workspace_bytes(int32_t M, int32_t m, int32_t n);
 int32_t lora_tsqr(const void *src, int32_t dtype, const int32_t *cols, int32_t M, int32_t m,
                   int32_t n, float *Qt, float *R, void *ws, size_t ws_bytes, void *stream);
 
+/* Retained-rank recompression of M adapters of rank n ([LoRAForge]
+ * LoRAForge的核心设计: explicit retained ranks, LoRAForge-U a uniform fraction
+ * of each module's rank, LoRAForge-S by each module's spectral energy; the
+ * factors come from batched QRs, section FlashTSQR：批量因子构造的加速器).
+ * For adapter adapters[i] with factors A (d_in x n) and B (n x d_out) in the
+ * pool: A = Q_A.R_A and B^T = Q_B.R_B (lora_tsqr on its pages), the n x n core
+ * R_A.R_B^T = U.S.V^T (one-sided Jacobi, float64), retained rank
+ *   policy 0 (uniform):  k = ceil(ratio * n), product in float32;
+ *   policy 1 (spectral): the smallest k whose leading squared singular values
+ *                        reach the fraction `energy` of their sum;
+ *   then k = min(n, max(k, floor_rank, 1)),
+ * and the best rank-k factors A' = Q_A.U_k.sqrt(S_k), B' = sqrt(S_k).V_k^T.Q_B^T
+ * (A'.B' is the best rank-k approximation of A.B) are written, in the pool's
+ * dtype, as pages: column j of A' is row i * n + j of out_a [M * n][d_in], row
+ * j of B' row i * n + j of out_b [M * n][d_out], for j < k (other rows are not
+ * written).  out_rank [M] int32 (0 for an adapter whose rank is not n or
+ * whose page table is bad), out_sigma [M][n] float32 (descending).  All
+ * device memory; 1 <= n <= 64, n <= d_in, d_out; the adapter scale is not
+ * folded in (it stays the adapter's).
+ * Errors: INVALID_ARG, UNSUPPORTED, CAPACITY (ws below
+ * lora_compress_workspace_bytes), DEVICE. */
+size_t lora_compress_workspace_bytes(int32_t M, int32_t d_in, int32_t d_out, int32_t n);
+int32_t lora_compress(const lora_pool_desc *pool, const int32_t *adapters, int32_t M, int32_t n,
+                      int32_t policy, float ratio, float energy, int32_t floor_rank, void *out_a,
+                      void *out_b, int32_t *out_rank, float *out_sigma, void *ws, size_t ws_bytes,
+                      void *stream);
+
 /* ------------------------------------------------------------ grad of X
  * Input gradient of the fine-tune backward, handed to the layer below
  * ([LoRAFusion] 解决什么真问题: W frozen, A and B trained, dropout on the LoRA

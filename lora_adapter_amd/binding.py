@@ -34,6 +34,7 @@ EXPORTS = (
     "lora_page_table_tables", "lora_residency_table_ints", "lora_residency_create",
     "lora_residency_destroy", "lora_residency_prepare", "lora_residency_finish",
     "lora_residency_stats", "lora_residency_page_table", "lora_tsqr_workspace_bytes", "lora_tsqr",
+    "lora_compress_workspace_bytes", "lora_compress",
 )
 
 
@@ -124,6 +125,9 @@ _PROTOS = {
     "lora_residency_page_table": (_VP, [_VP]),
     "lora_tsqr_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "lora_tsqr": (_I32, [_VP, _I32, _VP, _I32, _I32, _I32, _VP, _VP, _VP, _SZ, _VP]),
+    "lora_compress_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+    "lora_compress": (_I32, [_PD, _VP, _I32, _I32, _I32, _F32, _F32, _I32, _VP, _VP, _VP, _VP, _VP,
+                             _SZ, _VP]),
 }
 
 
@@ -475,3 +479,15 @@ def lora_tsqr_workspace_bytes(M: int, m: int, n: int) -> int:
 def lora_tsqr(src, dtype: int, cols, M: int, m: int, n: int, Qt, R, ws, stream=None):
     _check("lora_tsqr", lib().lora_tsqr(_ptr(src), dtype, _ptr(cols), M, m, n, _ptr(Qt), _ptr(R),
                                         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def lora_compress_workspace_bytes(M: int, d_in: int, d_out: int, n: int) -> int:
+    return int(lib().lora_compress_workspace_bytes(M, d_in, d_out, n))
+
+
+def lora_compress(pool: Pool, adapters, M: int, n: int, policy: int, ratio: float, energy: float,
+                  floor_rank: int, out_a, out_b, out_rank, out_sigma, ws, stream=None):
+    _check("lora_compress", lib().lora_compress(
+        pool.ref, _ptr(adapters), M, n, policy, float(ratio), float(energy), floor_rank,
+        _ptr(out_a), _ptr(out_b), _ptr(out_rank), _ptr(out_sigma), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))

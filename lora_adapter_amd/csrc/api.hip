@@ -648,3 +648,32 @@ int32_t lora_tsqr(const void *src, int32_t dtype, const int32_t *cols, int32_t M
 }
 
 }  // extern "C"
+
+extern "C" {
+
+size_t lora_compress_workspace_bytes(int32_t M, int32_t d_in, int32_t d_out, int32_t n) {
+  if (M < 1 || n < 1 || n > 64 || !dims_ok(d_in) || !dims_ok(d_out) || n > d_in || n > d_out)
+    return 0;
+  return align_up(compress_workspace_bytes(M, d_in, d_out, n));
+}
+
+int32_t lora_compress(const lora_pool_desc *pool, const int32_t *adapters, int32_t M, int32_t n,
+                      int32_t policy, float ratio, float energy, int32_t floor_rank, void *out_a,
+                      void *out_b, int32_t *out_rank, float *out_sigma, void *ws, size_t ws_bytes,
+                      void *stream) {
+  int32_t st = check_pool(pool, true);
+  if (st != LORA_OK) return st;
+  if (M < 0 || n < 1 || (policy != 0 && policy != 1)) return LORA_ERR_INVALID_ARG;
+  if (!(ratio > 0.f && ratio <= 1.f) || !(energy > 0.f && energy <= 1.f) || floor_rank < 0)
+    return LORA_ERR_INVALID_ARG;
+  if (M == 0) return LORA_OK;
+  if (n > 64 || n > pool->d_in || n > pool->d_out) return LORA_ERR_UNSUPPORTED;
+  if (!adapters || !out_a || !out_b || !out_rank || !out_sigma || !ws || pool->n_pages < 1 ||
+      !pool->page_ids)
+    return LORA_ERR_INVALID_ARG;
+  if (ws_bytes < lora_compress_workspace_bytes(M, pool->d_in, pool->d_out, n)) return LORA_ERR_CAPACITY;
+  return dev(launch_compress(pool_view(pool), adapters, M, n, policy, ratio, energy, floor_rank,
+                             out_a, out_b, out_rank, out_sigma, ws, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

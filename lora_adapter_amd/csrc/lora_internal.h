@@ -427,6 +427,12 @@ size_t tsqr_workspace_bytes(int M, int m, int n);
 hipError_t launch_tsqr(const void *src, int dtype, const int32_t *cols, int M, int m, int n,
                        float *Qt, float *R, void *ws, hipStream_t s);
 
+// Retained-rank recompression (see compress.hip).
+size_t compress_workspace_bytes(int M, int d_in, int d_out, int n);
+hipError_t launch_compress(const PoolView &pool, const int32_t *adapters, int M, int n, int policy,
+                           float ratio, float energy, int floor_rank, void *out_a, void *out_b,
+                           int32_t *out_rank, float *out_sigma, void *ws, hipStream_t s);
+
 hipError_t launch_merge(const MergeArgs &a, int dtype, hipStream_t s);
 // n layers' merges (same list, each layer's own W and pool): one launch per
 // LORA_MERGE_MAX_LAYERS layers when every layer takes the MFMA form.

@@ -925,3 +925,62 @@ def test_tsqr_zero_column():
     assert np.all(R[1][:, 3] == 0)
     for i in range(M):
         assert rel_err(Qt[i].T @ R[i], A[i].T.astype(np.float64)) <= TSQR_TOL
+
+
+# ---------------------------------------------------------------- recompression
+
+def _spectral_fleet(dtype, M=12, n=16, d_in=512, d_out=704, seed=61):
+    """M adapters of rank n whose products A.B have prescribed, decaying
+    spectra (A = P.diag(s), B = Q^T, P and Q with orthonormal columns), plus
+    one adapter of another rank (its compression is refused: rank 0)."""
+    rng = np.random.default_rng(seed)
+    rank = np.full(M + 1, n, np.int32)
+    rank[M] = n // 2
+    w = wl.build("spectral-fleet", seed, dtype, 4, 1, d_in, d_out, rank,
+                 np.zeros((4, 1), np.int32), np.ones((4, 1), np.float32),
+                 x_var=1.0, w_var=0.02, a_var=1 / 64, b_var=0.02)
+    to = (lambda v: v.astype(np.float32)) if dtype == "f32" else \
+        (lambda v: wl.f32_to_bf16_bits(v.astype(np.float32)))
+    for a in range(M):
+        P, _ = np.linalg.qr(rng.standard_normal((d_in, n)))
+        Q, _ = np.linalg.qr(rng.standard_normal((d_out, n)))
+        s = 2.0 * 0.5 ** (np.arange(n) * rng.uniform(0.4, 1.2))
+        A, Bm = P * s[None, :], Q.T
+        pages = w.page_ids[w.page_start[a]:w.page_start[a + 1]]
+        w.a_pages[pages] = to(A.T)
+        w.b_pages[pages] = to(Bm)
+    return w, M + 1, n
+
+
+@pytest.mark.parametrize("dtype,policy", [("bf16", 1), ("bf16", 0), ("f32", 1)])
+def test_compress_matches_oracle(dtype, policy):
+    from oracle import tsqr as TQ
+    w, M, n = _spectral_fleet(dtype)
+    L = D.DeviceLayer(w)
+    ratio, energy, floor_rank = 0.3, 0.97, 2
+    ad = D.to_device(np.arange(M, dtype=np.int32), "cuda")
+    et = torch.float32 if dtype == "f32" else torch.bfloat16
+    oa = torch.zeros((M * n, w.d_in), dtype=et, device="cuda")
+    ob = torch.zeros((M * n, w.d_out), dtype=et, device="cuda")
+    ork = torch.full((M,), -7, dtype=torch.int32, device="cuda")
+    osg = torch.zeros((M, n), dtype=torch.float32, device="cuda")
+    ws = torch.empty(B.lora_compress_workspace_bytes(M, w.d_in, w.d_out, n), dtype=torch.uint8,
+                     device="cuda")
+    B.lora_compress(L.pool, ad, M, n, policy, ratio, energy, floor_rank, oa, ob, ork, osg, ws)
+    torch.cuda.synchronize()
+    k_gpu, sig = ork.cpu().numpy(), osg.cpu().numpy().astype(np.float64)
+    A2, B2 = D.as_f64(D.to_host(oa)), D.as_f64(D.to_host(ob))
+    tol = TOL[dtype]
+    for a in range(M):
+        if w.rank[a] != n:
+            assert k_gpu[a] == 0
+            continue
+        Ad, Bd = O.factors(a, w.rank, w.page_start, w.page_ids, w.a_pages, w.b_pages)
+        k, s, Ao, Bo = TQ.compress(Ad, Bd, policy, ratio, energy, floor_rank)
+        # the decision has margin: the oracle's cumulative energy is not at the threshold
+        cum = np.cumsum(s ** 2) / np.sum(s ** 2)
+        assert policy == 0 or np.min(np.abs(cum - np.float32(energy))) > 1e-4
+        assert k_gpu[a] == k, (a, k_gpu[a], k)
+        assert rel_err(sig[a], s) <= 1e-5
+        prod = A2[a * n:a * n + k].T @ B2[a * n:a * n + k]
+        assert rel_err(prod, Ao @ Bo) <= tol, a
