@@ -84,6 +84,7 @@ def parse():
                     help="1: also time the heterogeneous-rank workload with its pool held to "
                          "--residency-frac of the fleet (pages copied in from pinned host memory)")
     ap.add_argument("--residency-frac", type=float, default=0.6)
+    ap.add_argument("--no-tsqr", action="store_true", help="skip the fleet QR/compression timing")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs of a --copy-probe run into "
@@ -489,6 +490,61 @@ def gemm_roofline(w, L, B, kind, st, base_flops, P, R_pairs, R_used, e):
     return r
 
 
+def tsqr_bench(torch, np, B):
+    """Factor construction for a fleet of 1024 rank-16 adapters of a 4096 x
+    4096 projection (bf16 pages, seeded synthetic): the batched QR of every A
+    (lora_tsqr, with Q), and the whole recompression to retained ranks
+    (lora_compress: QRs of A and B^T, core SVDs, new factors); torch's batched
+    QR (the ROCm library routine) on the same A matrices in float32 beside it,
+    as context."""
+    M, n, d = 1024, 16, 4096
+    g = torch.Generator(device="cuda").manual_seed(77)
+    a = (torch.randn((M * n, d), generator=g, device="cuda") / 8).to(torch.bfloat16)
+    b = (torch.randn((M * n, d), generator=g, device="cuda") * 0.14).to(torch.bfloat16)
+    cols = torch.arange(M * n, dtype=torch.int32, device="cuda")
+    Qt = torch.empty((M, n, d), dtype=torch.float32, device="cuda")
+    R = torch.empty((M, n, n), dtype=torch.float32, device="cuda")
+    ws = torch.empty(B.lora_tsqr_workspace_bytes(M, d, n), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def ev(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+    t_tsqr = ev(lambda: B.lora_tsqr(a, B.LORA_BF16, cols, M, d, n, Qt, R, ws))
+    A32 = a.float().view(M, n, d).transpose(1, 2).contiguous()
+    try:
+        t_lib = ev(lambda: torch.linalg.qr(A32, mode="reduced"), reps=3)
+    except Exception:
+        t_lib = None
+    rank = torch.full((M,), n, dtype=torch.int32, device="cuda")
+    ps = torch.arange(0, M * n + 1, n, dtype=torch.int32, device="cuda")
+    scale = torch.ones(M, dtype=torch.float32, device="cuda")
+    pool = B.Pool(B.LORA_BF16, d, d, a, b, rank, ps, cols, scale)
+    oa, ob = torch.empty_like(a), torch.empty_like(b)
+    ork = torch.empty(M, dtype=torch.int32, device="cuda")
+    osg = torch.empty((M, n), dtype=torch.float32, device="cuda")
+    cws = torch.empty(B.lora_compress_workspace_bytes(M, d, d, n), dtype=torch.uint8, device="cuda")
+    ad = torch.arange(M, dtype=torch.int32, device="cuda")
+    t_cmp = ev(lambda: B.lora_compress(pool, ad, M, n, 1, 1.0, 0.9, 1, oa, ob, ork, osg, cws), reps=3)
+    in_bytes = M * n * d * 2
+    out = {"modules": M, "rank": n, "rows": d, "tsqr_us": t_tsqr,
+           "tsqr_input_GB_s": in_bytes / t_tsqr / 1e3,
+           "torch_linalg_qr_fp32_us": t_lib,
+           "compress_us": t_cmp, "compress_mean_retained_rank": float(ork.float().mean()),
+           "note": "lora_tsqr forms Q and R from bf16 pages; torch.linalg.qr is given the same "
+                   "matrices as float32 (M, 4096, 16), context only"}
+    del a, b, Qt, R, ws, A32, oa, ob, cws
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -542,6 +598,8 @@ def main():
         others[wo.name] = r
         del wo
 
+    fleet = None if args.no_tsqr else tsqr_bench(torch, np, B)
+
     out = {
         "metric": METRIC,
         "value": head["tokens_per_s"],
@@ -567,6 +625,7 @@ def main():
                   "TFLOP_s": (base_flops + head["lora_path"]["flops"]) / t_step / 1e12},
         "headline": head,
         "workloads": others,
+        "fleet_compression": fleet,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -142,9 +142,10 @@ __global__ __launch_bounds__(256) void core_svd_kernel(CoreArgs a) {
     s_pos[tid] = pos;
   }
   __syncthreads();
+  __shared__ double srt[kCN];
+  if (tid < n) srt[s_pos[tid]] = s_sig[tid];
+  __syncthreads();
   if (tid == 0) {
-    double srt[kCN];
-    for (int c = 0; c < n; ++c) srt[s_pos[c]] = s_sig[c];
     int k;
     if (a.policy == 0) {
       k = int(ceilf(a.ratio * float(n)));
@@ -190,16 +191,16 @@ __global__ __launch_bounds__(256) void compress_rebuild_kernel(const float *Qt, 
                                                                const int32_t *rank, int n, int m,
                                                                E *out) {
   __shared__ float w[kCN][kCN];
-  const int mat = blockIdx.y, x = blockIdx.x * 256 + threadIdx.x;
+  __shared__ float qs[kCN][256];          // this chunk of Q's columns
+  const int mat = blockIdx.y, tid = threadIdx.x, x = blockIdx.x * 256 + tid;
   const int k = rank[mat];
-  for (int e = threadIdx.x; e < n * n; e += 256) w[e / n][e % n] = W[int64_t(mat) * n * n + e];
+  for (int e = tid; e < n * n; e += 256) w[e / n][e % n] = W[int64_t(mat) * n * n + e];
+  for (int l = 0; l < n; ++l) qs[l][tid] = x < m ? Qt[(int64_t(mat) * n + l) * m + x] : 0.f;
   __syncthreads();
   if (x >= m || k == 0) return;
-  float q[kCN];
-  for (int l = 0; l < n; ++l) q[l] = Qt[(int64_t(mat) * n + l) * m + x];
   for (int j = 0; j < k; ++j) {
     float v = 0.f;
-    for (int l = 0; l < n; ++l) v = fmaf(q[l], w[l][j], v);
+    for (int l = 0; l < n; ++l) v = fmaf(qs[l][tid], w[l][j], v);
     Elem<E>::store1(out + (int64_t(mat) * n + j) * m + x, v);
   }
 }

@@ -457,9 +457,10 @@ __device__ __forceinline__ void tile_coords(int T, int tiles_m, int tiles_n, int
 //     by row (all lanes on one row).
 //   * Every block is staged in LDS and stored with 16-byte stores when it
 //     needs no row-by-row expand.
-// The per-block loop is kept rolled (its body once in the code object):
-// block i is always in acc[0] and the blocks rotate down after each step,
-// since a runtime index into acc would send it to scratch memory.
+// The per-block loop is unrolled, so every block's accumulators, descriptors
+// and U values are addressed by compile-time indices (a rolled loop that
+// rotated the blocks down into position 0 needed 11 dwords of scratch per
+// block for the rotation temporaries).
 template <int BM, int BN, int WM, int WN>
 __device__ __forceinline__ void fused_epilogue(const GemmArgs &g,
                                                f32x16_t (&acc)[TileCfg<BM, BN, WM, WN>::TM]
@@ -524,11 +525,11 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs &g,
   cache.r = -1;
   int bkey_ps = -1, bkey_r = -1;             // adapter slice held in bfr
   bf16x8_t bfr[TN] = {};
-#pragma unroll 1
+#pragma unroll
   for (int i = 0; i < TM; ++i) {
-    if (mfma_ok && !(rowwise & 1u)) {
+    if (mfma_ok && !((rowwise >> i) & 1u)) {
       // one MFMA pass per adapter present in the block (lanes 0-31 = rows)
-      const int4 sd = sdv[0];
+      const int4 sd = sdv[i];
       unsigned long long pending = __ballot(sd.x >= 0) & 0xffffffffull;
       while (pending) {
         const int leader = __ffsll(pending) - 1;
@@ -564,7 +565,7 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs &g,
         uint32_t hw[4], lw[4];
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          const float ua = mine ? uv[0][e] : 0.f, ub = mine ? uv[0][e + 1] : 0.f;
+          const float ua = mine ? uv[i][e] : 0.f, ub = mine ? uv[i][e + 1] : 0.f;
           const uint16_t ha = f2bf(ua), hb = f2bf(ub);
           const uint16_t la = f2bf(ua - bf2f(ha)), lb = f2bf(ub - bf2f(hb));
           hw[e >> 1] = uint32_t(ha) | (uint32_t(hb) << 16);
@@ -577,8 +578,8 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs &g,
         __builtin_memcpy(&alo, &pl, 16);
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bfr[j], acc[0][j], 0, 0, 0);
-          acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bfr[j], acc[0][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bfr[j], acc[i][j], 0, 0, 0);
         }
       }
     }
@@ -590,10 +591,10 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs &g,
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = (v >> 2) * 8 + half * 4 + (v & 3);
-        stage[r * SC + j * 32 + frow] = acc[0][j][v];
+        stage[r * SC + j * 32 + frow] = acc[i][j][v];
       }
     const int rbase = m0 + wm * TM * 32 + i * 32;
-    if (!(rowwise & 1u)) {
+    if (!((rowwise >> i) & 1u)) {
 #pragma unroll
       for (int rr0 = 0; rr0 < 32; rr0 += RPS) {
         const int rr = rr0 + vr;
@@ -616,16 +617,6 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs &g,
         if (col_ok) Cols<uint16_t, CPL>::store(Y + int64_t(row) * g.N + col, v);
       }
     }
-    // next block into position 0
-#pragma unroll
-    for (int k = 0; k + 1 < TM; ++k) {
-#pragma unroll
-      for (int j = 0; j < TN; ++j) acc[k][j] = acc[k + 1][j];
-      sdv[k] = sdv[k + 1];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) uv[k][e] = uv[k + 1][e];
-    }
-    rowwise >>= 1;
   }
 }
 
