@@ -205,6 +205,37 @@ def test_apply_short_k(case):
     assert err <= TOL[w.dtype], err
 
 
+@pytest.mark.parametrize("masked", [False, True])
+def test_apply_rank_bucket_edges(masked):
+    """Ranks at and around every rank-bucket edge of the plan (1, 2 | 3, 4 |
+    5, 8 | 9, 16 | 17, 33), two slots per token, with and without a keep mask:
+    plan, Y and every pair's U against the oracle."""
+    rng = np.random.default_rng(91 + masked)
+    rank = np.array([1, 2, 3, 4, 5, 8, 9, 16, 17, 33], np.int32)
+    N, T, K = len(rank), 300, 2
+    ids = rng.integers(-1, N, size=(T, K)).astype(np.int32)
+    gates = rng.uniform(0.2, 1.5, size=(T, K)).astype(np.float32)
+    w = wl.build("bucket-edges", 91, "bf16", T, K, 1024, 704, rank, ids, gates,
+                 x_var=1.0, w_var=0.02, a_var=1 / 64, b_var=0.02,
+                 keep_p=0.9 if masked else None)
+    L = run(w)
+    assert_plan_equal(L.read_plan(), O.plan_workload(w))
+    assert rel_err(D.as_f64(L.Y_host()), O.apply_workload(w)) <= TOL["bf16"]
+    # U against the oracle's x~.A.c for every pair
+    P = L.read_plan()
+    U = L.U()
+    for p in range(int(P["header"][B.PH_PAIRS])):
+        tk = int(P["pair_tk"][p]); t, k = divmod(tk, K)
+        a = int(w.ids[t, k])
+        A, _ = O.factors(a, w.rank, w.page_start, w.page_ids, w.a_pages, w.b_pages)
+        x = D.as_f64(w.X[t])
+        if masked:
+            x = x * w.keep_mask[t] * float(np.float32(w.keep_scale))
+        ref = float(w.gates[t, k]) * float(w.scale[a]) * (x @ A)
+        got = U[P["u_off"][p]:P["u_off"][p + 1]].astype(np.float64)
+        assert np.max(np.abs(got - ref)) <= 1e-5 * max(1.0, np.max(np.abs(ref))), (p, a)
+
+
 def test_apply_fused_rowwise_expand():
     """The fused 256 x 256 epilogue's row-by-row expand (K = 2, ranks above 16),
     every row against the oracle."""
