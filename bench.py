@@ -654,8 +654,13 @@ def measured_traffic(kernel, workload):
             table = json.load(fh)
     except (OSError, ValueError):
         return None
-    ent = table.get(kernel + "|" + workload)
-    if not ent or ent.get("source_sha256_16") != kernel_source_hash():
+    # the instantiation of this kernel with the most dispatches in the run
+    cands = [v for k, v in table.items()
+             if k.endswith("|" + workload) and (k.startswith(kernel + "<") or k.startswith(kernel + "|"))]
+    if not cands:
+        return None
+    ent = max(cands, key=lambda v: v["fetch"]["dispatches"])
+    if ent.get("source_sha256_16") != kernel_source_hash():
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -665,7 +670,7 @@ KERNELS = ("decode_gemm_slot_kernel", "gemm_tile_plan_kernel", "decode_gemm_shri
            "gemm_decode_kernel", "gemm_tile_kernel", "gemm_f32_kernel", "shrink_both_kernel",
            "shrink_units_kernel", "shrink_tile_kernel", "epilogue_kernel", "plan_kernel",
            "merge_mfma_kernel", "seg_outer_mfma_kernel", "seg_outer_reduce_kernel",
-           "g_reduce_kernel")
+           "g_reduce_kernel", "transpose_kernel")
 
 
 def pmc_summary(workload_id, fetch_csv, write_csv):
@@ -678,10 +683,13 @@ def pmc_summary(workload_id, fetch_csv, write_csv):
     from lora_adapter_amd import workloads as wl
 
     def name_of(k):
-        base = k.split("(")[0]
+        """The kernel's name with its template arguments (one entry per
+        instantiation), for the library's kernels."""
+        import re
         for n in KERNELS:
-            if n in base:
-                return n
+            m = re.search(r"(?:::|^)(" + n + r"(?:<[^()]*>)?)\(", k)
+            if m:
+                return m.group(1)
         return None
 
     def per_kernel(path, counter):
