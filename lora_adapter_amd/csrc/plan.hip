@@ -20,7 +20,7 @@ PlanLaunch plan_setup(const int32_t *ids, const float *gates, int T, int K, cons
   PlanLaunch pl{};
   pl.a = PlanArgs{ids, gates, T, K, pool.n_adapters, pool.rank, pool.page_start, pool.page_ids,
                   pool.n_pages, pool.n_page_ids, plan, 0,
-                  shrink_tile_enabled(pool.dtype, TK, pool.d_in, pool.d_out) ? 1 : 0, 0, 0,
+                  shrink_tile_enabled(pool.dtype, TK, pool.d_in, pool.d_out) ? 1 : 0, 0, 0, 0,
                   nullptr, nullptr, 0, 0};
   int64_t cap = int64_t(lds_cap / sizeof(int));
   if (cap > kPlanLdsInts) cap = kPlanLdsInts;
@@ -31,7 +31,12 @@ PlanLaunch plan_setup(const int32_t *ids, const float *gates, int T, int K, cons
   pl.a.slot_cache = fixed + 2 * TK <= cap ? 1 : 0;
   const int64_t used = fixed + (pl.a.slot_cache ? 2 * TK : 0);
   pl.a.page_cache = pl.a.slot_cache && pool.n_page_ids > 0 && used + pool.n_page_ids <= cap ? 1 : 0;
-  pl.lds_bytes = size_t(used + (pl.a.page_cache ? pool.n_page_ids : 0)) * sizeof(int);
+  const int64_t used2 = used + (pl.a.page_cache ? pool.n_page_ids : 0);
+  // the placement's (wave, adapter) count table, when it fits beside them and
+  // saves barriers (three per chunk of slots against one per wave of it)
+  const int64_t table = int64_t(nt / 64) * N;
+  pl.a.place_table = pl.lds && pl.a.slot_cache && nt >= 256 && used2 + table <= cap ? 1 : 0;
+  pl.lds_bytes = size_t(used2 + (pl.a.place_table ? table : 0)) * sizeof(int);
   return pl;
 }
 

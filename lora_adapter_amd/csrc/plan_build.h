@@ -32,7 +32,11 @@
 //      each other with one ballot per id bit, the first of them takes
 //      positions from the adapter's cursor, and the waves of each chunk of
 //      slots (one slot per thread) take their turns in order, which keeps the
-//      sort stable.
+//      sort stable; with a (wave, adapter) count table in LDS, every slot
+//      instead adds the counts of the chunk's earlier waves to the cursor,
+//      the same positions with three barriers a chunk instead of one a wave.
+// The ids and gates of the first 8 chunks of slots are fetched in one round
+// trip at the start (a later chunk's loads would each be one more).
 // Per-adapter arrays live in LDS when they fit (96 KiB); then the barriers
 // order LDS only, and global stores (outputs only) never stall them.  Larger
 // pools keep those arrays in the plan buffer's scratch (agent-scope atomics
@@ -150,6 +154,7 @@ __device__ __forceinline__ uint64_t match_lanes(int a, int nbits) {
 }
 
 // Loads in flight per thread in the adapter and page-id passes.
+constexpr int kPreChunks = 8;        // chunks of nt slots whose ids and gates are fetched up front
 constexpr int kAdBatch = 4;
 constexpr int kRowBatch = 12;
 constexpr int kWsBatch = 8;
@@ -194,18 +199,28 @@ __device__ __forceinline__ void plan_build(const PlanArgs &a, int *dyn) {
   // global round trip after the segment order)
   int *slot_g = slot_ad + TK;                 // gate bits of each slot (with the cache)
   int *pcache = slot_ad + (a.slot_cache ? 2 * TK : 0);
+  // placement counts per (wave, adapter), zero between chunks
+  int *ptab = pcache + (a.page_cache ? a.n_page_ids : 0);
+  if (a.place_table)
+    for (int e = tid; e < nwv * N; e += nt) ptab[e] = 0;
   // counts of used adapters per (bucket, round of nt adapters, wave)
   const int Q = (N + nt - 1) / nt;
   const int E = Q * nwv;
   int *wcnt = kLds ? s_wcnt : P + L.wcnt;
 
-  // The first nt slots are fetched now, so their round trip overlaps the
-  // adapter loads below.
-  int id_pre = -1;
-  float g_pre = 0.0f;
-  if (tid < TK) {
-    id_pre = a.ids[tid];
-    g_pre = a.gates[tid];
+  // The first kPreChunks x nt slots are fetched now, in one round trip that
+  // overlaps the adapter loads below (each later chunk costs a round trip).
+  int id_pre[kPreChunks];
+  float g_pre[kPreChunks];
+#pragma unroll
+  for (int c = 0; c < kPreChunks; ++c) {
+    const int64_t i = int64_t(c) * nt + tid;
+    id_pre[c] = -1;
+    g_pre[c] = 0.0f;
+    if (i < TK) {
+      id_pre[c] = a.ids[i];
+      g_pre[c] = a.gates[i];
+    }
   }
 
   // 0. per-adapter data; adapter ad belongs to thread ad % nt.  The page
@@ -249,12 +264,9 @@ __device__ __forceinline__ void plan_build(const PlanArgs &a, int *dyn) {
   // 1. classify and count
   const int nbits = N > 1 ? 32 - __clz(N - 1) : 1;
   int err = 0;
-  for (int64_t base = 0; base < TK; base += nt) {
-    const int64_t i = base + tid;
+  auto classify = [&](int64_t i, int id, float g) __attribute__((always_inline)) {
     int ad = -1;
     if (i < TK) {
-      const int id = base == 0 ? id_pre : a.ids[i];
-      const float g = base == 0 ? g_pre : a.gates[i];
       if (id < -1 || id >= N) {
         err |= LORA_DEVERR_BAD_ID;
       } else if (id >= 0) {
@@ -269,6 +281,13 @@ __device__ __forceinline__ void plan_build(const PlanArgs &a, int *dyn) {
     }
     const uint64_t mm = match_lanes(ad, nbits);
     if (ad >= 0 && (mm & lt_mask) == 0) atomicAdd(&cnt[ad], __popcll(mm));
+  };
+#pragma unroll
+  for (int c = 0; c < kPreChunks; ++c)
+    if (int64_t(c) * nt < TK) classify(int64_t(c) * nt + tid, id_pre[c], g_pre[c]);
+  for (int64_t base = int64_t(kPreChunks) * nt; base < TK; base += nt) {
+    const int64_t i = base + tid;
+    classify(i, i < TK ? a.ids[i] : -1, i < TK ? a.gates[i] : 0.0f);
   }
   if (err) atomicOr(&s_err, err);
   bar<kLds>();
@@ -517,13 +536,34 @@ __device__ __forceinline__ void plan_build(const PlanArgs &a, int *dyn) {
     const int64_t here = TK - base < nt ? TK - base : nt;
     const int nw = int((here + 63) >> 6);
     int pos = -1;
-    for (int w = 0; w < nw; ++w) {
+    if (a.place_table) {
+      // the same positions as the waves taking turns: the adapter's cursor,
+      // plus its slots in the chunk's earlier waves (the count table), plus
+      // the slot's rank in its own wave; cursors move after every wave has
+      // read them, and each wave clears its own table entries
+      const bool lead = ad >= 0 && rank_in_wave == 0;
       bar<kLds>();
-      if (wave == w) {
-        int b0 = 0;
-        if (ad >= 0 && rank_in_wave == 0) b0 = atomicAdd(&cur[ad], __popcll(mm));
-        b0 = __shfl(b0, leader, 64);
-        if (ad >= 0) pos = b0 + rank_in_wave;
+      if (lead) ptab[wave * N + ad] = __popcll(mm);
+      bar<kLds>();
+      if (ad >= 0) {
+        int before = 0;
+        for (int w = 0; w < wave; ++w) before += ptab[w * N + ad];
+        pos = ld_ctr(&cur[ad]) + before + rank_in_wave;
+      }
+      bar<kLds>();
+      if (lead) {
+        atomicAdd(&cur[ad], __popcll(mm));
+        ptab[wave * N + ad] = 0;
+      }
+    } else {
+      for (int w = 0; w < nw; ++w) {
+        bar<kLds>();
+        if (wave == w) {
+          int b0 = 0;
+          if (ad >= 0 && rank_in_wave == 0) b0 = atomicAdd(&cur[ad], __popcll(mm));
+          b0 = __shfl(b0, leader, 64);
+          if (ad >= 0) pos = b0 + rank_in_wave;
+        }
       }
     }
     if (i < TK) {
