@@ -620,6 +620,17 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs &g,
   }
 }
 
+// Fragment read slot i of a K step (A blocks 0 .. TM-1 are fragments
+// 0 .. TM-1, B blocks TM ..): block (i, j) takes MFMA i * TN + j, so the
+// next step needs A 0 and B 0 first, then B 1 .. TN-1, then A 1, A 2, ...;
+// read in that order, one after each of the first TM + TN MFMAs of a step,
+// every fragment has at least TM * TN - 2 MFMAs between its read and its
+// first use.
+template <int TM, int TN>
+__device__ __forceinline__ constexpr int frag_order(int i) {
+  return i == 0 ? 0 : i <= TN ? TM + i - 1 : i - TN;
+}
+
 // One K tile of MFMAs from an LDS stage.  pre_step(s) runs before each of
 // the four 16-wide K steps (the ring pipeline issues a quarter of the next
 // tile's copies there, so that they queue while the MFMAs execute).
@@ -638,8 +649,9 @@ __device__ __forceinline__ void tile_mfma(const char *As,
   const int wm = wave / WN, wn = wave % WN;
   const int frow = lane & 31, half = lane >> 5;
   // Fragments are pipelined inside the tile: the LDS reads of K step s + 1
-  // go out under the MFMAs of step s (two register sets), each step's
-  // instructions pinned in this order (sched_barrier).
+  // go out under the first MFMAs of step s (two register sets) in the order
+  // that step s + 1 uses them, each step's instructions pinned in this order
+  // (sched_barrier).
   bf16x8_t fa0[TM], fb0[TN], fa1[TM], fb1[TN];
   // fragment q (A blocks 0 .. TM-1, then B blocks) of K step s
   auto frag = [&](int s, int q) __attribute__((always_inline)) {
@@ -650,6 +662,7 @@ __device__ __forceinline__ void tile_mfma(const char *As,
                    bf16x8_t (&yb)[TN]) __attribute__((always_inline)) {
     constexpr bool kNext = decltype(nxt)::value;
     constexpr int NM = TM * TN, NF = TM + TN;
+    static_assert(NF <= NM, "one fragment read after each of the first MFMAs");
     pre_step(s);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -657,8 +670,8 @@ __device__ __forceinline__ void tile_mfma(const char *As,
       acc[m / TN][m % TN] =
           __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[m / TN], xb[m % TN], acc[m / TN][m % TN], 0, 0, 0);
       if constexpr (kNext) {
-#pragma unroll
-        for (int q = m * NF / NM; q < (m + 1) * NF / NM; ++q) {
+        const int q = frag_order<TM, TN>(m);
+        if (m < NF) {
           if (q < TM) ya[q] = frag(s + 1, q);
           else yb[q - TM] = frag(s + 1, q);
         }
@@ -782,20 +795,22 @@ __device__ __forceinline__ void tile_run(const GemmArgs &g, char *smem, int m0, 
       else lds_dma16(bbase + kt * 64 + boff[i - C::A_INS], lds + BM * C::ROWB + (wave * C::B_INS + i - C::A_INS) * 1024);
     };
     // One K step: MFMA m on block (m / TN, m % TN) from (xa, xb), each
-    // followed by its share of the next step's fragment reads from src (into
-    // ya, yb; mode bit 0) and of the copies of K tile kn into dst (bit 1).
+    // followed by one of the next step's fragment reads from src (into ya,
+    // yb, in frag_order; mode bit 0) and its share of the copies of K tile
+    // kn into dst (bit 1).
     auto kstep = [&](auto mode, bf16x8_t (&xa)[TM], bf16x8_t (&xb)[TN], bf16x8_t (&ya)[TM],
                      bf16x8_t (&yb)[TN], const char *src, int s_next, char *dst,
                      int kn) __attribute__((always_inline)) {
       constexpr int MD = decltype(mode)::value;
       constexpr int NM = TM * TN, NQ = TM + TN;
+      static_assert(NQ <= NM, "one fragment read after each of the first MFMAs");
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         acc[m / TN][m % TN] =
             __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[m / TN], xb[m % TN], acc[m / TN][m % TN], 0, 0, 0);
         if constexpr ((MD & 1) != 0) {
-#pragma unroll
-          for (int q = m * NQ / NM; q < (m + 1) * NQ / NM; ++q) {
+          const int q = frag_order<TM, TN>(m);
+          if (m < NQ) {
             if (q < TM) ya[q] = frag(src, s_next, q);
             else yb[q - TM] = frag(src, s_next, q);
           }
