@@ -13,7 +13,9 @@ import os
 from typing import Optional
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "liblora.so")
+# LORA_ADAPTER_LIB names another build of the same library (the host-sanitized
+# one that the CPU tests load under the address sanitizer runtime)
+LIB_PATH = os.environ.get("LORA_ADAPTER_LIB") or os.path.join(PKG, "liblora.so")
 
 LORA_OK, LORA_ERR_INVALID_ARG, LORA_ERR_UNSUPPORTED, LORA_ERR_CAPACITY, LORA_ERR_DEVICE = range(5)
 LORA_F32, LORA_BF16 = 0, 1
