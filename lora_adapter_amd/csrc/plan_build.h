@@ -395,7 +395,9 @@ __device__ __forceinline__ void plan_build(const PlanArgs &a, int *dyn) {
       const int r = inf[ad] & kInfRankMask;
       const bool big = a.use_tile && c >= kBigSegPairs;
       x.v[0] += c; x.v[1] += c * r; x.v[2] += r;
-      x.v[3] += big ? 0 : c * ((r + kShrinkRows - 1) / kShrinkRows);
+      // decode-shrink units: every pair of a small segment, the last c % 16
+      // pairs of a big one (its whole 16-pair tiles go to the MFMA shrink)
+      x.v[3] += (big ? c % kTileTok : c) * ((r + kShrinkRows - 1) / kShrinkRows);
       x.v[4] += big ? 1 : 0;
     }
     ScanV<5> tot;
@@ -421,7 +423,7 @@ __device__ __forceinline__ void plan_build(const PlanArgs &a, int *dyn) {
       }
       if (big) P[L.big_list + 1 + bi] = sg;
       st += c; ub += c * r; rb += r; bi += big ? 1 : 0;
-      uo += big ? 0 : c * ((r + kShrinkRows - 1) / kShrinkRows);
+      uo += (big ? c % kTileTok : c) * ((r + kShrinkRows - 1) / kShrinkRows);
     }
     pair_base = tot.v[0];
     u_base = tot.v[1];

@@ -15,8 +15,11 @@
 //     persistent grid of kShrinkWaves waves over the plan's unit schedule
 //     (see shrink_units_kernel); A pages stream from HBM with 16-byte
 //     coalesced loads, token rows come from L2.
-//   * tile kernel (segments of kBigSegPairs pairs or more, bf16, large
-//     batches, i.e. prefill): an MFMA tile of 16 tokens x 16 rank rows
+//   * tile kernel (the whole 16-pair tiles of segments of kBigSegPairs
+//     pairs or more, bf16, large batches, i.e. prefill; the units kernel
+//     takes each such segment's last len % 16 pairs, so there are at most
+//     T*K / 16 tiles and a batch of 8192 pairs fills exactly 512
+//     workgroups): an MFMA tile of 16 tokens x 16 rank rows
 //     (v_mfma_f32_16x16x32_bf16), token rows and A pages read straight from
 //     global memory as MFMA fragments, the dropout mask applied to the bf16
 //     fragment (exact), the four waves of a workgroup splitting d and adding
@@ -31,7 +34,6 @@
 namespace lora {
 namespace {
 
-constexpr int kTileTok = 16;        // tokens per MFMA tile
 constexpr int kTileRank = 16;       // rank rows per MFMA tile
 constexpr int kTileAhead = 8;       // K steps per batch of loads
 
@@ -63,7 +65,7 @@ __device__ __forceinline__ bool tile_of(const PlanView &pv, int b, int lane, int
       sg = pv.big_list[1 + i];
       pb_ = pv.seg_desc[2 * sg].w;
       pe_ = pv.seg_desc[2 * sg + 1].x;
-      nt = (pe_ - pb_ + kTileTok - 1) / kTileTok;
+      nt = (pe_ - pb_) / kTileTok;                  // whole tiles only
     }
     int incl = nt;
 #pragma unroll
@@ -205,13 +207,11 @@ __global__ __launch_bounds__(256) void shrink_both_kernel(ShrinkArgs s, int n_ti
   shrink_units_wave<uint16_t, kMask, kCh, true>(s, (b - n_tile) * 4 + int(threadIdx.x >> 6));
 }
 
-// Workgroups of the tile shrink: big segments number at most T*K /
-// kBigSegPairs (and at most the number of segments), each at most T*K
-// pairs; their 16-pair tiles sum to at most TK / 16 + nbig.
+// Workgroups of the tile shrink: the whole 16-pair tiles of the big
+// segments, at most T*K / 16 (at least one workgroup).
 int shrink_tile_wgs(int64_t TK, int64_t n_adapters) {
-  const int64_t segs = TK < n_adapters ? TK : n_adapters;
-  const int64_t nbig = TK / kBigSegPairs < segs ? TK / kBigSegPairs : segs;
-  return int((TK + kTileTok - 1) / kTileTok + (nbig > 0 ? nbig : 1));
+  (void)n_adapters;
+  return int(TK / kTileTok > 0 ? TK / kTileTok : 1);
 }
 
 }  // namespace

@@ -156,13 +156,16 @@ __device__ __forceinline__ void shrink_units_wave(const ShrinkArgs &s, const int
   while (left > 0) {
     const int n = pe - pb;
     const int G = (r + RW - 1) / RW;
-    const bool skip = s.big_segments && n >= kBigSegPairs;   // the MFMA shrink's
-    const int here = skip ? 0 : min(left, n * G - loc);
-    int g = here > 0 ? loc / n : 0, i = here > 0 ? loc % n : 0;
+    // the MFMA shrink takes the whole 16-pair tiles of a big segment: the
+    // units cover its last n % 16 pairs only (every pair of a small one)
+    const int n_tiled = s.big_segments && n >= kBigSegPairs ? n / kTileTok * kTileTok : 0;
+    const int nu = n - n_tiled;
+    const int here = min(left, nu * G - loc);
+    int g = here > 0 ? loc / nu : 0, i = here > 0 ? loc % nu : 0;
     int rem = here;
     while (rem > 0) {
       const int j0 = g * RW, nr = min(RW, r - j0);
-      const int i_end = min(n, i + rem);
+      const int i_end = min(nu, i + rem);
       for (int ib = i; ib < i_end; ib += 64) {
         const int nb = min(64, i_end - ib);
         // round trip 2: page ids (lanes < RW), scale (lane RW), and per pair
@@ -171,7 +174,7 @@ __device__ __forceinline__ void shrink_units_wave(const ShrinkArgs &s, const int
         float scw = 0.f;
         if (lane < RW) pw = s.page_ids[ps + j0 + min(lane, nr - 1)];
         else if (lane == RW) scw = s.scale[ad];
-        const int q = pb + ib + min(lane, nb - 1);
+        const int q = pb + n_tiled + ib + min(lane, nb - 1);
         const int tkl = s.plan.pair_tk[q];
         const float gl = s.plan.pair_gate[q];
         const int ul = s.plan.u_off[q];
