@@ -21,7 +21,9 @@ Measurement
     pool, R chosen so that the copies exceed 1 GiB: every step reads from HBM,
     not from the 256 MiB Infinity Cache.  value_forward: the same without the
     gradients; value_apply_only: the forward on a plan built once per batch
-    (shared by every layer of a model).
+    (shared by every layer of a model); value_plan_shared: the full step
+    (forward + gradients) on such a plan, i.e. the cost per projection once
+    the batch's one lora_plan is paid (value itself includes it).
   * per-launch durations: HIP events on the launch stream around blocks of
     back-to-back launches of one stage on the rotated copies, queued behind a
     busy prefix (so the events time the kernels, not host launch gaps).
@@ -295,6 +297,14 @@ def measure(w, args, torch, np, B, D, steps, warmup, full):
     el_base = None if skip0 else bn.timed(lambda c: bn.forward(c, bn.empty_ids), steps, warmup)
     bn.plan_all(bn.ids)
     el_apply = bn.timed(lambda c: bn.apply(c), steps, warmup)
+
+    def shared(c):
+        # the batch's plan already built (lora_plan once per batch, shared by
+        # every LoRA projection that routes the same tokens): apply + grads
+        bn.apply(c)
+        if bn.grads:
+            bn.grad(c)
+    el_shared = bn.timed(shared, steps, warmup)
     el_graph = bn.timed_graph(steps, warmup) if args.graph else None
     bn.step(bn.copies[0])
     torch.cuda.synchronize()
@@ -321,6 +331,8 @@ def measure(w, args, torch, np, B, D, steps, warmup, full):
         "tokens_per_s": T / t_step,
         "forward_us": t_fwd * 1e6, "forward_tokens_per_s": T / t_fwd,
         "apply_only_us": el_apply / steps * 1e6, "apply_only_tokens_per_s": T * steps / el_apply,
+        "step_plan_shared_us": el_shared / steps * 1e6,
+        "step_plan_shared_tokens_per_s": T * steps / el_shared,
         "forward_empty_plan_us": None if skip0 else t_base * 1e6,
         "step_us_graph_replay": None if el_graph is None else el_graph / steps * 1e6,
         "stages_us": st, "stages_us_empty_plan": st0,
@@ -620,6 +632,7 @@ def main():
         "roofline": roofline,
         "value_forward": head["forward_tokens_per_s"],
         "value_apply_only": head["apply_only_tokens_per_s"],
+        "value_plan_shared": head["step_plan_shared_tokens_per_s"],
         "lora_path": head["lora_path"],
         "layer": {"bytes": layer_bytes, "GB_s": layer_bytes / t_step / 1e9,
                   "TFLOP_s": (base_flops + head["lora_path"]["flops"]) / t_step / 1e12},

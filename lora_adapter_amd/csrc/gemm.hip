@@ -224,9 +224,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // read (it cannot tell which LDS stage an in-flight copy writes); the
 // instruction has no register result, and the kernel waits for these copies
 // itself (wait_vmcnt) before the barrier that precedes reading the stage.
+// On this architecture family an LDS DMA needs one wait state after a
+// scalar write of m0, which the compiler cannot insert inside the asm
+// block: the s_nop provides it.
 __device__ __forceinline__ void lds_dma16(const void *gptr, uint32_t lds) {
   const uint32_t lds_s = __builtin_amdgcn_readfirstlane(lds);   // wave-uniform LDS base
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(gptr), "s"(lds_s)
                : "memory", "m0");
