@@ -15,6 +15,8 @@
 // module: columns of the core are rotated in pairs (round-robin, n/2 disjoint
 // pairs per round, fixed order) until a sweep rotates nothing or after 30
 // sweeps; singular values are the column norms, sorted by a stable rank.
+#include <type_traits>
+
 #include "lora_internal.h"
 
 namespace lora {
@@ -66,10 +68,13 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   return v;
 }
 
+// CN: the smallest of 16, 32, 64 that holds n (LDS sized for it, so that
+// many modules' workgroups share a CU).
+template <int CN>
 __global__ __launch_bounds__(256) void core_svd_kernel(CoreArgs a) {
-  __shared__ double G[kCN][kCN];   // G[c][r]: column c of the core (rotated in place)
-  __shared__ double V[kCN][kCN];   // V[c][r]: column c of the accumulated rotation
-  __shared__ double s_sig[kCN];
+  __shared__ double G[CN][CN];     // G[c][r]: column c of the core (rotated in place)
+  __shared__ double V[CN][CN];     // V[c][r]: column c of the accumulated rotation
+  __shared__ double s_sig[CN];
   __shared__ int s_rot;
   const int mat = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = a.n;
@@ -133,7 +138,7 @@ __global__ __launch_bounds__(256) void core_svd_kernel(CoreArgs a) {
     }
   }
   __syncthreads();
-  __shared__ int s_pos[kCN];
+  __shared__ int s_pos[CN];
   __shared__ int s_k;
   if (tid < n) {
     int pos = 0;
@@ -142,7 +147,7 @@ __global__ __launch_bounds__(256) void core_svd_kernel(CoreArgs a) {
     s_pos[tid] = pos;
   }
   __syncthreads();
-  __shared__ double srt[kCN];
+  __shared__ double srt[CN];
   if (tid < n) srt[s_pos[tid]] = s_sig[tid];
   __syncthreads();
   if (tid == 0) {
@@ -186,12 +191,12 @@ __global__ __launch_bounds__(256) void core_svd_kernel(CoreArgs a) {
 
 // out rows mat * n + j (j < k) of [M * n][m]: column j of Q.W, Q given by its
 // columns Qt [M][n][m], W [M][n][n] (row l, column j).
-template <typename E>
+template <typename E, int CN>
 __global__ __launch_bounds__(256) void compress_rebuild_kernel(const float *Qt, const float *W,
                                                                const int32_t *rank, int n, int m,
                                                                E *out) {
-  __shared__ float w[kCN][kCN];
-  __shared__ float qs[kCN][256];          // this chunk of Q's columns
+  __shared__ float w[CN][CN];
+  __shared__ float qs[CN][256];           // this chunk of Q's columns
   const int mat = blockIdx.y, tid = threadIdx.x, x = blockIdx.x * 256 + tid;
   const int k = rank[mat];
   for (int e = tid; e < n * n; e += 256) w[e / n][e % n] = W[int64_t(mat) * n * n + e];
@@ -241,19 +246,27 @@ hipError_t launch_compress(const PoolView &pool, const int32_t *adapters, int M,
   if ((e = launch_tsqr(pool.b_pages, pool.dtype, cols, M, pool.d_out, n, Qb, Rb, tws, s)) != hipSuccess)
     return e;
   CoreArgs c{Ra, Rb, bad, M, n, policy, ratio, energy, floor_rank, Ua, Vb, out_rank, out_sigma};
-  hipLaunchKernelGGL(core_svd_kernel, dim3(unsigned(M)), dim3(256), 0, s, c);
+  if (n <= 16) hipLaunchKernelGGL(core_svd_kernel<16>, dim3(unsigned(M)), dim3(256), 0, s, c);
+  else if (n <= 32) hipLaunchKernelGGL(core_svd_kernel<32>, dim3(unsigned(M)), dim3(256), 0, s, c);
+  else hipLaunchKernelGGL(core_svd_kernel<kCN>, dim3(unsigned(M)), dim3(256), 0, s, c);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const dim3 ga(unsigned((pool.d_in + 255) / 256), unsigned(M)), gb(unsigned((pool.d_out + 255) / 256), unsigned(M));
+  auto rebuild = [&](auto tag, auto cn) {
+    using E = decltype(tag);
+    constexpr int CN = decltype(cn)::value;
+    hipLaunchKernelGGL((compress_rebuild_kernel<E, CN>), ga, dim3(256), 0, s, Qa, Ua, out_rank, n,
+                       pool.d_in, static_cast<E *>(out_a));
+    hipLaunchKernelGGL((compress_rebuild_kernel<E, CN>), gb, dim3(256), 0, s, Qb, Vb, out_rank, n,
+                       pool.d_out, static_cast<E *>(out_b));
+  };
   if (pool.dtype == LORA_BF16) {
-    hipLaunchKernelGGL(compress_rebuild_kernel<uint16_t>, ga, dim3(256), 0, s, Qa, Ua, out_rank, n,
-                       pool.d_in, static_cast<uint16_t *>(out_a));
-    hipLaunchKernelGGL(compress_rebuild_kernel<uint16_t>, gb, dim3(256), 0, s, Qb, Vb, out_rank, n,
-                       pool.d_out, static_cast<uint16_t *>(out_b));
+    if (n <= 16) rebuild(uint16_t{}, std::integral_constant<int, 16>{});
+    else if (n <= 32) rebuild(uint16_t{}, std::integral_constant<int, 32>{});
+    else rebuild(uint16_t{}, std::integral_constant<int, kCN>{});
   } else {
-    hipLaunchKernelGGL(compress_rebuild_kernel<float>, ga, dim3(256), 0, s, Qa, Ua, out_rank, n,
-                       pool.d_in, static_cast<float *>(out_a));
-    hipLaunchKernelGGL(compress_rebuild_kernel<float>, gb, dim3(256), 0, s, Qb, Vb, out_rank, n,
-                       pool.d_out, static_cast<float *>(out_b));
+    if (n <= 16) rebuild(float{}, std::integral_constant<int, 16>{});
+    else if (n <= 32) rebuild(float{}, std::integral_constant<int, 32>{});
+    else rebuild(float{}, std::integral_constant<int, kCN>{});
   }
   return hipGetLastError();
 }

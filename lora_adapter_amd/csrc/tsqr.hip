@@ -56,9 +56,14 @@ __device__ __forceinline__ float block_sum4(float v, float *red) {
   return s;
 }
 
+// A tile lives in dynamic LDS sized for its n columns (n x 256 floats, 16
+// KiB at n = 16 instead of the 64 KiB n = 64 needs), so that many tiles'
+// workgroups share a CU: each one is a chain of per-column reductions and
+// barriers, and the device runs at the rate of the workgroups in flight.
 template <typename E, bool kLevel0>
 __global__ __launch_bounds__(256) void tsqr_factor_kernel(TsqrLevel a) {
-  __shared__ float col[kTN][kTR];       // the tile, column-major
+  extern __shared__ float tsqr_dyn[];
+  float (*col)[kTR] = reinterpret_cast<float (*)[kTR]>(tsqr_dyn);   // the tile, column-major
   __shared__ float s_tau[kTN];
   __shared__ float red[4];
   const int tile = blockIdx.x, mat = blockIdx.y;
@@ -151,8 +156,9 @@ struct TsqrForm {
 };
 
 __global__ __launch_bounds__(256) void tsqr_form_kernel(TsqrForm a) {
-  __shared__ float C[kTN][kTR];
-  __shared__ float Vs[kTN][kTR];
+  extern __shared__ float tsqr_dyn[];
+  float (*C)[kTR] = reinterpret_cast<float (*)[kTR]>(tsqr_dyn);               // n x 256
+  float (*Vs)[kTR] = reinterpret_cast<float (*)[kTR]>(tsqr_dyn + a.n * kTR);  // n x 256
   const int tile = blockIdx.x, mat = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = a.n;
@@ -196,6 +202,197 @@ __global__ __launch_bounds__(256) void tsqr_form_kernel(TsqrForm a) {
   float *Q = a.Q + int64_t(mat) * n * a.m_l;
   for (int c = 0; c < n; ++c)
     if (tid < rows) Q[int64_t(c) * a.m_l + r0 + tid] = C[c][tid];
+}
+
+// The same factorisation and Q formation with one wave per tile, for n <= 16
+// (the ranks of compressed adapters): the tile lives in registers, lane l
+// holding rows l, l + 64, l + 128, l + 192 of every column, and every
+// reduction is one butterfly over the wave (no barrier).  Four tiles per
+// workgroup.  Same reflectors, taus, triangles and signs as the workgroup
+// kernels above, summed in another (fixed) order.
+constexpr int kWN = 16;         // most columns of the wave kernels
+constexpr int kWQ = kTR / 64;   // rows per lane
+
+// Sum over the 64 lanes with DPP moves (vector ALU, no LDS round trip):
+// quad sums, then rows of 16 (row_shr 4, 8), then the row sums carried by
+// row_bcast 15 and 31 into lane 63, read back as a wave-uniform value.  A
+// fixed order, so deterministic.
+__device__ __forceinline__ float wave_total(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xb1, 0xf, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4e, 0xf, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xf, 0xe, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x118, 0xf, 0xc, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xa, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xc, 0xf, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+template <typename E, bool kLevel0>
+__global__ __launch_bounds__(256) void tsqr_factor_wave_kernel(TsqrLevel a) {
+  const int lane = threadIdx.x & 63;
+  const int t = int(blockIdx.x) * 4 + int(threadIdx.x >> 6);
+  if (t >= a.tiles * a.M) return;
+  const int mat = t / a.tiles, tile = t % a.tiles;
+  const int n = a.n;
+  const int r0 = tile * kTR;
+  const int rows = min(kTR, a.m_l - r0);
+  float x[kWN][kWQ];
+#pragma unroll
+  for (int c = 0; c < kWN; ++c)
+#pragma unroll
+    for (int q = 0; q < kWQ; ++q) {
+      const int r = lane + 64 * q;
+      float v = 0.f;
+      if (c < n && r < rows) {
+        if constexpr (kLevel0) {
+          const int64_t srow = a.cols[int64_t(mat) * n + c];
+          v = Elem<E>::to_f(static_cast<const E *>(a.src)[srow * a.m_l + r0 + r]);
+        } else {
+          v = a.X[(int64_t(mat) * n + c) * a.m_l + r0 + r];
+        }
+      }
+      x[c][q] = v;
+    }
+  float taus[kWN];
+#pragma unroll
+  for (int j = 0; j < kWN; ++j) {
+    taus[j] = 0.f;
+    if (j >= n) continue;
+    // reflector for column j (row j is lane j's first row)
+    const float xj = __shfl(x[j][0], j, 64);
+    float part = 0.f;
+#pragma unroll
+    for (int q = 0; q < kWQ; ++q) {
+      const int r = lane + 64 * q;
+      if (r > j) part = fmaf(x[j][q], x[j][q], part);
+    }
+    const float below = wave_total(part);
+    float beta = xj, tau = 0.f, scl = 0.f;
+    if (below > 0.f) {
+      const float nrm = sqrtf(xj * xj + below);
+      beta = xj >= 0.f ? -nrm : nrm;
+      tau = (beta - xj) / beta;
+      scl = 1.f / (xj - beta);
+    }
+    taus[j] = tau;
+    // v (v_j = 1 implicit) into column j below the diagonal, beta on it
+    float v[kWQ];
+#pragma unroll
+    for (int q = 0; q < kWQ; ++q) {
+      const int r = lane + 64 * q;
+      if (r > j) x[j][q] *= scl;
+      v[q] = r > j ? x[j][q] : (r == j ? 1.f : 0.f);
+      if (r == j) x[j][q] = beta;
+    }
+    if (tau != 0.f) {
+      // apply H_j to the later columns: all their dot products first
+      float d[kWN];
+#pragma unroll
+      for (int c = j + 1; c < kWN; ++c) {
+        float pc = 0.f;
+#pragma unroll
+        for (int q = 0; q < kWQ; ++q) pc = fmaf(v[q], x[c][q], pc);
+        d[c] = c < n ? wave_total(pc) : 0.f;
+      }
+#pragma unroll
+      for (int c = j + 1; c < kWN; ++c) {
+        const float w = tau * d[c];
+#pragma unroll
+        for (int q = 0; q < kWQ; ++q) x[c][q] = fmaf(-w, v[q], x[c][q]);
+      }
+    }
+  }
+  // reflectors and taus out
+  float *V = a.V + int64_t(mat) * n * a.m_l;
+#pragma unroll
+  for (int c = 0; c < kWN; ++c)
+#pragma unroll
+    for (int q = 0; q < kWQ; ++q) {
+      const int r = lane + 64 * q;
+      if (c < n && r < rows) V[int64_t(c) * a.m_l + r0 + r] = r > c ? x[c][q] : 0.f;
+    }
+#pragma unroll
+  for (int j = 0; j < kWN; ++j)
+    if (j < n && lane == j) a.tau[(int64_t(mat) * a.tiles + tile) * n + j] = taus[j];
+  // the triangle (rows < n are lane's first row, lanes 0 .. n-1)
+  if (a.Xn) {
+    const int mn = a.tiles * n;
+#pragma unroll
+    for (int c = 0; c < kWN; ++c)
+      if (c < n && lane < n)
+        a.Xn[(int64_t(mat) * n + c) * mn + tile * n + lane] = lane <= c ? x[c][0] : 0.f;
+  } else {
+    float diag = 0.f;
+#pragma unroll
+    for (int c = 0; c < kWN; ++c)
+      if (lane == c) diag = x[c][0];
+    const float sg = diag < 0.f ? -1.f : 1.f;
+#pragma unroll
+    for (int c = 0; c < kWN; ++c)
+      if (c < n && lane < n) a.R[(int64_t(mat) * n + lane) * n + c] = lane <= c ? sg * x[c][0] : 0.f;
+    if (lane < n) a.sgn[int64_t(mat) * n + lane] = sg;
+  }
+}
+
+__global__ __launch_bounds__(256) void tsqr_form_wave_kernel(TsqrForm a) {
+  const int lane = threadIdx.x & 63;
+  const int t = int(blockIdx.x) * 4 + int(threadIdx.x >> 6);
+  if (t >= a.tiles * a.M) return;
+  const int mat = t / a.tiles, tile = t % a.tiles;
+  const int n = a.n;
+  const int r0 = tile * kTR;
+  const int rows = min(kTR, a.m_l - r0);
+  const float *V = a.V + int64_t(mat) * n * a.m_l;
+  float C[kWN][kWQ];
+#pragma unroll
+  for (int c = 0; c < kWN; ++c)
+#pragma unroll
+    for (int q = 0; q < kWQ; ++q) {
+      const int r = lane + 64 * q;
+      float b = 0.f;
+      if (c < n && r < n) {
+        if (a.Qup) b = a.Qup[(int64_t(mat) * n + c) * (int64_t(a.tiles) * n) + tile * n + r];
+        else b = r == c ? a.sgn[int64_t(mat) * n + c] : 0.f;
+      }
+      C[c][q] = b;
+    }
+  const float *tau = a.tau + (int64_t(mat) * a.tiles + tile) * n;
+#pragma unroll
+  for (int jj = 0; jj < kWN; ++jj) {
+    const int j = kWN - 1 - jj;            // reflectors last to first
+    const float tj = j < n ? tau[j] : 0.f;
+    if (tj == 0.f) continue;
+    // reflector j (read from the level's V; other waves cover the latency)
+    float v[kWQ];
+#pragma unroll
+    for (int q = 0; q < kWQ; ++q) {
+      const int r = lane + 64 * q;
+      const float vr = r < rows ? V[int64_t(j) * a.m_l + r0 + r] : 0.f;
+      v[q] = r > j ? vr : (r == j ? 1.f : 0.f);
+    }
+    float d[kWN];
+#pragma unroll
+    for (int c = 0; c < kWN; ++c) {
+      float pc = 0.f;
+#pragma unroll
+      for (int q = 0; q < kWQ; ++q) pc = fmaf(v[q], C[c][q], pc);
+      d[c] = c < n ? wave_total(pc) : 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < kWN; ++c) {
+      const float w = tj * d[c];
+#pragma unroll
+      for (int q = 0; q < kWQ; ++q) C[c][q] = fmaf(-w, v[q], C[c][q]);
+    }
+  }
+  float *Q = a.Q + int64_t(mat) * n * a.m_l;
+#pragma unroll
+  for (int c = 0; c < kWN; ++c)
+#pragma unroll
+    for (int q = 0; q < kWQ; ++q) {
+      const int r = lane + 64 * q;
+      if (c < n && r < rows) Q[int64_t(c) * a.m_l + r0 + r] = C[c][q];
+    }
 }
 
 // Rows of each level: m, then tiles * n while more than one tile.
@@ -248,11 +445,17 @@ hipError_t launch_tsqr(const void *src, int dtype, const int32_t *cols, int M, i
     a.Xn = l + 1 < L ? X[l + 1] : nullptr;
     a.R = R; a.sgn = sgn;
     const dim3 grid(unsigned(a.tiles), unsigned(M)), block(256);
-    if (l == 0) {
-      if (dtype == LORA_BF16) hipLaunchKernelGGL((tsqr_factor_kernel<uint16_t, true>), grid, block, 0, s, a);
-      else hipLaunchKernelGGL((tsqr_factor_kernel<float, true>), grid, block, 0, s, a);
+    const size_t lds = size_t(n) * kTR * sizeof(float);
+    if (n <= kWN) {
+      const dim3 gw(unsigned((int64_t(a.tiles) * M + 3) / 4));
+      if (l > 0) hipLaunchKernelGGL((tsqr_factor_wave_kernel<float, false>), gw, block, 0, s, a);
+      else if (dtype == LORA_BF16) hipLaunchKernelGGL((tsqr_factor_wave_kernel<uint16_t, true>), gw, block, 0, s, a);
+      else hipLaunchKernelGGL((tsqr_factor_wave_kernel<float, true>), gw, block, 0, s, a);
+    } else if (l == 0) {
+      if (dtype == LORA_BF16) hipLaunchKernelGGL((tsqr_factor_kernel<uint16_t, true>), grid, block, lds, s, a);
+      else hipLaunchKernelGGL((tsqr_factor_kernel<float, true>), grid, block, lds, s, a);
     } else {
-      hipLaunchKernelGGL((tsqr_factor_kernel<float, false>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((tsqr_factor_kernel<float, false>), grid, block, lds, s, a);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -265,7 +468,12 @@ hipError_t launch_tsqr(const void *src, int dtype, const int32_t *cols, int M, i
     f.Qup = l + 1 < L ? X[l + 1] : nullptr;
     f.sgn = sgn;
     f.Q = l == 0 ? Qt : X[l];
-    hipLaunchKernelGGL(tsqr_form_kernel, dim3(unsigned(f.tiles), unsigned(M)), dim3(256), 0, s, f);
+    if (n <= kWN)
+      hipLaunchKernelGGL(tsqr_form_wave_kernel, dim3(unsigned((int64_t(f.tiles) * M + 3) / 4)), dim3(256), 0,
+                         s, f);
+    else
+      hipLaunchKernelGGL(tsqr_form_kernel, dim3(unsigned(f.tiles), unsigned(M)), dim3(256),
+                         2 * size_t(n) * kTR * sizeof(float), s, f);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
