@@ -62,10 +62,29 @@ struct CoreArgs {
   float *out_sigma;       // [M][n]
 };
 
+// One DPP move of a double (its two halves; lanes without a source read 0).
+template <int kCtrl, int kRowMask, int kBankMask>
+__device__ __forceinline__ double dpp_d(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(b)), kCtrl, kRowMask, kBankMask, false));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(b >> 32)), kCtrl, kRowMask, kBankMask, false));
+  return __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
+}
+
+// Sum over the 64 lanes by DPP moves (quad sums, rows of 16 by row_shr 4
+// and 8, then row_bcast 15 and 31 into lane 63), read back wave-uniform: a
+// fixed order without LDS round trips.
 __device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_d<0xb1, 0xf, 0xf>(v);
+  v += dpp_d<0x4e, 0xf, 0xf>(v);
+  v += dpp_d<0x114, 0xf, 0xe>(v);
+  v += dpp_d<0x118, 0xf, 0xc>(v);
+  v += dpp_d<0x142, 0xa, 0xf>(v);
+  v += dpp_d<0x143, 0xc, 0xf>(v);
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(b)), 63));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(b >> 32)), 63));
+  return __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
 }
 
 // CN: the smallest of 16, 32, 64 that holds n (LDS sized for it, so that

@@ -206,9 +206,9 @@ __global__ __launch_bounds__(256) void tsqr_form_kernel(TsqrForm a) {
 
 // The same factorisation and Q formation with one wave per tile, for n <= 16
 // (the ranks of compressed adapters): the tile lives in registers, lane l
-// holding rows l, l + 64, l + 128, l + 192 of every column, and every
-// reduction is one butterfly over the wave (no barrier).  Four tiles per
-// workgroup.  Same reflectors, taus, triangles and signs as the workgroup
+// holding rows 4l .. 4l + 3 of every column (one vector load or store per
+// column), and every reduction is a DPP sum over the wave (no barrier, no
+// LDS).  Four tiles per workgroup.  Same reflectors, taus, triangles and signs as the workgroup
 // kernels above, summed in another (fixed) order.
 constexpr int kWN = 16;         // most columns of the wave kernels
 constexpr int kWQ = kTR / 64;   // rows per lane
@@ -227,6 +227,34 @@ __device__ __forceinline__ float wave_total(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// Four consecutive rows of a column, as floats: one vector load when the
+// four are in the tile and aligned (m_l % 4 == 0, 16-byte aligned bases).
+template <typename E>
+__device__ __forceinline__ void load4(const E *p, int avail, bool vec, float (&v)[4]) {
+  if (vec && avail >= 4) {
+    if constexpr (sizeof(E) == 2) {
+      const uint2 w = *reinterpret_cast<const uint2 *>(p);
+      v[0] = bf_lo(w.x); v[1] = bf_hi(w.x); v[2] = bf_lo(w.y); v[3] = bf_hi(w.y);
+    } else {
+      const float4 w = *reinterpret_cast<const float4 *>(p);
+      v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = q < avail ? Elem<E>::to_f(p[q]) : 0.f;
+  }
+}
+
+__device__ __forceinline__ void store4(float *p, int avail, bool vec, const float (&v)[4]) {
+  if (vec && avail >= 4) {
+    *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (q < avail) p[q] = v[q];
+  }
+}
+
 template <typename E, bool kLevel0>
 __global__ __launch_bounds__(256) void tsqr_factor_wave_kernel(TsqrLevel a) {
   const int lane = threadIdx.x & 63;
@@ -236,36 +264,36 @@ __global__ __launch_bounds__(256) void tsqr_factor_wave_kernel(TsqrLevel a) {
   const int n = a.n;
   const int r0 = tile * kTR;
   const int rows = min(kTR, a.m_l - r0);
+  const int rl = 4 * lane;                       // the lane's rows: rl .. rl + 3
+  const int avail = min(4, max(0, rows - rl));
+  const uintptr_t in = kLevel0 ? reinterpret_cast<uintptr_t>(a.src) : reinterpret_cast<uintptr_t>(a.X);
+  const bool vec = a.m_l % 4 == 0 && (in | reinterpret_cast<uintptr_t>(a.V)) % 16 == 0;
   float x[kWN][kWQ];
 #pragma unroll
-  for (int c = 0; c < kWN; ++c)
-#pragma unroll
-    for (int q = 0; q < kWQ; ++q) {
-      const int r = lane + 64 * q;
-      float v = 0.f;
-      if (c < n && r < rows) {
-        if constexpr (kLevel0) {
-          const int64_t srow = a.cols[int64_t(mat) * n + c];
-          v = Elem<E>::to_f(static_cast<const E *>(a.src)[srow * a.m_l + r0 + r]);
-        } else {
-          v = a.X[(int64_t(mat) * n + c) * a.m_l + r0 + r];
-        }
+  for (int c = 0; c < kWN; ++c) {
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (c < n) {
+      if constexpr (kLevel0) {
+        const int64_t srow = a.cols[int64_t(mat) * n + c];
+        load4<E>(static_cast<const E *>(a.src) + srow * a.m_l + r0 + rl, avail, vec, v);
+      } else {
+        load4<float>(a.X + (int64_t(mat) * n + c) * a.m_l + r0 + rl, avail, vec, v);
       }
-      x[c][q] = v;
     }
+#pragma unroll
+    for (int q = 0; q < kWQ; ++q) x[c][q] = v[q];
+  }
   float taus[kWN];
 #pragma unroll
   for (int j = 0; j < kWN; ++j) {
     taus[j] = 0.f;
     if (j >= n) continue;
-    // reflector for column j (row j is lane j's first row)
-    const float xj = __shfl(x[j][0], j, 64);
+    // reflector for column j (row j is lane j / 4's row j % 4)
+    const float xj = __shfl(x[j][j & 3], j >> 2, 64);
     float part = 0.f;
 #pragma unroll
-    for (int q = 0; q < kWQ; ++q) {
-      const int r = lane + 64 * q;
-      if (r > j) part = fmaf(x[j][q], x[j][q], part);
-    }
+    for (int q = 0; q < kWQ; ++q)
+      if (rl + q > j) part = fmaf(x[j][q], x[j][q], part);
     const float below = wave_total(part);
     float beta = xj, tau = 0.f, scl = 0.f;
     if (below > 0.f) {
@@ -279,7 +307,7 @@ __global__ __launch_bounds__(256) void tsqr_factor_wave_kernel(TsqrLevel a) {
     float v[kWQ];
 #pragma unroll
     for (int q = 0; q < kWQ; ++q) {
-      const int r = lane + 64 * q;
+      const int r = rl + q;
       if (r > j) x[j][q] *= scl;
       v[q] = r > j ? x[j][q] : (r == j ? 1.f : 0.f);
       if (r == j) x[j][q] = beta;
@@ -305,32 +333,46 @@ __global__ __launch_bounds__(256) void tsqr_factor_wave_kernel(TsqrLevel a) {
   // reflectors and taus out
   float *V = a.V + int64_t(mat) * n * a.m_l;
 #pragma unroll
-  for (int c = 0; c < kWN; ++c)
+  for (int c = 0; c < kWN; ++c) {
+    if (c >= n) continue;
+    float v[4];
 #pragma unroll
-    for (int q = 0; q < kWQ; ++q) {
-      const int r = lane + 64 * q;
-      if (c < n && r < rows) V[int64_t(c) * a.m_l + r0 + r] = r > c ? x[c][q] : 0.f;
-    }
+    for (int q = 0; q < kWQ; ++q) v[q] = rl + q > c ? x[c][q] : 0.f;
+    store4(V + int64_t(c) * a.m_l + r0 + rl, avail, vec, v);
+  }
 #pragma unroll
   for (int j = 0; j < kWN; ++j)
     if (j < n && lane == j) a.tau[(int64_t(mat) * a.tiles + tile) * n + j] = taus[j];
-  // the triangle (rows < n are lane's first row, lanes 0 .. n-1)
+  // the triangle: rows t < n (lanes 0 .. 3)
   if (a.Xn) {
     const int mn = a.tiles * n;
 #pragma unroll
     for (int c = 0; c < kWN; ++c)
-      if (c < n && lane < n)
-        a.Xn[(int64_t(mat) * n + c) * mn + tile * n + lane] = lane <= c ? x[c][0] : 0.f;
+#pragma unroll
+      for (int q = 0; q < kWQ; ++q) {
+        const int tr = rl + q;
+        if (c < n && tr < n) a.Xn[(int64_t(mat) * n + c) * mn + tile * n + tr] = tr <= c ? x[c][q] : 0.f;
+      }
   } else {
-    float diag = 0.f;
+    float sg[kWQ];
+#pragma unroll
+    for (int q = 0; q < kWQ; ++q) {
+      float diag = 0.f;
+#pragma unroll
+      for (int c = 0; c < kWN; ++c)
+        if (rl + q == c) diag = x[c][q];
+      sg[q] = diag < 0.f ? -1.f : 1.f;
+    }
 #pragma unroll
     for (int c = 0; c < kWN; ++c)
-      if (lane == c) diag = x[c][0];
-    const float sg = diag < 0.f ? -1.f : 1.f;
 #pragma unroll
-    for (int c = 0; c < kWN; ++c)
-      if (c < n && lane < n) a.R[(int64_t(mat) * n + lane) * n + c] = lane <= c ? sg * x[c][0] : 0.f;
-    if (lane < n) a.sgn[int64_t(mat) * n + lane] = sg;
+      for (int q = 0; q < kWQ; ++q) {
+        const int tr = rl + q;
+        if (c < n && tr < n) a.R[(int64_t(mat) * n + tr) * n + c] = tr <= c ? sg[q] * x[c][q] : 0.f;
+      }
+#pragma unroll
+    for (int q = 0; q < kWQ; ++q)
+      if (rl + q < n) a.sgn[int64_t(mat) * n + rl + q] = sg[q];
   }
 }
 
@@ -342,13 +384,17 @@ __global__ __launch_bounds__(256) void tsqr_form_wave_kernel(TsqrForm a) {
   const int n = a.n;
   const int r0 = tile * kTR;
   const int rows = min(kTR, a.m_l - r0);
+  const int rl = 4 * lane;
+  const int avail = min(4, max(0, rows - rl));
+  const bool vec = a.m_l % 4 == 0 &&
+                   (reinterpret_cast<uintptr_t>(a.V) | reinterpret_cast<uintptr_t>(a.Q)) % 16 == 0;
   const float *V = a.V + int64_t(mat) * n * a.m_l;
   float C[kWN][kWQ];
 #pragma unroll
   for (int c = 0; c < kWN; ++c)
 #pragma unroll
     for (int q = 0; q < kWQ; ++q) {
-      const int r = lane + 64 * q;
+      const int r = rl + q;
       float b = 0.f;
       if (c < n && r < n) {
         if (a.Qup) b = a.Qup[(int64_t(mat) * n + c) * (int64_t(a.tiles) * n) + tile * n + r];
@@ -363,12 +409,13 @@ __global__ __launch_bounds__(256) void tsqr_form_wave_kernel(TsqrForm a) {
     const float tj = j < n ? tau[j] : 0.f;
     if (tj == 0.f) continue;
     // reflector j (read from the level's V; other waves cover the latency)
+    float vr[4];
+    load4<float>(V + int64_t(j) * a.m_l + r0 + rl, avail, vec, vr);
     float v[kWQ];
 #pragma unroll
     for (int q = 0; q < kWQ; ++q) {
-      const int r = lane + 64 * q;
-      const float vr = r < rows ? V[int64_t(j) * a.m_l + r0 + r] : 0.f;
-      v[q] = r > j ? vr : (r == j ? 1.f : 0.f);
+      const int r = rl + q;
+      v[q] = r > j ? vr[q] : (r == j ? 1.f : 0.f);
     }
     float d[kWN];
 #pragma unroll
@@ -388,11 +435,7 @@ __global__ __launch_bounds__(256) void tsqr_form_wave_kernel(TsqrForm a) {
   float *Q = a.Q + int64_t(mat) * n * a.m_l;
 #pragma unroll
   for (int c = 0; c < kWN; ++c)
-#pragma unroll
-    for (int q = 0; q < kWQ; ++q) {
-      const int r = lane + 64 * q;
-      if (c < n && r < rows) Q[int64_t(c) * a.m_l + r0 + r] = C[c][q];
-    }
+    if (c < n) store4(Q + int64_t(c) * a.m_l + r0 + rl, avail, vec, C[c]);
 }
 
 // Rows of each level: m, then tiles * n while more than one tile.
