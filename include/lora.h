@@ -403,7 +403,11 @@ int32_t lora_residency_create(const lora_residency_config *cfg, lora_residency *
 void lora_residency_destroy(lora_residency *r);
 /* Admits a batch (host ids [n]) and, on copy_stream, copies its missing
  * adapters' rows into their pages and uploads its tables (one of two table
- * sets, alternating); compute_stream then waits for those copies.  Pages and
+ * sets, alternating); compute_stream then waits for those copies.  When the
+ * store is mapped into the device's address space (hipHostMalloc memory,
+ * every base 16-byte aligned) the rows are copied by one gather kernel that
+ * reads the store over the host link; otherwise by one copy call per run of
+ * consecutive pages.  Pages and
  * the table set that batch i - 2 used are overwritten only after batch i - 2's
  * finish point, so the copies of batch i + 1 may run while batch i computes.
  * pool_out: the descriptor the batch's calls must use.  Every prepare is

@@ -26,7 +26,11 @@
 // stream waits for both.  Batch i overwrites pages and the table set last
 // used by batch i - 2 only after that batch's kernels have finished (its
 // finish event), so with one compute stream the next batch's copies overlap
-// the current batch's kernels.
+// the current batch's kernels.  When the store is mapped into the device's
+// address space (pinned memory from hipHostMalloc is), the copies are one
+// gather kernel that reads every copied row over the host link: one launch
+// per batch instead of one copy call per run of pages, whose fixed cost
+// dominated batches of many short runs.
 #include <algorithm>
 #include <set>
 #include <vector>
@@ -59,14 +63,36 @@ struct lora_residency {
   int64_t rows_copied = 0, evictions = 0, bytes_copied = 0;
   std::vector<lora_page_copy> copies;
   std::vector<int32_t> evicted;
+  bool gather = false;                        // copies by the gather kernel
+  const char *dev_a = nullptr, *dev_b = nullptr;   // device addresses of the store
 };
 
 namespace {
 
 int64_t align64(int64_t x) { return (x + 63) & ~int64_t(63); }
 
+// One table set: rank [N], page_start [N+1], page_ids [n_pages], then the
+// batch's copied rows as (store row, page) pairs [n_pages] (a page is written
+// at most once per batch).
 int64_t table_set_ints(int32_t N, int64_t n_pages) {
-  return align64(N) + align64(int64_t(N) + 1) + align64(n_pages > 0 ? n_pages : 1);
+  const int64_t np = n_pages > 0 ? n_pages : 1;
+  return align64(N) + align64(int64_t(N) + 1) + align64(np) + align64(2 * np);
+}
+
+// Copies rows [n_rows] of the store (mapped host memory) into the pool's
+// pages: workgroups stride over the rows, 16 bytes per thread per step.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const int2 *rows, int n_rows, const char *sa,
+                                                          const char *sb, char *ap, char *bp, int64_t ra,
+                                                          int64_t rb) {
+  for (int i = blockIdx.x; i < n_rows; i += gridDim.x) {
+    const int2 e = rows[i];
+    const uint4 *src_a = reinterpret_cast<const uint4 *>(sa + int64_t(e.x) * ra);
+    const uint4 *src_b = reinterpret_cast<const uint4 *>(sb + int64_t(e.x) * rb);
+    uint4 *dst_a = reinterpret_cast<uint4 *>(ap + int64_t(e.y) * ra);
+    uint4 *dst_b = reinterpret_cast<uint4 *>(bp + int64_t(e.y) * rb);
+    for (int64_t k = threadIdx.x; k < ra / 16; k += 256) dst_a[k] = src_a[k];
+    for (int64_t k = threadIdx.x; k < rb / 16; k += 256) dst_b[k] = src_b[k];
+  }
 }
 
 // The policy above.  On refusal nothing changes.
@@ -235,6 +261,21 @@ int32_t lora_residency_create(const lora_residency_config *cfg, lora_residency *
     lora_residency_destroy(r);
     return LORA_ERR_DEVICE;
   }
+  // the gather kernel when the store is device-mapped and every base is
+  // 16-byte aligned (row sizes are multiples of 128 bytes); else one copy
+  // call per run of pages
+  void *da = nullptr, *db = nullptr;
+  const bool aligned = ((reinterpret_cast<uintptr_t>(cfg->store_a) | reinterpret_cast<uintptr_t>(cfg->store_b) |
+                         reinterpret_cast<uintptr_t>(cfg->a_pages) | reinterpret_cast<uintptr_t>(cfg->b_pages)) %
+                        16) == 0;
+  if (aligned && hipHostGetDevicePointer(&da, const_cast<void *>(cfg->store_a), 0) == hipSuccess &&
+      hipHostGetDevicePointer(&db, const_cast<void *>(cfg->store_b), 0) == hipSuccess && da && db) {
+    r->gather = true;
+    r->dev_a = static_cast<const char *>(da);
+    r->dev_b = static_cast<const char *>(db);
+  } else {
+    (void)hipGetLastError();   // not mapped: the copy-call path, no error left behind
+  }
   *out = r;
   return LORA_OK;
 }
@@ -273,21 +314,41 @@ int32_t lora_residency_prepare(lora_residency *r, const int32_t *ids, int64_t n,
   const char *sa = static_cast<const char *>(c.store_a);
   const char *sb = static_cast<const char *>(c.store_b);
   const size_t ra = size_t(c.d_in) * r->esize, rb = size_t(c.d_out) * r->esize;
+  const int64_t np = c.n_pages > 0 ? c.n_pages : 1;
+  const int64_t list_off = align64(N) + align64(int64_t(N) + 1) + align64(np);
+  int32_t *list = stg + list_off;             // (store row, page) of every copied row
+  int64_t n_rows = 0;
   for (const lora_page_copy &q : r->copies) {
     const int64_t row = c.store_row[q.adapter] + q.row;
-    if (hipMemcpyAsync(ap + size_t(q.page) * ra, sa + size_t(row) * ra, size_t(q.count) * ra,
-                       hipMemcpyHostToDevice, cs) != hipSuccess ||
-        hipMemcpyAsync(bp + size_t(q.page) * rb, sb + size_t(row) * rb, size_t(q.count) * rb,
-                       hipMemcpyHostToDevice, cs) != hipSuccess)
+    if (r->gather) {
+      for (int32_t i = 0; i < q.count; ++i) {
+        list[2 * n_rows] = int32_t(row + i);
+        list[2 * n_rows + 1] = q.page + i;
+        ++n_rows;
+      }
+    } else if (hipMemcpyAsync(ap + size_t(q.page) * ra, sa + size_t(row) * ra, size_t(q.count) * ra,
+                              hipMemcpyHostToDevice, cs) != hipSuccess ||
+               hipMemcpyAsync(bp + size_t(q.page) * rb, sb + size_t(row) * rb, size_t(q.count) * rb,
+                              hipMemcpyHostToDevice, cs) != hipSuccess) {
       return LORA_ERR_DEVICE;
+    }
     r->rows_copied += q.count;
     r->bytes_copied += int64_t(q.count) * int64_t(ra + rb);
   }
   r->evictions += int64_t(r->evicted.size());
   int32_t *dev = c.tables + s * r->set_ints;
-  if (hipMemcpyAsync(dev, stg, size_t(r->set_ints) * sizeof(int32_t), hipMemcpyHostToDevice, cs) !=
-          hipSuccess ||
-      hipEventRecord(r->upload[s], cs) != hipSuccess || hipEventRecord(r->ready, cs) != hipSuccess ||
+  // the tables, and the row list when the gather kernel copies
+  const int64_t up = r->gather ? list_off + 2 * n_rows : list_off;
+  if (hipMemcpyAsync(dev, stg, size_t(up) * sizeof(int32_t), hipMemcpyHostToDevice, cs) != hipSuccess)
+    return LORA_ERR_DEVICE;
+  if (r->gather && n_rows > 0) {
+    const unsigned grid = unsigned(n_rows < 1024 ? n_rows : 1024);
+    hipLaunchKernelGGL(gather_rows_kernel, dim3(grid), dim3(256), 0, cs,
+                       reinterpret_cast<const int2 *>(dev + list_off), int(n_rows), r->dev_a, r->dev_b, ap, bp,
+                       int64_t(ra), int64_t(rb));
+    if (hipGetLastError() != hipSuccess) return LORA_ERR_DEVICE;
+  }
+  if (hipEventRecord(r->upload[s], cs) != hipSuccess || hipEventRecord(r->ready, cs) != hipSuccess ||
       hipStreamWaitEvent(ks, r->ready, 0) != hipSuccess)
     return LORA_ERR_DEVICE;
   r->upload_rec[s] = true;
