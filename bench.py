@@ -667,14 +667,15 @@ def measured_traffic(kernel, workload):
             table = json.load(fh)
     except (OSError, ValueError):
         return None
-    # the instantiation of this kernel with the most dispatches in the run
+    # the instantiation of this kernel with the most dispatches in the run,
+    # among entries taken from the current sources
+    h = kernel_source_hash()
     cands = [v for k, v in table.items()
-             if k.endswith("|" + workload) and (k.startswith(kernel + "<") or k.startswith(kernel + "|"))]
+             if k.endswith("|" + workload) and (k.startswith(kernel + "<") or k.startswith(kernel + "|"))
+             and v.get("source_sha256_16") == h]
     if not cands:
         return None
     ent = max(cands, key=lambda v: v["fetch"]["dispatches"])
-    if ent.get("source_sha256_16") != kernel_source_hash():
-        return None
     return ent.get("hbm_bytes_per_launch")
 
 
