@@ -412,8 +412,10 @@ def measure(w, args, torch, np, B, D, steps, warmup, full):
 
 def residency_run(w, bn, args, torch, np, B, D):
     """The pool held to --residency-frac of the fleet's rank rows, filled from
-    a pinned host store: batch b + 1's copies (on a side stream) overlap batch
-    b's forward; against the same batches on the fully resident pool."""
+    a pinned host store: batch b + 1's copies (a gather kernel reading the
+    device-mapped store, or one copy per page run where the store cannot be
+    mapped, on a side stream) overlap batch b's forward; against the same
+    batches on the fully resident pool."""
     from lora_adapter_amd import workloads as wl
     rows = np.concatenate([w.page_ids[w.page_start[a]:w.page_start[a + 1]]
                            for a in range(w.n_adapters)]).astype(np.int64)
@@ -457,8 +459,9 @@ def residency_run(w, bn, args, torch, np, B, D):
             "copied_bytes_per_batch": moved,
             "evictions_per_batch": (s1["evictions"] - s0["evictions"]) / nb,
             "h2d_GB_s_lower_bound": moved / t_managed / 1e9,
-            "note": "each batch's missing adapters copied H2D on a side stream while the "
-                    "previous batch computes; wall time per batch over 40 Zipf batches"}
+            "note": "each batch's missing adapters copied from the pinned host store on a "
+                    "side stream while the previous batch computes; wall time per batch over "
+                    "40 Zipf batches"}
 
 
 def gemm_roofline(w, L, B, kind, st, base_flops, P, R_pairs, R_used, e):
