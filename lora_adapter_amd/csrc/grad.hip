@@ -20,6 +20,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
 constexpr int kGradThreads = 256;
 constexpr int kGradCPL = 4;                           // columns per lane
@@ -189,182 +190,320 @@ __device__ __forceinline__ void lds_bar() {
 constexpr int kOuterCols = 256;
 constexpr int kOuterK = 32;
 
-template <bool kMask>
-__global__ __launch_bounds__(256) void seg_outer_mfma_kernel(SegOuterArgs a) {
+// Segment index of pair p, found by the whole workgroup: each round tests
+// 256 evenly spaced segment starts, one load per thread, so S <= 256 takes
+// one round trip and S <= 65536 two (a binary search took log2 S dependent
+// ones).  seg_off[0] = 0 <= p < seg_off[S] holds throughout.
+__device__ __forceinline__ int seg_of_wg(const int32_t *seg_off, int S, int p, int *s_cnt) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int lo = 0, hi = S;
+  while (hi - lo > 1) {
+    const int step = (hi - lo + 255) / 256;
+    const int i = lo + tid * step;
+    const uint64_t b = __ballot(i < hi && seg_off[i] <= p);
+    if (lane == 0) s_cnt[wave] = __popcll(b);
+    lds_bar();
+    const int c = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];   // >= 1: i = lo passes
+    lds_bar();                                                  // s_cnt reused next round
+    lo += (c - 1) * step;
+    hi = min(hi, lo + step);
+  }
+  return lo;
+}
+
+// First pair after l that starts a segment (bit set in the chunk's start
+// mask), or n.
+__device__ __forceinline__ int next_start(const uint64_t *bits, int l, int n) {
+  for (int w = (l + 1) >> 6; w < 4; ++w) {
+    uint64_t b = bits[w];
+    const int lo = (l + 1) - 64 * w;
+    if (lo > 0) b &= ~0ull << lo;
+    if (b) return min(n, 64 * w + __builtin_ctzll(b));
+  }
+  return n;
+}
+
+template <bool kMask, bool kG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMask ? 2 : 3)))
+void seg_outer_mfma_kernel(SegOuterArgs a) {
   constexpr int RB = kGradRankChunk;
-  // staged row pitch (bf16): rows 8 apart (the four lane groups of a
-  // transposed 16-bit read) then start 16 banks apart
-  constexpr int ZP = kOuterCols + 4;
+  // staged row pitch (bf16; 4 banks): the 16 rows of a 16-byte G operand
+  // read fall on distinct banks
+  constexpr int ZP = kOuterCols + 8;
   __shared__ int s_row[kGradPairChunk];
-  __shared__ __attribute__((aligned(16))) float s_cf[kGradPairChunk][RB];
+  __shared__ int s_ad[kGradPairChunk];
+  __shared__ int s_rk[kGradPairChunk];
+  // the coefficients split once into bf16 high and low parts, rank row
+  // major, so that a lane's A operand (8 consecutive pairs of one rank row)
+  // is one 16-byte read; the row pitch puts the 16 rank rows of a read on
+  // distinct banks
+  constexpr int AP = kGradPairChunk + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t s_ah[RB][AP];
+  __shared__ __attribute__((aligned(16))) uint16_t s_al[RB][AP];
   __shared__ __attribute__((aligned(16))) uint16_t s_z[kOuterK][ZP];
-  const int P = a.plan.hdr[LORA_PH_PAIRS];
-  const int S = a.plan.hdr[LORA_PH_SEGS];
+  __shared__ uint64_t s_start[4];          // segment starts of the chunk, one bit per pair
+  __shared__ int s_cnt[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = blockIdx.y;
   const int pbeg = q * kGradPairChunk;
+  const int64_t TK = int64_t(a.T) * a.K;
+  // The prologue keeps its dependent round trips few and overlapped: the
+  // header and this thread's pair in one; then the pair's rank, the first
+  // segment's B page entry, the first step's token rows and the segment
+  // search together; then the coefficients and the B page ids; then the B
+  // rows.  Plan entries past the pair count are read (in bounds) but unused.
+  const int P = a.plan.hdr[LORA_PH_PAIRS];
+  const int S = a.plan.hdr[LORA_PH_SEGS];
+  const int64_t rpairs = a.plan.hdr[LORA_PH_RPAIRS];
+  const int pp = pbeg + tid;
+  const bool inb = pp < TK;
+  const int tk = inb ? a.plan.pair_tk[pp] : 0;
+  const int adp = inb ? a.plan.pair_adapter[pp] : 0;
+  const int uo = inb ? a.plan.u_off[pp] : 0;
   if (pbeg >= P) return;
-  if (int64_t(a.plan.hdr[LORA_PH_RPAIRS]) > a.coef_cap) {
-    if (q == 0 && blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x == 0)
+  if (rpairs > a.coef_cap) {
+    if (q == 0 && blockIdx.x == 0 && blockIdx.z == 0 && tid == 0)
       atomicOr(a.err_word, LORA_DEVERR_CAPACITY);
     return;
   }
-  const int pend = min(P, pbeg + kGradPairChunk);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = min(P, pbeg + kGradPairChunk) - pbeg;
+  const bool valid = tid < n;
   const int j0 = blockIdx.z * RB;
+  const int rk = valid ? a.rank[adp] : 0;
+  s_row[tid] = valid ? tk / a.K : 0;
+  s_ad[tid] = valid ? adp : -1;
+  lds_bar();
   {
-    const int pp = pbeg + tid;
-    int row = 0;
-    float cf[RB];
-#pragma unroll
-    for (int jj = 0; jj < RB; ++jj) cf[jj] = 0.f;
-    if (pp < pend) {
-      row = a.plan.pair_tk[pp] / a.K;
-      const int r = a.rank[a.plan.pair_adapter[pp]];
-      const int nr = min(RB, min(r, a.max_rank) - j0);
-      const float *c = a.coef + a.plan.u_off[pp] + j0;
-#pragma unroll
-      for (int jj = 0; jj < RB; ++jj)
-        if (jj < nr) cf[jj] = c[jj];
-    }
-    s_row[tid] = row;
-#pragma unroll
-    for (int jj = 0; jj < RB; jj += 4)
-      *reinterpret_cast<float4 *>(&s_cf[tid][jj]) = make_float4(cf[jj], cf[jj + 1], cf[jj + 2], cf[jj + 3]);
+    const uint64_t b = __ballot(valid && (tid == 0 || s_ad[tid - 1] != adp));
+    if (lane == 0) s_start[wave] = b;
   }
-  __syncthreads();
+  lds_bar();
 
   const int c0 = blockIdx.x * kOuterCols;
   const uint16_t *Z = static_cast<const uint16_t *>(a.Z);
   // staging: thread tid fills row tid / 8 of the step, columns (tid % 8) * 32 .. +31
   const int zr = tid >> 3, zc = (tid & 7) * 32;
-  int s = seg_of(a.plan.seg_off, S, pbeg);
-  for (int p = pbeg; p < pend; ++s) {
-    const int send = min(pend, a.plan.seg_off[s + 1]);
-    const int ad = a.plan.seg_adapter[s];
-    const int r = a.rank[ad];
+  // two steps of token rows in flight: buffer A holds a segment's even
+  // steps, buffer B its odd ones.  Every fetch is issued unconditionally
+  // (past the segment's end it re-reads its last row, a cache hit, and the
+  // staging zeroes it): a conditional fetch leaves the compiler a merge of
+  // old and new register values, which it resolves with copies that wait
+  // for the loads just issued, and the prefetch is lost.
+  uint4 zA[4], zB[4];
+  uint4 mA[2], mB[2];
+  auto fetch = [&](uint4 (&zv)[4], uint4 (&mv)[2], int k0, int l_beg, int l_end) {
+    const int64_t row = s_row[min(max(k0 + zr, l_beg), l_end - 1)];
+    const uint16_t *src = Z + row * a.d + c0 + zc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) zv[e] = *reinterpret_cast<const uint4 *>(src + 8 * e);
+    if (kMask) {
+      const uint8_t *m = a.mask + row * a.d + c0 + zc;
+      mv[0] = *reinterpret_cast<const uint4 *>(m);
+      mv[1] = *reinterpret_cast<const uint4 *>(m + 16);
+    }
+  };
+  auto stage = [&](const uint4 (&zv)[4], const uint4 (&mv)[2], int k0, int l_beg, int l_end) {
+    uint32_t w[16];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      w[4 * e] = zv[e].x; w[4 * e + 1] = zv[e].y; w[4 * e + 2] = zv[e].z; w[4 * e + 3] = zv[e].w;
+    }
+    // rows outside the segment (a step that crosses one of its ends) are
+    // zeroed; the test is uniform over the workgroup
+    if (k0 < l_beg || k0 + kOuterK > l_end) {
+      const bool in = k0 + zr >= l_beg && k0 + zr < l_end;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) w[i] = in ? w[i] : 0u;
+    }
+    if constexpr (kMask) {
+      // keep-mask bytes are 0 or 1: the bytes of elements 2i and 2i + 1 go
+      // to bits 0 and 16 of x (one byte permute), and x . 0xffff (as
+      // (x << 16) - x) is the 16-bit lane mask of the pair
+      const uint32_t mb[8] = {mv[0].x, mv[0].y, mv[0].z, mv[0].w, mv[1].x, mv[1].y, mv[1].z, mv[1].w};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t x = __builtin_amdgcn_perm(0u, mb[i >> 1], (i & 1) ? 0x0c030c02u : 0x0c010c00u);
+        w[i] &= (x << 16) - x;
+      }
+    }
+    // rows are 8-byte aligned (pitch ZP): memcpy lets the compiler pick
+    // the widest aligned LDS stores
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint4 v4 = make_uint4(w[4 * e], w[4 * e + 1], w[4 * e + 2], w[4 * e + 3]);
+      __builtin_memcpy(&s_z[zr][zc + 8 * e], &v4, 16);
+    }
+  };
+  // dY.B^T partials (dB pass): the segment's 16 B rows over this column
+  // tile, staged in LDS (row pitch GP: the 16 rows of one 16-byte column
+  // chunk, read by 16 lanes at once, fall on distinct banks).  Thread tid
+  // moves column chunk tid % 32 of rows tid / 32 and tid / 32 + 8.
+  constexpr int GP = kOuterCols + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t s_gb[kG ? RB : 1][kG ? GP : 8];
+  const int jr = lane & 15;
+  const int gj = tid >> 5, gc = (tid & 31) * 8;
+  int gpid[2] = {0, 0};
+  uint4 gv[2];
+  auto g_ids = [&](int ps, int nr) {
+    if constexpr (kG) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        if (gj + 8 * h < nr) gpid[h] = a.page_ids[ps + j0 + gj + 8 * h];
+    }
+  };
+  auto g_rows = [&](int nr) {
+    if constexpr (kG) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        gv[h] = make_uint4(0u, 0u, 0u, 0u);
+        if (gj + 8 * h < nr)
+          gv[h] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.b_pages) +
+                                                   int64_t(gpid[h]) * a.d + c0 + gc);
+      }
+    }
+  };
+  auto g_put = [&]() {
+    if constexpr (kG) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) __builtin_memcpy(&s_gb[gj + 8 * h][gc], &gv[h], 16);
+    }
+  };
+
+  // first segment: its adapter's page entry and rank (dB pass) and its
+  // first two steps' token rows; then its B page ids and this thread's
+  // coefficients; then the search for its index (uniform over the
+  // workgroup) and its B rows
+  const int ad0 = s_ad[0];
+  const int l_end0 = next_start(s_start, 0, n);
+  int ps0 = 0, r0 = 0;
+  if constexpr (kG) {
+    ps0 = a.page_start[ad0];
+    r0 = a.rank[ad0];
+  }
+  fetch(zA, mA, 0, 0, l_end0);
+  fetch(zB, mB, kOuterK, 0, l_end0);
+  const int nr0 = min(RB, r0 - j0);
+  const bool g0 = kG && r0 <= a.max_rank && nr0 > 0;
+  if (g0) g_ids(ps0, nr0);
+  {
+    // the coefficients of this thread's pair (zero past its rank)
+    float cf[RB];
+#pragma unroll
+    for (int jj = 0; jj < RB; ++jj) cf[jj] = 0.f;
+    const int nr = min(RB, min(rk, a.max_rank) - j0);
+    const float *c = a.coef + uo + j0;
+#pragma unroll
+    for (int jj = 0; jj < RB; ++jj)
+      if (valid && jj < nr) cf[jj] = c[jj];
+    s_rk[tid] = rk;
+#pragma unroll
+    for (int jj = 0; jj < RB; ++jj) {
+      const uint16_t h = f2bf(cf[jj]);
+      s_ah[jj][tid] = h;
+      s_al[jj][tid] = f2bf(cf[jj] - bf2f(h));
+    }
+  }
+  int s = seg_of_wg(a.plan.seg_off, S, pbeg, s_cnt);
+  if (g0) {
+    g_rows(nr0);
+    g_put();
+  }
+  lds_bar();                                             // s_rk, s_ah, s_al, s_gb
+
+  for (int l_beg = 0; l_beg < n; ++s) {
+    const int l_end = l_beg == 0 ? l_end0 : next_start(s_start, l_beg, n);
+    const int ad = s_ad[l_beg];
+    const int r = s_rk[l_beg];
     if (r > a.max_rank) {
       if (tid == 0 && blockIdx.x == 0 && j0 == 0) atomicOr(a.err_word, LORA_DEVERR_CAPACITY);
     } else if (j0 < r) {
       const int nr = min(RB, r - j0);
-      const int l_beg = p - pbeg, l_end = send - pbeg;
-      uint4 zv[4];
-      uint4 mv[2];
-      auto fetch = [&](int k0) {
-        const int64_t row = s_row[min(k0 + zr, l_end - 1)];
-        const uint16_t *src = Z + row * a.d + c0 + zc;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) zv[e] = *reinterpret_cast<const uint4 *>(src + 8 * e);
-        if (kMask) {
-          const uint8_t *m = a.mask + row * a.d + c0 + zc;
-          mv[0] = *reinterpret_cast<const uint4 *>(m);
-          mv[1] = *reinterpret_cast<const uint4 *>(m + 16);
+      if (l_beg > 0) {
+        const int k1 = l_beg & ~(kOuterK - 1);
+        fetch(zA, mA, k1, l_beg, l_end);
+        fetch(zB, mB, k1 + kOuterK, l_beg, l_end);
+        if constexpr (kG) {
+          g_ids(a.page_start[ad], nr);
+          g_rows(nr);
+          lds_bar();                           // the last segment's G steps are done with s_gb
+          g_put();                             // published by the first step's barrier
         }
-      };
-      auto stage = [&](int k0) {
-        const bool in = k0 + zr < l_end;
-        uint32_t w[16];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          w[4 * e] = zv[e].x; w[4 * e + 1] = zv[e].y; w[4 * e + 2] = zv[e].z; w[4 * e + 3] = zv[e].w;
-        }
-        const uint32_t mb[8] = {mv[0].x, mv[0].y, mv[0].z, mv[0].w, mv[1].x, mv[1].y, mv[1].z, mv[1].w};
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          uint32_t keep = in ? 0xffffffffu : 0u;
-          if (kMask) {
-            // element 2i is byte (2i) of the mask, element 2i+1 byte (2i+1)
-            const uint32_t m4 = mb[i >> 1] >> (16 * (i & 1));
-            keep &= ((m4 & 0xffu) ? 0x0000ffffu : 0u) | ((m4 & 0xff00u) ? 0xffff0000u : 0u);
-          }
-          w[i] &= keep;
-        }
-        // rows are 8-byte aligned (pitch ZP): memcpy lets the compiler pick
-        // the widest aligned LDS stores
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint4 v4 = make_uint4(w[4 * e], w[4 * e + 1], w[4 * e + 2], w[4 * e + 3]);
-          __builtin_memcpy(&s_z[zr][zc + 8 * e], &v4, 16);
-        }
-      };
+      }
       f32x4_t acc[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      // dY.B^T partials (dB pass): B operand = rank row j0 + lane % 16 of the
-      // segment's adapter, 8 columns at 32 ks + 8 (lane / 16) of this tile
-      uint4 gb[8];
-      const bool with_g = a.gpart != nullptr;
-      if (with_g) {
-        const int jr = lane & 15;
-        const uint16_t *Bp = static_cast<const uint16_t *>(a.b_pages);
-        const uint16_t *brow =
-            Bp + int64_t(a.page_ids[a.page_start[ad] + j0 + min(jr, nr - 1)]) * a.d + c0 + 8 * (lane >> 4);
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          gb[ks] = *reinterpret_cast<const uint4 *>(brow + 32 * ks);
-          if (jr >= nr) gb[ks] = make_uint4(0u, 0u, 0u, 0u);
-        }
-      }
-      fetch(l_beg);
-      for (int k0 = l_beg; k0 < l_end; k0 += kOuterK) {
+      // one step of 32 pairs from buffer (zv, mv), which then takes the
+      // rows two steps ahead.  Steps start at multiples of 32 pairs of the
+      // chunk (aligned A operand reads); rows outside the segment are staged
+      // as exact zeros, so a step that is partly or wholly outside it adds
+      // exact zeros and stores no G partial there.  The fetch goes out after
+      // the step's G partial stores: those may or may not issue, so the
+      // compiler counts none of them, and a fetch issued before them would
+      // be waited for at the next step's staging.
+      auto step = [&](uint4 (&zv)[4], uint4 (&mv)[2], int k0) {
+        // nothing of this step is scheduled above the previous step's fetch
+        // (its staging would wait for this buffer's loads before that fetch
+        // goes out)
+        __builtin_amdgcn_sched_barrier(0);
         lds_bar();                             // the previous step is done with s_z
-        stage(k0);
+        stage(zv, mv, k0, l_beg, l_end);
         lds_bar();
-        if (k0 + kOuterK < l_end) fetch(k0 + kOuterK);
-        // A operand: rank row j = lane % 16, pairs k0 + 8 * (lane / 16) + e
+        // A operand: rank row j = lane % 16, pairs k0 + 8 * (lane / 16) .. + 7
+        // (pairs of other segments meet zeroed rows; past the chunk's end
+        // the coefficients are zero)
+        // (a step wholly past the chunk's end reads the last step's)
         const int kk = (lane >> 4) * 8;
-        uint32_t hw[4], lw[4];
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const int la = k0 + kk + e, lb = la + 1;
-          const float ua = la < l_end ? s_cf[la][lane & 15] : 0.f;
-          const float ub = lb < l_end ? s_cf[lb][lane & 15] : 0.f;
-          const uint16_t ha = f2bf(ua), hb = f2bf(ub);
-          const uint16_t xa = f2bf(ua - bf2f(ha)), xb = f2bf(ub - bf2f(hb));
-          hw[e >> 1] = uint32_t(ha) | (uint32_t(hb) << 16);
-          lw[e >> 1] = uint32_t(xa) | (uint32_t(xb) << 16);
-        }
+        const int ka = min(k0, kGradPairChunk - kOuterK) + kk;
         bf16x8_t ahi, alo;
-        const uint4 ph = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        const uint4 pl = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-        __builtin_memcpy(&ahi, &ph, 16);
-        __builtin_memcpy(&alo, &pl, 16);
+        __builtin_memcpy(&ahi, &s_ah[lane & 15][ka], 16);
+        __builtin_memcpy(&alo, &s_al[lane & 15][ka], 16);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          // B operand: column wave*64 + 16b + lane % 16, the same 8 pairs
-          const int col = wave * 64 + 16 * b + (lane & 15);
-          uint32_t bw[4];
-#pragma unroll
-          for (int e = 0; e < 8; e += 2)
-            bw[e >> 1] = uint32_t(s_z[kk + e][col]) | (uint32_t(s_z[kk + e + 1][col]) << 16);
+          // B operand: column wave*64 + 16b + lane % 16, the same 8 pairs,
+          // by two transposing reads: in each group of 16 lanes, lane L
+          // gives the address of row (L / 4) of a 4-row block, columns
+          // 4 (L % 4) .. + 3, and receives column L of the 4 rows
+          const int cb = wave * 64 + 16 * b + 4 * (lane & 3);
+          const int rb = kk + ((lane & 15) >> 2);
+          const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16_t *)(&s_z[rb][cb]));
+          const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16_t *)(&s_z[rb + 4][cb]));
           bf16x8_t bfrag;
-          const uint4 pb = make_uint4(bw[0], bw[1], bw[2], bw[3]);
-          __builtin_memcpy(&bfrag, &pb, 16);
+          __builtin_memcpy(&bfrag, &lo, 8);
+          __builtin_memcpy(reinterpret_cast<char *>(&bfrag) + 8, &hi, 8);
           acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bfrag, acc[b], 0, 0, 0);
           acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bfrag, acc[b], 0, 0, 0);
         }
-        if (with_g && wave < 2) {
-          // waves 0 and 1: pairs k0 + 16 * wave .. + 15 of the step (rows of
-          // s_z) times the B rows, over the tile's 256 columns in 8 K steps
-          f32x4_t ga = {0.f, 0.f, 0.f, 0.f};
-          const int zrow = 16 * wave + (lane & 15);
+        if constexpr (kG) {
+          if (wave < 2) {
+            // waves 0 and 1: pairs k0 + 16 * wave .. + 15 of the step (rows
+            // of s_z) times the B rows, over the tile's 256 columns in 8 K steps
+            f32x4_t ga = {0.f, 0.f, 0.f, 0.f};
+            const int zrow = 16 * wave + (lane & 15);
 #pragma unroll
-          for (int ks = 0; ks < 8; ++ks) {
-            bf16x8_t fa, fb;
-            __builtin_memcpy(&fa, &s_z[zrow][32 * ks + 8 * (lane >> 4)], 16);
-            __builtin_memcpy(&fb, &gb[ks], 16);
-            ga = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, ga, 0, 0, 0);
-          }
-          // lane holds rank column (lane % 16) and pair rows 4 * (lane / 16) + i
-          const int jj = lane & 15;
-          if (jj < nr) {
+            for (int ks = 0; ks < 8; ++ks) {
+              bf16x8_t fa, fb;
+              __builtin_memcpy(&fa, &s_z[zrow][32 * ks + 8 * (lane >> 4)], 16);
+              __builtin_memcpy(&fb, &s_gb[jr][32 * ks + 8 * (lane >> 4)], 16);
+              ga = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, ga, 0, 0, 0);
+            }
+            // lane holds rank column (lane % 16) and pair rows 4 * (lane / 16) + i
+            if (jr < nr) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int l = k0 + 16 * wave + (lane >> 4) * 4 + i;
-              if (l < l_end)
-                a.gpart[(int64_t(blockIdx.x) * a.T * a.K + pbeg + l) * a.max_rank + j0 + jj] = ga[i];
+              for (int i = 0; i < 4; ++i) {
+                const int l = k0 + 16 * wave + (lane >> 4) * 4 + i;
+                if (l >= l_beg && l < l_end)
+                  a.gpart[(int64_t(blockIdx.x) * TK + pbeg + l) * a.max_rank + j0 + jr] = ga[i];
+              }
             }
           }
         }
+        fetch(zv, mv, k0 + 2 * kOuterK, l_beg, l_end);
+      };
+      for (int k0 = l_beg & ~(kOuterK - 1); k0 < l_end; k0 += 2 * kOuterK) {
+        step(zA, mA, k0);
+        step(zB, mB, k0 + kOuterK);
       }
       // lane holds column (lane % 16) of each block and rank rows 4 * (lane / 16) + i
       float *dst = a.part + (int64_t(s + q) * a.max_rank + j0) * a.d + c0 + wave * 64 + (lane & 15);
@@ -376,7 +515,7 @@ __global__ __launch_bounds__(256) void seg_outer_mfma_kernel(SegOuterArgs a) {
           if (jj < nr) dst[int64_t(jj) * a.d + 16 * b] = acc[b][i];
         }
     }
-    p = send;
+    l_beg = l_end;
   }
 }
 
@@ -470,8 +609,9 @@ hipError_t launch_seg_outer(const SegOuterArgs &a, int dtype, int64_t TK, int64_
   if (grad_mfma_form(dtype, TK, a.d)) {
     // prefill-size batches: the MFMA form (long segments make it dense)
     const dim3 gm(unsigned(a.d / kOuterCols), chunks, rchunks);
-    if (a.mask) hipLaunchKernelGGL((seg_outer_mfma_kernel<true>), gm, block, 0, st, a);
-    else hipLaunchKernelGGL((seg_outer_mfma_kernel<false>), gm, block, 0, st, a);
+    if (a.mask) hipLaunchKernelGGL((seg_outer_mfma_kernel<true, false>), gm, block, 0, st, a);
+    else if (a.gpart) hipLaunchKernelGGL((seg_outer_mfma_kernel<false, true>), gm, block, 0, st, a);
+    else hipLaunchKernelGGL((seg_outer_mfma_kernel<false, false>), gm, block, 0, st, a);
   } else if (dtype == LORA_BF16) {
     if (a.mask) hipLaunchKernelGGL((seg_outer_partial_kernel<uint16_t, true>), g1, block, 0, st, a);
     else hipLaunchKernelGGL((seg_outer_partial_kernel<uint16_t, false>), g1, block, 0, st, a);

@@ -692,6 +692,24 @@ def test_grads_mfma_mixed_ranks_top2():
     _check_grads(w, run(w))
 
 
+@pytest.mark.parametrize("d_in,N,seed", [(512, 600, 31), (320, 300, 32), (768, 40, 33)])
+def test_grads_mfma_many_segments(d_in, N, seed):
+    """The MFMA outer products with hundreds of segments (more than 256, so
+    the workgroup's segment search takes two rounds), several segments per
+    256-pair chunk, ranks from 1 to 40 (segments that skip a 16-row block),
+    empty slots and a keep mask; d_in = 320 sends dA to the vector form."""
+    rng = np.random.default_rng(seed)
+    T, K = 2048, 1
+    rank = rng.integers(1, 41, size=N).astype(np.int32)
+    ids = rng.integers(-1, N, size=(T, K)).astype(np.int32)
+    gates = rng.standard_normal((T, K)).astype(np.float32)
+    w = wl.build(f"grad-mfma-segs-{seed}", seed, "bf16", T, K, d_in, 512, rank, ids, gates,
+                 x_var=1.0, w_var=0.02, a_var=1 / 64, b_var=0.02, keep_p=0.9, with_dY=True,
+                 scale=rng.uniform(0.5, 2, N).astype(np.float32))
+    print(f"case {w.name}: segments {len(np.unique(ids[ids >= 0]))}", flush=True)
+    _check_grads(w, run(w))
+
+
 def test_grads_full_prefill():
     w = full(4)
     _check_grads(w, run(w))
