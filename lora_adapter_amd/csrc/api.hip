@@ -514,14 +514,13 @@ int32_t lora_grad(const void *X, const uint8_t *keep_mask, float keep_scale, con
     ob.rank = pool->rank; ob.page_start = pool->page_start; ob.page_ids = pool->page_ids;
     ob.part = partB; ob.max_rank = max_rank; ob.out_pages = dB_pages; ob.err_word = err_word;
     ob.gpart = gpart; ob.b_pages = pool->b_pages;
-    hipError_t e = launch_seg_outer(ob, pool->dtype, TK, pool->n_adapters, s);
-    if (e != hipSuccess) return LORA_ERR_DEVICE;
     GReduceArgs gr{};
     gr.gpart = gpart; gr.n_tiles = grad_gpart_tiles(pool->d_out); gr.TK = TK;
     gr.max_rank = max_rank; gr.plan = pv; gr.rank = pool->rank; gr.scale = pool->scale;
     gr.extra_scale = keep_mask ? keep_scale : 1.0f;
     gr.G = G; gr.g_cap = int64_t(TK) * max_rank;
-    e = launch_g_reduce(gr, s);
+    // dB with the per-tile partials; its reduction launch also forms G
+    hipError_t e = launch_seg_outer(ob, pool->dtype, TK, pool->n_adapters, s, &gr);
     if (e != hipSuccess) return LORA_ERR_DEVICE;
     SegOuterArgs oa = ob;
     oa.Z = X; oa.mask = keep_mask; oa.d = pool->d_in; oa.coef = G; oa.coef_cap = gr.g_cap;

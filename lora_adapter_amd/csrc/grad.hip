@@ -521,14 +521,14 @@ void seg_outer_mfma_kernel(SegOuterArgs a) {
 
 // Adds each segment's partials in chunk order (up to 8 loads in flight) and
 // writes the fp32 gradient page of every rank row: one workgroup per (1024
-// columns, segment, rank row).
-__global__ __launch_bounds__(kGradThreads) void seg_outer_reduce_kernel(SegOuterArgs a) {
+// columns, segment, rank row); workgroup (bx, by, bz) of a (., gy, .) grid.
+__device__ __forceinline__ void seg_outer_reduce_wg(const SegOuterArgs &a, int bx, int by, int bz, int gy) {
   const int S = a.plan.hdr[LORA_PH_SEGS];
-  const int col = (blockIdx.x * kGradThreads + threadIdx.x) * kGradCPL;
+  const int col = (bx * kGradThreads + threadIdx.x) * kGradCPL;
   if (col >= a.d) return;
   if (int64_t(a.plan.hdr[LORA_PH_RPAIRS]) > a.coef_cap) return;
-  const int j = blockIdx.z;
-  for (int s = blockIdx.y; s < S; s += gridDim.y) {
+  const int j = bz;
+  for (int s = by; s < S; s += gy) {
     const int ad = a.plan.seg_adapter[s];
     const int r = a.rank[ad];
     if (r > a.max_rank || j >= r) continue;
@@ -552,10 +552,14 @@ __global__ __launch_bounds__(kGradThreads) void seg_outer_reduce_kernel(SegOuter
   }
 }
 
+__global__ __launch_bounds__(kGradThreads) void seg_outer_reduce_kernel(SegOuterArgs a) {
+  seg_outer_reduce_wg(a, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.y);
+}
+
 // G[u_off[p] + j] = (gate . scale . extra) . sum over tiles of gpart, one
-// thread per (pair, rank row), tiles added in order.
-__global__ __launch_bounds__(256) void g_reduce_kernel(GReduceArgs a) {
-  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+// thread per (pair, rank row), tiles added in order; workgroup b.
+__device__ __forceinline__ void g_reduce_wg(const GReduceArgs &a, int64_t b) {
+  const int64_t idx = b * 256 + threadIdx.x;
   const int P = a.plan.hdr[LORA_PH_PAIRS];
   const int64_t p = idx / a.max_rank;
   const int j = int(idx % a.max_rank);
@@ -580,6 +584,20 @@ __global__ __launch_bounds__(256) void g_reduce_kernel(GReduceArgs a) {
   a.G[a.plan.u_off[p] + j] = a.plan.pair_gate[p] * sc * sum;
 }
 
+// The dB pass's two reductions in one launch (they read different partials
+// and write different outputs): workgroups 0 .. n_seg - 1 add the dB chunk
+// partials ((cols, gy, rank rows) flattened, cols fastest), the rest form G.
+static_assert(kGradThreads == 256, "both reductions run 256-thread workgroups");
+__global__ __launch_bounds__(256) void seg_g_reduce_kernel(SegOuterArgs a, GReduceArgs g, int cols,
+                                                           int gy, int64_t n_seg) {
+  const int64_t b = blockIdx.x;
+  if (b < n_seg) {
+    seg_outer_reduce_wg(a, int(b % cols), int((b / cols) % gy), int(b / (int64_t(cols) * gy)), gy);
+  } else {
+    g_reduce_wg(g, b - n_seg);
+  }
+}
+
 }  // namespace
 
 bool grad_mfma_form(int dtype, int64_t TK, int d_out) {
@@ -588,19 +606,13 @@ bool grad_mfma_form(int dtype, int64_t TK, int d_out) {
 
 int grad_gpart_tiles(int d_out) { return d_out / kOuterCols; }
 
-hipError_t launch_g_reduce(const GReduceArgs &a, hipStream_t st) {
-  const int64_t n = a.TK * a.max_rank;
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(g_reduce_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-
 int64_t grad_pieces(int64_t TK, int64_t N) {
   const int64_t segs = TK < N ? TK : N;
   return segs + (TK + kGradPairChunk - 1) / kGradPairChunk + 1;
 }
 
-hipError_t launch_seg_outer(const SegOuterArgs &a, int dtype, int64_t TK, int64_t N, hipStream_t st) {
+hipError_t launch_seg_outer(const SegOuterArgs &a, int dtype, int64_t TK, int64_t N, hipStream_t st,
+                            const GReduceArgs *g) {
   if (TK == 0) return hipSuccess;
   const unsigned cols = unsigned((a.d + kGradCols - 1) / kGradCols);
   const unsigned chunks = unsigned((TK + kGradPairChunk - 1) / kGradPairChunk);
@@ -622,7 +634,15 @@ hipError_t launch_seg_outer(const SegOuterArgs &a, int dtype, int64_t TK, int64_
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t segs = TK < N ? TK : N;
-  const dim3 g2(cols, unsigned(segs < 65535 ? segs : 65535), unsigned(a.max_rank));
+  const unsigned gy = unsigned(segs < 65535 ? segs : 65535);
+  if (g != nullptr) {
+    const int64_t n_seg = int64_t(cols) * gy * a.max_rank;
+    const int64_t n_g = (g->TK * g->max_rank + 255) / 256;
+    hipLaunchKernelGGL(seg_g_reduce_kernel, dim3(unsigned(n_seg + n_g)), block, 0, st, a, *g,
+                       int(cols), int(gy), n_seg);
+    return hipGetLastError();
+  }
+  const dim3 g2(cols, gy, unsigned(a.max_rank));
   hipLaunchKernelGGL(seg_outer_reduce_kernel, g2, block, 0, st, a);
   return hipGetLastError();
 }

@@ -443,8 +443,9 @@ int64_t grad_pieces(int64_t TK, int64_t n_adapters);
 // The MFMA outer-product form (and the fused dY.B^T partials) applies.
 bool grad_mfma_form(int dtype, int64_t TK, int d_out);
 int grad_gpart_tiles(int d_out);
-hipError_t launch_g_reduce(const GReduceArgs &a, hipStream_t s);
+// The outer products, then the chunk partials' reduction; with g, the
+// reduction launch also forms G from gpart.
 hipError_t launch_seg_outer(const SegOuterArgs &a, int dtype, int64_t TK, int64_t n_adapters,
-                            hipStream_t s);
+                            hipStream_t s, const GReduceArgs *g = nullptr);
 
 }  // namespace lora
