@@ -15,7 +15,7 @@ constexpr int kPlanLdsInts = 24576;               // LDS the plan kernel may use
 constexpr int kGradPairChunk = 256;               // pairs per partial in the gradient reduction
 constexpr int kGradRankChunk = 16;                // rank rows per gradient register block
 constexpr int kBigSegPairs = 64;                  // segments this large may use the MFMA shrink
-constexpr int kTileTok = 16;                      // pairs per MFMA shrink tile
+constexpr int kTileTok = 32;                      // pairs per MFMA shrink tile (two 16-row blocks)
 constexpr int kShrinkRows = 2;                    // rank rows per decode-shrink unit
 constexpr int kShrinkWaves = 2048;                // waves of the decode shrink (its units split evenly)
 

@@ -396,7 +396,7 @@ __device__ __forceinline__ void plan_build(const PlanArgs &a, int *dyn) {
       const bool big = a.use_tile && c >= kBigSegPairs;
       x.v[0] += c; x.v[1] += c * r; x.v[2] += r;
       // decode-shrink units: every pair of a small segment, the last c % 16
-      // pairs of a big one (its whole 16-pair tiles go to the MFMA shrink)
+      // pairs of a big one (its whole 32-pair tiles go to the MFMA shrink)
       x.v[3] += (big ? c % kTileTok : c) * ((r + kShrinkRows - 1) / kShrinkRows);
       x.v[4] += big ? 1 : 0;
     }

@@ -15,15 +15,16 @@
 //     persistent grid of kShrinkWaves waves over the plan's unit schedule
 //     (see shrink_units_kernel); A pages stream from HBM with 16-byte
 //     coalesced loads, token rows come from L2.
-//   * tile kernel (the whole 16-pair tiles of segments of kBigSegPairs
+//   * tile kernel (the whole 32-pair tiles of segments of kBigSegPairs
 //     pairs or more, bf16, large batches, i.e. prefill; the units kernel
-//     takes each such segment's last len % 16 pairs, so there are at most
-//     T*K / 16 tiles and a batch of 8192 pairs fills exactly 512
-//     workgroups): an MFMA tile of 16 tokens x 16 rank rows
-//     (v_mfma_f32_16x16x32_bf16), token rows and A pages read straight from
-//     global memory as MFMA fragments, the dropout mask applied to the bf16
-//     fragment (exact), the four waves of a workgroup splitting d and adding
-//     through LDS.  X is read once from HBM per rank-row block.
+//     takes each such segment's last len % 32 pairs, so there are at most
+//     T*K / 32 tiles and a batch of 8192 pairs fills exactly 256
+//     workgroups): two MFMA blocks of 16 tokens x 16 rank rows
+//     (v_mfma_f32_16x16x32_bf16) sharing each A page fragment, token rows
+//     and A pages read straight from global memory as MFMA fragments, the
+//     dropout mask applied to the bf16 fragment (exact), the four waves of a
+//     workgroup splitting d and adding through LDS.  X is read once from HBM
+//     per rank-row block; the A pages, from L2, once per 32 pairs.
 // When the tile kernel is on and d <= 6144, both run in one launch
 // (shrink_both_kernel): its tiles first, then the units schedule.
 // The same kernels compute the gradient's dY.B^T (Z = dY, pages = B) where
@@ -35,7 +36,7 @@ namespace lora {
 namespace {
 
 constexpr int kTileRank = 16;       // rank rows per MFMA tile
-constexpr int kTileAhead = 8;       // K steps per batch of loads
+constexpr int kTileAhead = 4;       // K steps per batch of loads
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -52,7 +53,7 @@ __global__ __launch_bounds__(64) void shrink_units_kernel(ShrinkArgs s) {
   shrink_units_wave<E, kMask, kCh, kResident>(s, blockIdx.x);
 }
 
-// Finds the big segment and the 16-pair tile of workgroup b, the tiles of the
+// Finds the big segment and the 32-pair tile of workgroup b, the tiles of the
 // big list numbered in list order (a wave-wide scan over 64 entries at a
 // time).  Returns false past the last tile.
 __device__ __forceinline__ bool tile_of(const PlanView &pv, int b, int lane, int &seg, int &q0, int &pe) {
@@ -87,7 +88,7 @@ __device__ __forceinline__ bool tile_of(const PlanView &pv, int b, int lane, int
   return false;
 }
 
-// One workgroup per 16-pair tile of the big segments, numbered across the
+// One workgroup per 32-pair tile of the big segments, numbered across the
 // list so that consecutive workgroups (which the dispatcher spreads over the
 // XCDs) cover every segment evenly.
 template <bool kMask>
@@ -100,20 +101,37 @@ __device__ __forceinline__ void shrink_tile_wg(const ShrinkArgs &s, const int b)
   const int ad = d0.x, r = d0.y, ps = d0.z;
   const int nq = min(kTileTok, pe - q0);
 
-  __shared__ f32x4_t red[4][64];
+  // two 16-pair MFMA row blocks per tile share every A page fragment
+  __shared__ f32x4_t red[4][2][64];
   const int d = s.d;
   const int kw = d / 4;                          // this wave's part of d (multiple of 16)
-  const int kbeg = wave * kw, kend = kbeg + kw;
+  const int kbeg = wave * kw;
   const uint16_t *Z = static_cast<const uint16_t *>(s.Z);
   const uint16_t *pages = static_cast<const uint16_t *>(s.pages);
-  // A operand: token row (lane % 16) of the tile, 8 values at k + (lane / 16) * 8
+  // A operand of block h: token row (lane % 16) of its 16 pairs, 8 values
+  // at k + (lane / 16) * 8
   const int trow = lane & 15, kofs = (lane >> 4) * 8;
-  const int pq = q0 + min(trow, nq - 1);
-  const int64_t t = s.plan.pair_tk[pq] / s.K;
-  const uint16_t *zrow = Z + t * d;
-  const uint8_t *mrow = kMask ? s.mask + t * d : nullptr;
+  const int64_t t0 = s.plan.pair_tk[q0 + min(trow, nq - 1)] / s.K;
+  const int64_t t1 = s.plan.pair_tk[q0 + min(16 + trow, nq - 1)] / s.K;
+  const uint16_t *zrow0 = Z + t0 * d, *zrow1 = Z + t1 * d;
+  const uint8_t *mrow0 = kMask ? s.mask + t0 * d : nullptr;
+  const uint8_t *mrow1 = kMask ? s.mask + t1 * d : nullptr;
   const float sc = s.scale[ad] * s.extra_scale;
 
+  // the keep mask (bytes 0 or 1) on a bf16 fragment: the bytes of elements
+  // 2i and 2i + 1 go to bits 0 and 16 (one byte permute), times 0xffff
+  auto masked = [&](uint4 z, uint2 m) {
+    if constexpr (kMask) {
+      uint32_t w[4] = {z.x, z.y, z.z, z.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t x = __builtin_amdgcn_perm(0u, i < 2 ? m.x : m.y, (i & 1) ? 0x0c030c02u : 0x0c010c00u);
+        w[i] &= (x << 16) - x;
+      }
+      z = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    return z;
+  };
   // K steps of 32 in batches of kTileAhead, the next batch's loads in flight
   // while the current batch's MFMAs run (kw is a multiple of 32)
   const int nsteps = kw / 32;
@@ -121,54 +139,56 @@ __device__ __forceinline__ void shrink_tile_wg(const ShrinkArgs &s, const int b)
     // B operand: rank row jb + (lane % 16), same k offsets
     const int jr = jb + (lane & 15);
     const uint16_t *arow = pages + int64_t(s.page_ids[ps + min(jr, r - 1)]) * d;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    uint4 za[kTileAhead], pa[kTileAhead], zb[kTileAhead], pb2[kTileAhead];
-    uint2 ma[kTileAhead], mb[kTileAhead];
-    auto load_batch = [&](uint4 (&z)[kTileAhead], uint4 (&p)[kTileAhead], uint2 (&m)[kTileAhead], int i0) {
+    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    uint4 za0[kTileAhead], za1[kTileAhead], pa[kTileAhead];
+    uint4 zb0[kTileAhead], zb1[kTileAhead], pb2[kTileAhead];
+    uint2 ma0[kTileAhead], ma1[kTileAhead], mb0[kTileAhead], mb1[kTileAhead];
+    auto load_batch = [&](uint4 (&z0)[kTileAhead], uint4 (&z1)[kTileAhead], uint4 (&p)[kTileAhead],
+                          uint2 (&m0)[kTileAhead], uint2 (&m1)[kTileAhead], int i0) {
 #pragma unroll
       for (int u = 0; u < kTileAhead; ++u) {
         const int k = kbeg + min(i0 + u, nsteps - 1) * 32 + kofs;
-        z[u] = *reinterpret_cast<const uint4 *>(zrow + k);
+        z0[u] = *reinterpret_cast<const uint4 *>(zrow0 + k);
+        z1[u] = *reinterpret_cast<const uint4 *>(zrow1 + k);
         p[u] = *reinterpret_cast<const uint4 *>(arow + k);
-        if (kMask) m[u] = *reinterpret_cast<const uint2 *>(mrow + k);
+        if (kMask) {
+          m0[u] = *reinterpret_cast<const uint2 *>(mrow0 + k);
+          m1[u] = *reinterpret_cast<const uint2 *>(mrow1 + k);
+        }
       }
     };
-    auto mfma_batch = [&](const uint4 (&z)[kTileAhead], const uint4 (&p)[kTileAhead],
-                          const uint2 (&m)[kTileAhead], int i0) {
+    auto mfma_batch = [&](const uint4 (&z0)[kTileAhead], const uint4 (&z1)[kTileAhead],
+                          const uint4 (&p)[kTileAhead], const uint2 (&m0)[kTileAhead],
+                          const uint2 (&m1)[kTileAhead], int i0) {
 #pragma unroll
       for (int u = 0; u < kTileAhead; ++u) {
         if (i0 + u >= nsteps) break;
-        uint4 xa = z[u];
-        if (kMask) {
-          uint32_t w[4] = {xa.x, xa.y, xa.z, xa.w};
-          const uint32_t mw[2] = {m[u].x, m[u].y};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            if (((mw[e >> 2] >> (8 * (e & 3))) & 0xffu) == 0) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-          }
-          xa = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-        bf16x8_t fa, fb;
-        __builtin_memcpy(&fa, &xa, 16);
+        const uint4 x0 = masked(z0[u], m0[u]), x1 = masked(z1[u], m1[u]);
+        bf16x8_t fa0, fa1, fb;
+        __builtin_memcpy(&fa0, &x0, 16);
+        __builtin_memcpy(&fa1, &x1, 16);
         __builtin_memcpy(&fb, &p[u], 16);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa0, fb, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa1, fb, acc1, 0, 0, 0);
       }
     };
-    load_batch(za, pa, ma, 0);
+    load_batch(za0, za1, pa, ma0, ma1, 0);
     for (int i0 = 0; i0 < nsteps; i0 += 2 * kTileAhead) {
-      load_batch(zb, pb2, mb, i0 + kTileAhead);
-      mfma_batch(za, pa, ma, i0);
+      load_batch(zb0, zb1, pb2, mb0, mb1, i0 + kTileAhead);
+      mfma_batch(za0, za1, pa, ma0, ma1, i0);
       if (i0 + kTileAhead >= nsteps) break;
-      load_batch(za, pa, ma, i0 + 2 * kTileAhead);
-      mfma_batch(zb, pb2, mb, i0 + kTileAhead);
+      load_batch(za0, za1, pa, ma0, ma1, i0 + 2 * kTileAhead);
+      mfma_batch(zb0, zb1, pb2, mb0, mb1, i0 + kTileAhead);
     }
-    red[wave][lane] = acc;
+    red[wave][0][lane] = acc0;
+    red[wave][1][lane] = acc1;
     __syncthreads();
-    if (wave == 0) {
-      f32x4_t v = red[0][lane];
+    if (wave < 2) {
+      // wave h adds block h over the four K quarters
+      f32x4_t v = red[0][wave][lane];
 #pragma unroll
       for (int w = 1; w < 4; ++w) {
-        const f32x4_t o = red[w][lane];
+        const f32x4_t o = red[w][wave][lane];
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] += o[i];
       }
@@ -177,7 +197,7 @@ __device__ __forceinline__ void shrink_tile_wg(const ShrinkArgs &s, const int b)
       if (j < r) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int tr = (lane >> 4) * 4 + i;
+          const int tr = 16 * wave + (lane >> 4) * 4 + i;
           if (tr < nq) {
             const int p = q0 + tr;
             s.out[s.plan.u_off[p] + j] = s.plan.pair_gate[p] * sc * v[i];
@@ -207,8 +227,8 @@ __global__ __launch_bounds__(256) void shrink_both_kernel(ShrinkArgs s, int n_ti
   shrink_units_wave<uint16_t, kMask, kCh, true>(s, (b - n_tile) * 4 + int(threadIdx.x >> 6));
 }
 
-// Workgroups of the tile shrink: the whole 16-pair tiles of the big
-// segments, at most T*K / 16 (at least one workgroup).
+// Workgroups of the tile shrink: the whole 32-pair tiles of the big
+// segments, at most T*K / 32 (at least one workgroup).
 int shrink_tile_wgs(int64_t TK, int64_t n_adapters) {
   (void)n_adapters;
   return int(TK / kTileTok > 0 ? TK / kTileTok : 1);

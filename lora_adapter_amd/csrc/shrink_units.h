@@ -156,8 +156,8 @@ __device__ __forceinline__ void shrink_units_wave(const ShrinkArgs &s, const int
   while (left > 0) {
     const int n = pe - pb;
     const int G = (r + RW - 1) / RW;
-    // the MFMA shrink takes the whole 16-pair tiles of a big segment: the
-    // units cover its last n % 16 pairs only (every pair of a small one)
+    // the MFMA shrink takes the whole 32-pair tiles of a big segment: the
+    // units cover its last n % 32 pairs only (every pair of a small one)
     const int n_tiled = s.big_segments && n >= kBigSegPairs ? n / kTileTok * kTileTok : 0;
     const int nu = n - n_tiled;
     const int here = min(left, nu * G - loc);
