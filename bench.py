@@ -687,7 +687,7 @@ KERNELS = ("decode_gemm_slot_kernel", "gemm_tile_plan_kernel", "decode_gemm_shri
            "gemm_decode_kernel", "gemm_tile_kernel", "gemm_f32_kernel", "shrink_both_kernel",
            "shrink_units_kernel", "shrink_tile_kernel", "epilogue_kernel", "plan_kernel",
            "merge_mfma_kernel", "seg_outer_mfma_kernel", "seg_outer_reduce_kernel",
-           "g_reduce_kernel", "transpose_kernel")
+           "seg_g_reduce_kernel", "transpose_kernel", "merge_layers_mfma_kernel")
 
 
 def pmc_summary(workload_id, fetch_csv, write_csv):
