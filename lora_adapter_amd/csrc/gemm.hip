@@ -123,8 +123,12 @@ __device__ __forceinline__ void expand_row8(float (&v)[8], int4 sd, int col, con
   const E *B = static_cast<const E *>(e.b_pages);
   const int lane = lane_id();
   for (int k = 0; k < e.K; ++k) {
-    if (__shfl(sd.x, k, 64) < 0) continue;
-    const int r = __shfl(sd.y, k, 64), uo = __shfl(sd.z, k, 64), ps = __shfl(sd.w, k, 64);
+    // the slot's descriptor, the same in every lane: scalar registers, so
+    // that the loops below branch uniformly
+    if (__builtin_amdgcn_readfirstlane(__shfl(sd.x, k, 64)) < 0) continue;
+    const int r = __builtin_amdgcn_readfirstlane(__shfl(sd.y, k, 64));
+    const int uo = __builtin_amdgcn_readfirstlane(__shfl(sd.z, k, 64));
+    const int ps = __builtin_amdgcn_readfirstlane(__shfl(sd.w, k, 64));
     for (int jb = 0; jb < r; jb += 64) {
       const int nrb = min(64, r - jb);
       const int jl = jb + min(lane, nrb - 1);
@@ -148,12 +152,15 @@ __device__ __forceinline__ void expand_row8(float (&v)[8], int4 sd, int col, con
           }
         }
       };
+      // both batches' loads are issued unconditionally (rows past nrb
+      // re-read row nrb - 1, a cache hit, and are not added): a load under
+      // a condition leaves the compiler unable to count what is in flight,
+      // and it then waits for every load, the batch just issued included
       loadb(ba, 0);
       for (int q0 = 0; q0 < nrb; q0 += 2 * NB) {
-        if (q0 + NB < nrb) loadb(bb, q0 + NB);
+        loadb(bb, q0 + NB);
         addb(ba, q0);
-        if (q0 + NB >= nrb) break;
-        if (q0 + 2 * NB < nrb) loadb(ba, q0 + 2 * NB);
+        loadb(ba, q0 + 2 * NB);
         addb(bb, q0 + NB);
       }
     }
