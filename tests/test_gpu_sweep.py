@@ -1,6 +1,10 @@
 """Seeded property sweep over the layer's input space, with canary guards
 around every buffer the library writes.
 
+A second, smaller sweep draws prefill-size batches (T in [512, 4096]) so
+that the MFMA paths run: the 32-pair shrink tiles with the segments' tails
+on the units schedule, the tile GEMMs and the MFMA gradient form.
+
 Each case draws a batch at random: T in [0, 300], K in {1, 2}, d_in and d_out
 multiples of 64 up to 1024, 1..40 adapters of ranks 0..130 (odd ones
 included), empty slots (id -1), zero gates, an optional keep mask, fp32 or
@@ -144,6 +148,62 @@ def test_sweep_plan_apply_forward(seed):
         if used.any() and np.max(np.abs(rA[used])) > 0:
             assert rel_err(gA[used], rA[used]) <= TOL[w.dtype]
             assert rel_err(gB[used], rB[used]) <= TOL[w.dtype]
+
+
+def draw_large(seed: int) -> wl.Workload:
+    """A prefill-size bf16 batch: Zipf-weighted adapters so that some
+    segments are long (MFMA shrink tiles, with tails of any length) and many
+    are short; d_in a multiple of 128 and d_out of 256 (the MFMA shrink and
+    gradient forms), K of 1 or 2, empty slots, an optional keep mask."""
+    rng = np.random.default_rng(5000 + seed)
+    T = int(rng.integers(512, 4097))
+    K = int(rng.integers(1, 3))
+    d_in = 128 * int(rng.integers(1, 9))
+    d_out = 256 * int(rng.integers(1, 5))
+    N = int(rng.integers(1, 40))
+    rank = rng.integers(1, 65, size=N).astype(np.int32)
+    ids = wl.zipf_ids(rng, T * K, N, s=1.2).reshape(T, K)
+    ids[rng.random((T, K)) < 0.05] = -1
+    gates = rng.standard_normal((T, K)).astype(np.float32)
+    keep_p = 0.9 if seed % 2 == 0 else None
+    return wl.build(f"sweep-large-{seed}", 5000 + seed, "bf16", T, K, d_in, d_out, rank, ids, gates,
+                    x_var=1.0, w_var=1.0 / d_in, a_var=1.0 / d_in, b_var=0.02,
+                    scale=rng.uniform(0.25, 4.0, N).astype(np.float32), keep_p=keep_p,
+                    with_dY=True)
+
+
+@pytest.mark.parametrize("seed", list(range(10)))
+def test_sweep_large_batches(seed):
+    w = draw_large(seed)
+    print(f"case {w.name}: T={w.T} K={w.K} d={w.d_in}x{w.d_out} N={w.n_adapters} "
+          f"mask={w.keep_mask is not None}", flush=True)
+    L = GuardedLayer(w)
+    L.run_plan()
+    L.run_apply()
+    torch.cuda.synchronize()
+    assert all(L.intact().values()), L.intact()
+    check_plan_apply(w, L)
+    F = GuardedLayer(w)
+    B.lora_forward(F.ids, F.gates, F.T, F.K, F.X, F.W_t, F.Y, F.keep_mask, F.keep_scale, F.pool,
+                   F.plan, F.ws)
+    torch.cuda.synchronize()
+    assert all(F.intact().values()), F.intact()
+    assert np.array_equal(D.to_host(F.Y), D.to_host(L.Y))      # same kernels, same bits
+    dA = Guarded((w.n_pages, w.d_in), torch.float32, fill=float("nan"))
+    dB = Guarded((w.n_pages, w.d_out), torch.float32, fill=float("nan"))
+    n = B.lora_grad_workspace_bytes(w.T, w.K, w.n_adapters, w.d_in, w.d_out, L.max_rank, L.dtype)
+    gws = Guarded((n,), torch.uint8)
+    L.run_grad(dA.t, dB.t, gws.t)
+    torch.cuda.synchronize()
+    assert dA.intact() and dB.intact() and gws.intact()
+    g = O.grad_workload(w)
+    rA, rB = O.grad_pages(g, w.rank, w.page_start, w.page_ids, w.n_pages, w.d_in, w.d_out)
+    gA = dA.t.cpu().numpy().astype(np.float64)
+    gB = dB.t.cpu().numpy().astype(np.float64)
+    used = ~np.isnan(rA[:, 0])
+    assert np.all(np.isnan(gA[~used])) and np.all(np.isnan(gB[~used]))
+    assert rel_err(gA[used], rA[used]) <= TOL["bf16"]
+    assert rel_err(gB[used], rB[used]) <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("cfg", [1, 4, 5])
