@@ -5,14 +5,17 @@
 // derivatives of <dY, Y> for the forward computed by the apply:
 //   dB_a[j][n] = sum_{p of a} U[u_off[p]+j] . dY[t_p][n]
 //   dA_a[i][j] = sum_{p of a} (X . m)[t_p][i] . G[u_off[p]+j],
-//   G[u_off[p]+j] = kappa . g . s_a . (dY[t_p] . B_a[j])   (the shrink kernel on dY, B)
+//   G[u_off[p]+j] = kappa . g . s_a . (dY[t_p] . B_a[j])
 // Both are out_page(a, j)[c] = sum over the segment's pairs of coef[u_off[p]+j]
 // . Z[t_p][c].  Pairs are cut into fixed chunks of 256 (in plan order); each
 // (chunk, column slice, 16-rank-row block) workgroup accumulates in registers
 // and writes one partial per segment it meets, then a second kernel adds a
 // segment's partials in chunk order.  No atomics: results are deterministic.
-// The work per (pair, column, rank row) is one fma, so it stays on the vector
-// ALU; the kernels are organised for bandwidth (rows in flight, 16-byte loads).
+// Prefill-size bf16 batches run the outer products on MFMA with the pairs as
+// K (seg_outer_mfma_kernel), and the dB pass also forms the per-tile partials
+// of G from the same staged dY rows; other batches use the vector ALU
+// (seg_outer_partial_kernel) and the shrink kernel on (dY, B pages) for G.
+// Both forms are organised for bandwidth (rows in flight, 16-byte loads).
 #include "lora_internal.h"
 
 namespace lora {
