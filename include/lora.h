@@ -489,7 +489,8 @@ int32_t lora_compress(const lora_pool_desc *pool, const int32_t *adapters, int32
  *   scale is already in G); plan as for the forward; max_rank as given to
  *   lora_grad; dX [T][d_in] dtype, must not alias dY or W;
  *   ws >= lora_grad_x_workspace_bytes(T, d_in, d_out, dtype) (fp32 partial
- *   products of dY . W^T).
+ *   products of dY . W^T; a few bytes, unused, when the batch fills the GPU
+ *   with 256 x 256 output tiles, whose epilogue adds the masked LoRA term).
  * Rows whose slots are all inactive equal dY . W^T (rounded once) exactly.
  * Errors: INVALID_ARG, UNSUPPORTED, CAPACITY (grad_ws smaller than
  * lora_grad_workspace_bytes for these sizes, or ws too small), DEVICE. */

@@ -563,9 +563,10 @@ namespace {
 // dX GEMM: dY [T][d_out] times W [d_in][d_out] along d_out, into fp32 partials
 // (the epilogue adds the masked LoRA term before the one rounding).
 GemmConfig grad_x_config(int32_t T, int32_t d_in, int32_t d_out, int32_t dtype) {
-  GemmConfig c = choose_gemm(T > 0 ? T : 1, d_out, d_in, dtype);
-  c.fused = false;   // 256 x 256 tiles write their one partial slot
-  return c;
+  // the forward's choice: with 256 x 256 tiles the LoRA term and the keep
+  // mask go into the GEMM's own epilogue, otherwise split partials and the
+  // epilogue launch
+  return choose_gemm(T > 0 ? T : 1, d_out, d_in, dtype);
 }
 
 }  // namespace
@@ -621,6 +622,10 @@ int32_t lora_grad_x(const void *dY, const void *W, const uint8_t *keep_mask, int
   g.ex.U = static_cast<const float *>(grad_ws); g.ex.hdr = pv.hdr;
   g.ex.u_cap = TK * max_rank;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (c.fused) {
+    g.mask = keep_mask;
+    return dev(launch_base_gemm(c, g, s));
+  }
   hipError_t e = launch_base_gemm(c, g, s);
   if (e == hipSuccess) e = launch_grad_x_epilogue(c, g, pool->dtype, keep_mask, s);
   return dev(e);

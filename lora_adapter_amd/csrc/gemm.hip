@@ -12,9 +12,10 @@
 //
 // Two epilogue placements, chosen from the shape:
 //   * fused: when the tile grid alone fills the GPU (prefill), each tile
-//     stages its accumulators through LDS, walks its rows once per wave and
-//     adds the expand with the adapter's B slice cached in registers while
-//     consecutive rows share an adapter (long prefill segments);
+//     adds the expand to its accumulators (MFMA blocks for rank <= 16, one
+//     slot per token; row by row with the adapter's B slice cached in
+//     registers otherwise), stages them through LDS and stores; the input
+//     gradient uses the same epilogue with its keep mask on the LoRA term;
 //   * split-K: decode shapes have too few output tiles to stream W at full
 //     bandwidth, so K is split across workgroups that write fp32 partial
 //     products; the epilogue kernel then sums the partials in a fixed order,
@@ -475,7 +476,13 @@ __device__ __forceinline__ void tile_coords(int T, int tiles_m, int tiles_n, int
 // and U values are addressed by compile-time indices (a rolled loop that
 // rotated the blocks down into position 0 needed 11 dwords of scratch per
 // block for the rotation temporaries).
-template <int BM, int BN, int WM, int WN>
+// kMask (the input gradient, whose LoRA term is multiplied by the keep mask
+// g.mask [M][N]): the LoRA term is accumulated apart from the base product
+// and added times the mask bytes, one rounding, as the split-K epilogue does.
+// An MFMA block stages its base product first, accumulates the LoRA term in
+// the same registers, and moves it through a second, 8-row staging region a
+// quarter at a time; the row path keeps the term in registers of its own.
+template <int BM, int BN, int WM, int WN, bool kMask>
 __device__ __forceinline__ void fused_epilogue(const GemmArgs &g,
                                                f32x16_t (&acc)[TileCfg<BM, BN, WM, WN>::TM]
                                                               [TileCfg<BM, BN, WM, WN>::TN],
@@ -488,7 +495,7 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs &g,
   static_assert(CPL == 1 || CPL == 2, "fused epilogue handles 64 or 128 columns per wave");
   static_assert(WC % 8 == 0 && 64 % (WC / 8) == 0, "16-byte store layout");
   // waves 0..NW/2-1 stage in lds0, the others in lds1
-  static_assert((C::NW / 2) * 32 * SC * 4 <= C::STAGE, "staging must fit in LDS");
+  static_assert((C::NW / 2) * (kMask ? 40 : 32) * SC * 4 <= C::STAGE, "staging must fit in LDS");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int frow = lane & 31, half = lane >> 5;
@@ -524,6 +531,9 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs &g,
 
   float *stage = reinterpret_cast<float *>(wave < C::NW / 2 ? lds0 : lds1) +
                  (wave % (C::NW / 2)) * 32 * SC;
+  // kMask: 8 rows of the LoRA term, past every wave's staging region
+  float *lstage = reinterpret_cast<float *>(wave < C::NW / 2 ? lds0 : lds1) +
+                  (C::NW / 2) * 32 * SC + (wave % (C::NW / 2)) * 8 * SC;
   uint16_t *Y = static_cast<uint16_t *>(g.Y);
   const int cbase = n0 + wn * WC;
   // row-by-row path: lane owns CPL consecutive columns
@@ -532,6 +542,7 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs &g,
   const int col = col_ok ? col_raw : g.N - CPL;     // loads stay in bounds
   // 16-byte path: lane owns 8 columns of one of 64 / (WC / 8) rows per step
   constexpr int LPR = WC / 8, RPS = 64 / LPR;
+  static_assert(RPS <= 8, "the kMask quarter holds 8 rows");
   const int vr = lane / LPR, vc = (lane % LPR) * 8;
   const bool c8 = cbase + vc + 8 <= g.N;
   BCache<CPL, 16> cache;
@@ -541,10 +552,25 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs &g,
   bf16x8_t bfr[TN] = {};
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    bool lterm = false;                      // kMask: acc[i] holds the LoRA term
     if (mfma_ok && !((rowwise >> i) & 1u)) {
       // one MFMA pass per adapter present in the block (lanes 0-31 = rows)
       const int4 sd = sdv[i];
       unsigned long long pending = __ballot(sd.x >= 0) & 0xffffffffull;
+      if constexpr (kMask) {
+        lterm = pending != 0;
+        if (lterm) {
+          // the staging region is this wave's own (see below)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int r = (v >> 2) * 8 + half * 4 + (v & 3);
+              stage[r * SC + j * 32 + frow] = acc[i][j][v];
+              acc[i][j][v] = 0.f;
+            }
+        }
+      }
       while (pending) {
         const int leader = __ffsll(pending) - 1;
         const int kps = __shfl(sd.w, leader, 64), kr = __shfl(sd.y, leader, 64);
@@ -600,15 +626,50 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs &g,
     // the staging region is this wave's own, and the K loop ended with a
     // workgroup barrier: no barrier here (LDS accesses of one wave stay in
     // order)
+    if (!(kMask && lterm)) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = (v >> 2) * 8 + half * 4 + (v & 3);
-        stage[r * SC + j * 32 + frow] = acc[i][j][v];
-      }
+        for (int v = 0; v < 16; ++v) {
+          const int r = (v >> 2) * 8 + half * 4 + (v & 3);
+          stage[r * SC + j * 32 + frow] = acc[i][j][v];
+        }
+    }
     const int rbase = m0 + wm * TM * 32 + i * 32;
-    if (!((rowwise >> i) & 1u)) {
+    if (kMask && lterm) {
+      // quarter qr: MFMA registers v = 4qr .. 4qr+3 hold rows 8qr .. 8qr+7
+#pragma unroll
+      for (int qr = 0; qr < 4; ++qr) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int v = 4 * qr; v < 4 * qr + 4; ++v)
+            lstage[(half * 4 + (v & 3)) * SC + j * 32 + frow] = acc[i][j][v];
+#pragma unroll
+        for (int q = 0; q < 8 / RPS; ++q) {
+          const int lr = q * RPS + vr;
+          const int rr = qr * 8 + lr;
+          const int row = rbase + rr;
+          if (row < g.M && c8) {
+            const float *sb = stage + rr * SC + vc, *sl = lstage + lr * SC + vc;
+            const float4 b0 = *reinterpret_cast<const float4 *>(sb);
+            const float4 b1 = *reinterpret_cast<const float4 *>(sb + 4);
+            const float4 l0 = *reinterpret_cast<const float4 *>(sl);
+            const float4 l1 = *reinterpret_cast<const float4 *>(sl + 4);
+            const float b8[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+            const float l8[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+            const uint2 mw = *reinterpret_cast<const uint2 *>(g.mask + int64_t(row) * g.N + cbase + vc);
+            float v8[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+              const uint32_t word = c < 4 ? mw.x : mw.y;
+              v8[c] = b8[c] + float((word >> (8 * (c & 3))) & 0xffu) * l8[c];
+            }
+            store8_nt(Y + int64_t(row) * g.N + cbase + vc, v8);
+          }
+        }
+      }
+    } else if (!((rowwise >> i) & 1u)) {
 #pragma unroll
       for (int rr0 = 0; rr0 < 32; rr0 += RPS) {
         const int rr = rr0 + vr;
@@ -627,7 +688,17 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs &g,
         float v[CPL];
 #pragma unroll
         for (int c = 0; c < CPL; ++c) v[c] = stage[rr * SC + lane * CPL + c];
-        expand_row_cached<CPL, 16>(v, row, col, g.ex, cache);
+        if constexpr (kMask) {
+          float l[CPL];
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) l[c] = 0.f;
+          expand_row_cached<CPL, 16>(l, row, col, g.ex, cache);
+          const uint8_t *mr = g.mask + int64_t(row) * g.N + col;
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) v[c] += float(mr[c]) * l[c];
+        } else {
+          expand_row_cached<CPL, 16>(v, row, col, g.ex, cache);
+        }
         if (col_ok) Cols<uint16_t, CPL>::store(Y + int64_t(row) * g.N + col, v);
       }
     }
@@ -718,7 +789,7 @@ __device__ __forceinline__ void wait_tiles(int n) {
 
 // One output tile (m0, n0) over K tiles [k_begin / 64, + nk): the K loop
 // and the epilogue (fp32 partials into slot `slot`, or the fused expand).
-template <int BM, int BN, int WM, int WN, int NS, bool kFused>
+template <int BM, int BN, int WM, int WN, int NS, bool kFused, bool kMask = false>
 __device__ __forceinline__ void tile_run(const GemmArgs &g, char *smem, int m0, int n0,
                                          int k_begin, int nk, int slot) {
   using C = TileCfg<BM, BN, WM, WN>;
@@ -908,7 +979,7 @@ __device__ __forceinline__ void tile_run(const GemmArgs &g, char *smem, int m0, 
         }
       }
   } else {
-    fused_epilogue<BM, BN, WM, WN>(g, acc, st0, st1, m0, n0);
+    fused_epilogue<BM, BN, WM, WN, kMask>(g, acc, st0, st1, m0, n0);
   }
 }
 
@@ -936,7 +1007,7 @@ __device__ __forceinline__ void stream_k(const GemmArgs &g, char *smem, int w) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int NS, bool kFused>
+template <int BM, int BN, int WM, int WN, int NS, bool kFused, bool kMask = false>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_tile_kernel(GemmArgs g) {
   using C = TileCfg<BM, BN, WM, WN>;
   static_assert(NS >= 2 && (NS - 2) * C::LPW < 64, "stages / vmcnt range");
@@ -976,13 +1047,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_tile_kernel(GemmArgs g) 
       // the same waves as a 4 x 2 grid when the full tile's is 2 x 4 (each
       // wave then keeps 64 columns, which the fused epilogue needs)
       constexpr int HWM = WN == 4 ? 4 : WM, HWN = WN == 4 ? 2 : WN;
-      tile_run<BM, BN / 2, HWM, HWN, NS, kFused>(g, smem, tm * BM, n0, k_begin, (k_end - k_begin) / 64,
-                                                 blockIdx.y);
+      tile_run<BM, BN / 2, HWM, HWN, NS, kFused, kMask>(g, smem, tm * BM, n0, k_begin,
+                                                        (k_end - k_begin) / 64, blockIdx.y);
       return;
     }
   }
-  tile_run<BM, BN, WM, WN, NS, kFused>(g, smem, tm * BM, tn * BN, k_begin, (k_end - k_begin) / 64,
-                                       blockIdx.y);
+  tile_run<BM, BN, WM, WN, NS, kFused, kMask>(g, smem, tm * BM, tn * BN, k_begin,
+                                              (k_end - k_begin) / 64, blockIdx.y);
 }
 
 // Stream-K GEMM over workgroups 0 .. G-1, with the plan built by workgroup
@@ -1295,6 +1366,7 @@ hipError_t launch_base_gemm(const GemmConfig &c, const GemmArgs &g, hipStream_t 
     else hipLaunchKernelGGL(gemm_decode_kernel<4>, grid, dim3(256), 0, s, g);
     return hipGetLastError();
   }
+  if (g.mask && !(c.kind == 5 && c.fused)) return hipErrorInvalidConfiguration;
   if (c.kind == 5 || c.kind == 6) {
     const int tiles = ((g.M + c.bm - 1) / c.bm) * ((g.N + c.bn - 1) / c.bn);
     const dim3 grid = c.sk > 0 ? dim3(c.sk, 1) : dim3(8 * ((tiles + 7) / 8), c.splits);
@@ -1304,7 +1376,10 @@ hipError_t launch_base_gemm(const GemmConfig &c, const GemmArgs &g, hipStream_t 
         unsigned gx = grid.x;
         const unsigned nf = gx - gx % 256, rem = gx - nf;
         if (nf > 0 && rem > 0 && rem <= 128) gx = nf + 2 * rem;
-        hipLaunchKernelGGL((gemm_tile_kernel<256, 256, 2, 4, 2, true>), dim3(gx, grid.y), dim3(512), 0, s, g);
+        if (g.mask)
+          hipLaunchKernelGGL((gemm_tile_kernel<256, 256, 2, 4, 2, true, true>), dim3(gx, grid.y), dim3(512), 0, s, g);
+        else
+          hipLaunchKernelGGL((gemm_tile_kernel<256, 256, 2, 4, 2, true>), dim3(gx, grid.y), dim3(512), 0, s, g);
       }
       else hipLaunchKernelGGL((gemm_tile_kernel<256, 256, 2, 4, 2, false>), grid, dim3(512), 0, s, g);
     } else {

@@ -249,6 +249,9 @@ struct GemmArgs {
   float *partial;           // [splits][M][N]
   void *Y;                  // fused epilogue output [M][N]
   ExpandArgs ex;
+  // not null (fused 256 x 256 tiles only): keep mask [M][N] of 0/1 bytes that
+  // multiplies the expand term before the rounding (the input gradient)
+  const uint8_t *mask;
 };
 
 struct EpilogueArgs {

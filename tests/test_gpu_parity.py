@@ -773,6 +773,54 @@ def test_grad_x_prefill_fused_shape():
     assert rel_err(D.as_f64(got), ref) <= TOL["bf16"]
 
 
+def _with_mask(w, keep_p=0.9, seed=12):
+    """The workload with a seeded Bernoulli(keep_p) keep mask on X when its
+    recipe has none (the forward, the gradients and dX all see it)."""
+    if w.keep_mask is None:
+        rng = np.random.default_rng(seed)
+        w.keep_mask = (rng.random((w.T, w.d_in)) < keep_p).astype(np.uint8)
+        w.keep_scale = float(np.float32(1.0 / keep_p))
+    return w
+
+
+# 17 x 16 output tiles of 256 x 256 (ragged in both): the dX GEMM takes the
+# LoRA term and the keep mask in its own epilogue, the last 16 tiles as
+# 256 x 128 halves
+_FUSED_X = dict(T=4300, d_in=3904, d_out=512)
+
+
+@pytest.mark.parametrize("cfg,mask", [(4, True), (5, True), (3, True), (3, False), (5, False)])
+def test_grad_x_fused_tiles(cfg, mask):
+    """dX with the LoRA term in the 256 x 256 tile GEMM's epilogue, every row
+    against the oracle: rank-16 segments (MFMA blocks), top-2 routing (the
+    row path), mixed ranks up to 128 (both paths in one batch), with and
+    without the keep mask."""
+    extra = {} if cfg == 4 else {"n_adapters": 40}
+    w = _with_dY(wl.config(cfg, seed=460 + cfg, **_FUSED_X, **extra))
+    if mask:
+        w = _with_mask(w)
+    else:
+        w.keep_mask = None
+        w.keep_scale = 1.0
+    assert B.lora_grad_x_workspace_bytes(w.T, w.d_in, w.d_out, B.LORA_BF16) < 1024
+    L, got = _grad_x_run(w)
+    ref = O.grad_x_workload(w)
+    assert rel_err(D.as_f64(got), ref) <= TOL["bf16"]
+
+
+def test_grad_x_fused_inactive_rows_equal_base_bit_for_bit():
+    """In the fused epilogue a row with no active slot, inside a block whose
+    other rows carry a masked LoRA term, is dY.W^T rounded once."""
+    w = wl.config(4, seed=470, **_FUSED_X)
+    w.ids[::3] = -1
+    L, got = _grad_x_run(w)
+    w0 = wl.config(4, seed=470, **_FUSED_X)
+    w0.ids[:] = -1
+    L0, base = _grad_x_run(w0)
+    assert np.array_equal(got[::3], base[::3])
+    assert rel_err(D.as_f64(got), O.grad_x_workload(w)) <= TOL["bf16"]
+
+
 def test_grad_x_full_prefill_sampled_rows():
     w = full(4)
     L, got = _grad_x_run(w)
