@@ -345,7 +345,8 @@ struct PlanArgs {
   int use_tile;      // 1: segments of >= kBigSegPairs pairs go to the MFMA shrink
   int page_cache;    // 1: the page table is copied to LDS (after the slot cache)
   int no_sched;      // 1: skip the decode-shrink wave records (header word kPhSched = 0)
-  int place_table;   // 1: placement counts per (wave, adapter) in LDS (after the page table)
+  int place_table;   // placement counts in LDS (after the page table) per 1: (wave, adapter),
+                     // 2: (chunk of slots, wave, adapter); 0: none
   // not null: U per slot (stride slot_stride) to be stored in the u_off layout
   // at u_out when the plan's R_pairs <= u_cap (else LORA_DEVERR_CAPACITY)
   const float *slot_u;

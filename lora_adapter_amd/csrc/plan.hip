@@ -32,11 +32,15 @@ PlanLaunch plan_setup(const int32_t *ids, const float *gates, int T, int K, cons
   const int64_t used = fixed + (pl.a.slot_cache ? 2 * TK : 0);
   pl.a.page_cache = pl.a.slot_cache && pool.n_page_ids > 0 && used + pool.n_page_ids <= cap ? 1 : 0;
   const int64_t used2 = used + (pl.a.page_cache ? pool.n_page_ids : 0);
-  // the placement's (wave, adapter) count table, when it fits beside them and
-  // saves barriers (three per chunk of slots against one per wave of it)
+  // the placement's count table, when it fits beside them: per (chunk of nt
+  // slots, wave, adapter), no barrier in the placement; else per (wave,
+  // adapter), three barriers a chunk against one per wave of it
   const int64_t table = int64_t(nt / 64) * N;
-  pl.a.place_table = pl.lds && pl.a.slot_cache && nt >= 256 && used2 + table <= cap ? 1 : 0;
-  pl.lds_bytes = size_t(used2 + (pl.a.place_table ? table : 0)) * sizeof(int);
+  const int64_t table2 = (TK + nt - 1) / nt * table;
+  if (pl.lds && pl.a.slot_cache && used2 + table2 <= cap) pl.a.place_table = 2;
+  else if (pl.lds && pl.a.slot_cache && nt >= 256 && used2 + table <= cap) pl.a.place_table = 1;
+  const int64_t tab = pl.a.place_table == 2 ? table2 : pl.a.place_table == 1 ? table : 0;
+  pl.lds_bytes = size_t(used2 + tab) * sizeof(int);
   return pl;
 }
 

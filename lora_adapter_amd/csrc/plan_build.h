@@ -34,7 +34,10 @@
 //      slots (one slot per thread) take their turns in order, which keeps the
 //      sort stable; with a (wave, adapter) count table in LDS, every slot
 //      instead adds the counts of the chunk's earlier waves to the cursor,
-//      the same positions with three barriers a chunk instead of one a wave.
+//      the same positions with three barriers a chunk instead of one a wave;
+//      and when a (chunk, wave, adapter) table fits, step 1 fills it, one
+//      scan per adapter turns it into start positions, and the placement
+//      needs no barrier at all.
 // The ids and gates of the first 8 chunks of slots are fetched in one round
 // trip at the start (a later chunk's loads would each be one more).
 // Per-adapter arrays live in LDS when they fit (96 KiB); then the barriers
@@ -199,10 +202,13 @@ __device__ __forceinline__ void plan_build(const PlanArgs &a, int *dyn) {
   // global round trip after the segment order)
   int *slot_g = slot_ad + TK;                 // gate bits of each slot (with the cache)
   int *pcache = slot_ad + (a.slot_cache ? 2 * TK : 0);
-  // placement counts per (wave, adapter), zero between chunks
+  // place_table 1: placement counts per (wave, adapter), zero between
+  // chunks; 2: per (chunk, wave, adapter), counted by step 1 and turned into
+  // start positions before step 5
+  const int nch = int((TK + nt - 1) / nt);
   int *ptab = pcache + (a.page_cache ? a.n_page_ids : 0);
   if (a.place_table)
-    for (int e = tid; e < nwv * N; e += nt) ptab[e] = 0;
+    for (int e = tid; e < (a.place_table == 2 ? nch : 1) * nwv * N; e += nt) ptab[e] = 0;
   // counts of used adapters per (bucket, round of nt adapters, wave)
   const int Q = (N + nt - 1) / nt;
   const int E = Q * nwv;
@@ -264,7 +270,7 @@ __device__ __forceinline__ void plan_build(const PlanArgs &a, int *dyn) {
   // 1. classify and count
   const int nbits = N > 1 ? 32 - __clz(N - 1) : 1;
   int err = 0;
-  auto classify = [&](int64_t i, int id, float g) __attribute__((always_inline)) {
+  auto classify = [&](int64_t i, int ch, int id, float g) __attribute__((always_inline)) {
     int ad = -1;
     if (i < TK) {
       if (id < -1 || id >= N) {
@@ -274,20 +280,27 @@ __device__ __forceinline__ void plan_build(const PlanArgs &a, int *dyn) {
         if (v & kInfBadRank) err |= LORA_DEVERR_BAD_RANK;
         else if ((v & kInfRankMask) > 0 && g != 0.0f) ad = id;
       }
-      if (a.slot_cache) {
-        slot_ad[i] = ad;
-        slot_g[i] = __float_as_int(g);
-      }
+      if (a.slot_cache) slot_g[i] = __float_as_int(g);
     }
     const uint64_t mm = match_lanes(ad, nbits);
-    if (ad >= 0 && (mm & lt_mask) == 0) atomicAdd(&cnt[ad], __popcll(mm));
+    // place_table 2 packs the slot's rank among its wave's slots of ad
+    // (below 64; ad < 2^25 there, as the table fits in LDS)
+    if (a.slot_cache && i < TK)
+      slot_ad[i] = a.place_table == 2 && ad >= 0 ? ad * 64 + __popcll(mm & lt_mask) : ad;
+    if (ad >= 0 && (mm & lt_mask) == 0) {
+      atomicAdd(&cnt[ad], __popcll(mm));
+      if (a.place_table == 2) ptab[(ch * nwv + wave) * N + ad] = __popcll(mm);
+    }
   };
 #pragma unroll
   for (int c = 0; c < kPreChunks; ++c)
-    if (int64_t(c) * nt < TK) classify(int64_t(c) * nt + tid, id_pre[c], g_pre[c]);
-  for (int64_t base = int64_t(kPreChunks) * nt; base < TK; base += nt) {
-    const int64_t i = base + tid;
-    classify(i, i < TK ? a.ids[i] : -1, i < TK ? a.gates[i] : 0.0f);
+    if (int64_t(c) * nt < TK) classify(int64_t(c) * nt + tid, c, id_pre[c], g_pre[c]);
+  {
+    int ch = kPreChunks;
+    for (int64_t base = int64_t(kPreChunks) * nt; base < TK; base += nt, ++ch) {
+      const int64_t i = base + tid;
+      classify(i, ch, i < TK ? a.ids[i] : -1, i < TK ? a.gates[i] : 0.0f);
+    }
   }
   if (err) atomicOr(&s_err, err);
   bar<kLds>();
@@ -504,6 +517,25 @@ __device__ __forceinline__ void plan_build(const PlanArgs &a, int *dyn) {
     bar<kLds>();
   }
 
+  // place_table 2: each used adapter's (chunk, wave) counts, in slot order,
+  // become start positions: its first pair plus the exclusive scan (one wave
+  // per adapter)
+  if (a.place_table == 2) {
+    const int EC = nch * nwv;
+    for (int ad = wave; ad < N; ad += nwv) {
+      if (ld_ctr(&cnt[ad]) <= 0) continue;
+      int carry = ld_ctr(&cur[ad]);
+      for (int e0 = 0; e0 < EC; e0 += 64) {
+        const int e = e0 + lane;
+        const int v = e < EC ? ptab[e * N + ad] : 0;
+        const int inc = wave_scan_incl(v);
+        if (e < EC) ptab[e * N + ad] = carry + inc - v;
+        carry += __builtin_amdgcn_readlane(inc, 63);
+      }
+    }
+    bar<kLds>();
+  }
+
   // U per slot to the u_off layout needs room for R_pairs floats
   const bool copy_u = a.slot_u != nullptr && int64_t(u_base) <= a.u_cap;
   if (a.slot_u != nullptr && !copy_u && tid == 0) atomicOr(&s_err, LORA_DEVERR_CAPACITY);
@@ -514,90 +546,109 @@ __device__ __forceinline__ void plan_build(const PlanArgs &a, int *dyn) {
   // 5. ordered placement: within each nt-slot chunk the waves holding slots
   //    take positions from the adapter cursors in wave order (stable sort)
   int4 *slot_desc = reinterpret_cast<int4 *>(P + L.slot_desc);
-  for (int64_t base = 0; base < TK; base += nt) {
-    const int64_t i = base + tid;
-    int ad = -1;
-    float gate = 0.0f;
-    if (i < TK) {
-      if (a.slot_cache) {
-        ad = slot_ad[i];
-        gate = __int_as_float(slot_g[i]);
-      } else {
-        const int id = a.ids[i];
-        gate = a.gates[i];
-        if (id >= 0 && id < N) {
-          const int v = inf[id];
-          if (!(v & kInfBadRank) && (v & kInfRankMask) > 0 && gate != 0.0f) ad = id;
-        }
-      }
-      if (ad >= 0 && ld_ctr(&cnt[ad]) <= 0) ad = -1;
-    }
-    const uint64_t mm = match_lanes(ad, nbits);
-    const int rank_in_wave = __popcll(mm & lt_mask);
-    const int leader = mm ? __ffsll((unsigned long long)mm) - 1 : lane;
-    const int64_t here = TK - base < nt ? TK - base : nt;
-    const int nw = int((here + 63) >> 6);
-    int pos = -1;
-    if (a.place_table) {
-      // the same positions as the waves taking turns: the adapter's cursor,
-      // plus its slots in the chunk's earlier waves (the count table), plus
-      // the slot's rank in its own wave; cursors move after every wave has
-      // read them, and each wave clears its own table entries
-      const bool lead = ad >= 0 && rank_in_wave == 0;
-      bar<kLds>();
-      if (lead) ptab[wave * N + ad] = __popcll(mm);
-      bar<kLds>();
-      if (ad >= 0) {
-        int before = 0;
-        for (int w = 0; w < wave; ++w) before += ptab[w * N + ad];
-        pos = ld_ctr(&cur[ad]) + before + rank_in_wave;
-      }
-      bar<kLds>();
-      if (lead) {
-        atomicAdd(&cur[ad], __popcll(mm));
-        ptab[wave * N + ad] = 0;
-      }
-    } else {
-      for (int w = 0; w < nw; ++w) {
-        bar<kLds>();
-        if (wave == w) {
-          int b0 = 0;
-          if (ad >= 0 && rank_in_wave == 0) b0 = atomicAdd(&cur[ad], __popcll(mm));
-          b0 = __shfl(b0, leader, 64);
-          if (ad >= 0) pos = b0 + rank_in_wave;
-        }
-      }
-    }
-    if (i < TK) {
-      P[L.slot_pos + i] = pos;
-      if (pos >= 0) {
-        const int r = inf[ad] & kInfRankMask;
-        const int uo = ubias[ad] + pos * r;
-        P[L.pair_tk + pos] = int32_t(i);
-        P[L.pair_adapter + pos] = ad;
-        P[L.pair_gate + pos] = __float_as_int(gate);
-        P[L.u_off + pos] = uo;
-        slot_desc[i] = make_int4(pos, r, uo, psa[ad]);
-        if (copy_u) {
-          // this slot's U (per-slot layout, 16-byte aligned rows of
-          // slot_stride floats) to its u_off place: 8 loads in flight
-          const float4 *src = reinterpret_cast<const float4 *>(a.slot_u + i * int64_t(a.slot_stride));
-          for (int j0 = 0; j0 < r; j0 += 32) {
-            float4 v[8];
+  // the slot's outputs: its position, and for a placed pair the pair arrays,
+  // its descriptor and (decode) its U moved to the u_off layout
+  auto emit = [&](int64_t i, int ad, int pos, float gate) __attribute__((always_inline)) {
+    P[L.slot_pos + i] = pos;
+    if (pos >= 0) {
+      const int r = inf[ad] & kInfRankMask;
+      const int uo = ubias[ad] + pos * r;
+      P[L.pair_tk + pos] = int32_t(i);
+      P[L.pair_adapter + pos] = ad;
+      P[L.pair_gate + pos] = __float_as_int(gate);
+      P[L.u_off + pos] = uo;
+      slot_desc[i] = make_int4(pos, r, uo, psa[ad]);
+      if (copy_u) {
+        // this slot's U (per-slot layout, 16-byte aligned rows of
+        // slot_stride floats) to its u_off place: 8 loads in flight
+        const float4 *src = reinterpret_cast<const float4 *>(a.slot_u + i * int64_t(a.slot_stride));
+        for (int j0 = 0; j0 < r; j0 += 32) {
+          float4 v[8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = src[min(j0 / 4 + q, (r - 1) / 4)];
+          for (int q = 0; q < 8; ++q) v[q] = src[min(j0 / 4 + q, (r - 1) / 4)];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-              const float e4[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+          for (int q = 0; q < 8; ++q) {
+            const float e4[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (j0 + 4 * q + e < r) a.u_out[uo + j0 + 4 * q + e] = e4[e];
-            }
+            for (int e = 0; e < 4; ++e)
+              if (j0 + 4 * q + e < r) a.u_out[uo + j0 + 4 * q + e] = e4[e];
           }
         }
-      } else {
-        slot_desc[i] = make_int4(-1, 0, 0, 0);
       }
+    } else {
+      slot_desc[i] = make_int4(-1, 0, 0, 0);
+    }
+  };
+  if (a.place_table == 2) {
+    // no barrier and no ballot: the slot cache holds each slot's adapter and
+    // its rank among its wave's slots of that adapter (step 1), the table the
+    // start of every (chunk, wave, adapter)
+    int ch = 0;
+    for (int64_t base = 0; base < TK; base += nt, ++ch) {
+      const int64_t i = base + tid;
+      if (i >= TK) break;
+      const int sa = slot_ad[i];
+      const int ad = sa >= 0 ? sa >> 6 : -1;
+      int pos = -1;
+      if (ad >= 0 && ld_ctr(&cnt[ad]) > 0) pos = ptab[(ch * nwv + wave) * N + ad] + (sa & 63);
+      emit(i, pos >= 0 ? ad : -1, pos, __int_as_float(slot_g[i]));
+    }
+  } else {
+    for (int64_t base = 0; base < TK; base += nt) {
+      const int64_t i = base + tid;
+      int ad = -1;
+      float gate = 0.0f;
+      if (i < TK) {
+        if (a.slot_cache) {
+          ad = slot_ad[i];
+          gate = __int_as_float(slot_g[i]);
+        } else {
+          const int id = a.ids[i];
+          gate = a.gates[i];
+          if (id >= 0 && id < N) {
+            const int v = inf[id];
+            if (!(v & kInfBadRank) && (v & kInfRankMask) > 0 && gate != 0.0f) ad = id;
+          }
+        }
+        if (ad >= 0 && ld_ctr(&cnt[ad]) <= 0) ad = -1;
+      }
+      const uint64_t mm = match_lanes(ad, nbits);
+      const int rank_in_wave = __popcll(mm & lt_mask);
+      const int leader = mm ? __ffsll((unsigned long long)mm) - 1 : lane;
+      const int64_t here = TK - base < nt ? TK - base : nt;
+      const int nw = int((here + 63) >> 6);
+      int pos = -1;
+      if (a.place_table == 1) {
+        // the same positions as the waves taking turns: the adapter's cursor,
+        // plus its slots in the chunk's earlier waves (the count table), plus
+        // the slot's rank in its own wave; cursors move after every wave has
+        // read them, and each wave clears its own table entries
+        const bool lead = ad >= 0 && rank_in_wave == 0;
+        bar<kLds>();
+        if (lead) ptab[wave * N + ad] = __popcll(mm);
+        bar<kLds>();
+        if (ad >= 0) {
+          int before = 0;
+          for (int w = 0; w < wave; ++w) before += ptab[w * N + ad];
+          pos = ld_ctr(&cur[ad]) + before + rank_in_wave;
+        }
+        bar<kLds>();
+        if (lead) {
+          atomicAdd(&cur[ad], __popcll(mm));
+          ptab[wave * N + ad] = 0;
+        }
+      } else {
+        for (int w = 0; w < nw; ++w) {
+          bar<kLds>();
+          if (wave == w) {
+            int b0 = 0;
+            if (ad >= 0 && rank_in_wave == 0) b0 = atomicAdd(&cur[ad], __popcll(mm));
+            b0 = __shfl(b0, leader, 64);
+            if (ad >= 0) pos = b0 + rank_in_wave;
+          }
+        }
+      }
+      if (i < TK) emit(i, ad, pos, gate);
     }
   }
   bar<kLds>();
