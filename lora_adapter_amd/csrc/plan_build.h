@@ -518,19 +518,39 @@ __device__ __forceinline__ void plan_build(const PlanArgs &a, int *dyn) {
   }
 
   // place_table 2: each used adapter's (chunk, wave) counts, in slot order,
-  // become start positions: its first pair plus the exclusive scan (one wave
-  // per adapter)
+  // become start positions: its first pair plus the exclusive scan.  A pool
+  // of a few adapters takes one wave per adapter (a wave-wide scan of its
+  // counts); larger pools one lane per adapter walking its counts in order,
+  // so that no wave steps through the adapters one LDS round trip at a time
+  // (1024 adapters on 4 waves: 256 dependent trips each)
   if (a.place_table == 2) {
     const int EC = nch * nwv;
-    for (int ad = wave; ad < N; ad += nwv) {
-      if (ld_ctr(&cnt[ad]) <= 0) continue;
-      int carry = ld_ctr(&cur[ad]);
-      for (int e0 = 0; e0 < EC; e0 += 64) {
-        const int e = e0 + lane;
-        const int v = e < EC ? ptab[e * N + ad] : 0;
-        const int inc = wave_scan_incl(v);
-        if (e < EC) ptab[e * N + ad] = carry + inc - v;
-        carry += __builtin_amdgcn_readlane(inc, 63);
+    if (N > 2 * nwv) {
+      for (int ad = tid; ad < N; ad += nt) {
+        if (ld_ctr(&cnt[ad]) <= 0) continue;
+        int carry = ld_ctr(&cur[ad]);
+        for (int e0 = 0; e0 < EC; e0 += 8) {
+          int v[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) v[q] = e0 + q < EC ? ptab[(e0 + q) * N + ad] : 0;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            if (e0 + q < EC) ptab[(e0 + q) * N + ad] = carry;
+            carry += v[q];
+          }
+        }
+      }
+    } else {
+      for (int ad = wave; ad < N; ad += nwv) {
+        if (ld_ctr(&cnt[ad]) <= 0) continue;
+        int carry = ld_ctr(&cur[ad]);
+        for (int e0 = 0; e0 < EC; e0 += 64) {
+          const int e = e0 + lane;
+          const int v = e < EC ? ptab[e * N + ad] : 0;
+          const int inc = wave_scan_incl(v);
+          if (e < EC) ptab[e * N + ad] = carry + inc - v;
+          carry += __builtin_amdgcn_readlane(inc, 63);
+        }
       }
     }
     bar<kLds>();
