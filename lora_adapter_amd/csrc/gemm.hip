@@ -458,6 +458,53 @@ __device__ __forceinline__ void tile_coords(int T, int tiles_m, int tiles_n, int
   tn = in / gm;
 }
 
+// Operands of the fused epilogue's MFMA expand that do not depend on the
+// product: the slot descriptors of the tile's rows and the page ids of the
+// first adapter of the wave's first block.  They are fetched while the K loop
+// runs (the descriptors before its first copies, the page ids once those have
+// landed); after the loop each would be a round trip of its own with the MFMA
+// pipe idle.  U is not held across the loop (32 more registers would spill):
+// the epilogue issues it together with the B values, one round trip for both.
+template <int TM>
+struct EpiPre {
+  int4 sd[TM];        // slot descriptor of row frow of each 32-row block
+  int pid;            // lanes 0-15: page id of rank row `lane` of (kps, kr)
+  int kps, kr;        // page start and rank of block 0's first adapter (-1: none)
+};
+
+// The descriptors (none when U is absent or K > 1: those tiles take the row
+// path or no LoRA term).
+template <int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void epi_fetch_desc(const GemmArgs &g, int m0,
+                                               EpiPre<TileCfg<BM, BN, WM, WN>::TM> &p) {
+  constexpr int TM = TileCfg<BM, BN, WM, WN>::TM;
+  const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) / WN;
+  const bool want = g.ex.U != nullptr && g.ex.K == 1;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int row = m0 + wm * TM * 32 + i * 32 + (lane & 31);
+    p.sd[i] = want ? g.ex.slot_desc[min(row, g.M - 1)] : make_int4(-1, 0, 0, 0);
+    if (row >= g.M) p.sd[i].x = -1;
+  }
+  p.kps = -1;
+  p.kr = -1;
+  p.pid = 0;
+}
+
+// The page ids of block 0's first adapter (the load the epilogue would issue
+// for it).
+template <int TM>
+__device__ __forceinline__ void epi_fetch_pid(const GemmArgs &g, EpiPre<TM> &p) {
+  const int lane = threadIdx.x & 63;
+  const unsigned long long m = __ballot(p.sd[0].x >= 0) & 0xffffffffull;
+  if (m && expand_enabled(g.ex)) {
+    const int leader = __ffsll(m) - 1;
+    p.kps = __shfl(p.sd[0].w, leader, 64);
+    p.kr = __shfl(p.sd[0].y, leader, 64);
+    if (lane < 16) p.pid = g.ex.page_ids[p.kps + min(lane, p.kr - 1)];
+  }
+}
+
 // Fused epilogue of a tile: add the expand to the fp32 accumulators, round
 // once, store Y.
 //   * One slot per token (K = 1) and ranks <= 16 -- prefill: the expand of a
@@ -466,8 +513,9 @@ __device__ __forceinline__ void tile_coords(int T, int tiles_m, int tiles_n, int
 //     MFMA block), accumulated into the base product's registers.  A block
 //     spanning several adapters takes one pass per adapter, with the U rows
 //     of the other adapters zero.  The B fragments of the last adapter are
-//     kept, so a long segment loads them once.  The slot descriptors of all
-//     blocks, then U and page ids, then B values, are each one round trip.
+//     kept, so a long segment loads them once.  The slot descriptors, U and
+//     the first adapter's page ids come prefetched (EpiPre); B values are
+//     the one round trip left after the K loop.
 //   * Blocks with higher ranks or several slots per token add the expand row
 //     by row (all lanes on one row).
 //   * Every block is staged in LDS and stored with 16-byte stores when it
@@ -486,7 +534,8 @@ template <int BM, int BN, int WM, int WN, bool kMask>
 __device__ __forceinline__ void fused_epilogue(const GemmArgs &g,
                                                f32x16_t (&acc)[TileCfg<BM, BN, WM, WN>::TM]
                                                               [TileCfg<BM, BN, WM, WN>::TN],
-                                               char *lds0, char *lds1, int m0, int n0) {
+                                               char *lds0, char *lds1, int m0, int n0,
+                                               const EpiPre<TileCfg<BM, BN, WM, WN>::TM> &pre) {
   using C = TileCfg<BM, BN, WM, WN>;
   constexpr int TM = C::TM, TN = C::TN;
   constexpr int WC = TN * 32;                // columns of this wave's sub-tile
@@ -503,18 +552,13 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs &g,
   const bool mfma_ok = lora_on && g.ex.K == 1;
   const uint16_t *Bp = static_cast<const uint16_t *>(g.ex.b_pages);
 
-  // round trip 1: slot descriptor of row frow of every block; round trip 2:
-  // that row's U values (rank rows 8*half .. +7)
-  int4 sdv[TM];
+  // slot descriptor of row frow of every block (fetched during the K loop),
+  // and that row's U values (rank rows 8*half .. +7), whose loads share their
+  // round trip with the first B values
+  const int4 (&sdv)[TM] = pre.sd;
   float uv[TM][8];
   unsigned rowwise = lora_on && !mfma_ok ? (1u << TM) - 1 : 0u;   // blocks for the row path
   if (mfma_ok) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int row = m0 + wm * TM * 32 + i * 32 + frow;
-      sdv[i] = g.ex.slot_desc[min(row, g.M - 1)];
-      if (row >= g.M) sdv[i].x = -1;
-    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const bool act = sdv[i].x >= 0;
@@ -579,7 +623,8 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs &g,
         if (kps != bkey_ps || kr != bkey_r) {
           // B operand: lane (column frow of block j, rank rows 8*half .. +7)
           int pidl = 0;
-          if (lane < 16) pidl = g.ex.page_ids[kps + min(lane, kr - 1)];
+          if (kps == pre.kps && kr == pre.kr) pidl = pre.pid;
+          else if (lane < 16) pidl = g.ex.page_ids[kps + min(lane, kr - 1)];
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
             const int cj = min(n0 + wn * TN * 32 + j * 32 + frow, g.N - 1);
@@ -851,6 +896,10 @@ __device__ __forceinline__ void tile_run(const GemmArgs &g, char *smem, int m0, 
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
+  // the fused epilogue's descriptors go out ahead of the first copies
+  EpiPre<TM> pre;
+  if constexpr (kFused) epi_fetch_desc<BM, BN, WM, WN>(g, m0, pre);
+
   const int frow = lane & 31, half = lane >> 5;
   // NS >= 3 stages in a ring: K tile kt lives in stage kt % NS.  At the top
   // of step kt, once tile kt has landed and every wave has left step kt - 1,
@@ -935,7 +984,15 @@ __device__ __forceinline__ void tile_run(const GemmArgs &g, char *smem, int m0, 
       kstep(std::integral_constant<int, 1>{}, fa0, fb0, fa1, fb1, cur, 3, cur, 0);
       wait_vmcnt<0>();   // tile kt + 1, the only copies in flight, has landed
       lds_bar();         // for every wave, and every wave has read cur
+      // fused: the descriptors have landed with the first copies; the page
+      // ids go out now and land under the following K tiles
+      if constexpr (kFused) {
+        if (kt == 0) epi_fetch_pid(g, pre);
+      }
       kstep(std::integral_constant<int, 3>{}, fa1, fb1, fa0, fb0, nxt, 0, cur, min(kt + 2, nk - 1));
+    }
+    if constexpr (kFused) {
+      if (nk <= 0) epi_fetch_pid(g, pre);
     }
     // the copies of the last step have landed and every wave is done with
     // the stages before anything else uses this LDS
@@ -960,6 +1017,7 @@ __device__ __forceinline__ void tile_run(const GemmArgs &g, char *smem, int m0, 
         }
       }
     }
+    if constexpr (kFused) epi_fetch_pid(g, pre);
     __syncthreads();   // the epilogue reuses the stages
   }
 
@@ -979,7 +1037,7 @@ __device__ __forceinline__ void tile_run(const GemmArgs &g, char *smem, int m0, 
         }
       }
   } else {
-    fused_epilogue<BM, BN, WM, WN, kMask>(g, acc, st0, st1, m0, n0);
+    fused_epilogue<BM, BN, WM, WN, kMask>(g, acc, st0, st1, m0, n0, pre);
   }
 }
 
