@@ -563,12 +563,35 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs &g,
     for (int i = 0; i < TM; ++i) {
       const bool act = sdv[i].x >= 0;
       if (__ballot(act && sdv[i].y > 16) != 0) rowwise |= 1u << i;
-      const int r = act ? min(sdv[i].y, 16) : 1;
+      // 32 consecutive pairs of one adapter of rank 8 or 16 hold their U as
+      // one run of 32 r floats: the wave loads it in 16-byte pieces (lane l
+      // floats 8l .. 8l+7, i.e. row l r/8 ... ) and hands each row's values
+      // to its lanes by shuffles.  Otherwise each lane loads its 8 values
+      // one by one (every such load touches 16 cache lines).
+      const int r0 = __shfl(sdv[i].y, 0, 64), z0 = __shfl(sdv[i].z, 0, 64);
+      const int w0 = __shfl(sdv[i].w, 0, 64);
+      const bool in_run = act && sdv[i].y == r0 && sdv[i].w == w0 && sdv[i].z == z0 + r0 * frow;
+      const bool run = __ballot(!in_run) == 0 && (r0 == 8 || r0 == 16) &&
+                       (reinterpret_cast<uintptr_t>(g.ex.U + z0) & 15) == 0;
+      if (run) {
+        const float4 *src = reinterpret_cast<const float4 *>(g.ex.U + z0) + 2 * min(lane, 4 * r0 - 1);
+        const float4 lo4 = src[0], hi4 = src[1];
+        const float v8[8] = {lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
+        // row frow's rank rows 8*half .. +7 sit in lane frow * r/8 + half
+        const int from = min(frow * (r0 / 8) + half, 63);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int ja = half * 8 + e;
-        uv[i][e] = act ? g.ex.U[sdv[i].z + min(ja, r - 1)] : 0.f;
-        if (ja >= r) uv[i][e] = 0.f;
+        for (int e = 0; e < 8; ++e) {
+          const float x = __shfl(v8[e], from, 64);
+          uv[i][e] = half * 8 < r0 ? x : 0.f;
+        }
+      } else {
+        const int r = act ? min(sdv[i].y, 16) : 1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int ja = half * 8 + e;
+          uv[i][e] = act ? g.ex.U[sdv[i].z + min(ja, r - 1)] : 0.f;
+          if (ja >= r) uv[i][e] = 0.f;
+        }
       }
     }
   }
