@@ -183,6 +183,38 @@ def test_apply_fused_epilogue_path(d_out):
     assert err <= TOL["bf16"], err
 
 
+FUSED_RUN_CASES = {
+    # contiguous segments of ranks 8 and 16 whose U runs start 16-byte
+    # aligned: 32-row blocks inside a segment load U in 16-byte pieces
+    "aligned_r8_r16": ((8, 16, 8, 16), (512, 544, 480, 564)),
+    # a rank-5 segment of odd length first, so the rank-8 and rank-16 runs
+    # after it start misaligned (element-wise loads), a rank-12 segment (no
+    # run form) and segment edges inside blocks
+    "misaligned_r5_r12": ((5, 8, 12, 16, 16), (333, 421, 389, 517, 440)),
+}
+
+
+@pytest.mark.parametrize("case", sorted(FUSED_RUN_CASES))
+def test_apply_fused_u_runs(case):
+    """The fused epilogue's U loads: a block of consecutive pairs of one
+    rank-8 or rank-16 adapter whose U starts 16-byte aligned is loaded in
+    16-byte pieces and shuffled to its lanes; other blocks element by
+    element.  Every row of Y against the oracle."""
+    ranks, lens = FUSED_RUN_CASES[case]
+    rank = np.asarray(ranks, np.int32)
+    T = int(sum(lens))
+    ids = np.repeat(np.arange(len(rank), dtype=np.int32), lens).reshape(T, 1)
+    gates = np.ones((T, 1), np.float32)
+    w = wl.build("fused-u-runs-" + case, 97, "bf16", T, 1, 256, 8192, rank, ids, gates,
+                 x_var=1.0, w_var=0.02, a_var=1 / 64, b_var=0.02)
+    # 9 x 32 tiles of 256 x 256: the fused-epilogue form
+    assert T == 2100 and ((T + 255) // 256) * (8192 // 256) >= 256
+    L = run(w)
+    assert L.read_plan()["header"][B.PH_ERR] == 0
+    err = rel_err(D.as_f64(L.Y_host()), O.apply_workload(w))
+    assert err <= TOL["bf16"], err
+
+
 SHORT_K_CASES = {
     # 256x256 fused tiles with 1, 2 and 3 K tiles of 64 (prologue, loop and
     # the copies clamped past the end)
