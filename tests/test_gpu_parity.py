@@ -471,9 +471,11 @@ FORWARD_CASES = {
                                  "full5", "dec4", "dec3", "decmix", "dec_k4", "dec_k8", "sk_k8",
                                  "split_k4"])
 def test_forward_matches_plan_then_apply(cfg):
-    """lora_forward in two launches (decode: GEMM + per-slot shrink, then
-    epilogue + plan; stream-K: GEMM + plan, then shrink and epilogue): the
-    plan, U and Y equal those of lora_plan then lora_apply bit for bit.  The same call captured in a graph is replayed three times, with
+    """lora_forward in two launches (decode: the plan in workgroup 0 beside
+    the GEMM and the per-slot shrink, then the epilogue, which also moves U
+    to the plan's layout; stream-K: the plan beside the GEMM, then shrink and
+    epilogue): the plan, U and Y equal those of lora_plan then lora_apply bit
+    for bit.  The same call captured in a graph is replayed three times, with
     eager work and synchronisation in between, and every replay gives the
     same Y."""
     if cfg in FORWARD_CASES:
