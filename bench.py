@@ -41,6 +41,9 @@ Measurement
     difference is reported beside it.
   * cpu_baseline: the CPU oracle (fp64 numpy, untuned) on a bounded sample of
     the same workload, on the host's cores.
+  * hipblaslt_gemm_us (each workload): torch.mm (hipBLASLt) of X by W on the
+    same rotated copies, timed like the launches: the plain GEMM without the
+    LoRA term, context only.
 
   --copy-probe runs a 256 MiB device-to-device copy five times first, so that
   a rocprofv3 --pmc run of this script also holds the calibration kernel.
@@ -87,6 +90,8 @@ def parse():
                          "--residency-frac of the fleet (pages copied in from pinned host memory)")
     ap.add_argument("--residency-frac", type=float, default=0.6)
     ap.add_argument("--no-tsqr", action="store_true", help="skip the fleet QR/compression timing")
+    ap.add_argument("--no-blas-ref", action="store_true",
+                    help="skip the context timing of torch.mm (hipBLASLt) on each workload's GEMM")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs of a --copy-probe run into "
@@ -313,6 +318,15 @@ def measure(w, args, torch, np, B, D, steps, warmup, full):
 
     st = bn.stage_us(bn.ids, args.event_steps if full else 32)
     st0 = None if skip0 else bn.stage_us(bn.empty_ids, args.event_steps if full else 32)
+    # context only: the vendor library's plain GEMM (no LoRA term) on the same
+    # rotated operands, timed the same way
+    blas_us = None
+    if bn.L.dtype == B.LORA_BF16 and not args.no_blas_ref:
+        n_ev = args.event_steps if full else 32
+        reps = min(bn.R, 32) if bn.R >= 8 else 8
+        blas_us = bn.event_us(lambda i: torch.mm(bn.copies[i % bn.R].X, bn.copies[i % bn.R].W_t.t(),
+                                                 out=bn.copies[i % bn.R].Y),
+                              reps, max(3, n_ev // reps))
     lb = lora_bytes(w, P, R_pairs, R_used, e, w.keep_mask is not None)
     lf = 2.0 * R_pairs * (w.d_in + w.d_out)
     # LoRA path from the apply's launches (the plan built once per batch):
@@ -336,6 +350,7 @@ def measure(w, args, torch, np, B, D, steps, warmup, full):
         "forward_empty_plan_us": None if skip0 else t_base * 1e6,
         "step_us_graph_replay": None if el_graph is None else el_graph / steps * 1e6,
         "stages_us": st, "stages_us_empty_plan": st0,
+        "hipblaslt_gemm_us": blas_us,
         "lora_path": {
             "t_us": t_lora if ok else None,
             "bytes": lb, "flops": lf,
