@@ -44,17 +44,17 @@ template <> struct Cols<uint16_t, 2> {
     v[0] = bf_lo(w); v[1] = bf_hi(w);
   }
   static __device__ __forceinline__ void store(uint16_t *p, const float v[2]) {
-    *reinterpret_cast<uint32_t *>(p) = uint32_t(f2bf(v[0])) | (uint32_t(f2bf(v[1])) << 16);
+    *reinterpret_cast<uint32_t *>(p) = f2bf2(v[0], v[1]);
   }
 };
 template <> struct Cols<uint16_t, 8> {
   static __device__ __forceinline__ void load(const uint16_t *p, float v[8]) { Elem<uint16_t>::load8(p, v); }
   static __device__ __forceinline__ void store(uint16_t *p, const float v[8]) {
     uint4 w;
-    w.x = uint32_t(f2bf(v[0])) | (uint32_t(f2bf(v[1])) << 16);
-    w.y = uint32_t(f2bf(v[2])) | (uint32_t(f2bf(v[3])) << 16);
-    w.z = uint32_t(f2bf(v[4])) | (uint32_t(f2bf(v[5])) << 16);
-    w.w = uint32_t(f2bf(v[6])) | (uint32_t(f2bf(v[7])) << 16);
+    w.x = f2bf2(v[0], v[1]);
+    w.y = f2bf2(v[2], v[3]);
+    w.z = f2bf2(v[4], v[5]);
+    w.w = f2bf2(v[6], v[7]);
     *reinterpret_cast<uint4 *>(p) = w;
   }
 };
@@ -63,10 +63,10 @@ template <> struct Cols<uint16_t, 8> {
 __device__ __forceinline__ void store8_nt(uint16_t *p, const float v[8]) {
   typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
   u32x4_t w;
-  w.x = uint32_t(f2bf(v[0])) | (uint32_t(f2bf(v[1])) << 16);
-  w.y = uint32_t(f2bf(v[2])) | (uint32_t(f2bf(v[3])) << 16);
-  w.z = uint32_t(f2bf(v[4])) | (uint32_t(f2bf(v[5])) << 16);
-  w.w = uint32_t(f2bf(v[6])) | (uint32_t(f2bf(v[7])) << 16);
+  w.x = f2bf2(v[0], v[1]);
+  w.y = f2bf2(v[2], v[3]);
+  w.z = f2bf2(v[4], v[5]);
+  w.w = f2bf2(v[6], v[7]);
   __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t *>(p));
 }
 template <> struct Cols<float, 8> {
@@ -674,10 +674,9 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs &g,
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const float ua = mine ? uv[i][e] : 0.f, ub = mine ? uv[i][e + 1] : 0.f;
-          const uint16_t ha = f2bf(ua), hb = f2bf(ub);
-          const uint16_t la = f2bf(ua - bf2f(ha)), lb = f2bf(ub - bf2f(hb));
-          hw[e >> 1] = uint32_t(ha) | (uint32_t(hb) << 16);
-          lw[e >> 1] = uint32_t(la) | (uint32_t(lb) << 16);
+          const uint32_t h2 = f2bf2(ua, ub);
+          hw[e >> 1] = h2;
+          lw[e >> 1] = f2bf2(ua - bf_lo(h2), ub - bf_hi(h2));
         }
         bf16x8_t ahi, alo;
         const uint4 ph = make_uint4(hw[0], hw[1], hw[2], hw[3]);

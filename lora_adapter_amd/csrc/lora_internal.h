@@ -37,12 +37,24 @@ __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w <<
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf2f(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
 
-// float32 -> bf16, round to nearest even; NaN stays NaN (quiet bit set).
+// float32 -> bf16 by the hardware conversion: round to nearest even, a NaN
+// gives a quiet NaN.
 __device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+  const __bf16 h = (__bf16)f;          // v_cvt_pk_bf16_f32
+  uint16_t u;
+  __builtin_memcpy(&u, &h, 2);
+  return u;
+}
+
+// Two values to bf16 in one hardware conversion (v_cvt_pk_bf16_f32, round to
+// nearest even): a in bits 0-15, b in bits 16-31.
+__device__ __forceinline__ uint32_t f2bf2(float a, float b) {
+  typedef float f32x2_cvt_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_cvt_t __attribute__((ext_vector_type(2)));
+  const bf16x2_cvt_t h = __builtin_convertvector((f32x2_cvt_t){a, b}, bf16x2_cvt_t);
+  uint32_t u;
+  __builtin_memcpy(&u, &h, 4);
+  return u;
 }
 
 // Element traits: storage type E is float (fp32) or uint16_t (bf16 bits).

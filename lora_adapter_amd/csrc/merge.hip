@@ -33,8 +33,8 @@ template <> struct W4<uint16_t> {
     v[0] = bf_lo(w.x); v[1] = bf_hi(w.x); v[2] = bf_lo(w.y); v[3] = bf_hi(w.y);
   }
   static __device__ __forceinline__ void store(uint16_t *p, const float v[4]) {
-    *reinterpret_cast<uint2 *>(p) = make_uint2(uint32_t(f2bf(v[0])) | (uint32_t(f2bf(v[1])) << 16),
-                                               uint32_t(f2bf(v[2])) | (uint32_t(f2bf(v[3])) << 16));
+    *reinterpret_cast<uint2 *>(p) = make_uint2(f2bf2(v[0], v[1]),
+                                               f2bf2(v[2], v[3]));
   }
 };
 template <> struct W4<float> {
@@ -283,10 +283,8 @@ __device__ __forceinline__ void qstage(const MergeArgs &m, int i0, int n0, int j
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float x0 = cf[2 * q] * bf_lo(w[q]), x1 = cf[2 * q + 1] * bf_hi(w[q]);
-      const uint16_t h0 = f2bf(x0), h1 = f2bf(x1);
-      const uint16_t l0 = f2bf(x0 - bf2f(h0)), l1 = f2bf(x1 - bf2f(h1));
-      hw[q] = uint32_t(h0) | (uint32_t(h1) << 16);
-      lw[q] = uint32_t(l0) | (uint32_t(l1) << 16);
+      hw[q] = f2bf2(x0, x1);
+      lw[q] = f2bf2(x0 - bf_lo(hw[q]), x1 - bf_hi(hw[q]));
     }
     s_bh[n][qswz(n, jg)] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
     s_bl[n][qswz(n, jg)] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
@@ -414,12 +412,11 @@ __device__ __forceinline__ void merge_stream(const MergeArgs &m, int total, uint
         const uint32_t va = wa[u >> 1], vb = wb[u >> 1];
         const float xa = oka ? ca * ((u & 1) ? bf_hi(va) : bf_lo(va)) : 0.f;
         const float xb = okb ? cb * ((u & 1) ? bf_hi(vb) : bf_lo(vb)) : 0.f;
-        const uint16_t ha = f2bf(xa), hb = f2bf(xb);
-        const uint16_t la = f2bf(xa - bf2f(ha)), lb = f2bf(xb - bf2f(hb));
+        const uint32_t h2 = f2bf2(xa, xb);
         const int n = 8 * nc + u;
         const int word = qswz(n, jp >> 2) * 4 + (jp & 3);
-        s_bh[n][word] = uint32_t(ha) | (uint32_t(hb) << 16);
-        s_bl[n][word] = uint32_t(la) | (uint32_t(lb) << 16);
+        s_bh[n][word] = h2;
+        s_bl[n][word] = f2bf2(xa - bf_lo(h2), xb - bf_hi(h2));
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -460,7 +457,7 @@ __device__ __forceinline__ void merge_stream(const MergeArgs &m, int total, uint
           for (int e = 0; e < 4; ++e) {
             const float lo = bf_lo(w[e]) + acc[b][8 * q + 2 * e];
             const float hi = bf_hi(w[e]) + acc[b][8 * q + 2 * e + 1];
-            o[e] = uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
+            o[e] = f2bf2(lo, hi);
           }
           slot = make_uint4(o[0], o[1], o[2], o[3]);
         }
@@ -575,7 +572,7 @@ __device__ __forceinline__ void merge_mfma_body(const MergeArgs &m, int bid, int
           for (int e = 0; e < 4; ++e) {
             const float lo = bf_lo(w[e]) + acc[b][8 * q + 2 * e];
             const float hi = bf_hi(w[e]) + acc[b][8 * q + 2 * e + 1];
-            o[e] = uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
+            o[e] = f2bf2(lo, hi);
           }
           *reinterpret_cast<uint4 *>(p + 32 * b + 16 * q) = make_uint4(o[0], o[1], o[2], o[3]);
         }
