@@ -469,29 +469,27 @@ __device__ __forceinline__ void plan_build(const PlanArgs &a, int *dyn) {
         gq[q] = min(h0 + q * nt + tid, row_base - 1);
         lo[q] = 0;
       }
-      // seg_row[S] = row_base exceeds every row, so clamping to S never moves lo
+      // seg_row[S] = row_base exceeds every row, so clamping to S never moves lo.
+      // Every slot of the batch is searched and loaded, past nq too (its row
+      // is clamped to the last one, a valid row): a load under a condition
+      // leaves the compiler waiting for each load before the next.
       for (int step = top; step > 0; step >>= 1) {
         int rc[kRowBatch];
 #pragma unroll
-        for (int q = 0; q < kRowBatch; ++q)
-          if (q < nq) rc[q] = seg_row[min(lo[q] + step, S)];
+        for (int q = 0; q < kRowBatch; ++q) rc[q] = seg_row[min(lo[q] + step, S)];
 #pragma unroll
-        for (int q = 0; q < kRowBatch; ++q)
-          if (q < nq) lo[q] = rc[q] <= gq[q] ? min(lo[q] + step, S) : lo[q];
+        for (int q = 0; q < kRowBatch; ++q) lo[q] = rc[q] <= gq[q] ? min(lo[q] + step, S) : lo[q];
       }
       int pix[kRowBatch];
       if constexpr (kLds) {
 #pragma unroll
-        for (int q = 0; q < kRowBatch; ++q)
-          if (q < nq) pix[q] = seg_pgb[lo[q]] + gq[q];
+        for (int q = 0; q < kRowBatch; ++q) pix[q] = seg_pgb[lo[q]] + gq[q];
       } else {
 #pragma unroll
-        for (int q = 0; q < kRowBatch; ++q)
-          if (q < nq) pix[q] = psa[seg_ad[lo[q]]] - seg_row[lo[q]] + gq[q];
+        for (int q = 0; q < kRowBatch; ++q) pix[q] = psa[seg_ad[lo[q]]] - seg_row[lo[q]] + gq[q];
       }
 #pragma unroll
-      for (int q = 0; q < kRowBatch; ++q)
-        if (q < nq) pg[q] = a.page_ids[pix[q]];
+      for (int q = 0; q < kRowBatch; ++q) pg[q] = a.page_ids[pix[q]];
 #pragma unroll
       for (int q = 0; q < kRowBatch; ++q) {
         if (q < nq && h0 + q * nt + tid < row_base && (pg[q] < 0 || pg[q] >= a.n_pages)) {
