@@ -276,7 +276,7 @@ struct EpilogueArgs {
   // the per-slot shrink; the plan is not read (lora_forward's decode path)
   const int4 *sdesc;
   // not null (one slot per token, plan available): rows in the plan's pair
-  // order, 8 consecutive pairs per workgroup (one per wave), so the rows of
+  // order, 4 consecutive pairs per workgroup (one per wave), so the rows of
   // one adapter in a workgroup share its B lines in the CU's caches (1-D
   // grid: n_a workgroups of pair rows over n_x column chunks, then the rows
   // without an active slot in token order)
