@@ -389,8 +389,9 @@ __global__ __launch_bounds__(256, 2) void decode_gemm_shrink_kernel(GemmArgs g, 
 // what another writes, and neither the shrink nor the GEMM needs the plan.
 // GEMM tiles first: they are dispatched one per CU whatever the shrink does.
 // With the shrink parts first, a batch whose slots are all inactive (parts
-// that end at once) had its tiles packed unevenly onto CUs: workload 2
-// with an empty plan took 22.3 us per step against 17.3 us this way, and
+// that end at once) had its tiles packed unevenly onto CUs: the q_proj
+// decode batch (64 tokens, 4096 -> 4096, 64 rank-16 adapters) with an empty
+// plan took 22.3 us per step against 17.3 us this way, and
 // the full step is the same either way (21.9 us).
 template <int MB, bool kMask, bool kLds>
 __global__ __launch_bounds__(256) void decode_gemm_slot_kernel(GemmArgs g, SlotShrinkArgs ss,
@@ -1553,8 +1554,8 @@ hipError_t launch_decode_slot_plan(const GemmConfig &c, const GemmArgs &g,
 
 // Row-major epilogue grid: one wave per (row, 512-column chunk), 4 waves a
 // workgroup; with so few rows that this leaves CUs idle (decode), one wave a
-// workgroup, so that the waves spread over every CU (workload 2: 8.3 ->
-// 7.7 us for the decode epilogue).
+// workgroup, so that the waves spread over every CU (64 tokens, 4096 ->
+// 4096: 8.3 -> 7.7 us for the decode epilogue).
 static hipError_t launch_epilogue_rows(const EpilogueArgs &e, const GemmArgs &g, int dtype,
                                        hipStream_t s) {
   const unsigned n_x = unsigned((g.N + 511) / 512);
@@ -1605,7 +1606,8 @@ hipError_t launch_epilogue(const GemmConfig &c, const GemmArgs &g, int dtype, hi
                  nullptr, 0, 0};
   if (dtype == LORA_BF16 && c.kind == 6 && g.ex.K == 1 && g.ex.pair_tk) {
     // one slot per token: rows in pair order, 4 per workgroup (see EpilogueArgs;
-    // 8-wave workgroups held 16 of the 20 waves a CU takes: workload 3 49.0 -> 45.3 us)
+    // 8-wave workgroups held 16 of the 20 waves a CU takes: 256 tokens,
+    // 4096 -> 11008, 1024 adapters of ranks 8-128, 49.0 -> 45.3 us)
     const int n_x = (g.N + 511) / 512;
     e.pair_tk = g.ex.pair_tk;
     e.n_x = n_x;

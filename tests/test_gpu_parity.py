@@ -647,9 +647,9 @@ def test_merge_elementwise_bound(which):
 @pytest.mark.parametrize("which", [3, 2])
 def test_merge_long_list_with_duplicates(which):
     """300 entries (two groups of list reads), repeated ids and signed
-    coefficients, more listed rank rows than one LDS list holds (workload 3:
-    d_out 1344, the float32-FMA kernel; workload 2: 512 x 768, the MFMA
-    kernel's chunked path)."""
+    coefficients, more listed rank rows than one LDS list holds (the small
+    heterogeneous-rank recipe: d_out 1344, the float32-FMA kernel; the small
+    decode recipe: 512 x 768, the MFMA kernel's chunked path)."""
     w = small(which)
     rng = np.random.default_rng(3)
     ids = rng.integers(0, w.n_adapters, size=300).astype(np.int32)
