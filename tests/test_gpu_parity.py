@@ -1115,3 +1115,59 @@ def test_compress_matches_oracle(dtype, policy):
         assert rel_err(sig[a], s) <= 1e-5
         prod = A2[a * n:a * n + k].T @ B2[a * n:a * n + k]
         assert rel_err(prod, Ao @ Bo) <= tol, a
+
+
+# ---------------------------------------------------------------- output rounding
+
+RNE_CASES = {
+    # 256 x 256 tiles: the rounding in the fused epilogue
+    "fused_tiles": (2100, 8192),
+    # decode tile, split-K partials: the rounding in the epilogue kernel
+    "decode": (64, 640),
+    # 256 x 128 tiles: the rounding in the epilogue kernel after the tile GEMM
+    "tiles_split": (300, 2048),
+}
+
+
+@pytest.mark.parametrize("case", sorted(RNE_CASES))
+def test_output_rounding_is_nearest_even(case):
+    """Every output is rounded once to bf16, to nearest with ties to even.
+    Inputs make each pre-rounding value exact in fp32 and place it on a bf16
+    tie, just above or below one, or on a bf16 value: X rows [1, e, d, 0..],
+    W rows [a, 1, 1, 0..] with a of 7 fraction bits in [1, 2) (ulp 2^-7), e
+    in {0, 2^-9, +-2^-8, +-3*2^-9} and d in {0, +-2^-16}, so Y = a + e + d
+    (every partial sum exact).  Expected bits from torch's own float32 to
+    bfloat16 conversion; no slot is active (gates 0), so Y is the base
+    product alone."""
+    T, d_out = RNE_CASES[case]
+    d_in = 64
+    ids = np.full((T, 1), -1, np.int32)
+    gates = np.zeros((T, 1), np.float32)
+    w = wl.build("rne-" + case, 5, "bf16", T, 1, d_in, d_out, np.array([4], np.int32), ids, gates,
+                 x_var=1.0, w_var=0.02, a_var=1 / 64, b_var=0.02)
+    j = np.arange(d_out)
+    a = (1.0 + (j % 128) / 128.0) * np.where((j // 128) % 2 == 0, 1.0, -1.0)
+    e_set = np.array([0.0, 2.0 ** -9, 2.0 ** -8, -2.0 ** -8, 3 * 2.0 ** -9, -3 * 2.0 ** -9])
+    d_set = np.array([0.0, 2.0 ** -16, -2.0 ** -16])
+    t = np.arange(T)
+    e = e_set[t % len(e_set)]
+    d = d_set[(t // len(e_set)) % len(d_set)]
+    X = np.zeros((T, d_in), np.float32)
+    X[:, 0], X[:, 1], X[:, 2] = 1.0, e, d
+    Wt = np.zeros((d_out, d_in), np.float32)
+    Wt[:, 0], Wt[:, 1], Wt[:, 2] = a, 1.0, 1.0
+    bits = lambda f: (np.asarray(f, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    for arr in (X, Wt):   # every input value is a bf16 value
+        assert np.array_equal(wl.bf16_bits_to_f32(bits(arr)), arr)
+    w.X, w.W_t = bits(X), bits(Wt)
+    L = run(w)
+    assert L.read_plan()["header"][B.PH_PAIRS] == 0
+    exact = (a[None, :] + e[:, None] + d[:, None]).astype(np.float32)
+    assert np.array_equal(exact.astype(np.float64), a[None, :] + e[:, None] + d[:, None])
+    want = torch.from_numpy(exact).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = L.Y_host()
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, (len(bad), bad[:4].tolist())
+    # the ties to even were reached: some outputs sit exactly half-way
+    half = np.abs(exact - wl.bf16_bits_to_f32(bits(exact))) == 2.0 ** -8
+    assert half.any()
