@@ -1171,3 +1171,42 @@ def test_output_rounding_is_nearest_even(case):
     # the ties to even were reached: some outputs sit exactly half-way
     half = np.abs(exact - wl.bf16_bits_to_f32(bits(exact))) == 2.0 ** -8
     assert half.any()
+
+
+def test_merge_rounding_is_nearest_even():
+    """lora_merge_delta rounds W + delta once to bf16, to nearest with ties to
+    even: one rank-2 adapter of scale 1 with A rows e and d and B rows of
+    ones makes delta[n][i] = e_i + d_i, and W[n][i] = a_n of 7 fraction bits,
+    so W + delta is exact in fp32 and sits on, near or off bf16 ties.
+    Expected bits from torch's float32 to bfloat16 conversion."""
+    d_in, d_out = 256, 512
+    ids = np.zeros((1, 1), np.int32)
+    w = wl.build("rne-merge", 6, "bf16", 1, 1, d_in, d_out, np.array([2], np.int32), ids,
+                 np.ones((1, 1), np.float32), x_var=1.0, w_var=0.02, a_var=1 / 64, b_var=0.02,
+                 scale=np.ones(1, np.float32))
+    n = np.arange(d_out)
+    a = (1.0 + (n % 128) / 128.0) * np.where((n // 128) % 2 == 0, 1.0, -1.0)
+    i = np.arange(d_in)
+    e = np.array([0.0, 2.0 ** -9, 2.0 ** -8, -2.0 ** -8, 3 * 2.0 ** -9, -3 * 2.0 ** -9])[i % 6]
+    d = np.array([0.0, 2.0 ** -16, -2.0 ** -16])[(i // 6) % 3]
+    bits = lambda f: (np.asarray(f, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    Wt = np.repeat(a[:, None], d_in, axis=1).astype(np.float32)
+    a_pages, b_pages = w.a_pages.copy(), w.b_pages.copy()
+    p0, p1 = int(w.page_ids[w.page_start[0]]), int(w.page_ids[w.page_start[0] + 1])
+    a_pages[p0], a_pages[p1] = bits(e), bits(d)
+    b_pages[p0], b_pages[p1] = bits(np.ones(d_out)), bits(np.ones(d_out))
+    for v in (Wt, e, d):   # every input value is a bf16 value
+        assert np.array_equal(wl.bf16_bits_to_f32(bits(v)), np.asarray(v, np.float32))
+    w.W_t, w.a_pages, w.b_pages = bits(Wt), a_pages, b_pages
+    L = D.DeviceLayer(w)
+    W = L.W_t.clone()
+    L.run_merge(W, np.zeros(1, np.int32), np.ones(1, np.float32))
+    torch.cuda.synchronize()
+    exact64 = a[:, None] + e[None, :] + d[None, :]
+    exact = exact64.astype(np.float32)
+    assert np.array_equal(exact.astype(np.float64), exact64)
+    want = torch.from_numpy(exact).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = D.to_host(W)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, (len(bad), bad[:4].tolist())
+    assert (np.abs(exact - wl.bf16_bits_to_f32(bits(exact))) == 2.0 ** -8).any()
