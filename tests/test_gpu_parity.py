@@ -865,6 +865,14 @@ def test_grad_x_full_prefill_sampled_rows():
     assert rel_err(D.as_f64(got[rows]), ref) <= TOL["bf16"]
 
 
+def test_grad_x_full_prefill_every_row():
+    """The input gradient of the full fine-tune prefill batch (8192 x 11008
+    -> 4096, keep mask, one fused launch) on every row against the oracle."""
+    w = full(4)
+    L, got = _grad_x_run(w)
+    assert rel_err(D.as_f64(got), O.grad_x_workload(w)) <= TOL["bf16"]
+
+
 def test_grad_x_inactive_rows_equal_base_bit_for_bit():
     w = _with_dY(wl.small(5))
     L, got = _grad_x_run(w)
